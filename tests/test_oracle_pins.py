@@ -1,0 +1,381 @@
+"""Pins for the CPU oracle.
+
+Each oracle function is checked against something other than itself, so that a
+dropped term, a wrong sign, a swapped nibble or a transposed operand inside the
+oracle fails a test here:
+
+* binary16 codec: every one of the 65,536 patterns against Python's ``struct``
+  binary16 decoder, and the encoder against ``numpy.float16`` (round to nearest
+  even) at every rounding boundary.
+* Q4_0 / Q8_0: hand-worked blocks in ``tests/golden`` (from the block layout and
+  rules on the page "fuel-vulkan-kernels — quantized (GGML) kernel contracts",
+  sections dequant_q4_0, dequant_q8_0 and quantize_q8_0), the closed form of the
+  Q4_0 decode over every (scale, nibble) pair, and brute-force nearest-code
+  searches for both quantizers.
+* The product (sections qmatvec_q4_0 and matmul_q4_0_tiled): exact rational
+  sums on tiny shapes, ``math.fsum`` on medium ones, closed forms (one-hot
+  activations, all-8 nibbles, the ramp block, integer data) and linearity, with
+  weights packed here from the layout definition rather than by the oracle.
+"""
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from block_quantized_weight_dequant_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16_value(bits):
+    return struct.unpack("<e", int(bits).to_bytes(2, "little"))[0]
+
+
+def _bits32(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+# ------------------------------------------------------------------ binary16
+
+def test_f16_decode_every_pattern(orc):
+    for h in range(65536):
+        ref = _f16_value(h)
+        got = orc.f16_to_f32(h)
+        if math.isnan(ref):
+            assert np.isnan(got), hex(h)
+        else:
+            assert _bits32(ref) == _bits32(got), hex(h)
+
+
+def _encode_probe_values():
+    h = np.arange(65536, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    v = np.unique(np.abs(v[np.isfinite(v)]))          # every finite magnitude
+    mids = (v[:-1] + v[1:]) / 2                        # every rounding boundary
+    mids32 = mids.astype(np.float32)                   # exact: 12 significant bits
+    up = np.nextafter(mids32, np.float32(np.inf))
+    down = np.nextafter(mids32, np.float32(0))
+    extra = np.array([65504, 65519, 65519.996, 65520, 65536, 1e6, 3e38,
+                      2.0 ** -24, 2.0 ** -25, 2.0 ** -26, 1.5 * 2.0 ** -25, 1e-30,
+                      2.0 ** -14, 2.0 ** -15], dtype=np.float64).astype(np.float32)
+    rnd = wl.normal_f32(7, 100000, 1.0) * np.float32(2.0) ** wl.uniform_ints(8, -30, 20, 100000).astype(np.float32)
+    xs = np.concatenate([v.astype(np.float32), mids32, up, down, extra, rnd])
+    return np.concatenate([xs, -xs]).astype(np.float32)
+
+
+def test_f16_encode_round_to_nearest_even(orc):
+    xs = _encode_probe_values()
+    with np.errstate(over="ignore"):
+        expected = xs.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(x) for x in xs], dtype=np.uint16)
+    bad = np.nonzero(got != expected)[0]
+    assert bad.size == 0, [(float(xs[i]), hex(got[i]), hex(expected[i])) for i in bad[:5]]
+
+
+def test_f16_special_values(orc):
+    assert orc.f32_to_f16(float("inf")) == 0x7C00
+    assert orc.f32_to_f16(float("-inf")) == 0xFC00
+    assert orc.f32_to_f16(-0.0) == 0x8000
+    assert (orc.f32_to_f16(float("nan")) & 0x7C00) == 0x7C00
+    assert orc.f32_to_f16(float("nan")) & 0x3FF
+
+
+# ---------------------------------------------------------------------- Q4_0
+
+def _unpack_q4_0(blob):
+    """Split a Q4_0 stream into (d bits, codes[n_blocks, 32]) from the layout:
+    f16 d little-endian, then byte j = element j (low) | element j+16 (high)."""
+    b = np.asarray(blob, dtype=np.uint8).reshape(-1, 18)
+    dbits = b[:, 0].astype(np.uint16) | (b[:, 1].astype(np.uint16) << 8)
+    codes = np.concatenate([b[:, 2:] & 0x0F, b[:, 2:] >> 4], axis=1).astype(np.int64)
+    return dbits, codes
+
+
+def _pack_q4_0(codes, dbits):
+    """Build a [N, K/32] Q4_0 stream from codes[N, K] in 0..15 and f16 scale
+    bits dbits[N, K/32], straight from the layout definition."""
+    codes = np.asarray(codes, dtype=np.int64)
+    N, K = codes.shape
+    nb = K // 32
+    blob = np.zeros((N, nb, 18), dtype=np.uint8)
+    dbits = np.asarray(dbits, dtype=np.uint16).reshape(N, nb)
+    blob[:, :, 0] = (dbits & 0xFF).astype(np.uint8)
+    blob[:, :, 1] = (dbits >> 8).astype(np.uint8)
+    c = codes.reshape(N, nb, 32)
+    blob[:, :, 2:] = (c[:, :, :16] | (c[:, :, 16:] << 4)).astype(np.uint8)
+    return blob.reshape(-1)
+
+
+@pytest.mark.parametrize("blk", _golden("q4_0_blocks.json")["blocks"], ids=lambda b: b["name"])
+def test_q4_0_hand_blocks(orc, blk):
+    x = np.array(blk["x"], dtype=np.float32)
+    assert orc.q4_0_quantize(x).tobytes().hex(" ") == blk["bytes"]
+    dec = orc.q4_0_dequant(bytes.fromhex(blk["bytes"]))
+    expected = np.array([float(s) for s in blk["decoded"]], dtype=np.float32)
+    assert (_bits32(dec) == _bits32(expected)).all()
+    if "sum_decoded" in blk:
+        assert float(np.sum(dec.astype(np.float64))) == blk["sum_decoded"]
+
+
+def test_q4_0_dequant_every_scale_and_nibble(orc):
+    # One block per f16 bit pattern of d; byte j carries code j in its low nibble
+    # and code 15-j in its high nibble, so each block covers all 16 codes twice.
+    qs = bytes((j | ((15 - j) << 4)) for j in range(16))
+    blob = b"".join(h.to_bytes(2, "little") + qs for h in range(65536))
+    out = orc.q4_0_dequant(blob).reshape(65536, 32)
+    d = np.array([_f16_value(h) for h in range(65536)], dtype=np.float64)
+    codes = np.array(list(range(16)) + [15 - j for j in range(16)], dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        exact = (codes - 8.0)[None, :] * d[:, None]    # exact: 5-bit x 11-bit
+    exp32 = exact.astype(np.float32)                    # exact in f32 as well
+    nan = np.isnan(exp32)
+    assert (np.isnan(out) == nan).all()
+    assert (_bits32(out[~nan]) == _bits32(exp32[~nan])).all()   # signed zeros too
+
+
+def _nearest_q4_codes(t):
+    """Brute force over the 16 codes: the code c minimising |t - (c - 8)|, the
+    larger code on a tie (t is x / d, exact in f64)."""
+    levels = np.arange(16, dtype=np.float64) - 8.0
+    dist = np.abs(t[..., None].astype(np.float64) - levels)
+    rev = dist[..., ::-1]                                # ties -> larger code
+    return 15 - np.argmin(rev, axis=-1)
+
+
+@pytest.mark.parametrize("seed,scale", [(11, 0.02), (12, 1.0), (13, 1e-3), (14, 1e3), (15, 1e-30)])
+def test_q4_0_quantize_nearest_code(orc, seed, scale):
+    x = wl.normal_f32(seed, (4096, 32), scale)
+    x[::97] = 0.0                                        # some all-zero blocks
+    x[5::101, 3] = -x[5::101, 3]                         # and mixed signs at the max
+    blob = orc.q4_0_quantize(x)
+    dbits, codes = _unpack_q4_0(blob)
+    rows = np.arange(x.shape[0])
+    imax = np.argmax(np.abs(x), axis=1)                  # first index of the largest |x|
+    mx = x[rows, imax]
+    d = mx / np.float32(-8.0)
+    assert (dbits == d.astype(np.float16).view(np.uint16)).all()
+    zero = d == 0
+    assert (codes[zero] == 8).all()
+    nz = ~zero
+    assert (codes[rows[nz], imax[nz]] == 0).all()        # the max element maps to -8 * d
+    t = (x[nz] / d[nz, None]).astype(np.float32)         # the f32 quotient x / d
+    ref = _nearest_q4_codes(t)
+    # The sum x/d + 8.5 is one more f32 rounding; it can move the code only when
+    # x/d lies within one f32 ulp of a half-integer tie point.
+    s = t.astype(np.float64) + 8.5
+    near_tie = np.abs(s - np.round(s)) < 2.0 ** -19
+    near_tie &= s != np.round(s)
+    mism = (codes[nz] != ref) & ~near_tie
+    assert not mism.any()
+    assert near_tie.mean() < 1e-3
+    # Reconstruction: within |d|/2 of x, or |d| for the clamped top code.
+    rec = (codes[nz] - 8).astype(np.float64) * d[nz, None].astype(np.float64)
+    err = np.abs(rec - x[nz].astype(np.float64))
+    lim = np.abs(d[nz, None]).astype(np.float64) * np.where(codes[nz] == 15, 1.0, 0.5) * (1 + 2.0 ** -20)
+    assert (err <= lim).all()
+
+
+# ---------------------------------------------------------------------- Q8_0
+
+@pytest.mark.parametrize("blk", _golden("q8_0_blocks.json")["blocks"], ids=lambda b: b["name"])
+def test_q8_0_hand_blocks(orc, blk):
+    x = np.array(blk["x"], dtype=np.float32)
+    assert orc.q8_0_quantize(x).tobytes().hex(" ") == blk["bytes"]
+
+
+def _nearest_q8_codes(t):
+    """Brute force over the 255 codes: the c in [-127, 127] minimising |t - c|,
+    the one of larger magnitude on a tie."""
+    levels = np.arange(-127, 128, dtype=np.float64)
+    dist = np.abs(t[..., None].astype(np.float64) - levels)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = np.where(dist == best, np.abs(levels), -1.0)  # prefer larger |c|
+    idx = np.argmax(cand, axis=-1)
+    return levels[idx].astype(np.int64)
+
+
+@pytest.mark.parametrize("seed,scale", [(21, 1.0), (22, 1e-3), (23, 1e4), (24, 1e-30)])
+def test_q8_0_quantize_nearest_code(orc, seed, scale):
+    x = wl.normal_f32(seed, (2048, 32), scale)
+    x[::89] = 0.0
+    # exact ties: integer and half-integer multiples of d = 1
+    x[1, :] = np.array([127] + [k / 2 for k in range(-15, 16)], dtype=np.float32)
+    blob = orc.q8_0_quantize(x).reshape(-1, 34)
+    dbits = blob[:, 0].astype(np.uint16) | (blob[:, 1].astype(np.uint16) << 8)
+    q = blob[:, 2:].view(np.int8).astype(np.int64)
+    amax = np.max(np.abs(x), axis=1)
+    d = amax / np.float32(127.0)
+    assert (dbits == d.astype(np.float16).view(np.uint16)).all()
+    zero = d == 0
+    assert (q[zero] == 0).all()
+    t = (x[~zero] / d[~zero, None]).astype(np.float32)
+    assert (q[~zero] == _nearest_q8_codes(t)).all()
+    rows = np.arange(x.shape[0])[~zero]
+    imax = np.argmax(np.abs(x[~zero]), axis=1)
+    assert (np.abs(q[rows, imax]) == 127).all()
+
+
+def test_q8_0_round_trip(orc):
+    x = wl.normal_f32(31, 32 * 1000, 1.0)
+    blob = orc.q8_0_quantize(x)
+    back = orc.q8_0_dequant(blob).astype(np.float64).reshape(-1, 32)
+    xb = x.astype(np.float64).reshape(-1, 32)
+    d32 = (np.max(np.abs(x.reshape(-1, 32)), axis=1) / np.float32(127)).astype(np.float64)
+    d16 = (np.max(np.abs(x.reshape(-1, 32)), axis=1) / np.float32(127)).astype(np.float16).astype(np.float64)
+    # |x - q * d16| <= d/2 + 127 * |d - d16|
+    lim = d32 / 2 * (1 + 2.0 ** -20) + 127 * np.abs(d32 - d16)
+    assert (np.abs(back - xb) <= lim[:, None]).all()
+
+
+# ------------------------------------------------------------------- product
+
+def _random_scales(seed, n):
+    """f16 bit patterns of normal, finite scales with random sign."""
+    sign = wl.uniform_ints(seed, 0, 2, n) << 15
+    expo = wl.uniform_ints(seed + 1, 5, 20, n) << 10
+    mant = wl.uniform_ints(seed + 2, 0, 1024, n)
+    return (sign | expo | mant).astype(np.uint16)
+
+
+def _weights_f64(codes, dbits):
+    """Dequantized weights from the layout definition, in f64 (exact)."""
+    N, K = codes.shape
+    d = np.array([_f16_value(h) for h in np.asarray(dbits).reshape(-1)], dtype=np.float64)
+    d = d.reshape(N, K // 32)
+    return (codes.astype(np.float64) - 8.0) * np.repeat(d, 32, axis=1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 5, 32), (2, 4, 64), (3, 5, 96)])
+def test_product_exact_rational(orc, M, N, K):
+    seed = 100 * M + 10 * N + K
+    codes = wl.uniform_ints(seed, 0, 16, (N, K))
+    dbits = _random_scales(seed + 3, N * (K // 32))
+    blob = _pack_q4_0(codes, dbits)
+    a = wl.normal_f32(seed + 7, (M, K), 3.0)
+    w = _weights_f64(codes, dbits)
+    y, bound = orc.q4_0_matmul(a, blob, N, K)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(a[m, k])) * Fraction(w[n, k]) for k in range(K))
+            babs = sum(abs(Fraction(float(a[m, k])) * Fraction(w[n, k])) for k in range(K))
+            assert abs(Fraction(y[m, n]) - exact) <= Fraction(1, 10 ** 12) * babs
+            assert abs(Fraction(bound[m, n]) - babs) <= Fraction(1, 10 ** 12) * babs
+
+
+def test_product_fsum(orc):
+    M, N, K = 4, 37, 1024
+    codes = wl.uniform_ints(41, 0, 16, (N, K))
+    dbits = _random_scales(42, N * (K // 32))
+    blob = _pack_q4_0(codes, dbits)
+    a = wl.normal_f32(43, (M, K), 1.0)
+    w = _weights_f64(codes, dbits)
+    y, bound = orc.q4_0_matmul(a, blob, N, K)
+    for m in range(M):
+        for n in range(N):
+            prods = [float(a[m, k]) * float(w[n, k]) for k in range(K)]   # exact in f64
+            ref = math.fsum(prods)
+            babs = math.fsum(abs(p) for p in prods)
+            assert abs(y[m, n] - ref) <= K * 2.0 ** -53 * babs
+            assert abs(bound[m, n] - babs) <= K * 2.0 ** -53 * babs
+
+
+def test_product_one_hot_picks_the_weight(orc):
+    N, K = 9, 128
+    codes = wl.uniform_ints(51, 0, 16, (N, K))
+    dbits = _random_scales(52, N * (K // 32))
+    blob = _pack_q4_0(codes, dbits)
+    w = _weights_f64(codes, dbits)
+    ks = [0, 17, 31, 32, 77, 127]
+    a = np.zeros((len(ks), K), dtype=np.float32)
+    for m, k in enumerate(ks):
+        a[m, k] = 1.0
+    y, _ = orc.q4_0_matmul(a, blob, N, K)
+    for m, k in enumerate(ks):
+        assert (y[m] == w[:, k]).all()
+
+
+def test_product_all_eights_is_zero(orc):
+    N, K = 5, 256
+    codes = np.full((N, K), 8, dtype=np.int64)
+    blob = _pack_q4_0(codes, _random_scales(61, N * K // 32))
+    a = wl.normal_f32(62, (3, K), 10.0)
+    y, bound = orc.q4_0_matmul(a, blob, N, K)
+    assert (y == 0).all() and (bound == 0).all()
+
+
+def test_product_ramp_block(orc):
+    ramp = next(b for b in _golden("q4_0_blocks.json")["blocks"] if b["name"] == "ramp")
+    y, bound = orc.q4_0_matmul(np.ones((1, 32), np.float32), bytes.fromhex(ramp["bytes"]), 1, 32)
+    assert y[0, 0] == -2.0                               # sum of the decode, not of x (-16)
+    assert bound[0, 0] == 254.0                          # 128 + 126: the clamped top element is 14
+
+
+def test_product_integer_data_is_exact(orc):
+    M, N, K = 3, 6, 192
+    codes = wl.uniform_ints(71, 0, 16, (N, K))
+    dbits = np.full(N * K // 32, 0x3C00, dtype=np.uint16)   # d = 1.0
+    blob = _pack_q4_0(codes, dbits)
+    ai = wl.uniform_ints(72, -100, 101, (M, K))
+    y, _ = orc.q4_0_matmul(ai.astype(np.float32), blob, N, K)
+    ref = ai @ (codes - 8).T                                  # Python/numpy integers
+    assert (y == ref.astype(np.float64)).all()
+
+
+def test_product_is_linear_in_a(orc):
+    M, N, K = 2, 11, 320
+    codes = wl.uniform_ints(81, 0, 16, (N, K))
+    blob = _pack_q4_0(codes, _random_scales(82, N * K // 32))
+    a1 = wl.normal_f32(83, (M, K)).astype(np.float32)
+    a2 = wl.normal_f32(84, (M, K)).astype(np.float32)
+    a1[:, ::2] = 0.0                                          # disjoint supports keep
+    a2[:, 1::2] = 0.0                                         # 2*a1 + 4*a2 exact in f32
+    y1, b1 = orc.q4_0_matmul(a1, blob, N, K)
+    y2, b2 = orc.q4_0_matmul(a2, blob, N, K)
+    y3, _ = orc.q4_0_matmul(2 * a1 + 4 * a2, blob, N, K)     # exact scalings by 2 and 4
+    assert np.all(np.abs(y3 - (2 * y1 + 4 * y2)) <= 1e-12 * (2 * b1 + 4 * b2))
+
+
+def test_product_rows_and_columns_not_transposed(orc):
+    # Distinct per-row scales and per-column activations: a transposed operand or
+    # a swapped index gives a different matrix.
+    M, N, K = 3, 4, 64
+    codes = np.full((N, K), 9, dtype=np.int64)                # weight (9 - 8) * d = d
+    dvals = [1.0, 2.0, 4.0, 8.0]
+    dbits = np.array([[np.float16(v).view(np.uint16)] * (K // 32) for v in dvals]).reshape(-1)
+    blob = _pack_q4_0(codes, dbits)
+    a = np.zeros((M, K), dtype=np.float32)
+    a[0, :] = 1.0
+    a[1, :32] = 1.0
+    a[2, 63] = 3.0
+    y, _ = orc.q4_0_matmul(a, blob, N, K)
+    assert y.tolist() == [[64.0, 128.0, 256.0, 512.0], [32.0, 64.0, 128.0, 256.0], [3.0, 6.0, 12.0, 24.0]]
+
+
+def test_sampled_equals_full(orc):
+    M, N, K = 5, 33, 256
+    x = wl.weights_f32(91, N, K)
+    blob = orc.q4_0_quantize(x)
+    a = wl.activations_f32(92, M, K)
+    y, b = orc.q4_0_matmul(a, blob, N, K)
+    mi = wl.uniform_ints(93, 0, M, 50)
+    ni = wl.uniform_ints(94, 0, N, 50)
+    ys, bs = orc.q4_0_matmul_sampled(a, blob, N, K, mi, ni)
+    assert (ys == y[mi, ni]).all() and (bs == b[mi, ni]).all()
+
+
+def test_threads_do_not_change_results(orc):
+    M, N, K = 3, 64, 512
+    blob = orc.q4_0_quantize(wl.weights_f32(95, N, K))
+    a = wl.activations_f32(96, M, K)
+    y1, b1 = orc.q4_0_matmul(a, blob, N, K, threads=1)
+    y4, b4 = orc.q4_0_matmul(a, blob, N, K, threads=4)
+    assert (y1 == y4).all() and (b1 == b4).all()

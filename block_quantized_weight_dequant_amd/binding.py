@@ -1,0 +1,138 @@
+"""Thin ctypes binding over libq4.so (the C ABI in include/q4.h).
+
+Each function has the name of its C entry point and only marshals arguments:
+tensors become device pointers and byte/element counts, ``stream=None`` becomes
+PyTorch's current HIP stream, and a non-zero status becomes a ``Q4Error``.
+Every step of the computation runs in the library's HIP kernels. There is no
+fallback: if the library is missing this module raises on import.
+
+Arguments that are pointers accept a ``torch.Tensor`` (its ``data_ptr()``), a
+plain integer address, or ``None`` (NULL).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4.so")
+
+Q4_OK = 0
+Q4_ERR_NULL = 1
+Q4_ERR_SHAPE = 2
+Q4_ERR_SIZE = 3
+Q4_ERR_ALIGN = 4
+Q4_ERR_ALIAS = 5
+Q4_ERR_LAUNCH = 6
+Q4_GEMV_MAX_ROWS = 8
+
+#: Every symbol include/q4.h declares.
+EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
+           "q8_quantize", "q4_quantize")
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, entry: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (entry, q4_status_string(status), status))
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libq4.so is not built (%s); run "
+                          "`python -m block_quantized_weight_dequant_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.q4_abi_version.restype = i32
+    lib.q4_abi_version.argtypes = []
+    lib.q4_status_string.restype = ctypes.c_char_p
+    lib.q4_status_string.argtypes = [i32]
+    lib.q4_dequant.restype = i32
+    lib.q4_dequant.argtypes = [P, sz, P, sz, P]
+    for name in ("q4_gemv", "q4_gemm"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [P, P, sz, P, i32, i32, i32, P]
+    for name in ("q8_quantize", "q4_quantize"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [P, sz, P, sz, P]
+    return lib
+
+
+lib = _load_library()
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _nbytes(x) -> int:
+    return int(x.numel() * x.element_size())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return 0
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(status: int, entry: str) -> None:
+    if status != Q4_OK:
+        raise Q4Error(status, entry)
+
+
+def q4_abi_version() -> int:
+    return int(lib.q4_abi_version())
+
+
+def q4_status_string(status: int) -> str:
+    return lib.q4_status_string(int(status)).decode()
+
+
+def q4_dequant(w_q, out, w_bytes=None, out_elems=None, stream=None) -> None:
+    """Q4_0 blocks (uint8 tensor) -> f32 ``out``; sizes default to the tensors'."""
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    oe = int(out.numel()) if out_elems is None else int(out_elems)
+    _check(lib.q4_dequant(_addr(w_q), wb, _addr(out), oe, _stream(stream)), "q4_dequant")
+
+
+def q4_gemv(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for 1 <= M <= 8."""
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    _check(lib.q4_gemv(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                       _stream(stream)), "q4_gemv")
+
+
+def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M."""
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    _check(lib.q4_gemm(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                       _stream(stream)), "q4_gemm")
+
+
+def q8_quantize(x, out_q, n_elems=None, out_bytes=None, stream=None) -> None:
+    """f32 ``x`` -> Q8_0 blocks in the uint8 tensor ``out_q``."""
+    n = int(x.numel()) if n_elems is None else int(n_elems)
+    ob = _nbytes(out_q) if out_bytes is None else int(out_bytes)
+    _check(lib.q8_quantize(_addr(x), n, _addr(out_q), ob, _stream(stream)), "q8_quantize")
+
+
+def q4_quantize(x, out_q, n_elems=None, out_bytes=None, stream=None) -> None:
+    """f32 ``x`` -> Q4_0 blocks in the uint8 tensor ``out_q``."""
+    n = int(x.numel()) if n_elems is None else int(n_elems)
+    ob = _nbytes(out_q) if out_bytes is None else int(out_bytes)
+    _check(lib.q4_quantize(_addr(x), n, _addr(out_q), ob, _stream(stream)), "q4_quantize")
+
+
+def raw_status(entry: str, *args) -> int:
+    """Call a C entry point with raw integer arguments and return its status
+    (for tests of the argument checks)."""
+    return int(getattr(lib, entry)(*args))

@@ -1,0 +1,86 @@
+// The exported C ABI (include/q4.h): validate every argument, then enqueue the
+// kernel on the caller's stream. Only the functions declared in q4.h are
+// exported from the shared library (it is built with hidden visibility).
+#include "q4.h"
+
+#include "launch.h"
+#include "validate.h"
+
+#define Q4_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+int launched(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_LAUNCH; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+Q4_EXPORT int q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+Q4_EXPORT const char *q4_status_string(int status)
+{
+    switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 32, sizes non-negative, "
+                              "element counts a multiple of 32, GEMV rows in [0, 8])";
+    case Q4_ERR_SIZE: return "a byte or element count does not match the shape";
+    case Q4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case Q4_ERR_ALIAS: return "an output overlaps an input";
+    case Q4_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    default: return "unknown status";
+    }
+}
+
+Q4_EXPORT int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_dequant(w_q, w_bytes, out, out_elems, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_dequant(static_cast<const uint8_t *>(w_q), w_bytes / 18, out,
+                                        as_stream(stream)));
+}
+
+Q4_EXPORT int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                      void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemv(a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                     as_stream(stream)));
+}
+
+Q4_EXPORT int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                      void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, 0, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemm(a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                     as_stream(stream)));
+}
+
+Q4_EXPORT int q8_quantize(const float *x, size_t n_elems, void *out_q, size_t out_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_quantize(x, n_elems, out_q, out_bytes, 34, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_q8_quantize(x, n_elems / 32, static_cast<uint8_t *>(out_q),
+                                            as_stream(stream)));
+}
+
+Q4_EXPORT int q4_quantize(const float *x, size_t n_elems, void *out_q, size_t out_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_quantize(x, n_elems, out_q, out_bytes, 18, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_q4_quantize(x, n_elems / 32, static_cast<uint8_t *>(out_q),
+                                            as_stream(stream)));
+}

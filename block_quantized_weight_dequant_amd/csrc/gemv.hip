@@ -1,0 +1,241 @@
+// Decode-shaped Q4_0 x f32 product, y[m, n] = sum_k a[m, k] * w[n, k] for
+// 1 <= M <= 8 activation rows, on gfx950 matrix cores.
+//
+// Operation: docs.rs fuel-dispatch, "quantized (GGML) kernel contracts",
+// section qmatvec_q4_0 (one row there; up to eight rows here), with the Q4_0
+// block of section dequant_q4_0. The work is bound by streaming the weight
+// blocks once (N * K * 18/32 bytes).
+//
+// Design
+// ------
+// * One workgroup of 8 wavefronts owns 16 output columns (16 weight rows) and
+//   the whole K. Wavefront w owns a contiguous run of the K/32 blocks. Lane
+//   (j = lane % 16, g = lane / 16) reads, per block of weight row n0 + j, the
+//   binary16 scale and qs dword g (bytes 4g..4g+3) straight into registers:
+//   every weight byte is read once, and all of a wavefront's loads are issued
+//   before the activations are prepared, so HBM latency overlaps that work.
+// * The 32-element dot products of a block run on v_mfma_f32_16x16x32_f16.
+//   Operand B (32 x 16) holds the exact binary16 integers (q - 8) of 16 weight
+//   rows; operand A (16 x 32) holds the activations split into two binary16
+//   terms, hi = f16(v) and lo = f16(v - hi) (rows 2m and 2m+1 for activation
+//   row m), which together carry 22 significant bits. Each product of a
+//   binary16 pair is exact and the matrix core accumulates in f32.
+// * Decode: the dword's eight nibbles become four f16 pairs with one AND-OR
+//   against the exponent pattern of 1024 and one packed f16 subtraction each.
+//   The high nibbles are decoded in place (bits 4..7 of a half), which yields
+//   16 (q - 8); the activations paired with low nibbles carry the factor 16
+//   instead, so every product is 16 a (q - 8) and one power of two restores it.
+//   The K order inside a block is permuted (elements 4g, 4g+2, 4g+1, 4g+3,
+//   then +16); A uses the same permutation, so the sum is unchanged.
+// * Each block's f32 partial is scaled by its d into f32 accumulators
+//   (d * C + acc), giving the two-level order block partial -> scale -> sum of
+//   blocks. Wavefront partials are summed in LDS in a fixed order, so repeated
+//   calls return identical bits.
+// * Range: activation row m is scaled by a power of two 2^p_m chosen from its
+//   max |a| so that 16 max|a| 2^p_m lies in [2^14, 2^15): no binary16
+//   overflow, and elements far below the row maximum lose at most 2^-25 of
+//   2^p_m absolutely. The scale is undone exactly on the f32 result.
+#include "device_common.h"
+#include "launch.h"
+
+namespace q4k {
+
+constexpr int kGemvWaves = 8;
+constexpr int kGemvThreads = 64 * kGemvWaves;
+
+// B operand for qs dword x (bytes 4g..4g+3 of a block): slots hold
+// (q-8) of elements 4g+0, 4g+2, 4g+1, 4g+3 and 16 (q-8) of 16+4g+0, +2, +1, +3.
+__device__ __forceinline__ f16x8 decode_x16(uint32_t x)
+{
+    const uint32_t t = x >> 8;
+    const uint32_t v0 = (x & 0x000F000Fu) | 0x64006400u;   // 1024 + q (lo nibbles, bytes 0, 2)
+    const uint32_t v1 = (t & 0x000F000Fu) | 0x64006400u;   // 1024 + q (lo nibbles, bytes 1, 3)
+    const uint32_t v2 = (x & 0x00F000F0u) | 0x64006400u;   // 1024 + 16 q (hi nibbles, bytes 0, 2)
+    const uint32_t v3 = (t & 0x00F000F0u) | 0x64006400u;   // 1024 + 16 q (hi nibbles, bytes 1, 3)
+    const f16x2 lo_bias = {(f16)1032.0f, (f16)1032.0f};
+    const f16x2 hi_bias = {(f16)1152.0f, (f16)1152.0f};
+    f16x2 h0 = bitcast<f16x2>(v0) - lo_bias;
+    f16x2 h1 = bitcast<f16x2>(v1) - lo_bias;
+    f16x2 h2 = bitcast<f16x2>(v2) - hi_bias;
+    f16x2 h3 = bitcast<f16x2>(v3) - hi_bias;
+    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+// Split v into binary16 hi + lo with hi = f16(v) and lo = f16(v - hi).
+__device__ __forceinline__ void split2(float v, f16 &hi, f16 &lo)
+{
+    hi = (f16)v;
+    lo = (f16)(v - (float)hi);
+}
+
+template <int M>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restrict__ a,
+                                                           const uint8_t *__restrict__ w,
+                                                           float *__restrict__ y, int N, int K)
+{
+    constexpr int NW = kGemvWaves;
+    constexpr int CB = (M <= 4) ? 128 : 64;   // blocks per K chunk held in LDS
+    constexpr int PB = CB / NW;               // blocks per wavefront per chunk
+    constexpr int NI = 2 * M;                 // A rows in use (hi, lo per row)
+    constexpr int NACC = (M == 1) ? 2 : 4;    // accumulator rows a lane can own
+
+    __shared__ uint4 s_a[CB * 4 * NI];        // [block][g][i] 8-half A operands
+    __shared__ float s_part[NW][M][16];
+    __shared__ float s_amax[NW][M];
+    __shared__ int s_exp[M];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int nblk = K >> 5;
+    const size_t row_bytes = (size_t)nblk * kQ4Bytes;
+    const uint8_t *wrow = w + (size_t)min(n0 + j, N - 1) * row_bytes;
+
+    uint32_t wx[PB], wd[PB];
+    auto issue_loads = [&](int cb0, int cnt) {
+        const int per = (cnt + NW - 1) / NW, b0 = wave * per;
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int b = b0 + u;
+            if (u < per && b < cnt) {
+                const uint8_t *bp = wrow + (size_t)(cb0 + b) * kQ4Bytes;
+                wd[u] = load_u16(bp);
+                wx[u] = load_u32_unaligned(bp + 2 + 4 * g);
+            }
+        }
+    };
+    issue_loads(0, min(CB, nblk));
+
+    // Per-row power-of-two scale from max |a| over the whole row.
+    float mx[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        mx[m] = 0.0f;
+        const float4 *row = reinterpret_cast<const float4 *>(a + (size_t)m * K);
+        for (int f = tid; f < (K >> 2); f += kGemvThreads) {
+            float4 v = row[f];
+            mx[m] = fmaxf(mx[m], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], o));
+        if (lane == 0)
+            s_amax[wave][m] = mx[m];
+    }
+    __syncthreads();
+    if (tid < M) {
+        float am = 0.0f;
+        for (int ww = 0; ww < NW; ++ww)
+            am = fmaxf(am, s_amax[ww][tid]);
+        int e = 0;
+        frexpf(am, &e);                        // am in [2^(e-1), 2^e)
+        int p = (am == 0.0f) ? 0 : 11 - e;     // 16 am 2^p in [2^14, 2^15)
+        p = p > 120 ? 120 : (p < -120 ? -120 : p);
+        s_exp[tid] = p;
+    }
+    __syncthreads();
+    int pexp[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        pexp[m] = s_exp[m];
+
+    float acc[NACC];
+#pragma unroll
+    for (int r = 0; r < NACC; ++r)
+        acc[r] = 0.0f;
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const int nchunks = (nblk + CB - 1) / CB;
+    for (int c = 0; c < nchunks; ++c) {
+        const int cb0 = c * CB, cnt = min(CB, nblk - cb0);
+        if (c > 0) {
+            __syncthreads();                   // every wavefront is done with s_a
+            issue_loads(cb0, cnt);
+        }
+        // A operands of this chunk: entry (b, gg, 2m) = hi, (b, gg, 2m+1) = lo,
+        // slots = 16 a[4gg + {0,2,1,3}] then a[16 + 4gg + {0,2,1,3}], all x 2^p.
+        for (int q = tid; q < cnt * 4 * M; q += kGemvThreads) {
+            const int m = q % M, rest = q / M, gg = rest & 3, b = rest >> 2;
+            const float *src = a + (size_t)m * K + (size_t)(cb0 + b) * 32 + 4 * gg;
+            const float4 L = *reinterpret_cast<const float4 *>(src);
+            const float4 H = *reinterpret_cast<const float4 *>(src + 16);
+            const float sh = ldexpf(1.0f, pexp[m]), sl = 16.0f * sh;
+            const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
+                                H.x * sh, H.z * sh, H.y * sh, H.w * sh};
+            f16x8 hi, lo;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                f16 h, l;
+                split2(v[s], h, l);
+                hi[s] = h;
+                lo[s] = l;
+            }
+            uint4 *dst = &s_a[(b * 4 + gg) * NI + 2 * m];
+            dst[0] = bitcast<uint4>(hi);
+            dst[1] = bitcast<uint4>(lo);
+        }
+        __syncthreads();
+
+        const int per = (cnt + NW - 1) / NW, b0 = wave * per;
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int b = b0 + u;
+            if (u < per && b < cnt) {          // uniform across the wavefront
+                f16x8 aop = {};
+                if (j < NI)
+                    aop = bitcast<f16x8>(s_a[(b * 4 + g) * NI + j]);
+                const f16x8 bop = decode_x16(wx[u]);
+                const f32x4 C = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero4, 0, 0, 0);
+                const float d = f16_bits_to_f32(wd[u]);
+#pragma unroll
+                for (int r = 0; r < NACC; ++r)
+                    acc[r] = fmaf(d, C[r], acc[r]);
+            }
+        }
+    }
+
+    // Lane (j, g) holds C rows 4g..4g+3 of column j: activation rows 2g (hi, lo)
+    // and 2g+1 (hi, lo).
+#pragma unroll
+    for (int h = 0; h < NACC / 2; ++h) {
+        const int m = 2 * g + h;
+        if (m < M)
+            s_part[wave][m][j] = acc[2 * h] + acc[2 * h + 1];
+    }
+    __syncthreads();
+    if (tid < M * 16) {
+        const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
+        float s = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww)
+            s += s_part[ww][m][jj];
+        if (n < N)
+            y[(size_t)m * N + n] = ldexpf(s, -pexp[m] - 4);
+    }
+}
+
+template <int M>
+static hipError_t launch_gemv_m(const float *a, const uint8_t *w, float *y, int N, int K,
+                                hipStream_t s)
+{
+    const unsigned grid = (unsigned)((N + 15) / 16);
+    return launch_kernel(k_gemv_q4_0<M>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
+}
+
+hipError_t launch_gemv(const float *a, const uint8_t *w, float *y, int M, int N, int K,
+                       hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_gemv_m<1>(a, w, y, N, K, s);
+    case 2: return launch_gemv_m<2>(a, w, y, N, K, s);
+    case 3: return launch_gemv_m<3>(a, w, y, N, K, s);
+    case 4: return launch_gemv_m<4>(a, w, y, N, K, s);
+    case 5: return launch_gemv_m<5>(a, w, y, N, K, s);
+    case 6: return launch_gemv_m<6>(a, w, y, N, K, s);
+    case 7: return launch_gemv_m<7>(a, w, y, N, K, s);
+    case 8: return launch_gemv_m<8>(a, w, y, N, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace q4k

@@ -1,0 +1,17 @@
+// Kernel launchers behind the C ABI. Each validates nothing (the ABI layer has
+// already checked every argument) and returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4k {
+
+hipError_t launch_dequant(const uint8_t *w, size_t n_blocks, float *out, hipStream_t s);
+hipError_t launch_gemv(const float *a, const uint8_t *w, float *y, int M, int N, int K, hipStream_t s);
+hipError_t launch_gemm(const float *a, const uint8_t *w, float *y, int M, int N, int K, hipStream_t s);
+hipError_t launch_q8_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
+hipError_t launch_q4_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
+
+}  // namespace q4k

@@ -1,0 +1,98 @@
+// Argument validation for the C ABI (include/q4.h). The order of the checks is
+// fixed: shape, then sizes, then the empty case, then pointers (NULL, 16-byte
+// alignment, output/input overlap). Nothing here touches device memory.
+#include "validate.h"
+
+#include "q4.h"
+
+namespace q4v {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(Span a, Span b)
+{
+    if (a.n == 0 || b.n == 0)
+        return false;
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    // a0 + a.n cannot wrap for a real allocation; the compare stays in unsigned.
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+static bool mul_ok(size_t x, size_t y, size_t *r) { return !__builtin_mul_overflow(x, y, r); }
+
+int check_dequant(const void *w, size_t w_bytes, const float *out, size_t out_elems, bool *empty)
+{
+    *empty = false;
+    if (w_bytes % 18 != 0)
+        return Q4_ERR_SIZE;
+    size_t nb = w_bytes / 18, want = 0, out_bytes = 0;
+    if (!mul_ok(nb, 32, &want) || out_elems != want)
+        return Q4_ERR_SIZE;
+    if (!mul_ok(out_elems, sizeof(float), &out_bytes))
+        return Q4_ERR_SIZE;
+    if (nb == 0) {
+        *empty = true;
+        return Q4_OK;
+    }
+    if (!w || !out)
+        return Q4_ERR_NULL;
+    if (!aligned16(w) || !aligned16(out))
+        return Q4_ERR_ALIGN;
+    if (overlaps({w, w_bytes}, {out, out_bytes}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
+int check_product(const float *a, const void *w, size_t w_bytes, const float *y,
+                  int M, int N, int K, int max_rows, bool *empty)
+{
+    *empty = false;
+    if (M < 0 || N < 0 || K < 32 || K % 32 != 0)
+        return Q4_ERR_SHAPE;
+    if (max_rows > 0 && M > max_rows)
+        return Q4_ERR_SHAPE;
+    size_t row_bytes = (size_t)(K / 32) * 18, w_want = 0, a_bytes = 0, y_bytes = 0;
+    if (!mul_ok((size_t)N, row_bytes, &w_want) || w_bytes != w_want)
+        return Q4_ERR_SIZE;
+    if (!mul_ok((size_t)M, (size_t)K, &a_bytes) || !mul_ok(a_bytes, sizeof(float), &a_bytes))
+        return Q4_ERR_SIZE;
+    if (!mul_ok((size_t)M, (size_t)N, &y_bytes) || !mul_ok(y_bytes, sizeof(float), &y_bytes))
+        return Q4_ERR_SIZE;
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return Q4_OK;
+    }
+    if (!a || !w || !y)
+        return Q4_ERR_NULL;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(y))
+        return Q4_ERR_ALIGN;
+    if (overlaps({y, y_bytes}, {a, a_bytes}) || overlaps({y, y_bytes}, {w, w_bytes}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
+int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_bytes,
+                   size_t block_bytes, bool *empty)
+{
+    *empty = false;
+    if (n_elems % 32 != 0)
+        return Q4_ERR_SHAPE;
+    size_t want = 0, x_bytes = 0;
+    if (!mul_ok(n_elems / 32, block_bytes, &want) || out_bytes != want)
+        return Q4_ERR_SIZE;
+    if (!mul_ok(n_elems, sizeof(float), &x_bytes))
+        return Q4_ERR_SIZE;
+    if (n_elems == 0) {
+        *empty = true;
+        return Q4_OK;
+    }
+    if (!x || !out)
+        return Q4_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out))
+        return Q4_ERR_ALIGN;
+    if (overlaps({x, x_bytes}, {out, out_bytes}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
+}  // namespace q4v

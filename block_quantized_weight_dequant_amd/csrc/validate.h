@@ -1,0 +1,27 @@
+// Argument validation for the C ABI in include/q4.h. Pure host C++ with no HIP
+// dependency: every check here runs before anything is launched.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4v {
+
+// Byte extent [p, p + n) of one argument.
+struct Span {
+    const void *p;
+    size_t n;
+};
+
+// Each returns Q4_OK or a Q4_ERR_* code; *empty is set when the problem has no
+// work (then nothing is to be launched and the pointers were not inspected).
+int check_dequant(const void *w, size_t w_bytes, const float *out, size_t out_elems, bool *empty);
+int check_product(const float *a, const void *w, size_t w_bytes, const float *y,
+                  int M, int N, int K, int max_rows, bool *empty);
+int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_bytes,
+                   size_t block_bytes, bool *empty);
+
+bool aligned16(const void *p);
+bool overlaps(Span a, Span b);
+
+}  // namespace q4v

@@ -1,0 +1,127 @@
+/*
+ * q4.h — C ABI of the MI355X (gfx950) Q4_0 block-quantized weight library.
+ *
+ * Formats (docs.rs fuel-dispatch 0.20.71, page "fuel-vulkan-kernels — quantized
+ * (GGML) kernel contracts"):
+ *   Q4_0 block (section dequant_q4_0): 18 bytes for 32 elements, a little-endian
+ *     binary16 scale d, then 16 bytes; the low nibble of byte j is element j and
+ *     the high nibble is element j+16; element = (nibble - 8) * d, d widened to f32.
+ *   Q8_0 block (sections dequant_q8_0, quantize_q8_0): 34 bytes for 32 elements,
+ *     a little-endian binary16 scale d, then 32 signed bytes; element = q * d.
+ *   Q4_0 weight matrix W[N, K/32] (sections qmatvec_q4_0, matmul_q4_0_tiled): a
+ *     contiguous row-major block stream, K/32 blocks per row, N * (K/32) * 18
+ *     bytes in all, read from its first byte (no strides, no offsets).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates and frees nothing and keeps no state between calls.
+ *   - Every pointer must be 16-byte aligned (the pages' alignment_bytes: 16),
+ *     else Q4_ERR_ALIGN. Arrays are dense and contiguous; f32 matrices are
+ *     row-major.
+ *   - Outputs are fully overwritten, never accumulated into, and must not
+ *     overlap any input (the pages: aliasing none, in_place false), else
+ *     Q4_ERR_ALIAS. No byte outside an output's stated extent is written.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Calls are asynchronous: arguments are checked, the work is enqueued on
+ *     `stream`, and the call returns without synchronizing.
+ *   - Every argument error is detected before anything is launched, and then
+ *     nothing is written. Device faults surface at the caller's next
+ *     synchronization. An empty problem (a zero dimension or element count)
+ *     returns Q4_OK and launches nothing; its pointers may be NULL.
+ *   - Inputs are finite; results for NaN or infinite inputs are unspecified.
+ */
+#ifndef Q4MI_Q4_H
+#define Q4MI_Q4_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4_ABI_VERSION 1
+
+#define Q4_OK 0
+#define Q4_ERR_NULL 1   /* a required pointer is NULL */
+#define Q4_ERR_SHAPE 2  /* K % 32 != 0, K < 32, a negative size, M outside the GEMV range, n % 32 != 0 */
+#define Q4_ERR_SIZE 3   /* a byte or element count disagrees with the shape, or overflows size_t */
+#define Q4_ERR_ALIGN 4  /* a pointer is not 16-byte aligned */
+#define Q4_ERR_ALIAS 5  /* an output overlaps an input */
+#define Q4_ERR_LAUNCH 6 /* the HIP runtime refused the launch */
+
+/* Largest number of activation rows q4_gemv accepts. */
+#define Q4_GEMV_MAX_ROWS 8
+
+/* Returns Q4_ABI_VERSION of the library actually loaded. */
+int q4_abi_version(void);
+
+/* Returns a static, NUL-terminated description of a status code. */
+const char *q4_status_string(int status);
+
+/*
+ * q4_dequant — Q4_0 block stream to dense f32 (section dequant_q4_0).
+ *   w_q       n_blocks * 18 bytes of Q4_0 blocks, with n_blocks = w_bytes / 18.
+ *   w_bytes   must be a multiple of 18 (else Q4_ERR_SIZE).
+ *   out       out_elems f32; out_elems must equal w_bytes / 18 * 32 (else
+ *             Q4_ERR_SIZE). Element 32*b + j of out is element j of block b.
+ * Bit-exact: every output is the exact product (nibble - 8) * d, so results
+ * equal any correct evaluation bit for bit, signed zeros included.
+ */
+int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream);
+
+/*
+ * q4_gemv — decode-shaped product y = a @ dequant(W)^T for 1 <= M <= 8
+ * activation rows (section qmatvec_q4_0, widened from one row to eight).
+ *   a         [M, K] f32, row-major.
+ *   w_q       W[N, K/32] Q4_0 block stream; w_bytes == N * (K/32) * 18.
+ *   y         [M, N] f32, row-major: y[m, n] = sum_k a[m, k] * w[n, k].
+ *   M in [1, 8], N >= 1, K >= 32 and K % 32 == 0 (else Q4_ERR_SHAPE);
+ *   M == 0 or N == 0 is an empty problem.
+ * Accuracy: |y - y_exact| <= 1e-5 * sum_k |a[m, k] * w[n, k]| + 1e-6 per
+ * element. The reduction order is fixed, so repeated calls return identical bits.
+ */
+int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
+            int M, int N, int K, void *stream);
+
+/*
+ * q4_gemm — prefill-shaped product y = a @ dequant(W)^T for any M >= 1
+ * (section matmul_q4_0_tiled), tiled through LDS onto the matrix cores.
+ *   Arguments, layouts and the accuracy statement are those of q4_gemv, with
+ *   M >= 1 unbounded (M == 0 or N == 0 is an empty problem).
+ *   Activations must satisfy |a| < 65504 (they are split into two binary16
+ *   terms); results for larger activations are unspecified.
+ * The reduction order is fixed, so repeated calls return identical bits.
+ */
+int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
+            int M, int N, int K, void *stream);
+
+/*
+ * q8_quantize — f32 to Q8_0 blocks (section quantize_q8_0).
+ *   x         n_elems f32; n_elems % 32 == 0 (else Q4_ERR_SHAPE).
+ *   out_q     out_bytes == n_elems / 32 * 34 (else Q4_ERR_SIZE).
+ * Per 32-element block: d = max|x| / 127 in f32; the binary16 d (round to
+ * nearest even) is stored little-endian, then 32 bytes q = round(x / d) in
+ * two's complement, with round() half away from zero, the quotient formed from
+ * the f32 d, and q = 0 (d = +0) for an all-zero block. Bit-exact and
+ * deterministic.
+ */
+int q8_quantize(const float *x, size_t n_elems, void *out_q, size_t out_bytes, void *stream);
+
+/*
+ * q4_quantize — f32 to Q4_0 blocks with GGML's reference rule: per 32-element
+ * block, d = (the element of largest |x|, the first on ties) / -8 in f32, the
+ * binary16 d stored little-endian, then q_j = min(15, (int)(x_j / d + 8.5)) in
+ * two separately rounded f32 operations (q = 8 throughout when d == 0), packed
+ * as byte j = q_j | q_{j+16} << 4. This rule is not on the pages; it makes
+ * Q4_0 weights on the device from f32 ones.
+ *   x         n_elems f32; n_elems % 32 == 0 (else Q4_ERR_SHAPE).
+ *   out_q     out_bytes == n_elems / 32 * 18 (else Q4_ERR_SIZE).
+ * Bit-exact and deterministic.
+ */
+int q4_quantize(const float *x, size_t n_elems, void *out_q, size_t out_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MI_Q4_H */

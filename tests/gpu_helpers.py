@@ -1,0 +1,63 @@
+"""Helpers for the GPU parity tests: device buffers with guard regions, NaN
+prefill, and the Q4_0 test-weight blobs made by the oracle."""
+import numpy as np
+import torch
+
+import oracle
+from block_quantized_weight_dequant_amd import workloads as wl
+
+DEV = torch.device("cuda:0")
+GUARD = 256           # guard bytes on each side of an output (a multiple of 16)
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+class Guarded:
+    """A device output of `n` elements of `dtype` with GUARD bytes of a known
+    pattern before and after it. `.view` is the (16-byte aligned) output."""
+
+    def __init__(self, n: int, dtype: torch.dtype, fill=float("nan")):
+        self.esize = torch.empty((), dtype=dtype).element_size()
+        self.g = GUARD // self.esize
+        self.n = n
+        self.buf = torch.empty(n + 2 * self.g, dtype=dtype, device=DEV)
+        if dtype.is_floating_point:
+            self.buf.fill_(fill)
+            self.buf[: self.g].fill_(-1234.5)
+            self.buf[self.g + n:].fill_(-1234.5)
+        else:
+            self.buf.fill_(0xA5 if dtype == torch.uint8 else 0x5A5A)
+        self.pre = self.buf[: self.g].clone()
+        self.post = self.buf[self.g + n:].clone()
+        self.view = self.buf[self.g: self.g + n]
+        assert self.view.data_ptr() % 16 == 0
+
+    def guards_intact(self) -> bool:
+        return bool(torch.equal(self.buf[: self.g], self.pre)
+                    and torch.equal(self.buf[self.g + self.n:], self.post))
+
+    def host(self) -> np.ndarray:
+        return self.view.cpu().numpy()
+
+
+def q4_blob(N: int, K: int, seed: int) -> np.ndarray:
+    """Seeded N(0, 0.02^2) weights quantized to Q4_0 by the oracle."""
+    return oracle.q4_0_quantize(wl.weights_f32(seed, N, K))
+
+
+def assert_within_tolerance(y_gpu: np.ndarray, y_ref: np.ndarray, bound: np.ndarray, what=""):
+    """|y_gpu - y_ref| <= 1e-5 * sum|a w| + 1e-6 element by element."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    assert np.isfinite(y_gpu).all(), "%s: non-finite output" % what
+    err = np.abs(y_gpu - y_ref)
+    tol = oracle.tolerance(bound)
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, "%s: %d elements out of tolerance, first %s: got %r ref %r tol %r" % (
+        what, len(bad), tuple(bad[0]), y_gpu[tuple(bad[0])], y_ref[tuple(bad[0])], tol[tuple(bad[0])])
+    return float(np.max(err / tol)) if err.size else 0.0
+
+
+def f32_bits(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).view(np.uint32)

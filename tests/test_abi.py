@@ -1,0 +1,164 @@
+"""CPU tests of the C ABI (include/q4.h): the library loads, exports exactly the
+declared symbols, and rejects every invalid argument before launching anything.
+
+No call here reaches a kernel launch: every argument set is invalid (or empty),
+so the pointers, which are fake addresses or host buffers, are never touched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+binding = pytest.importorskip("block_quantized_weight_dequant_amd.binding")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The argument-check tests hand fake addresses to the library. Each call is
+# invalid, so nothing is launched; as a second safeguard they do not run at all
+# where a GPU is visible.
+fake_addresses = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: CPU-only test")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def _header_defines():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(Q4_\w+)\s+(\d+)", text)}
+
+
+def test_exports_match_header():
+    declared = _header_functions()
+    assert declared == sorted(binding.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines()
+                      if l.split()[-1].startswith(("q4_", "q8_")))
+    assert exported == declared
+    for name in declared:
+        assert hasattr(binding.lib, name)
+
+
+def test_version_and_status_codes():
+    defs = _header_defines()
+    assert binding.q4_abi_version() == defs["Q4_ABI_VERSION"]
+    for name in ("Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_SIZE", "Q4_ERR_ALIGN",
+                 "Q4_ERR_ALIAS", "Q4_ERR_LAUNCH", "Q4_GEMV_MAX_ROWS"):
+        assert getattr(binding, name) == defs[name]
+    strings = {binding.q4_status_string(c) for c in range(0, 7)}
+    assert len(strings) == 7 and binding.q4_status_string(99) == "unknown status"
+
+
+BASE = 0x7F0000000000       # fake, 16-byte aligned device-looking addresses
+A, W, Y = BASE, BASE + (1 << 32), BASE + (2 << 32)
+
+
+def _prod(entry, a, w, wb, y, M, N, K):
+    return binding.raw_status(entry, a, w, wb, y, M, N, K, 0)
+
+
+def _wb(N, K):
+    return N * (K // 32) * 18
+
+
+@fake_addresses
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm"])
+def test_product_argument_checks(entry):
+    S = binding
+    assert _prod(entry, A, W, _wb(4, 64), Y, 1, 4, 48) == S.Q4_ERR_SHAPE      # K % 32
+    assert _prod(entry, A, W, 0, Y, 1, 4, 0) == S.Q4_ERR_SHAPE                # K < 32
+    assert _prod(entry, A, W, _wb(4, 64), Y, -1, 4, 64) == S.Q4_ERR_SHAPE
+    assert _prod(entry, A, W, _wb(4, 64), Y, 1, -4, 64) == S.Q4_ERR_SHAPE
+    assert _prod(entry, A, W, _wb(4, 64) + 1, Y, 1, 4, 64) == S.Q4_ERR_SIZE   # blob length
+    assert _prod(entry, A, W, _wb(4, 64) - 18, Y, 1, 4, 64) == S.Q4_ERR_SIZE
+    assert _prod(entry, None, W, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_NULL
+    assert _prod(entry, A, None, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_NULL
+    assert _prod(entry, A, W, _wb(4, 64), None, 1, 4, 64) == S.Q4_ERR_NULL
+    assert _prod(entry, A + 4, W, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_ALIGN
+    assert _prod(entry, A, W + 2, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_ALIGN
+    assert _prod(entry, A, W, _wb(4, 64), Y + 8, 1, 4, 64) == S.Q4_ERR_ALIGN
+    assert _prod(entry, A, W, _wb(4, 64), A + 128, 2, 4, 64) == S.Q4_ERR_ALIAS  # y inside a
+    assert _prod(entry, A, W, _wb(4, 64), W + 32, 1, 4, 64) == S.Q4_ERR_ALIAS   # y inside w
+    assert _prod(entry, A, W, _wb(8, 64), W - 16, 1, 8, 64) == S.Q4_ERR_ALIAS   # y ends inside w
+    # empty problems: OK without looking at the pointers
+    assert _prod(entry, None, None, _wb(4, 64), None, 0, 4, 64) == S.Q4_OK
+    assert _prod(entry, None, None, 0, None, 3, 0, 64) == S.Q4_OK
+
+
+@fake_addresses
+def test_gemv_row_limit():
+    assert _prod("q4_gemv", A, W, _wb(4, 64), Y, 9, 4, 64) == binding.Q4_ERR_SHAPE
+    assert _prod("q4_gemv", None, None, _wb(4, 64), None, 0, 4, 64) == binding.Q4_OK
+
+
+@fake_addresses
+def test_size_overflow():
+    # 32-bit M, N, K cannot overflow a 64-bit byte count, but element counts can.
+    assert binding.raw_status("q4_dequant", W, 18 * 2 ** 60, Y, 0, 0) == binding.Q4_ERR_SIZE
+    assert binding.raw_status("q8_quantize", A, 2 ** 63, Y, 2 ** 58 * 34, 0) == binding.Q4_ERR_SIZE
+
+
+@fake_addresses
+def test_dequant_argument_checks():
+    S = binding
+    st = lambda w, wb, o, oe: binding.raw_status("q4_dequant", w, wb, o, oe, 0)
+    assert st(W, 35, Y, 64) == S.Q4_ERR_SIZE
+    assert st(W, 36, Y, 63) == S.Q4_ERR_SIZE
+    assert st(None, 0, None, 0) == S.Q4_OK
+    assert st(None, 36, Y, 64) == S.Q4_ERR_NULL
+    assert st(W, 36, None, 64) == S.Q4_ERR_NULL
+    assert st(W + 2, 36, Y, 64) == S.Q4_ERR_ALIGN
+    assert st(W, 36, Y + 4, 64) == S.Q4_ERR_ALIGN
+    assert st(W, 36, W + 16, 64) == S.Q4_ERR_ALIAS
+    assert st(W, 36, W - 240, 64) == S.Q4_ERR_ALIAS
+
+
+@fake_addresses
+@pytest.mark.parametrize("entry,blk", [("q8_quantize", 34), ("q4_quantize", 18)])
+def test_quantize_argument_checks(entry, blk):
+    S = binding
+    st = lambda x, n, o, ob: binding.raw_status(entry, x, n, o, ob, 0)
+    assert st(A, 33, Y, blk) == S.Q4_ERR_SHAPE
+    assert st(A, 64, Y, 2 * blk + 1) == S.Q4_ERR_SIZE
+    assert st(A, 64, Y, blk) == S.Q4_ERR_SIZE
+    assert st(None, 0, None, 0) == S.Q4_OK
+    assert st(None, 64, Y, 2 * blk) == S.Q4_ERR_NULL
+    assert st(A, 64, None, 2 * blk) == S.Q4_ERR_NULL
+    assert st(A + 8, 64, Y, 2 * blk) == S.Q4_ERR_ALIGN
+    assert st(A, 64, Y + 2, 2 * blk) == S.Q4_ERR_ALIGN
+    assert st(A, 64, A + 128, 2 * blk) == S.Q4_ERR_ALIAS
+
+
+def test_rejected_call_writes_nothing():
+    # Host buffers stand in for device memory; a rejected call never reads or
+    # writes them.
+    y = np.full(64, 7.0, dtype=np.float32)
+    a = np.ones(64, dtype=np.float32)
+    w = np.zeros(4 * 18, dtype=np.uint8)
+    st = binding.raw_status("q4_gemm", a.ctypes.data, w.ctypes.data, w.size + 1, y.ctypes.data,
+                            1, 2, 64, 0)
+    assert st == binding.Q4_ERR_SIZE
+    assert (y == 7.0).all()
+
+
+@fake_addresses
+def test_binding_raises_q4error():
+    with pytest.raises(binding.Q4Error) as e:
+        binding.q4_gemm(A, W, Y, 1, 4, 48, w_bytes=_wb(4, 64), stream=0)
+    assert e.value.status == binding.Q4_ERR_SHAPE

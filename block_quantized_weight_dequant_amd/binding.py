@@ -38,6 +38,12 @@ class Q4Error(RuntimeError):
 
 
 def _load_library():
+    # The caller's tensors and streams belong to PyTorch's HIP runtime, and
+    # PyTorch ships its own copy of it. Importing torch first makes the dynamic
+    # loader resolve libq4.so's libamdhip64.so.7 to that already-loaded copy
+    # (same soname); loaded the other way round, the process would hold two
+    # HIP runtimes and PyTorch's stream handles would be foreign to ours.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError("libq4.so is not built (%s); run "
                           "`python -m block_quantized_weight_dequant_amd.build`" % LIB_PATH)

@@ -42,6 +42,7 @@ namespace q4k {
 
 constexpr int kGemvWaves = 8;
 constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kGemvStreamWaves = 8;
 
 // B operand for qs dword x (bytes 4g..4g+3 of a block): slots hold
 // (q-8) of elements 4g+0, 4g+2, 4g+1, 4g+3 and 16 (q-8) of 16+4g+0, +2, +1, +3.
@@ -214,11 +215,325 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant for rows that are 16-byte aligned (K % 256 == 0), which
+// covers the decode shapes. Same arithmetic as above; what changes is how the
+// weight bytes reach the matrix cores:
+// * Each wavefront owns a run of blocks of the workgroup's 16 rows and walks it
+//   in chunks of CH blocks (CH * 18 bytes per row, a multiple of 144 and so of
+//   16). A chunk is fetched with aligned 16-byte loads, lane (r, c) taking
+//   16-byte column c of row r, and written unchanged into the wavefront's own
+//   LDS area. Operands are then read back with aligned LDS dword pairs and
+//   realigned with v_alignbyte. No global load is narrower than 16 bytes or
+//   misaligned, and the next chunk's loads are in flight while the current
+//   one is computed.
+// * The activations of a chunk are split by the whole wavefront (each lane a
+//   few 8-element groups) and passed to the A-operand lanes through LDS. The
+//   power-of-two scale is chosen per (chunk, activation row) from the chunk's
+//   own max |a|, and undone on that chunk's f32 partial, so no workgroup-wide
+//   pass over the activations is needed.
+// * Wavefront partials meet in LDS once, at the end, and are summed in a
+//   fixed order.
+
+// Order LDS traffic between the lanes of one wavefront: its LDS operations
+// execute in issue order, so it is enough that the compiler keeps them there.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int M, int NW, int CH_>
+struct GemvStreamCfg {
+    static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
+    static constexpr int CPR = CH * 18 / 16;              // 16-byte columns per staged row
+    static constexpr int NLOAD = (CPR + 3) / 4;           // 16-byte loads per lane per chunk
+    static constexpr int RS = CH * 18 + 16;               // LDS bytes per staged row
+    static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
+    static constexpr int NI = 2 * M;                      // A rows in use
+    static constexpr int ABYTES = CH * 4 * NI * 16;       // A operands per wavefront
+    static constexpr int NENT = CH * 4 * M;               // 8-element activation groups per chunk
+    static constexpr int EPL = (NENT + 63) / 64;          // ... per lane
+    static constexpr int LDS_PER_WAVE = WBYTES + ABYTES;
+    static_assert(CH == 8 || CH == 16, "chunks are 8 or 16 blocks");
+};
+
+// Maximum of a non-negative float over the wavefront, returned to every lane.
+// Non-negative IEEE floats order like their bit patterns, so the reduction
+// runs on integers: DPP within quads, half-rows and rows, then one readlane
+// per row of 16 lanes.
+__device__ __forceinline__ float wave_max_nonneg(float v)
+{
+    int x = __builtin_bit_cast(int, v);
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false));   // row_mirror
+    const int r = max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+                      max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+    return __builtin_bit_cast(float, r);
+}
+
+// decode_x16 with the exponent pattern supplied in a VGPR. gfx9 VOP3 takes
+// no literal operand, so with the pattern in a register the compiler can form
+// each (x & mask) | pattern as one v_and_or_b32 (mask in an SGPR) instead of
+// a v_and_b32 and a v_or_b32.
+__device__ __forceinline__ f16x8 decode_x16_fast(uint32_t x, uint32_t magic_v)
+{
+    const uint32_t t = x >> 8;
+    const uint32_t v0 = (x & 0x000F000Fu) | magic_v;
+    const uint32_t v1 = (t & 0x000F000Fu) | magic_v;
+    const uint32_t v2 = (x & 0x00F000F0u) | magic_v;
+    const uint32_t v3 = (t & 0x00F000F0u) | magic_v;
+    const f16x2 lo_bias = {(f16)1032.0f, (f16)1032.0f};
+    const f16x2 hi_bias = {(f16)1152.0f, (f16)1152.0f};
+    f16x2 h0 = bitcast<f16x2>(v0) - lo_bias;
+    f16x2 h1 = bitcast<f16x2>(v1) - lo_bias;
+    f16x2 h2 = bitcast<f16x2>(v2) - hi_bias;
+    f16x2 h3 = bitcast<f16x2>(v3) - hi_bias;
+    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+template <int M, int NW, int CH>
+__global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__restrict__ a,
+                                                             const uint8_t *__restrict__ w,
+                                                             float *__restrict__ y, int N, int K,
+                                                             int per)
+{
+    using C = GemvStreamCfg<M, NW, CH>;
+    constexpr int NACC = (M == 1) ? 2 : 4;
+    constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
+
+    // Per wavefront: [staged weight bytes | A operands].
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[NW * C::LDS_PER_WAVE];
+    __shared__ float s_part[NW][M][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int nblk = K >> 5;
+    const uint32_t row_bytes = (uint32_t)nblk * kQ4Bytes;
+    uint8_t *s_w = s_mem + wave * C::LDS_PER_WAVE;
+    uint8_t *s_a = s_w + C::WBYTES;
+
+    // This wavefront's blocks: [wb0, wb1), a whole number of CH-block chunks
+    // (the host picks per and CH so that every chunk is full).
+    const int wb0 = min(wave * per, nblk), wb1 = min(wb0 + per, nblk);
+
+    // Loader role: row lr = lane % 16, 16-byte columns lc0 + 4 i.
+    const int lr = lane & 15, lc0 = lane >> 4;
+    const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
+
+    u32x4 wreg[C::NLOAD];
+    float4 areg[C::EPL][2];
+    // Activation group e = (m * CH + b) * 4 + gg: row m, block b of the chunk,
+    // elements 4gg..4gg+3 and 16+4gg..16+4gg+3. Activations are requested first
+    // (vmcnt drains in issue order), so their split overlaps the weight loads.
+    const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a);
+    auto fetch = [&](int cb0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < C::EPL; ++r) {
+            const int e = lane + 64 * r;
+            const int m = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
+            if (e < C::NENT) {
+                const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + 4 * gg) * 4u;
+                areg[r][0] = *reinterpret_cast<const float4 *>(a8 + off);
+                areg[r][1] = *reinterpret_cast<const float4 *>(a8 + off + 64u);
+            }
+        }
+        const uint32_t base = lrow_off + (uint32_t)cb0 * kQ4Bytes;
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const int col = lc0 + 4 * i;
+            if (col < C::CPR)
+                wreg[i] = *reinterpret_cast<const u32x4 *>(w + (base + 16u * col));
+        }
+    };
+
+    if (wb0 < wb1)
+        fetch(wb0);
+
+    // A operands of a chunk live in registers. Lanes j >= NI (A rows no
+    // activation row uses) keep the zeros set here: each chunk refreshes only
+    // lanes j < NI, with reads masked to those lanes.
+    f16x8 aop[C::CH];
+#pragma unroll
+    for (int b = 0; b < C::CH; ++b)
+        aop[b] = (f16x8){};
+    const uint8_t *a_lane = s_a + (g * C::NI + min(j, C::NI - 1)) * 16;
+    // The exponent pattern of 1024.0 in both halves, as a value the compiler
+    // cannot fold back into a literal (one v_mov at kernel start; no MFMA is in
+    // flight there).
+    uint32_t magic_v;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic_v));
+
+    float ysum[NACC / 2];
+#pragma unroll
+    for (int h = 0; h < NACC / 2; ++h)
+        ysum[h] = 0.0f;
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    for (int cb0 = wb0; cb0 < wb1; cb0 += C::CH) {
+
+        // Per-row scale from this chunk's max |a|, then the split A operands.
+        float mx[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            mx[m] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < C::EPL; ++r) {
+            const int e = lane + 64 * r;
+            const int me = e / (4 * C::CH);
+            if (e < C::NENT) {
+                const float4 L = areg[r][0], H = areg[r][1];
+                const float v = fmaxf(fmaxf(fmaxf(fabsf(L.x), fabsf(L.y)), fmaxf(fabsf(L.z), fabsf(L.w))),
+                                      fmaxf(fmaxf(fabsf(H.x), fabsf(H.y)), fmaxf(fabsf(H.z), fabsf(H.w))));
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (m == me)
+                        mx[m] = fmaxf(mx[m], v);
+            }
+        }
+        int pexp[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float am = wave_max_nonneg(mx[m]);
+            int e2 = 0;
+            frexpf(am, &e2);
+            int p = (am == 0.0f) ? 0 : 11 - e2;        // 16 max|a| 2^p in [2^14, 2^15)
+            pexp[m] = p > 120 ? 120 : (p < -120 ? -120 : p);
+        }
+#pragma unroll
+        for (int r = 0; r < C::EPL; ++r) {
+            const int e = lane + 64 * r;
+            const int me = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
+            if (e < C::NENT) {
+                int pm = 0;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (m == me)
+                        pm = pexp[m];
+                const float sh = ldexpf(1.0f, pm), sl = 16.0f * sh;
+                const float4 L = areg[r][0], H = areg[r][1];
+                const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
+                                    H.x * sh, H.z * sh, H.y * sh, H.w * sh};
+                f16x8 hi, lo;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    f16 hh, ll;
+                    split2(v[s], hh, ll);
+                    hi[s] = hh;
+                    lo[s] = ll;
+                }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(s_a + b * ASTRIDE + (gg * C::NI + 2 * me) * 16);
+                dst[0] = bitcast<u32x4>(hi);
+                dst[1] = bitcast<u32x4>(lo);
+            }
+        }
+        // Stage this chunk's weight bytes.
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const int col = lc0 + 4 * i;
+            if (col < C::CPR)
+                *reinterpret_cast<u32x4 *>(s_w + lr * C::RS + 16 * col) = wreg[i];
+        }
+        // Prefetch the next chunk while this one is computed.
+        if (cb0 + C::CH < wb1)
+            fetch(cb0 + C::CH);
+        wave_lds_sync();
+        if (j < C::NI) {
+#pragma unroll
+            for (int b = 0; b < C::CH; ++b)
+                aop[b] = *reinterpret_cast<const f16x8 *>(a_lane + b * ASTRIDE);
+        }
+
+        float acc[NACC];
+#pragma unroll
+        for (int r = 0; r < NACC; ++r)
+            acc[r] = 0.0f;
+        // qs dword g of block b starts at byte 18 b + 2 + 4 g of the staged row:
+        // 2 bytes past a dword boundary for even b, on one for odd b. Blocks go
+        // in groups of four independent MFMAs, then their scale FMAs, so the
+        // matrix-core latency overlaps the next group's decode.
+        const uint8_t *wl = s_w + j * C::RS;
+        const uint32_t *wq = reinterpret_cast<const uint32_t *>(wl + 4 * g);
+#pragma unroll
+        for (int b4 = 0; b4 < C::CH; b4 += 4) {
+            f32x4 Cv[4];
+            float d[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int b = b4 + u;
+                uint32_t x;
+                if (b % 2 == 0)
+                    x = __builtin_amdgcn_alignbyte(wq[(18 * b) / 4 + 1], wq[(18 * b) / 4], 2u);
+                else
+                    x = wq[(18 * b + 2) / 4];
+                d[u] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * kQ4Bytes));
+                Cv[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[b], decode_x16_fast(x, magic_v),
+                                                                zero4, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < NACC; ++r)
+                    acc[r] = fmaf(d[u], Cv[u][r], acc[r]);
+        }
+        // Undo this chunk's scale (and the factor 16) on its partial.
+#pragma unroll
+        for (int h = 0; h < NACC / 2; ++h) {
+            const int m = 2 * g + h;
+            int pm = 0;
+#pragma unroll
+            for (int mm = 0; mm < M; ++mm)
+                if (mm == m)
+                    pm = pexp[mm];
+            ysum[h] += ldexpf(acc[2 * h] + acc[2 * h + 1], -pm - 4);
+        }
+        wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
+    }
+
+#pragma unroll
+    for (int h = 0; h < NACC / 2; ++h) {
+        const int m = 2 * g + h;
+        if (m < M)
+            s_part[wave][m][j] = ysum[h];
+    }
+    __syncthreads();
+    if (tid < M * 16) {
+        const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
+        float s = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww)
+            s += s_part[ww][m][jj];
+        if (n < N)
+            y[(size_t)m * N + n] = s;
+    }
+}
+
 template <int M>
 static hipError_t launch_gemv_m(const float *a, const uint8_t *w, float *y, int N, int K,
                                 hipStream_t s)
 {
     const unsigned grid = (unsigned)((N + 15) / 16);
+    // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0) and
+    // 32-bit byte offsets. Each wavefront gets `per` blocks (a multiple of 8);
+    // chunks of 16 blocks when every wavefront's share divides by 16, else 8.
+    constexpr int NW = kGemvStreamWaves;
+    const int nblk = K / 32;
+    if (K % 256 == 0 && (size_t)N * (size_t)nblk * 18 < ((size_t)1 << 31) &&
+        (size_t)M * (size_t)K * 4 < ((size_t)1 << 31)) {
+        const int per = (((nblk + NW - 1) / NW) + 7) & ~7;
+        const int last = nblk - (nblk - 1) / per * per;       // blocks of the last busy wavefront
+        if constexpr (M <= 4) {
+            if (per % 16 == 0 && last % 16 == 0)
+                return launch_kernel(k_gemv_q4_0_stream<M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s,
+                                     a, w, y, N, K, per);
+        }
+        return launch_kernel(k_gemv_q4_0_stream<M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, a, w,
+                             y, N, K, per);
+    }
     return launch_kernel(k_gemv_q4_0<M>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
 }
 

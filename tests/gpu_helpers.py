@@ -11,7 +11,7 @@ GUARD = 256           # guard bytes on each side of an output (a multiple of 16)
 
 
 def to_dev(x: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    return torch.from_numpy(np.array(x, copy=True, order="C")).to(DEV)
 
 
 class Guarded:

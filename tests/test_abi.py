@@ -162,3 +162,11 @@ def test_binding_raises_q4error():
     with pytest.raises(binding.Q4Error) as e:
         binding.q4_gemm(A, W, Y, 1, 4, 48, w_bytes=_wb(4, 64), stream=0)
     assert e.value.status == binding.Q4_ERR_SHAPE
+
+
+def test_one_hip_runtime_in_process():
+    # The binding loads PyTorch's HIP runtime before libq4.so, so both resolve
+    # to one copy and PyTorch's stream handles are valid for the library.
+    maps = open("/proc/self/maps").read().splitlines()
+    runtimes = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(runtimes) == 1, runtimes

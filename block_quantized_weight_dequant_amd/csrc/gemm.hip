@@ -12,12 +12,14 @@
 //   each own a 64 x 64 quadrant as 4 x 4 tiles of v_mfma_f32_16x16x32_f16.
 //   K advances one Q4_0 block (32 elements) per step.
 // * Per step the workgroup stages, in LDS, the activation slab a[128 x 32] as
-//   binary16 hi = f16(a) and lo = f16((a - hi) * 2^12), and the weight slab as
-//   the exact binary16 integers (q - 8) plus the same values times 2^-12, with
-//   the f32 scales d of the 128 weight rows. The 2^12 keeps the low term in the
-//   normal binary16 range for any |a| < 65504, and the matching 2^-12 on the
-//   weights ((q - 8) 2^-12 is exact) makes hi * (q - 8) + lo * (q - 8) 2^-12
-//   equal a (q - 8) to about 2^-22 relative, so both land in one MFMA chain.
+//   binary16 hi = f16(a) and lo = f16((a - hi) * 2^11), and the weight slab as
+//   the exact binary16 integers (q - 8) plus the same values times 2^-11, with
+//   the f32 scales d of the 128 weight rows. For a in [2^e, 2^(e+1)) the
+//   residual a - hi is at most 2^(e-11), so lo is at most 2^e <= |a|: no
+//   overflow for |a| < 65504, and lo stays a normal binary16 unless the
+//   residual is below 2^-25. The matching 2^-11 on the weights ((q - 8) 2^-11
+//   is exact) makes hi * (q - 8) + lo * (q - 8) 2^-11 equal a (q - 8) to about
+//   2^-22 relative (2^-36 absolute at worst), so both land in one MFMA chain.
 // * Every 16 x 16 tile's block partial is scaled by its column's d into an f32
 //   accumulator (d * C + acc): block partial -> scale -> sum of blocks.
 // * Two LDS stages with the next step's global loads issued before the current
@@ -53,7 +55,7 @@ __device__ __forceinline__ f16x8 decode_plain(uint32_t x)
 
 struct GemmStage {
     uint4 a[2][kEntries];   // [hi | lo][subtile][g][row] 8-half operands
-    uint4 b[2][kEntries];   // [(q-8) | (q-8) 2^-12][subtile][g][col]
+    uint4 b[2][kEntries];   // [(q-8) | (q-8) 2^-11][subtile][g][col]
     float d[kGemmBN];
 };
 
@@ -104,14 +106,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0(const float *__restr
             for (int c = 0; c < 4; ++c) {
                 const f16 x = (f16)e[c];
                 hi[c] = x;
-                lo[c] = (f16)((e[c] - (float)x) * 4096.0f);
+                lo[c] = (f16)((e[c] - (float)x) * 2048.0f);
             }
             const int idx = (sub * 4 + gg) * 16 + i;
             reinterpret_cast<uint2 *>(&s.a[0][idx])[h] = bitcast<uint2>(hi);
             reinterpret_cast<uint2 *>(&s.a[1][idx])[h] = bitcast<uint2>(lo);
         }
-        const f16x8 scale = {(f16)0x1p-12f, (f16)0x1p-12f, (f16)0x1p-12f, (f16)0x1p-12f,
-                             (f16)0x1p-12f, (f16)0x1p-12f, (f16)0x1p-12f, (f16)0x1p-12f};
+        const f16x8 scale = {(f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f,
+                             (f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f};
         const f16x8 b0 = decode_plain(wx0), b1 = decode_plain(wx1);
         const int idx0 = (sub * 4 + 2 * h) * 16 + i, idx1 = idx0 + 16;
         s.b[0][idx0] = bitcast<uint4>(b0);

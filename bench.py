@@ -1,27 +1,37 @@
 """Benchmark of the Q4_0 hot path on one MI355X.
 
-Headline (the JSON line's ``value``): the decode GEMV, y[1, 4096] = a[1, 4096] @
-dequant(W[4096, 4096])^T, as whole-job GB/s of algorithmic traffic (weight
-blocks + activations + output) over K timed launches with the weights read
-cold: each launch uses the next of R device copies of the weight blob, with R
-copies spanning more than twice the 256 MiB last-level cache. One step is one
-such GEMV. Inputs are resident in HBM before the timed region starts.
+Headline (the JSON line's ``value``): the decode GEMV y[1, 4096] =
+a[1, 4096] @ dequant(W[4096, 4096])^T, as whole-job GB/s of algorithmic
+traffic (weight blocks + activations + output) over K timed steps. One step is
+one GEMV. The weights are read cold: step k uses the (k mod R)-th of R device
+copies of the weight blob, and the R copies span more than twice the 256 MiB
+last-level cache. All inputs are resident in HBM before timing starts.
 
-Every other row of the path is measured too and reported under ``rows``: the
-8-row GEMV, the prefill GEMMs (1024 x 4096 x 4096 and 2048 x 14336 x 4096), the
-dequant of the 14336 x 4096 weight and the Q8_0 quantize of a 2048 x 4096
-tensor. Kernel durations come from HIP events recorded on the launch stream
-around each launch; the roofline fraction uses the kernel's algorithmic bytes
-or flops over that duration.
+Timing: the K launches of a timed region are captured once into a HIP graph
+(plain kernel nodes, no memset nodes) and replayed, so host submission cannot
+starve the GPU; the region is bracketed by HIP events recorded on the launch
+stream and by torch.cuda.synchronize() on both sides. A kernel's duration is
+the event-measured region divided by K (back-to-back launches, so it includes
+the inter-kernel gap and is never shorter than the kernel itself).
 
-The oracle (CPU, f64) is timed on this host's cores on a bounded sample of the
-decode GEMV and reported as ``cpu_baseline``; it is a reference point only.
+Every other row of the path is measured the same way and reported under
+``rows``: the 8-row GEMV, the prefill GEMMs (1024 x 4096 x 4096 and
+2048 x 14336 x 4096), a warm-cache GEMV, the dequant of the 14336 x 4096 weight
+and the Q8_0 quantize of a 2048 x 4096 tensor.
+
+``roofline.traffic`` comes from the committed counter summary
+profiles/traffic.json (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy of
+known size) and is null when the kernel source has changed since.
+
+The oracle (CPU, f64) is timed on this host's cores on repeated full decode
+GEMVs for a bounded time and reported as ``cpu_baseline``.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|headline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,9 +39,16 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6      # MI355X dense f16 MFMA (no sparsity)
 LLC_BYTES = 256 * 2 ** 20          # MI355X last-level (MALL) cache
+KERNEL_SOURCES = {
+    "gemv": "block_quantized_weight_dequant_amd/csrc/gemv.hip",
+    "gemm": "block_quantized_weight_dequant_amd/csrc/gemm.hip",
+    "dequant": "block_quantized_weight_dequant_amd/csrc/dequant.hip",
+    "quantize": "block_quantized_weight_dequant_amd/csrc/quantize.hip",
+}
 
 
 def parse_args():
@@ -42,6 +59,8 @@ def parse_args():
     p.add_argument("--rows", choices=["all", "headline"], default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a 256 MiB device copy (counter calibration)")
     return p.parse_args()
 
 
@@ -49,56 +68,71 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-# ----------------------------------------------------------------- helpers
+def source_sha256(kind):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
-class Timer:
-    """Per-launch HIP event pairs on the current stream."""
 
-    def __init__(self, torch, n):
-        self.torch = torch
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
+def load_traffic(workload, kernel, kind):
+    """Measured HBM bytes per launch (reads + writes) of `kernel` on `workload`,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["workloads"].get(workload)
+    except (OSError, ValueError, KeyError):
+        return None
+    if not rec or rec.get("kernel") != kernel or rec.get("source_sha256") != source_sha256(kind):
+        return None
+    return rec.get("bytes_per_launch")
 
-    def durations_ms(self):
-        return np.array([s.elapsed_time(e) for s, e in self.ev])
 
+# ----------------------------------------------------------------- timing
 
 def run_timed(torch, fn, steps, warmup, min_warm_s=0.3):
-    """Warm up (>= warmup launches and >= min_warm_s), then time `steps`
-    launches twice: once back to back (whole-job time), once with an event pair
-    around each launch (kernel durations)."""
-    t0 = time.perf_counter()
-    i = 0
-    while i < warmup or time.perf_counter() - t0 < min_warm_s:
-        fn(i)
-        i += 1
-        if i % 64 == 0:
-            torch.cuda.synchronize()
+    """Capture `steps` launches (fn(k), k = 0..steps-1) into one HIP graph, warm
+    up by replaying it (>= warmup launches and >= min_warm_s), then time one
+    replay with events on the current stream and the host clock."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(min(steps, 3)):
+            fn(k)                                    # eager warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(steps):
+            fn(k)
+    done, t0 = 0, time.perf_counter()
+    while done < warmup or time.perf_counter() - t0 < min_warm_s:
+        graph.replay()
+        done += steps
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record()
-    for k in range(steps):
-        fn(k)
+    graph.replay()
     end.record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - w0
     region_ms = start.elapsed_time(end)
-    timer = Timer(torch, steps)
-    for k in range(steps):
-        timer.ev[k][0].record()
-        fn(k)
-        timer.ev[k][1].record()
-    torch.cuda.synchronize()
-    d = timer.durations_ms()
-    return {"region_ms": region_ms, "wall_s": wall_s, "kernel_ms_mean": float(d.mean()),
-            "kernel_ms_median": float(np.median(d)), "kernel_ms_min": float(d.min()),
-            "kernel_ms_p90": float(np.percentile(d, 90))}
+    del graph
+    return {"region_ms": region_ms, "wall_s": wall_s, "kernel_us": region_ms * 1e3 / steps,
+            "steps": steps, "launch": "hip-graph replay of the timed launches"}
 
 
 def copies_for_cold(nbytes):
     return max(2, int(np.ceil(2.2 * LLC_BYTES / max(nbytes, 1))))
+
+
+def hbm_roofline(algo_bytes, kernel_us, workload, kernel, kind):
+    achieved = algo_bytes / (kernel_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(workload, kernel, kind),
+            "kernel": kernel}
 
 
 # ------------------------------------------------------------------- rows
@@ -112,6 +146,16 @@ def make_q4_weight(torch, q4, wl, N, K, seed):
     return blob
 
 
+def gemv_kernel_name(M, K):
+    if K % 256:
+        return "k_gemv_q4_0<%d>" % M
+    nblk = K // 32
+    per = (((nblk + 7) // 8) + 7) & ~7
+    last = nblk - (nblk - 1) // per * per
+    ch = 16 if (M <= 4 and per % 16 == 0 and last % 16 == 0) else 8
+    return "k_gemv_q4_0_stream<%d, 8, %d>" % (M, ch)
+
+
 def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     s = wl.WORKLOADS[name]
     M, N, K = s["M"], s["N"], s["K"]
@@ -121,28 +165,31 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
-    fn_entry = q4.q4_gemv if s["kind"] == "gemv" else q4.q4_gemm
-    fn = lambda i: fn_entry(a, blobs[i % R], y, M, N, K)
+    entry = q4.q4_gemv if s["kind"] == "gemv" else q4.q4_gemm
+    fn = lambda k: entry(a, blobs[k % R], y, M, N, K)
     t = run_timed(torch, fn, steps, warmup)
     algo_bytes = wbytes + M * K * 4 + M * N * 4
     flops = 2.0 * M * N * K
-    row = {"workload": name, "M": M, "N": N, "K": K, "kernel": "k_%s_q4_0" % s["kind"],
-           "weight_copies": R, "cache": "cold" if R > 1 else "warm",
-           "algorithmic_bytes": algo_bytes, "flops": flops, **t}
-    kern_s = t["kernel_ms_mean"] * 1e-3
-    row["kernel_GBs"] = algo_bytes / kern_s / 1e9
-    row["kernel_TFLOPs"] = flops / kern_s / 1e12
-    row["job_GBs"] = algo_bytes * steps / (t["region_ms"] * 1e-3) / 1e9
-    row["job_TFLOPs"] = flops * steps / (t["region_ms"] * 1e-3) / 1e12
+    kern_s = t["kernel_us"] * 1e-6
+    row = {"workload": name, "M": M, "N": N, "K": K, "weight_copies": R,
+           "cache": "cold" if R > 1 else "warm (one weight copy, MALL-resident)",
+           "algorithmic_bytes": algo_bytes, "flops": flops, **t,
+           "kernel_GBs": algo_bytes / kern_s / 1e9, "kernel_TFLOPs": flops / kern_s / 1e12,
+           "job_GBs": algo_bytes * steps / t["wall_s"] / 1e9,
+           "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
     if s["kind"] == "gemv":
-        row["roofline"] = {"bound": "hbm", "achieved": row["kernel_GBs"], "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": row["kernel_GBs"] / HBM_PEAK_GBS}
+        kernel = gemv_kernel_name(M, K)
+        row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
     else:
+        kernel = "k_gemm_q4_0"
         row["roofline"] = {"bound": "mfma", "achieved": row["kernel_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": row["kernel_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
-                           "note": "f16 MFMA dense peak; the two-term activation split "
-                                   "issues 2 MFMA flops per useful flop"}
+                           "traffic": load_traffic(name, kernel, "gemm"), "kernel": kernel,
+                           "note": "useful 2MNK flops over the dense f16 MFMA peak; the "
+                                   "two-term activation split issues 2 MFMA flops per "
+                                   "useful flop, so 0.5 is this design's ceiling"}
+    row["kernel"] = kernel
     del blobs, blob, a, y
     torch.cuda.empty_cache()
     return row
@@ -153,15 +200,15 @@ def bench_dequant(torch, q4, wl, steps, warmup):
     N, K = s["N"], s["K"]
     blob = make_q4_weight(torch, q4, wl, N, K, s["w_seed"])
     outs = [torch.empty(N * K, dtype=torch.float32, device="cuda") for _ in range(2)]
-    fn = lambda i: q4.q4_dequant(blob, outs[i % 2])
+    fn = lambda k: q4.q4_dequant(blob, outs[k % 2])
     t = run_timed(torch, fn, steps, warmup)
     algo = blob.numel() + N * K * 4
-    kern_s = t["kernel_ms_mean"] * 1e-3
-    row = {"workload": "dequant_14336x4096", "kernel": "k_dequant_q4_0", "cache": "cold",
-           "algorithmic_bytes": algo, **t, "kernel_GBs": algo / kern_s / 1e9,
-           "job_GBs": algo * steps / (t["region_ms"] * 1e-3) / 1e9}
-    row["roofline"] = {"bound": "hbm", "achieved": row["kernel_GBs"], "peak": HBM_PEAK_GBS,
-                       "unit": "GB/s", "frac": row["kernel_GBs"] / HBM_PEAK_GBS}
+    kern_s = t["kernel_us"] * 1e-6
+    row = {"workload": "dequant_14336x4096", "kernel": "k_dequant_q4_0",
+           "cache": "cold (268 MB per call)", "algorithmic_bytes": algo, **t,
+           "kernel_GBs": algo / kern_s / 1e9, "job_GBs": algo * steps / t["wall_s"] / 1e9}
+    row["roofline"] = hbm_roofline(algo, t["kernel_us"], "dequant_14336x4096", "k_dequant_q4_0",
+                                   "dequant")
     del blob, outs
     torch.cuda.empty_cache()
     return row
@@ -174,18 +221,30 @@ def bench_quantize(torch, q4, wl, steps, warmup):
     R = copies_for_cold(n * 4)
     xs = [x] + [x.clone() for _ in range(R - 1)]
     out = torch.empty(n // 32 * 34, dtype=torch.uint8, device="cuda")
-    fn = lambda i: q4.q8_quantize(xs[i % R], out)
+    fn = lambda k: q4.q8_quantize(xs[k % R], out)
     t = run_timed(torch, fn, steps, warmup)
     algo = n * 4 + n // 32 * 34
-    kern_s = t["kernel_ms_mean"] * 1e-3
+    kern_s = t["kernel_us"] * 1e-6
     row = {"workload": "quantize_2048x4096", "kernel": "k_quantize_q8_0", "input_copies": R,
            "cache": "cold", "algorithmic_bytes": algo, **t, "kernel_GBs": algo / kern_s / 1e9,
-           "job_GBs": algo * steps / (t["region_ms"] * 1e-3) / 1e9}
-    row["roofline"] = {"bound": "hbm", "achieved": row["kernel_GBs"], "peak": HBM_PEAK_GBS,
-                       "unit": "GB/s", "frac": row["kernel_GBs"] / HBM_PEAK_GBS}
+           "job_GBs": algo * steps / t["wall_s"] / 1e9}
+    row["roofline"] = hbm_roofline(algo, t["kernel_us"], "quantize_2048x4096", "k_quantize_q8_0",
+                                   "quantize")
     del xs, x, out
     torch.cuda.empty_cache()
     return row
+
+
+def copy_calibration(torch):
+    """One 256 MiB device-to-device copy (read 256 MiB, write 256 MiB), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 64 * 2 ** 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_each_way": n * 4, "launches": 3}
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -217,7 +276,8 @@ def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(see the sharding design); run with --gpus 1", file=sys.stderr)
+              "(the sharding design is written up, not built); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -247,35 +307,36 @@ def main():
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10)))
         log("row: Q8_0 quantize 2048x4096")
         rows.append(bench_quantize(torch, q4, wl, args.steps, args.warmup))
+    calib = copy_calibration(torch) if args.calibrate_copy else None
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")
         cpu = cpu_baseline(wl, args.cpu_seconds)
 
-    value = head["job_GBs"]
     line = {
         "metric": "Q4_0 GEMV GB/s (M=1, 4096²) + prefill GEMM TFLOP/s, % of roofline",
-        "value": round(value, 2),
+        "value": round(head["job_GBs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["region_ms"] / args.steps,
+        "ms_per_step": head["wall_s"] * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32 in/out; f16x2-split MFMA, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "gemv_1x4096x4096", "M": 1, "N": 4096, "K": 4096,
-                   "cache": head["cache"], "weight_copies": head["weight_copies"]},
-        "roofline": {**head["roofline"], "traffic": None,
-                     "kernel": head["kernel"], "kernel_us_mean": head["kernel_ms_mean"] * 1e3,
-                     "kernel_us_median": head["kernel_ms_median"] * 1e3},
+                   "cache": head["cache"], "weight_copies": head["weight_copies"],
+                   "launch": head["launch"]},
+        "roofline": {**head["roofline"], "kernel_us": head["kernel_us"]},
         "cpu_baseline": cpu,
         "rows": rows,
         "device": props.name,
     }
+    if calib:
+        line["copy_calibration"] = calib
     print(json.dumps(line), flush=True)
 
 

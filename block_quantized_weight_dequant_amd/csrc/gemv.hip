@@ -35,6 +35,9 @@
 //   max |a| so that 16 max|a| 2^p_m lies in [2^14, 2^15): no binary16
 //   overflow, and elements far below the row maximum lose at most 2^-25 of
 //   2^p_m absolutely. The scale is undone exactly on the f32 result.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -249,6 +252,7 @@ struct GemvStreamCfg {
     static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
     static constexpr int CPR = CH * 18 / 16;              // 16-byte columns per staged row
     static constexpr int NLOAD = (CPR + 3) / 4;           // 16-byte loads per lane per chunk
+    static constexpr int NFULL = CPR / 4;                 // ... that no lane clamps
     static constexpr int RS = CH * 18 + 16;               // LDS bytes per staged row
     static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
     static constexpr int NI = 2 * M;                      // A rows in use
@@ -256,8 +260,23 @@ struct GemvStreamCfg {
     static constexpr int NENT = CH * 4 * M;               // 8-element activation groups per chunk
     static constexpr int EPL = (NENT + 63) / 64;          // ... per lane
     static constexpr int LDS_PER_WAVE = WBYTES + ABYTES;
+    static constexpr int NPART = CH == 16 ? 4 : 2;        // parts a chunk is contracted in
+    // Loads (per lane) that hold every byte of the chunk's first b blocks.
+    static constexpr int loads_for(int b) { return b == 0 ? 0 : ((18 * b - 1) / 16) / 4 + 1; }
     static_assert(CH == 8 || CH == 16, "chunks are 8 or 16 blocks");
 };
+
+// Calls f(integral_constant<int, P>) for P = 0 .. NP-1, in order.
+template <int NP, class F, int... P>
+__device__ __forceinline__ void for_each_part_impl(F &&f, std::integer_sequence<int, P...>)
+{
+    (f(std::integral_constant<int, P>{}), ...);
+}
+template <int NP, class F>
+__device__ __forceinline__ void for_each_part(F &&f)
+{
+    for_each_part_impl<NP>(f, std::make_integer_sequence<int, NP>{});
+}
 
 // Maximum of a non-negative float over the wavefront, returned to every lane.
 // Non-negative IEEE floats order like their bit patterns, so the reduction
@@ -324,6 +343,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     // Loader role: row lr = lane % 16, 16-byte columns lc0 + 4 i.
     const int lr = lane & 15, lc0 = lane >> 4;
     const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
+    // Offset of the last (clamped) 16-byte column from column lc0.
+    const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
 
     u32x4 wreg[C::NLOAD];
     float4 areg[C::EPL][2];
@@ -331,36 +352,48 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     // elements 4gg..4gg+3 and 16+4gg..16+4gg+3. Activations are requested first
     // (vmcnt drains in issue order), so their split overlaps the weight loads.
     const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a);
+    // Every lane issues every load (surplus lanes re-read an in-bounds group or
+    // column that is then ignored), so the compiler's in-order wait counts are
+    // exact and the first half of a chunk waits only for its own loads.
     auto fetch = [&](int cb0) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < C::EPL; ++r) {
-            const int e = lane + 64 * r;
+            const int e = min(lane + 64 * r, C::NENT - 1);
             const int m = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
-            if (e < C::NENT) {
-                const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + 4 * gg) * 4u;
-                areg[r][0] = *reinterpret_cast<const float4 *>(a8 + off);
-                areg[r][1] = *reinterpret_cast<const float4 *>(a8 + off + 64u);
-            }
+            const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + 4 * gg) * 4u;
+            areg[r][0] = *reinterpret_cast<const float4 *>(a8 + off);
+            areg[r][1] = *reinterpret_cast<const float4 *>(a8 + off + 64u);
         }
-        const uint32_t base = lrow_off + (uint32_t)cb0 * kQ4Bytes;
+        // Columns lc0 + 4 i are in the row for i < NFULL on every lane: one
+        // address with immediate offsets. The last load clamps its column.
+        // The scheduling barriers keep the loads in column order.
+        const uint32_t woff = lrow_off + (uint32_t)cb0 * kQ4Bytes + 16u * lc0;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < C::NLOAD; ++i) {
-            const int col = lc0 + 4 * i;
-            if (col < C::CPR)
-                wreg[i] = *reinterpret_cast<const u32x4 *>(w + (base + 16u * col));
+        for (int i = 0; i < C::NFULL; ++i) {
+            wreg[i] = *reinterpret_cast<const u32x4 *>(w + (woff + 64u * i));
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (C::NFULL < C::NLOAD)
+            wreg[C::NFULL] = *reinterpret_cast<const u32x4 *>(w + (woff + last_off));
+        // Issue point: the weight pointer escapes into an empty asm statement
+        // with a memory clobber, so no pass sinks the loads below this line,
+        // and the scheduling barrier keeps later work (which waits on loads)
+        // from being hoisted above them.
+        asm volatile("" ::"s"(w) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (wb0 < wb1)
-        fetch(wb0);
+    // Unconditional, so no copies of the loaded registers are needed after a
+    // branch (they would wait for the loads). A wavefront without blocks
+    // (possible only when the workgroup's share is short) fetches the last full
+    // chunk of the row, K/32 >= CH, and never reads it.
+    fetch(min(wb0, nblk - C::CH));
 
-    // A operands of a chunk live in registers. Lanes j >= NI (A rows no
-    // activation row uses) keep the zeros set here: each chunk refreshes only
-    // lanes j < NI, with reads masked to those lanes.
+    // A operands of a chunk live in registers (set by split_activations).
     f16x8 aop[C::CH];
-#pragma unroll
-    for (int b = 0; b < C::CH; ++b)
-        aop[b] = (f16x8){};
+    // Clamped, so the address stays inside the A area even where the read is
+    // masked off.
     const uint8_t *a_lane = s_a + (g * C::NI + min(j, C::NI - 1)) * 16;
     // The exponent pattern of 1024.0 in both halves, as a value the compiler
     // cannot fold back into a literal (one v_mov at kernel start; no MFMA is in
@@ -373,10 +406,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     for (int h = 0; h < NACC / 2; ++h)
         ysum[h] = 0.0f;
 
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    for (int cb0 = wb0; cb0 < wb1; cb0 += C::CH) {
-
-        // Per-row scale from this chunk's max |a|, then the split A operands.
+    // Activation split of the chunk whose loads are in areg: per-row scale
+    // from the chunk's own max |a|, then the two-term A operands into s_a.
+    // It runs as soon as those loads land, never across a loop back edge, so
+    // no copy of the loaded registers is kept alive while the weight loads are
+    // being issued.
+    int pexp[M];
+    auto split_activations = [&]() __attribute__((always_inline)) {
         float mx[M];
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -395,7 +431,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
                         mx[m] = fmaxf(mx[m], v);
             }
         }
-        int pexp[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float am = wave_max_nonneg(mx[m]);
@@ -431,67 +466,109 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
                 dst[1] = bitcast<u32x4>(lo);
             }
         }
-        // Stage this chunk's weight bytes.
-#pragma unroll
-        for (int i = 0; i < C::NLOAD; ++i) {
-            const int col = lc0 + 4 * i;
-            if (col < C::CPR)
-                *reinterpret_cast<u32x4 *>(s_w + lr * C::RS + 16 * col) = wreg[i];
-        }
-        // Prefetch the next chunk while this one is computed.
-        if (cb0 + C::CH < wb1)
-            fetch(cb0 + C::CH);
+        // A operands into registers now, while the weight bytes are still in
+        // flight. Only lanes j < NI read: the other A rows belong to no
+        // activation row and only fill MFMA output rows that are never read.
         wave_lds_sync();
         if (j < C::NI) {
 #pragma unroll
             for (int b = 0; b < C::CH; ++b)
                 aop[b] = *reinterpret_cast<const f16x8 *>(a_lane + b * ASTRIDE);
         }
+    };
 
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    split_activations();
+    for (int cb0 = wb0; cb0 < wb1; cb0 += C::CH) {
+        // The chunk is contracted in NPART parts. Part p needs only loads
+        // [0, loads_for(end of p)) of every lane, which drain first (vmcnt
+        // counts in issue order), so its decode and MFMAs run while the rest of
+        // the chunk is still arriving.
+        auto stage = [&](auto i0_c, auto i1_c) __attribute__((always_inline)) {
+            constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
+#pragma unroll
+            for (int i = I0; i < I1; ++i) {
+                const int col = lc0 + 4 * i;
+                if (col < C::CPR)
+                    *reinterpret_cast<u32x4 *>(s_w + lr * C::RS + 16 * col) = wreg[i];
+            }
+        };
         float acc[NACC];
 #pragma unroll
         for (int r = 0; r < NACC; ++r)
             acc[r] = 0.0f;
         // qs dword g of block b starts at byte 18 b + 2 + 4 g of the staged row:
-        // 2 bytes past a dword boundary for even b, on one for odd b. Blocks go
-        // in groups of four independent MFMAs, then their scale FMAs, so the
-        // matrix-core latency overlaps the next group's decode.
+        // 2 bytes past a dword boundary for even b, on one for odd b. All MFMAs
+        // of a part are issued before its scale FMAs, so the matrix-core latency
+        // overlaps the decode of the following blocks.
         const uint8_t *wl = s_w + j * C::RS;
         const uint32_t *wq = reinterpret_cast<const uint32_t *>(wl + 4 * g);
+        auto contract = [&](auto b0_c, auto b1_c) __attribute__((always_inline)) {
+            constexpr int B0 = decltype(b0_c)::value, B1 = decltype(b1_c)::value;
+            f32x4 Cv[B1 - B0];
+            float d[B1 - B0];
 #pragma unroll
-        for (int b4 = 0; b4 < C::CH; b4 += 4) {
-            f32x4 Cv[4];
-            float d[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int b = b4 + u;
+            for (int b = B0; b < B1; ++b) {
                 uint32_t x;
                 if (b % 2 == 0)
                     x = __builtin_amdgcn_alignbyte(wq[(18 * b) / 4 + 1], wq[(18 * b) / 4], 2u);
                 else
                     x = wq[(18 * b + 2) / 4];
-                d[u] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * kQ4Bytes));
-                Cv[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[b], decode_x16_fast(x, magic_v),
-                                                                zero4, 0, 0, 0);
+                d[b - B0] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * kQ4Bytes));
+                Cv[b - B0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[b], decode_x16_fast(x, magic_v),
+                                                                     zero4, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < B1 - B0; ++u)
 #pragma unroll
                 for (int r = 0; r < NACC; ++r)
                     acc[r] = fmaf(d[u], Cv[u][r], acc[r]);
-        }
+            // Keep every MFMA result register allocated up to here: rows this
+            // lane does not accumulate would otherwise be handed to the next
+            // decode while the MFMA is still writing them (a stall on each).
+#pragma unroll
+            for (int u = 0; u < B1 - B0; ++u)
+                asm volatile("" ::"v"(Cv[u]));
+        };
         // Undo this chunk's scale (and the factor 16) on its partial.
+        auto finish_chunk = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < NACC / 2; ++h) {
-            const int m = 2 * g + h;
-            int pm = 0;
+            for (int h = 0; h < NACC / 2; ++h) {
+                const int m = 2 * g + h;
+                int pm = 0;
 #pragma unroll
-            for (int mm = 0; mm < M; ++mm)
-                if (mm == m)
-                    pm = pexp[mm];
-            ysum[h] += ldexpf(acc[2 * h] + acc[2 * h + 1], -pm - 4);
-        }
-        wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
+                for (int mm = 0; mm < M; ++mm)
+                    if (mm == m)
+                        pm = pexp[mm];
+                ysum[h] += ldexpf(acc[2 * h] + acc[2 * h + 1], -pm - 4);
+            }
+        };
+        for_each_part<C::NPART>([&](auto p_c) __attribute__((always_inline)) {
+            constexpr int P = decltype(p_c)::value;
+            constexpr int B0 = P * C::CH / C::NPART, B1 = (P + 1) * C::CH / C::NPART;
+            constexpr int L0 = C::loads_for(B0), L1 = C::loads_for(B1);
+            stage(std::integral_constant<int, L0>{}, std::integral_constant<int, L1>{});
+            auto run_part = [&]() __attribute__((always_inline)) {
+                wave_lds_sync();
+                contract(std::integral_constant<int, B0>{}, std::integral_constant<int, B1>{});
+            };
+            if constexpr (P < C::NPART - 1) {
+                run_part();
+            } else if (cb0 + C::CH < wb1) {
+                // Every load of this chunk is staged: prefetch the next chunk,
+                // finish this one, then split the next chunk's activations. The
+                // fetch and the split sit in one branch, so the loaded
+                // activation registers never meet a join.
+                fetch(cb0 + C::CH);
+                run_part();
+                finish_chunk();
+                wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
+                split_activations();
+            } else {
+                run_part();
+                finish_chunk();
+            }
+        });
     }
 
 #pragma unroll

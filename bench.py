@@ -156,6 +156,10 @@ def gemv_kernel_name(M, K):
     return "k_gemv_q4_0_stream<%d, 8, %d>" % (M, ch)
 
 
+def gemm_kernel_name(K):
+    return "k_gemm_q4_0_split" if K % 64 == 0 else "k_gemm_q4_0_any"
+
+
 def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     s = wl.WORKLOADS[name]
     M, N, K = s["M"], s["N"], s["K"]
@@ -165,8 +169,12 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
-    entry = q4.q4_gemv if s["kind"] == "gemv" else q4.q4_gemm
-    fn = lambda k: entry(a, blobs[k % R], y, M, N, K)
+    if s["kind"] == "gemv":
+        fn = lambda k: q4.q4_gemv(a, blobs[k % R], y, M, N, K)
+    else:
+        ws_bytes = q4.q4_gemm_workspace_bytes(M, N, K)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        fn = lambda k: q4.q4_gemm(a, blobs[k % R], y, M, N, K, workspace=ws)
     t = run_timed(torch, fn, steps, warmup)
     algo_bytes = wbytes + M * K * 4 + M * N * 4
     flops = 2.0 * M * N * K
@@ -181,14 +189,16 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
         kernel = gemv_kernel_name(M, K)
         row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
     else:
-        kernel = "k_gemm_q4_0"
+        kernel = gemm_kernel_name(K)
         row["roofline"] = {"bound": "mfma", "achieved": row["kernel_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": row["kernel_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
                            "traffic": load_traffic(name, kernel, "gemm"), "kernel": kernel,
                            "note": "useful 2MNK flops over the dense f16 MFMA peak; the "
                                    "two-term activation split issues 2 MFMA flops per "
-                                   "useful flop, so 0.5 is this design's ceiling"}
+                                   "useful flop, so 0.5 is this design's ceiling; the "
+                                   "time is the whole step (activation split kernel plus "
+                                   "the GEMM kernel)"}
     row["kernel"] = kernel
     del blobs, blob, a, y
     torch.cuda.empty_cache()

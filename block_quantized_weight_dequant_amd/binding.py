@@ -24,11 +24,13 @@ Q4_ERR_SIZE = 3
 Q4_ERR_ALIGN = 4
 Q4_ERR_ALIAS = 5
 Q4_ERR_LAUNCH = 6
+Q4_ERR_WORKSPACE = 7
 Q4_GEMV_MAX_ROWS = 8
+SIZE_MAX = 2 ** 64 - 1
 
 #: Every symbol include/q4.h declares.
 EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
-           "q8_quantize", "q4_quantize")
+           "q4_gemm_workspace_bytes", "q8_quantize", "q4_quantize")
 
 
 class Q4Error(RuntimeError):
@@ -55,9 +57,12 @@ def _load_library():
     lib.q4_status_string.argtypes = [i32]
     lib.q4_dequant.restype = i32
     lib.q4_dequant.argtypes = [P, sz, P, sz, P]
-    for name in ("q4_gemv", "q4_gemm"):
-        getattr(lib, name).restype = i32
-        getattr(lib, name).argtypes = [P, P, sz, P, i32, i32, i32, P]
+    lib.q4_gemv.restype = i32
+    lib.q4_gemv.argtypes = [P, P, sz, P, i32, i32, i32, P]
+    lib.q4_gemm.restype = i32
+    lib.q4_gemm.argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
+    lib.q4_gemm_workspace_bytes.restype = sz
+    lib.q4_gemm_workspace_bytes.argtypes = [i32, i32, i32]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -117,10 +122,42 @@ def q4_gemv(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> Non
                        _stream(stream)), "q4_gemv")
 
 
-def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
-    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M."""
+def q4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q4_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def _scratch(nbytes: int, stream, like):
+    """A uint8 device tensor of nbytes from PyTorch's caching allocator, marked
+    as in use by ``stream`` so that it is not handed out again before the work
+    queued there has finished."""
+    import torch
+    dev = like.device if hasattr(like, "device") else torch.device("cuda", torch.cuda.current_device())
+    t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if isinstance(stream, torch.cuda.Stream):
+        t.record_stream(stream)
+    elif isinstance(stream, int) and stream != 0:
+        t.record_stream(torch.cuda.ExternalStream(stream, device=dev))
+    return t
+
+
+def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+            workspace_bytes=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M.
+
+    ``workspace=None`` takes a scratch tensor of q4_gemm_workspace_bytes(M, N, K)
+    bytes from PyTorch's caching allocator for this call; pass a tensor (or an
+    address with ``workspace_bytes``) to reuse one."""
     wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
-    _check(lib.q4_gemm(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+    ws = workspace
+    if ws is None:
+        need = q4_gemm_workspace_bytes(M, N, K)
+        if 0 < need < SIZE_MAX:
+            ws = _scratch(need, stream, y)
+    if workspace_bytes is not None:
+        wsb = int(workspace_bytes)
+    else:
+        wsb = _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0
+    _check(lib.q4_gemm(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K), _addr(ws), wsb,
                        _stream(stream)), "q4_gemm")
 
 

@@ -29,6 +29,7 @@ Q4_EXPORT const char *q4_status_string(int status)
     case Q4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case Q4_ERR_ALIAS: return "an output overlaps an input";
     case Q4_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case Q4_ERR_WORKSPACE: return "the workspace is smaller than q4_gemm_workspace_bytes";
     default: return "unknown status";
     }
 }
@@ -54,14 +55,23 @@ Q4_EXPORT int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
                                      as_stream(stream)));
 }
 
+Q4_EXPORT size_t q4_gemm_workspace_bytes(int M, int N, int K)
+{
+    return q4v::gemm_workspace_bytes(M, N, K);
+}
+
 Q4_EXPORT int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
-                      void *stream)
+                      void *workspace, size_t workspace_bytes, void *stream)
 {
     bool empty = false;
     int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, 0, &empty);
     if (st != Q4_OK || empty)
         return st;
+    st = q4v::check_workspace(a, w_q, w_bytes, y, M, N, K, workspace, workspace_bytes);
+    if (st != Q4_OK)
+        return st;
     return launched(q4k::launch_gemm(a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                     q4v::gemm_splits_activations(K) ? workspace : nullptr,
                                      as_stream(stream)));
 }
 

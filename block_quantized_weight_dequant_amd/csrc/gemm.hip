@@ -29,6 +29,7 @@
 //   same activation rows, which then stay in that XCD's L2.
 #include "device_common.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace q4k {
 
@@ -39,12 +40,14 @@ constexpr int kEntries = 8 * 4 * 16;   // 16-row subtiles x k-groups x rows: 512
 
 // B operand for qs dword x (bytes 4g..4g+3 of a block): slots hold (q - 8) of
 // elements 4g+0, 4g+2, 4g+1, 4g+3, 16+4g+0, 16+4g+2, 16+4g+1, 16+4g+3.
-__device__ __forceinline__ f16x8 decode_plain(uint32_t x)
+// magic is the exponent pattern of 1024.0 in both halves (0x64006400); kept in
+// a VGPR, each (field & mask) | magic is one v_and_or_b32.
+__device__ __forceinline__ f16x8 decode_plain(uint32_t x, uint32_t magic = 0x64006400u)
 {
-    const uint32_t v0 = (x & 0x000F000Fu) | 0x64006400u;
-    const uint32_t v1 = ((x >> 8) & 0x000F000Fu) | 0x64006400u;
-    const uint32_t v2 = ((x >> 4) & 0x000F000Fu) | 0x64006400u;
-    const uint32_t v3 = ((x >> 12) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t v0 = (x & 0x000F000Fu) | magic;
+    const uint32_t v1 = ((x >> 8) & 0x000F000Fu) | magic;
+    const uint32_t v2 = ((x >> 4) & 0x000F000Fu) | magic;
+    const uint32_t v3 = ((x >> 12) & 0x000F000Fu) | magic;
     const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
     f16x2 h0 = bitcast<f16x2>(v0) - bias;
     f16x2 h1 = bitcast<f16x2>(v1) - bias;
@@ -59,10 +62,10 @@ struct GemmStage {
     float d[kGemmBN];
 };
 
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0(const float *__restrict__ a,
-                                                           const uint8_t *__restrict__ w,
-                                                           float *__restrict__ y, int M, int N,
-                                                           int K, int tiles_m, int tiles_n)
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0_any(const float *__restrict__ a,
+                                                               const uint8_t *__restrict__ w,
+                                                               float *__restrict__ y, int M, int N,
+                                                               int K, int tiles_m, int tiles_n)
 {
     __shared__ GemmStage st[2];
 
@@ -191,15 +194,304 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0(const float *__restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// Split-activation path, for K % 64 == 0 (every weight row then starts on a
+// 4-byte boundary and K splits into pairs of blocks).
+//
+// * k_gemm_split_a writes the activations once, already split (hi = f16(a),
+//   lo = f16((a - hi) 2^11)) and laid out as the matrix cores' A operands:
+//   16-byte operand [mt][kb][hl][sub][lane] holds, for row 128 mt + 16 sub +
+//   lane % 16 and block kb, the slots of k-group g = lane / 16 (elements 4g,
+//   4g+2, 4g+1, 4g+3, 16+4g, 16+4g+2, 16+4g+1, 16+4g+3), hi for hl = 0 and
+//   lo for hl = 1. Rows past M are zero. The split then costs one pass over
+//   the activations instead of one per column tile, and a workgroup's
+//   activation slab for a pair of blocks is 32 contiguous KB.
+// * k_gemm_q4_0_split: a 512-thread workgroup computes a 128 x 128 tile. Its
+//   eight wavefronts are two K groups of four: group kg takes the even (kg =
+//   0) or odd (kg = 1) block of each pair, and wavefront (wm, wn) of a group
+//   owns a 64 x 64 quadrant as 4 x 4 MFMA tiles. Two wavefronts per SIMD
+//   hide each other's VALU work and latencies; the two groups' partial tiles
+//   are added once, through LDS, at the end.
+// * Per pair of blocks the workgroup stages the 32 KB activation slab and the
+//   36 raw weight bytes of each of its 128 rows in LDS (double-buffered, one
+//   barrier per pair). Each wavefront decodes its own B operands from the raw
+//   bytes: the qs dword g of the block for column lane % 16, realigned with
+//   v_alignbyte where it straddles a dword, becomes (q - 8) and (q - 8) 2^-11
+//   as binary16, and d stays binary16 until the scale FMA.
+// * Accumulation as in the general kernel: two chained MFMAs per 16 x 16 tile
+//   and block (hi x (q - 8), lo x (q - 8) 2^-11), then d * C + acc in f32.
+
+constexpr int kSplitWaves = 4;
+constexpr int kOpsPerBlockTile = 2 * 8 * 64;   // 16-byte A operands per (128-row tile, block)
+
+__global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *__restrict__ a,
+                                                                 u32x4 *__restrict__ ahl, int M,
+                                                                 int K, long long n_waves)
+{
+    const int lane = threadIdx.x & 63;
+    const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
+    if (gw >= n_waves)   // whole wavefronts only
+        return;
+    const int nblk = K >> 5;
+    const long long R = gw / nblk;                // 16-row group
+    const int kb = (int)(gw - R * nblk);
+    const int li = lane & 15, g = lane >> 4;
+    const long long m = R * 16 + li;
+    f16x8 hi = {}, lo = {};
+    if (m < M) {
+        const float *src = a + m * K + (long long)kb * 32 + 4 * g;
+        const float4 L = *reinterpret_cast<const float4 *>(src);
+        const float4 H = *reinterpret_cast<const float4 *>(src + 16);
+        const float e[8] = {L.x, L.z, L.y, L.w, H.x, H.z, H.y, H.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const f16 h = (f16)e[s];
+            hi[s] = h;
+            lo[s] = (f16)((e[s] - (float)h) * 2048.0f);
+        }
+    }
+    const long long mt = R >> 3;
+    const long long idx = (mt * nblk + kb) * kOpsPerBlockTile + (R & 7) * 64 + lane;
+    ahl[idx] = bitcast<u32x4>(hi);
+    ahl[idx + 8 * 64] = bitcast<u32x4>(lo);
+}
+
+constexpr int kSplitGemmThreads = 512;
+constexpr int kBRowDwords = 10;   // LDS dwords per weight row and pair: 9 (36 bytes) + 1 pad
+
+struct SplitStage {
+    u32x4 a[2 * kOpsPerBlockTile];      // [kg][hl][sub][lane]
+    uint32_t b[kGemmBN * kBRowDwords];  // [row][dword]: blocks 2s and 2s+1 of the row
+};
+
+__global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
+    const u32x4 *__restrict__ ahl, const uint8_t *__restrict__ w, float *__restrict__ y, int M,
+    int N, int K, int tiles_m, int tiles_n)
+{
+    __shared__ SplitStage st[2];
+
+    const int T = tiles_m * tiles_n, L = blockIdx.x;
+    const int t = (T % 8 == 0) ? (L % 8) * (T / 8) + L / 8 : L;
+    const int mt = t / tiles_n, m0 = mt * kGemmBM, n0 = (t % tiles_n) * kGemmBN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The wavefront index, made visibly uniform so that branches on kg are scalar.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+    const int li = lane & 15, g = lane >> 4;
+    const int nblk = K >> 5, npairs = nblk >> 1;
+    // 0x64006400 as a value the compiler cannot fold back into a literal.
+    uint32_t magic_v;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic_v));
+    const size_t row_bytes = (size_t)nblk * kQ4Bytes;
+
+    // Staging roles. A: operands tid + 512 q of the pair's 32 KB slab, which
+    // has the LDS layout already. B: dword i = tid + 512 r (i < 128 * 9) is
+    // dword i % 9 of the pair's 36 bytes of row i / 9.
+    const u32x4 *asrc = ahl + (size_t)mt * nblk * kOpsPerBlockTile + tid;
+    constexpr int kBDwords = kGemmBN * 9;
+    const uint32_t *bsrc[3];
+    int bdst[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const int i = min(tid + 512 * r, kBDwords - 1), row = i / 9, dw = i % 9;
+        bsrc[r] = reinterpret_cast<const uint32_t *>(w + (size_t)min(n0 + row, N - 1) * row_bytes) + dw;
+        bdst[r] = row * kBRowDwords + dw;
+    }
+    const bool b2 = tid + 1024 < kBDwords;   // the third B dword exists for this thread
+
+    // Staged pairs travel through registers: the loads of pair p + 2 are
+    // issued before pair p is computed and written to LDS after pair p + 1 is,
+    // so each load has two pairs' worth of compute to arrive in. The loop is
+    // unrolled by two so that the two register sets have fixed names.
+    struct PairRegs {
+        u32x4 a[4];
+        uint32_t b[3];
+    };
+    auto load_pair = [&](PairRegs &R, int p) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            R.a[q] = asrc[(size_t)p * 2 * kOpsPerBlockTile + 512 * q];
+        R.b[0] = bsrc[0][9 * p];
+        R.b[1] = bsrc[1][9 * p];
+        if (b2)
+            R.b[2] = bsrc[2][9 * p];
+    };
+    auto store_pair = [&](const PairRegs &R, SplitStage &S) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            S.a[tid + 512 * q] = R.a[q];
+        S.b[bdst[0]] = R.b[0];
+        S.b[bdst[1]] = R.b[1];
+        if (b2)
+            S.b[bdst[2]] = R.b[2];
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+            acc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const f16 sc = (f16)0x1p-11f;
+    const f16x8 scale = {sc, sc, sc, sc, sc, sc, sc, sc};
+    // B of column group ns, block 2p + kg: qs dword g of the block for column
+    // wn*64 + ns*16 + li starts at byte 18 kg + 2 + 4 g of the staged row, which
+    // is dword g + 5 kg shifted by 2 (1 - kg) bytes; d is the 16-bit half kg of
+    // dword 4 kg. Branch-free, so a pair's compute is one scheduling region.
+    const int bi0 = g + 5 * kg, bsh = 2 * (1 - kg), bdi = 4 * kg, bds = 16 * kg;
+    struct BCol {
+        uint32_t lo, hi, dw;
+    };
+    auto read_b = [&](const SplitStage &cur, int ns) __attribute__((always_inline)) {
+        const uint32_t *rb = cur.b + (wn * 64 + ns * 16 + li) * kBRowDwords;
+        return BCol{rb[bi0], rb[bi0 + 1], rb[bdi]};
+    };
+    // Software pipeline over the four column groups of a pair: the MFMAs of
+    // group ns are issued between the scale FMAs of group ns - 1 (whose results
+    // are ready) and the decode of group ns + 1. Group results alternate
+    // between two register sets by the parity of ns, and the group before
+    // group 0 is group 3 of the previous pair (zeros before the first pair),
+    // so every index is a compile-time constant. The scheduling-group barriers
+    // ask for one MFMA then three VALU instructions, eight times per group.
+    f32x4 cbuf[2][4];
+    float dbuf[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+            cbuf[h][ms] = zero4;
+    auto compute_pair = [&](const SplitStage &cur) __attribute__((always_inline)) {
+        f16x8 ahi[4], alo[4];
+        const u32x4 *ap = cur.a + kg * kOpsPerBlockTile + wm * 4 * 64 + lane;
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+            ahi[ms] = bitcast<f16x8>(ap[ms * 64]);
+            alo[ms] = bitcast<f16x8>(ap[8 * 64 + ms * 64]);
+        }
+        BCol bc = read_b(cur, 0);
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+            const uint32_t x = __builtin_amdgcn_alignbyte(bc.hi, bc.lo, (uint32_t)bsh);
+            const float d = f16_bits_to_f32((bc.dw >> bds) & 0xFFFFu);
+            if (ns + 1 < 4)
+                bc = read_b(cur, ns + 1);
+            const f16x8 bq = decode_plain(x, magic_v), bs = bq * scale;
+            f32x4 *c = cbuf[ns & 1];
+            const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
+            const float dp = dbuf[(ns + 1) & 1];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[ms][(ns + 3) & 3][q] = fmaf(dp, cp[ms][q], acc[ms][(ns + 3) & 3][q]);
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bq, zero4, 0, 0, 0);
+                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bs, c[ms], 0, 0, 0);
+            }
+            dbuf[ns & 1] = d;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+            }
+        }
+    };
+    // FMAs of the last column group (group 3 of the last pair, in set 1).
+    auto scale_last = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
+    };
+
+    PairRegs R0, R1;
+    load_pair(R0, 0);
+    if (npairs > 1)
+        load_pair(R1, 1);
+    store_pair(R0, st[0]);
+    __syncthreads();
+    // One step: compute pair p from LDS stage p & 1 while pair p + 2 loads into
+    // the register set pair p used, then move pair p + 1 into the other stage.
+    auto step = [&](int p, PairRegs &Rp, PairRegs &Rn) __attribute__((always_inline)) {
+        if (p + 2 < npairs)
+            load_pair(Rp, p + 2);
+        compute_pair(st[p & 1]);
+        if (p + 1 < npairs)
+            store_pair(Rn, st[(p + 1) & 1]);
+        __syncthreads();
+    };
+    for (int p = 0; p < npairs; p += 2) {
+        step(p, R0, R1);
+        if (p + 1 < npairs)
+            step(p + 1, R1, R0);
+    }
+    scale_last();
+
+    // Group 1 hands its partial tile to group 0 through LDS (the stages are
+    // free after the loop's last barrier): [wavefront of the group][value][lane].
+    float *red = reinterpret_cast<float *>(&st[0]);
+    static_assert(sizeof(st) >= 4 * 64 * 64 * sizeof(float), "reduction buffer");
+    const int wq = wave & 3;
+    if (kg == 1) {
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane] = acc[ms][ns][q];
+    }
+    __syncthreads();
+    if (kg == 0) {
+        // Lane (li, g) of tile (ms, ns) holds rows 4g..4g+3 of column li.
+        // Offsets are 32-bit (M N < 2^31 on this path, checked at launch).
+        const int mb = m0 + wm * 64 + 4 * g, nb = n0 + wn * 64 + li;
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = mb + ms * 16 + q;
+                const uint32_t row_off = (uint32_t)m * (uint32_t)N + (uint32_t)nb;
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns) {
+                    const float v = acc[ms][ns][q] + red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane];
+                    if (m < M && nb + ns * 16 < N)
+                        y[row_off + ns * 16] = v;
+                }
+            }
+        }
+    }
+}
+
 hipError_t launch_gemm(const float *a, const uint8_t *w, float *y, int M, int N, int K,
-                       hipStream_t s)
+                       void *workspace, hipStream_t s)
 {
     const int tiles_m = (M + kGemmBM - 1) / kGemmBM, tiles_n = (N + kGemmBN - 1) / kGemmBN;
     const long long T = (long long)tiles_m * tiles_n;
     if (T > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    return launch_kernel(k_gemm_q4_0, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w, y, M, N,
-                         K, tiles_m, tiles_n);
+    if (!q4v::gemm_splits_activations(K))
+        return launch_kernel(k_gemm_q4_0_any, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w,
+                             y, M, N, K, tiles_m, tiles_n);
+    if ((long long)M * N >= (1LL << 31))   // the split kernel stores with 32-bit offsets
+        return launch_kernel(k_gemm_q4_0_any, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w,
+                             y, M, N, K, tiles_m, tiles_n);
+    u32x4 *ahl = static_cast<u32x4 *>(workspace);
+    const long long n_waves = (long long)tiles_m * 8 * (K / 32);
+    const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
+    if (split_grid > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    hipError_t e = launch_kernel(k_gemm_split_a, dim3((unsigned)split_grid), dim3(64 * kSplitWaves),
+                                 0, s, a, ahl, M, K, n_waves);
+    if (e != hipSuccess)
+        return e;
+    return launch_kernel(k_gemm_q4_0_split, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
+                         (const u32x4 *)ahl, w, y, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace q4k

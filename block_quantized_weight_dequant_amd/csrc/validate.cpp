@@ -95,4 +95,37 @@ int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_b
     return Q4_OK;
 }
 
+size_t gemm_workspace_bytes(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0 || !gemm_splits_activations(K))
+        return 0;
+    // Rows are padded to whole 128-row tiles; hi and lo binary16 per element.
+    size_t mp = ((size_t)M + 127) / 128 * 128, n = 0;
+    if (!mul_ok(mp, (size_t)K, &n) || !mul_ok(n, 4, &n))
+        return SIZE_MAX;
+    return n;
+}
+
+int check_workspace(const float *a, const void *w, size_t w_bytes, const float *y, int M, int N,
+                    int K, const void *ws, size_t ws_bytes)
+{
+    const size_t need = gemm_workspace_bytes(M, N, K);
+    if (need == 0)
+        return Q4_OK;   // this shape takes no workspace; ws is not read
+    if (need == SIZE_MAX)
+        return Q4_ERR_SIZE;
+    if (ws_bytes < need)
+        return Q4_ERR_WORKSPACE;
+    if (!ws)
+        return Q4_ERR_NULL;
+    if (!aligned16(ws))
+        return Q4_ERR_ALIGN;
+    const size_t a_bytes = (size_t)M * (size_t)K * sizeof(float);
+    const size_t y_bytes = (size_t)M * (size_t)N * sizeof(float);
+    if (overlaps({ws, need}, {a, a_bytes}) || overlaps({ws, need}, {w, w_bytes}) ||
+        overlaps({ws, need}, {y, y_bytes}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
 }  // namespace q4v

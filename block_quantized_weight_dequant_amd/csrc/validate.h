@@ -21,6 +21,19 @@ int check_product(const float *a, const void *w, size_t w_bytes, const float *y,
 int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_bytes,
                    size_t block_bytes, bool *empty);
 
+// True when q4_gemm takes the split-activation path for this K (the path that
+// needs a workspace). The GEMM launcher branches on the same predicate.
+inline bool gemm_splits_activations(int K) { return K > 0 && K % 64 == 0; }
+
+// Workspace bytes q4_gemm needs: 0 when none (no split path, or an empty or
+// invalid shape), SIZE_MAX when the size does not fit in size_t.
+size_t gemm_workspace_bytes(int M, int N, int K);
+
+// Checks of q4_gemm's workspace, after check_product has passed for a
+// non-empty problem: size, then NULL, alignment and overlap with a, w and y.
+int check_workspace(const float *a, const void *w, size_t w_bytes, const float *y, int M, int N,
+                    int K, const void *ws, size_t ws_bytes);
+
 bool aligned16(const void *p);
 bool overlaps(Span a, Span b);
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 1
+#define Q4_ABI_VERSION 2
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -48,6 +48,7 @@ extern "C" {
 #define Q4_ERR_ALIGN 4  /* a pointer is not 16-byte aligned */
 #define Q4_ERR_ALIAS 5  /* an output overlaps an input */
 #define Q4_ERR_LAUNCH 6 /* the HIP runtime refused the launch */
+#define Q4_ERR_WORKSPACE 7 /* q4_gemm's workspace is smaller than q4_gemm_workspace_bytes */
 
 /* Largest number of activation rows q4_gemv accepts. */
 #define Q4_GEMV_MAX_ROWS 8
@@ -90,10 +91,30 @@ int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
  *   M >= 1 unbounded (M == 0 or N == 0 is an empty problem).
  *   Activations must satisfy |a| < 65504 (they are split into two binary16
  *   terms); results for larger activations are unspecified.
+ *   workspace, workspace_bytes: device scratch owned by the caller, at least
+ *             q4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, not
+ *             overlapping a, W or y, and not used by other work while this
+ *             call runs on `stream`. When that function returns 0 (K % 64 != 0
+ *             or an empty problem) the workspace is not read or written and
+ *             may be NULL. Errors, after those of q4_gemv's checks:
+ *             Q4_ERR_SIZE if the needed size overflows size_t,
+ *             Q4_ERR_WORKSPACE if workspace_bytes is smaller, then
+ *             Q4_ERR_NULL, Q4_ERR_ALIGN, Q4_ERR_ALIAS for the pointer.
+ *             The library allocates nothing, so the call may be captured in
+ *             a HIP graph; its contents after the call are unspecified.
  * The reduction order is fixed, so repeated calls return identical bits.
  */
 int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
-            int M, int N, int K, void *stream);
+            int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * q4_gemm_workspace_bytes — bytes of workspace q4_gemm needs for this shape:
+ * ceil(M / 128) * 128 * K * 4 when K % 64 == 0 (the activations split once
+ * into binary16 hi and lo terms, in matrix-core operand order), 0 otherwise or
+ * when M, N or K is invalid or the problem is empty, and SIZE_MAX when the
+ * product does not fit in size_t. Pure function of its arguments.
+ */
+size_t q4_gemm_workspace_bytes(int M, int N, int K);
 
 /*
  * q8_quantize — f32 to Q8_0 blocks (section quantize_q8_0).

@@ -59,10 +59,10 @@ def test_version_and_status_codes():
     defs = _header_defines()
     assert binding.q4_abi_version() == defs["Q4_ABI_VERSION"]
     for name in ("Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_SIZE", "Q4_ERR_ALIGN",
-                 "Q4_ERR_ALIAS", "Q4_ERR_LAUNCH", "Q4_GEMV_MAX_ROWS"):
+                 "Q4_ERR_ALIAS", "Q4_ERR_LAUNCH", "Q4_ERR_WORKSPACE", "Q4_GEMV_MAX_ROWS"):
         assert getattr(binding, name) == defs[name]
-    strings = {binding.q4_status_string(c) for c in range(0, 7)}
-    assert len(strings) == 7 and binding.q4_status_string(99) == "unknown status"
+    strings = {binding.q4_status_string(c) for c in range(0, 8)}
+    assert len(strings) == 8 and binding.q4_status_string(99) == "unknown status"
 
 
 BASE = 0x7F0000000000       # fake, 16-byte aligned device-looking addresses
@@ -70,6 +70,8 @@ A, W, Y = BASE, BASE + (1 << 32), BASE + (2 << 32)
 
 
 def _prod(entry, a, w, wb, y, M, N, K):
+    if entry == "q4_gemm":   # no workspace: these checks all come before its own
+        return binding.raw_status(entry, a, w, wb, y, M, N, K, 0, 0, 0)
     return binding.raw_status(entry, a, w, wb, y, M, N, K, 0)
 
 
@@ -152,9 +154,42 @@ def test_rejected_call_writes_nothing():
     a = np.ones(64, dtype=np.float32)
     w = np.zeros(4 * 18, dtype=np.uint8)
     st = binding.raw_status("q4_gemm", a.ctypes.data, w.ctypes.data, w.size + 1, y.ctypes.data,
-                            1, 2, 64, 0)
+                            1, 2, 64, 0, 0, 0)
     assert st == binding.Q4_ERR_SIZE
     assert (y == 7.0).all()
+
+
+def test_gemm_workspace_bytes():
+    f = binding.q4_gemm_workspace_bytes
+    # Rows padded to whole 128-row tiles, binary16 hi and lo per element.
+    assert f(1, 1, 64) == 128 * 64 * 4
+    assert f(128, 7, 4096) == 128 * 4096 * 4
+    assert f(129, 7, 4096) == 256 * 4096 * 4
+    assert f(1024, 4096, 4096) == 1024 * 4096 * 4
+    assert f(2 ** 31 - 1, 1, 2 ** 31 - 64) == 2 ** 31 * (2 ** 31 - 64) * 4
+    # No split path (K % 64 != 0), empty or invalid shapes: no workspace.
+    for M, N, K in [(5, 5, 96), (5, 5, 32), (5, 5, 4128), (0, 5, 64), (5, 0, 64), (-1, 5, 64),
+                    (5, -1, 64), (5, 5, 48), (5, 5, 0), (5, 5, -64)]:
+        assert f(M, N, K) == 0, (M, N, K)
+
+
+@fake_addresses
+def test_gemm_workspace_checks():
+    S = binding
+    M, N, K = 3, 4, 64
+    need = binding.q4_gemm_workspace_bytes(M, N, K)
+    WS = BASE + (3 << 32)
+    st = lambda ws, wsb: binding.raw_status("q4_gemm", A, W, _wb(N, K), Y, M, N, K, ws, wsb, 0)
+    assert st(WS, need - 1) == S.Q4_ERR_WORKSPACE
+    assert st(None, 0) == S.Q4_ERR_WORKSPACE
+    assert st(None, need) == S.Q4_ERR_NULL
+    assert st(WS + 8, need) == S.Q4_ERR_ALIGN
+    assert st(A + 16, need) == S.Q4_ERR_ALIAS                        # inside a
+    assert st(W - need + 16, need) == S.Q4_ERR_ALIAS                 # ends inside w
+    assert st(Y, need) == S.Q4_ERR_ALIAS                             # on y
+    # Checks of a, w and y come first, and an empty problem needs nothing.
+    assert binding.raw_status("q4_gemm", A, W, _wb(N, K), Y, M, N, 48, None, 0, 0) == S.Q4_ERR_SHAPE
+    assert binding.raw_status("q4_gemm", None, None, _wb(N, K), None, 0, N, K, None, 0, 0) == S.Q4_OK
 
 
 @fake_addresses

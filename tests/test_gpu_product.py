@@ -186,3 +186,66 @@ def test_empty_problems_are_no_ops():
     for fn in (binding.q4_gemv, binding.q4_gemm):
         fn(None, None, None, 0, 16, 64, w_bytes=16 * 2 * 18)
         fn(None, None, None, 3, 0, 64, w_bytes=0)
+
+
+# ------------------------------------------------------- the GEMM workspace
+
+def test_gemm_workspace_exact_size_and_garbage():
+    # A workspace of exactly q4_gemm_workspace_bytes, filled with garbage and
+    # fenced by guard bytes: the result is right and nothing outside is written.
+    M, N, K = 130, 200, 512
+    need = binding.q4_gemm_workspace_bytes(M, N, K)
+    assert need == 256 * K * 4
+    ws = Guarded(need, torch.uint8)
+    ws.view.fill_(0x7F)                      # binary16 NaN patterns everywhere
+    blob = q4_blob(N, K, 21)
+    a = wl.activations_f32(22, M, K)
+    y = Guarded(M * N, torch.float32)
+    binding.q4_gemm(to_dev(a), to_dev(blob), y.view, M, N, K, workspace=ws.view)
+    torch.cuda.synchronize()
+    assert ws.guards_intact() and y.guards_intact()
+    ref, bound = oracle.q4_0_matmul(a, blob, N, K)
+    assert_within_tolerance(y.host().reshape(M, N), ref, bound, "exact workspace")
+
+
+def test_gemm_too_small_workspace_is_rejected():
+    M, N, K = 4, 16, 128
+    need = binding.q4_gemm_workspace_bytes(M, N, K)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    y = torch.full((M * N,), 3.0, device=DEV)
+    with pytest.raises(binding.Q4Error) as e:
+        binding.q4_gemm(to_dev(wl.activations_f32(1, M, K)), to_dev(q4_blob(N, K, 2)), y,
+                        M, N, K, workspace=ws)
+    assert e.value.status == binding.Q4_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+def test_gemm_graph_replays_match_eager():
+    # The call allocates nothing, so it can be captured; every replay (with
+    # other eager work and synchronizations in between) must equal the eager
+    # result bit for bit.
+    M, N, K = 96, 384, 1024
+    blob = to_dev(q4_blob(N, K, 23))
+    a = to_dev(wl.activations_f32(24, M, K))
+    ws = torch.empty(binding.q4_gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    y_eager = torch.empty(M * N, device=DEV)
+    binding.q4_gemm(a, blob, y_eager, M, N, K, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty(M * N, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.q4_gemm(a, blob, y, M, N, K, workspace=ws)   # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.q4_gemm(a, blob, y, M, N, K, workspace=ws)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        binding.q4_gemm(a, blob, torch.empty_like(y), M, N, K)   # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), rep

@@ -257,25 +257,45 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
 }
 
 constexpr int kSplitGemmThreads = 512;
-constexpr int kBRowDwords = 10;   // LDS dwords per weight row and pair: 9 (36 bytes) + 1 pad
+constexpr int kRingStages = 4;
+constexpr int kBDwords = kGemmBN * 9;      // a pair's raw weight bytes: 36 per row
+constexpr int kBSlots = 8 * 3 * 64;        // dword slots of three loads per wavefront
 
-struct SplitStage {
-    u32x4 a[2 * kOpsPerBlockTile];      // [kg][hl][sub][lane]
-    uint32_t b[kGemmBN * kBRowDwords];  // [row][dword]: blocks 2s and 2s+1 of the row
+// One ring stage: the pair's activation slab and raw weight bytes.
+struct RingStage {
+    u32x4 a[2 * kOpsPerBlockTile];  // 32 KB, [kg][hl][sub][lane], as in the workspace
+    uint32_t b[kBSlots];            // [row][9 dwords]; slots >= 128 * 9 are never read
 };
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) lgkmcnt(0), expcnt unchanged.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+
+// Wait until this wavefront has at most `vm` vector-memory operations
+// outstanding and all its LDS operations are done, then meet the workgroup.
+// A raw s_barrier: __syncthreads() would also wait for every outstanding
+// direct-to-LDS load, which are meant to stay in flight. The empty asm
+// statements keep the compiler from moving LDS accesses across it.
+template <int VM>
+__device__ __forceinline__ void ring_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
     const u32x4 *__restrict__ ahl, const uint8_t *__restrict__ w, float *__restrict__ y, int M,
     int N, int K, int tiles_m, int tiles_n)
 {
-    __shared__ SplitStage st[2];
+    __shared__ RingStage st[kRingStages];
 
     const int T = tiles_m * tiles_n, L = blockIdx.x;
     const int t = (T % 8 == 0) ? (L % 8) * (T / 8) + L / 8 : L;
     const int mt = t / tiles_n, m0 = mt * kGemmBM, n0 = (t % tiles_n) * kGemmBN;
 
     const int tid = threadIdx.x, lane = tid & 63;
-    // The wavefront index, made visibly uniform so that branches on kg are scalar.
+    // The wavefront index, made visibly uniform so that branches on it are scalar.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
     const int li = lane & 15, g = lane >> 4;
@@ -285,46 +305,35 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic_v));
     const size_t row_bytes = (size_t)nblk * kQ4Bytes;
 
-    // Staging roles. A: operands tid + 512 q of the pair's 32 KB slab, which
-    // has the LDS layout already. B: dword i = tid + 512 r (i < 128 * 9) is
-    // dword i % 9 of the pair's 36 bytes of row i / 9.
-    const u32x4 *asrc = ahl + (size_t)mt * nblk * kOpsPerBlockTile + tid;
-    constexpr int kBDwords = kGemmBN * 9;
-    const uint32_t *bsrc[3];
-    int bdst[3];
+    // Direct-to-LDS loads, seven per wavefront per pair (so every wavefront's
+    // vmcnt moves in the same steps). A: four 16-byte loads, 1 KB each, at
+    // entries (4 wave + i) * 64 + lane of the slab, whose workspace order is
+    // the LDS order. B: three 4-byte loads at dword slots j * 64 + lane, j =
+    // wave + 8 r; slot t < 128 * 9 is dword t % 9 of the pair's 36 bytes of row
+    // t / 9, higher slots re-read a valid dword into unused LDS.
+    const u32x4 *asrc = ahl + (size_t)mt * nblk * kOpsPerBlockTile + wave * 4 * 64 + lane;
+    const uint8_t *bsrc[3];
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
-        const int i = min(tid + 512 * r, kBDwords - 1), row = i / 9, dw = i % 9;
-        bsrc[r] = reinterpret_cast<const uint32_t *>(w + (size_t)min(n0 + row, N - 1) * row_bytes) + dw;
-        bdst[r] = row * kBRowDwords + dw;
+        const int tt = min((wave + 8 * r) * 64 + lane, kBDwords - 1), row = tt / 9, dw = tt % 9;
+        bsrc[r] = w + (size_t)min(n0 + row, N - 1) * row_bytes + 4 * dw;
     }
-    const bool b2 = tid + 1024 < kBDwords;   // the third B dword exists for this thread
-
-    // Staged pairs travel through registers: the loads of pair p + 2 are
-    // issued before pair p is computed and written to LDS after pair p + 1 is,
-    // so each load has two pairs' worth of compute to arrive in. The loop is
-    // unrolled by two so that the two register sets have fixed names.
-    struct PairRegs {
-        u32x4 a[4];
-        uint32_t b[3];
+    // Load k (0..6) of pair p: four A loads, then three B loads.
+    auto issue_load = [&](int p, int k) __attribute__((always_inline)) {
+        RingStage &S = st[p % kRingStages];
+        if (k < 4)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(asrc + (size_t)p * 2 * kOpsPerBlockTile + k * 64),
+                (__attribute__((address_space(3))) void *)(S.a + (wave * 4 + k) * 64), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(bsrc[k - 4] + 36 * p),
+                (__attribute__((address_space(3))) void *)(S.b + (wave + 8 * (k - 4)) * 64), 4, 0, 0);
     };
-    auto load_pair = [&](PairRegs &R, int p) __attribute__((always_inline)) {
+    auto issue_pair = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            R.a[q] = asrc[(size_t)p * 2 * kOpsPerBlockTile + 512 * q];
-        R.b[0] = bsrc[0][9 * p];
-        R.b[1] = bsrc[1][9 * p];
-        if (b2)
-            R.b[2] = bsrc[2][9 * p];
-    };
-    auto store_pair = [&](const PairRegs &R, SplitStage &S) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            S.a[tid + 512 * q] = R.a[q];
-        S.b[bdst[0]] = R.b[0];
-        S.b[bdst[1]] = R.b[1];
-        if (b2)
-            S.b[bdst[2]] = R.b[2];
+        for (int k = 0; k < 7; ++k)
+            issue_load(p, k);
     };
 
     f32x4 acc[4][4];
@@ -333,22 +342,34 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
             acc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const f16 sc = (f16)0x1p-11f;
     const f16x8 scale = {sc, sc, sc, sc, sc, sc, sc, sc};
+
     // B of column group ns, block 2p + kg: qs dword g of the block for column
-    // wn*64 + ns*16 + li starts at byte 18 kg + 2 + 4 g of the staged row, which
-    // is dword g + 5 kg shifted by 2 (1 - kg) bytes; d is the 16-bit half kg of
-    // dword 4 kg. Branch-free, so a pair's compute is one scheduling region.
+    // wn*64 + ns*16 + li starts at byte 18 kg + 2 + 4 g of the row's 36 bytes,
+    // which is dword g + 5 kg shifted by 2 (1 - kg) bytes; d is the 16-bit half
+    // kg of dword 4 kg. Branch-free, so a pair's compute is one scheduling region.
     const int bi0 = g + 5 * kg, bsh = 2 * (1 - kg), bdi = 4 * kg, bds = 16 * kg;
     struct BCol {
         uint32_t lo, hi, dw;
     };
-    auto read_b = [&](const SplitStage &cur, int ns) __attribute__((always_inline)) {
-        const uint32_t *rb = cur.b + (wn * 64 + ns * 16 + li) * kBRowDwords;
+    auto read_b = [&](const RingStage &S, int ns) __attribute__((always_inline)) {
+        const uint32_t *rb = S.b + (wn * 64 + ns * 16 + li) * 9;
         return BCol{rb[bi0], rb[bi0 + 1], rb[bdi]};
     };
+    struct AOps {
+        f16x8 hi[4], lo[4];
+    };
+    auto read_a = [&](const RingStage &S, AOps &A) __attribute__((always_inline)) {
+        const u32x4 *ap = S.a + kg * kOpsPerBlockTile + wm * 4 * 64 + lane;
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+            A.hi[ms] = bitcast<f16x8>(ap[ms * 64]);
+            A.lo[ms] = bitcast<f16x8>(ap[8 * 64 + ms * 64]);
+        }
+    };
+
     // Software pipeline over the four column groups of a pair: the MFMAs of
     // group ns are issued between the scale FMAs of group ns - 1 (whose results
     // are ready) and the decode of group ns + 1. Group results alternate
@@ -363,77 +384,113 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms)
             cbuf[h][ms] = zero4;
-    auto compute_pair = [&](const SplitStage &cur) __attribute__((always_inline)) {
-        f16x8 ahi[4], alo[4];
-        const u32x4 *ap = cur.a + kg * kOpsPerBlockTile + wm * 4 * 64 + lane;
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-            ahi[ms] = bitcast<f16x8>(ap[ms * 64]);
-            alo[ms] = bitcast<f16x8>(ap[8 * 64 + ms * 64]);
-        }
-        BCol bc = read_b(cur, 0);
+    struct BOps {
+        f16x8 q, s;   // (q - 8) and (q - 8) 2^-11
+        float d;
+    };
+    auto decode_b = [&](const BCol &bc) __attribute__((always_inline)) {
+        const uint32_t x = __builtin_amdgcn_alignbyte(bc.hi, bc.lo, (uint32_t)bsh);
+        BOps o;
+        o.d = f16_bits_to_f32((bc.dw >> bds) & 0xFFFFu);
+        o.q = decode_plain(x, magic_v);
+        o.s = o.q * scale;
+        return o;
+    };
+    // One scheduling region per column group ns: its eight MFMAs (the four hi
+    // products, then the four lo products that add onto them) interleaved
+    // with the scale FMAs of group ns - 1 and the decode of group ns + 1.
+    // Hard scheduling barriers between regions keep that order.
+    auto compute_pair = [&](const BCol (&bcol)[4], const AOps &A, int dma_pair) __attribute__((always_inline)) {
+        BOps cur = decode_b(bcol[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) {
-            const uint32_t x = __builtin_amdgcn_alignbyte(bc.hi, bc.lo, (uint32_t)bsh);
-            const float d = f16_bits_to_f32((bc.dw >> bds) & 0xFFFFu);
-            if (ns + 1 < 4)
-                bc = read_b(cur, ns + 1);
-            const f16x8 bq = decode_plain(x, magic_v), bs = bq * scale;
+            // The loads of pair dma_pair go out two per region (one in the
+            // last), between MFMAs, so the address unit works while the
+            // matrix cores do and no wavefront's MFMAs queue behind a load.
+            if (dma_pair >= 0) {
+                issue_load(dma_pair, 2 * ns);
+                if (2 * ns + 1 < 7)
+                    issue_load(dma_pair, 2 * ns + 1);
+            }
             f32x4 *c = cbuf[ns & 1];
             const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
             const float dp = dbuf[(ns + 1) & 1];
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms)
+                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.hi[ms], cur.q, zero4, 0, 0, 0);
+            const int np = (ns + 3) & 3;
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    acc[ms][(ns + 3) & 3][q] = fmaf(dp, cp[ms][q], acc[ms][(ns + 3) & 3][q]);
+                    acc[ms][np][q] = fmaf(dp, cp[ms][q], acc[ms][np][q]);
+            // Pin these FMAs to this region: IR passes would otherwise sink
+            // them past the scheduling barriers, to the end of the pair.
+            asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]));
+            BOps nxt = cur;
+            if (ns + 1 < 4)
+                nxt = decode_b(bcol[ns + 1]);
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bq, zero4, 0, 0, 0);
-                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bs, c[ms], 0, 0, 0);
-            }
-            dbuf[ns & 1] = d;
+            for (int ms = 0; ms < 4; ++ms)
+                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.lo[ms], cur.s, c[ms], 0, 0, 0);
+            dbuf[ns & 1] = cur.d;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
             }
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
         }
     };
-    // FMAs of the last column group (group 3 of the last pair, in set 1).
-    auto scale_last = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
-    };
 
-    PairRegs R0, R1;
-    load_pair(R0, 0);
-    if (npairs > 1)
-        load_pair(R1, 1);
-    store_pair(R0, st[0]);
-    __syncthreads();
-    // One step: compute pair p from LDS stage p & 1 while pair p + 2 loads into
-    // the register set pair p used, then move pair p + 1 into the other stage.
-    auto step = [&](int p, PairRegs &Rp, PairRegs &Rn) __attribute__((always_inline)) {
-        if (p + 2 < npairs)
-            load_pair(Rp, p + 2);
-        compute_pair(st[p & 1]);
+    // Ring schedule: pair q is loaded into stage q % 4 during step q - 3, is
+    // complete by the barrier ending step q - 2, has its A operands read into
+    // registers during step q - 1 and is computed in step q. Stage q % 4 is
+    // loaded again (pair q + 4) in step q + 1, after the barrier that ends
+    // step q, by which every wavefront has read it.
+    const int pre = min(npairs, 3);
+    for (int p = 0; p < pre; ++p)
+        issue_pair(p);
+    if (pre == 3)
+        ring_barrier<7>();    // pairs 0 and 1 complete, pair 2 in flight
+    else
+        ring_barrier<0>();
+    AOps A0, A1;
+    read_a(st[0], A0);
+    auto step = [&](int p, const AOps &Acur, AOps &Anext) __attribute__((always_inline)) {
+        // This pair's raw weight dwords first (one wait covers them), then
+        // the next pair's A operands, which land during this pair's MFMAs.
+        BCol bcol[4];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+            bcol[ns] = read_b(st[p % kRingStages], ns);
+        __builtin_amdgcn_sched_barrier(0);
         if (p + 1 < npairs)
-            store_pair(Rn, st[(p + 1) & 1]);
-        __syncthreads();
+            read_a(st[(p + 1) % kRingStages], Anext);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_pair(bcol, Acur, p + 3 < npairs ? p + 3 : -1);
+        if (p + 3 < npairs)
+            ring_barrier<7>();    // pair p + 2 complete, pair p + 3 in flight
+        else
+            ring_barrier<0>();
     };
     for (int p = 0; p < npairs; p += 2) {
-        step(p, R0, R1);
+        step(p, A0, A1);
         if (p + 1 < npairs)
-            step(p + 1, R1, R0);
+            step(p + 1, A1, A0);
     }
-    scale_last();
+    // FMAs of the last column group (group 3 of the last pair, in set 1).
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
 
-    // Group 1 hands its partial tile to group 0 through LDS (the stages are
-    // free after the loop's last barrier): [wavefront of the group][value][lane].
+    // Group 1 hands its partial tile to group 0 through LDS (every load has
+    // landed and every wavefront has passed the last barrier):
+    // [wavefront of the group][value][lane].
     float *red = reinterpret_cast<float *>(&st[0]);
     static_assert(sizeof(st) >= 4 * 64 * 64 * sizeof(float), "reduction buffer");
     const int wq = wave & 3;

@@ -245,6 +245,36 @@ def bench_quantize(torch, q4, wl, steps, warmup):
     return row
 
 
+def bench_stream_ceiling(torch, nbytes, steps, warmup, cold=True):
+    """A plain 16-byte streaming read of `nbytes` (libq4probe.so) in the same
+    harness and cache state as the GEMV rows: the practical ceiling for one
+    launch that reads that much."""
+    import ctypes
+    path = os.path.join(ROOT, "block_quantized_weight_dequant_amd", "libq4probe.so")
+    lib = ctypes.CDLL(path)
+    lib.q4probe_stream_read.restype = ctypes.c_int
+    lib.q4probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    R = copies_for_cold(nbytes) if cold else 1
+    bufs = [torch.full((nbytes,), 0x37, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+
+    def fn(k):
+        st = lib.q4probe_stream_read(bufs[k % R].data_ptr(), nbytes, sink.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError("q4probe_stream_read status %d" % st)
+
+    t = run_timed(torch, fn, steps, warmup)
+    row = {"workload": "stream_read_%dB" % nbytes, "kernel": "k_stream_read (libq4probe)",
+           "copies": R, "cache": "cold" if R > 1 else "warm", "bytes": nbytes, **t,
+           "kernel_GBs": nbytes / (t["kernel_us"] * 1e-6) / 1e9}
+    row["frac_of_hbm_peak"] = row["kernel_GBs"] / HBM_PEAK_GBS
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return row
+
+
 def copy_calibration(torch):
     """One 256 MiB device-to-device copy (read 256 MiB, write 256 MiB), for
     scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -317,6 +347,16 @@ def main():
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10)))
         log("row: Q8_0 quantize 2048x4096")
         rows.append(bench_quantize(torch, q4, wl, args.steps, args.warmup))
+    # Measured ceilings: a plain streaming read of the headline's bytes in the
+    # same harness (cold), and of 1 GiB (the chip's sustained read rate).
+    log("row: streaming-read ceilings")
+    ceil = bench_stream_ceiling(torch, head["algorithmic_bytes"], args.steps, args.warmup)
+    rows.append(ceil)
+    if args.rows == "all":
+        rows.append(bench_stream_ceiling(torch, 2 ** 30, 10, 3))
+    head["roofline"]["frac_of_measured_read_ceiling"] = (
+        head["roofline"]["achieved"] / ceil["kernel_GBs"])
+    head["roofline"]["measured_read_ceiling_GBs"] = ceil["kernel_GBs"]
     calib = copy_calibration(torch) if args.calibrate_copy else None
 
     cpu = None

@@ -55,6 +55,19 @@ def test_exports_match_header():
         assert hasattr(binding.lib, name)
 
 
+def test_probe_library_exports_its_header():
+    # The measurement-only library: every function include/q4_probe.h
+    # declares, and nothing else, is exported.
+    hdr = os.path.join(ROOT, "include", "q4_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"^\s*\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    lib = os.path.join(os.path.dirname(binding.LIB_PATH), "libq4probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
+                         check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("q4"))
+    assert declared == exported == ["q4probe_stream_read"]
+
+
 def test_version_and_status_codes():
     defs = _header_defines()
     assert binding.q4_abi_version() == defs["Q4_ABI_VERSION"]

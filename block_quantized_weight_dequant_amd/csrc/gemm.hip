@@ -27,6 +27,8 @@
 // * Tiles are renumbered so that each of the chip's 8 XCDs (which receive
 //   workgroups round-robin) works on a contiguous run of tiles sharing the
 //   same activation rows, which then stay in that XCD's L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "validate.h"
@@ -53,6 +55,23 @@ __device__ __forceinline__ f16x8 decode_plain(uint32_t x, uint32_t magic = 0x640
     f16x2 h1 = bitcast<f16x2>(v1) - bias;
     f16x2 h2 = bitcast<f16x2>(v2) - bias;
     f16x2 h3 = bitcast<f16x2>(v3) - bias;
+    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+// B operand for qs dword x as decode_plain, but with the high nibbles decoded
+// in place: slots 4..7 hold 16 (q - 8) (one shift instead of three). The
+// split-activation path pairs it with activations that carry a / 16 there.
+__device__ __forceinline__ f16x8 decode_x16m(uint32_t x, uint32_t magic)
+{
+    const uint32_t t = x >> 8;
+    const uint32_t v0 = (x & 0x000F000Fu) | magic;   // 1024 + q, bytes 0, 2 low nibbles
+    const uint32_t v1 = (t & 0x000F000Fu) | magic;   // bytes 1, 3 low nibbles
+    const uint32_t v2 = (x & 0x00F000F0u) | magic;   // 1024 + 16 q, bytes 0, 2 high nibbles
+    const uint32_t v3 = (t & 0x00F000F0u) | magic;   // bytes 1, 3 high nibbles
+    const f16x2 lo_bias = {(f16)1032.0f, (f16)1032.0f};
+    const f16x2 hi_bias = {(f16)1152.0f, (f16)1152.0f};
+    const f16x2 h0 = bitcast<f16x2>(v0) - lo_bias, h1 = bitcast<f16x2>(v1) - lo_bias;
+    const f16x2 h2 = bitcast<f16x2>(v2) - hi_bias, h3 = bitcast<f16x2>(v3) - hi_bias;
     return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
@@ -242,7 +261,10 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
         const float *src = a + m * K + (long long)kb * 32 + 4 * g;
         const float4 L = *reinterpret_cast<const float4 *>(src);
         const float4 H = *reinterpret_cast<const float4 *>(src + 16);
-        const float e[8] = {L.x, L.z, L.y, L.w, H.x, H.z, H.y, H.w};
+        // Slots 4..7 pair with high nibbles, which the GEMM decodes as 16 (q - 8):
+        // they carry a / 16 (exact), so every product is a (q - 8).
+        const float e[8] = {L.x, L.z, L.y, L.w, H.x * 0.0625f, H.z * 0.0625f, H.y * 0.0625f,
+                            H.w * 0.0625f};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const f16 h = (f16)e[s];
@@ -346,147 +368,157 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
     const f16 sc = (f16)0x1p-11f;
     const f16x8 scale = {sc, sc, sc, sc, sc, sc, sc, sc};
 
-    // B of column group ns, block 2p + kg: qs dword g of the block for column
-    // wn*64 + ns*16 + li starts at byte 18 kg + 2 + 4 g of the row's 36 bytes,
-    // which is dword g + 5 kg shifted by 2 (1 - kg) bytes; d is the 16-bit half
-    // kg of dword 4 kg. Branch-free, so a pair's compute is one scheduling region.
-    const int bi0 = g + 5 * kg, bsh = 2 * (1 - kg), bdi = 4 * kg, bds = 16 * kg;
-    struct BCol {
-        uint32_t lo, hi, dw;
-    };
-    auto read_b = [&](const RingStage &S, int ns) __attribute__((always_inline)) {
-        const uint32_t *rb = S.b + (wn * 64 + ns * 16 + li) * 9;
-        return BCol{rb[bi0], rb[bi0 + 1], rb[bdi]};
-    };
-    struct AOps {
-        f16x8 hi[4], lo[4];
-    };
-    auto read_a = [&](const RingStage &S, AOps &A) __attribute__((always_inline)) {
-        const u32x4 *ap = S.a + kg * kOpsPerBlockTile + wm * 4 * 64 + lane;
+    auto run_group = [&](auto kg_c) __attribute__((always_inline)) {
+        constexpr int KG = decltype(kg_c)::value;
+        // B of column group ns, block 2p + KG: qs dword g of the block for column
+        // wn*64 + ns*16 + li starts at byte 18 KG + 2 + 4 g of the row's 36 bytes,
+        // which is dword g + 5 KG shifted by 2 (1 - KG) bytes; d is the 16-bit half
+        // KG of dword 4 KG. KG is a compile-time constant (the loop exists once per
+        // K group), so group 1 needs no realignment and d feeds the scale FMA
+        // straight from its half.
+        const int bi0 = g + 5 * KG;
+        struct BCol {
+            uint32_t lo, hi, dw;
+        };
+        auto read_b = [&](const RingStage &S, int ns) __attribute__((always_inline)) {
+            const uint32_t *rb = S.b + (wn * 64 + ns * 16 + li) * 9;
+            return BCol{rb[bi0], KG == 0 ? rb[bi0 + 1] : 0u, rb[4 * KG]};
+        };
+        struct AOps {
+            f16x8 hi[4], lo[4];
+        };
+        auto read_a = [&](const RingStage &S, AOps &A) __attribute__((always_inline)) {
+            const u32x4 *ap = S.a + KG * kOpsPerBlockTile + wm * 4 * 64 + lane;
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-            A.hi[ms] = bitcast<f16x8>(ap[ms * 64]);
-            A.lo[ms] = bitcast<f16x8>(ap[8 * 64 + ms * 64]);
-        }
-    };
+            for (int ms = 0; ms < 4; ++ms) {
+                A.hi[ms] = bitcast<f16x8>(ap[ms * 64]);
+                A.lo[ms] = bitcast<f16x8>(ap[8 * 64 + ms * 64]);
+            }
+        };
 
-    // Software pipeline over the four column groups of a pair: the MFMAs of
-    // group ns are issued between the scale FMAs of group ns - 1 (whose results
-    // are ready) and the decode of group ns + 1. Group results alternate
-    // between two register sets by the parity of ns, and the group before
-    // group 0 is group 3 of the previous pair (zeros before the first pair),
-    // so every index is a compile-time constant. The scheduling-group barriers
-    // ask for one MFMA then three VALU instructions, eight times per group.
-    f32x4 cbuf[2][4];
-    float dbuf[2] = {0.0f, 0.0f};
+        // Software pipeline over the four column groups of a pair: the MFMAs of
+        // group ns are issued between the scale FMAs of group ns - 1 (whose results
+        // are ready) and the decode of group ns + 1. Group results alternate
+        // between two register sets by the parity of ns, and the group before
+        // group 0 is group 3 of the previous pair (zeros before the first pair),
+        // so every index is a compile-time constant. The scheduling-group barriers
+        // ask for one MFMA then three VALU instructions, eight times per group.
+        f32x4 cbuf[2][4];
+        float dbuf[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-            cbuf[h][ms] = zero4;
-    struct BOps {
-        f16x8 q, s;   // (q - 8) and (q - 8) 2^-11
-        float d;
-    };
-    auto decode_b = [&](const BCol &bc) __attribute__((always_inline)) {
-        const uint32_t x = __builtin_amdgcn_alignbyte(bc.hi, bc.lo, (uint32_t)bsh);
-        BOps o;
-        o.d = f16_bits_to_f32((bc.dw >> bds) & 0xFFFFu);
-        o.q = decode_plain(x, magic_v);
-        o.s = o.q * scale;
-        return o;
-    };
-    // One scheduling region per column group ns: its eight MFMAs (the four hi
-    // products, then the four lo products that add onto them) interleaved
-    // with the scale FMAs of group ns - 1 and the decode of group ns + 1.
-    // Hard scheduling barriers between regions keep that order.
-    auto compute_pair = [&](const BCol (&bcol)[4], const AOps &A, int dma_pair) __attribute__((always_inline)) {
-        BOps cur = decode_b(bcol[0]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-            // The loads of pair dma_pair go out two per region (one in the
-            // last), between MFMAs, so the address unit works while the
-            // matrix cores do and no wavefront's MFMAs queue behind a load.
-            if (dma_pair >= 0) {
-                issue_load(dma_pair, 2 * ns);
-                if (2 * ns + 1 < 7)
-                    issue_load(dma_pair, 2 * ns + 1);
-            }
-            f32x4 *c = cbuf[ns & 1];
-            const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
-            const float dp = dbuf[(ns + 1) & 1];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms)
-                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.hi[ms], cur.q, zero4, 0, 0, 0);
-            const int np = (ns + 3) & 3;
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc[ms][np][q] = fmaf(dp, cp[ms][q], acc[ms][np][q]);
-            // Pin these FMAs to this region: IR passes would otherwise sink
-            // them past the scheduling barriers, to the end of the pair.
-            asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]));
-            BOps nxt = cur;
-            if (ns + 1 < 4)
-                nxt = decode_b(bcol[ns + 1]);
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
-                c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.lo[ms], cur.s, c[ms], 0, 0, 0);
-            dbuf[ns & 1] = cur.d;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
-            }
+                cbuf[h][ms] = zero4;
+        struct BOps {
+            f16x8 q, s;   // (q - 8) (x16 in slots 4..7) and the same times 2^-11
+            float d;
+        };
+        auto decode_b = [&](const BCol &bc) __attribute__((always_inline)) {
+            const uint32_t x = KG == 0 ? __builtin_amdgcn_alignbyte(bc.hi, bc.lo, 2u) : bc.lo;
+            BOps o;
+            o.d = f16_bits_to_f32(KG == 0 ? (bc.dw & 0xFFFFu) : (bc.dw >> 16));
+            o.q = decode_x16m(x, magic_v);
+            o.s = o.q * scale;
+            return o;
+        };
+        // One scheduling region per column group ns: its eight MFMAs (the four hi
+        // products, then the four lo products that add onto them) interleaved
+        // with the scale FMAs of group ns - 1 and the decode of group ns + 1.
+        // Hard scheduling barriers between regions keep that order.
+        auto compute_pair = [&](const BCol (&bcol)[4], const AOps &A, int dma_pair) __attribute__((always_inline)) {
+            BOps cur = decode_b(bcol[0]);
             __builtin_amdgcn_sched_barrier(0);
-            cur = nxt;
-        }
-    };
-
-    // Ring schedule: pair q is loaded into stage q % 4 during step q - 3, is
-    // complete by the barrier ending step q - 2, has its A operands read into
-    // registers during step q - 1 and is computed in step q. Stage q % 4 is
-    // loaded again (pair q + 4) in step q + 1, after the barrier that ends
-    // step q, by which every wavefront has read it.
-    const int pre = min(npairs, 3);
-    for (int p = 0; p < pre; ++p)
-        issue_pair(p);
-    if (pre == 3)
-        ring_barrier<7>();    // pairs 0 and 1 complete, pair 2 in flight
-    else
-        ring_barrier<0>();
-    AOps A0, A1;
-    read_a(st[0], A0);
-    auto step = [&](int p, const AOps &Acur, AOps &Anext) __attribute__((always_inline)) {
-        // This pair's raw weight dwords first (one wait covers them), then
-        // the next pair's A operands, which land during this pair's MFMAs.
-        BCol bcol[4];
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-            bcol[ns] = read_b(st[p % kRingStages], ns);
-        __builtin_amdgcn_sched_barrier(0);
-        if (p + 1 < npairs)
-            read_a(st[(p + 1) % kRingStages], Anext);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_pair(bcol, Acur, p + 3 < npairs ? p + 3 : -1);
-        if (p + 3 < npairs)
-            ring_barrier<7>();    // pair p + 2 complete, pair p + 3 in flight
+            for (int ns = 0; ns < 4; ++ns) {
+                // The loads of pair dma_pair go out two per region (one in the
+                // last), between MFMAs, so the address unit works while the
+                // matrix cores do and no wavefront's MFMAs queue behind a load.
+                if (dma_pair >= 0) {
+                    issue_load(dma_pair, 2 * ns);
+                    if (2 * ns + 1 < 7)
+                        issue_load(dma_pair, 2 * ns + 1);
+                }
+                f32x4 *c = cbuf[ns & 1];
+                const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
+                const float dp = dbuf[(ns + 1) & 1];
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms)
+                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.hi[ms], cur.q, zero4, 0, 0, 0);
+                const int np = (ns + 3) & 3;
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[ms][np][q] = fmaf(dp, cp[ms][q], acc[ms][np][q]);
+                // Pin these FMAs to this region: IR passes would otherwise sink
+                // them past the scheduling barriers, to the end of the pair.
+                asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]));
+                BOps nxt = cur;
+                if (ns + 1 < 4)
+                    nxt = decode_b(bcol[ns + 1]);
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms)
+                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.lo[ms], cur.s, c[ms], 0, 0, 0);
+                dbuf[ns & 1] = cur.d;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                cur = nxt;
+            }
+        };
+
+        // Ring schedule: pair q is loaded into stage q % 4 during step q - 3, is
+        // complete by the barrier ending step q - 2, has its A operands read into
+        // registers during step q - 1 and is computed in step q. Stage q % 4 is
+        // loaded again (pair q + 4) in step q + 1, after the barrier that ends
+        // step q, by which every wavefront has read it.
+        const int pre = min(npairs, 3);
+        for (int p = 0; p < pre; ++p)
+            issue_pair(p);
+        if (pre == 3)
+            ring_barrier<7>();    // pairs 0 and 1 complete, pair 2 in flight
         else
             ring_barrier<0>();
+        AOps A0, A1;
+        read_a(st[0], A0);
+        auto step = [&](int p, const AOps &Acur, AOps &Anext) __attribute__((always_inline)) {
+            // This pair's raw weight dwords first (one wait covers them), then
+            // the next pair's A operands, which land during this pair's MFMAs.
+            BCol bcol[4];
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns)
+                bcol[ns] = read_b(st[p % kRingStages], ns);
+            __builtin_amdgcn_sched_barrier(0);
+            if (p + 1 < npairs)
+                read_a(st[(p + 1) % kRingStages], Anext);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_pair(bcol, Acur, p + 3 < npairs ? p + 3 : -1);
+            if (p + 3 < npairs)
+                ring_barrier<7>();    // pair p + 2 complete, pair p + 3 in flight
+            else
+                ring_barrier<0>();
+        };
+        for (int p = 0; p < npairs; p += 2) {
+            step(p, A0, A1);
+            if (p + 1 < npairs)
+                step(p + 1, A1, A0);
+        }
+        // FMAs of the last column group (group 3 of the last pair, in set 1).
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
+
     };
-    for (int p = 0; p < npairs; p += 2) {
-        step(p, A0, A1);
-        if (p + 1 < npairs)
-            step(p + 1, A1, A0);
-    }
-    // FMAs of the last column group (group 3 of the last pair, in set 1).
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
+    if (kg == 0)
+        run_group(std::integral_constant<int, 0>{});
+    else
+        run_group(std::integral_constant<int, 1>{});
 
     // Group 1 hands its partial tile to group 0 through LDS (every load has
     // landed and every wavefront has passed the last barrier):

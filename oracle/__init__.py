@@ -1,4 +1,5 @@
-"""Plain CPU oracle for Q4_0 / Q8_0 block quantization and the Q4_0 x f32 product.
+"""Plain CPU oracle for Q4_0 / Q8_0 block quantization and the Q4_0 x f32 and
+Q8_0 x f32 products.
 
 TEST INFRASTRUCTURE, not part of the product: only the test suite,
 ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
@@ -14,6 +15,9 @@ What each function follows (the docs.rs page "fuel-vulkan-kernels — quantized
 * ``q8_0_dequant``   section "dequant_q8_0" (x = qs * d).
 * ``q4_0_matmul``    sections "qmatvec_q4_0" / "matmul_q4_0_tiled"
                      (y = a @ dequant(W)^T), summed in f64.
+* ``q8_0_matmul``    the same product over Q8_0 weights (the quantized-matmul
+                     binding picks Q4_0 or Q8_0 blocks by quant type, section
+                     "qmatvec_q4_0"; weights decoded per "dequant_q8_0").
 * ``q4_0_quantize``  GGML's Q4_0 reference rule as stated with the benchmark
                      workloads (not on the pages); it only makes test weights.
 * ``f16_to_f32`` / ``f32_to_f16``  IEEE 754 binary16 (round to nearest even).
@@ -73,12 +77,13 @@ def _load():
     for name in ("orc_q4_0_quantize", "orc_q8_0_quantize"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [P, sz, P]
-    lib.orc_q4_0_matmul.restype = ctypes.c_int
-    lib.orc_q4_0_matmul.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                    P, P, ctypes.c_int]
-    lib.orc_q4_0_matmul_sampled.restype = ctypes.c_int
-    lib.orc_q4_0_matmul_sampled.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                            P, P, ctypes.c_int64, P, P, ctypes.c_int]
+    i32 = ctypes.c_int
+    for name in ("orc_q4_0_matmul", "orc_q8_0_matmul"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [P, P, i32, i32, i32, P, P, i32]
+    for name in ("orc_q4_0_matmul_sampled", "orc_q8_0_matmul_sampled"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [P, P, i32, i32, i32, P, P, ctypes.c_int64, P, P, i32]
     lib.orc_max_threads.restype = ctypes.c_int
     lib.orc_max_threads.argtypes = []
     _lib = lib
@@ -161,41 +166,37 @@ def q8_0_dequant(blob) -> np.ndarray:
 
 # ----------------------------------------------------------------- product
 
-def q4_0_matmul(a, w_blob, N: int, K: int, threads: int = 0):
-    """y[m, n] = sum_k a[m, k] * dequant(W)[n, k] in f64, and the bound
-    B[m, n] = sum_k |a[m, k] * w[n, k]|. a is [M, K] f32, W is the [N, K/32]
-    Q4_0 block stream. Returns (y, B), both float64 [M, N]."""
+_BLOCK_BYTES = {"q4_0": Q4_0_BLOCK_BYTES, "q8_0": Q8_0_BLOCK_BYTES}
+
+
+def _product_args(a, w_blob, N: int, K: int, fmt: str):
     af = _f32(a)
     if af.ndim == 1:
         af = af.reshape(1, -1)
-    M = af.shape[0]
     if af.shape[1] != K:
         raise ValueError("a has %d columns, K is %d" % (af.shape[1], K))
     wb = _u8(w_blob).reshape(-1)
-    if K % QK or wb.size != N * (K // QK) * Q4_0_BLOCK_BYTES:
+    if K % QK or wb.size != N * (K // QK) * _BLOCK_BYTES[fmt]:
         raise ValueError("weight blob does not match N=%d K=%d" % (N, K))
+    return af, wb
+
+
+def _matmul(fmt, a, w_blob, N, K, threads):
+    af, wb = _product_args(a, w_blob, N, K, fmt)
+    M = af.shape[0]
     y = np.zeros((M, N), dtype=np.float64)
     bound = np.zeros((M, N), dtype=np.float64)
     if M and N:
-        rc = _load().orc_q4_0_matmul(_ptr(af), _ptr(wb), M, N, K, _ptr(y), _ptr(bound),
-                                     int(threads))
+        rc = getattr(_load(), "orc_%s_matmul" % fmt)(_ptr(af), _ptr(wb), M, N, K, _ptr(y),
+                                                     _ptr(bound), int(threads))
         if rc:
             raise RuntimeError("oracle matmul failed (%d)" % rc)
     return y, bound
 
 
-def q4_0_matmul_sampled(a, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 0):
-    """The product at sampled outputs (m_idx[i], n_idx[i]); returns (y, B) as
-    float64 vectors of the same length."""
-    af = _f32(a)
-    if af.ndim == 1:
-        af = af.reshape(1, -1)
+def _matmul_sampled(fmt, a, w_blob, N, K, m_idx, n_idx, threads):
+    af, wb = _product_args(a, w_blob, N, K, fmt)
     M = af.shape[0]
-    if af.shape[1] != K:
-        raise ValueError("a has %d columns, K is %d" % (af.shape[1], K))
-    wb = _u8(w_blob).reshape(-1)
-    if K % QK or wb.size != N * (K // QK) * Q4_0_BLOCK_BYTES:
-        raise ValueError("weight blob does not match N=%d K=%d" % (N, K))
     mi = np.ascontiguousarray(m_idx, dtype=np.int64).reshape(-1)
     ni = np.ascontiguousarray(n_idx, dtype=np.int64).reshape(-1)
     if mi.size != ni.size:
@@ -203,11 +204,35 @@ def q4_0_matmul_sampled(a, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 
     y = np.zeros(mi.size, dtype=np.float64)
     bound = np.zeros(mi.size, dtype=np.float64)
     if mi.size:
-        rc = _load().orc_q4_0_matmul_sampled(_ptr(af), _ptr(wb), M, N, K, _ptr(mi), _ptr(ni),
-                                             mi.size, _ptr(y), _ptr(bound), int(threads))
+        rc = getattr(_load(), "orc_%s_matmul_sampled" % fmt)(
+            _ptr(af), _ptr(wb), M, N, K, _ptr(mi), _ptr(ni), mi.size, _ptr(y), _ptr(bound),
+            int(threads))
         if rc:
             raise RuntimeError("oracle sampled matmul failed (%d)" % rc)
     return y, bound
+
+
+def q4_0_matmul(a, w_blob, N: int, K: int, threads: int = 0):
+    """y[m, n] = sum_k a[m, k] * dequant(W)[n, k] in f64, and the bound
+    B[m, n] = sum_k |a[m, k] * w[n, k]|. a is [M, K] f32, W is the [N, K/32]
+    Q4_0 block stream. Returns (y, B), both float64 [M, N]."""
+    return _matmul("q4_0", a, w_blob, N, K, threads)
+
+
+def q4_0_matmul_sampled(a, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 0):
+    """The Q4_0 product at sampled outputs (m_idx[i], n_idx[i]); returns (y, B)
+    as float64 vectors of the same length."""
+    return _matmul_sampled("q4_0", a, w_blob, N, K, m_idx, n_idx, threads)
+
+
+def q8_0_matmul(a, w_blob, N: int, K: int, threads: int = 0):
+    """As q4_0_matmul, with W the [N, K/32] Q8_0 block stream."""
+    return _matmul("q8_0", a, w_blob, N, K, threads)
+
+
+def q8_0_matmul_sampled(a, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 0):
+    """As q4_0_matmul_sampled, with W the [N, K/32] Q8_0 block stream."""
+    return _matmul_sampled("q8_0", a, w_blob, N, K, m_idx, n_idx, threads)
 
 
 def max_threads() -> int:

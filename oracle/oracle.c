@@ -1,6 +1,6 @@
 /*
- * Plain CPU oracle for GGML Q4_0 / Q8_0 block quantization and the Q4_0 x f32
- * matrix product.
+ * Plain CPU oracle for GGML Q4_0 / Q8_0 block quantization and the
+ * Q4_0 x f32 and Q8_0 x f32 matrix products.
  *
  * TEST INFRASTRUCTURE. This file is the reference the GPU library is checked
  * against; it is not part of the product. Only the test suite, the smoke check
@@ -19,6 +19,10 @@
  *   - Q8_0 block and decode rule: section "dequant_q8_0".
  *   - Q8_0 quantize rule: section "quantize_q8_0".
  *   - Q4_0 x f32 product: sections "qmatvec_q4_0" and "matmul_q4_0_tiled".
+ *   - Q8_0 x f32 product: the same product over Q8_0 weights; the page's
+ *     quantized-matmul binding picks Q4_0 or Q8_0 blocks by quant type
+ *     (section "qmatvec_q4_0", as-built note), and a Q8_0 weight is the
+ *     value of section "dequant_q8_0".
  *   - Q4_0 quantize rule: not on the pages; it is GGML's reference rule as
  *     stated with the benchmark workloads (d = signed max-abs / -8,
  *     q = min(15, int(x/d + 8.5))). It only generates test weights.
@@ -191,14 +195,14 @@ void orc_q8_0_dequant(const uint8_t *blob, size_t n_blocks, float *out)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Q4_0 x f32 product ("qmatvec_q4_0", "matmul_q4_0_tiled"):
+/* Block-quantized x f32 product ("qmatvec_q4_0", "matmul_q4_0_tiled"):
  *   y[m, n] = sum_k a[m, k] * dequant(W)[n, k],
- * with a row-major [M, K] f32, W the row-major [N, K/32] Q4_0 block stream and
- * y row-major [M, N]. The weight is the dequantized Q4_0 value (the pages
+ * with a row-major [M, K] f32, W the row-major [N, K/32] block stream (Q4_0 or
+ * Q8_0) and y row-major [M, N]. The weight is the dequantized value (the pages
  * multiply by dequant(W)). The sum runs over k in ascending order in f64; each
- * product of an f32 activation and a dequantized weight (24 x 15 significant
- * bits) is exact in f64. bound[m, n] = sum_k |a[m, k] * w[n, k]| is the scale
- * of the parity tolerance. */
+ * product of an f32 activation and a dequantized weight (24 x at most 18
+ * significant bits) is exact in f64. bound[m, n] = sum_k |a[m, k] * w[n, k]| is
+ * the scale of the parity tolerance. */
 static void orc_dot_row(const float *arow, const float *wrow, int K,
                         double *y, double *bound)
 {
@@ -212,15 +216,19 @@ static void orc_dot_row(const float *arow, const float *wrow, int K,
     *bound = b;
 }
 
+/* Weight row n of the stream, dequantized into wrow[K]. */
+typedef void (*orc_dequant_fn)(const uint8_t *blob, size_t n_blocks, float *out);
+
 /* Full product. threads <= 0 means the OpenMP default; the parallel loop is
  * over independent output columns and changes no result. Returns 0, or 1 for
  * a shape that breaks K % 32 == 0, or 2 when scratch memory is unavailable. */
-int orc_q4_0_matmul(const float *a, const uint8_t *w, int M, int N, int K,
-                    double *y, double *bound, int threads)
+static int orc_matmul(const float *a, const uint8_t *w, int M, int N, int K,
+                      size_t block_bytes, orc_dequant_fn dequant,
+                      double *y, double *bound, int threads)
 {
     if (M < 0 || N < 0 || K < 0 || K % ORC_QK != 0)
         return 1;
-    size_t row_bytes = (size_t)(K / ORC_QK) * ORC_Q4_0_BLOCK_BYTES;
+    size_t row_bytes = (size_t)(K / ORC_QK) * block_bytes;
     int failed = 0;
     if (threads > 0)
         omp_set_num_threads(threads);
@@ -235,7 +243,7 @@ int orc_q4_0_matmul(const float *a, const uint8_t *w, int M, int N, int K,
         for (int n = 0; n < N; ++n) {
             if (!wrow)
                 continue;
-            orc_q4_0_dequant(w + (size_t)n * row_bytes, (size_t)(K / ORC_QK), wrow);
+            dequant(w + (size_t)n * row_bytes, (size_t)(K / ORC_QK), wrow);
             for (int m = 0; m < M; ++m)
                 orc_dot_row(a + (size_t)m * K, wrow, K,
                             y + (size_t)m * N + n, bound + (size_t)m * N + n);
@@ -247,16 +255,17 @@ int orc_q4_0_matmul(const float *a, const uint8_t *w, int M, int N, int K,
 
 /* The same product at a list of sampled outputs (m_idx[i], n_idx[i]), for
  * shapes too large to compute whole. */
-int orc_q4_0_matmul_sampled(const float *a, const uint8_t *w, int M, int N, int K,
-                            const int64_t *m_idx, const int64_t *n_idx,
-                            int64_t count, double *y, double *bound, int threads)
+static int orc_matmul_sampled(const float *a, const uint8_t *w, int M, int N, int K,
+                              size_t block_bytes, orc_dequant_fn dequant,
+                              const int64_t *m_idx, const int64_t *n_idx,
+                              int64_t count, double *y, double *bound, int threads)
 {
     if (M < 0 || N < 0 || K < 0 || K % ORC_QK != 0)
         return 1;
     for (int64_t i = 0; i < count; ++i)
         if (m_idx[i] < 0 || m_idx[i] >= M || n_idx[i] < 0 || n_idx[i] >= N)
             return 1;
-    size_t row_bytes = (size_t)(K / ORC_QK) * ORC_Q4_0_BLOCK_BYTES;
+    size_t row_bytes = (size_t)(K / ORC_QK) * block_bytes;
     int failed = 0;
     if (threads > 0)
         omp_set_num_threads(threads);
@@ -271,12 +280,40 @@ int orc_q4_0_matmul_sampled(const float *a, const uint8_t *w, int M, int N, int 
         for (int64_t i = 0; i < count; ++i) {
             if (!wrow)
                 continue;
-            orc_q4_0_dequant(w + (size_t)n_idx[i] * row_bytes, (size_t)(K / ORC_QK), wrow);
+            dequant(w + (size_t)n_idx[i] * row_bytes, (size_t)(K / ORC_QK), wrow);
             orc_dot_row(a + (size_t)m_idx[i] * K, wrow, K, y + i, bound + i);
         }
         free(wrow);
     }
     return failed ? 2 : 0;
+}
+
+int orc_q4_0_matmul(const float *a, const uint8_t *w, int M, int N, int K,
+                    double *y, double *bound, int threads)
+{
+    return orc_matmul(a, w, M, N, K, ORC_Q4_0_BLOCK_BYTES, orc_q4_0_dequant, y, bound, threads);
+}
+
+int orc_q4_0_matmul_sampled(const float *a, const uint8_t *w, int M, int N, int K,
+                            const int64_t *m_idx, const int64_t *n_idx,
+                            int64_t count, double *y, double *bound, int threads)
+{
+    return orc_matmul_sampled(a, w, M, N, K, ORC_Q4_0_BLOCK_BYTES, orc_q4_0_dequant,
+                              m_idx, n_idx, count, y, bound, threads);
+}
+
+int orc_q8_0_matmul(const float *a, const uint8_t *w, int M, int N, int K,
+                    double *y, double *bound, int threads)
+{
+    return orc_matmul(a, w, M, N, K, ORC_Q8_0_BLOCK_BYTES, orc_q8_0_dequant, y, bound, threads);
+}
+
+int orc_q8_0_matmul_sampled(const float *a, const uint8_t *w, int M, int N, int K,
+                            const int64_t *m_idx, const int64_t *n_idx,
+                            int64_t count, double *y, double *bound, int threads)
+{
+    return orc_matmul_sampled(a, w, M, N, K, ORC_Q8_0_BLOCK_BYTES, orc_q8_0_dequant,
+                              m_idx, n_idx, count, y, bound, threads);
 }
 
 /* Threads OpenMP will use for the next parallel region (for reporting). */

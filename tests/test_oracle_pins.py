@@ -12,10 +12,13 @@ oracle fails a test here:
   sections dequant_q4_0, dequant_q8_0 and quantize_q8_0), the closed form of the
   Q4_0 decode over every (scale, nibble) pair, and brute-force nearest-code
   searches for both quantizers.
-* The product (sections qmatvec_q4_0 and matmul_q4_0_tiled): exact rational
-  sums on tiny shapes, ``math.fsum`` on medium ones, closed forms (one-hot
-  activations, all-8 nibbles, the ramp block, integer data) and linearity, with
-  weights packed here from the layout definition rather than by the oracle.
+* Q8_0 decode: the closed form over every (scale, code) pair.
+* The products (sections qmatvec_q4_0 and matmul_q4_0_tiled; with Q8_0 weights
+  the same sum over the dequant_q8_0 values): exact rational sums on tiny
+  shapes, ``math.fsum`` on medium ones, closed forms (one-hot activations,
+  all-8 nibbles or all-zero bytes, the ramp block, integer data) and linearity,
+  with weights packed here from the layout definition rather than by the
+  oracle.
 """
 import json
 import math
@@ -236,6 +239,22 @@ def test_q8_0_round_trip(orc):
     assert (np.abs(back - xb) <= lim[:, None]).all()
 
 
+def test_q8_0_dequant_every_scale_and_code(orc):
+    # Eight blocks per f16 bit pattern of d carry the 256 signed codes -128..127
+    # in order, so every (d, code) pair appears once.
+    codes = np.arange(-128, 128, dtype=np.int64)
+    qs = [codes[32 * i:32 * i + 32].astype(np.int8).tobytes() for i in range(8)]
+    blob = b"".join(h.to_bytes(2, "little") + q for h in range(65536) for q in qs)
+    out = orc.q8_0_dequant(blob).reshape(65536, 256)
+    d = np.array([_f16_value(h) for h in range(65536)], dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        exact = codes.astype(np.float64)[None, :] * d[:, None]   # exact: 8-bit x 11-bit
+    exp32 = exact.astype(np.float32)                              # exact in f32 as well
+    nan = np.isnan(exp32)
+    assert (np.isnan(out) == nan).all()
+    assert (_bits32(out[~nan]) == _bits32(exp32[~nan])).all()     # signed zeros too
+
+
 # ------------------------------------------------------------------- product
 
 def _random_scales(seed, n):
@@ -246,23 +265,59 @@ def _random_scales(seed, n):
     return (sign | expo | mant).astype(np.uint16)
 
 
-def _weights_f64(codes, dbits):
+def _pack_q8_0(codes, dbits):
+    """Build a [N, K/32] Q8_0 stream from signed codes[N, K] in -128..127 and f16
+    scale bits dbits[N, K/32], straight from the layout definition: f16 d
+    little-endian, then byte j = element j in two's complement."""
+    codes = np.asarray(codes, dtype=np.int64)
+    N, K = codes.shape
+    nb = K // 32
+    blob = np.zeros((N, nb, 34), dtype=np.uint8)
+    dbits = np.asarray(dbits, dtype=np.uint16).reshape(N, nb)
+    blob[:, :, 0] = (dbits & 0xFF).astype(np.uint8)
+    blob[:, :, 1] = (dbits >> 8).astype(np.uint8)
+    blob[:, :, 2:] = (codes.reshape(N, nb, 32) & 0xFF).astype(np.uint8)
+    return blob.reshape(-1)
+
+
+# Per weight format: code range [low, high), the code whose weight is zero,
+# the packer and the oracle product. Q4_0 weights are (code - 8) d, Q8_0
+# weights code d.
+FORMATS = {
+    "q4_0": dict(low=0, high=16, zero=8, pack=_pack_q4_0, matmul="q4_0_matmul"),
+    "q8_0": dict(low=-128, high=128, zero=0, pack=_pack_q8_0, matmul="q8_0_matmul"),
+}
+
+
+def _weights_f64(codes, dbits, fmt="q4_0"):
     """Dequantized weights from the layout definition, in f64 (exact)."""
     N, K = codes.shape
     d = np.array([_f16_value(h) for h in np.asarray(dbits).reshape(-1)], dtype=np.float64)
     d = d.reshape(N, K // 32)
-    return (codes.astype(np.float64) - 8.0) * np.repeat(d, 32, axis=1)
+    return (codes.astype(np.float64) - FORMATS[fmt]["zero"]) * np.repeat(d, 32, axis=1)
 
 
+def _product_case(fmt, seed, N, K, dbits=None, codes=None):
+    F = FORMATS[fmt]
+    if codes is None:
+        codes = wl.uniform_ints(seed, F["low"], F["high"], (N, K))
+    if dbits is None:
+        dbits = _random_scales(seed + 3, N * (K // 32))
+    return codes, dbits, F["pack"](codes, dbits)
+
+
+def _matmul(orc, fmt):
+    return getattr(orc, FORMATS[fmt]["matmul"])
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 5, 32), (2, 4, 64), (3, 5, 96)])
-def test_product_exact_rational(orc, M, N, K):
+def test_product_exact_rational(orc, fmt, M, N, K):
     seed = 100 * M + 10 * N + K
-    codes = wl.uniform_ints(seed, 0, 16, (N, K))
-    dbits = _random_scales(seed + 3, N * (K // 32))
-    blob = _pack_q4_0(codes, dbits)
+    codes, dbits, blob = _product_case(fmt, seed, N, K)
     a = wl.normal_f32(seed + 7, (M, K), 3.0)
-    w = _weights_f64(codes, dbits)
-    y, bound = orc.q4_0_matmul(a, blob, N, K)
+    w = _weights_f64(codes, dbits, fmt)
+    y, bound = _matmul(orc, fmt)(a, blob, N, K)
     for m in range(M):
         for n in range(N):
             exact = sum(Fraction(float(a[m, k])) * Fraction(w[n, k]) for k in range(K))
@@ -271,14 +326,13 @@ def test_product_exact_rational(orc, M, N, K):
             assert abs(Fraction(bound[m, n]) - babs) <= Fraction(1, 10 ** 12) * babs
 
 
-def test_product_fsum(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_product_fsum(orc, fmt):
     M, N, K = 4, 37, 1024
-    codes = wl.uniform_ints(41, 0, 16, (N, K))
-    dbits = _random_scales(42, N * (K // 32))
-    blob = _pack_q4_0(codes, dbits)
+    codes, dbits, blob = _product_case(fmt, 41, N, K)
     a = wl.normal_f32(43, (M, K), 1.0)
-    w = _weights_f64(codes, dbits)
-    y, bound = orc.q4_0_matmul(a, blob, N, K)
+    w = _weights_f64(codes, dbits, fmt)
+    y, bound = _matmul(orc, fmt)(a, blob, N, K)
     for m in range(M):
         for n in range(N):
             prods = [float(a[m, k]) * float(w[n, k]) for k in range(K)]   # exact in f64
@@ -288,27 +342,28 @@ def test_product_fsum(orc):
             assert abs(bound[m, n] - babs) <= K * 2.0 ** -53 * babs
 
 
-def test_product_one_hot_picks_the_weight(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_product_one_hot_picks_the_weight(orc, fmt):
     N, K = 9, 128
-    codes = wl.uniform_ints(51, 0, 16, (N, K))
-    dbits = _random_scales(52, N * (K // 32))
-    blob = _pack_q4_0(codes, dbits)
-    w = _weights_f64(codes, dbits)
+    codes, dbits, blob = _product_case(fmt, 51, N, K)
+    w = _weights_f64(codes, dbits, fmt)
     ks = [0, 17, 31, 32, 77, 127]
     a = np.zeros((len(ks), K), dtype=np.float32)
     for m, k in enumerate(ks):
         a[m, k] = 1.0
-    y, _ = orc.q4_0_matmul(a, blob, N, K)
+    y, _ = _matmul(orc, fmt)(a, blob, N, K)
     for m, k in enumerate(ks):
         assert (y[m] == w[:, k]).all()
 
 
-def test_product_all_eights_is_zero(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_product_zero_codes_give_zero(orc, fmt):
+    # All nibbles 8 (Q4_0) or all bytes 0 (Q8_0): every weight is zero.
     N, K = 5, 256
-    codes = np.full((N, K), 8, dtype=np.int64)
-    blob = _pack_q4_0(codes, _random_scales(61, N * K // 32))
+    codes = np.full((N, K), FORMATS[fmt]["zero"], dtype=np.int64)
+    _, _, blob = _product_case(fmt, 61, N, K, codes=codes)
     a = wl.normal_f32(62, (3, K), 10.0)
-    y, bound = orc.q4_0_matmul(a, blob, N, K)
+    y, bound = _matmul(orc, fmt)(a, blob, N, K)
     assert (y == 0).all() and (bound == 0).all()
 
 
@@ -319,56 +374,59 @@ def test_product_ramp_block(orc):
     assert bound[0, 0] == 254.0                          # 128 + 126: the clamped top element is 14
 
 
-def test_product_integer_data_is_exact(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_product_integer_data_is_exact(orc, fmt):
     M, N, K = 3, 6, 192
-    codes = wl.uniform_ints(71, 0, 16, (N, K))
     dbits = np.full(N * K // 32, 0x3C00, dtype=np.uint16)   # d = 1.0
-    blob = _pack_q4_0(codes, dbits)
+    codes, _, blob = _product_case(fmt, 71, N, K, dbits=dbits)
     ai = wl.uniform_ints(72, -100, 101, (M, K))
-    y, _ = orc.q4_0_matmul(ai.astype(np.float32), blob, N, K)
-    ref = ai @ (codes - 8).T                                  # Python/numpy integers
+    y, _ = _matmul(orc, fmt)(ai.astype(np.float32), blob, N, K)
+    ref = ai @ (codes - FORMATS[fmt]["zero"]).T               # numpy integers
     assert (y == ref.astype(np.float64)).all()
 
 
-def test_product_is_linear_in_a(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_product_is_linear_in_a(orc, fmt):
     M, N, K = 2, 11, 320
-    codes = wl.uniform_ints(81, 0, 16, (N, K))
-    blob = _pack_q4_0(codes, _random_scales(82, N * K // 32))
+    _, _, blob = _product_case(fmt, 81, N, K)
+    mm = _matmul(orc, fmt)
     a1 = wl.normal_f32(83, (M, K)).astype(np.float32)
     a2 = wl.normal_f32(84, (M, K)).astype(np.float32)
     a1[:, ::2] = 0.0                                          # disjoint supports keep
     a2[:, 1::2] = 0.0                                         # 2*a1 + 4*a2 exact in f32
-    y1, b1 = orc.q4_0_matmul(a1, blob, N, K)
-    y2, b2 = orc.q4_0_matmul(a2, blob, N, K)
-    y3, _ = orc.q4_0_matmul(2 * a1 + 4 * a2, blob, N, K)     # exact scalings by 2 and 4
+    y1, b1 = mm(a1, blob, N, K)
+    y2, b2 = mm(a2, blob, N, K)
+    y3, _ = mm(2 * a1 + 4 * a2, blob, N, K)                  # exact scalings by 2 and 4
     assert np.all(np.abs(y3 - (2 * y1 + 4 * y2)) <= 1e-12 * (2 * b1 + 4 * b2))
 
 
-def test_product_rows_and_columns_not_transposed(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_product_rows_and_columns_not_transposed(orc, fmt):
     # Distinct per-row scales and per-column activations: a transposed operand or
     # a swapped index gives a different matrix.
     M, N, K = 3, 4, 64
-    codes = np.full((N, K), 9, dtype=np.int64)                # weight (9 - 8) * d = d
+    codes = np.full((N, K), FORMATS[fmt]["zero"] + 1, dtype=np.int64)   # weight = d
     dvals = [1.0, 2.0, 4.0, 8.0]
     dbits = np.array([[np.float16(v).view(np.uint16)] * (K // 32) for v in dvals]).reshape(-1)
-    blob = _pack_q4_0(codes, dbits)
+    _, _, blob = _product_case(fmt, 0, N, K, dbits=dbits, codes=codes)
     a = np.zeros((M, K), dtype=np.float32)
     a[0, :] = 1.0
     a[1, :32] = 1.0
     a[2, 63] = 3.0
-    y, _ = orc.q4_0_matmul(a, blob, N, K)
+    y, _ = _matmul(orc, fmt)(a, blob, N, K)
     assert y.tolist() == [[64.0, 128.0, 256.0, 512.0], [32.0, 64.0, 128.0, 256.0], [3.0, 6.0, 12.0, 24.0]]
 
 
-def test_sampled_equals_full(orc):
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_sampled_equals_full(orc, fmt):
     M, N, K = 5, 33, 256
     x = wl.weights_f32(91, N, K)
-    blob = orc.q4_0_quantize(x)
+    blob = getattr(orc, fmt + "_quantize")(x)
     a = wl.activations_f32(92, M, K)
-    y, b = orc.q4_0_matmul(a, blob, N, K)
+    y, b = _matmul(orc, fmt)(a, blob, N, K)
     mi = wl.uniform_ints(93, 0, M, 50)
     ni = wl.uniform_ints(94, 0, N, 50)
-    ys, bs = orc.q4_0_matmul_sampled(a, blob, N, K, mi, ni)
+    ys, bs = getattr(orc, fmt + "_matmul_sampled")(a, blob, N, K, mi, ni)
     assert (ys == y[mi, ni]).all() and (bs == b[mi, ni]).all()
 
 

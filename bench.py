@@ -1,4 +1,4 @@
-"""Benchmark of the Q4_0 hot path on one MI355X.
+"""Benchmark of the Q4_0 (and Q8_0-weight) hot path on one MI355X.
 
 Headline (the JSON line's ``value``): the decode GEMV y[1, 4096] =
 a[1, 4096] @ dequant(W[4096, 4096])^T, as whole-job GB/s of algorithmic
@@ -17,7 +17,8 @@ the inter-kernel gap and is never shorter than the kernel itself).
 Every other row of the path is measured the same way and reported under
 ``rows``: the 8-row GEMV, the prefill GEMMs (1024 x 4096 x 4096 and
 2048 x 14336 x 4096), a warm-cache GEMV, the dequant of the 14336 x 4096 weight
-and the Q8_0 quantize of a 2048 x 4096 tensor.
+and the Q8_0 quantize of a 2048 x 4096 tensor; then the GEMVs, GEMMs and
+dequant again over Q8_0 weights.
 
 ``roofline.traffic`` comes from the committed counter summary
 profiles/traffic.json (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy of
@@ -137,59 +138,69 @@ def hbm_roofline(algo_bytes, kernel_us, workload, kernel, kind):
 
 # ------------------------------------------------------------------- rows
 
-def make_q4_weight(torch, q4, wl, N, K, seed):
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+FMT_TYPE = {"q4_0": "FmtQ4_0", "q8_0": "FmtQ8_0"}
+
+
+def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
+    """The workload's f32 weights quantized on the device (q4_quantize or
+    q8_quantize)."""
     w32 = torch.from_numpy(wl.weights_f32(seed, N, K)).cuda()
-    blob = torch.empty(N * (K // 32) * 18, dtype=torch.uint8, device="cuda")
-    q4.q4_quantize(w32, blob)
+    blob = torch.empty(N * (K // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device="cuda")
+    (q4.q4_quantize if fmt == "q4_0" else q4.q8_quantize)(w32, blob)
     torch.cuda.synchronize()
     del w32
     return blob
 
 
-def gemv_kernel_name(M, K):
+def gemv_kernel_name(M, K, fmt="q4_0"):
     if K % 256:
-        return "k_gemv_q4_0<%d>" % M
+        return "k_gemv<%s, %d>" % (FMT_TYPE[fmt], M)
     nblk = K // 32
     per = (((nblk + 7) // 8) + 7) & ~7
     last = nblk - (nblk - 1) // per * per
     ch = 16 if (M <= 4 and per % 16 == 0 and last % 16 == 0) else 8
-    return "k_gemv_q4_0_stream<%d, 8, %d>" % (M, ch)
+    return "k_gemv_stream<%s, %d, 8, %d>" % (FMT_TYPE[fmt], M, ch)
 
 
-def gemm_kernel_name(K):
-    return "k_gemm_q4_0_split" if K % 64 == 0 else "k_gemm_q4_0_any"
+def gemm_kernel_name(K, fmt="q4_0"):
+    return "k_gemm_split<%s>" % FMT_TYPE[fmt] if K % 64 == 0 else "k_gemm_any<%s>" % FMT_TYPE[fmt]
 
 
 def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     s = wl.WORKLOADS[name]
     M, N, K = s["M"], s["N"], s["K"]
-    blob = make_q4_weight(torch, q4, wl, N, K, s["w_seed"])
+    fmt = s.get("fmt", "q4_0")
+    f = fmt[:2]
+    blob = make_weight(torch, q4, wl, N, K, s["w_seed"], fmt)
     a = torch.from_numpy(wl.activations_f32(s["a_seed"], M, K)).cuda()
     y = torch.empty(M * N, dtype=torch.float32, device="cuda")
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
     if s["kind"] == "gemv":
-        fn = lambda k: q4.q4_gemv(a, blobs[k % R], y, M, N, K)
+        gemv = getattr(q4, f + "_gemv")
+        fn = lambda k: gemv(a, blobs[k % R], y, M, N, K)
     else:
-        ws_bytes = q4.q4_gemm_workspace_bytes(M, N, K)
+        gemm = getattr(q4, f + "_gemm")
+        ws_bytes = getattr(q4, f + "_gemm_workspace_bytes")(M, N, K)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-        fn = lambda k: q4.q4_gemm(a, blobs[k % R], y, M, N, K, workspace=ws)
+        fn = lambda k: gemm(a, blobs[k % R], y, M, N, K, workspace=ws)
     t = run_timed(torch, fn, steps, warmup)
     algo_bytes = wbytes + M * K * 4 + M * N * 4
     flops = 2.0 * M * N * K
     kern_s = t["kernel_us"] * 1e-6
-    row = {"workload": name, "M": M, "N": N, "K": K, "weight_copies": R,
+    row = {"workload": name, "format": fmt, "M": M, "N": N, "K": K, "weight_copies": R,
            "cache": "cold" if R > 1 else "warm (one weight copy, MALL-resident)",
            "algorithmic_bytes": algo_bytes, "flops": flops, **t,
            "kernel_GBs": algo_bytes / kern_s / 1e9, "kernel_TFLOPs": flops / kern_s / 1e12,
            "job_GBs": algo_bytes * steps / t["wall_s"] / 1e9,
            "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
     if s["kind"] == "gemv":
-        kernel = gemv_kernel_name(M, K)
+        kernel = gemv_kernel_name(M, K, fmt)
         row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
     else:
-        kernel = gemm_kernel_name(K)
+        kernel = gemm_kernel_name(K, fmt)
         row["roofline"] = {"bound": "mfma", "achieved": row["kernel_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": row["kernel_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
@@ -205,20 +216,22 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     return row
 
 
-def bench_dequant(torch, q4, wl, steps, warmup):
-    s = wl.WORKLOADS["dequant_14336x4096"]
+def bench_dequant(torch, q4, wl, steps, warmup, name="dequant_14336x4096"):
+    s = wl.WORKLOADS[name]
     N, K = s["N"], s["K"]
-    blob = make_q4_weight(torch, q4, wl, N, K, s["w_seed"])
+    fmt = s.get("fmt", "q4_0")
+    blob = make_weight(torch, q4, wl, N, K, s["w_seed"], fmt)
     outs = [torch.empty(N * K, dtype=torch.float32, device="cuda") for _ in range(2)]
-    fn = lambda k: q4.q4_dequant(blob, outs[k % 2])
+    dequant = getattr(q4, fmt[:2] + "_dequant")
+    fn = lambda k: dequant(blob, outs[k % 2])
     t = run_timed(torch, fn, steps, warmup)
     algo = blob.numel() + N * K * 4
     kern_s = t["kernel_us"] * 1e-6
-    row = {"workload": "dequant_14336x4096", "kernel": "k_dequant_q4_0",
-           "cache": "cold (268 MB per call)", "algorithmic_bytes": algo, **t,
+    kernel = "k_dequant_" + fmt
+    row = {"workload": name, "format": fmt, "kernel": kernel,
+           "cache": "cold (%d MB per call)" % round(algo / 1e6), "algorithmic_bytes": algo, **t,
            "kernel_GBs": algo / kern_s / 1e9, "job_GBs": algo * steps / t["wall_s"] / 1e9}
-    row["roofline"] = hbm_roofline(algo, t["kernel_us"], "dequant_14336x4096", "k_dequant_q4_0",
-                                   "dequant")
+    row["roofline"] = hbm_roofline(algo, t["kernel_us"], name, kernel, "dequant")
     del blob, outs
     torch.cuda.empty_cache()
     return row
@@ -347,6 +360,16 @@ def main():
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10)))
         log("row: Q8_0 quantize 2048x4096")
         rows.append(bench_quantize(torch, q4, wl, args.steps, args.warmup))
+        # The same path over Q8_0 weights.
+        for name, st in (("q8_0_gemv_1x4096x4096", args.steps),
+                         ("q8_0_gemv_8x4096x4096", args.steps),
+                         ("q8_0_gemm_1024x4096x4096", 50), ("q8_0_gemm_2048x14336x4096", 20)):
+            log("row: %s" % name)
+            rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
+                                      min(args.warmup, 10)))
+        log("row: Q8_0 dequant 14336x4096")
+        rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10),
+                                  "q8_0_dequant_14336x4096"))
     # Measured ceilings: a plain streaming read of the headline's bytes in the
     # same harness (cold), and of 1 GiB (the chip's sustained read rate).
     log("row: streaming-read ceilings")

@@ -30,7 +30,8 @@ SIZE_MAX = 2 ** 64 - 1
 
 #: Every symbol include/q4.h declares.
 EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
-           "q4_gemm_workspace_bytes", "q8_quantize", "q4_quantize")
+           "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm",
+           "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize")
 
 
 class Q4Error(RuntimeError):
@@ -55,14 +56,15 @@ def _load_library():
     lib.q4_abi_version.argtypes = []
     lib.q4_status_string.restype = ctypes.c_char_p
     lib.q4_status_string.argtypes = [i32]
-    lib.q4_dequant.restype = i32
-    lib.q4_dequant.argtypes = [P, sz, P, sz, P]
-    lib.q4_gemv.restype = i32
-    lib.q4_gemv.argtypes = [P, P, sz, P, i32, i32, i32, P]
-    lib.q4_gemm.restype = i32
-    lib.q4_gemm.argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
-    lib.q4_gemm_workspace_bytes.restype = sz
-    lib.q4_gemm_workspace_bytes.argtypes = [i32, i32, i32]
+    for f in ("q4", "q8"):
+        getattr(lib, f + "_dequant").restype = i32
+        getattr(lib, f + "_dequant").argtypes = [P, sz, P, sz, P]
+        getattr(lib, f + "_gemv").restype = i32
+        getattr(lib, f + "_gemv").argtypes = [P, P, sz, P, i32, i32, i32, P]
+        getattr(lib, f + "_gemm").restype = i32
+        getattr(lib, f + "_gemm").argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
+        getattr(lib, f + "_gemm_workspace_bytes").restype = sz
+        getattr(lib, f + "_gemm_workspace_bytes").argtypes = [i32, i32, i32]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -108,22 +110,44 @@ def q4_status_string(status: int) -> str:
     return lib.q4_status_string(int(status)).decode()
 
 
-def q4_dequant(w_q, out, w_bytes=None, out_elems=None, stream=None) -> None:
-    """Q4_0 blocks (uint8 tensor) -> f32 ``out``; sizes default to the tensors'."""
+def _dequant(entry, w_q, out, w_bytes, out_elems, stream) -> None:
     wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
     oe = int(out.numel()) if out_elems is None else int(out_elems)
-    _check(lib.q4_dequant(_addr(w_q), wb, _addr(out), oe, _stream(stream)), "q4_dequant")
+    _check(getattr(lib, entry)(_addr(w_q), wb, _addr(out), oe, _stream(stream)), entry)
+
+
+def q4_dequant(w_q, out, w_bytes=None, out_elems=None, stream=None) -> None:
+    """Q4_0 blocks (uint8 tensor) -> f32 ``out``; sizes default to the tensors'."""
+    _dequant("q4_dequant", w_q, out, w_bytes, out_elems, stream)
+
+
+def q8_dequant(w_q, out, w_bytes=None, out_elems=None, stream=None) -> None:
+    """Q8_0 blocks (uint8 tensor) -> f32 ``out``; sizes default to the tensors'."""
+    _dequant("q8_dequant", w_q, out, w_bytes, out_elems, stream)
+
+
+def _gemv(entry, a, w_q, y, M, N, K, w_bytes, stream) -> None:
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    _check(getattr(lib, entry)(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                               _stream(stream)), entry)
 
 
 def q4_gemv(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
-    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for 1 <= M <= 8."""
-    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
-    _check(lib.q4_gemv(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
-                       _stream(stream)), "q4_gemv")
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for 1 <= M <= 8, W Q4_0."""
+    _gemv("q4_gemv", a, w_q, y, M, N, K, w_bytes, stream)
+
+
+def q8_gemv(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for 1 <= M <= 8, W Q8_0."""
+    _gemv("q8_gemv", a, w_q, y, M, N, K, w_bytes, stream)
 
 
 def q4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib.q4_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def q8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q8_gemm_workspace_bytes(int(M), int(N), int(K)))
 
 
 def _scratch(nbytes: int, stream, like):
@@ -140,25 +164,36 @@ def _scratch(nbytes: int, stream, like):
     return t
 
 
-def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
-            workspace_bytes=None) -> None:
-    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M.
-
-    ``workspace=None`` takes a scratch tensor of q4_gemm_workspace_bytes(M, N, K)
-    bytes from PyTorch's caching allocator for this call; pass a tensor (or an
-    address with ``workspace_bytes``) to reuse one."""
+def _gemm(fmt, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes) -> None:
+    entry = fmt + "_gemm"
     wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
     ws = workspace
     if ws is None:
-        need = q4_gemm_workspace_bytes(M, N, K)
+        need = int(getattr(lib, entry + "_workspace_bytes")(int(M), int(N), int(K)))
         if 0 < need < SIZE_MAX:
             ws = _scratch(need, stream, y)
     if workspace_bytes is not None:
         wsb = int(workspace_bytes)
     else:
         wsb = _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0
-    _check(lib.q4_gemm(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K), _addr(ws), wsb,
-                       _stream(stream)), "q4_gemm")
+    _check(getattr(lib, entry)(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                               _addr(ws), wsb, _stream(stream)), entry)
+
+
+def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+            workspace_bytes=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M, W Q4_0.
+
+    ``workspace=None`` takes a scratch tensor of q4_gemm_workspace_bytes(M, N, K)
+    bytes from PyTorch's caching allocator for this call; pass a tensor (or an
+    address with ``workspace_bytes``) to reuse one."""
+    _gemm("q4", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+
+
+def q8_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+            workspace_bytes=None) -> None:
+    """As q4_gemm, with W a Q8_0 stream (workspace from q8_gemm_workspace_bytes)."""
+    _gemm("q8", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
 
 
 def q8_quantize(x, out_q, n_elems=None, out_bytes=None, stream=None) -> None:

@@ -29,30 +29,70 @@ Q4_EXPORT const char *q4_status_string(int status)
     case Q4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case Q4_ERR_ALIAS: return "an output overlaps an input";
     case Q4_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
-    case Q4_ERR_WORKSPACE: return "the workspace is smaller than q4_gemm_workspace_bytes";
+    case Q4_ERR_WORKSPACE: return "the workspace is smaller than the GEMM's workspace_bytes function asks";
     default: return "unknown status";
     }
 }
 
-Q4_EXPORT int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream)
+// Shared bodies of the Q4_0 and Q8_0 entry points.
+static int dequant(q4k::WeightFormat fmt, size_t block_bytes, const void *w_q, size_t w_bytes,
+                   float *out, size_t out_elems, void *stream)
 {
     bool empty = false;
-    int st = q4v::check_dequant(w_q, w_bytes, out, out_elems, &empty);
+    int st = q4v::check_dequant(w_q, w_bytes, out, out_elems, block_bytes, &empty);
     if (st != Q4_OK || empty)
         return st;
-    return launched(q4k::launch_dequant(static_cast<const uint8_t *>(w_q), w_bytes / 18, out,
-                                        as_stream(stream)));
+    return launched(q4k::launch_dequant(fmt, static_cast<const uint8_t *>(w_q), w_bytes / block_bytes,
+                                        out, as_stream(stream)));
+}
+
+static int gemv(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const void *w_q,
+                size_t w_bytes, float *y, int M, int N, int K, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS, block_bytes, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemv(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                     as_stream(stream)));
+}
+
+static int gemm(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const void *w_q,
+                size_t w_bytes, float *y, int M, int N, int K, void *workspace,
+                size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, 0, block_bytes, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    st = q4v::check_workspace(a, w_q, w_bytes, y, M, N, K, workspace, workspace_bytes);
+    if (st != Q4_OK)
+        return st;
+    return launched(q4k::launch_gemm(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                     q4v::gemm_splits_activations(K) ? workspace : nullptr,
+                                     as_stream(stream)));
+}
+
+Q4_EXPORT int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream)
+{
+    return dequant(q4k::WeightFormat::kQ4_0, 18, w_q, w_bytes, out, out_elems, stream);
+}
+
+Q4_EXPORT int q8_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream)
+{
+    return dequant(q4k::WeightFormat::kQ8_0, 34, w_q, w_bytes, out, out_elems, stream);
 }
 
 Q4_EXPORT int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
                       void *stream)
 {
-    bool empty = false;
-    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS, &empty);
-    if (st != Q4_OK || empty)
-        return st;
-    return launched(q4k::launch_gemv(a, static_cast<const uint8_t *>(w_q), y, M, N, K,
-                                     as_stream(stream)));
+    return gemv(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT int q8_gemv(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                      void *stream)
+{
+    return gemv(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, stream);
 }
 
 Q4_EXPORT size_t q4_gemm_workspace_bytes(int M, int N, int K)
@@ -60,19 +100,23 @@ Q4_EXPORT size_t q4_gemm_workspace_bytes(int M, int N, int K)
     return q4v::gemm_workspace_bytes(M, N, K);
 }
 
+Q4_EXPORT size_t q8_gemm_workspace_bytes(int M, int N, int K)
+{
+    return q4v::gemm_workspace_bytes(M, N, K);
+}
+
 Q4_EXPORT int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
                       void *workspace, size_t workspace_bytes, void *stream)
 {
-    bool empty = false;
-    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, 0, &empty);
-    if (st != Q4_OK || empty)
-        return st;
-    st = q4v::check_workspace(a, w_q, w_bytes, y, M, N, K, workspace, workspace_bytes);
-    if (st != Q4_OK)
-        return st;
-    return launched(q4k::launch_gemm(a, static_cast<const uint8_t *>(w_q), y, M, N, K,
-                                     q4v::gemm_splits_activations(K) ? workspace : nullptr,
-                                     as_stream(stream)));
+    return gemm(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, workspace,
+                workspace_bytes, stream);
+}
+
+Q4_EXPORT int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, workspace,
+                workspace_bytes, stream);
 }
 
 Q4_EXPORT int q8_quantize(const float *x, size_t n_elems, void *out_q, size_t out_bytes, void *stream)

@@ -1,25 +1,27 @@
-// Prefill-shaped Q4_0 x f32 product, y[m, n] = sum_k a[m, k] * w[n, k] for any
-// M, tiled through LDS onto gfx950 matrix cores.
+// Prefill-shaped block-quantized x f32 product, y[m, n] = sum_k a[m, k] w[n, k]
+// for any M, tiled through LDS onto gfx950 matrix cores, for Q4_0 and Q8_0
+// weight streams.
 //
 // Operation: docs.rs fuel-dispatch, "quantized (GGML) kernel contracts",
 // section matmul_q4_0_tiled (M > 1, 2 M N K flops, the weight streamed once
-// per column block and reused across the rows of a tile), with the Q4_0 block
-// of section dequant_q4_0.
+// per column block and reused across the rows of a tile), with the blocks of
+// sections dequant_q4_0 and dequant_q8_0 (the quantized-matmul binding picks
+// either by quant type).
 //
-// Design
-// ------
+// General kernel (k_gemm_any, any K % 32 == 0)
+// -------------------------------------------
 // * A 256-thread workgroup computes a 128 x 128 tile of y; its four wavefronts
 //   each own a 64 x 64 quadrant as 4 x 4 tiles of v_mfma_f32_16x16x32_f16.
-//   K advances one Q4_0 block (32 elements) per step.
+//   K advances one block (32 elements) per step.
 // * Per step the workgroup stages, in LDS, the activation slab a[128 x 32] as
 //   binary16 hi = f16(a) and lo = f16((a - hi) * 2^11), and the weight slab as
-//   the exact binary16 integers (q - 8) plus the same values times 2^-11, with
+//   the exact binary16 weight codes plus the same values times 2^-11, with
 //   the f32 scales d of the 128 weight rows. For a in [2^e, 2^(e+1)) the
 //   residual a - hi is at most 2^(e-11), so lo is at most 2^e <= |a|: no
 //   overflow for |a| < 65504, and lo stays a normal binary16 unless the
-//   residual is below 2^-25. The matching 2^-11 on the weights ((q - 8) 2^-11
-//   is exact) makes hi * (q - 8) + lo * (q - 8) 2^-11 equal a (q - 8) to about
-//   2^-22 relative (2^-36 absolute at worst), so both land in one MFMA chain.
+//   residual is below 2^-25. The matching 2^-11 on the weights (exact) makes
+//   hi * c + lo * c 2^-11 equal a c to about 2^-22 relative, so both land in
+//   one MFMA chain.
 // * Every 16 x 16 tile's block partial is scaled by its column's d into an f32
 //   accumulator (d * C + acc): block partial -> scale -> sum of blocks.
 // * Two LDS stages with the next step's global loads issued before the current
@@ -27,9 +29,13 @@
 // * Tiles are renumbered so that each of the chip's 8 XCDs (which receive
 //   workgroups round-robin) works on a contiguous run of tiles sharing the
 //   same activation rows, which then stay in that XCD's L2.
+// The slot order of the operands and the decode of the weight bytes are the
+// format's (formats.h); where the decode leaves a factor 2^kHiLog2 on slots
+// 4..7 (Q4_0), the activations of those slots carry 2^-kHiLog2.
 #include <type_traits>
 
 #include "device_common.h"
+#include "formats.h"
 #include "launch.h"
 #include "validate.h"
 
@@ -40,51 +46,17 @@ constexpr int kGemmBN = 128;
 constexpr int kGemmThreads = 256;
 constexpr int kEntries = 8 * 4 * 16;   // 16-row subtiles x k-groups x rows: 512 x 16 bytes
 
-// B operand for qs dword x (bytes 4g..4g+3 of a block): slots hold (q - 8) of
-// elements 4g+0, 4g+2, 4g+1, 4g+3, 16+4g+0, 16+4g+2, 16+4g+1, 16+4g+3.
-// magic is the exponent pattern of 1024.0 in both halves (0x64006400); kept in
-// a VGPR, each (field & mask) | magic is one v_and_or_b32.
-__device__ __forceinline__ f16x8 decode_plain(uint32_t x, uint32_t magic = 0x64006400u)
-{
-    const uint32_t v0 = (x & 0x000F000Fu) | magic;
-    const uint32_t v1 = ((x >> 8) & 0x000F000Fu) | magic;
-    const uint32_t v2 = ((x >> 4) & 0x000F000Fu) | magic;
-    const uint32_t v3 = ((x >> 12) & 0x000F000Fu) | magic;
-    const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
-    f16x2 h0 = bitcast<f16x2>(v0) - bias;
-    f16x2 h1 = bitcast<f16x2>(v1) - bias;
-    f16x2 h2 = bitcast<f16x2>(v2) - bias;
-    f16x2 h3 = bitcast<f16x2>(v3) - bias;
-    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
-
-// B operand for qs dword x as decode_plain, but with the high nibbles decoded
-// in place: slots 4..7 hold 16 (q - 8) (one shift instead of three). The
-// split-activation path pairs it with activations that carry a / 16 there.
-__device__ __forceinline__ f16x8 decode_x16m(uint32_t x, uint32_t magic)
-{
-    const uint32_t t = x >> 8;
-    const uint32_t v0 = (x & 0x000F000Fu) | magic;   // 1024 + q, bytes 0, 2 low nibbles
-    const uint32_t v1 = (t & 0x000F000Fu) | magic;   // bytes 1, 3 low nibbles
-    const uint32_t v2 = (x & 0x00F000F0u) | magic;   // 1024 + 16 q, bytes 0, 2 high nibbles
-    const uint32_t v3 = (t & 0x00F000F0u) | magic;   // bytes 1, 3 high nibbles
-    const f16x2 lo_bias = {(f16)1032.0f, (f16)1032.0f};
-    const f16x2 hi_bias = {(f16)1152.0f, (f16)1152.0f};
-    const f16x2 h0 = bitcast<f16x2>(v0) - lo_bias, h1 = bitcast<f16x2>(v1) - lo_bias;
-    const f16x2 h2 = bitcast<f16x2>(v2) - hi_bias, h3 = bitcast<f16x2>(v3) - hi_bias;
-    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
-
 struct GemmStage {
     uint4 a[2][kEntries];   // [hi | lo][subtile][g][row] 8-half operands
-    uint4 b[2][kEntries];   // [(q-8) | (q-8) 2^-11][subtile][g][col]
+    uint4 b[2][kEntries];   // [code | code 2^-11][subtile][g][col]
     float d[kGemmBN];
 };
 
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0_any(const float *__restrict__ a,
-                                                               const uint8_t *__restrict__ w,
-                                                               float *__restrict__ y, int M, int N,
-                                                               int K, int tiles_m, int tiles_n)
+template <class F>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restrict__ a,
+                                                          const uint8_t *__restrict__ w,
+                                                          float *__restrict__ y, int M, int N,
+                                                          int K, int tiles_m, int tiles_n)
 {
     __shared__ GemmStage st[2];
 
@@ -97,32 +69,37 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0_any(const float *__r
     const int li = lane & 15, g = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
     const int nblk = K >> 5;
-    const size_t row_bytes = (size_t)nblk * kQ4Bytes;
+    const size_t row_bytes = (size_t)nblk * F::kBytes;
 
     // Staging role: row r of the slab, half h (elements 16h..16h+15 of the
-    // activation block; qs dwords 2h, 2h+1 of the weight block).
+    // activation block; the quant bytes of lane groups 2h and 2h+1 of the
+    // weight block).
     const int r = tid >> 1, h = tid & 1;
     const float *arow = a + (size_t)min(m0 + r, M - 1) * K + 16 * h;
     const uint8_t *wrow = w + (size_t)min(n0 + r, N - 1) * row_bytes;
 
     float4 av[4];
-    uint32_t wx0 = 0, wx1 = 0, wdb = 0;
+    uint32_t wx[2][F::kQsDwords];
+    uint32_t wdb = 0;
     auto load_step = [&](int kb) {
         const float4 *src = reinterpret_cast<const float4 *>(arow + (size_t)kb * 32);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             av[q] = src[q];
-        const uint8_t *bp = wrow + (size_t)kb * kQ4Bytes;
-        wx0 = load_u32_unaligned(bp + 2 + 8 * h);
-        wx1 = load_u32_unaligned(bp + 6 + 8 * h);
+        const uint8_t *bp = wrow + (size_t)kb * F::kBytes;
+        load_qs<F>(bp, 2 * h, wx[0]);
+        load_qs<F>(bp, 2 * h + 1, wx[1]);
         wdb = load_u16(bp);
     };
     auto store_step = [&](GemmStage &s) {
         const int sub = r >> 4, i = r & 15;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            const float4 v = av[gg];
-            const float e[4] = {v.x, v.z, v.y, v.w};   // slot order 0, 2, 1, 3
+        for (int q = 0; q < 4; ++q) {
+            // Elements 16h + 4q .. + 3 fill one slot half of one lane group.
+            const int e0 = 16 * h + 4 * q, gg = F::a_group(e0), half = F::a_half(e0);
+            const float sc = half ? 1.0f / (float)(1 << F::kHiLog2) : 1.0f;
+            const float4 v = av[q];
+            const float e[4] = {v.x * sc, v.z * sc, v.y * sc, v.w * sc};   // slot order 0, 2, 1, 3
             f16x4 hi, lo;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -131,12 +108,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0_any(const float *__r
                 lo[c] = (f16)((e[c] - (float)x) * 2048.0f);
             }
             const int idx = (sub * 4 + gg) * 16 + i;
-            reinterpret_cast<uint2 *>(&s.a[0][idx])[h] = bitcast<uint2>(hi);
-            reinterpret_cast<uint2 *>(&s.a[1][idx])[h] = bitcast<uint2>(lo);
+            reinterpret_cast<uint2 *>(&s.a[0][idx])[half] = bitcast<uint2>(hi);
+            reinterpret_cast<uint2 *>(&s.a[1][idx])[half] = bitcast<uint2>(lo);
         }
         const f16x8 scale = {(f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f,
                              (f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f, (f16)0x1p-11f};
-        const f16x8 b0 = decode_plain(wx0), b1 = decode_plain(wx1);
+        const f16x8 b0 = F::decode(wx[0], F::kMagic), b1 = F::decode(wx[1], F::kMagic);
         const int idx0 = (sub * 4 + 2 * h) * 16 + i, idx1 = idx0 + 16;
         s.b[0][idx0] = bitcast<uint4>(b0);
         s.b[1][idx0] = bitcast<uint4>(b0 * scale);
@@ -214,35 +191,38 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4_0_any(const float *__r
 }
 
 // ---------------------------------------------------------------------------
-// Split-activation path, for K % 64 == 0 (every weight row then starts on a
-// 4-byte boundary and K splits into pairs of blocks).
+// Split-activation path, for K % 64 == 0 (K splits into pairs of blocks, and a
+// weight row, a whole number of pairs of 36 or 68 bytes, starts on a 4-byte
+// boundary).
 //
 // * k_gemm_split_a writes the activations once, already split (hi = f16(a),
 //   lo = f16((a - hi) 2^11)) and laid out as the matrix cores' A operands:
 //   16-byte operand [mt][kb][hl][sub][lane] holds, for row 128 mt + 16 sub +
-//   lane % 16 and block kb, the slots of k-group g = lane / 16 (elements 4g,
-//   4g+2, 4g+1, 4g+3, 16+4g, 16+4g+2, 16+4g+1, 16+4g+3), hi for hl = 0 and
-//   lo for hl = 1. Rows past M are zero. The split then costs one pass over
-//   the activations instead of one per column tile, and a workgroup's
-//   activation slab for a pair of blocks is 32 contiguous KB.
-// * k_gemm_q4_0_split: a 512-thread workgroup computes a 128 x 128 tile. Its
-//   eight wavefronts are two K groups of four: group kg takes the even (kg =
-//   0) or odd (kg = 1) block of each pair, and wavefront (wm, wn) of a group
-//   owns a 64 x 64 quadrant as 4 x 4 MFMA tiles. Two wavefronts per SIMD
-//   hide each other's VALU work and latencies; the two groups' partial tiles
-//   are added once, through LDS, at the end.
+//   lane % 16 and block kb, the slots of lane group g = lane / 16 in the
+//   format's order (formats.h), hi for hl = 0 and lo for hl = 1. Rows past M
+//   are zero. The split then costs one pass over the activations instead of
+//   one per column tile, and a workgroup's activation slab for a pair of
+//   blocks is 32 contiguous KB.
+// * k_gemm_split: a 512-thread workgroup computes a 128 x 128 tile. Its eight
+//   wavefronts are two K groups of four: group kg takes the even (kg = 0) or
+//   odd (kg = 1) block of each pair, and wavefront (wm, wn) of a group owns a
+//   64 x 64 quadrant as 4 x 4 MFMA tiles. Two wavefronts per SIMD hide each
+//   other's VALU work and latencies; the two groups' partial tiles are added
+//   once, through LDS, at the end.
 // * Per pair of blocks the workgroup stages the 32 KB activation slab and the
-//   36 raw weight bytes of each of its 128 rows in LDS (double-buffered, one
-//   barrier per pair). Each wavefront decodes its own B operands from the raw
-//   bytes: the qs dword g of the block for column lane % 16, realigned with
-//   v_alignbyte where it straddles a dword, becomes (q - 8) and (q - 8) 2^-11
-//   as binary16, and d stays binary16 until the scale FMA.
+//   raw weight bytes of the pair (36 or 68 per row) of its 128 rows in LDS,
+//   with direct-to-LDS loads in a ring (below). Each wavefront decodes its own
+//   B operands from the raw bytes: the quant bytes of lane group g for column
+//   lane % 16, realigned with v_alignbyte where they straddle dwords, become
+//   the binary16 codes and the same times 2^-11, and d stays binary16 until
+//   the scale FMA.
 // * Accumulation as in the general kernel: two chained MFMAs per 16 x 16 tile
-//   and block (hi x (q - 8), lo x (q - 8) 2^-11), then d * C + acc in f32.
+//   and block (hi x code, lo x code 2^-11), then d * C + acc in f32.
 
 constexpr int kSplitWaves = 4;
 constexpr int kOpsPerBlockTile = 2 * 8 * 64;   // 16-byte A operands per (128-row tile, block)
 
+template <class F>
 __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *__restrict__ a,
                                                                  u32x4 *__restrict__ ahl, int M,
                                                                  int K, long long n_waves)
@@ -258,13 +238,13 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
     const long long m = R * 16 + li;
     f16x8 hi = {}, lo = {};
     if (m < M) {
-        const float *src = a + m * K + (long long)kb * 32 + 4 * g;
-        const float4 L = *reinterpret_cast<const float4 *>(src);
-        const float4 H = *reinterpret_cast<const float4 *>(src + 16);
-        // Slots 4..7 pair with high nibbles, which the GEMM decodes as 16 (q - 8):
-        // they carry a / 16 (exact), so every product is a (q - 8).
-        const float e[8] = {L.x, L.z, L.y, L.w, H.x * 0.0625f, H.z * 0.0625f, H.y * 0.0625f,
-                            H.w * 0.0625f};
+        const float *blk = a + m * K + (long long)kb * 32;
+        const float4 L = *reinterpret_cast<const float4 *>(blk + F::a_lo(g));
+        const float4 H = *reinterpret_cast<const float4 *>(blk + F::a_hi(g));
+        // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code: they carry
+        // a / 2^kHiLog2 (exact), so every product is a times the code.
+        constexpr float hs = 1.0f / (float)(1 << F::kHiLog2);
+        const float e[8] = {L.x, L.z, L.y, L.w, H.x * hs, H.z * hs, H.y * hs, H.w * hs};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const f16 h = (f16)e[s];
@@ -279,14 +259,23 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
 }
 
 constexpr int kSplitGemmThreads = 512;
-constexpr int kRingStages = 4;
-constexpr int kBDwords = kGemmBN * 9;      // a pair's raw weight bytes: 36 per row
-constexpr int kBSlots = 8 * 3 * 64;        // dword slots of three loads per wavefront
+constexpr int kARing = 3;   // activation slabs in LDS
+constexpr int kBRing = 4;   // raw weight stages in LDS
 
-// One ring stage: the pair's activation slab and raw weight bytes.
-struct RingStage {
-    u32x4 a[2 * kOpsPerBlockTile];  // 32 KB, [kg][hl][sub][lane], as in the workspace
-    uint32_t b[kBSlots];            // [row][9 dwords]; slots >= 128 * 9 are never read
+// Per-format geometry of one pair of blocks.
+template <class F>
+struct PairGeom {
+    static constexpr int kDwords = 2 * F::kBytes / 4;                 // raw dwords per row: 9 or 17
+    static constexpr int kBDwords = kGemmBN * kDwords;                // ... per tile
+    static constexpr int kBLoads = (kBDwords + 511) / 512;            // 4-byte loads per wavefront
+    static constexpr int kBSlots = kBLoads * 512;                     // LDS dwords per weight stage
+    static constexpr int kLoads = 4 + kBLoads;                        // loads per wavefront per pair
+};
+
+template <class F>
+struct SplitLds {
+    u32x4 a[kARing][2 * kOpsPerBlockTile];   // 32 KB each, [kg][hl][sub][lane], as in the workspace
+    uint32_t b[kBRing][PairGeom<F>::kBSlots];   // [row][kDwords]; slots past the tile are never read
 };
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(n) lgkmcnt(0), expcnt unchanged.
@@ -306,11 +295,14 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
+template <class F>
+__global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const u32x4 *__restrict__ ahl, const uint8_t *__restrict__ w, float *__restrict__ y, int M,
     int N, int K, int tiles_m, int tiles_n)
 {
-    __shared__ RingStage st[kRingStages];
+    using G = PairGeom<F>;
+    constexpr int NL = G::kLoads;
+    __shared__ SplitLds<F> lds;
 
     const int T = tiles_m * tiles_n, L = blockIdx.x;
     const int t = (T % 8 == 0) ? (L % 8) * (T / 8) + L / 8 : L;
@@ -322,39 +314,39 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
     const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
     const int li = lane & 15, g = lane >> 4;
     const int nblk = K >> 5, npairs = nblk >> 1;
-    // 0x64006400 as a value the compiler cannot fold back into a literal.
-    uint32_t magic_v;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic_v));
-    const size_t row_bytes = (size_t)nblk * kQ4Bytes;
+    const uint32_t magic_v = magic_vgpr<F>();
+    const size_t row_bytes = (size_t)nblk * F::kBytes;
 
-    // Direct-to-LDS loads, seven per wavefront per pair (so every wavefront's
+    // Direct-to-LDS loads, NL per wavefront per pair (so every wavefront's
     // vmcnt moves in the same steps). A: four 16-byte loads, 1 KB each, at
     // entries (4 wave + i) * 64 + lane of the slab, whose workspace order is
-    // the LDS order. B: three 4-byte loads at dword slots j * 64 + lane, j =
-    // wave + 8 r; slot t < 128 * 9 is dword t % 9 of the pair's 36 bytes of row
-    // t / 9, higher slots re-read a valid dword into unused LDS.
+    // the LDS order. B: kBLoads 4-byte loads at dword slots j * 64 + lane, j =
+    // wave + 8 r; slot t < 128 kDwords is dword t % kDwords of the pair's bytes
+    // of row t / kDwords, higher slots re-read a valid dword into unused LDS.
     const u32x4 *asrc = ahl + (size_t)mt * nblk * kOpsPerBlockTile + wave * 4 * 64 + lane;
-    const uint8_t *bsrc[3];
+    const uint8_t *bsrc[G::kBLoads];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        const int tt = min((wave + 8 * r) * 64 + lane, kBDwords - 1), row = tt / 9, dw = tt % 9;
+    for (int r = 0; r < G::kBLoads; ++r) {
+        const int tt = min((wave + 8 * r) * 64 + lane, G::kBDwords - 1);
+        const int row = tt / G::kDwords, dw = tt % G::kDwords;
         bsrc[r] = w + (size_t)min(n0 + row, N - 1) * row_bytes + 4 * dw;
     }
-    // Load k (0..6) of pair p: four A loads, then three B loads.
+    // Load k (0 .. NL-1) of pair p: four A loads, then the B loads.
     auto issue_load = [&](int p, int k) __attribute__((always_inline)) {
-        RingStage &S = st[p % kRingStages];
         if (k < 4)
             __builtin_amdgcn_global_load_lds(
                 (const void *)(asrc + (size_t)p * 2 * kOpsPerBlockTile + k * 64),
-                (__attribute__((address_space(3))) void *)(S.a + (wave * 4 + k) * 64), 16, 0, 0);
+                (__attribute__((address_space(3))) void *)(lds.a[p % kARing] + (wave * 4 + k) * 64),
+                16, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(
-                (const void *)(bsrc[k - 4] + 36 * p),
-                (__attribute__((address_space(3))) void *)(S.b + (wave + 8 * (k - 4)) * 64), 4, 0, 0);
+                (const void *)(bsrc[k - 4] + 2 * F::kBytes * p),
+                (__attribute__((address_space(3))) void *)(lds.b[p % kBRing] + (wave + 8 * (k - 4)) * 64),
+                4, 0, 0);
     };
     auto issue_pair = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 7; ++k)
+        for (int k = 0; k < NL; ++k)
             issue_load(p, k);
     };
 
@@ -370,25 +362,23 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
 
     auto run_group = [&](auto kg_c) __attribute__((always_inline)) {
         constexpr int KG = decltype(kg_c)::value;
-        // B of column group ns, block 2p + KG: qs dword g of the block for column
-        // wn*64 + ns*16 + li starts at byte 18 KG + 2 + 4 g of the row's 36 bytes,
-        // which is dword g + 5 KG shifted by 2 (1 - KG) bytes; d is the 16-bit half
-        // KG of dword 4 KG. KG is a compile-time constant (the loop exists once per
-        // K group), so group 1 needs no realignment and d feeds the scale FMA
-        // straight from its half.
-        const int bi0 = g + 5 * KG;
+        // B of column group ns, block 2p + KG: the row's raw pair bytes hold block
+        // KG at byte kBytes KG. KG is a compile-time constant (the loop exists
+        // once per K group), so the realignment (where the quant bytes straddle
+        // dwords) and the half of the dword that holds d are fixed per loop.
         struct BCol {
-            uint32_t lo, hi, dw;
+            QsRaw<F, KG> qs;
+            uint32_t dw;
         };
-        auto read_b = [&](const RingStage &S, int ns) __attribute__((always_inline)) {
-            const uint32_t *rb = S.b + (wn * 64 + ns * 16 + li) * 9;
-            return BCol{rb[bi0], KG == 0 ? rb[bi0 + 1] : 0u, rb[4 * KG]};
+        auto read_b = [&](const uint32_t *bstage, int ns) __attribute__((always_inline)) {
+            const uint32_t *rb = bstage + (wn * 64 + ns * 16 + li) * G::kDwords;
+            return BCol{read_qs_raw<F, KG>(rb, g), rb[d_dword<F, KG>()]};
         };
         struct AOps {
             f16x8 hi[4], lo[4];
         };
-        auto read_a = [&](const RingStage &S, AOps &A) __attribute__((always_inline)) {
-            const u32x4 *ap = S.a + KG * kOpsPerBlockTile + wm * 4 * 64 + lane;
+        auto read_a = [&](const u32x4 *slab, AOps &A) __attribute__((always_inline)) {
+            const u32x4 *ap = slab + KG * kOpsPerBlockTile + wm * 4 * 64 + lane;
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
                 A.hi[ms] = bitcast<f16x8>(ap[ms * 64]);
@@ -402,7 +392,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
         // between two register sets by the parity of ns, and the group before
         // group 0 is group 3 of the previous pair (zeros before the first pair),
         // so every index is a compile-time constant. The scheduling-group barriers
-        // ask for one MFMA then three VALU instructions, eight times per group.
+        // ask for one MFMA then four VALU instructions, eight times per group.
         f32x4 cbuf[2][4];
         float dbuf[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -411,14 +401,15 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
             for (int ms = 0; ms < 4; ++ms)
                 cbuf[h][ms] = zero4;
         struct BOps {
-            f16x8 q, s;   // (q - 8) (x16 in slots 4..7) and the same times 2^-11
+            f16x8 q, s;   // the codes (x 2^kHiLog2 in slots 4..7) and the same times 2^-11
             float d;
         };
         auto decode_b = [&](const BCol &bc) __attribute__((always_inline)) {
-            const uint32_t x = KG == 0 ? __builtin_amdgcn_alignbyte(bc.hi, bc.lo, 2u) : bc.lo;
+            uint32_t x[F::kQsDwords];
+            align_qs<F, KG>(bc.qs, x);
             BOps o;
-            o.d = f16_bits_to_f32(KG == 0 ? (bc.dw & 0xFFFFu) : (bc.dw >> 16));
-            o.q = decode_x16m(x, magic_v);
+            o.d = f16_bits_to_f32(d_from_dword<F, KG>(bc.dw));
+            o.q = F::decode(x, magic_v);
             o.s = o.q * scale;
             return o;
         };
@@ -431,13 +422,14 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
-                // The loads of pair dma_pair go out two per region (one in the
-                // last), between MFMAs, so the address unit works while the
-                // matrix cores do and no wavefront's MFMAs queue behind a load.
+                // The loads of pair dma_pair go out spread over the four regions
+                // (loads [NL ns / 4, NL (ns + 1) / 4), rounded up), between MFMAs, so
+                // the address unit works while the matrix cores do and no
+                // wavefront's MFMAs queue behind a load.
                 if (dma_pair >= 0) {
-                    issue_load(dma_pair, 2 * ns);
-                    if (2 * ns + 1 < 7)
-                        issue_load(dma_pair, 2 * ns + 1);
+#pragma unroll
+                    for (int k = (NL * ns + 3) / 4; k < (NL * (ns + 1) + 3) / 4; ++k)
+                        issue_load(dma_pair, k);
                 }
                 f32x4 *c = cbuf[ns & 1];
                 const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
@@ -471,34 +463,43 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
             }
         };
 
-        // Ring schedule: pair q is loaded into stage q % 4 during step q - 3, is
-        // complete by the barrier ending step q - 2, has its A operands read into
-        // registers during step q - 1 and is computed in step q. Stage q % 4 is
-        // loaded again (pair q + 4) in step q + 1, after the barrier that ends
-        // step q, by which every wavefront has read it.
+        // Ring schedule: pair q is loaded (activation slab into A slot q % 3, raw
+        // weight bytes into B slot q % 4) during step q - 3, is complete by the
+        // barrier ending step q - 2, has its A operands read into registers
+        // during step q - 1 and its B bytes read at the start of step q, and is
+        // computed in step q. A slot q % 3 is loaded again (pair q + 3) in step
+        // q, after the barrier that ends step q - 1, by which every wavefront has
+        // read it into registers; B slot q % 4 is loaded again (pair q + 4) in
+        // step q + 1, after the barrier that ends step q.
         const int pre = min(npairs, 3);
         for (int p = 0; p < pre; ++p)
             issue_pair(p);
         if (pre == 3)
-            ring_barrier<7>();    // pairs 0 and 1 complete, pair 2 in flight
+            ring_barrier<NL>();   // pairs 0 and 1 complete, pair 2 in flight
         else
             ring_barrier<0>();
         AOps A0, A1;
-        read_a(st[0], A0);
+        read_a(lds.a[0], A0);
+        // Step 0 reloads A slot 0 (pair 3): every wavefront must have read pair
+        // 0's slab first.
+        if (pre == 3)
+            ring_barrier<NL>();
+        else
+            ring_barrier<0>();
         auto step = [&](int p, const AOps &Acur, AOps &Anext) __attribute__((always_inline)) {
             // This pair's raw weight dwords first (one wait covers them), then
             // the next pair's A operands, which land during this pair's MFMAs.
             BCol bcol[4];
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
-                bcol[ns] = read_b(st[p % kRingStages], ns);
+                bcol[ns] = read_b(lds.b[p % kBRing], ns);
             __builtin_amdgcn_sched_barrier(0);
             if (p + 1 < npairs)
-                read_a(st[(p + 1) % kRingStages], Anext);
+                read_a(lds.a[(p + 1) % kARing], Anext);
             __builtin_amdgcn_sched_barrier(0);
             compute_pair(bcol, Acur, p + 3 < npairs ? p + 3 : -1);
             if (p + 3 < npairs)
-                ring_barrier<7>();    // pair p + 2 complete, pair p + 3 in flight
+                ring_barrier<NL>();   // pair p + 2 complete, pair p + 3 in flight
             else
                 ring_barrier<0>();
         };
@@ -513,7 +514,6 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
-
     };
     if (kg == 0)
         run_group(std::integral_constant<int, 0>{});
@@ -523,8 +523,8 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
     // Group 1 hands its partial tile to group 0 through LDS (every load has
     // landed and every wavefront has passed the last barrier):
     // [wavefront of the group][value][lane].
-    float *red = reinterpret_cast<float *>(&st[0]);
-    static_assert(sizeof(st) >= 4 * 64 * 64 * sizeof(float), "reduction buffer");
+    float *red = reinterpret_cast<float *>(&lds.a[0][0]);
+    static_assert(sizeof(lds.a) >= 4 * 64 * 64 * sizeof(float), "reduction buffer");
     const int wq = wave & 3;
     if (kg == 1) {
 #pragma unroll
@@ -557,30 +557,37 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_q4_0_split(
     }
 }
 
-hipError_t launch_gemm(const float *a, const uint8_t *w, float *y, int M, int N, int K,
-                       void *workspace, hipStream_t s)
+template <class F>
+static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int M, int N, int K,
+                                void *workspace, hipStream_t s)
 {
     const int tiles_m = (M + kGemmBM - 1) / kGemmBM, tiles_n = (N + kGemmBN - 1) / kGemmBN;
     const long long T = (long long)tiles_m * tiles_n;
     if (T > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    if (!q4v::gemm_splits_activations(K))
-        return launch_kernel(k_gemm_q4_0_any, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w,
-                             y, M, N, K, tiles_m, tiles_n);
-    if ((long long)M * N >= (1LL << 31))   // the split kernel stores with 32-bit offsets
-        return launch_kernel(k_gemm_q4_0_any, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w,
-                             y, M, N, K, tiles_m, tiles_n);
+    if (!q4v::gemm_splits_activations(K) ||
+        (long long)M * N >= (1LL << 31))   // the split kernel stores with 32-bit offsets
+        return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w, y,
+                             M, N, K, tiles_m, tiles_n);
     u32x4 *ahl = static_cast<u32x4 *>(workspace);
     const long long n_waves = (long long)tiles_m * 8 * (K / 32);
     const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
     if (split_grid > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    hipError_t e = launch_kernel(k_gemm_split_a, dim3((unsigned)split_grid), dim3(64 * kSplitWaves),
-                                 0, s, a, ahl, M, K, n_waves);
+    hipError_t e = launch_kernel(k_gemm_split_a<F>, dim3((unsigned)split_grid),
+                                 dim3(64 * kSplitWaves), 0, s, a, ahl, M, K, n_waves);
     if (e != hipSuccess)
         return e;
-    return launch_kernel(k_gemm_q4_0_split, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
+    return launch_kernel(k_gemm_split<F>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
                          (const u32x4 *)ahl, w, y, M, N, K, tiles_m, tiles_n);
+}
+
+hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
+                       int K, void *workspace, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemm_f<FmtQ8_0>(a, w, y, M, N, K, workspace, s);
+    return launch_gemm_f<FmtQ4_0>(a, w, y, M, N, K, workspace, s);
 }
 
 }  // namespace q4k

@@ -1,44 +1,47 @@
-// Decode-shaped Q4_0 x f32 product, y[m, n] = sum_k a[m, k] * w[n, k] for
-// 1 <= M <= 8 activation rows, on gfx950 matrix cores.
+// Decode-shaped block-quantized x f32 product, y[m, n] = sum_k a[m, k] w[n, k]
+// for 1 <= M <= 8 activation rows, on gfx950 matrix cores, for Q4_0 and Q8_0
+// weight streams.
 //
 // Operation: docs.rs fuel-dispatch, "quantized (GGML) kernel contracts",
-// section qmatvec_q4_0 (one row there; up to eight rows here), with the Q4_0
-// block of section dequant_q4_0. The work is bound by streaming the weight
-// blocks once (N * K * 18/32 bytes).
+// section qmatvec_q4_0 (one row there; up to eight rows here), with the blocks
+// of sections dequant_q4_0 and dequant_q8_0 (the quantized-matmul binding
+// described there picks either by quant type). The work is bound by streaming
+// the weight blocks once (N K 18/32 or 34/32 bytes).
 //
 // Design
 // ------
 // * One workgroup of 8 wavefronts owns 16 output columns (16 weight rows) and
 //   the whole K. Wavefront w owns a contiguous run of the K/32 blocks. Lane
-//   (j = lane % 16, g = lane / 16) reads, per block of weight row n0 + j, the
-//   binary16 scale and qs dword g (bytes 4g..4g+3) straight into registers:
-//   every weight byte is read once, and all of a wavefront's loads are issued
-//   before the activations are prepared, so HBM latency overlaps that work.
+//   (j = lane % 16, g = lane / 16) takes, per block of weight row n0 + j, the
+//   binary16 scale and the quant bytes of lane group g (formats.h): every
+//   weight byte is read once, and all of a wavefront's loads are issued before
+//   the activations are prepared, so HBM latency overlaps that work.
 // * The 32-element dot products of a block run on v_mfma_f32_16x16x32_f16.
-//   Operand B (32 x 16) holds the exact binary16 integers (q - 8) of 16 weight
-//   rows; operand A (16 x 32) holds the activations split into two binary16
-//   terms, hi = f16(v) and lo = f16(v - hi) (rows 2m and 2m+1 for activation
-//   row m), which together carry 22 significant bits. Each product of a
-//   binary16 pair is exact and the matrix core accumulates in f32.
-// * Decode: the dword's eight nibbles become four f16 pairs with one AND-OR
-//   against the exponent pattern of 1024 and one packed f16 subtraction each.
-//   The high nibbles are decoded in place (bits 4..7 of a half), which yields
-//   16 (q - 8); the activations paired with low nibbles carry the factor 16
-//   instead, so every product is 16 a (q - 8) and one power of two restores it.
-//   The K order inside a block is permuted (elements 4g, 4g+2, 4g+1, 4g+3,
-//   then +16); A uses the same permutation, so the sum is unchanged.
+//   Operand B (32 x 16) holds the exact binary16 weight codes of 16 weight rows;
+//   operand A (16 x 32) holds the activations split into two binary16 terms,
+//   hi = f16(v) and lo = f16(v - hi) (rows 2m and 2m+1 for activation row m),
+//   which together carry 22 significant bits. Each product of a binary16 pair
+//   is exact and the matrix core accumulates in f32.
+// * Decode (formats.h): Q4_0 nibbles become f16 pairs with one AND-OR against
+//   the exponent pattern of 1024 and one packed f16 subtraction each; the high
+//   nibbles are decoded in place, which yields 16 (q - 8), so the activations
+//   paired with low nibbles carry the factor 16 instead and one power of two
+//   restores every product. Q8_0 bytes go through one byte permute per pair and
+//   the same subtraction. The K order inside a block is permuted; A uses the
+//   same permutation, so the sum is unchanged.
 // * Each block's f32 partial is scaled by its d into f32 accumulators
 //   (d * C + acc), giving the two-level order block partial -> scale -> sum of
 //   blocks. Wavefront partials are summed in LDS in a fixed order, so repeated
 //   calls return identical bits.
 // * Range: activation row m is scaled by a power of two 2^p_m chosen from its
-//   max |a| so that 16 max|a| 2^p_m lies in [2^14, 2^15): no binary16
+//   max |a| so that the largest A value lies in [2^14, 2^15): no binary16
 //   overflow, and elements far below the row maximum lose at most 2^-25 of
 //   2^p_m absolutely. The scale is undone exactly on the f32 result.
 #include <type_traits>
 #include <utility>
 
 #include "device_common.h"
+#include "formats.h"
 #include "launch.h"
 
 namespace q4k {
@@ -47,24 +50,6 @@ constexpr int kGemvWaves = 8;
 constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kGemvStreamWaves = 8;
 
-// B operand for qs dword x (bytes 4g..4g+3 of a block): slots hold
-// (q-8) of elements 4g+0, 4g+2, 4g+1, 4g+3 and 16 (q-8) of 16+4g+0, +2, +1, +3.
-__device__ __forceinline__ f16x8 decode_x16(uint32_t x)
-{
-    const uint32_t t = x >> 8;
-    const uint32_t v0 = (x & 0x000F000Fu) | 0x64006400u;   // 1024 + q (lo nibbles, bytes 0, 2)
-    const uint32_t v1 = (t & 0x000F000Fu) | 0x64006400u;   // 1024 + q (lo nibbles, bytes 1, 3)
-    const uint32_t v2 = (x & 0x00F000F0u) | 0x64006400u;   // 1024 + 16 q (hi nibbles, bytes 0, 2)
-    const uint32_t v3 = (t & 0x00F000F0u) | 0x64006400u;   // 1024 + 16 q (hi nibbles, bytes 1, 3)
-    const f16x2 lo_bias = {(f16)1032.0f, (f16)1032.0f};
-    const f16x2 hi_bias = {(f16)1152.0f, (f16)1152.0f};
-    f16x2 h0 = bitcast<f16x2>(v0) - lo_bias;
-    f16x2 h1 = bitcast<f16x2>(v1) - lo_bias;
-    f16x2 h2 = bitcast<f16x2>(v2) - hi_bias;
-    f16x2 h3 = bitcast<f16x2>(v3) - hi_bias;
-    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
-
 // Split v into binary16 hi + lo with hi = f16(v) and lo = f16(v - hi).
 __device__ __forceinline__ void split2(float v, f16 &hi, f16 &lo)
 {
@@ -72,10 +57,20 @@ __device__ __forceinline__ void split2(float v, f16 &hi, f16 &lo)
     lo = (f16)(v - (float)hi);
 }
 
-template <int M>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restrict__ a,
-                                                           const uint8_t *__restrict__ w,
-                                                           float *__restrict__ y, int N, int K)
+// Largest A value of a row is 2^kHiLog2 max|a| 2^p: p puts it in [2^14, 2^15).
+template <class F>
+__device__ __forceinline__ int row_scale_exp(float am)
+{
+    int e = 0;
+    frexpf(am, &e);                                  // am in [2^(e-1), 2^e)
+    const int p = (am == 0.0f) ? 0 : 15 - F::kHiLog2 - e;
+    return p > 120 ? 120 : (p < -120 ? -120 : p);
+}
+
+template <class F, int M>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(const float *__restrict__ a,
+                                                      const uint8_t *__restrict__ w,
+                                                      float *__restrict__ y, int N, int K)
 {
     constexpr int NW = kGemvWaves;
     constexpr int CB = (M <= 4) ? 128 : 64;   // blocks per K chunk held in LDS
@@ -92,19 +87,19 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
     const int j = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int nblk = K >> 5;
-    const size_t row_bytes = (size_t)nblk * kQ4Bytes;
+    const size_t row_bytes = (size_t)nblk * F::kBytes;
     const uint8_t *wrow = w + (size_t)min(n0 + j, N - 1) * row_bytes;
 
-    uint32_t wx[PB], wd[PB];
+    uint32_t wx[PB][F::kQsDwords], wd[PB];
     auto issue_loads = [&](int cb0, int cnt) {
         const int per = (cnt + NW - 1) / NW, b0 = wave * per;
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
             const int b = b0 + u;
             if (u < per && b < cnt) {
-                const uint8_t *bp = wrow + (size_t)(cb0 + b) * kQ4Bytes;
+                const uint8_t *bp = wrow + (size_t)(cb0 + b) * F::kBytes;
                 wd[u] = load_u16(bp);
-                wx[u] = load_u32_unaligned(bp + 2 + 4 * g);
+                load_qs<F>(bp, g, wx[u]);
             }
         }
     };
@@ -131,11 +126,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
         float am = 0.0f;
         for (int ww = 0; ww < NW; ++ww)
             am = fmaxf(am, s_amax[ww][tid]);
-        int e = 0;
-        frexpf(am, &e);                        // am in [2^(e-1), 2^e)
-        int p = (am == 0.0f) ? 0 : 11 - e;     // 16 am 2^p in [2^14, 2^15)
-        p = p > 120 ? 120 : (p < -120 ? -120 : p);
-        s_exp[tid] = p;
+        s_exp[tid] = row_scale_exp<F>(am);
     }
     __syncthreads();
     int pexp[M];
@@ -157,13 +148,14 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
             issue_loads(cb0, cnt);
         }
         // A operands of this chunk: entry (b, gg, 2m) = hi, (b, gg, 2m+1) = lo,
-        // slots = 16 a[4gg + {0,2,1,3}] then a[16 + 4gg + {0,2,1,3}], all x 2^p.
+        // slots = 2^kHiLog2 a[lo(gg) + {0,2,1,3}] then a[hi(gg) + {0,2,1,3}],
+        // all x 2^p.
         for (int q = tid; q < cnt * 4 * M; q += kGemvThreads) {
             const int m = q % M, rest = q / M, gg = rest & 3, b = rest >> 2;
-            const float *src = a + (size_t)m * K + (size_t)(cb0 + b) * 32 + 4 * gg;
-            const float4 L = *reinterpret_cast<const float4 *>(src);
-            const float4 H = *reinterpret_cast<const float4 *>(src + 16);
-            const float sh = ldexpf(1.0f, pexp[m]), sl = 16.0f * sh;
+            const float *blk = a + (size_t)m * K + (size_t)(cb0 + b) * 32;
+            const float4 L = *reinterpret_cast<const float4 *>(blk + F::a_lo(gg));
+            const float4 H = *reinterpret_cast<const float4 *>(blk + F::a_hi(gg));
+            const float sh = ldexpf(1.0f, pexp[m]), sl = (float)(1 << F::kHiLog2) * sh;
             const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
                                 H.x * sh, H.z * sh, H.y * sh, H.w * sh};
             f16x8 hi, lo;
@@ -188,7 +180,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
                 f16x8 aop = {};
                 if (j < NI)
                     aop = bitcast<f16x8>(s_a[(b * 4 + g) * NI + j]);
-                const f16x8 bop = decode_x16(wx[u]);
+                const f16x8 bop = F::decode(wx[u], F::kMagic);
                 const f32x4 C = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, zero4, 0, 0, 0);
                 const float d = f16_bits_to_f32(wd[u]);
 #pragma unroll
@@ -214,7 +206,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
         for (int ww = 0; ww < NW; ++ww)
             s += s_part[ww][m][jj];
         if (n < N)
-            y[(size_t)m * N + n] = ldexpf(s, -pexp[m] - 4);
+            y[(size_t)m * N + n] = ldexpf(s, -pexp[m] - F::kHiLog2);
     }
 }
 
@@ -223,8 +215,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q4_0(const float *__restr
 // covers the decode shapes. Same arithmetic as above; what changes is how the
 // weight bytes reach the matrix cores:
 // * Each wavefront owns a run of blocks of the workgroup's 16 rows and walks it
-//   in chunks of CH blocks (CH * 18 bytes per row, a multiple of 144 and so of
-//   16). A chunk is fetched with aligned 16-byte loads, lane (r, c) taking
+//   in chunks of CH blocks (CH * 18 or CH * 34 bytes per row, a multiple of
+//   16 for CH = 8 or 16). A chunk is fetched with aligned 16-byte loads, lane (r, c) taking
 //   16-byte column c of row r, and written unchanged into the wavefront's own
 //   LDS area. Operands are then read back with aligned LDS dword pairs and
 //   realigned with v_alignbyte. No global load is narrower than 16 bytes or
@@ -247,13 +239,13 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int M, int NW, int CH_>
+template <class F, int M, int NW, int CH_>
 struct GemvStreamCfg {
     static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
-    static constexpr int CPR = CH * 18 / 16;              // 16-byte columns per staged row
+    static constexpr int CPR = CH * F::kBytes / 16;       // 16-byte columns per staged row
     static constexpr int NLOAD = (CPR + 3) / 4;           // 16-byte loads per lane per chunk
     static constexpr int NFULL = CPR / 4;                 // ... that no lane clamps
-    static constexpr int RS = CH * 18 + 16;               // LDS bytes per staged row
+    static constexpr int RS = CH * F::kBytes + 16;        // LDS bytes per staged row
     static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
     static constexpr int NI = 2 * M;                      // A rows in use
     static constexpr int ABYTES = CH * 4 * NI * 16;       // A operands per wavefront
@@ -262,8 +254,9 @@ struct GemvStreamCfg {
     static constexpr int LDS_PER_WAVE = WBYTES + ABYTES;
     static constexpr int NPART = CH == 16 ? 4 : 2;        // parts a chunk is contracted in
     // Loads (per lane) that hold every byte of the chunk's first b blocks.
-    static constexpr int loads_for(int b) { return b == 0 ? 0 : ((18 * b - 1) / 16) / 4 + 1; }
+    static constexpr int loads_for(int b) { return b == 0 ? 0 : ((F::kBytes * b - 1) / 16) / 4 + 1; }
     static_assert(CH == 8 || CH == 16, "chunks are 8 or 16 blocks");
+    static_assert((CH * F::kBytes) % 16 == 0, "a chunk row is whole 16-byte columns");
 };
 
 // Calls f(integral_constant<int, P>) for P = 0 .. NP-1, in order.
@@ -294,33 +287,25 @@ __device__ __forceinline__ float wave_max_nonneg(float v)
     return __builtin_bit_cast(float, r);
 }
 
-// decode_x16 with the exponent pattern supplied in a VGPR. gfx9 VOP3 takes
-// no literal operand, so with the pattern in a register the compiler can form
-// each (x & mask) | pattern as one v_and_or_b32 (mask in an SGPR) instead of
-// a v_and_b32 and a v_or_b32.
-__device__ __forceinline__ f16x8 decode_x16_fast(uint32_t x, uint32_t magic_v)
+// Calls f(integral_constant<int, B>) for B = B0 .. B1-1, in order.
+template <int B0, class F, int... P>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, P...>)
 {
-    const uint32_t t = x >> 8;
-    const uint32_t v0 = (x & 0x000F000Fu) | magic_v;
-    const uint32_t v1 = (t & 0x000F000Fu) | magic_v;
-    const uint32_t v2 = (x & 0x00F000F0u) | magic_v;
-    const uint32_t v3 = (t & 0x00F000F0u) | magic_v;
-    const f16x2 lo_bias = {(f16)1032.0f, (f16)1032.0f};
-    const f16x2 hi_bias = {(f16)1152.0f, (f16)1152.0f};
-    f16x2 h0 = bitcast<f16x2>(v0) - lo_bias;
-    f16x2 h1 = bitcast<f16x2>(v1) - lo_bias;
-    f16x2 h2 = bitcast<f16x2>(v2) - hi_bias;
-    f16x2 h3 = bitcast<f16x2>(v3) - hi_bias;
-    return (f16x8){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+    (f(std::integral_constant<int, B0 + P>{}), ...);
+}
+template <int B0, int B1, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl<B0>(f, std::make_integer_sequence<int, B1 - B0>{});
 }
 
-template <int M, int NW, int CH>
-__global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__restrict__ a,
-                                                             const uint8_t *__restrict__ w,
-                                                             float *__restrict__ y, int N, int K,
-                                                             int per)
+template <class F, int M, int NW, int CH>
+__global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict__ a,
+                                                        const uint8_t *__restrict__ w,
+                                                        float *__restrict__ y, int N, int K,
+                                                        int per)
 {
-    using C = GemvStreamCfg<M, NW, CH>;
+    using C = GemvStreamCfg<F, M, NW, CH>;
     constexpr int NACC = (M == 1) ? 2 : 4;
     constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
 
@@ -332,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     const int j = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int nblk = K >> 5;
-    const uint32_t row_bytes = (uint32_t)nblk * kQ4Bytes;
+    const uint32_t row_bytes = (uint32_t)nblk * F::kBytes;
     uint8_t *s_w = s_mem + wave * C::LDS_PER_WAVE;
     uint8_t *s_a = s_w + C::WBYTES;
 
@@ -349,8 +334,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     u32x4 wreg[C::NLOAD];
     float4 areg[C::EPL][2];
     // Activation group e = (m * CH + b) * 4 + gg: row m, block b of the chunk,
-    // elements 4gg..4gg+3 and 16+4gg..16+4gg+3. Activations are requested first
-    // (vmcnt drains in issue order), so their split overlaps the weight loads.
+    // elements lo(gg)..lo(gg)+3 and hi(gg)..hi(gg)+3. Activations are requested
+    // first (vmcnt drains in issue order), so their split overlaps the weight
+    // loads.
     const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a);
     // Every lane issues every load (surplus lanes re-read an in-bounds group or
     // column that is then ignored), so the compiler's in-order wait counts are
@@ -360,14 +346,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
         for (int r = 0; r < C::EPL; ++r) {
             const int e = min(lane + 64 * r, C::NENT - 1);
             const int m = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
-            const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + 4 * gg) * 4u;
+            const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * 4u;
             areg[r][0] = *reinterpret_cast<const float4 *>(a8 + off);
-            areg[r][1] = *reinterpret_cast<const float4 *>(a8 + off + 64u);
+            areg[r][1] = *reinterpret_cast<const float4 *>(a8 + off + 4u * (F::a_hi(0) - F::a_lo(0)));
         }
         // Columns lc0 + 4 i are in the row for i < NFULL on every lane: one
         // address with immediate offsets. The last load clamps its column.
         // The scheduling barriers keep the loads in column order.
-        const uint32_t woff = lrow_off + (uint32_t)cb0 * kQ4Bytes + 16u * lc0;
+        const uint32_t woff = lrow_off + (uint32_t)cb0 * F::kBytes + 16u * lc0;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < C::NFULL; ++i) {
@@ -395,11 +381,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     // Clamped, so the address stays inside the A area even where the read is
     // masked off.
     const uint8_t *a_lane = s_a + (g * C::NI + min(j, C::NI - 1)) * 16;
-    // The exponent pattern of 1024.0 in both halves, as a value the compiler
-    // cannot fold back into a literal (one v_mov at kernel start; no MFMA is in
-    // flight there).
-    uint32_t magic_v;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic_v));
+    // The decode's exponent pattern in a VGPR (one v_mov at kernel start; no
+    // MFMA is in flight there).
+    const uint32_t magic_v = magic_vgpr<F>();
 
     float ysum[NACC / 2];
 #pragma unroll
@@ -432,13 +416,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
             }
         }
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float am = wave_max_nonneg(mx[m]);
-            int e2 = 0;
-            frexpf(am, &e2);
-            int p = (am == 0.0f) ? 0 : 11 - e2;        // 16 max|a| 2^p in [2^14, 2^15)
-            pexp[m] = p > 120 ? 120 : (p < -120 ? -120 : p);
-        }
+        for (int m = 0; m < M; ++m)
+            pexp[m] = row_scale_exp<F>(wave_max_nonneg(mx[m]));
 #pragma unroll
         for (int r = 0; r < C::EPL; ++r) {
             const int e = lane + 64 * r;
@@ -449,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
                 for (int m = 0; m < M; ++m)
                     if (m == me)
                         pm = pexp[m];
-                const float sh = ldexpf(1.0f, pm), sl = 16.0f * sh;
+                const float sh = ldexpf(1.0f, pm), sl = (float)(1 << F::kHiLog2) * sh;
                 const float4 L = areg[r][0], H = areg[r][1];
                 const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
                                     H.x * sh, H.z * sh, H.y * sh, H.w * sh};
@@ -497,27 +476,24 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
 #pragma unroll
         for (int r = 0; r < NACC; ++r)
             acc[r] = 0.0f;
-        // qs dword g of block b starts at byte 18 b + 2 + 4 g of the staged row:
-        // 2 bytes past a dword boundary for even b, on one for odd b. All MFMAs
-        // of a part are issued before its scale FMAs, so the matrix-core latency
+        // Block b of the staged row starts at byte kBytes b; read_qs realigns the
+        // quant bytes of lane group g where they straddle dwords. All MFMAs of a
+        // part are issued before its scale FMAs, so the matrix-core latency
         // overlaps the decode of the following blocks.
         const uint8_t *wl = s_w + j * C::RS;
-        const uint32_t *wq = reinterpret_cast<const uint32_t *>(wl + 4 * g);
+        const uint32_t *wrow32 = reinterpret_cast<const uint32_t *>(wl);
         auto contract = [&](auto b0_c, auto b1_c) __attribute__((always_inline)) {
             constexpr int B0 = decltype(b0_c)::value, B1 = decltype(b1_c)::value;
             f32x4 Cv[B1 - B0];
             float d[B1 - B0];
-#pragma unroll
-            for (int b = B0; b < B1; ++b) {
-                uint32_t x;
-                if (b % 2 == 0)
-                    x = __builtin_amdgcn_alignbyte(wq[(18 * b) / 4 + 1], wq[(18 * b) / 4], 2u);
-                else
-                    x = wq[(18 * b + 2) / 4];
-                d[b - B0] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * kQ4Bytes));
-                Cv[b - B0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[b], decode_x16_fast(x, magic_v),
+            static_for<B0, B1>([&](auto b_c) __attribute__((always_inline)) {
+                constexpr int b = decltype(b_c)::value;
+                uint32_t x[F::kQsDwords];
+                read_qs<F, b>(wrow32, g, x);
+                d[b - B0] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * F::kBytes));
+                Cv[b - B0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[b], F::decode(x, magic_v),
                                                                      zero4, 0, 0, 0);
-            }
+            });
 #pragma unroll
             for (int u = 0; u < B1 - B0; ++u)
 #pragma unroll
@@ -530,7 +506,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
             for (int u = 0; u < B1 - B0; ++u)
                 asm volatile("" ::"v"(Cv[u]));
         };
-        // Undo this chunk's scale (and the factor 16) on its partial.
+        // Undo this chunk's scale (and the factor 2^kHiLog2) on its partial.
         auto finish_chunk = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int h = 0; h < NACC / 2; ++h) {
@@ -540,7 +516,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
                 for (int mm = 0; mm < M; ++mm)
                     if (mm == m)
                         pm = pexp[mm];
-                ysum[h] += ldexpf(acc[2 * h] + acc[2 * h + 1], -pm - 4);
+                ysum[h] += ldexpf(acc[2 * h] + acc[2 * h + 1], -pm - F::kHiLog2);
             }
         };
         for_each_part<C::NPART>([&](auto p_c) __attribute__((always_inline)) {
@@ -589,45 +565,55 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_stream(const float *__res
     }
 }
 
-template <int M>
+template <class F, int M>
 static hipError_t launch_gemv_m(const float *a, const uint8_t *w, float *y, int N, int K,
                                 hipStream_t s)
 {
     const unsigned grid = (unsigned)((N + 15) / 16);
-    // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0) and
-    // 32-bit byte offsets. Each wavefront gets `per` blocks (a multiple of 8);
-    // chunks of 16 blocks when every wavefront's share divides by 16, else 8.
+    // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0 and
+    // a row is a whole number of 16-byte columns in either format) and 32-bit
+    // byte offsets. Each wavefront gets `per` blocks (a multiple of 8); chunks
+    // of 16 blocks when every wavefront's share divides by 16, else 8.
     constexpr int NW = kGemvStreamWaves;
     const int nblk = K / 32;
-    if (K % 256 == 0 && (size_t)N * (size_t)nblk * 18 < ((size_t)1 << 31) &&
+    if (K % 256 == 0 && (size_t)N * (size_t)nblk * F::kBytes < ((size_t)1 << 31) &&
         (size_t)M * (size_t)K * 4 < ((size_t)1 << 31)) {
         const int per = (((nblk + NW - 1) / NW) + 7) & ~7;
         const int last = nblk - (nblk - 1) / per * per;       // blocks of the last busy wavefront
         if constexpr (M <= 4) {
             if (per % 16 == 0 && last % 16 == 0)
-                return launch_kernel(k_gemv_q4_0_stream<M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s,
+                return launch_kernel(k_gemv_stream<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s,
                                      a, w, y, N, K, per);
         }
-        return launch_kernel(k_gemv_q4_0_stream<M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, a, w,
-                             y, N, K, per);
+        return launch_kernel(k_gemv_stream<F, M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, a, w, y,
+                             N, K, per);
     }
-    return launch_kernel(k_gemv_q4_0<M>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
+    return launch_kernel(k_gemv<F, M>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
 }
 
-hipError_t launch_gemv(const float *a, const uint8_t *w, float *y, int M, int N, int K,
-                       hipStream_t s)
+template <class F>
+static hipError_t launch_gemv_f(const float *a, const uint8_t *w, float *y, int M, int N, int K,
+                                hipStream_t s)
 {
     switch (M) {
-    case 1: return launch_gemv_m<1>(a, w, y, N, K, s);
-    case 2: return launch_gemv_m<2>(a, w, y, N, K, s);
-    case 3: return launch_gemv_m<3>(a, w, y, N, K, s);
-    case 4: return launch_gemv_m<4>(a, w, y, N, K, s);
-    case 5: return launch_gemv_m<5>(a, w, y, N, K, s);
-    case 6: return launch_gemv_m<6>(a, w, y, N, K, s);
-    case 7: return launch_gemv_m<7>(a, w, y, N, K, s);
-    case 8: return launch_gemv_m<8>(a, w, y, N, K, s);
+    case 1: return launch_gemv_m<F, 1>(a, w, y, N, K, s);
+    case 2: return launch_gemv_m<F, 2>(a, w, y, N, K, s);
+    case 3: return launch_gemv_m<F, 3>(a, w, y, N, K, s);
+    case 4: return launch_gemv_m<F, 4>(a, w, y, N, K, s);
+    case 5: return launch_gemv_m<F, 5>(a, w, y, N, K, s);
+    case 6: return launch_gemv_m<F, 6>(a, w, y, N, K, s);
+    case 7: return launch_gemv_m<F, 7>(a, w, y, N, K, s);
+    case 8: return launch_gemv_m<F, 8>(a, w, y, N, K, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
+                       int K, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemv_f<FmtQ8_0>(a, w, y, M, N, K, s);
+    return launch_gemv_f<FmtQ4_0>(a, w, y, M, N, K, s);
 }
 
 }  // namespace q4k

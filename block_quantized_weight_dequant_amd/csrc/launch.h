@@ -8,12 +8,17 @@
 
 namespace q4k {
 
-hipError_t launch_dequant(const uint8_t *w, size_t n_blocks, float *out, hipStream_t s);
-hipError_t launch_gemv(const float *a, const uint8_t *w, float *y, int M, int N, int K, hipStream_t s);
+// Block format of a weight stream.
+enum class WeightFormat { kQ4_0, kQ8_0 };
+
+hipError_t launch_dequant(WeightFormat fmt, const uint8_t *w, size_t n_blocks, float *out,
+                          hipStream_t s);
+hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
+                       int K, hipStream_t s);
 // workspace: q4v::gemm_workspace_bytes(M, N, K) bytes when the split path is
 // taken (q4v::gemm_splits_activations(K)), else unused.
-hipError_t launch_gemm(const float *a, const uint8_t *w, float *y, int M, int N, int K,
-                       void *workspace, hipStream_t s);
+hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
+                       int K, void *workspace, hipStream_t s);
 hipError_t launch_q8_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
 hipError_t launch_q4_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
 

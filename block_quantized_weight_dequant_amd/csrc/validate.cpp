@@ -20,12 +20,13 @@ bool overlaps(Span a, Span b)
 
 static bool mul_ok(size_t x, size_t y, size_t *r) { return !__builtin_mul_overflow(x, y, r); }
 
-int check_dequant(const void *w, size_t w_bytes, const float *out, size_t out_elems, bool *empty)
+int check_dequant(const void *w, size_t w_bytes, const float *out, size_t out_elems,
+                  size_t block_bytes, bool *empty)
 {
     *empty = false;
-    if (w_bytes % 18 != 0)
+    if (w_bytes % block_bytes != 0)
         return Q4_ERR_SIZE;
-    size_t nb = w_bytes / 18, want = 0, out_bytes = 0;
+    size_t nb = w_bytes / block_bytes, want = 0, out_bytes = 0;
     if (!mul_ok(nb, 32, &want) || out_elems != want)
         return Q4_ERR_SIZE;
     if (!mul_ok(out_elems, sizeof(float), &out_bytes))
@@ -44,14 +45,14 @@ int check_dequant(const void *w, size_t w_bytes, const float *out, size_t out_el
 }
 
 int check_product(const float *a, const void *w, size_t w_bytes, const float *y,
-                  int M, int N, int K, int max_rows, bool *empty)
+                  int M, int N, int K, int max_rows, size_t block_bytes, bool *empty)
 {
     *empty = false;
     if (M < 0 || N < 0 || K < 32 || K % 32 != 0)
         return Q4_ERR_SHAPE;
     if (max_rows > 0 && M > max_rows)
         return Q4_ERR_SHAPE;
-    size_t row_bytes = (size_t)(K / 32) * 18, w_want = 0, a_bytes = 0, y_bytes = 0;
+    size_t row_bytes = (size_t)(K / 32) * block_bytes, w_want = 0, a_bytes = 0, y_bytes = 0;
     if (!mul_ok((size_t)N, row_bytes, &w_want) || w_bytes != w_want)
         return Q4_ERR_SIZE;
     if (!mul_ok((size_t)M, (size_t)K, &a_bytes) || !mul_ok(a_bytes, sizeof(float), &a_bytes))

@@ -17,7 +17,8 @@ import numpy as np
 #: Named workloads: the decode GEMV (1 and 8 activation rows) against a
 #: 4096 x 4096 weight, the prefill GEMM of an attention projection and of an FFN
 #: up-projection, the standalone dequant of that FFN weight and the Q8_0
-#: quantize of a 2048 x 4096 activation tensor.
+#: quantize of a 2048 x 4096 activation tensor. Weights are Q4_0 unless
+#: ``fmt`` says Q8_0.
 WORKLOADS = {
     "gemv_1x256x512": dict(kind="gemv", M=1, N=256, K=512, w_seed=100, a_seed=101),
     "gemv_1x4096x4096": dict(kind="gemv", M=1, N=4096, K=4096, w_seed=200, a_seed=201),
@@ -26,6 +27,17 @@ WORKLOADS = {
     "gemm_2048x14336x4096": dict(kind="gemm", M=2048, N=14336, K=4096, w_seed=400, a_seed=401),
     "dequant_14336x4096": dict(kind="dequant", N=14336, K=4096, w_seed=400),
     "quantize_2048x4096": dict(kind="quantize", M=2048, K=4096, x_seed=402),
+    # The same decode, prefill and dequant shapes over Q8_0 weights (the same
+    # f32 weights, quantized to Q8_0 instead).
+    "q8_0_gemv_1x4096x4096": dict(kind="gemv", fmt="q8_0", M=1, N=4096, K=4096, w_seed=200,
+                                  a_seed=201),
+    "q8_0_gemv_8x4096x4096": dict(kind="gemv", fmt="q8_0", M=8, N=4096, K=4096, w_seed=200,
+                                  a_seed=202),
+    "q8_0_gemm_1024x4096x4096": dict(kind="gemm", fmt="q8_0", M=1024, N=4096, K=4096,
+                                     w_seed=200, a_seed=203),
+    "q8_0_gemm_2048x14336x4096": dict(kind="gemm", fmt="q8_0", M=2048, N=14336, K=4096,
+                                      w_seed=400, a_seed=401),
+    "q8_0_dequant_14336x4096": dict(kind="dequant", fmt="q8_0", N=14336, K=4096, w_seed=400),
 }
 
 WEIGHT_SIGMA = np.float32(0.02)

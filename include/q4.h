@@ -1,5 +1,6 @@
 /*
- * q4.h — C ABI of the MI355X (gfx950) Q4_0 block-quantized weight library.
+ * q4.h — C ABI of the MI355X (gfx950) block-quantized (GGML Q4_0 / Q8_0)
+ * weight library.
  *
  * Formats (docs.rs fuel-dispatch 0.20.71, page "fuel-vulkan-kernels — quantized
  * (GGML) kernel contracts"):
@@ -8,9 +9,12 @@
  *     the high nibble is element j+16; element = (nibble - 8) * d, d widened to f32.
  *   Q8_0 block (sections dequant_q8_0, quantize_q8_0): 34 bytes for 32 elements,
  *     a little-endian binary16 scale d, then 32 signed bytes; element = q * d.
- *   Q4_0 weight matrix W[N, K/32] (sections qmatvec_q4_0, matmul_q4_0_tiled): a
+ *   Weight matrix W[N, K/32] (sections qmatvec_q4_0, matmul_q4_0_tiled): a
  *     contiguous row-major block stream, K/32 blocks per row, N * (K/32) * 18
- *     bytes in all, read from its first byte (no strides, no offsets).
+ *     bytes in all for Q4_0 and N * (K/32) * 34 for Q8_0, read from its first
+ *     byte (no strides, no offsets). The quantized-matmul binding on the page
+ *     picks Q4_0 or Q8_0 blocks by quant type; the q8_* products are the q4_*
+ *     ones over Q8_0 weights.
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a DEVICE pointer owned by the caller; the library
@@ -39,7 +43,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 2
+#define Q4_ABI_VERSION 3
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -48,9 +52,9 @@ extern "C" {
 #define Q4_ERR_ALIGN 4  /* a pointer is not 16-byte aligned */
 #define Q4_ERR_ALIAS 5  /* an output overlaps an input */
 #define Q4_ERR_LAUNCH 6 /* the HIP runtime refused the launch */
-#define Q4_ERR_WORKSPACE 7 /* q4_gemm's workspace is smaller than q4_gemm_workspace_bytes */
+#define Q4_ERR_WORKSPACE 7 /* a GEMM workspace is smaller than its *_gemm_workspace_bytes */
 
-/* Largest number of activation rows q4_gemv accepts. */
+/* Largest number of activation rows q4_gemv and q8_gemv accept. */
 #define Q4_GEMV_MAX_ROWS 8
 
 /* Returns Q4_ABI_VERSION of the library actually loaded. */
@@ -115,6 +119,39 @@ int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
  * product does not fit in size_t. Pure function of its arguments.
  */
 size_t q4_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * q8_dequant — Q8_0 block stream to dense f32 (section dequant_q8_0).
+ *   w_q       n_blocks * 34 bytes of Q8_0 blocks, with n_blocks = w_bytes / 34.
+ *   w_bytes   must be a multiple of 34 (else Q4_ERR_SIZE).
+ *   out       out_elems f32; out_elems must equal w_bytes / 34 * 32 (else
+ *             Q4_ERR_SIZE). Element 32*b + j of out is element j of block b.
+ * Bit-exact: every output is the exact product q * d (q the signed byte), so
+ * results equal any correct evaluation bit for bit, signed zeros included.
+ */
+int q8_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream);
+
+/*
+ * q8_gemv — q4_gemv over a Q8_0 weight stream: y = a @ dequant(W)^T for
+ * 1 <= M <= 8, with w_bytes == N * (K/32) * 34. Arguments, errors, accuracy
+ * and determinism as q4_gemv.
+ */
+int q8_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
+            int M, int N, int K, void *stream);
+
+/*
+ * q8_gemm — q4_gemm over a Q8_0 weight stream, with w_bytes == N * (K/32) * 34.
+ * Arguments, errors, the activation range, the workspace contract (with
+ * q8_gemm_workspace_bytes) and determinism as q4_gemm.
+ */
+int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
+            int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * q8_gemm_workspace_bytes — bytes of workspace q8_gemm needs for this shape;
+ * the same function of (M, N, K) as q4_gemm_workspace_bytes.
+ */
+size_t q8_gemm_workspace_bytes(int M, int N, int K);
 
 /*
  * q8_quantize — f32 to Q8_0 blocks (section quantize_q8_0).

@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: device buffers with guard regions, NaN
-prefill, and the Q4_0 test-weight blobs made by the oracle."""
+prefill, and the Q4_0 / Q8_0 test-weight blobs made by the oracle."""
 import numpy as np
 import torch
 
@@ -45,6 +45,38 @@ class Guarded:
 def q4_blob(N: int, K: int, seed: int) -> np.ndarray:
     """Seeded N(0, 0.02^2) weights quantized to Q4_0 by the oracle."""
     return oracle.q4_0_quantize(wl.weights_f32(seed, N, K))
+
+
+FORMATS = ("q4_0", "q8_0")
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34}
+
+
+def weight_blob(fmt: str, N: int, K: int, seed: int) -> np.ndarray:
+    """Seeded N(0, 0.02^2) weights quantized to `fmt` by the oracle."""
+    return getattr(oracle, fmt + "_quantize")(wl.weights_f32(seed, N, K))
+
+
+def oracle_matmul(fmt: str):
+    return getattr(oracle, fmt + "_matmul")
+
+
+def oracle_matmul_sampled(fmt: str):
+    return getattr(oracle, fmt + "_matmul_sampled")
+
+
+def oracle_dequant(fmt: str):
+    return getattr(oracle, fmt + "_dequant")
+
+
+def random_blocks(fmt: str, n_blocks: int, seed: int) -> np.ndarray:
+    """Uniformly random block bytes (every code, including Q8_0's -128) with the
+    scale forced finite and normal: exponent field 5..20 of binary16, so no
+    product overflows or is subnormal."""
+    b = BLOCK_BYTES[fmt]
+    blob = wl.uniform_bytes(seed, n_blocks * b).reshape(n_blocks, b)
+    expo = wl.uniform_ints(seed + 1, 5, 21, n_blocks).astype(np.uint8)
+    blob[:, 1] = (blob[:, 1] & 0x83) | (expo << 2)
+    return blob.reshape(-1)
 
 
 def assert_within_tolerance(y_gpu: np.ndarray, y_ref: np.ndarray, bound: np.ndarray, what=""):

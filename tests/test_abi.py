@@ -82,66 +82,79 @@ BASE = 0x7F0000000000       # fake, 16-byte aligned device-looking addresses
 A, W, Y = BASE, BASE + (1 << 32), BASE + (2 << 32)
 
 
+BLOCK_BYTES = {"q4": 18, "q8": 34}
+
+
 def _prod(entry, a, w, wb, y, M, N, K):
-    if entry == "q4_gemm":   # no workspace: these checks all come before its own
+    if entry.endswith("_gemm"):   # no workspace: these checks all come before its own
         return binding.raw_status(entry, a, w, wb, y, M, N, K, 0, 0, 0)
     return binding.raw_status(entry, a, w, wb, y, M, N, K, 0)
 
 
-def _wb(N, K):
-    return N * (K // 32) * 18
+def _wb(N, K, fmt="q4"):
+    return N * (K // 32) * BLOCK_BYTES[fmt]
 
 
 @fake_addresses
-@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm"])
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm", "q8_gemv", "q8_gemm"])
 def test_product_argument_checks(entry):
     S = binding
-    assert _prod(entry, A, W, _wb(4, 64), Y, 1, 4, 48) == S.Q4_ERR_SHAPE      # K % 32
+    f = entry[:2]
+    wb = lambda N, K: _wb(N, K, f)
+    # A blob of the other format's length is a size error.
+    other = _wb(4, 64, "q8" if f == "q4" else "q4")
+    assert _prod(entry, A, W, other, Y, 1, 4, 64) == S.Q4_ERR_SIZE
+    assert _prod(entry, A, W, wb(4, 64), Y, 1, 4, 48) == S.Q4_ERR_SHAPE      # K % 32
     assert _prod(entry, A, W, 0, Y, 1, 4, 0) == S.Q4_ERR_SHAPE                # K < 32
-    assert _prod(entry, A, W, _wb(4, 64), Y, -1, 4, 64) == S.Q4_ERR_SHAPE
-    assert _prod(entry, A, W, _wb(4, 64), Y, 1, -4, 64) == S.Q4_ERR_SHAPE
-    assert _prod(entry, A, W, _wb(4, 64) + 1, Y, 1, 4, 64) == S.Q4_ERR_SIZE   # blob length
-    assert _prod(entry, A, W, _wb(4, 64) - 18, Y, 1, 4, 64) == S.Q4_ERR_SIZE
-    assert _prod(entry, None, W, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_NULL
-    assert _prod(entry, A, None, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_NULL
-    assert _prod(entry, A, W, _wb(4, 64), None, 1, 4, 64) == S.Q4_ERR_NULL
-    assert _prod(entry, A + 4, W, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_ALIGN
-    assert _prod(entry, A, W + 2, _wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_ALIGN
-    assert _prod(entry, A, W, _wb(4, 64), Y + 8, 1, 4, 64) == S.Q4_ERR_ALIGN
-    assert _prod(entry, A, W, _wb(4, 64), A + 128, 2, 4, 64) == S.Q4_ERR_ALIAS  # y inside a
-    assert _prod(entry, A, W, _wb(4, 64), W + 32, 1, 4, 64) == S.Q4_ERR_ALIAS   # y inside w
-    assert _prod(entry, A, W, _wb(8, 64), W - 16, 1, 8, 64) == S.Q4_ERR_ALIAS   # y ends inside w
+    assert _prod(entry, A, W, wb(4, 64), Y, -1, 4, 64) == S.Q4_ERR_SHAPE
+    assert _prod(entry, A, W, wb(4, 64), Y, 1, -4, 64) == S.Q4_ERR_SHAPE
+    assert _prod(entry, A, W, wb(4, 64) + 1, Y, 1, 4, 64) == S.Q4_ERR_SIZE   # blob length
+    assert _prod(entry, A, W, wb(4, 64) - BLOCK_BYTES[f], Y, 1, 4, 64) == S.Q4_ERR_SIZE
+    assert _prod(entry, None, W, wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_NULL
+    assert _prod(entry, A, None, wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_NULL
+    assert _prod(entry, A, W, wb(4, 64), None, 1, 4, 64) == S.Q4_ERR_NULL
+    assert _prod(entry, A + 4, W, wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_ALIGN
+    assert _prod(entry, A, W + 2, wb(4, 64), Y, 1, 4, 64) == S.Q4_ERR_ALIGN
+    assert _prod(entry, A, W, wb(4, 64), Y + 8, 1, 4, 64) == S.Q4_ERR_ALIGN
+    assert _prod(entry, A, W, wb(4, 64), A + 128, 2, 4, 64) == S.Q4_ERR_ALIAS  # y inside a
+    assert _prod(entry, A, W, wb(4, 64), W + 32, 1, 4, 64) == S.Q4_ERR_ALIAS   # y inside w
+    assert _prod(entry, A, W, wb(8, 64), W - 16, 1, 8, 64) == S.Q4_ERR_ALIAS   # y ends inside w
     # empty problems: OK without looking at the pointers
-    assert _prod(entry, None, None, _wb(4, 64), None, 0, 4, 64) == S.Q4_OK
+    assert _prod(entry, None, None, wb(4, 64), None, 0, 4, 64) == S.Q4_OK
     assert _prod(entry, None, None, 0, None, 3, 0, 64) == S.Q4_OK
 
 
 @fake_addresses
-def test_gemv_row_limit():
-    assert _prod("q4_gemv", A, W, _wb(4, 64), Y, 9, 4, 64) == binding.Q4_ERR_SHAPE
-    assert _prod("q4_gemv", None, None, _wb(4, 64), None, 0, 4, 64) == binding.Q4_OK
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemv_row_limit(f):
+    assert _prod(f + "_gemv", A, W, _wb(4, 64, f), Y, 9, 4, 64) == binding.Q4_ERR_SHAPE
+    assert _prod(f + "_gemv", None, None, _wb(4, 64, f), None, 0, 4, 64) == binding.Q4_OK
 
 
 @fake_addresses
 def test_size_overflow():
     # 32-bit M, N, K cannot overflow a 64-bit byte count, but element counts can.
     assert binding.raw_status("q4_dequant", W, 18 * 2 ** 60, Y, 0, 0) == binding.Q4_ERR_SIZE
+    assert binding.raw_status("q8_dequant", W, 34 * 2 ** 60, Y, 0, 0) == binding.Q4_ERR_SIZE
     assert binding.raw_status("q8_quantize", A, 2 ** 63, Y, 2 ** 58 * 34, 0) == binding.Q4_ERR_SIZE
 
 
 @fake_addresses
-def test_dequant_argument_checks():
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_dequant_argument_checks(f):
     S = binding
-    st = lambda w, wb, o, oe: binding.raw_status("q4_dequant", w, wb, o, oe, 0)
-    assert st(W, 35, Y, 64) == S.Q4_ERR_SIZE
-    assert st(W, 36, Y, 63) == S.Q4_ERR_SIZE
+    b = BLOCK_BYTES[f]
+    st = lambda w, wb, o, oe: binding.raw_status(f + "_dequant", w, wb, o, oe, 0)
+    assert st(W, 2 * b - 1, Y, 64) == S.Q4_ERR_SIZE
+    assert st(W, 2 * b, Y, 63) == S.Q4_ERR_SIZE
+    assert st(W, 2 * BLOCK_BYTES["q4" if f == "q8" else "q8"], Y, 64) == S.Q4_ERR_SIZE
     assert st(None, 0, None, 0) == S.Q4_OK
-    assert st(None, 36, Y, 64) == S.Q4_ERR_NULL
-    assert st(W, 36, None, 64) == S.Q4_ERR_NULL
-    assert st(W + 2, 36, Y, 64) == S.Q4_ERR_ALIGN
-    assert st(W, 36, Y + 4, 64) == S.Q4_ERR_ALIGN
-    assert st(W, 36, W + 16, 64) == S.Q4_ERR_ALIAS
-    assert st(W, 36, W - 240, 64) == S.Q4_ERR_ALIAS
+    assert st(None, 2 * b, Y, 64) == S.Q4_ERR_NULL
+    assert st(W, 2 * b, None, 64) == S.Q4_ERR_NULL
+    assert st(W + 2, 2 * b, Y, 64) == S.Q4_ERR_ALIGN
+    assert st(W, 2 * b, Y + 4, 64) == S.Q4_ERR_ALIGN
+    assert st(W, 2 * b, W + 16, 64) == S.Q4_ERR_ALIAS
+    assert st(W, 2 * b, W - 240, 64) == S.Q4_ERR_ALIAS
 
 
 @fake_addresses
@@ -172,8 +185,9 @@ def test_rejected_call_writes_nothing():
     assert (y == 7.0).all()
 
 
-def test_gemm_workspace_bytes():
-    f = binding.q4_gemm_workspace_bytes
+@pytest.mark.parametrize("fn", ["q4_gemm_workspace_bytes", "q8_gemm_workspace_bytes"])
+def test_gemm_workspace_bytes(fn):
+    f = getattr(binding, fn)
     # Rows padded to whole 128-row tiles, binary16 hi and lo per element.
     assert f(1, 1, 64) == 128 * 64 * 4
     assert f(128, 7, 4096) == 128 * 4096 * 4
@@ -187,12 +201,14 @@ def test_gemm_workspace_bytes():
 
 
 @fake_addresses
-def test_gemm_workspace_checks():
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemm_workspace_checks(f):
     S = binding
     M, N, K = 3, 4, 64
-    need = binding.q4_gemm_workspace_bytes(M, N, K)
+    need = getattr(binding, f + "_gemm_workspace_bytes")(M, N, K)
     WS = BASE + (3 << 32)
-    st = lambda ws, wsb: binding.raw_status("q4_gemm", A, W, _wb(N, K), Y, M, N, K, ws, wsb, 0)
+    wbn = _wb(N, K, f)
+    st = lambda ws, wsb: binding.raw_status(f + "_gemm", A, W, wbn, Y, M, N, K, ws, wsb, 0)
     assert st(WS, need - 1) == S.Q4_ERR_WORKSPACE
     assert st(None, 0) == S.Q4_ERR_WORKSPACE
     assert st(None, need) == S.Q4_ERR_NULL
@@ -201,8 +217,8 @@ def test_gemm_workspace_checks():
     assert st(W - need + 16, need) == S.Q4_ERR_ALIAS                 # ends inside w
     assert st(Y, need) == S.Q4_ERR_ALIAS                             # on y
     # Checks of a, w and y come first, and an empty problem needs nothing.
-    assert binding.raw_status("q4_gemm", A, W, _wb(N, K), Y, M, N, 48, None, 0, 0) == S.Q4_ERR_SHAPE
-    assert binding.raw_status("q4_gemm", None, None, _wb(N, K), None, 0, N, K, None, 0, 0) == S.Q4_OK
+    assert binding.raw_status(f + "_gemm", A, W, wbn, Y, M, N, 48, None, 0, 0) == S.Q4_ERR_SHAPE
+    assert binding.raw_status(f + "_gemm", None, None, wbn, None, 0, N, K, None, 0, 0) == S.Q4_OK
 
 
 @fake_addresses

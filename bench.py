@@ -227,7 +227,7 @@ def bench_dequant(torch, q4, wl, steps, warmup, name="dequant_14336x4096"):
     t = run_timed(torch, fn, steps, warmup)
     algo = blob.numel() + N * K * 4
     kern_s = t["kernel_us"] * 1e-6
-    kernel = "k_dequant_" + fmt
+    kernel = "k_dequant<%s>" % FMT_TYPE[fmt]
     row = {"workload": name, "format": fmt, "kernel": kernel,
            "cache": "cold (%d MB per call)" % round(algo / 1e6), "algorithmic_bytes": algo, **t,
            "kernel_GBs": algo / kern_s / 1e9, "job_GBs": algo * steps / t["wall_s"] / 1e9}

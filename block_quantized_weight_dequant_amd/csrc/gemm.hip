@@ -259,8 +259,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
 }
 
 constexpr int kSplitGemmThreads = 512;
-constexpr int kARing = 3;   // activation slabs in LDS
-constexpr int kBRing = 4;   // raw weight stages in LDS
+constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
 
 // Per-format geometry of one pair of blocks.
 template <class F>
@@ -272,11 +271,30 @@ struct PairGeom {
     static constexpr int kLoads = 4 + kBLoads;                        // loads per wavefront per pair
 };
 
+// Ring depths: a pair's activation slab is loaded kA steps before the pair is
+// computed, its raw weight bytes kB >= kA steps before. Measured on MI355X
+// (2048 x 14336 x 4096, one process): Q4_0 is fastest at 4 / 4 (3 / 3 costs
+// 2.5 %, deeper weight rings cost more), Q8_0, whose four activation stages
+// do not fit next to its weight stages, at 3 / 4.
+template <class F>
+struct RingDepth;
+template <>
+struct RingDepth<FmtQ4_0> {
+    static constexpr int kA = 4, kB = 4;
+};
+template <>
+struct RingDepth<FmtQ8_0> {
+    static constexpr int kA = 3, kB = 4;
+};
+
 template <class F>
 struct SplitLds {
-    u32x4 a[kARing][2 * kOpsPerBlockTile];   // 32 KB each, [kg][hl][sub][lane], as in the workspace
-    uint32_t b[kBRing][PairGeom<F>::kBSlots];   // [row][kDwords]; slots past the tile are never read
+    static constexpr int DA = RingDepth<F>::kA, DB = RingDepth<F>::kB;
+    u32x4 a[DA][2 * kOpsPerBlockTile];      // 32 KB each, [kg][hl][sub][lane], as in the workspace
+    uint32_t b[DB][PairGeom<F>::kBSlots];   // [row][kDwords]; slots past the tile are never read
 };
+static_assert(sizeof(SplitLds<FmtQ4_0>) <= kLdsBytes && sizeof(SplitLds<FmtQ8_0>) <= kLdsBytes,
+              "the rings fit in LDS");
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(n) lgkmcnt(0), expcnt unchanged.
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
@@ -301,7 +319,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     int N, int K, int tiles_m, int tiles_n)
 {
     using G = PairGeom<F>;
-    constexpr int NL = G::kLoads;
+    constexpr int NL = G::kLoads, NB = G::kBLoads;
+    constexpr int DA = RingDepth<F>::kA, DB = RingDepth<F>::kB;
+    static_assert(DA >= 3 && DB >= DA, "ring depths");
     __shared__ SplitLds<F> lds;
 
     const int T = tiles_m * tiles_n, L = blockIdx.x;
@@ -319,35 +339,31 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
 
     // Direct-to-LDS loads, NL per wavefront per pair (so every wavefront's
     // vmcnt moves in the same steps). A: four 16-byte loads, 1 KB each, at
-    // entries (4 wave + i) * 64 + lane of the slab, whose workspace order is
-    // the LDS order. B: kBLoads 4-byte loads at dword slots j * 64 + lane, j =
-    // wave + 8 r; slot t < 128 kDwords is dword t % kDwords of the pair's bytes
-    // of row t / kDwords, higher slots re-read a valid dword into unused LDS.
+    // entries (4 wave + i) * 64 + lane of the slab, whose workspace order is the
+    // LDS order. B: NB 4-byte loads at dword slots j * 64 + lane, j = wave + 8 r;
+    // slot t < 128 kDwords is dword t % kDwords of the pair's bytes of row
+    // t / kDwords, higher slots re-read a valid dword into unused LDS.
     const u32x4 *asrc = ahl + (size_t)mt * nblk * kOpsPerBlockTile + wave * 4 * 64 + lane;
-    const uint8_t *bsrc[G::kBLoads];
+    const uint8_t *bsrc[NB];
 #pragma unroll
-    for (int r = 0; r < G::kBLoads; ++r) {
+    for (int r = 0; r < NB; ++r) {
         const int tt = min((wave + 8 * r) * 64 + lane, G::kBDwords - 1);
         const int row = tt / G::kDwords, dw = tt % G::kDwords;
         bsrc[r] = w + (size_t)min(n0 + row, N - 1) * row_bytes + 4 * dw;
     }
-    // Load k (0 .. NL-1) of pair p: four A loads, then the B loads.
-    auto issue_load = [&](int p, int k) __attribute__((always_inline)) {
+    // Load k (0 .. NL-1) of a step: the four A loads of pair pa, then the NB B
+    // loads of pair pb (k is a compile-time constant where this is called).
+    auto issue_load = [&](int pa, int pb, int k) __attribute__((always_inline)) {
         if (k < 4)
             __builtin_amdgcn_global_load_lds(
-                (const void *)(asrc + (size_t)p * 2 * kOpsPerBlockTile + k * 64),
-                (__attribute__((address_space(3))) void *)(lds.a[p % kARing] + (wave * 4 + k) * 64),
+                (const void *)(asrc + (size_t)pa * 2 * kOpsPerBlockTile + k * 64),
+                (__attribute__((address_space(3))) void *)(lds.a[pa % DA] + (wave * 4 + k) * 64),
                 16, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(
-                (const void *)(bsrc[k - 4] + 2 * F::kBytes * p),
-                (__attribute__((address_space(3))) void *)(lds.b[p % kBRing] + (wave + 8 * (k - 4)) * 64),
+                (const void *)(bsrc[k - 4] + 2 * F::kBytes * pb),
+                (__attribute__((address_space(3))) void *)(lds.b[pb % DB] + (wave + 8 * (k - 4)) * 64),
                 4, 0, 0);
-    };
-    auto issue_pair = [&](int p) __attribute__((always_inline)) {
-#pragma unroll
-        for (int k = 0; k < NL; ++k)
-            issue_load(p, k);
     };
 
     f32x4 acc[4][4];
@@ -374,25 +390,28 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             const uint32_t *rb = bstage + (wn * 64 + ns * 16 + li) * G::kDwords;
             return BCol{read_qs_raw<F, KG>(rb, g), rb[d_dword<F, KG>()]};
         };
-        struct AOps {
+        // The operands of one pair held in registers: the A operands of the
+        // wavefront's four row groups and the raw B bytes of its four column
+        // groups.
+        struct Ops {
             f16x8 hi[4], lo[4];
+            BCol b[4];
         };
-        auto read_a = [&](const u32x4 *slab, AOps &A) __attribute__((always_inline)) {
-            const u32x4 *ap = slab + KG * kOpsPerBlockTile + wm * 4 * 64 + lane;
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                A.hi[ms] = bitcast<f16x8>(ap[ms * 64]);
-                A.lo[ms] = bitcast<f16x8>(ap[8 * 64 + ms * 64]);
-            }
+        // Part i of pair q's operands (row group i, column group i).
+        auto read_ops = [&](int q, Ops &o, int i) __attribute__((always_inline)) {
+            const u32x4 *ap = lds.a[q % DA] + KG * kOpsPerBlockTile + wm * 4 * 64 + lane;
+            o.hi[i] = bitcast<f16x8>(ap[i * 64]);
+            o.lo[i] = bitcast<f16x8>(ap[8 * 64 + i * 64]);
+            o.b[i] = read_b(lds.b[q % DB], i);
         };
+        constexpr int kDsReads = 2 + QsRaw<F, KG>::n + 1;   // LDS reads of one part
 
         // Software pipeline over the four column groups of a pair: the MFMAs of
         // group ns are issued between the scale FMAs of group ns - 1 (whose results
         // are ready) and the decode of group ns + 1. Group results alternate
         // between two register sets by the parity of ns, and the group before
         // group 0 is group 3 of the previous pair (zeros before the first pair),
-        // so every index is a compile-time constant. The scheduling-group barriers
-        // ask for one MFMA then four VALU instructions, eight times per group.
+        // so every index is a compile-time constant.
         f32x4 cbuf[2][4];
         float dbuf[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -415,28 +434,34 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         };
         // One scheduling region per column group ns: its eight MFMAs (the four hi
         // products, then the four lo products that add onto them) interleaved
-        // with the scale FMAs of group ns - 1 and the decode of group ns + 1.
-        // Hard scheduling barriers between regions keep that order.
-        auto compute_pair = [&](const BCol (&bcol)[4], const AOps &A, int dma_pair) __attribute__((always_inline)) {
-            BOps cur = decode_b(bcol[0]);
+        // with the scale FMAs of group ns - 1, the decode of group ns + 1 and
+        // part ns of the next pair's operands (LDS reads that land during this
+        // pair's MFMAs, so no step starts by waiting on LDS). The scheduling-group
+        // barriers ask for one MFMA, one LDS read while any remain, then four VALU
+        // instructions, eight times per region; hard barriers between regions
+        // keep that order.
+        auto compute_pair = [&](const Ops &cur_ops, Ops &next_ops, int next_pair, int dma_a,
+                                int dma_b) __attribute__((always_inline)) {
+            BOps cur = decode_b(cur_ops.b[0]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
-                // The loads of pair dma_pair go out spread over the four regions
-                // (loads [NL ns / 4, NL (ns + 1) / 4), rounded up), between MFMAs, so
-                // the address unit works while the matrix cores do and no
-                // wavefront's MFMAs queue behind a load.
-                if (dma_pair >= 0) {
-#pragma unroll
-                    for (int k = (NL * ns + 3) / 4; k < (NL * (ns + 1) + 3) / 4; ++k)
-                        issue_load(dma_pair, k);
-                }
                 f32x4 *c = cbuf[ns & 1];
                 const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
                 const float dp = dbuf[(ns + 1) & 1];
 #pragma unroll
                 for (int ms = 0; ms < 4; ++ms)
-                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.hi[ms], cur.q, zero4, 0, 0, 0);
+                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.hi[ms], cur.q, zero4, 0, 0, 0);
+                read_ops(next_pair, next_ops, ns);
+                // The step's loads go out spread over the four regions (loads
+                // [NL ns / 4, NL (ns + 1) / 4), rounded up) and, within a region,
+                // between MFMAs, so the address unit works while the matrix cores
+                // do and no wavefront's MFMAs queue behind a load. They write LDS,
+                // so they follow this region's LDS reads in program order (the
+                // compiler keeps LDS accesses it cannot tell apart in order).
+#pragma unroll
+                for (int k = (NL * ns + 3) / 4; k < (NL * (ns + 1) + 3) / 4; ++k)
+                    issue_load(dma_a, dma_b, k);
                 const int np = (ns + 3) & 3;
 #pragma unroll
                 for (int ms = 0; ms < 4; ++ms)
@@ -448,14 +473,20 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]));
                 BOps nxt = cur;
                 if (ns + 1 < 4)
-                    nxt = decode_b(bcol[ns + 1]);
+                    nxt = decode_b(cur_ops.b[ns + 1]);
 #pragma unroll
                 for (int ms = 0; ms < 4; ++ms)
-                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A.lo[ms], cur.s, c[ms], 0, 0, 0);
+                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.lo[ms], cur.s, c[ms], 0, 0, 0);
                 dbuf[ns & 1] = cur.d;
+                constexpr int kRegionLoads = 3;   // at most (NL ns / 4 ranges hold 1 .. 3)
+                const int nl = (NL * (ns + 1) + 3) / 4 - (NL * ns + 3) / 4;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    if (u < kDsReads)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    if (u >= 8 - nl && u >= 8 - kRegionLoads)
+                        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one load
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -463,50 +494,60 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             }
         };
 
-        // Ring schedule: pair q is loaded (activation slab into A slot q % 3, raw
-        // weight bytes into B slot q % 4) during step q - 3, is complete by the
-        // barrier ending step q - 2, has its A operands read into registers
-        // during step q - 1 and its B bytes read at the start of step q, and is
-        // computed in step q. A slot q % 3 is loaded again (pair q + 3) in step
-        // q, after the barrier that ends step q - 1, by which every wavefront has
-        // read it into registers; B slot q % 4 is loaded again (pair q + 4) in
-        // step q + 1, after the barrier that ends step q.
-        const int pre = min(npairs, 3);
-        for (int p = 0; p < pre; ++p)
-            issue_pair(p);
-        if (pre == 3)
-            ring_barrier<NL>();   // pairs 0 and 1 complete, pair 2 in flight
-        else
-            ring_barrier<0>();
-        AOps A0, A1;
-        read_a(lds.a[0], A0);
-        // Step 0 reloads A slot 0 (pair 3): every wavefront must have read pair
-        // 0's slab first.
-        if (pre == 3)
-            ring_barrier<NL>();
-        else
-            ring_barrier<0>();
-        auto step = [&](int p, const AOps &Acur, AOps &Anext) __attribute__((always_inline)) {
-            // This pair's raw weight dwords first (one wait covers them), then
-            // the next pair's A operands, which land during this pair's MFMAs.
-            BCol bcol[4];
+        // Ring schedule: step p issues the A loads of pair p + DA, then the B loads
+        // of pair p + DB, so pair q's A slab goes to A stage q % DA during step
+        // q - DA and its B bytes to B stage q % DB during step q - DB. Both are
+        // complete by the barrier ending step q - 2, are read into registers
+        // during step q - 1, and pair q is computed in step q. Each stage is
+        // loaded again in step q (pair q + DA or q + DB), after the barrier that
+        // ends step q - 1, by which every wavefront has read it. Loads complete
+        // in issue order. The last loads pair p + 2 needs are its A loads (step
+        // p + 2 - DA) when DB > DA, else its B loads, which follow them in the
+        // same step; at the barrier ending step p the loads issued after those
+        // may still be in flight: the B loads of that step (when DB > DA) and all
+        // loads of the DA - 2 later steps (near the end, where fewer are issued,
+        // the barrier waits for everything). The last step reads stages no load
+        // is writing any more, and discards what it read.
+        constexpr int kInFlight = (DB > DA ? NB : 0) + (DA - 2) * NL;
+        static_assert(kInFlight < 64, "vmcnt counts to 63");
+        // The loads of steps -DB .. -1, in the order those steps would issue them
+        // (a step before the first A load issues only its B loads). A step whose
+        // pair is past the last one reloads the last pair into its own stage
+        // (the same bytes), so every step issues NL loads and, with at least DB
+        // pairs, every barrier can count them; shorter problems wait for all.
+        const bool counted = npairs >= DB;
+        const int last = npairs - 1;
+        for (int t = -DB; t < 0; ++t) {
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns)
-                bcol[ns] = read_b(lds.b[p % kBRing], ns);
-            __builtin_amdgcn_sched_barrier(0);
-            if (p + 1 < npairs)
-                read_a(lds.a[(p + 1) % kARing], Anext);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_pair(bcol, Acur, p + 3 < npairs ? p + 3 : -1);
-            if (p + 3 < npairs)
-                ring_barrier<NL>();   // pair p + 2 complete, pair p + 3 in flight
+            for (int k = 0; k < NL; ++k)
+                if (k >= 4 || t + DA >= 0)
+                    issue_load(min(t + DA, last), min(t + DB, last), k);
+        }
+        if (counted)
+            ring_barrier<kInFlight>();   // pairs 0 and 1 complete
+        else
+            ring_barrier<0>();
+        Ops O0, O1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            read_ops(0, O0, i);
+        // Step 0 reloads stage 0 of both rings: every wavefront must have read
+        // pair 0's operands first.
+        if (counted)
+            ring_barrier<kInFlight>();
+        else
+            ring_barrier<0>();
+        auto step = [&](int p, const Ops &cur_ops, Ops &next_ops) __attribute__((always_inline)) {
+            compute_pair(cur_ops, next_ops, p + 1, min(p + DA, last), min(p + DB, last));
+            if (counted)
+                ring_barrier<kInFlight>();   // pair p + 2 complete
             else
                 ring_barrier<0>();
         };
         for (int p = 0; p < npairs; p += 2) {
-            step(p, A0, A1);
+            step(p, O0, O1);
             if (p + 1 < npairs)
-                step(p + 1, A1, A0);
+                step(p + 1, O1, O0);
         }
         // FMAs of the last column group (group 3 of the last pair, in set 1).
 #pragma unroll

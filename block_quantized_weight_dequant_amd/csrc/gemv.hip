@@ -248,7 +248,11 @@ struct GemvStreamCfg {
     static constexpr int RS = CH * F::kBytes + 16;        // LDS bytes per staged row
     static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
     static constexpr int NI = 2 * M;                      // A rows in use
-    static constexpr int ABYTES = CH * 4 * NI * 16;       // A operands per wavefront
+    // The A operands of a chunk pass through LDS in AH halves when a whole
+    // chunk's would not fit (16 blocks of more than four rows).
+    static constexpr int AH = (CH == 16 && M > 4) ? 2 : 1;
+    static constexpr int CHH = CH / AH;                   // blocks per A pass
+    static constexpr int ABYTES = CHH * 4 * NI * 16;      // A operands per wavefront
     static constexpr int NENT = CH * 4 * M;               // 8-element activation groups per chunk
     static constexpr int EPL = (NENT + 63) / 64;          // ... per lane
     static constexpr int LDS_PER_WAVE = WBYTES + ABYTES;
@@ -418,11 +422,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
 #pragma unroll
         for (int m = 0; m < M; ++m)
             pexp[m] = row_scale_exp<F>(wave_max_nonneg(mx[m]));
+        // Each pass writes the groups of its blocks (a lane's groups all belong
+        // to one block, b = (lane / 4) % CH) and reads them back as A operands
+        // at once; the next pass reuses the same LDS area.
+#pragma unroll
+        for (int h = 0; h < C::AH; ++h) {
+        if (h > 0)
+            wave_lds_sync();   // the previous pass's reads precede these writes
 #pragma unroll
         for (int r = 0; r < C::EPL; ++r) {
             const int e = lane + 64 * r;
             const int me = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
-            if (e < C::NENT) {
+            if (e < C::NENT && b / C::CHH == h) {
                 int pm = 0;
 #pragma unroll
                 for (int m = 0; m < M; ++m)
@@ -440,7 +451,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
                     hi[s] = hh;
                     lo[s] = ll;
                 }
-                u32x4 *dst = reinterpret_cast<u32x4 *>(s_a + b * ASTRIDE + (gg * C::NI + 2 * me) * 16);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(s_a + (b % C::CHH) * ASTRIDE +
+                                                       (gg * C::NI + 2 * me) * 16);
                 dst[0] = bitcast<u32x4>(hi);
                 dst[1] = bitcast<u32x4>(lo);
             }
@@ -451,8 +463,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
         wave_lds_sync();
         if (j < C::NI) {
 #pragma unroll
-            for (int b = 0; b < C::CH; ++b)
-                aop[b] = *reinterpret_cast<const f16x8 *>(a_lane + b * ASTRIDE);
+            for (int b = h * C::CHH; b < (h + 1) * C::CHH; ++b)
+                aop[b] = *reinterpret_cast<const f16x8 *>(a_lane + (b - h * C::CHH) * ASTRIDE);
+        }
         }
     };
 
@@ -573,18 +586,17 @@ static hipError_t launch_gemv_m(const float *a, const uint8_t *w, float *y, int 
     // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0 and
     // a row is a whole number of 16-byte columns in either format) and 32-bit
     // byte offsets. Each wavefront gets `per` blocks (a multiple of 8); chunks
-    // of 16 blocks when every wavefront's share divides by 16, else 8.
+    // of 16 blocks when every wavefront's share divides by 16 (one memory round
+    // trip for the whole share at K = 4096), else 8.
     constexpr int NW = kGemvStreamWaves;
     const int nblk = K / 32;
     if (K % 256 == 0 && (size_t)N * (size_t)nblk * F::kBytes < ((size_t)1 << 31) &&
         (size_t)M * (size_t)K * 4 < ((size_t)1 << 31)) {
         const int per = (((nblk + NW - 1) / NW) + 7) & ~7;
         const int last = nblk - (nblk - 1) / per * per;       // blocks of the last busy wavefront
-        if constexpr (M <= 4) {
-            if (per % 16 == 0 && last % 16 == 0)
-                return launch_kernel(k_gemv_stream<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s,
-                                     a, w, y, N, K, per);
-        }
+        if (per % 16 == 0 && last % 16 == 0)
+            return launch_kernel(k_gemv_stream<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s, a,
+                                 w, y, N, K, per);
         return launch_kernel(k_gemv_stream<F, M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, a, w, y,
                              N, K, per);
     }

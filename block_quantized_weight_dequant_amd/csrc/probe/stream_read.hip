@@ -1,6 +1,6 @@
 // Streaming-read ceiling kernel of libq4probe.so (include/q4_probe.h): each
-// thread XORs a grid-strided run of 16-byte words. Measurement only; no part
-// of the Q4_0 method.
+// thread XORs a few grid-strided 16-byte words. Measurement only; no part of
+// the block-quantized method.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,24 +10,37 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void k_stream_read(const u32x4 *__restrict__ src,
-                                                         size_t n16, u32x4 *__restrict__ sink)
+// Thread t reads words t, t + S, ..., t + (R - 1) S (S = all threads of the
+// grid), every load issued before any is used, so each thread has R loads in
+// flight at once and no load waits for another.
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_stream_read(const u32x4 *__restrict__ src, size_t n16,
+                                                         u32x4 *__restrict__ sink)
 {
     const size_t stride = (size_t)gridDim.x * kThreads;
-    u32x4 acc = {0u, 0u, 0u, 0u};
-    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-    // Four independent loads in flight per thread per iteration.
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride],
-                    x3 = src[i + 3 * stride];
-        acc ^= x0 ^ x1 ^ x2 ^ x3;
+    const size_t i0 = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    u32x4 x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const size_t i = i0 + r * stride;
+        x[r] = i < n16 ? src[i] : (u32x4){0u, 0u, 0u, 0u};
     }
-    for (; i < n16; i += stride)
-        acc ^= src[i];
+    u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc ^= x[r];
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x5bd1e995u)
         *sink = acc;
+}
+
+template <int R>
+hipError_t launch_read(const u32x4 *src, size_t n16, u32x4 *sink, hipStream_t s)
+{
+    const size_t blocks = (n16 + (size_t)R * kThreads - 1) / ((size_t)R * kThreads);
+    hipLaunchKernelGGL(k_stream_read<R>, dim3((unsigned)blocks), dim3(kThreads), 0, s, src, n16, sink);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -45,16 +58,22 @@ extern "C" __attribute__((visibility("default"))) int q4probe_stream_read(const 
     if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) & 15u)
         return 4;
     const size_t n16 = n_bytes / 16;
-    // At least one 512-thread workgroup per CU (256), so a small buffer is
-    // read by every CU at once (its fastest shape: all loads issued up
-    // front); large buffers get up to 2048 workgroups of 16+ words a thread.
-    size_t blocks = (n16 + 16 * kThreads - 1) / (16 * kThreads);
-    if (blocks < 256)
-        blocks = 256;
-    if (blocks > 2048)
-        blocks = 2048;
-    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src), n16,
-                       static_cast<u32x4 *>(sink));
-    return hipGetLastError() == hipSuccess ? 0 : 6;
+    // One to four loads per thread: the fewest that keep the grid within
+    // 65,536 workgroups. Measured on MI355X at 9.47 MB, every load issued up
+    // front reads 13% faster than a grid-stride loop of four-load batches,
+    // whose leftover loads each wait for the one before.
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const u32x4 *in = static_cast<const u32x4 *>(src);
+    u32x4 *out = static_cast<u32x4 *>(sink);
+    const size_t per_r1 = (n16 + kThreads - 1) / kThreads;   // workgroups at one load per thread
+    if (per_r1 > 4 * (size_t)65536)
+        return 2;   // more than 4 GiB: not a size this measurement is for
+    hipError_t e;
+    if (per_r1 <= 65536)
+        e = launch_read<1>(in, n16, out, s);
+    else if (per_r1 <= 2 * (size_t)65536)
+        e = launch_read<2>(in, n16, out, s);
+    else
+        e = launch_read<4>(in, n16, out, s);
+    return e == hipSuccess ? 0 : 6;
 }

@@ -21,6 +21,9 @@ What each function follows (the docs.rs page "fuel-vulkan-kernels — quantized
 * ``q4_0_quantize``  GGML's Q4_0 reference rule as stated with the benchmark
                      workloads (not on the pages); it only makes test weights.
 * ``f16_to_f32`` / ``f32_to_f16``  IEEE 754 binary16 (round to nearest even).
+* ``bf16_to_f32``    bfloat16 activations widened to f32 (exact: bfloat16 is
+                     the upper half of binary32); the products of bfloat16
+                     activations are the f32 products of the widened values.
 
 Every function is pinned in ``tests/test_oracle_pins.py`` against values that
 do not come from this module: hand-worked blocks, library routines
@@ -71,6 +74,8 @@ def _load():
     lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
     lib.orc_f32_to_f16.restype = ctypes.c_uint16
     lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.orc_bf16_to_f32_array.restype = None
+    lib.orc_bf16_to_f32_array.argtypes = [P, sz, P]
     for name in ("orc_q4_0_dequant", "orc_q8_0_dequant"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [P, sz, P]
@@ -112,6 +117,15 @@ def f16_to_f32(bits: int) -> np.float32:
 
 def f32_to_f16(value) -> int:
     return int(_load().orc_f32_to_f16(float(np.float32(value))))
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """bfloat16 bit patterns (any shape, uint16) -> f32 values of that shape."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    if b.size:
+        _load().orc_bf16_to_f32_array(_ptr(b), b.size, _ptr(out))
+    return out
 
 
 # -------------------------------------------------------------------- Q4_0

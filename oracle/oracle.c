@@ -44,6 +44,24 @@
  * ("quantize_q8_0": the f16-narrowed d). Byte order of the stored d is not
  * stated on the pages; this oracle reads it little-endian (GGML's order). */
 
+/* bfloat16 -> binary32. A bfloat16 value is the binary32 value whose upper
+ * 16 bits are its bits and whose lower 16 bits are zero (the format is the
+ * top half of binary32), so the widening is exact. Activations given as
+ * bfloat16 enter the products through this. */
+float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+void orc_bf16_to_f32_array(const uint16_t *h, size_t n, float *out)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = orc_bf16_to_f32(h[i]);
+}
+
 /* binary16 -> binary32. Exact: every binary16 value is a binary32 value. */
 float orc_f16_to_f32(uint16_t h)
 {

@@ -84,6 +84,17 @@ def test_f16_encode_round_to_nearest_even(orc):
     assert bad.size == 0, [(float(xs[i]), hex(got[i]), hex(expected[i])) for i in bad[:5]]
 
 
+def test_bf16_decode_every_pattern(orc):
+    # Every bfloat16 pattern against PyTorch's CPU bfloat16 -> float32 conversion.
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.bf16_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (_bits32(got[~nan]) == _bits32(ref[~nan])).all()
+
+
 def test_f16_special_values(orc):
     assert orc.f32_to_f16(float("inf")) == 0x7C00
     assert orc.f32_to_f16(float("-inf")) == 0xFC00

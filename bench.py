@@ -163,8 +163,10 @@ def gemv_kernel_name(M, K, fmt="q4_0"):
     return "k_gemv_stream<%s, %d, 8, %d>" % (FMT_TYPE[fmt], M, ch)
 
 
-def gemm_kernel_name(K, fmt="q4_0"):
-    return "k_gemm_split<%s>" % FMT_TYPE[fmt] if K % 64 == 0 else "k_gemm_any<%s>" % FMT_TYPE[fmt]
+def gemm_kernel_name(K, fmt="q4_0", act="f32"):
+    if K % 64:
+        return "k_gemm_any<%s>" % FMT_TYPE[fmt]
+    return "k_gemm_split<%s, %s>" % (FMT_TYPE[fmt], "true" if act == "bf16" else "false")
 
 
 def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
@@ -172,8 +174,12 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     M, N, K = s["M"], s["N"], s["K"]
     fmt = s.get("fmt", "q4_0")
     f = fmt[:2]
+    act = s.get("act", "f32")
     blob = make_weight(torch, q4, wl, N, K, s["w_seed"], fmt)
-    a = torch.from_numpy(wl.activations_f32(s["a_seed"], M, K)).cuda()
+    if act == "bf16":
+        a = torch.from_numpy(wl.activations_bf16(s["a_seed"], M, K).view("int16")).cuda()
+    else:
+        a = torch.from_numpy(wl.activations_f32(s["a_seed"], M, K)).cuda()
     y = torch.empty(M * N, dtype=torch.float32, device="cuda")
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
@@ -182,15 +188,17 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
         gemv = getattr(q4, f + "_gemv")
         fn = lambda k: gemv(a, blobs[k % R], y, M, N, K)
     else:
-        gemm = getattr(q4, f + "_gemm")
-        ws_bytes = getattr(q4, f + "_gemm_workspace_bytes")(M, N, K)
+        entry = f + ("_gemm_bf16" if act == "bf16" else "_gemm")
+        gemm = getattr(q4, entry)
+        ws_bytes = getattr(q4, entry + "_workspace_bytes")(M, N, K)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         fn = lambda k: gemm(a, blobs[k % R], y, M, N, K, workspace=ws)
     t = run_timed(torch, fn, steps, warmup)
-    algo_bytes = wbytes + M * K * 4 + M * N * 4
+    algo_bytes = wbytes + M * K * (2 if act == "bf16" else 4) + M * N * 4
     flops = 2.0 * M * N * K
     kern_s = t["kernel_us"] * 1e-6
-    row = {"workload": name, "format": fmt, "M": M, "N": N, "K": K, "weight_copies": R,
+    row = {"workload": name, "format": fmt, "activations": act, "M": M, "N": N, "K": K,
+           "weight_copies": R,
            "cache": "cold" if R > 1 else "warm (one weight copy, MALL-resident)",
            "algorithmic_bytes": algo_bytes, "flops": flops, **t,
            "kernel_GBs": algo_bytes / kern_s / 1e9, "kernel_TFLOPs": flops / kern_s / 1e12,
@@ -200,16 +208,21 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
         kernel = gemv_kernel_name(M, K, fmt)
         row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
     else:
-        kernel = gemm_kernel_name(K, fmt)
+        kernel = gemm_kernel_name(K, fmt, act)
+        if act == "bf16":
+            note = ("useful 2MNK flops over the dense f16 MFMA peak; one binary16 term per "
+                    "bfloat16 activation, so 1.0 is this design's ceiling; the time is the "
+                    "whole step (row-exponent and operand kernels plus the GEMM kernel)")
+        else:
+            note = ("useful 2MNK flops over the dense f16 MFMA peak; the two-term activation "
+                    "split issues 2 MFMA flops per useful flop, so 0.5 is this design's "
+                    "ceiling; the time is the whole step (activation split kernel plus the "
+                    "GEMM kernel)")
         row["roofline"] = {"bound": "mfma", "achieved": row["kernel_TFLOPs"],
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": row["kernel_TFLOPs"] / MFMA_F16_PEAK_TFLOPS,
                            "traffic": load_traffic(name, kernel, "gemm"), "kernel": kernel,
-                           "note": "useful 2MNK flops over the dense f16 MFMA peak; the "
-                                   "two-term activation split issues 2 MFMA flops per "
-                                   "useful flop, so 0.5 is this design's ceiling; the "
-                                   "time is the whole step (activation split kernel plus "
-                                   "the GEMM kernel)"}
+                           "note": note}
     row["kernel"] = kernel
     del blobs, blob, a, y
     torch.cuda.empty_cache()
@@ -366,6 +379,11 @@ def main():
                          ("q8_0_gemm_1024x4096x4096", 50), ("q8_0_gemm_2048x14336x4096", 20)):
             log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
+                                      min(args.warmup, 10)))
+        for name in ("gemm_bf16_1024x4096x4096", "gemm_bf16_2048x14336x4096",
+                     "q8_0_gemm_bf16_2048x14336x4096"):
+            log("row: %s" % name)
+            rows.append(bench_product(torch, q4, wl, name, min(20, args.steps),
                                       min(args.warmup, 10)))
         log("row: Q8_0 dequant 14336x4096")
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10),

@@ -31,7 +31,8 @@ SIZE_MAX = 2 ** 64 - 1
 #: Every symbol include/q4.h declares.
 EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
            "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm",
-           "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize")
+           "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize", "q4_gemm_bf16",
+           "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes")
 
 
 class Q4Error(RuntimeError):
@@ -61,10 +62,11 @@ def _load_library():
         getattr(lib, f + "_dequant").argtypes = [P, sz, P, sz, P]
         getattr(lib, f + "_gemv").restype = i32
         getattr(lib, f + "_gemv").argtypes = [P, P, sz, P, i32, i32, i32, P]
-        getattr(lib, f + "_gemm").restype = i32
-        getattr(lib, f + "_gemm").argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
-        getattr(lib, f + "_gemm_workspace_bytes").restype = sz
-        getattr(lib, f + "_gemm_workspace_bytes").argtypes = [i32, i32, i32]
+        for g in ("_gemm", "_gemm_bf16"):
+            getattr(lib, f + g).restype = i32
+            getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
+            getattr(lib, f + g + "_workspace_bytes").restype = sz
+            getattr(lib, f + g + "_workspace_bytes").argtypes = [i32, i32, i32]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -164,8 +166,15 @@ def _scratch(nbytes: int, stream, like):
     return t
 
 
-def _gemm(fmt, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes) -> None:
-    entry = fmt + "_gemm"
+def q4_gemm_bf16_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q4_gemm_bf16_workspace_bytes(int(M), int(N), int(K)))
+
+
+def q8_gemm_bf16_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q8_gemm_bf16_workspace_bytes(int(M), int(N), int(K)))
+
+
+def _gemm(entry, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes) -> None:
     wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
     ws = workspace
     if ws is None:
@@ -187,13 +196,26 @@ def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, worksp
     ``workspace=None`` takes a scratch tensor of q4_gemm_workspace_bytes(M, N, K)
     bytes from PyTorch's caching allocator for this call; pass a tensor (or an
     address with ``workspace_bytes``) to reuse one."""
-    _gemm("q4", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+    _gemm("q4_gemm", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
 
 
 def q8_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
             workspace_bytes=None) -> None:
     """As q4_gemm, with W a Q8_0 stream (workspace from q8_gemm_workspace_bytes)."""
-    _gemm("q8", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+    _gemm("q8_gemm", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+
+
+def q4_gemm_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+                 workspace_bytes=None) -> None:
+    """As q4_gemm with ``a`` a [M, K] bfloat16 tensor (or its address); the
+    workspace, from q4_gemm_bf16_workspace_bytes, is always needed."""
+    _gemm("q4_gemm_bf16", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+
+
+def q8_gemm_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+                 workspace_bytes=None) -> None:
+    """As q4_gemm_bf16, with W a Q8_0 stream."""
+    _gemm("q8_gemm_bf16", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
 
 
 def q8_quantize(x, out_q, n_elems=None, out_bytes=None, stream=None) -> None:

@@ -50,7 +50,8 @@ static int gemv(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const
                 size_t w_bytes, float *y, int M, int N, int K, void *stream)
 {
     bool empty = false;
-    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS, block_bytes, &empty);
+    int st = q4v::check_product(a, sizeof(float), w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS,
+                                block_bytes, &empty);
     if (st != Q4_OK || empty)
         return st;
     return launched(q4k::launch_gemv(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
@@ -62,15 +63,32 @@ static int gemm(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const
                 size_t workspace_bytes, void *stream)
 {
     bool empty = false;
-    int st = q4v::check_product(a, w_q, w_bytes, y, M, N, K, 0, block_bytes, &empty);
+    int st = q4v::check_product(a, sizeof(float), w_q, w_bytes, y, M, N, K, 0, block_bytes, &empty);
     if (st != Q4_OK || empty)
         return st;
-    st = q4v::check_workspace(a, w_q, w_bytes, y, M, N, K, workspace, workspace_bytes);
+    st = q4v::check_workspace(q4v::gemm_workspace_bytes(M, N, K), a, sizeof(float), w_q, w_bytes,
+                              y, M, N, K, workspace, workspace_bytes);
     if (st != Q4_OK)
         return st;
     return launched(q4k::launch_gemm(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
                                      q4v::gemm_splits_activations(K) ? workspace : nullptr,
                                      as_stream(stream)));
+}
+
+static int gemm_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *a,
+                     const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, 2, w_q, w_bytes, y, M, N, K, 0, block_bytes, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    st = q4v::check_workspace(q4v::gemm_bf16_workspace_bytes(M, N, K), a, 2, w_q, w_bytes, y, M,
+                              N, K, workspace, workspace_bytes);
+    if (st != Q4_OK)
+        return st;
+    return launched(q4k::launch_gemm_bf16(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                          workspace, as_stream(stream)));
 }
 
 Q4_EXPORT int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, void *stream)
@@ -117,6 +135,30 @@ Q4_EXPORT int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
 {
     return gemm(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, workspace,
                 workspace_bytes, stream);
+}
+
+Q4_EXPORT size_t q4_gemm_bf16_workspace_bytes(int M, int N, int K)
+{
+    return q4v::gemm_bf16_workspace_bytes(M, N, K);
+}
+
+Q4_EXPORT size_t q8_gemm_bf16_workspace_bytes(int M, int N, int K)
+{
+    return q4v::gemm_bf16_workspace_bytes(M, N, K);
+}
+
+Q4_EXPORT int q4_gemm_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y, int M,
+                           int N, int K, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_bf16(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, workspace,
+                     workspace_bytes, stream);
+}
+
+Q4_EXPORT int q8_gemm_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y, int M,
+                           int N, int K, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_bf16(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, workspace,
+                     workspace_bytes, stream);
 }
 
 Q4_EXPORT int q8_quantize(const float *x, size_t n_elems, void *out_q, size_t out_bytes, void *stream)

@@ -52,11 +52,14 @@ struct GemmStage {
     float d[kGemmBN];
 };
 
+// row_exp: when not null, row m of a was scaled by 2^row_exp[m] (the bfloat16
+// path's per-row scale), and the result row is scaled back by 2^-row_exp[m].
 template <class F>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restrict__ a,
                                                           const uint8_t *__restrict__ w,
                                                           float *__restrict__ y, int M, int N,
-                                                          int K, int tiles_m, int tiles_n)
+                                                          int K, int tiles_m, int tiles_n,
+                                                          const int *__restrict__ row_exp)
 {
     __shared__ GemmStage st[2];
 
@@ -180,11 +183,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
             const int m = m0 + wm * 64 + ms * 16 + 4 * g + q;
             if (m >= M)
                 continue;
+            const int pe = row_exp ? row_exp[m] : 0;
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
                 const int n = n0 + wn * 64 + ns * 16 + li;
                 if (n < N)
-                    y[(size_t)m * N + n] = acc[ms][ns][q];
+                    y[(size_t)m * N + n] = ldexpf(acc[ms][ns][q], -pe);
             }
         }
     }
@@ -276,24 +280,42 @@ struct PairGeom {
 // (2048 x 14336 x 4096, one process): Q4_0 is fastest at 4 / 4 (3 / 3 costs
 // 2.5 %, deeper weight rings cost more), Q8_0, whose four activation stages
 // do not fit next to its weight stages, at 3 / 4.
-template <class F>
+// HO ("hi only") selects the bfloat16-activation form: one binary16 term per
+// activation (exact, see k_gemm_prep_bf16), so a slab is half the size and a
+// tile-block needs one MFMA instead of two.
+template <class F, bool HO>
 struct RingDepth;
 template <>
-struct RingDepth<FmtQ4_0> {
+struct RingDepth<FmtQ4_0, false> {
     static constexpr int kA = 4, kB = 4;
 };
 template <>
-struct RingDepth<FmtQ8_0> {
+struct RingDepth<FmtQ8_0, false> {
     static constexpr int kA = 3, kB = 4;
 };
+template <>
+struct RingDepth<FmtQ4_0, true> {
+    static constexpr int kA = 5, kB = 5;
+};
+template <>
+struct RingDepth<FmtQ8_0, true> {
+    static constexpr int kA = 5, kB = 5;
+};
 
-template <class F>
+// 16-byte A operands per (128-row tile, block): hi and lo, or hi only.
+template <bool HO>
+constexpr int slab_ops() { return HO ? kOpsPerBlockTile / 2 : kOpsPerBlockTile; }
+
+template <class F, bool HO>
 struct SplitLds {
-    static constexpr int DA = RingDepth<F>::kA, DB = RingDepth<F>::kB;
-    u32x4 a[DA][2 * kOpsPerBlockTile];      // 32 KB each, [kg][hl][sub][lane], as in the workspace
+    static constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
+    u32x4 a[DA][2 * slab_ops<HO>()];        // a pair's slab: [kg][hl][sub][lane], as in the workspace
     uint32_t b[DB][PairGeom<F>::kBSlots];   // [row][kDwords]; slots past the tile are never read
 };
-static_assert(sizeof(SplitLds<FmtQ4_0>) <= kLdsBytes && sizeof(SplitLds<FmtQ8_0>) <= kLdsBytes,
+static_assert(sizeof(SplitLds<FmtQ4_0, false>) <= kLdsBytes &&
+                  sizeof(SplitLds<FmtQ8_0, false>) <= kLdsBytes &&
+                  sizeof(SplitLds<FmtQ4_0, true>) <= kLdsBytes &&
+                  sizeof(SplitLds<FmtQ8_0, true>) <= kLdsBytes,
               "the rings fit in LDS");
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(n) lgkmcnt(0), expcnt unchanged.
@@ -313,16 +335,19 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <class F>
+// row_exp: per-row exponents of the bfloat16 form (HO), else unused.
+template <class F, bool HO>
 __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const u32x4 *__restrict__ ahl, const uint8_t *__restrict__ w, float *__restrict__ y, int M,
-    int N, int K, int tiles_m, int tiles_n)
+    int N, int K, int tiles_m, int tiles_n, const int *__restrict__ row_exp)
 {
     using G = PairGeom<F>;
-    constexpr int NL = G::kLoads, NB = G::kBLoads;
-    constexpr int DA = RingDepth<F>::kA, DB = RingDepth<F>::kB;
+    constexpr int SO = slab_ops<HO>();           // A operands per (tile, block)
+    constexpr int NA = 2 * SO / (8 * 64);         // A loads (1 KB each) per wavefront per pair
+    constexpr int NB = G::kBLoads, NL = NA + NB;
+    constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
     static_assert(DA >= 3 && DB >= DA, "ring depths");
-    __shared__ SplitLds<F> lds;
+    __shared__ SplitLds<F, HO> lds;
 
     const int T = tiles_m * tiles_n, L = blockIdx.x;
     const int t = (T % 8 == 0) ? (L % 8) * (T / 8) + L / 8 : L;
@@ -338,12 +363,12 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const size_t row_bytes = (size_t)nblk * F::kBytes;
 
     // Direct-to-LDS loads, NL per wavefront per pair (so every wavefront's
-    // vmcnt moves in the same steps). A: four 16-byte loads, 1 KB each, at
-    // entries (4 wave + i) * 64 + lane of the slab, whose workspace order is the
-    // LDS order. B: NB 4-byte loads at dword slots j * 64 + lane, j = wave + 8 r;
+    // vmcnt moves in the same steps). A: NA (4, or 2 hi-only) 16-byte loads,
+    // 1 KB each, at entries (NA wave + i) * 64 + lane of the slab, whose
+    // workspace order is the LDS order. B: NB 4-byte loads at dword slots j * 64 + lane, j = wave + 8 r;
     // slot t < 128 kDwords is dword t % kDwords of the pair's bytes of row
     // t / kDwords, higher slots re-read a valid dword into unused LDS.
-    const u32x4 *asrc = ahl + (size_t)mt * nblk * kOpsPerBlockTile + wave * 4 * 64 + lane;
+    const u32x4 *asrc = ahl + (size_t)mt * nblk * SO + wave * NA * 64 + lane;
     const uint8_t *bsrc[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
@@ -351,18 +376,18 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         const int row = tt / G::kDwords, dw = tt % G::kDwords;
         bsrc[r] = w + (size_t)min(n0 + row, N - 1) * row_bytes + 4 * dw;
     }
-    // Load k (0 .. NL-1) of a step: the four A loads of pair pa, then the NB B
+    // Load k (0 .. NL-1) of a step: the NA A loads of pair pa, then the NB B
     // loads of pair pb (k is a compile-time constant where this is called).
     auto issue_load = [&](int pa, int pb, int k) __attribute__((always_inline)) {
-        if (k < 4)
+        if (k < NA)
             __builtin_amdgcn_global_load_lds(
-                (const void *)(asrc + (size_t)pa * 2 * kOpsPerBlockTile + k * 64),
-                (__attribute__((address_space(3))) void *)(lds.a[pa % DA] + (wave * 4 + k) * 64),
+                (const void *)(asrc + (size_t)pa * 2 * SO + k * 64),
+                (__attribute__((address_space(3))) void *)(lds.a[pa % DA] + (wave * NA + k) * 64),
                 16, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(
-                (const void *)(bsrc[k - 4] + 2 * F::kBytes * pb),
-                (__attribute__((address_space(3))) void *)(lds.b[pb % DB] + (wave + 8 * (k - 4)) * 64),
+                (const void *)(bsrc[k - NA] + 2 * F::kBytes * pb),
+                (__attribute__((address_space(3))) void *)(lds.b[pb % DB] + (wave + 8 * (k - NA)) * 64),
                 4, 0, 0);
     };
 
@@ -394,17 +419,18 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         // wavefront's four row groups and the raw B bytes of its four column
         // groups.
         struct Ops {
-            f16x8 hi[4], lo[4];
+            f16x8 hi[4], lo[HO ? 1 : 4];
             BCol b[4];
         };
         // Part i of pair q's operands (row group i, column group i).
         auto read_ops = [&](int q, Ops &o, int i) __attribute__((always_inline)) {
-            const u32x4 *ap = lds.a[q % DA] + KG * kOpsPerBlockTile + wm * 4 * 64 + lane;
+            const u32x4 *ap = lds.a[q % DA] + KG * SO + wm * 4 * 64 + lane;
             o.hi[i] = bitcast<f16x8>(ap[i * 64]);
-            o.lo[i] = bitcast<f16x8>(ap[8 * 64 + i * 64]);
+            if constexpr (!HO)
+                o.lo[i] = bitcast<f16x8>(ap[8 * 64 + i * 64]);
             o.b[i] = read_b(lds.b[q % DB], i);
         };
-        constexpr int kDsReads = 2 + QsRaw<F, KG>::n + 1;   // LDS reads of one part
+        constexpr int kDsReads = (HO ? 1 : 2) + QsRaw<F, KG>::n + 1;   // LDS reads of one part
 
         // Software pipeline over the four column groups of a pair: the MFMAs of
         // group ns are issued between the scale FMAs of group ns - 1 (whose results
@@ -429,7 +455,8 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             BOps o;
             o.d = f16_bits_to_f32(d_from_dword<F, KG>(bc.dw));
             o.q = F::decode(x, magic_v);
-            o.s = o.q * scale;
+            if constexpr (!HO)
+                o.s = o.q * scale;
             return o;
         };
         // One scheduling region per column group ns: its eight MFMAs (the four hi
@@ -474,20 +501,28 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 BOps nxt = cur;
                 if (ns + 1 < 4)
                     nxt = decode_b(cur_ops.b[ns + 1]);
+                if constexpr (!HO) {
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
-                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.lo[ms], cur.s, c[ms], 0, 0, 0);
+                    for (int ms = 0; ms < 4; ++ms)
+                        c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.lo[ms], cur.s, c[ms], 0, 0, 0);
+                }
                 dbuf[ns & 1] = cur.d;
+                // Eight MFMAs per region (four hi-only), each followed by LDS
+                // reads while any remain, the region's loads towards its end, and
+                // its share of the VALU work.
+                constexpr int NM = HO ? 4 : 8;
+                constexpr int kDsPerSlot = (kDsReads + NM - 1) / NM;
+                constexpr int kValuPerSlot = HO ? 7 : 4;
                 constexpr int kRegionLoads = 3;   // at most (NL ns / 4 ranges hold 1 .. 3)
                 const int nl = (NL * (ns + 1) + 3) / 4 - (NL * ns + 3) / 4;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < NM; ++u) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    if (u < kDsReads)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-                    if (u >= 8 - nl && u >= 8 - kRegionLoads)
+                    if (u * kDsPerSlot < kDsReads)
+                        __builtin_amdgcn_sched_group_barrier(0x100, kDsPerSlot, 0);   // LDS reads
+                    if (u >= NM - nl && u >= NM - kRegionLoads)
                         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one load
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerSlot, 0);   // VALU
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 cur = nxt;
@@ -520,7 +555,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         for (int t = -DB; t < 0; ++t) {
 #pragma unroll
             for (int k = 0; k < NL; ++k)
-                if (k >= 4 || t + DA >= 0)
+                if (k >= NA || t + DA >= 0)
                     issue_load(min(t + DA, last), min(t + DB, last), k);
         }
         if (counted)
@@ -587,15 +622,132 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             for (int q = 0; q < 4; ++q) {
                 const int m = mb + ms * 16 + q;
                 const uint32_t row_off = (uint32_t)m * (uint32_t)N + (uint32_t)nb;
+                int pe = 0;
+                if constexpr (HO)
+                    pe = m < M ? row_exp[m] : 0;
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns) {
-                    const float v = acc[ms][ns][q] + red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane];
+                    float v = acc[ms][ns][q] + red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane];
+                    if constexpr (HO)
+                        v = ldexpf(v, -pe);
                     if (m < M && nb + ns * 16 < N)
                         y[row_off + ns * 16] = v;
                 }
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 activations. A bfloat16 value has an 8-bit significand, so once its
+// row is scaled by a power of two 2^p that brings the row's largest magnitude
+// into [2^15, 2^16), every element within 2^32 of that maximum (2^28 on Q4_0's
+// slots 4..7, which carry a further 2^-4) is exactly a binary16 number: one f16
+// term per activation replaces the hi / lo pair of the f32 path, and the same
+// MFMAs on the same weight decode give products that are exact in f32. The
+// result row is scaled back by 2^-p in the epilogue (exact unless it lands in
+// the f32 subnormal range). Smaller elements round to the binary16 grid (2^-24
+// after scaling, 2^(E - 39) in the row's own units for max |a| in [2^E,
+// 2^(E+1))).
+//
+// * k_row_exp_bf16: one wavefront per row finds the largest magnitude (the
+//   largest bfloat16 bit pattern with the sign cleared, which orders finite
+//   values by magnitude) and stores p = 15 - E; p = 0 for an all-zero row or
+//   one that holds an infinity or NaN.
+// * k_gemm_prep_bf16: as k_gemm_split_a, one wavefront per 16-row group and
+//   block, writing only the hi operand: operand [mt][kb][sub][lane] in the
+//   format's slot order, rows past M zero.
+// * k_gemm_prep_bf16_f32: for shapes that take the general kernel, the scaled
+//   activations as f32, row-major (f16(a') is then exact and the lo term 0).
+
+constexpr int kRowExpWaves = 4;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_bf16(const uint16_t *__restrict__ a,
+                                                                   int *__restrict__ row_exp,
+                                                                   int M, int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
+    if (m >= M)   // whole wavefronts only
+        return;
+    // K % 32 == 0: a row is a whole number of 64-byte lines, read 16 bytes a lane.
+    const uint4 *row = reinterpret_cast<const uint4 *>(a + (size_t)m * K);
+    uint32_t mx = 0;
+    for (int i = lane; i < K / 8; i += 64) {
+        const uint4 v = row[i];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mx = max(mx, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if (lane == 0) {
+        int p = 0;
+        if (mx != 0 && mx < 0x7F80u) {
+            const int ef = (int)(mx >> 7);
+            // max |a| in [2^E, 2^(E+1)): subnormals are (mantissa) 2^-133.
+            const int E = ef > 0 ? ef - 127 : (31 - __builtin_clz(mx)) - 133;
+            p = 15 - E;
+        }
+        row_exp[m] = p;
+    }
+}
+
+template <class F>
+__global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_prep_bf16(const uint16_t *__restrict__ a,
+                                                                   const int *__restrict__ row_exp,
+                                                                   u32x4 *__restrict__ ops, int M,
+                                                                   int K, long long n_waves)
+{
+    const int lane = threadIdx.x & 63;
+    const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
+    if (gw >= n_waves)   // whole wavefronts only
+        return;
+    const int nblk = K >> 5;
+    const long long R = gw / nblk;                // 16-row group
+    const int kb = (int)(gw - R * nblk);
+    const int li = lane & 15, g = lane >> 4;
+    const long long m = R * 16 + li;
+    f16x8 hi = {};
+    if (m < M) {
+        const uint16_t *blk = a + m * K + (long long)kb * 32;
+        const uint2 L = *reinterpret_cast<const uint2 *>(blk + F::a_lo(g));
+        const uint2 H = *reinterpret_cast<const uint2 *>(blk + F::a_hi(g));
+        const int p = row_exp[m];
+        const int ph = p - F::kHiLog2;   // slots 4..7 carry a further 2^-kHiLog2
+        // Elements 0..3 of a group are the low and high halves of two dwords,
+        // in the slot order x, z, y, w of the f32 path.
+        const float e[8] = {
+            ldexpf(bf16_bits_to_f32(L.x & 0xFFFFu), p), ldexpf(bf16_bits_to_f32(L.y & 0xFFFFu), p),
+            ldexpf(bf16_bits_to_f32(L.x >> 16), p),     ldexpf(bf16_bits_to_f32(L.y >> 16), p),
+            ldexpf(bf16_bits_to_f32(H.x & 0xFFFFu), ph), ldexpf(bf16_bits_to_f32(H.y & 0xFFFFu), ph),
+            ldexpf(bf16_bits_to_f32(H.x >> 16), ph),    ldexpf(bf16_bits_to_f32(H.y >> 16), ph)};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            hi[s] = (f16)e[s];
+    }
+    const long long mt = R >> 3;
+    ops[(mt * nblk + kb) * slab_ops<true>() + (R & 7) * 64 + lane] = bitcast<u32x4>(hi);
+}
+
+__global__ __launch_bounds__(256) void k_gemm_prep_bf16_f32(const uint16_t *__restrict__ a,
+                                                           const int *__restrict__ row_exp,
+                                                           float4 *__restrict__ out, int K,
+                                                           long long n_quads)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_quads)
+        return;
+    const int p = row_exp[(i * 4) / K];   // K % 32 == 0: a quad never straddles rows
+    const uint2 v = reinterpret_cast<const uint2 *>(a)[i];
+    out[i] = make_float4(ldexpf(bf16_bits_to_f32(v.x & 0xFFFFu), p),
+                         ldexpf(bf16_bits_to_f32(v.x >> 16), p),
+                         ldexpf(bf16_bits_to_f32(v.y & 0xFFFFu), p),
+                         ldexpf(bf16_bits_to_f32(v.y >> 16), p));
 }
 
 template <class F>
@@ -609,7 +761,7 @@ static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int 
     if (!q4v::gemm_splits_activations(K) ||
         (long long)M * N >= (1LL << 31))   // the split kernel stores with 32-bit offsets
         return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w, y,
-                             M, N, K, tiles_m, tiles_n);
+                             M, N, K, tiles_m, tiles_n, (const int *)nullptr);
     u32x4 *ahl = static_cast<u32x4 *>(workspace);
     const long long n_waves = (long long)tiles_m * 8 * (K / 32);
     const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
@@ -619,8 +771,47 @@ static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int 
                                  dim3(64 * kSplitWaves), 0, s, a, ahl, M, K, n_waves);
     if (e != hipSuccess)
         return e;
-    return launch_kernel(k_gemm_split<F>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
-                         (const u32x4 *)ahl, w, y, M, N, K, tiles_m, tiles_n);
+    return launch_kernel(k_gemm_split<F, false>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
+                         (const u32x4 *)ahl, w, y, M, N, K, tiles_m, tiles_n, (const int *)nullptr);
+}
+
+template <class F>
+static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float *y, int M, int N,
+                                     int K, void *workspace, hipStream_t s)
+{
+    const int tiles_m = (M + kGemmBM - 1) / kGemmBM, tiles_n = (N + kGemmBN - 1) / kGemmBN;
+    const long long T = (long long)tiles_m * tiles_n;
+    if (T > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    int *row_exp = static_cast<int *>(workspace);
+    void *act = static_cast<char *>(workspace) + q4v::gemm_bf16_row_exp_bytes(M);
+    hipError_t e = launch_kernel(k_row_exp_bf16, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
+                                 dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
+    if (e != hipSuccess)
+        return e;
+    if (!q4v::gemm_bf16_splits(M, N, K)) {
+        const long long n_quads = (long long)M * K / 4;
+        const long long grid = (n_quads + 255) / 256;
+        if (grid > 0x7fffffffLL)
+            return hipErrorInvalidValue;
+        e = launch_kernel(k_gemm_prep_bf16_f32, dim3((unsigned)grid), dim3(256), 0, s, a,
+                          (const int *)row_exp, static_cast<float4 *>(act), K, n_quads);
+        if (e != hipSuccess)
+            return e;
+        return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s,
+                             (const float *)act, w, y, M, N, K, tiles_m, tiles_n,
+                             (const int *)row_exp);
+    }
+    const long long n_waves = (long long)tiles_m * 8 * (K / 32);
+    const long long grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
+    if (grid > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    e = launch_kernel(k_gemm_prep_bf16<F>, dim3((unsigned)grid), dim3(64 * kSplitWaves), 0, s, a,
+                      (const int *)row_exp, static_cast<u32x4 *>(act), M, K, n_waves);
+    if (e != hipSuccess)
+        return e;
+    return launch_kernel(k_gemm_split<F, true>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
+                         (const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n, (const int *)row_exp);
 }
 
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
@@ -629,6 +820,14 @@ hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float
     if (fmt == WeightFormat::kQ8_0)
         return launch_gemm_f<FmtQ8_0>(a, w, y, M, N, K, workspace, s);
     return launch_gemm_f<FmtQ4_0>(a, w, y, M, N, K, workspace, s);
+}
+
+hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
+                            int N, int K, void *workspace, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemm_bf16_f<FmtQ8_0>(a, w, y, M, N, K, workspace, s);
+    return launch_gemm_bf16_f<FmtQ4_0>(a, w, y, M, N, K, workspace, s);
 }
 
 }  // namespace q4k

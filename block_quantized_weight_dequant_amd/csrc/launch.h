@@ -19,6 +19,10 @@ hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float
 // taken (q4v::gemm_splits_activations(K)), else unused.
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
                        int K, void *workspace, hipStream_t s);
+// a: [M, K] bfloat16 bit patterns. workspace:
+// q4v::gemm_bf16_workspace_bytes(M, N, K) bytes (always used).
+hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
+                            int N, int K, void *workspace, hipStream_t s);
 hipError_t launch_q8_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
 hipError_t launch_q4_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
 

@@ -44,7 +44,7 @@ int check_dequant(const void *w, size_t w_bytes, const float *out, size_t out_el
     return Q4_OK;
 }
 
-int check_product(const float *a, const void *w, size_t w_bytes, const float *y,
+int check_product(const void *a, size_t a_elem, const void *w, size_t w_bytes, const float *y,
                   int M, int N, int K, int max_rows, size_t block_bytes, bool *empty)
 {
     *empty = false;
@@ -55,7 +55,7 @@ int check_product(const float *a, const void *w, size_t w_bytes, const float *y,
     size_t row_bytes = (size_t)(K / 32) * block_bytes, w_want = 0, a_bytes = 0, y_bytes = 0;
     if (!mul_ok((size_t)N, row_bytes, &w_want) || w_bytes != w_want)
         return Q4_ERR_SIZE;
-    if (!mul_ok((size_t)M, (size_t)K, &a_bytes) || !mul_ok(a_bytes, sizeof(float), &a_bytes))
+    if (!mul_ok((size_t)M, (size_t)K, &a_bytes) || !mul_ok(a_bytes, a_elem, &a_bytes))
         return Q4_ERR_SIZE;
     if (!mul_ok((size_t)M, (size_t)N, &y_bytes) || !mul_ok(y_bytes, sizeof(float), &y_bytes))
         return Q4_ERR_SIZE;
@@ -107,10 +107,26 @@ size_t gemm_workspace_bytes(int M, int N, int K)
     return n;
 }
 
-int check_workspace(const float *a, const void *w, size_t w_bytes, const float *y, int M, int N,
-                    int K, const void *ws, size_t ws_bytes)
+size_t gemm_bf16_workspace_bytes(int M, int N, int K)
 {
-    const size_t need = gemm_workspace_bytes(M, N, K);
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0)
+        return 0;
+    size_t n = 0;
+    if (gemm_bf16_splits(M, N, K)) {
+        // Rows padded to whole 128-row tiles, one binary16 per element.
+        const size_t mp = ((size_t)M + 127) / 128 * 128;
+        if (!mul_ok(mp, (size_t)K, &n) || !mul_ok(n, 2, &n))
+            return SIZE_MAX;
+    } else if (!mul_ok((size_t)M, (size_t)K, &n) || !mul_ok(n, 4, &n)) {
+        return SIZE_MAX;
+    }
+    const size_t r = gemm_bf16_row_exp_bytes(M);
+    return n > SIZE_MAX - r ? SIZE_MAX : n + r;
+}
+
+int check_workspace(size_t need, const void *a, size_t a_elem, const void *w, size_t w_bytes,
+                    const float *y, int M, int N, int K, const void *ws, size_t ws_bytes)
+{
     if (need == 0)
         return Q4_OK;   // this shape takes no workspace; ws is not read
     if (need == SIZE_MAX)
@@ -121,7 +137,7 @@ int check_workspace(const float *a, const void *w, size_t w_bytes, const float *
         return Q4_ERR_NULL;
     if (!aligned16(ws))
         return Q4_ERR_ALIGN;
-    const size_t a_bytes = (size_t)M * (size_t)K * sizeof(float);
+    const size_t a_bytes = (size_t)M * (size_t)K * a_elem;
     const size_t y_bytes = (size_t)M * (size_t)N * sizeof(float);
     if (overlaps({ws, need}, {a, a_bytes}) || overlaps({ws, need}, {w, w_bytes}) ||
         overlaps({ws, need}, {y, y_bytes}))

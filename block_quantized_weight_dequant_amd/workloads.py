@@ -6,7 +6,8 @@ nothing else is shared between them.
 
 Weights are f32 draws from N(0, 0.02^2) (0.02 read as the standard deviation)
 that a caller turns into Q4_0 blocks with a quantizer of its own; activations
-and the tensor to be Q8_0-quantized are N(0, 1) f32. Every draw uses numpy's
+and the tensor to be Q8_0-quantized are N(0, 1) f32, and bfloat16 activations
+are the high 16 bits of such f32 draws. Every draw uses numpy's
 PCG64 generator (``numpy.random.default_rng(seed)``) so the bytes are the same on
 every machine.
 """
@@ -38,6 +39,13 @@ WORKLOADS = {
     "q8_0_gemm_2048x14336x4096": dict(kind="gemm", fmt="q8_0", M=2048, N=14336, K=4096,
                                       w_seed=400, a_seed=401),
     "q8_0_dequant_14336x4096": dict(kind="dequant", fmt="q8_0", N=14336, K=4096, w_seed=400),
+    # The prefill GEMMs with bfloat16 activations (``act="bf16"``).
+    "gemm_bf16_1024x4096x4096": dict(kind="gemm", act="bf16", M=1024, N=4096, K=4096, w_seed=200,
+                                     a_seed=203),
+    "gemm_bf16_2048x14336x4096": dict(kind="gemm", act="bf16", M=2048, N=14336, K=4096,
+                                      w_seed=400, a_seed=401),
+    "q8_0_gemm_bf16_2048x14336x4096": dict(kind="gemm", act="bf16", fmt="q8_0", M=2048, N=14336,
+                                           K=4096, w_seed=400, a_seed=401),
 }
 
 WEIGHT_SIGMA = np.float32(0.02)
@@ -53,6 +61,12 @@ def activations_f32(seed: int, M: int, K: int) -> np.ndarray:
     """[M, K] f32 ~ N(0, 1), row-major."""
     rng = np.random.default_rng(seed)
     return rng.standard_normal((M, K), dtype=np.float32)
+
+
+def activations_bf16(seed: int, M: int, K: int) -> np.ndarray:
+    """[M, K] bfloat16 bit patterns (uint16): the high halves of the f32 draws
+    of ``activations_f32(seed, M, K)``, i.e. N(0, 1) values cut to bfloat16."""
+    return (activations_f32(seed, M, K).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def uniform_bytes(seed: int, n: int) -> np.ndarray:

@@ -38,12 +38,13 @@
 #define Q4MI_Q4_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 3
+#define Q4_ABI_VERSION 4
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -152,6 +153,52 @@ int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
  * the same function of (M, N, K) as q4_gemm_workspace_bytes.
  */
 size_t q8_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * q4_gemm_bf16 — q4_gemm with bfloat16 activations: y = a @ dequant(W)^T for
+ * any M >= 1, y in f32. The 4-bit prefill measured in TensorFold pull request
+ * #2017 ("Vulkan: qmm_q4_tile_rows computes four rows and two columns of a
+ * prompt chunk per thread", section Setup) multiplies bfloat16 activations;
+ * that checkpoint's 4-bit format is another one, so only the activation type
+ * is taken from it, and the weight blocks are those of section dequant_q4_0,
+ * as for q4_gemm.
+ *   a         [M, K] bfloat16, row-major, as raw 16-bit patterns (the high
+ *             half of the f32 with the same value).
+ *   w_q, y, M, N, K: as q4_gemm (w_bytes == N * (K/32) * 18).
+ *   workspace, workspace_bytes: as q4_gemm's, sized by
+ *             q4_gemm_bf16_workspace_bytes, which is non-zero for every
+ *             non-empty shape (the workspace is always used).
+ * Each row of a is scaled by a power of two 2^p that brings its largest
+ * magnitude into [2^15, 2^16); every element within 2^28 of that magnitude
+ * (2^32 for q8_gemm_bf16) is then exactly a binary16 number, the products
+ * with the weight codes are exact in f32, and the row of y is scaled back by
+ * 2^-p. Elements further below the row maximum are rounded to 2^-24 on the
+ * scaled grid. Accuracy, for rows within that range: as q4_gemm. Errors: as
+ * q4_gemm, with a counted at 2 bytes per element. Deterministic.
+ */
+int q4_gemm_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y,
+                 int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * q4_gemm_bf16_workspace_bytes — bytes of workspace q4_gemm_bf16 needs:
+ * the row exponents (M int32, padded to a multiple of 256 bytes), then
+ * ceil(M / 128) * 128 * K * 2 when K % 64 == 0 and M * N < 2^31 (one binary16
+ * term per activation, in matrix-core operand order), else M * K * 4 (the
+ * scaled activations in f32). 0 when M, N or K is invalid or the problem is
+ * empty, SIZE_MAX when the size does not fit in size_t. Pure function.
+ */
+size_t q4_gemm_bf16_workspace_bytes(int M, int N, int K);
+
+/*
+ * q8_gemm_bf16 — q4_gemm_bf16 over a Q8_0 weight stream (w_bytes ==
+ * N * (K/32) * 34); exact for elements within 2^32 of their row's largest
+ * magnitude. Everything else as q4_gemm_bf16.
+ */
+int q8_gemm_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y,
+                 int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+
+/* q8_gemm_bf16_workspace_bytes — the same function as q4_gemm_bf16_workspace_bytes. */
+size_t q8_gemm_bf16_workspace_bytes(int M, int N, int K);
 
 /*
  * q8_quantize — f32 to Q8_0 blocks (section quantize_q8_0).

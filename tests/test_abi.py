@@ -86,7 +86,7 @@ BLOCK_BYTES = {"q4": 18, "q8": 34}
 
 
 def _prod(entry, a, w, wb, y, M, N, K):
-    if entry.endswith("_gemm"):   # no workspace: these checks all come before its own
+    if entry.endswith(("_gemm", "_gemm_bf16")):   # no workspace: these checks come before its own
         return binding.raw_status(entry, a, w, wb, y, M, N, K, 0, 0, 0)
     return binding.raw_status(entry, a, w, wb, y, M, N, K, 0)
 
@@ -96,7 +96,8 @@ def _wb(N, K, fmt="q4"):
 
 
 @fake_addresses
-@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm", "q8_gemv", "q8_gemm"])
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm", "q8_gemv", "q8_gemm", "q4_gemm_bf16",
+                                   "q8_gemm_bf16"])
 def test_product_argument_checks(entry):
     S = binding
     f = entry[:2]
@@ -122,6 +123,18 @@ def test_product_argument_checks(entry):
     # empty problems: OK without looking at the pointers
     assert _prod(entry, None, None, wb(4, 64), None, 0, 4, 64) == S.Q4_OK
     assert _prod(entry, None, None, 0, None, 3, 0, 64) == S.Q4_OK
+
+
+@fake_addresses
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_bf16_activations_are_two_bytes(f):
+    # [2, 64] activations end 256 bytes (bfloat16) or 512 bytes (f32) after a:
+    # an output at a + 256 overlaps the f32 form only. The bfloat16 call then
+    # passes every product check and stops at its (missing) workspace.
+    wb = _wb(4, 64, f)
+    assert _prod(f + "_gemm", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_ALIAS
+    assert _prod(f + "_gemm_bf16", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_WORKSPACE
+    assert _prod(f + "_gemm_bf16", A, W, wb, A + 240, 2, 4, 64) == binding.Q4_ERR_ALIAS
 
 
 @fake_addresses
@@ -200,15 +213,39 @@ def test_gemm_workspace_bytes(fn):
         assert f(M, N, K) == 0, (M, N, K)
 
 
+@pytest.mark.parametrize("fn", ["q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16_workspace_bytes"])
+def test_gemm_bf16_workspace_bytes(fn):
+    f = getattr(binding, fn)
+    # Row exponents (int32, padded to 256 bytes), then one binary16 per element
+    # of the 128-row-padded activations on the split path ...
+    assert f(1, 1, 64) == 256 + 128 * 64 * 2
+    assert f(64, 7, 4096) == 256 + 128 * 4096 * 2
+    assert f(65, 7, 4096) == 512 + 128 * 4096 * 2
+    assert f(2048, 14336, 4096) == 2048 * 4 + 2048 * 4096 * 2
+    # ... else the f32 scaled activations: K % 64 != 0, or M N >= 2^31.
+    assert f(5, 5, 96) == 256 + 5 * 96 * 4
+    assert f(3, 9, 32) == 256 + 3 * 32 * 4
+    assert f(65536, 32768, 64) == 65536 * 4 + 65536 * 64 * 4
+    assert f(65536, 32767, 64) == 65536 * 4 + 65536 * 64 * 2
+    for M, N, K in [(0, 5, 64), (5, 0, 64), (-1, 5, 64), (5, -1, 64), (5, 5, 48), (5, 5, 0),
+                    (5, 5, -64)]:
+        assert f(M, N, K) == 0, (M, N, K)
+
+
 @fake_addresses
-@pytest.mark.parametrize("f", ["q4", "q8"])
-def test_gemm_workspace_checks(f):
+@pytest.mark.parametrize("g", ["q4_gemm", "q8_gemm", "q4_gemm_bf16", "q8_gemm_bf16"])
+@pytest.mark.parametrize("K", [64, 96])
+def test_gemm_workspace_checks(g, K):
     S = binding
-    M, N, K = 3, 4, 64
-    need = getattr(binding, f + "_gemm_workspace_bytes")(M, N, K)
+    f = g[:2]
+    M, N = 3, 4
+    need = getattr(binding, g + "_workspace_bytes")(M, N, K)
+    if need == 0:   # only the f32 GEMM with K % 64 != 0 takes no workspace
+        assert g.endswith("_gemm") and K % 64
+        return
     WS = BASE + (3 << 32)
     wbn = _wb(N, K, f)
-    st = lambda ws, wsb: binding.raw_status(f + "_gemm", A, W, wbn, Y, M, N, K, ws, wsb, 0)
+    st = lambda ws, wsb: binding.raw_status(g, A, W, wbn, Y, M, N, K, ws, wsb, 0)
     assert st(WS, need - 1) == S.Q4_ERR_WORKSPACE
     assert st(None, 0) == S.Q4_ERR_WORKSPACE
     assert st(None, need) == S.Q4_ERR_NULL
@@ -217,8 +254,8 @@ def test_gemm_workspace_checks(f):
     assert st(W - need + 16, need) == S.Q4_ERR_ALIAS                 # ends inside w
     assert st(Y, need) == S.Q4_ERR_ALIAS                             # on y
     # Checks of a, w and y come first, and an empty problem needs nothing.
-    assert binding.raw_status(f + "_gemm", A, W, wbn, Y, M, N, 48, None, 0, 0) == S.Q4_ERR_SHAPE
-    assert binding.raw_status(f + "_gemm", None, None, wbn, None, 0, N, K, None, 0, 0) == S.Q4_OK
+    assert binding.raw_status(g, A, W, wbn, Y, M, N, 48, None, 0, 0) == S.Q4_ERR_SHAPE
+    assert binding.raw_status(g, None, None, wbn, None, 0, N, K, None, 0, 0) == S.Q4_OK
 
 
 @fake_addresses

@@ -1,0 +1,286 @@
+"""GPU parity of q4_gemm_bf16 / q8_gemm_bf16 (bfloat16 activations, the
+activation type of the 4-bit prefill in TensorFold pull request #2017, section
+Setup) against the oracle: the bfloat16 patterns widened to f32 by the oracle's
+decode, then the oracle's f64 product over the dequantized weights (sections
+matmul_q4_0_tiled, dequant_q4_0 and dequant_q8_0 of "fuel-vulkan-kernels —
+quantized (GGML) kernel contracts"). Every output must satisfy
+|y - y_ref| <= 1e-5 * sum|a w| + 1e-6."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from block_quantized_weight_dequant_amd import binding  # noqa: E402
+from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
+from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_matmul,  # noqa: E402
+                         oracle_matmul_sampled, random_blocks, to_dev, weight_blob)
+
+GEMM_BF16 = {"q4_0": binding.q4_gemm_bf16, "q8_0": binding.q8_gemm_bf16}
+GEMM_F32 = {"q4_0": binding.q4_gemm, "q8_0": binding.q8_gemm}
+WS_BYTES = {"q4_0": binding.q4_gemm_bf16_workspace_bytes,
+            "q8_0": binding.q8_gemm_bf16_workspace_bytes}
+
+
+def _bits_dev(bits: np.ndarray) -> torch.Tensor:
+    return to_dev(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+
+
+def _run(fmt, bits: np.ndarray, blob: np.ndarray, N: int, K: int, w_dev=None, workspace=None):
+    M = bits.shape[0]
+    y = Guarded(M * N, torch.float32)
+    w = to_dev(blob) if w_dev is None else w_dev
+    GEMM_BF16[fmt](_bits_dev(bits), w, y.view, M, N, K, workspace=workspace)
+    torch.cuda.synchronize()
+    assert y.guards_intact()
+    return y.host().reshape(M, N)
+
+
+def _full_check(fmt, bits, blob, N, K, what):
+    got = _run(fmt, bits, blob, N, K)
+    ref, bound = oracle_matmul(fmt)(oracle.bf16_to_f32(bits), blob, N, K)
+    return assert_within_tolerance(got, ref, bound, "%s %s" % (fmt, what))
+
+
+def _shift(bits: np.ndarray, k: int) -> np.ndarray:
+    """bfloat16 patterns times 2^k (every value stays a normal number)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ------------------------------------------------------------- the workloads
+
+@pytest.mark.parametrize("name", ["gemm_bf16_1024x4096x4096", "gemm_bf16_2048x14336x4096",
+                                  "q8_0_gemm_bf16_2048x14336x4096"])
+def test_workloads_sampled(name):
+    s = wl.WORKLOADS[name]
+    fmt = s.get("fmt", "q4_0")
+    M, N, K = s["M"], s["N"], s["K"]
+    blob = weight_blob(fmt, N, K, s["w_seed"])
+    bits = wl.activations_bf16(s["a_seed"], M, K)
+    got = _run(fmt, bits, blob, N, K)
+    mi = np.concatenate([wl.uniform_ints(7, 0, M, 4096), np.zeros(N, np.int64),
+                         np.full(N, M - 1), np.arange(M), np.arange(M)])
+    ni = np.concatenate([wl.uniform_ints(8, 0, N, 4096), np.arange(N), np.arange(N),
+                         np.zeros(M, np.int64), np.full(M, N - 1)])
+    ref, bound = oracle_matmul_sampled(fmt)(oracle.bf16_to_f32(bits), blob, N, K, mi, ni)
+    assert np.isfinite(got).all()
+    assert_within_tolerance(got[mi, ni], ref, bound, "%s %s" % (fmt, name))
+
+
+# ------------------------------------------------------ shapes and tails
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M,N,K", [(1, 300, 256), (8, 129, 64), (65, 70, 160), (5, 257, 128),
+                                   (33, 6144, 2048), (128, 128, 32), (129, 129, 96),
+                                   (300, 17, 4128), (257, 384, 512), (1, 1, 32), (200, 1000, 4096)])
+def test_shapes(fmt, M, N, K):
+    # K % 64 != 0 (32, 96, 160, 4128) takes the general kernel on scaled f32.
+    blob = weight_blob(fmt, N, K, 3 * M + N)
+    bits = wl.activations_bf16(5 * M + K, M, K)
+    _full_check(fmt, bits, blob, N, K, "gemm_bf16 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M,K", [(70, 1024), (9, 96)])
+def test_every_code_and_random_scales(fmt, M, K):
+    N = 160
+    blob = random_blocks(fmt, N * K // 32, 31 + M)
+    bits = wl.activations_bf16(32 + M, M, K)
+    _full_check(fmt, bits, blob, N, K, "random blocks %dx%dx%d" % (M, N, K))
+
+
+# ---------------------------------------------- the per-row power-of-two scale
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [1024, 96])
+@pytest.mark.parametrize("k", [-90, -40, -7, 9, 60, 100])
+def test_row_scaling_commutes_exactly(fmt, K, k):
+    # Scaling a row by 2^k moves only its exponent, so the device result must
+    # be the unscaled one times 2^k bit for bit (no result is subnormal or
+    # overflows at these k), on the split path (K = 1024) and the general one.
+    M, N = 40, 96
+    blob = weight_blob(fmt, N, K, 40)
+    bits = wl.activations_bf16(41, M, K)
+    y0 = _run(fmt, bits, blob, N, K)
+    yk = _run(fmt, _shift(bits, k), blob, N, K)
+    assert np.array_equal(yk, (y0.astype(np.float64) * 2.0 ** k).astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [1024, 96])
+def test_mixed_magnitude_rows(fmt, K):
+    # Rows of very different size, each within its own exact range, an
+    # all-zero row, a row of bfloat16 subnormals, and the largest finite value.
+    M, N = 8, 64
+    bits = wl.activations_bf16(8, M, K)
+    bits[1] = _shift(bits[1], -60)
+    bits[2] = _shift(bits[2], 90)
+    bits[3, ::97] = 0x4500                         # 2048.0 outliers in an N(0,1) row
+    bits[4] = 0
+    bits[5] = wl.uniform_bytes(9, K).astype(np.uint16) | 0x8000 * (np.arange(K) % 2)  # subnormals
+    bits[6] = _shift(bits[6], 20) & 0x7FFF          # |a| up to ~2^22, all positive
+    bits[7] = 0                                     # the largest finite bfloat16,
+    bits[7, [0, 33, K // 2, K - 1]] = [0x7F7F, 0xFF7F, 0x7F7F, 0xFF7F]   # four times
+    _full_check(fmt, bits, weight_blob(fmt, N, K, 9), N, K, "mixed rows K=%d" % K)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_row_span_at_the_exact_limit(fmt):
+    # Elements from the row maximum down to 2^-28 (Q4_0) or 2^-32 (Q8_0) of it
+    # are all exact binary16 numbers after the row scale: with d = 1 blocks and
+    # every product placed in its own output column, each output is one exact
+    # product a * code.
+    K = 64
+    span = 28 if fmt == "q4_0" else 32
+    codes_n = 4 if fmt == "q4_0" else 100       # one nonzero code per weight row
+    N = K
+    codes = np.zeros((N, K), np.int64)
+    codes[np.arange(N), np.arange(N)] = codes_n
+    zero = 8 if fmt == "q4_0" else 0
+    blob = _integer_blob(fmt, codes + zero)
+    expo = np.linspace(0, -span, K).round().astype(np.int64) + 10   # 2^10 .. 2^(10 - span)
+    mant = wl.uniform_ints(3, 0, 128, K)
+    vals = (1.0 + mant / 128.0) * 2.0 ** expo
+    vals[1::3] *= -1
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)[None, :]
+    got = _run(fmt, bits, blob, N, K)[0]
+    want = (oracle.bf16_to_f32(bits)[0].astype(np.float64) * codes_n).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+def _integer_blob(fmt, codes):
+    """d = 1.0 blocks of the given raw codes (Q4_0 nibbles 0..15, Q8_0 bytes)."""
+    N, K = codes.shape
+    nb = K // 32
+    c = codes.reshape(N, nb, 32)
+    if fmt == "q4_0":
+        blob = np.zeros((N, nb, 18), np.uint8)
+        blob[:, :, 2:] = c[:, :, :16] | (c[:, :, 16:] << 4)
+    else:
+        blob = np.zeros((N, nb, 34), np.uint8)
+        blob[:, :, 2:] = (c & 0xFF).astype(np.uint8)
+    blob[:, :, 1] = 0x3C
+    return blob.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [512, 96])
+def test_integer_data_is_exact(fmt, K):
+    N, M = 32, 3
+    lo, hi, zero = (0, 16, 8) if fmt == "q4_0" else (-128, 128, 0)
+    codes = wl.uniform_ints(10, lo, hi, (N, K))
+    codes[0, :] = lo
+    codes[1, :] = hi - 1
+    blob = _integer_blob(fmt, codes)
+    a = wl.uniform_ints(11, -8, 9, (M, K)).astype(np.float32)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    ref = (a.astype(np.int64) @ (codes - zero).T).astype(np.float64)
+    assert (_run(fmt, bits, blob, N, K) == ref).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_one_hot_activations_pick_weights_exactly(fmt):
+    N, K, M = 96, 1024, 19
+    blob = random_blocks(fmt, N * K // 32, 3)
+    w = getattr(oracle, fmt + "_dequant")(blob).reshape(N, K)
+    ks = wl.uniform_ints(4, 0, K, M)
+    bits = np.zeros((M, K), np.uint16)
+    bits[np.arange(M), ks] = 0x3F80                 # 1.0
+    assert (_run(fmt, bits, blob, N, K) == w[:, ks].T).all()
+
+
+# ------------------------------------------------------ agreement and gates
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [2048, 96])
+def test_agrees_with_the_f32_gemm(fmt, K):
+    M, N = 100, 256
+    blob = weight_blob(fmt, N, K, 14)
+    bits = wl.activations_bf16(15, M, K)
+    a32 = oracle.bf16_to_f32(bits)
+    y16 = _run(fmt, bits, blob, N, K)
+    y32 = torch.empty(M * N, device=DEV)
+    GEMM_F32[fmt](to_dev(a32), to_dev(blob), y32, M, N, K)
+    torch.cuda.synchronize()
+    _, bound = oracle_matmul(fmt)(a32, blob, N, K)
+    diff = np.abs(y16.astype(np.float64) - y32.cpu().numpy().reshape(M, N))
+    assert (diff <= 2 * oracle.tolerance(bound)).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_repeat_is_bitwise_identical(fmt):
+    N, K, M = 272, 1024, 200
+    blob = weight_blob(fmt, N, K, 12)
+    bits = wl.activations_bf16(13, M, K)
+    w = to_dev(blob)
+    y1 = _run(fmt, bits, blob, N, K, w_dev=w)
+    y2 = _run(fmt, bits, blob, N, K, w_dev=w)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_empty_problems_are_no_ops(fmt):
+    bb = 18 if fmt == "q4_0" else 34
+    GEMM_BF16[fmt](None, None, None, 0, 16, 64, w_bytes=16 * 2 * bb)
+    GEMM_BF16[fmt](None, None, None, 3, 0, 64, w_bytes=0)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M,N,K", [(130, 200, 512), (70, 50, 96)])
+def test_workspace_exact_size_and_garbage(fmt, M, N, K):
+    need = WS_BYTES[fmt](M, N, K)
+    ws = Guarded(need, torch.uint8)
+    ws.view.fill_(0x7F)
+    blob = weight_blob(fmt, N, K, 21)
+    bits = wl.activations_bf16(22, M, K)
+    got = _run(fmt, bits, blob, N, K, workspace=ws.view)
+    assert ws.guards_intact()
+    ref, bound = oracle_matmul(fmt)(oracle.bf16_to_f32(bits), blob, N, K)
+    assert_within_tolerance(got, ref, bound, "exact workspace")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_too_small_workspace_is_rejected(fmt):
+    M, N, K = 4, 16, 128
+    ws = torch.empty(WS_BYTES[fmt](M, N, K) - 16, dtype=torch.uint8, device=DEV)
+    y = torch.full((M * N,), 3.0, device=DEV)
+    with pytest.raises(binding.Q4Error) as e:
+        GEMM_BF16[fmt](_bits_dev(wl.activations_bf16(1, M, K)), to_dev(weight_blob(fmt, N, K, 2)),
+                       y, M, N, K, workspace=ws)
+    assert e.value.status == binding.Q4_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_graph_replays_match_eager(fmt):
+    M, N, K = 96, 384, 1024
+    gemm = GEMM_BF16[fmt]
+    blob = to_dev(weight_blob(fmt, N, K, 23))
+    a = _bits_dev(wl.activations_bf16(24, M, K))
+    ws = torch.empty(WS_BYTES[fmt](M, N, K), dtype=torch.uint8, device=DEV)
+    y_eager = torch.empty(M * N, device=DEV)
+    gemm(a, blob, y_eager, M, N, K, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty(M * N, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gemm(a, blob, y, M, N, K, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gemm(a, blob, y, M, N, K, workspace=ws)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        gemm(a, blob, torch.empty_like(y), M, N, K)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), rep

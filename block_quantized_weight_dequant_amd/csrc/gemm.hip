@@ -263,6 +263,8 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
 }
 
 constexpr int kSplitGemmThreads = 512;
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9: 32-bit data format.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
 
 // Per-format geometry of one pair of blocks.
@@ -363,32 +365,40 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const size_t row_bytes = (size_t)nblk * F::kBytes;
 
     // Direct-to-LDS loads, NL per wavefront per pair (so every wavefront's
-    // vmcnt moves in the same steps). A: NA (4, or 2 hi-only) 16-byte loads,
-    // 1 KB each, at entries (NA wave + i) * 64 + lane of the slab, whose
-    // workspace order is the LDS order. B: NB 4-byte loads at dword slots j * 64 + lane, j = wave + 8 r;
+    // vmcnt moves in the same steps), as buffer loads: one buffer resource
+    // per operand for the workgroup's tile, a fixed per-lane offset and a
+    // per-pair scalar offset, so the step's addressing is scalar work.
+    // A: NA (4, or 2 hi-only) 16-byte loads, 1 KB each, at entries
+    // (NA wave + i) * 64 + lane of the slab, whose workspace order is the LDS
+    // order. B: NB 4-byte loads at dword slots j * 64 + lane, j = wave + 8 r;
     // slot t < 128 kDwords is dword t % kDwords of the pair's bytes of row
-    // t / kDwords, higher slots re-read a valid dword into unused LDS.
-    const u32x4 *asrc = ahl + (size_t)mt * nblk * SO + wave * NA * 64 + lane;
-    const uint8_t *bsrc[NB];
+    // t / kDwords, higher slots re-read a valid dword into unused LDS. The
+    // ranges of both resources fit 32 bits (K <= 2^22 on this path).
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(ahl + (size_t)mt * nblk * SO), (short)0, (int)((uint32_t)nblk * SO * 16u),
+        kBufferRsrcWord3);
+    const int brows = min(kGemmBN, N - n0);
+    const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(w + (size_t)n0 * row_bytes), (short)0, (int)(brows * row_bytes), kBufferRsrcWord3);
+    const uint32_t a_voff = (uint32_t)((wave * NA * 64 + lane) * 16);
+    uint32_t b_voff[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         const int tt = min((wave + 8 * r) * 64 + lane, G::kBDwords - 1);
         const int row = tt / G::kDwords, dw = tt % G::kDwords;
-        bsrc[r] = w + (size_t)min(n0 + row, N - 1) * row_bytes + 4 * dw;
+        b_voff[r] = (uint32_t)(min(row, brows - 1) * (int)row_bytes + 4 * dw);
     }
     // Load k (0 .. NL-1) of a step: the NA A loads of pair pa, then the NB B
     // loads of pair pb (k is a compile-time constant where this is called).
     auto issue_load = [&](int pa, int pb, int k) __attribute__((always_inline)) {
         if (k < NA)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(asrc + (size_t)pa * 2 * SO + k * 64),
-                (__attribute__((address_space(3))) void *)(lds.a[pa % DA] + (wave * NA + k) * 64),
-                16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                arsrc, (__attribute__((address_space(3))) void *)(lds.a[pa % DA] + (wave * NA + k) * 64),
+                16, a_voff + k * 1024, (int)((uint32_t)pa * (2u * SO * 16u)), 0, 0);
         else
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(bsrc[k - NA] + 2 * F::kBytes * pb),
-                (__attribute__((address_space(3))) void *)(lds.b[pb % DB] + (wave + 8 * (k - NA)) * 64),
-                4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                brsrc, (__attribute__((address_space(3))) void *)(lds.b[pb % DB] + (wave + 8 * (k - NA)) * 64),
+                4, b_voff[k - NA], pb * (2 * F::kBytes), 0, 0);
     };
 
     f32x4 acc[4][4];

@@ -27,7 +27,9 @@ int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_b
 // True when q4_gemm / q8_gemm take the split-activation path for this K (the
 // path that needs a workspace). The GEMM launcher branches on the same
 // predicate.
-inline bool gemm_splits_activations(int K) { return K > 0 && K % 64 == 0; }
+// K <= 2^22 keeps every byte offset of the split kernel's buffer loads within
+// 32 bits.
+inline bool gemm_splits_activations(int K) { return K > 0 && K % 64 == 0 && K <= (1 << 22); }
 
 // Workspace bytes q4_gemm and q8_gemm need: 0 when none (no split path, or an empty or
 // invalid shape), SIZE_MAX when the size does not fit in size_t.

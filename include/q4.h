@@ -99,9 +99,9 @@ int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
  *   workspace, workspace_bytes: device scratch owned by the caller, at least
  *             q4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, not
  *             overlapping a, W or y, and not used by other work while this
- *             call runs on `stream`. When that function returns 0 (K % 64 != 0
- *             or an empty problem) the workspace is not read or written and
- *             may be NULL. Errors, after those of q4_gemv's checks:
+ *             call runs on `stream`. When that function returns 0 (K % 64 != 0,
+ *             K > 2^22 or an empty problem) the workspace is not read or
+ *             written and may be NULL. Errors, after those of q4_gemv's checks:
  *             Q4_ERR_SIZE if the needed size overflows size_t,
  *             Q4_ERR_WORKSPACE if workspace_bytes is smaller, then
  *             Q4_ERR_NULL, Q4_ERR_ALIGN, Q4_ERR_ALIAS for the pointer.
@@ -114,8 +114,9 @@ int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
 
 /*
  * q4_gemm_workspace_bytes — bytes of workspace q4_gemm needs for this shape:
- * ceil(M / 128) * 128 * K * 4 when K % 64 == 0 (the activations split once
- * into binary16 hi and lo terms, in matrix-core operand order), 0 otherwise or
+ * ceil(M / 128) * 128 * K * 4 when K % 64 == 0 and K <= 2^22 (the
+ * activations split once into binary16 hi and lo terms, in matrix-core
+ * operand order), 0 otherwise or
  * when M, N or K is invalid or the problem is empty, and SIZE_MAX when the
  * product does not fit in size_t. Pure function of its arguments.
  */
@@ -182,7 +183,7 @@ int q4_gemm_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y,
 /*
  * q4_gemm_bf16_workspace_bytes — bytes of workspace q4_gemm_bf16 needs:
  * the row exponents (M int32, padded to a multiple of 256 bytes), then
- * ceil(M / 128) * 128 * K * 2 when K % 64 == 0 and M * N < 2^31 (one binary16
+ * ceil(M / 128) * 128 * K * 2 when K % 64 == 0, K <= 2^22 and M * N < 2^31 (one binary16
  * term per activation, in matrix-core operand order), else M * K * 4 (the
  * scaled activations in f32). 0 when M, N or K is invalid or the problem is
  * empty, SIZE_MAX when the size does not fit in size_t. Pure function.

@@ -153,14 +153,15 @@ def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
     return blob
 
 
-def gemv_kernel_name(M, K, fmt="q4_0"):
+def gemv_kernel_name(M, K, fmt="q4_0", act="f32"):
+    bf = "true" if act == "bf16" else "false"
     if K % 256:
-        return "k_gemv<%s, %d>" % (FMT_TYPE[fmt], M)
+        return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
     per = (((nblk + 7) // 8) + 7) & ~7
     last = nblk - (nblk - 1) // per * per
-    ch = 16 if (M <= 4 and per % 16 == 0 and last % 16 == 0) else 8
-    return "k_gemv_stream<%s, %d, 8, %d>" % (FMT_TYPE[fmt], M, ch)
+    ch = 16 if (per % 16 == 0 and last % 16 == 0) else 8
+    return "k_gemv_stream<%s, %d, 8, %d, %s>" % (FMT_TYPE[fmt], M, ch, bf)
 
 
 def gemm_kernel_name(K, fmt="q4_0", act="f32"):
@@ -185,7 +186,7 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
     if s["kind"] == "gemv":
-        gemv = getattr(q4, f + "_gemv")
+        gemv = getattr(q4, f + ("_gemv_bf16" if act == "bf16" else "_gemv"))
         fn = lambda k: gemv(a, blobs[k % R], y, M, N, K)
     else:
         entry = f + ("_gemm_bf16" if act == "bf16" else "_gemm")
@@ -205,7 +206,7 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
            "job_GBs": algo_bytes * steps / t["wall_s"] / 1e9,
            "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
     if s["kind"] == "gemv":
-        kernel = gemv_kernel_name(M, K, fmt)
+        kernel = gemv_kernel_name(M, K, fmt, act)
         row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
     else:
         kernel = gemm_kernel_name(K, fmt, act)
@@ -380,10 +381,13 @@ def main():
             log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
-        for name in ("gemm_bf16_1024x4096x4096", "gemm_bf16_2048x14336x4096",
-                     "q8_0_gemm_bf16_2048x14336x4096"):
+        for name, st in (("gemv_bf16_1x4096x4096", args.steps),
+                         ("gemv_bf16_8x4096x4096", args.steps),
+                         ("q8_0_gemv_bf16_1x4096x4096", args.steps),
+                         ("gemm_bf16_1024x4096x4096", 50), ("gemm_bf16_2048x14336x4096", 20),
+                         ("q8_0_gemm_bf16_2048x14336x4096", 20)):
             log("row: %s" % name)
-            rows.append(bench_product(torch, q4, wl, name, min(20, args.steps),
+            rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
         log("row: Q8_0 dequant 14336x4096")
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10),

@@ -32,7 +32,8 @@ SIZE_MAX = 2 ** 64 - 1
 EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
            "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm",
            "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize", "q4_gemm_bf16",
-           "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes")
+           "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes",
+           "q4_gemv_bf16", "q8_gemv_bf16")
 
 
 class Q4Error(RuntimeError):
@@ -60,8 +61,9 @@ def _load_library():
     for f in ("q4", "q8"):
         getattr(lib, f + "_dequant").restype = i32
         getattr(lib, f + "_dequant").argtypes = [P, sz, P, sz, P]
-        getattr(lib, f + "_gemv").restype = i32
-        getattr(lib, f + "_gemv").argtypes = [P, P, sz, P, i32, i32, i32, P]
+        for g in ("_gemv", "_gemv_bf16"):
+            getattr(lib, f + g).restype = i32
+            getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P]
         for g in ("_gemm", "_gemm_bf16"):
             getattr(lib, f + g).restype = i32
             getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
@@ -142,6 +144,16 @@ def q4_gemv(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> Non
 def q8_gemv(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
     """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for 1 <= M <= 8, W Q8_0."""
     _gemv("q8_gemv", a, w_q, y, M, N, K, w_bytes, stream)
+
+
+def q4_gemv_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """As q4_gemv with ``a`` a [M, K] bfloat16 tensor (or its address)."""
+    _gemv("q4_gemv_bf16", a, w_q, y, M, N, K, w_bytes, stream)
+
+
+def q8_gemv_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """As q8_gemv with ``a`` a [M, K] bfloat16 tensor (or its address)."""
+    _gemv("q8_gemv_bf16", a, w_q, y, M, N, K, w_bytes, stream)
 
 
 def q4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -75,6 +75,18 @@ static int gemm(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const
                                      as_stream(stream)));
 }
 
+static int gemv_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *a,
+                     const void *w_q, size_t w_bytes, float *y, int M, int N, int K, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, 2, w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS, block_bytes,
+                                &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemv_bf16(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                          as_stream(stream)));
+}
+
 static int gemm_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *a,
                      const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
                      void *workspace, size_t workspace_bytes, void *stream)
@@ -135,6 +147,18 @@ Q4_EXPORT int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
 {
     return gemm(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, workspace,
                 workspace_bytes, stream);
+}
+
+Q4_EXPORT int q4_gemv_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y, int M,
+                           int N, int K, void *stream)
+{
+    return gemv_bf16(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT int q8_gemv_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y, int M,
+                           int N, int K, void *stream)
+{
+    return gemv_bf16(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, stream);
 }
 
 Q4_EXPORT size_t q4_gemm_bf16_workspace_bytes(int M, int N, int K)

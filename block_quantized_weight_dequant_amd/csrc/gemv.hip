@@ -67,16 +67,45 @@ __device__ __forceinline__ int row_scale_exp(float am)
     return p > 120 ? 120 : (p < -120 ? -120 : p);
 }
 
-template <class F, int M>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(const float *__restrict__ a,
+// bfloat16 activations (BF): a bfloat16 value has an 8-bit significand, so
+// after a power-of-two scale that puts the largest A value of its row in
+// [2^15, 2^16) every element within 2^28 (Q4_0) or 2^32 (Q8_0) of the row's
+// largest magnitude is exactly a binary16 number. One A row per activation
+// row then replaces the hi / lo pair: A row m is activation row m, and lane
+// (j, g) accumulates C rows 4g..4g+3, activation rows 4g + r.
+template <class F>
+__device__ __forceinline__ int row_scale_exp_bf16(float am)
+{
+    int e = 0;
+    frexpf(am, &e);                                  // am in [2^(e-1), 2^e)
+    return (am == 0.0f || !(am <= 3.4e38f)) ? 0 : 16 - F::kHiLog2 - e;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+template <bool BF, int M>
+struct GemvRows {
+    static constexpr int NI = BF ? M : 2 * M;                              // A rows in use
+    static constexpr int NACC = BF ? (M < 4 ? M : 4) : (M == 1 ? 2 : 4);   // C rows a lane owns
+    static constexpr int NOUT = BF ? NACC : NACC / 2;                      // activation rows a lane owns
+    // Activation row of a lane's output h (lane group g).
+    static __device__ __forceinline__ int row(int g, int h) { return BF ? 4 * g + h : 2 * g + h; }
+};
+
+template <class F, int M, bool BF>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(const void *__restrict__ a_,
                                                       const uint8_t *__restrict__ w,
                                                       float *__restrict__ y, int N, int K)
 {
     constexpr int NW = kGemvWaves;
     constexpr int CB = (M <= 4) ? 128 : 64;   // blocks per K chunk held in LDS
     constexpr int PB = CB / NW;               // blocks per wavefront per chunk
-    constexpr int NI = 2 * M;                 // A rows in use (hi, lo per row)
-    constexpr int NACC = (M == 1) ? 2 : 4;    // accumulator rows a lane can own
+    using R = GemvRows<BF, M>;
+    constexpr int NI = R::NI;                 // A rows in use (hi, lo per row; hi only for BF)
+    constexpr int NACC = R::NACC;             // accumulator rows a lane can own
+    const float *a = static_cast<const float *>(a_);
+    const uint16_t *ab = static_cast<const uint16_t *>(a_);
 
     __shared__ uint4 s_a[CB * 4 * NI];        // [block][g][i] 8-half A operands
     __shared__ float s_part[NW][M][16];
@@ -110,10 +139,20 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const float *__restrict__
 #pragma unroll
     for (int m = 0; m < M; ++m) {
         mx[m] = 0.0f;
-        const float4 *row = reinterpret_cast<const float4 *>(a + (size_t)m * K);
-        for (int f = tid; f < (K >> 2); f += kGemvThreads) {
-            float4 v = row[f];
-            mx[m] = fmaxf(mx[m], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        if constexpr (BF) {
+            // K % 32 == 0: 8-byte groups of four bfloat16 values.
+            const uint2 *row = reinterpret_cast<const uint2 *>(ab + (size_t)m * K);
+            for (int f = tid; f < (K >> 2); f += kGemvThreads) {
+                const uint2 v = row[f];
+                mx[m] = fmaxf(mx[m], fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                                           fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
+            }
+        } else {
+            const float4 *row = reinterpret_cast<const float4 *>(a + (size_t)m * K);
+            for (int f = tid; f < (K >> 2); f += kGemvThreads) {
+                float4 v = row[f];
+                mx[m] = fmaxf(mx[m], fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1)
@@ -126,7 +165,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const float *__restrict__
         float am = 0.0f;
         for (int ww = 0; ww < NW; ++ww)
             am = fmaxf(am, s_amax[ww][tid]);
-        s_exp[tid] = row_scale_exp<F>(am);
+        s_exp[tid] = BF ? row_scale_exp_bf16<F>(am) : row_scale_exp<F>(am);
     }
     __syncthreads();
     int pexp[M];
@@ -152,6 +191,23 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const float *__restrict__
         // all x 2^p.
         for (int q = tid; q < cnt * 4 * M; q += kGemvThreads) {
             const int m = q % M, rest = q / M, gg = rest & 3, b = rest >> 2;
+            if constexpr (BF) {
+                // Slots as below, one binary16 term each (exact, see above).
+                const uint16_t *blk = ab + (size_t)m * K + (size_t)(cb0 + b) * 32;
+                const uint2 L = *reinterpret_cast<const uint2 *>(blk + F::a_lo(gg));
+                const uint2 H = *reinterpret_cast<const uint2 *>(blk + F::a_hi(gg));
+                const int pl = pexp[m] + F::kHiLog2, ph = pexp[m];
+                const float v[8] = {ldexpf(bf16_lo(L.x), pl), ldexpf(bf16_lo(L.y), pl),
+                                    ldexpf(bf16_hi(L.x), pl), ldexpf(bf16_hi(L.y), pl),
+                                    ldexpf(bf16_lo(H.x), ph), ldexpf(bf16_lo(H.y), ph),
+                                    ldexpf(bf16_hi(H.x), ph), ldexpf(bf16_hi(H.y), ph)};
+                f16x8 hi;
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    hi[s] = (f16)v[s];
+                s_a[(b * 4 + gg) * NI + m] = bitcast<uint4>(hi);
+                continue;
+            }
             const float *blk = a + (size_t)m * K + (size_t)(cb0 + b) * 32;
             const float4 L = *reinterpret_cast<const float4 *>(blk + F::a_lo(gg));
             const float4 H = *reinterpret_cast<const float4 *>(blk + F::a_hi(gg));
@@ -191,12 +247,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const float *__restrict__
     }
 
     // Lane (j, g) holds C rows 4g..4g+3 of column j: activation rows 2g (hi, lo)
-    // and 2g+1 (hi, lo).
+    // and 2g+1 (hi, lo), or for BF activation rows 4g..4g+3.
 #pragma unroll
-    for (int h = 0; h < NACC / 2; ++h) {
-        const int m = 2 * g + h;
+    for (int h = 0; h < R::NOUT; ++h) {
+        const int m = R::row(g, h);
         if (m < M)
-            s_part[wave][m][j] = acc[2 * h] + acc[2 * h + 1];
+            s_part[wave][m][j] = BF ? acc[h] : acc[2 * h] + acc[2 * h + 1];
     }
     __syncthreads();
     if (tid < M * 16) {
@@ -239,7 +295,7 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <class F, int M, int NW, int CH_>
+template <class F, int M, int NW, int CH_, bool BF>
 struct GemvStreamCfg {
     static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
     static constexpr int CPR = CH * F::kBytes / 16;       // 16-byte columns per staged row
@@ -247,10 +303,10 @@ struct GemvStreamCfg {
     static constexpr int NFULL = CPR / 4;                 // ... that no lane clamps
     static constexpr int RS = CH * F::kBytes + 16;        // LDS bytes per staged row
     static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
-    static constexpr int NI = 2 * M;                      // A rows in use
+    static constexpr int NI = GemvRows<BF, M>::NI;        // A rows in use
     // The A operands of a chunk pass through LDS in AH halves when a whole
-    // chunk's would not fit (16 blocks of more than four rows).
-    static constexpr int AH = (CH == 16 && M > 4) ? 2 : 1;
+    // chunk's would not fit (16 blocks of more than eight A rows).
+    static constexpr int AH = (CH == 16 && NI > 8) ? 2 : 1;
     static constexpr int CHH = CH / AH;                   // blocks per A pass
     static constexpr int ABYTES = CHH * 4 * NI * 16;      // A operands per wavefront
     static constexpr int NENT = CH * 4 * M;               // 8-element activation groups per chunk
@@ -303,14 +359,16 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl<B0>(f, std::make_integer_sequence<int, B1 - B0>{});
 }
 
-template <class F, int M, int NW, int CH>
-__global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict__ a,
+template <class F, int M, int NW, int CH, bool BF>
+__global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
                                                         int per)
 {
-    using C = GemvStreamCfg<F, M, NW, CH>;
-    constexpr int NACC = (M == 1) ? 2 : 4;
+    using C = GemvStreamCfg<F, M, NW, CH, BF>;
+    using R = GemvRows<BF, M>;
+    constexpr int NACC = R::NACC;
+    constexpr uint32_t ES = BF ? 2 : 4;           // bytes per activation
     constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
 
     // Per wavefront: [staged weight bytes | A operands].
@@ -336,7 +394,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
     const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
 
     u32x4 wreg[C::NLOAD];
-    float4 areg[C::EPL][2];
+    // Four activations per half group: f32, or bfloat16 pairs.
+    using AV = std::conditional_t<BF, uint2, float4>;
+    AV areg[C::EPL][2];
     // Activation group e = (m * CH + b) * 4 + gg: row m, block b of the chunk,
     // elements lo(gg)..lo(gg)+3 and hi(gg)..hi(gg)+3. Activations are requested
     // first (vmcnt drains in issue order), so their split overlaps the weight
@@ -350,9 +410,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
         for (int r = 0; r < C::EPL; ++r) {
             const int e = min(lane + 64 * r, C::NENT - 1);
             const int m = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
-            const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * 4u;
-            areg[r][0] = *reinterpret_cast<const float4 *>(a8 + off);
-            areg[r][1] = *reinterpret_cast<const float4 *>(a8 + off + 4u * (F::a_hi(0) - F::a_lo(0)));
+            const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * ES;
+            areg[r][0] = *reinterpret_cast<const AV *>(a8 + off);
+            areg[r][1] = *reinterpret_cast<const AV *>(a8 + off + ES * (F::a_hi(0) - F::a_lo(0)));
         }
         // Columns lc0 + 4 i are in the row for i < NFULL on every lane: one
         // address with immediate offsets. The last load clamps its column.
@@ -389,9 +449,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
     // MFMA is in flight there).
     const uint32_t magic_v = magic_vgpr<F>();
 
-    float ysum[NACC / 2];
+    float ysum[R::NOUT];
 #pragma unroll
-    for (int h = 0; h < NACC / 2; ++h)
+    for (int h = 0; h < R::NOUT; ++h)
         ysum[h] = 0.0f;
 
     // Activation split of the chunk whose loads are in areg: per-row scale
@@ -410,9 +470,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
             const int e = lane + 64 * r;
             const int me = e / (4 * C::CH);
             if (e < C::NENT) {
-                const float4 L = areg[r][0], H = areg[r][1];
-                const float v = fmaxf(fmaxf(fmaxf(fabsf(L.x), fabsf(L.y)), fmaxf(fabsf(L.z), fabsf(L.w))),
-                                      fmaxf(fmaxf(fabsf(H.x), fabsf(H.y)), fmaxf(fabsf(H.z), fabsf(H.w))));
+                float v;
+                if constexpr (BF) {
+                    const uint2 L = areg[r][0], H = areg[r][1];
+                    v = fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(L.x)), fabsf(bf16_hi(L.x))),
+                                    fmaxf(fabsf(bf16_lo(L.y)), fabsf(bf16_hi(L.y)))),
+                              fmaxf(fmaxf(fabsf(bf16_lo(H.x)), fabsf(bf16_hi(H.x))),
+                                    fmaxf(fabsf(bf16_lo(H.y)), fabsf(bf16_hi(H.y)))));
+                } else {
+                    const float4 L = areg[r][0], H = areg[r][1];
+                    v = fmaxf(fmaxf(fmaxf(fabsf(L.x), fabsf(L.y)), fmaxf(fabsf(L.z), fabsf(L.w))),
+                              fmaxf(fmaxf(fabsf(H.x), fabsf(H.y)), fmaxf(fabsf(H.z), fabsf(H.w))));
+                }
 #pragma unroll
                 for (int m = 0; m < M; ++m)
                     if (m == me)
@@ -420,8 +489,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
             }
         }
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-            pexp[m] = row_scale_exp<F>(wave_max_nonneg(mx[m]));
+        for (int m = 0; m < M; ++m) {
+            const float am = wave_max_nonneg(mx[m]);
+            pexp[m] = BF ? row_scale_exp_bf16<F>(am) : row_scale_exp<F>(am);
+        }
         // Each pass writes the groups of its blocks (a lane's groups all belong
         // to one block, b = (lane / 4) % CH) and reads them back as A operands
         // at once; the next pass reuses the same LDS area.
@@ -439,22 +510,37 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
                 for (int m = 0; m < M; ++m)
                     if (m == me)
                         pm = pexp[m];
-                const float sh = ldexpf(1.0f, pm), sl = (float)(1 << F::kHiLog2) * sh;
-                const float4 L = areg[r][0], H = areg[r][1];
-                const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
-                                    H.x * sh, H.z * sh, H.y * sh, H.w * sh};
-                f16x8 hi, lo;
+                if constexpr (BF) {
+                    const uint2 L = areg[r][0], H = areg[r][1];
+                    const int pl = pm + F::kHiLog2;
+                    const float v[8] = {ldexpf(bf16_lo(L.x), pl), ldexpf(bf16_lo(L.y), pl),
+                                        ldexpf(bf16_hi(L.x), pl), ldexpf(bf16_hi(L.y), pl),
+                                        ldexpf(bf16_lo(H.x), pm), ldexpf(bf16_lo(H.y), pm),
+                                        ldexpf(bf16_hi(H.x), pm), ldexpf(bf16_hi(H.y), pm)};
+                    f16x8 hi;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    f16 hh, ll;
-                    split2(v[s], hh, ll);
-                    hi[s] = hh;
-                    lo[s] = ll;
+                    for (int s = 0; s < 8; ++s)
+                        hi[s] = (f16)v[s];
+                    *reinterpret_cast<u32x4 *>(s_a + (b % C::CHH) * ASTRIDE + (gg * C::NI + me) * 16) =
+                        bitcast<u32x4>(hi);
+                } else {
+                    const float sh = ldexpf(1.0f, pm), sl = (float)(1 << F::kHiLog2) * sh;
+                    const float4 L = areg[r][0], H = areg[r][1];
+                    const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
+                                        H.x * sh, H.z * sh, H.y * sh, H.w * sh};
+                    f16x8 hi, lo;
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        f16 hh, ll;
+                        split2(v[s], hh, ll);
+                        hi[s] = hh;
+                        lo[s] = ll;
+                    }
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(s_a + (b % C::CHH) * ASTRIDE +
+                                                           (gg * C::NI + 2 * me) * 16);
+                    dst[0] = bitcast<u32x4>(hi);
+                    dst[1] = bitcast<u32x4>(lo);
                 }
-                u32x4 *dst = reinterpret_cast<u32x4 *>(s_a + (b % C::CHH) * ASTRIDE +
-                                                       (gg * C::NI + 2 * me) * 16);
-                dst[0] = bitcast<u32x4>(hi);
-                dst[1] = bitcast<u32x4>(lo);
             }
         }
         // A operands into registers now, while the weight bytes are still in
@@ -522,14 +608,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
         // Undo this chunk's scale (and the factor 2^kHiLog2) on its partial.
         auto finish_chunk = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int h = 0; h < NACC / 2; ++h) {
-                const int m = 2 * g + h;
+            for (int h = 0; h < R::NOUT; ++h) {
+                const int m = R::row(g, h);
                 int pm = 0;
 #pragma unroll
                 for (int mm = 0; mm < M; ++mm)
                     if (mm == m)
                         pm = pexp[mm];
-                ysum[h] += ldexpf(acc[2 * h] + acc[2 * h + 1], -pm - F::kHiLog2);
+                ysum[h] += ldexpf(BF ? acc[h] : acc[2 * h] + acc[2 * h + 1], -pm - F::kHiLog2);
             }
         };
         for_each_part<C::NPART>([&](auto p_c) __attribute__((always_inline)) {
@@ -561,8 +647,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
     }
 
 #pragma unroll
-    for (int h = 0; h < NACC / 2; ++h) {
-        const int m = 2 * g + h;
+    for (int h = 0; h < R::NOUT; ++h) {
+        const int m = R::row(g, h);
         if (m < M)
             s_part[wave][m][j] = ysum[h];
     }
@@ -578,8 +664,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const float *__restrict
     }
 }
 
-template <class F, int M>
-static hipError_t launch_gemv_m(const float *a, const uint8_t *w, float *y, int N, int K,
+template <class F, int M, bool BF>
+static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N, int K,
                                 hipStream_t s)
 {
     const unsigned grid = (unsigned)((N + 15) / 16);
@@ -591,31 +677,31 @@ static hipError_t launch_gemv_m(const float *a, const uint8_t *w, float *y, int 
     constexpr int NW = kGemvStreamWaves;
     const int nblk = K / 32;
     if (K % 256 == 0 && (size_t)N * (size_t)nblk * F::kBytes < ((size_t)1 << 31) &&
-        (size_t)M * (size_t)K * 4 < ((size_t)1 << 31)) {
+        (size_t)M * (size_t)K * (BF ? 2 : 4) < ((size_t)1 << 31)) {
         const int per = (((nblk + NW - 1) / NW) + 7) & ~7;
         const int last = nblk - (nblk - 1) / per * per;       // blocks of the last busy wavefront
         if (per % 16 == 0 && last % 16 == 0)
-            return launch_kernel(k_gemv_stream<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s, a,
-                                 w, y, N, K, per);
-        return launch_kernel(k_gemv_stream<F, M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, a, w, y,
-                             N, K, per);
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF>, dim3(grid), dim3(64 * NW), 0, s,
+                                 a, w, y, N, K, per);
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF>, dim3(grid), dim3(64 * NW), 0, s, a, w,
+                             y, N, K, per);
     }
-    return launch_kernel(k_gemv<F, M>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
+    return launch_kernel(k_gemv<F, M, BF>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
 }
 
-template <class F>
-static hipError_t launch_gemv_f(const float *a, const uint8_t *w, float *y, int M, int N, int K,
+template <class F, bool BF>
+static hipError_t launch_gemv_f(const void *a, const uint8_t *w, float *y, int M, int N, int K,
                                 hipStream_t s)
 {
     switch (M) {
-    case 1: return launch_gemv_m<F, 1>(a, w, y, N, K, s);
-    case 2: return launch_gemv_m<F, 2>(a, w, y, N, K, s);
-    case 3: return launch_gemv_m<F, 3>(a, w, y, N, K, s);
-    case 4: return launch_gemv_m<F, 4>(a, w, y, N, K, s);
-    case 5: return launch_gemv_m<F, 5>(a, w, y, N, K, s);
-    case 6: return launch_gemv_m<F, 6>(a, w, y, N, K, s);
-    case 7: return launch_gemv_m<F, 7>(a, w, y, N, K, s);
-    case 8: return launch_gemv_m<F, 8>(a, w, y, N, K, s);
+    case 1: return launch_gemv_m<F, 1, BF>(a, w, y, N, K, s);
+    case 2: return launch_gemv_m<F, 2, BF>(a, w, y, N, K, s);
+    case 3: return launch_gemv_m<F, 3, BF>(a, w, y, N, K, s);
+    case 4: return launch_gemv_m<F, 4, BF>(a, w, y, N, K, s);
+    case 5: return launch_gemv_m<F, 5, BF>(a, w, y, N, K, s);
+    case 6: return launch_gemv_m<F, 6, BF>(a, w, y, N, K, s);
+    case 7: return launch_gemv_m<F, 7, BF>(a, w, y, N, K, s);
+    case 8: return launch_gemv_m<F, 8, BF>(a, w, y, N, K, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -624,8 +710,16 @@ hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float
                        int K, hipStream_t s)
 {
     if (fmt == WeightFormat::kQ8_0)
-        return launch_gemv_f<FmtQ8_0>(a, w, y, M, N, K, s);
-    return launch_gemv_f<FmtQ4_0>(a, w, y, M, N, K, s);
+        return launch_gemv_f<FmtQ8_0, false>(a, w, y, M, N, K, s);
+    return launch_gemv_f<FmtQ4_0, false>(a, w, y, M, N, K, s);
+}
+
+hipError_t launch_gemv_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
+                            int N, int K, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemv_f<FmtQ8_0, true>(a, w, y, M, N, K, s);
+    return launch_gemv_f<FmtQ4_0, true>(a, w, y, M, N, K, s);
 }
 
 }  // namespace q4k

@@ -15,6 +15,9 @@ hipError_t launch_dequant(WeightFormat fmt, const uint8_t *w, size_t n_blocks, f
                           hipStream_t s);
 hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
                        int K, hipStream_t s);
+// a: [M, K] bfloat16 bit patterns, 1 <= M <= 8.
+hipError_t launch_gemv_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
+                            int N, int K, hipStream_t s);
 // workspace: q4v::gemm_workspace_bytes(M, N, K) bytes when the split path is
 // taken (q4v::gemm_splits_activations(K)), else unused.
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,

@@ -39,7 +39,13 @@ WORKLOADS = {
     "q8_0_gemm_2048x14336x4096": dict(kind="gemm", fmt="q8_0", M=2048, N=14336, K=4096,
                                       w_seed=400, a_seed=401),
     "q8_0_dequant_14336x4096": dict(kind="dequant", fmt="q8_0", N=14336, K=4096, w_seed=400),
-    # The prefill GEMMs with bfloat16 activations (``act="bf16"``).
+    # The decode GEMVs and prefill GEMMs with bfloat16 activations (``act="bf16"``).
+    "gemv_bf16_1x4096x4096": dict(kind="gemv", act="bf16", M=1, N=4096, K=4096, w_seed=200,
+                                  a_seed=201),
+    "gemv_bf16_8x4096x4096": dict(kind="gemv", act="bf16", M=8, N=4096, K=4096, w_seed=200,
+                                  a_seed=202),
+    "q8_0_gemv_bf16_1x4096x4096": dict(kind="gemv", act="bf16", fmt="q8_0", M=1, N=4096,
+                                       K=4096, w_seed=200, a_seed=201),
     "gemm_bf16_1024x4096x4096": dict(kind="gemm", act="bf16", M=1024, N=4096, K=4096, w_seed=200,
                                      a_seed=203),
     "gemm_bf16_2048x14336x4096": dict(kind="gemm", act="bf16", M=2048, N=14336, K=4096,

@@ -156,6 +156,30 @@ int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
 size_t q8_gemm_workspace_bytes(int M, int N, int K);
 
 /*
+ * q4_gemv_bf16 — q4_gemv with bfloat16 activations: y = a @ dequant(W)^T for
+ * 1 <= M <= 8, y in f32 (section qmatvec_q4_0 as for q4_gemv; the activation
+ * type is the one of the 4-bit workload in TensorFold pull request #2017,
+ * section Setup, whose own 4-bit format is another one).
+ *   a         [M, K] bfloat16, row-major, as raw 16-bit patterns.
+ *   w_q, y, M, N, K: as q4_gemv. Errors: as q4_gemv, with a counted at
+ *             2 bytes per element.
+ * The activations of each row are scaled, per stretch of K the kernel
+ * handles at once (256 or 512 elements of K on 16-byte aligned rows, the whole
+ * row otherwise), by a power of two that brings the stretch's largest
+ * magnitude to [2^15, 2^16) on the matrix-core operand; every element within
+ * 2^28 of that magnitude (2^32 for q8_gemv_bf16) is then an exact binary16
+ * number and each product with a weight code is exact in f32. Smaller
+ * elements are rounded to 2^-24 on the scaled grid. Accuracy, for rows within
+ * that range: as q4_gemv. Deterministic.
+ */
+int q4_gemv_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y,
+                 int M, int N, int K, void *stream);
+
+/* q8_gemv_bf16 — q4_gemv_bf16 over a Q8_0 weight stream (w_bytes == N * (K/32) * 34). */
+int q8_gemv_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y,
+                 int M, int N, int K, void *stream);
+
+/*
  * q4_gemm_bf16 — q4_gemm with bfloat16 activations: y = a @ dequant(W)^T for
  * any M >= 1, y in f32. The 4-bit prefill measured in TensorFold pull request
  * #2017 ("Vulkan: qmm_q4_tile_rows computes four rows and two columns of a

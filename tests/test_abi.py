@@ -97,7 +97,7 @@ def _wb(N, K, fmt="q4"):
 
 @fake_addresses
 @pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm", "q8_gemv", "q8_gemm", "q4_gemm_bf16",
-                                   "q8_gemm_bf16"])
+                                   "q8_gemm_bf16", "q4_gemv_bf16", "q8_gemv_bf16"])
 def test_product_argument_checks(entry):
     S = binding
     f = entry[:2]
@@ -135,13 +135,16 @@ def test_bf16_activations_are_two_bytes(f):
     assert _prod(f + "_gemm", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_ALIAS
     assert _prod(f + "_gemm_bf16", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_WORKSPACE
     assert _prod(f + "_gemm_bf16", A, W, wb, A + 240, 2, 4, 64) == binding.Q4_ERR_ALIAS
+    assert _prod(f + "_gemv", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_ALIAS
+    assert _prod(f + "_gemv_bf16", A, W, wb, A + 240, 2, 4, 64) == binding.Q4_ERR_ALIAS
 
 
 @fake_addresses
 @pytest.mark.parametrize("f", ["q4", "q8"])
-def test_gemv_row_limit(f):
-    assert _prod(f + "_gemv", A, W, _wb(4, 64, f), Y, 9, 4, 64) == binding.Q4_ERR_SHAPE
-    assert _prod(f + "_gemv", None, None, _wb(4, 64, f), None, 0, 4, 64) == binding.Q4_OK
+@pytest.mark.parametrize("act", ["", "_bf16"])
+def test_gemv_row_limit(f, act):
+    assert _prod(f + "_gemv" + act, A, W, _wb(4, 64, f), Y, 9, 4, 64) == binding.Q4_ERR_SHAPE
+    assert _prod(f + "_gemv" + act, None, None, _wb(4, 64, f), None, 0, 4, 64) == binding.Q4_OK
 
 
 @fake_addresses

@@ -1,9 +1,10 @@
-"""GPU parity of q4_gemm_bf16 / q8_gemm_bf16 (bfloat16 activations, the
-activation type of the 4-bit prefill in TensorFold pull request #2017, section
-Setup) against the oracle: the bfloat16 patterns widened to f32 by the oracle's
-decode, then the oracle's f64 product over the dequantized weights (sections
-matmul_q4_0_tiled, dequant_q4_0 and dequant_q8_0 of "fuel-vulkan-kernels —
-quantized (GGML) kernel contracts"). Every output must satisfy
+"""GPU parity of q4_gemv_bf16 / q8_gemv_bf16 and q4_gemm_bf16 / q8_gemm_bf16
+(bfloat16 activations, the activation type of the 4-bit workload in
+TensorFold pull request #2017, section Setup) against the oracle: the bfloat16
+patterns widened to f32 by the oracle's decode, then the oracle's f64 product
+over the dequantized weights (sections qmatvec_q4_0, matmul_q4_0_tiled,
+dequant_q4_0 and dequant_q8_0 of "fuel-vulkan-kernels — quantized (GGML)
+kernel contracts"). Every output must satisfy
 |y - y_ref| <= 1e-5 * sum|a w| + 1e-6."""
 import numpy as np
 import pytest
@@ -21,7 +22,9 @@ from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_
                          oracle_matmul_sampled, random_blocks, to_dev, weight_blob)
 
 GEMM_BF16 = {"q4_0": binding.q4_gemm_bf16, "q8_0": binding.q8_gemm_bf16}
+GEMV_BF16 = {"q4_0": binding.q4_gemv_bf16, "q8_0": binding.q8_gemv_bf16}
 GEMM_F32 = {"q4_0": binding.q4_gemm, "q8_0": binding.q8_gemm}
+GEMV_F32 = {"q4_0": binding.q4_gemv, "q8_0": binding.q8_gemv}
 WS_BYTES = {"q4_0": binding.q4_gemm_bf16_workspace_bytes,
             "q8_0": binding.q8_gemm_bf16_workspace_bytes}
 
@@ -30,18 +33,22 @@ def _bits_dev(bits: np.ndarray) -> torch.Tensor:
     return to_dev(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
 
 
-def _run(fmt, bits: np.ndarray, blob: np.ndarray, N: int, K: int, w_dev=None, workspace=None):
+def _run(fmt, bits: np.ndarray, blob: np.ndarray, N: int, K: int, w_dev=None, workspace=None,
+         kind="gemm"):
     M = bits.shape[0]
     y = Guarded(M * N, torch.float32)
     w = to_dev(blob) if w_dev is None else w_dev
-    GEMM_BF16[fmt](_bits_dev(bits), w, y.view, M, N, K, workspace=workspace)
+    if kind == "gemm":
+        GEMM_BF16[fmt](_bits_dev(bits), w, y.view, M, N, K, workspace=workspace)
+    else:
+        GEMV_BF16[fmt](_bits_dev(bits), w, y.view, M, N, K)
     torch.cuda.synchronize()
     assert y.guards_intact()
     return y.host().reshape(M, N)
 
 
-def _full_check(fmt, bits, blob, N, K, what):
-    got = _run(fmt, bits, blob, N, K)
+def _full_check(fmt, bits, blob, N, K, what, kind="gemm"):
+    got = _run(fmt, bits, blob, N, K, kind=kind)
     ref, bound = oracle_matmul(fmt)(oracle.bf16_to_f32(bits), blob, N, K)
     return assert_within_tolerance(got, ref, bound, "%s %s" % (fmt, what))
 
@@ -72,7 +79,27 @@ def test_workloads_sampled(name):
     assert_within_tolerance(got[mi, ni], ref, bound, "%s %s" % (fmt, name))
 
 
+@pytest.mark.parametrize("name", ["gemv_bf16_1x4096x4096", "gemv_bf16_8x4096x4096",
+                                  "q8_0_gemv_bf16_1x4096x4096"])
+def test_gemv_workloads_full_output(name):
+    s = wl.WORKLOADS[name]
+    fmt = s.get("fmt", "q4_0")
+    blob = weight_blob(fmt, s["N"], s["K"], s["w_seed"])
+    bits = wl.activations_bf16(s["a_seed"], s["M"], s["K"])
+    _full_check(fmt, bits, blob, s["N"], s["K"], name, kind="gemv")
+
+
 # ------------------------------------------------------ shapes and tails
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", [(17, 32), (300, 256), (129, 1056), (64, 4096), (33, 8192)])
+def test_gemv_shapes(fmt, M, N, K):
+    # K % 256 != 0 (32, 1056) takes the general kernel.
+    blob = weight_blob(fmt, N, K, 10 * M + K)
+    bits = wl.activations_bf16(20 * M + N, M, K)
+    _full_check(fmt, bits, blob, N, K, "gemv_bf16 %dx%dx%d" % (M, N, K), kind="gemv")
+
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M,N,K", [(1, 300, 256), (8, 129, 64), (65, 70, 160), (5, 257, 128),
@@ -97,23 +124,24 @@ def test_every_code_and_random_scales(fmt, M, K):
 # ---------------------------------------------- the per-row power-of-two scale
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("K", [1024, 96])
+@pytest.mark.parametrize("kind,M,K", [("gemm", 40, 1024), ("gemm", 40, 96), ("gemv", 1, 4096),
+                                      ("gemv", 7, 2048), ("gemv", 3, 96)])
 @pytest.mark.parametrize("k", [-90, -40, -7, 9, 60, 100])
-def test_row_scaling_commutes_exactly(fmt, K, k):
+def test_row_scaling_commutes_exactly(fmt, kind, M, K, k):
     # Scaling a row by 2^k moves only its exponent, so the device result must
     # be the unscaled one times 2^k bit for bit (no result is subnormal or
-    # overflows at these k), on the split path (K = 1024) and the general one.
-    M, N = 40, 96
+    # overflows at these k), on every kernel path of either product.
+    N = 96
     blob = weight_blob(fmt, N, K, 40)
     bits = wl.activations_bf16(41, M, K)
-    y0 = _run(fmt, bits, blob, N, K)
-    yk = _run(fmt, _shift(bits, k), blob, N, K)
+    y0 = _run(fmt, bits, blob, N, K, kind=kind)
+    yk = _run(fmt, _shift(bits, k), blob, N, K, kind=kind)
     assert np.array_equal(yk, (y0.astype(np.float64) * 2.0 ** k).astype(np.float32))
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("K", [1024, 96])
-def test_mixed_magnitude_rows(fmt, K):
+@pytest.mark.parametrize("kind,K", [("gemm", 1024), ("gemm", 96), ("gemv", 1024), ("gemv", 96)])
+def test_mixed_magnitude_rows(fmt, kind, K):
     # Rows of very different size, each within its own exact range, an
     # all-zero row, a row of bfloat16 subnormals, and the largest finite value.
     M, N = 8, 64
@@ -126,16 +154,18 @@ def test_mixed_magnitude_rows(fmt, K):
     bits[6] = _shift(bits[6], 20) & 0x7FFF          # |a| up to ~2^22, all positive
     bits[7] = 0                                     # the largest finite bfloat16,
     bits[7, [0, 33, K // 2, K - 1]] = [0x7F7F, 0xFF7F, 0x7F7F, 0xFF7F]   # four times
-    _full_check(fmt, bits, weight_blob(fmt, N, K, 9), N, K, "mixed rows K=%d" % K)
+    _full_check(fmt, bits, weight_blob(fmt, N, K, 9), N, K, "%s mixed rows K=%d" % (kind, K),
+                kind=kind)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_row_span_at_the_exact_limit(fmt):
+@pytest.mark.parametrize("kind,K", [("gemm", 64), ("gemv", 256), ("gemv", 64)])
+def test_row_span_at_the_exact_limit(fmt, kind, K):
     # Elements from the row maximum down to 2^-28 (Q4_0) or 2^-32 (Q8_0) of it
     # are all exact binary16 numbers after the row scale: with d = 1 blocks and
     # every product placed in its own output column, each output is one exact
-    # product a * code.
-    K = 64
+    # product a * code. (The GEMV scales per stretch of K; the whole row is one
+    # stretch at these K.)
     span = 28 if fmt == "q4_0" else 32
     codes_n = 4 if fmt == "q4_0" else 100       # one nonzero code per weight row
     N = K
@@ -148,7 +178,7 @@ def test_row_span_at_the_exact_limit(fmt):
     vals = (1.0 + mant / 128.0) * 2.0 ** expo
     vals[1::3] *= -1
     bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)[None, :]
-    got = _run(fmt, bits, blob, N, K)[0]
+    got = _run(fmt, bits, blob, N, K, kind=kind)[0]
     want = (oracle.bf16_to_f32(bits)[0].astype(np.float64) * codes_n).astype(np.float32)
     assert np.array_equal(got, want)
 
@@ -169,8 +199,8 @@ def _integer_blob(fmt, codes):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("K", [512, 96])
-def test_integer_data_is_exact(fmt, K):
+@pytest.mark.parametrize("kind,K", [("gemm", 512), ("gemm", 96), ("gemv", 512), ("gemv", 96)])
+def test_integer_data_is_exact(fmt, kind, K):
     N, M = 32, 3
     lo, hi, zero = (0, 16, 8) if fmt == "q4_0" else (-128, 128, 0)
     codes = wl.uniform_ints(10, lo, hi, (N, K))
@@ -180,32 +210,34 @@ def test_integer_data_is_exact(fmt, K):
     a = wl.uniform_ints(11, -8, 9, (M, K)).astype(np.float32)
     bits = (a.view(np.uint32) >> 16).astype(np.uint16)
     ref = (a.astype(np.int64) @ (codes - zero).T).astype(np.float64)
-    assert (_run(fmt, bits, blob, N, K) == ref).all()
+    assert (_run(fmt, bits, blob, N, K, kind=kind) == ref).all()
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_one_hot_activations_pick_weights_exactly(fmt):
-    N, K, M = 96, 1024, 19
+@pytest.mark.parametrize("kind,M", [("gemm", 19), ("gemv", 1), ("gemv", 8)])
+def test_one_hot_activations_pick_weights_exactly(fmt, kind, M):
+    N, K = 96, 1024
     blob = random_blocks(fmt, N * K // 32, 3)
     w = getattr(oracle, fmt + "_dequant")(blob).reshape(N, K)
     ks = wl.uniform_ints(4, 0, K, M)
     bits = np.zeros((M, K), np.uint16)
     bits[np.arange(M), ks] = 0x3F80                 # 1.0
-    assert (_run(fmt, bits, blob, N, K) == w[:, ks].T).all()
+    assert (_run(fmt, bits, blob, N, K, kind=kind) == w[:, ks].T).all()
 
 
 # ------------------------------------------------------ agreement and gates
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("K", [2048, 96])
-def test_agrees_with_the_f32_gemm(fmt, K):
-    M, N = 100, 256
+@pytest.mark.parametrize("kind,M,K", [("gemm", 100, 2048), ("gemm", 100, 96), ("gemv", 1, 4096),
+                                      ("gemv", 8, 2048), ("gemv", 4, 96)])
+def test_agrees_with_the_f32_path(fmt, kind, M, K):
+    N = 256
     blob = weight_blob(fmt, N, K, 14)
     bits = wl.activations_bf16(15, M, K)
     a32 = oracle.bf16_to_f32(bits)
-    y16 = _run(fmt, bits, blob, N, K)
+    y16 = _run(fmt, bits, blob, N, K, kind=kind)
     y32 = torch.empty(M * N, device=DEV)
-    GEMM_F32[fmt](to_dev(a32), to_dev(blob), y32, M, N, K)
+    (GEMM_F32 if kind == "gemm" else GEMV_F32)[fmt](to_dev(a32), to_dev(blob), y32, M, N, K)
     torch.cuda.synchronize()
     _, bound = oracle_matmul(fmt)(a32, blob, N, K)
     diff = np.abs(y16.astype(np.float64) - y32.cpu().numpy().reshape(M, N))
@@ -213,13 +245,14 @@ def test_agrees_with_the_f32_gemm(fmt, K):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-def test_repeat_is_bitwise_identical(fmt):
-    N, K, M = 272, 1024, 200
+@pytest.mark.parametrize("kind,M", [("gemm", 200), ("gemv", 3)])
+def test_repeat_is_bitwise_identical(fmt, kind, M):
+    N, K = 272, 1024
     blob = weight_blob(fmt, N, K, 12)
     bits = wl.activations_bf16(13, M, K)
     w = to_dev(blob)
-    y1 = _run(fmt, bits, blob, N, K, w_dev=w)
-    y2 = _run(fmt, bits, blob, N, K, w_dev=w)
+    y1 = _run(fmt, bits, blob, N, K, w_dev=w, kind=kind)
+    y2 = _run(fmt, bits, blob, N, K, w_dev=w, kind=kind)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
@@ -228,6 +261,8 @@ def test_empty_problems_are_no_ops(fmt):
     bb = 18 if fmt == "q4_0" else 34
     GEMM_BF16[fmt](None, None, None, 0, 16, 64, w_bytes=16 * 2 * bb)
     GEMM_BF16[fmt](None, None, None, 3, 0, 64, w_bytes=0)
+    GEMV_BF16[fmt](None, None, None, 0, 16, 64, w_bytes=16 * 2 * bb)
+    GEMV_BF16[fmt](None, None, None, 3, 0, 64, w_bytes=0)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

@@ -389,6 +389,10 @@ def main():
             log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
+        for name, st in (("gemv_1x512x4096", args.steps), ("gemm_2048x1792x4096", 50)):
+            log("row: %s (one GPU's share of an 8-way row split)" % name)
+            rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
+                                      min(args.warmup, 10)))
         log("row: Q8_0 dequant 14336x4096")
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10),
                                   "q8_0_dequant_14336x4096"))
@@ -407,6 +411,13 @@ def main():
         qrow["roofline"]["measured_read_ceiling_GBs"] = qceil["kernel_GBs"]
         qrow["roofline"]["frac_of_measured_read_ceiling"] = (
             qrow["roofline"]["achieved"] / qceil["kernel_GBs"])
+        # The same for the 8-way shard of the decode GEMV.
+        srow = next(r for r in rows if r["workload"] == "gemv_1x512x4096")
+        sceil = bench_stream_ceiling(torch, srow["algorithmic_bytes"], args.steps, args.warmup)
+        rows.append(sceil)
+        srow["roofline"]["measured_read_ceiling_GBs"] = sceil["kernel_GBs"]
+        srow["roofline"]["frac_of_measured_read_ceiling"] = (
+            srow["roofline"]["achieved"] / sceil["kernel_GBs"])
     head["roofline"]["frac_of_measured_read_ceiling"] = (
         head["roofline"]["achieved"] / ceil["kernel_GBs"])
     head["roofline"]["measured_read_ceiling_GBs"] = ceil["kernel_GBs"]

@@ -660,19 +660,55 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
 // after scaling, 2^(E - 39) in the row's own units for max |a| in [2^E,
 // 2^(E+1))).
 //
-// * k_row_exp_bf16: one wavefront per row finds the largest magnitude (the
-//   largest bfloat16 bit pattern with the sign cleared, which orders finite
-//   values by magnitude) and stores p = 15 - E; p = 0 for an all-zero row or
-//   one that holds an infinity or NaN.
-// * k_gemm_prep_bf16: as k_gemm_split_a, one wavefront per 16-row group and
-//   block, writing only the hi operand: operand [mt][kb][sub][lane] in the
-//   format's slot order, rows past M zero.
-// * k_gemm_prep_bf16_f32: for shapes that take the general kernel, the scaled
-//   activations as f32, row-major (f16(a') is then exact and the lo term 0).
+// * The row's exponent: the largest magnitude is the largest bfloat16 bit
+//   pattern with the sign cleared (which orders finite values by magnitude),
+//   and p = 15 - E; p = 0 for an all-zero row or one that holds an infinity
+//   or NaN.
+// * k_row_exp_bf16: one wavefront per row, all of its loads in flight at once.
+// * k_gemm_prep_bf16 (split path): as k_gemm_split_a, one wavefront per
+//   16-row group and pair of blocks, writing only the hi operand: operand
+//   [mt][kb][sub][lane] in the format's slot order, rows past M zero. (One
+//   workgroup per 16-row group doing both passes was measured slower: at
+//   M = 1024 it leaves three quarters of the CUs idle.)
+// * k_gemm_prep_bf16_f32 (general kernel's shapes): the scaled activations as
+//   f32, row-major (f16(a') is then exact and the lo term 0).
 
 constexpr int kRowExpWaves = 4;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Largest |a| of row `row` (K bfloat16 values, K % 32 == 0) as a cleared-sign
+// bit pattern, in every lane of the wavefront.
+__device__ __forceinline__ uint32_t row_max_bits_bf16(const uint16_t *__restrict__ row, int K,
+                                                      int lane)
+{
+    // A row is a whole number of 64-byte lines, read 16 bytes a lane.
+    const uint4 *r4 = reinterpret_cast<const uint4 *>(row);
+    uint32_t mx = 0;
+#pragma unroll 8
+    for (int i = lane; i < K / 8; i += 64) {
+        const uint4 v = r4[i];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mx = max(mx, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    return mx;
+}
+
+// p = 15 - E for a largest magnitude in [2^E, 2^(E+1)); 0 for zero or non-finite.
+__device__ __forceinline__ int row_exp_from_bits(uint32_t mx)
+{
+    if (mx == 0 || mx >= 0x7F80u)
+        return 0;
+    const int ef = (int)(mx >> 7);
+    // Subnormals are (mantissa) 2^-133.
+    const int E = ef > 0 ? ef - 127 : (31 - __builtin_clz(mx)) - 133;
+    return 15 - E;
+}
 
 __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_bf16(const uint16_t *__restrict__ a,
                                                                    int *__restrict__ row_exp,
@@ -682,30 +718,14 @@ __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_bf16(const uint16
     const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
     if (m >= M)   // whole wavefronts only
         return;
-    // K % 32 == 0: a row is a whole number of 64-byte lines, read 16 bytes a lane.
-    const uint4 *row = reinterpret_cast<const uint4 *>(a + (size_t)m * K);
-    uint32_t mx = 0;
-    for (int i = lane; i < K / 8; i += 64) {
-        const uint4 v = row[i];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            mx = max(mx, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    if (lane == 0) {
-        int p = 0;
-        if (mx != 0 && mx < 0x7F80u) {
-            const int ef = (int)(mx >> 7);
-            // max |a| in [2^E, 2^(E+1)): subnormals are (mantissa) 2^-133.
-            const int E = ef > 0 ? ef - 127 : (31 - __builtin_clz(mx)) - 133;
-            p = 15 - E;
-        }
+    const int p = row_exp_from_bits(row_max_bits_bf16(a + (size_t)m * K, K, lane));
+    if (lane == 0)
         row_exp[m] = p;
-    }
 }
+
+// Blocks per wavefront of k_gemm_prep_bf16 (the split path has an even number
+// of blocks per row): each lane's row segment is a whole 128-byte line.
+constexpr int kPrepBlocks = 2;
 
 template <class F>
 __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_prep_bf16(const uint16_t *__restrict__ a,
@@ -717,31 +737,40 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_prep_bf16(const uint1
     const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
     if (gw >= n_waves)   // whole wavefronts only
         return;
-    const int nblk = K >> 5;
-    const long long R = gw / nblk;                // 16-row group
-    const int kb = (int)(gw - R * nblk);
+    const int nblk = K >> 5, npb = nblk / kPrepBlocks;
+    const long long R = gw / npb;                 // 16-row group
+    const int kb0 = (int)(gw - R * npb) * kPrepBlocks;
     const int li = lane & 15, g = lane >> 4;
     const long long m = R * 16 + li;
-    f16x8 hi = {};
+    f16x8 hi[kPrepBlocks] = {};
     if (m < M) {
-        const uint16_t *blk = a + m * K + (long long)kb * 32;
-        const uint2 L = *reinterpret_cast<const uint2 *>(blk + F::a_lo(g));
-        const uint2 H = *reinterpret_cast<const uint2 *>(blk + F::a_hi(g));
+        const uint16_t *blk0 = a + m * K + (long long)kb0 * 32;
+        uint2 L[kPrepBlocks], H[kPrepBlocks];
+#pragma unroll
+        for (int u = 0; u < kPrepBlocks; ++u) {
+            L[u] = *reinterpret_cast<const uint2 *>(blk0 + u * 32 + F::a_lo(g));
+            H[u] = *reinterpret_cast<const uint2 *>(blk0 + u * 32 + F::a_hi(g));
+        }
         const int p = row_exp[m];
         const int ph = p - F::kHiLog2;   // slots 4..7 carry a further 2^-kHiLog2
-        // Elements 0..3 of a group are the low and high halves of two dwords,
-        // in the slot order x, z, y, w of the f32 path.
-        const float e[8] = {
-            ldexpf(bf16_bits_to_f32(L.x & 0xFFFFu), p), ldexpf(bf16_bits_to_f32(L.y & 0xFFFFu), p),
-            ldexpf(bf16_bits_to_f32(L.x >> 16), p),     ldexpf(bf16_bits_to_f32(L.y >> 16), p),
-            ldexpf(bf16_bits_to_f32(H.x & 0xFFFFu), ph), ldexpf(bf16_bits_to_f32(H.y & 0xFFFFu), ph),
-            ldexpf(bf16_bits_to_f32(H.x >> 16), ph),    ldexpf(bf16_bits_to_f32(H.y >> 16), ph)};
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            hi[s] = (f16)e[s];
+        for (int u = 0; u < kPrepBlocks; ++u) {
+            // Elements 0..3 of a group are the low and high halves of two
+            // dwords, in the slot order x, z, y, w of the f32 path.
+            const float e[8] = {
+                ldexpf(bf16_bits_to_f32(L[u].x & 0xFFFFu), p), ldexpf(bf16_bits_to_f32(L[u].y & 0xFFFFu), p),
+                ldexpf(bf16_bits_to_f32(L[u].x >> 16), p),     ldexpf(bf16_bits_to_f32(L[u].y >> 16), p),
+                ldexpf(bf16_bits_to_f32(H[u].x & 0xFFFFu), ph), ldexpf(bf16_bits_to_f32(H[u].y & 0xFFFFu), ph),
+                ldexpf(bf16_bits_to_f32(H[u].x >> 16), ph),    ldexpf(bf16_bits_to_f32(H[u].y >> 16), ph)};
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                hi[u][s] = (f16)e[s];
+        }
     }
-    const long long mt = R >> 3;
-    ops[(mt * nblk + kb) * slab_ops<true>() + (R & 7) * 64 + lane] = bitcast<u32x4>(hi);
+    u32x4 *dst = ops + ((R >> 3) * nblk + kb0) * slab_ops<true>() + (R & 7) * 64 + lane;
+#pragma unroll
+    for (int u = 0; u < kPrepBlocks; ++u)
+        dst[u * slab_ops<true>()] = bitcast<u32x4>(hi[u]);
 }
 
 __global__ __launch_bounds__(256) void k_gemm_prep_bf16_f32(const uint16_t *__restrict__ a,
@@ -812,7 +841,9 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
                              (const float *)act, w, y, M, N, K, tiles_m, tiles_n,
                              (const int *)row_exp);
     }
-    const long long n_waves = (long long)tiles_m * 8 * (K / 32);
+    // One wavefront per 16-row group of the padded tiles and pair of blocks
+    // (groups past M write zeros).
+    const long long n_waves = (long long)tiles_m * 8 * (K / 32 / kPrepBlocks);
     const long long grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
     if (grid > 0x7fffffffLL)
         return hipErrorInvalidValue;

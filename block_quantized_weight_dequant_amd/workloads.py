@@ -39,6 +39,10 @@ WORKLOADS = {
     "q8_0_gemm_2048x14336x4096": dict(kind="gemm", fmt="q8_0", M=2048, N=14336, K=4096,
                                       w_seed=400, a_seed=401),
     "q8_0_dequant_14336x4096": dict(kind="dequant", fmt="q8_0", N=14336, K=4096, w_seed=400),
+    # One GPU's share when the weight rows are split eight ways: the decode GEMV
+    # and the FFN prefill GEMM at N / 8.
+    "gemv_1x512x4096": dict(kind="gemv", M=1, N=512, K=4096, w_seed=500, a_seed=201),
+    "gemm_2048x1792x4096": dict(kind="gemm", M=2048, N=1792, K=4096, w_seed=501, a_seed=401),
     # The decode GEMVs and prefill GEMMs with bfloat16 activations (``act="bf16"``).
     "gemv_bf16_1x4096x4096": dict(kind="gemv", act="bf16", M=1, N=4096, K=4096, w_seed=200,
                                   a_seed=201),

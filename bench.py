@@ -153,14 +153,25 @@ def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
     return blob
 
 
-def gemv_kernel_name(M, K, fmt="q4_0", act="f32"):
+def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0):
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
-    per = (((nblk + 7) // 8) + 7) & ~7
-    last = nblk - (nblk - 1) // per * per
-    ch = 16 if (per % 16 == 0 and last % 16 == 0) else 8
+    ks = kl = nblk
+    if splitk:   # the library's automatic split (q4v::gemv_split_plan)
+        groups = (N + 15) // 16
+        want = min(-(-256 // groups), nblk // 64, nblk // 8)
+        p0 = (((nblk + 7) // 8) + 7) & ~7
+        l0 = nblk - (nblk - 1) // p0 * p0
+        if p0 // (16 if (p0 % 16 == 0 and l0 % 16 == 0) else 8) < 3:
+            want = 1
+        if want > 1:
+            ks = (-(-nblk // want) + 7) & ~7
+            kl = nblk - (-(-nblk // ks) - 1) * ks
+    per = (((ks + 7) // 8) + 7) & ~7
+    last, tail = ks - (ks - 1) // per * per, kl - (kl - 1) // per * per
+    ch = 16 if (per % 16 == 0 and last % 16 == 0 and tail % 16 == 0) else 8
     return "k_gemv_stream<%s, %d, 8, %d, %s>" % (FMT_TYPE[fmt], M, ch, bf)
 
 
@@ -185,7 +196,12 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
-    if s["kind"] == "gemv":
+    if s["kind"] == "gemv" and s.get("splitk"):
+        gemv = getattr(q4, f + "_gemv_splitk")
+        ws_bytes = getattr(q4, f + "_gemv_splitk_workspace_bytes")(M, N, K, 0)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        fn = lambda k: gemv(a, blobs[k % R], y, M, N, K, 0, workspace=ws)
+    elif s["kind"] == "gemv":
         gemv = getattr(q4, f + ("_gemv_bf16" if act == "bf16" else "_gemv"))
         fn = lambda k: gemv(a, blobs[k % R], y, M, N, K)
     else:
@@ -206,8 +222,11 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
            "job_GBs": algo_bytes * steps / t["wall_s"] / 1e9,
            "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
     if s["kind"] == "gemv":
-        kernel = gemv_kernel_name(M, K, fmt, act)
+        kernel = gemv_kernel_name(M, K, fmt, act, s.get("splitk", False), N)
         row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
+        if s.get("splitk"):
+            row["roofline"]["note"] = ("the time is the whole call: the split GEMV kernel plus "
+                                       "the kernel that adds the splits' partials")
     else:
         kernel = gemm_kernel_name(K, fmt, act)
         if act == "bf16":
@@ -389,7 +408,8 @@ def main():
             log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
-        for name, st in (("gemv_1x512x4096", args.steps), ("gemm_2048x1792x4096", 50)):
+        for name, st in (("gemv_1x512x4096", args.steps), ("gemm_2048x1792x4096", 50),
+                         ("gemv_1x512x14336", args.steps), ("gemv_splitk_1x512x14336", args.steps)):
             log("row: %s (one GPU's share of an 8-way row split)" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
@@ -418,6 +438,13 @@ def main():
         srow["roofline"]["measured_read_ceiling_GBs"] = sceil["kernel_GBs"]
         srow["roofline"]["frac_of_measured_read_ceiling"] = (
             srow["roofline"]["achieved"] / sceil["kernel_GBs"])
+        # And for the K = 14336 share, plain and split across workgroups.
+        krows = [r for r in rows if r["workload"] in ("gemv_1x512x14336", "gemv_splitk_1x512x14336")]
+        kceil = bench_stream_ceiling(torch, krows[0]["algorithmic_bytes"], args.steps, args.warmup)
+        rows.append(kceil)
+        for r in krows:
+            r["roofline"]["measured_read_ceiling_GBs"] = kceil["kernel_GBs"]
+            r["roofline"]["frac_of_measured_read_ceiling"] = r["roofline"]["achieved"] / kceil["kernel_GBs"]
     head["roofline"]["frac_of_measured_read_ceiling"] = (
         head["roofline"]["achieved"] / ceil["kernel_GBs"])
     head["roofline"]["measured_read_ceiling_GBs"] = ceil["kernel_GBs"]

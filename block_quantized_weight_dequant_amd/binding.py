@@ -33,7 +33,8 @@ EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_ge
            "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm",
            "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize", "q4_gemm_bf16",
            "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes",
-           "q4_gemv_bf16", "q8_gemv_bf16")
+           "q4_gemv_bf16", "q8_gemv_bf16", "q4_gemv_splitk", "q4_gemv_splitk_workspace_bytes",
+           "q8_gemv_splitk", "q8_gemv_splitk_workspace_bytes")
 
 
 class Q4Error(RuntimeError):
@@ -69,6 +70,10 @@ def _load_library():
             getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
             getattr(lib, f + g + "_workspace_bytes").restype = sz
             getattr(lib, f + g + "_workspace_bytes").argtypes = [i32, i32, i32]
+        getattr(lib, f + "_gemv_splitk").restype = i32
+        getattr(lib, f + "_gemv_splitk").argtypes = [P, P, sz, P, i32, i32, i32, i32, P, sz, P]
+        getattr(lib, f + "_gemv_splitk_workspace_bytes").restype = sz
+        getattr(lib, f + "_gemv_splitk_workspace_bytes").argtypes = [i32, i32, i32, i32]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -154,6 +159,46 @@ def q4_gemv_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -
 def q8_gemv_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
     """As q8_gemv with ``a`` a [M, K] bfloat16 tensor (or its address)."""
     _gemv("q8_gemv_bf16", a, w_q, y, M, N, K, w_bytes, stream)
+
+
+def q4_gemv_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    return int(lib.q4_gemv_splitk_workspace_bytes(int(M), int(N), int(K), int(splits)))
+
+
+def q8_gemv_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    return int(lib.q8_gemv_splitk_workspace_bytes(int(M), int(N), int(K), int(splits)))
+
+
+def _gemv_splitk(entry, a, w_q, y, M, N, K, splits, w_bytes, stream, workspace,
+                 workspace_bytes) -> None:
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    ws = workspace
+    if ws is None:
+        need = int(getattr(lib, entry + "_workspace_bytes")(int(M), int(N), int(K), int(splits)))
+        if 0 < need < SIZE_MAX:
+            ws = _scratch(need, stream, y)
+    if workspace_bytes is not None:
+        wsb = int(workspace_bytes)
+    else:
+        wsb = _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0
+    _check(getattr(lib, entry)(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                               int(splits), _addr(ws), wsb, _stream(stream)), entry)
+
+
+def q4_gemv_splitk(a, w_q, y, M: int, N: int, K: int, splits: int = 0, w_bytes=None,
+                   stream=None, workspace=None, workspace_bytes=None) -> None:
+    """As q4_gemv with K split across workgroups (``splits=0``: the library's
+    choice); the partials' workspace is taken from PyTorch's caching allocator
+    unless one is passed."""
+    _gemv_splitk("q4_gemv_splitk", a, w_q, y, M, N, K, splits, w_bytes, stream, workspace,
+                 workspace_bytes)
+
+
+def q8_gemv_splitk(a, w_q, y, M: int, N: int, K: int, splits: int = 0, w_bytes=None,
+                   stream=None, workspace=None, workspace_bytes=None) -> None:
+    """As q4_gemv_splitk over a Q8_0 weight stream."""
+    _gemv_splitk("q8_gemv_splitk", a, w_q, y, M, N, K, splits, w_bytes, stream, workspace,
+                 workspace_bytes)
 
 
 def q4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -75,6 +75,28 @@ static int gemm(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const
                                      as_stream(stream)));
 }
 
+static int gemv_splitk(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const void *w_q,
+                       size_t w_bytes, float *y, int M, int N, int K, int splits, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, sizeof(float), w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS,
+                                block_bytes, &empty);
+    if (st != Q4_OK)
+        return st;
+    if (splits < 0)
+        return Q4_ERR_SHAPE;
+    if (empty)
+        return Q4_OK;
+    st = q4v::check_workspace(q4v::gemv_splitk_workspace_bytes(M, N, K, splits, block_bytes), a,
+                              sizeof(float), w_q, w_bytes, y, M, N, K, workspace, workspace_bytes);
+    if (st != Q4_OK)
+        return st;
+    return launched(q4k::launch_gemv_splitk(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                            q4v::gemv_split_plan(M, N, K, splits, block_bytes),
+                                            workspace, as_stream(stream)));
+}
+
 static int gemv_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *a,
                      const void *w_q, size_t w_bytes, float *y, int M, int N, int K, void *stream)
 {
@@ -159,6 +181,32 @@ Q4_EXPORT int q8_gemv_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, f
                            int N, int K, void *stream)
 {
     return gemv_bf16(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT size_t q4_gemv_splitk_workspace_bytes(int M, int N, int K, int splits)
+{
+    return q4v::gemv_splitk_workspace_bytes(M, N, K, splits, 18);
+}
+
+Q4_EXPORT size_t q8_gemv_splitk_workspace_bytes(int M, int N, int K, int splits)
+{
+    return q4v::gemv_splitk_workspace_bytes(M, N, K, splits, 34);
+}
+
+Q4_EXPORT int q4_gemv_splitk(const float *a, const void *w_q, size_t w_bytes, float *y, int M,
+                             int N, int K, int splits, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    return gemv_splitk(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, splits,
+                       workspace, workspace_bytes, stream);
+}
+
+Q4_EXPORT int q8_gemv_splitk(const float *a, const void *w_q, size_t w_bytes, float *y, int M,
+                             int N, int K, int splits, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    return gemv_splitk(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, splits,
+                       workspace, workspace_bytes, stream);
 }
 
 Q4_EXPORT size_t q4_gemm_bf16_workspace_bytes(int M, int N, int K)

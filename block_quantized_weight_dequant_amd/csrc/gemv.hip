@@ -43,6 +43,7 @@
 #include "device_common.h"
 #include "formats.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace q4k {
 
@@ -363,7 +364,7 @@ template <class F, int M, int NW, int CH, bool BF>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
-                                                        int per)
+                                                        int per, int ks)
 {
     using C = GemvStreamCfg<F, M, NW, CH, BF>;
     using R = GemvRows<BF, M>;
@@ -383,9 +384,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     uint8_t *s_w = s_mem + wave * C::LDS_PER_WAVE;
     uint8_t *s_a = s_w + C::WBYTES;
 
-    // This wavefront's blocks: [wb0, wb1), a whole number of CH-block chunks
-    // (the host picks per and CH so that every chunk is full).
-    const int wb0 = min(wave * per, nblk), wb1 = min(wb0 + per, nblk);
+    // The workgroup's K split: blocks [kb_lo, kb_hi) (the whole row unless the
+    // call splits K across workgroups, blockIdx.y being the split; each split
+    // then writes its own partial y, M x N f32, at y + split M N). This
+    // wavefront's blocks: [wb0, wb1), a whole number of CH-block chunks (the
+    // host picks ks, per and CH so that every chunk is full).
+    const int kb_lo = (int)blockIdx.y * ks, kb_hi = min(kb_lo + ks, nblk);
+    const int wb0 = min(kb_lo + wave * per, kb_hi), wb1 = min(wb0 + per, kb_hi);
+    y += (size_t)blockIdx.y * (size_t)M * (size_t)N;
 
     // Loader role: row lr = lane % 16, 16-byte columns lc0 + 4 i.
     const int lr = lane & 15, lc0 = lane >> 4;
@@ -664,9 +670,31 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     }
 }
 
+// Sums the partials of a K-split GEMV in split order: y[i] = sum_s part[s][i].
+__global__ __launch_bounds__(256) void k_gemv_split_sum(const float *__restrict__ part,
+                                                       float *__restrict__ y, long long n,
+                                                       int splits)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    float acc = part[i];
+    for (int sp = 1; sp < splits; ++sp)
+        acc += part[(long long)sp * n + i];
+    y[i] = acc;
+}
+
+// Chunk size for a wavefront share of `per` blocks over splits of ks blocks
+// (the last one kl): 16 when every busy wavefront's share divides by 16.
+static int stream_chunk(int per, int ks, int kl)
+{
+    const int last_full = ks - (ks - 1) / per * per, last_tail = kl - (kl - 1) / per * per;
+    return (per % 16 == 0 && last_full % 16 == 0 && last_tail % 16 == 0) ? 16 : 8;
+}
+
 template <class F, int M, bool BF>
 static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N, int K,
-                                hipStream_t s)
+                                hipStream_t s, const q4v::GemvSplit &sp = {1, 0})
 {
     const unsigned grid = (unsigned)((N + 15) / 16);
     // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0 and
@@ -676,15 +704,20 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
     // trip for the whole share at K = 4096), else 8.
     constexpr int NW = kGemvStreamWaves;
     const int nblk = K / 32;
-    if (K % 256 == 0 && (size_t)N * (size_t)nblk * F::kBytes < ((size_t)1 << 31) &&
-        (size_t)M * (size_t)K * (BF ? 2 : 4) < ((size_t)1 << 31)) {
-        const int per = (((nblk + NW - 1) / NW) + 7) & ~7;
-        const int last = nblk - (nblk - 1) / per * per;       // blocks of the last busy wavefront
-        if (per % 16 == 0 && last % 16 == 0)
-            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF>, dim3(grid), dim3(64 * NW), 0, s,
-                                 a, w, y, N, K, per);
-        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF>, dim3(grid), dim3(64 * NW), 0, s, a, w,
-                             y, N, K, per);
+    if (q4v::gemv_streams(M, N, K, F::kBytes, BF ? 2 : 4)) {
+        // K split across sp.splits workgroups of ks blocks each (one split: ks = K/32).
+        const int splits = sp.splits > 1 ? sp.splits : 1;
+        const int ks = splits > 1 ? sp.ks : nblk, kl = nblk - (splits - 1) * ks;
+        const int per = (((ks + NW - 1) / NW) + 7) & ~7;
+        const dim3 g2(grid, (unsigned)splits);
+        hipError_t e;
+        if (stream_chunk(per, ks, kl) == 16)
+            e = launch_kernel(k_gemv_stream<F, M, NW, 16, BF>, g2, dim3(64 * NW), 0, s, a, w,
+                              y, N, K, per, ks);
+        else
+            e = launch_kernel(k_gemv_stream<F, M, NW, 8, BF>, g2, dim3(64 * NW), 0, s, a, w, y,
+                              N, K, per, ks);
+        return e;
     }
     return launch_kernel(k_gemv<F, M, BF>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
 }
@@ -720,6 +753,40 @@ hipError_t launch_gemv_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *
     if (fmt == WeightFormat::kQ8_0)
         return launch_gemv_f<FmtQ8_0, true>(a, w, y, M, N, K, s);
     return launch_gemv_f<FmtQ4_0, true>(a, w, y, M, N, K, s);
+}
+
+template <class F>
+static hipError_t launch_gemv_splitk_f(const float *a, const uint8_t *w, float *y, int M, int N,
+                                       int K, const q4v::GemvSplit &sp, float *part, hipStream_t s)
+{
+    float *out = sp.splits > 1 ? part : y;
+    hipError_t e;
+    switch (M) {
+    case 1: e = launch_gemv_m<F, 1, false>(a, w, out, N, K, s, sp); break;
+    case 2: e = launch_gemv_m<F, 2, false>(a, w, out, N, K, s, sp); break;
+    case 3: e = launch_gemv_m<F, 3, false>(a, w, out, N, K, s, sp); break;
+    case 4: e = launch_gemv_m<F, 4, false>(a, w, out, N, K, s, sp); break;
+    case 5: e = launch_gemv_m<F, 5, false>(a, w, out, N, K, s, sp); break;
+    case 6: e = launch_gemv_m<F, 6, false>(a, w, out, N, K, s, sp); break;
+    case 7: e = launch_gemv_m<F, 7, false>(a, w, out, N, K, s, sp); break;
+    case 8: e = launch_gemv_m<F, 8, false>(a, w, out, N, K, s, sp); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || sp.splits <= 1)
+        return e;
+    const long long n = (long long)M * N;
+    return launch_kernel(k_gemv_split_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                         (const float *)part, y, n, sp.splits);
+}
+
+hipError_t launch_gemv_splitk(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M,
+                              int N, int K, const q4v::GemvSplit &sp, void *workspace,
+                              hipStream_t s)
+{
+    float *part = static_cast<float *>(workspace);
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemv_splitk_f<FmtQ8_0>(a, w, y, M, N, K, sp, part, s);
+    return launch_gemv_splitk_f<FmtQ4_0>(a, w, y, M, N, K, sp, part, s);
 }
 
 }  // namespace q4k

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "validate.h"
+
 namespace q4k {
 
 // Block format of a weight stream.
@@ -18,6 +20,12 @@ hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float
 // a: [M, K] bfloat16 bit patterns, 1 <= M <= 8.
 hipError_t launch_gemv_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
                             int N, int K, hipStream_t s);
+// K split across workgroups: partials of sp.splits splits into `workspace`
+// (sp.splits * M * N f32), then summed into y in split order. sp.splits <= 1
+// runs launch_gemv's kernel (workspace unused).
+hipError_t launch_gemv_splitk(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M,
+                              int N, int K, const q4v::GemvSplit &sp, void *workspace,
+                              hipStream_t s);
 // workspace: q4v::gemm_workspace_bytes(M, N, K) bytes when the split path is
 // taken (q4v::gemm_splits_activations(K)), else unused.
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,

@@ -107,6 +107,19 @@ size_t gemm_workspace_bytes(int M, int N, int K)
     return n;
 }
 
+size_t gemv_splitk_workspace_bytes(int M, int N, int K, int requested, size_t block_bytes)
+{
+    if (M <= 0 || M > Q4_GEMV_MAX_ROWS || N <= 0 || K < 32 || K % 32 != 0 || requested < 0)
+        return 0;
+    const GemvSplit sp = gemv_split_plan(M, N, K, requested, block_bytes);
+    if (sp.splits <= 1)
+        return 0;
+    size_t n = 0;
+    if (!mul_ok((size_t)sp.splits * (size_t)M, (size_t)N, &n) || !mul_ok(n, 4, &n))
+        return SIZE_MAX;
+    return n;
+}
+
 size_t gemm_bf16_workspace_bytes(int M, int N, int K)
 {
     if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0)

@@ -42,6 +42,61 @@ inline bool gemm_bf16_splits(int M, int N, int K)
     return gemm_splits_activations(K) && (long long)M * N < (1LL << 31);
 }
 
+// The streaming GEMV kernel's shapes: 16-byte aligned weight rows (K % 256 ==
+// 0) and 32-bit byte offsets into W and a. Other shapes take the general GEMV
+// kernel.
+inline bool gemv_streams(int M, int N, int K, size_t block_bytes, size_t a_elem)
+{
+    return K > 0 && K % 256 == 0 && (size_t)N * (size_t)(K / 32) * block_bytes < ((size_t)1 << 31) &&
+           (size_t)M * (size_t)K * a_elem < ((size_t)1 << 31);
+}
+
+// A K split of the decode GEMV: `splits` workgroups per 16 output columns, each
+// over ks consecutive blocks (a multiple of 8; the last split takes the rest).
+struct GemvSplit {
+    int splits;
+    int ks;
+};
+
+// Chunks of the streaming GEMV each wavefront walks in turn when K is not
+// split: its share of K/32 blocks (a multiple of 8) over chunks of 16 blocks
+// when every share divides by 16, else 8.
+inline int gemv_chunks_per_wave(int nblk)
+{
+    const int per = ((nblk + 7) / 8 + 7) & ~7, last = nblk - (nblk - 1) / per * per;
+    return per / ((per % 16 == 0 && last % 16 == 0) ? 16 : 8);
+}
+
+// The split a q4_gemv_splitk / q8_gemv_splitk call uses: `requested` splits,
+// at most one per 8 blocks, and 1 (no split) for shapes off the streaming
+// kernel or invalid ones. 0 asks for the library's choice: no split unless
+// each wavefront would walk at least 3 chunks in turn (below that, the extra
+// kernel that adds the partials costs more than the split saves), else
+// ceil(256 / ceil(N / 16)) splits (enough workgroups for 256 compute units),
+// at most one per 64 blocks.
+inline GemvSplit gemv_split_plan(int M, int N, int K, int requested, size_t block_bytes)
+{
+    if (M <= 0 || N <= 0 || requested < 0 || !gemv_streams(M, N, K, block_bytes, 4))
+        return {1, 0};
+    const int nblk = K / 32, groups = (N + 15) / 16;
+    int want = requested;
+    if (want == 0) {
+        want = (256 + groups - 1) / groups;
+        want = want < nblk / 64 ? want : nblk / 64;
+        if (gemv_chunks_per_wave(nblk) < 3)
+            want = 1;
+    }
+    want = want < nblk / 8 ? want : nblk / 8;
+    if (want <= 1)
+        return {1, nblk};
+    const int ks = ((nblk + want - 1) / want + 7) & ~7;
+    return {(nblk + ks - 1) / ks, ks};
+}
+
+// Workspace bytes of a K-split GEMV: splits * M * N f32 partials, or 0 when the
+// call does not split (then the workspace is not used).
+size_t gemv_splitk_workspace_bytes(int M, int N, int K, int requested, size_t block_bytes);
+
 // Bytes at the start of a bfloat16 GEMM workspace that hold the per-row
 // exponents (M int32, padded to 256 bytes); the activation operands follow.
 inline size_t gemm_bf16_row_exp_bytes(int M) { return ((size_t)M * 4 + 255) / 256 * 256; }

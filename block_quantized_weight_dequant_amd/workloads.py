@@ -43,6 +43,11 @@ WORKLOADS = {
     # and the FFN prefill GEMM at N / 8.
     "gemv_1x512x4096": dict(kind="gemv", M=1, N=512, K=4096, w_seed=500, a_seed=201),
     "gemm_2048x1792x4096": dict(kind="gemm", M=2048, N=1792, K=4096, w_seed=501, a_seed=401),
+    # The same share of an FFN down-projection decode (K = 14336), plain and
+    # with K split across workgroups (``splitk``: the library's choice of splits).
+    "gemv_1x512x14336": dict(kind="gemv", M=1, N=512, K=14336, w_seed=502, a_seed=503),
+    "gemv_splitk_1x512x14336": dict(kind="gemv", splitk=True, M=1, N=512, K=14336, w_seed=502,
+                                    a_seed=503),
     # The decode GEMVs and prefill GEMMs with bfloat16 activations (``act="bf16"``).
     "gemv_bf16_1x4096x4096": dict(kind="gemv", act="bf16", M=1, N=4096, K=4096, w_seed=200,
                                   a_seed=201),

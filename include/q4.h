@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 4
+#define Q4_ABI_VERSION 5
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -154,6 +154,45 @@ int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
  * the same function of (M, N, K) as q4_gemm_workspace_bytes.
  */
 size_t q8_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * q4_gemv_splitk — q4_gemv with K split across workgroups, for decode shapes
+ * with few output columns per compute unit (for example one GPU's share of a
+ * weight split by rows) and long rows. Splitting the reduction over K is the
+ * direction of virtio-accel ADR 10 ("Vulkan kernel throughput ...", section
+ * Consequences) for a GEMV whose flat geometry stalls.
+ *   a, w_q, w_bytes, y, M, N, K: as q4_gemv (1 <= M <= 8).
+ *   splits    0 lets the library choose: no split when the plain GEMV
+ *             walks fewer than 3 chunks of K per wavefront (K < 12288 or so),
+ *             else enough workgroups for 256 compute units, ceil(256 /
+ *             ceil(N / 16)), at most one per 64 blocks of K. A positive value
+ *             asks for that many. Either is capped at one
+ *             split per 8 blocks of K, and rounded so every split holds a
+ *             multiple of 8 blocks (the last one the rest). Negative:
+ *             Q4_ERR_SHAPE.
+ *   workspace, workspace_bytes: at least q4_gemv_splitk_workspace_bytes(M,
+ *             N, K, splits) bytes of device scratch (the splits' partial
+ *             outputs), as for q4_gemm; 0 bytes (NULL allowed) when the call
+ *             does not split: one split, or K % 256 != 0 (then it is q4_gemv).
+ * Each split writes its partial y; a second kernel adds the partials in split
+ * order, so repeated calls return identical bits. Accuracy: as q4_gemv.
+ */
+int q4_gemv_splitk(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N,
+                   int K, int splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * q4_gemv_splitk_workspace_bytes — splits * M * N * 4 for the split the call
+ * would use, 0 when it does not split or the shape is invalid or empty,
+ * SIZE_MAX on overflow. Pure function of its arguments.
+ */
+size_t q4_gemv_splitk_workspace_bytes(int M, int N, int K, int splits);
+
+/* q8_gemv_splitk — q4_gemv_splitk over a Q8_0 weight stream (w_bytes == N * (K/32) * 34). */
+int q8_gemv_splitk(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N,
+                   int K, int splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* q8_gemv_splitk_workspace_bytes — as q4_gemv_splitk_workspace_bytes, for q8_gemv_splitk. */
+size_t q8_gemv_splitk_workspace_bytes(int M, int N, int K, int splits);
 
 /*
  * q4_gemv_bf16 — q4_gemv with bfloat16 activations: y = a @ dequant(W)^T for

@@ -263,6 +263,46 @@ def test_gemm_workspace_checks(g, K):
     assert binding.raw_status(g, None, None, wbn, None, 0, N, K, None, 0, 0) == S.Q4_OK
 
 
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemv_splitk_workspace_bytes(f):
+    ws = getattr(binding, f + "_gemv_splitk_workspace_bytes")
+    # Auto: no split below 3 chunks per wavefront, else ceil(256 / (N/16)) splits,
+    # at most K/32/64; each split a multiple of 8 blocks.
+    assert ws(1, 512, 14336, 0) == 7 * 512 * 4          # 448 blocks (7 chunks): 8 wanted, 7 allowed
+    assert ws(1, 512, 4096, 0) == 0                     # one 16-block chunk per wavefront
+    assert ws(8, 1024, 8192, 0) == 0                    # two chunks per wavefront
+    assert ws(1, 4096, 14336, 0) == 0                   # 256 column groups: no split
+    assert ws(1, 64, 32768, 0) == 16 * 64 * 4           # 8 chunks, 4 groups: 64 wanted, 16 allowed
+    assert ws(2, 1024, 32768, 0) == 4 * 2 * 1024 * 4    # 64 groups -> 4 splits
+    # Requested splits, capped at one per 8 blocks and rounded to 8-block splits.
+    assert ws(2, 300, 4096, 3) == 3 * 2 * 300 * 4       # 128 blocks -> 48, 48, 32
+    assert ws(1, 64, 4096, 5) == 4 * 64 * 4             # ks = 26 rounded up to 32: 4 splits
+    assert ws(1, 64, 256, 9) == 0                       # 8 blocks: one split at most
+    assert ws(1, 64, 4096, 1) == 0
+    # Off the streaming kernel (K % 256 != 0), invalid or empty: no workspace.
+    for M, N, K, s in [(1, 64, 4128, 4), (0, 64, 4096, 2), (9, 64, 4096, 2), (1, 0, 4096, 2),
+                       (1, 64, 4096, -1), (1, 64, 48, 2)]:
+        assert ws(M, N, K, s) == 0, (M, N, K, s)
+
+
+@fake_addresses
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemv_splitk_checks(f):
+    S = binding
+    wbn = _wb(64, 4096, f)
+    st = lambda a, y, M, N, K, s, ws, wsb: binding.raw_status(f + "_gemv_splitk", a, W, wbn if N == 64 else _wb(N, K, f), y, M, N, K, s, ws, wsb, 0)
+    need = getattr(binding, f + "_gemv_splitk_workspace_bytes")(1, 64, 4096, 4)
+    assert need == 4 * 64 * 4
+    WS = BASE + (3 << 32)
+    assert st(A, Y, 9, 64, 4096, 4, WS, need) == S.Q4_ERR_SHAPE        # M > 8
+    assert st(A, Y, 1, 64, 4096, -1, WS, need) == S.Q4_ERR_SHAPE       # negative splits
+    assert st(A, Y, 1, 64, 4096, 4, WS, need - 4) == S.Q4_ERR_WORKSPACE
+    assert st(A, Y, 1, 64, 4096, 4, None, need) == S.Q4_ERR_NULL
+    assert st(A, Y, 1, 64, 4096, 4, WS + 4, need) == S.Q4_ERR_ALIGN
+    assert st(A, Y, 1, 64, 4096, 4, Y, need) == S.Q4_ERR_ALIAS
+    assert st(None, None, 0, 64, 4096, 4, None, 0) == S.Q4_OK          # empty
+
+
 @fake_addresses
 def test_binding_raises_q4error():
     with pytest.raises(binding.Q4Error) as e:

@@ -172,7 +172,13 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0):
     per = (((ks + 7) // 8) + 7) & ~7
     last, tail = ks - (ks - 1) // per * per, kl - (kl - 1) // per * per
     ch = 16 if (per % 16 == 0 and last % 16 == 0 and tail % 16 == 0) else 8
-    return "k_gemv_stream<%s, %d, 8, %d, %s>" % (FMT_TYPE[fmt], M, ch, bf)
+    # A operands from LDS: more workgroups than compute units, or several chunks
+    # per wavefront, where one pass holds the chunk's A operands.
+    ni = M if act == "bf16" else 2 * M
+    splits = -(-nblk // ks)
+    al = ((N + 15) // 16 * splits > 256 or per > ch) and not (ch == 16 and ni > 8)
+    return "k_gemv_stream<%s, %d, 8, %d, %s, %s>" % (FMT_TYPE[fmt], M, ch, bf,
+                                                     "true" if al else "false")
 
 
 def gemm_kernel_name(K, fmt="q4_0", act="f32"):

@@ -360,7 +360,12 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl<B0>(f, std::make_integer_sequence<int, B1 - B0>{});
 }
 
-template <class F, int M, int NW, int CH, bool BF>
+// AL: the MFMAs read the chunk's A operands from LDS block by block instead of
+// holding all of them in registers (only where one pass holds the chunk's A
+// operands, AH == 1). That frees CH * 4 VGPRs, so two workgroups share a
+// compute unit and one's loads overlap the other's work: taken when there are
+// more workgroups than compute units or more than one chunk per wavefront.
+template <class F, int M, int NW, int CH, bool BF, bool AL>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
@@ -368,6 +373,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
 {
     using C = GemvStreamCfg<F, M, NW, CH, BF>;
     using R = GemvRows<BF, M>;
+    static_assert(!AL || C::AH == 1, "A operands read from LDS need the whole chunk's in one pass");
     constexpr int NACC = R::NACC;
     constexpr uint32_t ES = BF ? 2 : 4;           // bytes per activation
     constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         // flight. Only lanes j < NI read: the other A rows belong to no
         // activation row and only fill MFMA output rows that are never read.
         wave_lds_sync();
-        if (j < C::NI) {
+        if (!AL && j < C::NI) {
 #pragma unroll
             for (int b = h * C::CHH; b < (h + 1) * C::CHH; ++b)
                 aop[b] = *reinterpret_cast<const f16x8 *>(a_lane + (b - h * C::CHH) * ASTRIDE);
@@ -596,7 +602,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 uint32_t x[F::kQsDwords];
                 read_qs<F, b>(wrow32, g, x);
                 d[b - B0] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * F::kBytes));
-                Cv[b - B0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[b], F::decode(x, magic_v),
+                f16x8 av;
+                if constexpr (AL)
+                    av = *reinterpret_cast<const f16x8 *>(a_lane + b * ASTRIDE);
+                else
+                    av = aop[b];
+                Cv[b - B0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, F::decode(x, magic_v),
                                                                      zero4, 0, 0, 0);
             });
 #pragma unroll
@@ -710,14 +721,23 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
         const int ks = splits > 1 ? sp.ks : nblk, kl = nblk - (splits - 1) * ks;
         const int per = (((ks + NW - 1) / NW) + 7) & ~7;
         const dim3 g2(grid, (unsigned)splits);
-        hipError_t e;
-        if (stream_chunk(per, ks, kl) == 16)
-            e = launch_kernel(k_gemv_stream<F, M, NW, 16, BF>, g2, dim3(64 * NW), 0, s, a, w,
-                              y, N, K, per, ks);
-        else
-            e = launch_kernel(k_gemv_stream<F, M, NW, 8, BF>, g2, dim3(64 * NW), 0, s, a, w, y,
-                              N, K, per, ks);
-        return e;
+        const int ch = stream_chunk(per, ks, kl);
+        // A operands from LDS when a compute unit gets more than one workgroup
+        // or a wavefront more than one chunk (and one pass holds them).
+        const bool al = (long long)grid * splits > 256 || per > ch;
+        if (ch == 16) {
+            if constexpr (GemvStreamCfg<F, M, NW, 16, BF>::AH == 1)
+                if (al)
+                    return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, true>, g2, dim3(64 * NW),
+                                         0, s, a, w, y, N, K, per, ks);
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, false>, g2, dim3(64 * NW), 0, s,
+                                 a, w, y, N, K, per, ks);
+        }
+        if (al)
+            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, true>, g2, dim3(64 * NW), 0, s, a,
+                                 w, y, N, K, per, ks);
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, false>, g2, dim3(64 * NW), 0, s, a, w,
+                             y, N, K, per, ks);
     }
     return launch_kernel(k_gemv<F, M, BF>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
 }

@@ -74,8 +74,11 @@ def test_gemm_workloads_sampled(fmt, name):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(17, 32), (300, 256), (129, 1056), (64, 4096), (33, 8192)])
+@pytest.mark.parametrize("N,K", [(17, 32), (300, 256), (129, 1056), (64, 4096), (33, 8192),
+                                 (4200, 4096), (5000, 2048)])
 def test_gemv_shapes(fmt, M, N, K):
+    # N > 4096 gives more workgroups than compute units and K = 8192 several
+    # chunks per wavefront: the streaming kernel then reads A from LDS.
     blob = weight_blob(fmt, N, K, 10 * M + K)
     a = wl.activations_f32(20 * M + N, M, K)
     _full_check(fmt, "gemv", a, blob, N, K, "gemv %dx%dx%d" % (M, N, K))

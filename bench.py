@@ -154,29 +154,25 @@ def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
 
 
 def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0):
+    """The kernel the library launches (mirrors launch_gemv_m and gemv_split_plan)."""
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
     ks = kl = nblk
-    if splitk:   # the library's automatic split (q4v::gemv_split_plan)
+    if splitk:   # the library's automatic split
         groups = (N + 15) // 16
         want = min(-(-256 // groups), nblk // 64, nblk // 8)
-        p0 = (((nblk + 7) // 8) + 7) & ~7
-        l0 = nblk - (nblk - 1) // p0 * p0
-        if p0 // (16 if (p0 % 16 == 0 and l0 % 16 == 0) else 8) < 3:
+        ch0 = 16 if nblk % 16 == 0 else 8
+        if -(-(nblk // ch0) // 8) < 3:
             want = 1
         if want > 1:
             ks = (-(-nblk // want) + 7) & ~7
             kl = nblk - (-(-nblk // ks) - 1) * ks
-    per = (((ks + 7) // 8) + 7) & ~7
-    last, tail = ks - (ks - 1) // per * per, kl - (kl - 1) // per * per
-    ch = 16 if (per % 16 == 0 and last % 16 == 0 and tail % 16 == 0) else 8
-    # A operands from LDS: more workgroups than compute units, or several chunks
-    # per wavefront, where one pass holds the chunk's A operands.
+    ch = 16 if (ks % 16 == 0 and kl % 16 == 0) else 8
     ni = M if act == "bf16" else 2 * M
     splits = -(-nblk // ks)
-    al = ((N + 15) // 16 * splits > 256 or per > ch) and not (ch == 16 and ni > 8)
+    al = ((N + 15) // 16 * splits > 256 or ks > 8 * ch) and not (ch == 16 and ni > 8)
     return "k_gemv_stream<%s, %d, 8, %d, %s, %s>" % (FMT_TYPE[fmt], M, ch, bf,
                                                      "true" if al else "false")
 

@@ -369,7 +369,7 @@ template <class F, int M, int NW, int CH, bool BF, bool AL>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
-                                                        int per, int ks)
+                                                        int ks)
 {
     using C = GemvStreamCfg<F, M, NW, CH, BF>;
     using R = GemvRows<BF, M>;
@@ -392,11 +392,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
 
     // The workgroup's K split: blocks [kb_lo, kb_hi) (the whole row unless the
     // call splits K across workgroups, blockIdx.y being the split; each split
-    // then writes its own partial y, M x N f32, at y + split M N). This
-    // wavefront's blocks: [wb0, wb1), a whole number of CH-block chunks (the
-    // host picks ks, per and CH so that every chunk is full).
+    // then writes its own partial y, M x N f32, at y + split M N), a whole
+    // number of CH-block chunks (the host picks CH so). The chunks are dealt
+    // to the wavefronts in turn: wavefront w takes chunks w, w + NW, ... So
+    // the chunk size depends only on K, not on how K divides among the
+    // wavefronts, and long rows keep 16-block chunks (more bytes in flight).
     const int kb_lo = (int)blockIdx.y * ks, kb_hi = min(kb_lo + ks, nblk);
-    const int wb0 = min(kb_lo + wave * per, kb_hi), wb1 = min(wb0 + per, kb_hi);
+    const int wb0 = kb_lo + wave * C::CH;       // this wavefront's first chunk
+    constexpr int kStride = NW * C::CH;         // ... and the step to its next
     y += (size_t)blockIdx.y * (size_t)M * (size_t)N;
 
     // Loader role: row lr = lane % 16, 16-byte columns lc0 + 4 i.
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     split_activations();
-    for (int cb0 = wb0; cb0 < wb1; cb0 += C::CH) {
+    for (int cb0 = wb0; cb0 < kb_hi; cb0 += kStride) {
         // The chunk is contracted in NPART parts. Part p needs only loads
         // [0, loads_for(end of p)) of every lane, which drain first (vmcnt
         // counts in issue order), so its decode and MFMAs run while the rest of
@@ -646,12 +649,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
             };
             if constexpr (P < C::NPART - 1) {
                 run_part();
-            } else if (cb0 + C::CH < wb1) {
+            } else if (cb0 + kStride < kb_hi) {
                 // Every load of this chunk is staged: prefetch the next chunk,
                 // finish this one, then split the next chunk's activations. The
                 // fetch and the split sit in one branch, so the loaded
                 // activation registers never meet a join.
-                fetch(cb0 + C::CH);
+                fetch(cb0 + kStride);
                 run_part();
                 finish_chunk();
                 wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
@@ -695,13 +698,6 @@ __global__ __launch_bounds__(256) void k_gemv_split_sum(const float *__restrict_
     y[i] = acc;
 }
 
-// Chunk size for a wavefront share of `per` blocks over splits of ks blocks
-// (the last one kl): 16 when every busy wavefront's share divides by 16.
-static int stream_chunk(int per, int ks, int kl)
-{
-    const int last_full = ks - (ks - 1) / per * per, last_tail = kl - (kl - 1) / per * per;
-    return (per % 16 == 0 && last_full % 16 == 0 && last_tail % 16 == 0) ? 16 : 8;
-}
 
 template <class F, int M, bool BF>
 static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N, int K,
@@ -710,34 +706,32 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
     const unsigned grid = (unsigned)((N + 15) / 16);
     // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0 and
     // a row is a whole number of 16-byte columns in either format) and 32-bit
-    // byte offsets. Each wavefront gets `per` blocks (a multiple of 8); chunks
-    // of 16 blocks when every wavefront's share divides by 16 (one memory round
-    // trip for the whole share at K = 4096), else 8.
+    // byte offsets. Chunks of 16 blocks when every split's length divides by
+    // 16 (at K = 4096, one chunk and one memory round trip per wavefront), else 8.
     constexpr int NW = kGemvStreamWaves;
     const int nblk = K / 32;
     if (q4v::gemv_streams(M, N, K, F::kBytes, BF ? 2 : 4)) {
         // K split across sp.splits workgroups of ks blocks each (one split: ks = K/32).
         const int splits = sp.splits > 1 ? sp.splits : 1;
         const int ks = splits > 1 ? sp.ks : nblk, kl = nblk - (splits - 1) * ks;
-        const int per = (((ks + NW - 1) / NW) + 7) & ~7;
         const dim3 g2(grid, (unsigned)splits);
-        const int ch = stream_chunk(per, ks, kl);
+        const int ch = q4v::gemv_chunk_blocks(ks, kl);
         // A operands from LDS when a compute unit gets more than one workgroup
         // or a wavefront more than one chunk (and one pass holds them).
-        const bool al = (long long)grid * splits > 256 || per > ch;
+        const bool al = (long long)grid * splits > 256 || ks > NW * ch;
         if (ch == 16) {
             if constexpr (GemvStreamCfg<F, M, NW, 16, BF>::AH == 1)
                 if (al)
                     return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, true>, g2, dim3(64 * NW),
-                                         0, s, a, w, y, N, K, per, ks);
+                                         0, s, a, w, y, N, K, ks);
             return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, false>, g2, dim3(64 * NW), 0, s,
-                                 a, w, y, N, K, per, ks);
+                                 a, w, y, N, K, ks);
         }
         if (al)
             return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, true>, g2, dim3(64 * NW), 0, s, a,
-                                 w, y, N, K, per, ks);
+                                 w, y, N, K, ks);
         return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, false>, g2, dim3(64 * NW), 0, s, a, w,
-                             y, N, K, per, ks);
+                             y, N, K, ks);
     }
     return launch_kernel(k_gemv<F, M, BF>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
 }

@@ -58,13 +58,17 @@ struct GemvSplit {
     int ks;
 };
 
-// Chunks of the streaming GEMV each wavefront walks in turn when K is not
-// split: its share of K/32 blocks (a multiple of 8) over chunks of 16 blocks
-// when every share divides by 16, else 8.
+// Blocks per chunk of the streaming GEMV for splits of ks blocks (the last one
+// kl): 16 when both divide by 16, else 8 (K % 256 == 0 makes every split a
+// multiple of 8).
+inline int gemv_chunk_blocks(int ks, int kl) { return (ks % 16 == 0 && kl % 16 == 0) ? 16 : 8; }
+
+// Chunks the busiest wavefront of the streaming GEMV walks in turn when K is
+// not split (the chunks of a row are dealt to its 8 wavefronts in turn).
 inline int gemv_chunks_per_wave(int nblk)
 {
-    const int per = ((nblk + 7) / 8 + 7) & ~7, last = nblk - (nblk - 1) / per * per;
-    return per / ((per % 16 == 0 && last % 16 == 0) ? 16 : 8);
+    const int chunks = nblk / gemv_chunk_blocks(nblk, nblk);
+    return (chunks + 7) / 8;
 }
 
 // The split a q4_gemv_splitk / q8_gemv_splitk call uses: `requested` splits,

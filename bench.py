@@ -153,12 +153,15 @@ def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
     return blob
 
 
-def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0):
+def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=False):
     """The kernel the library launches (mirrors launch_gemv_m and gemv_split_plan)."""
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
+    if prepared:
+        return "k_gemv_stream<%s, %d, 8, %d, false, 2>" % (FMT_TYPE[fmt], M,
+                                                           16 if nblk % 16 == 0 else 8)
     ks = kl = nblk
     if splitk:   # the library's automatic split
         groups = (N + 15) // 16
@@ -173,8 +176,7 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0):
     ni = M if act == "bf16" else 2 * M
     splits = -(-nblk // ks)
     al = ((N + 15) // 16 * splits > 256 or ks > 8 * ch) and not (ch == 16 and ni > 8)
-    return "k_gemv_stream<%s, %d, 8, %d, %s, %s>" % (FMT_TYPE[fmt], M, ch, bf,
-                                                     "true" if al else "false")
+    return "k_gemv_stream<%s, %d, 8, %d, %s, %d>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0)
 
 
 def gemm_kernel_name(K, fmt="q4_0", act="f32"):
@@ -198,7 +200,16 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
-    if s["kind"] == "gemv" and s.get("splitk"):
+    prep_us = None
+    if s["kind"] == "gemv" and s.get("prepared"):
+        prep = torch.empty(getattr(q4, f + "_gemv_prepare_bytes")(M, K), dtype=torch.uint8,
+                           device="cuda")
+        prepare = getattr(q4, f + "_gemv_prepare")
+        prepare(a, M, K, prep)
+        gemv = getattr(q4, f + "_gemv_prepared")
+        fn = lambda k: gemv(prep, blobs[k % R], y, M, N, K)
+        prep_us = run_timed(torch, lambda k: prepare(a, M, K, prep), min(steps, 50), 5)["kernel_us"]
+    elif s["kind"] == "gemv" and s.get("splitk"):
         gemv = getattr(q4, f + "_gemv_splitk")
         ws_bytes = getattr(q4, f + "_gemv_splitk_workspace_bytes")(M, N, K, 0)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
@@ -223,8 +234,13 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
            "kernel_GBs": algo_bytes / kern_s / 1e9, "kernel_TFLOPs": flops / kern_s / 1e12,
            "job_GBs": algo_bytes * steps / t["wall_s"] / 1e9,
            "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
+    if prep_us is not None:
+        row["prepare_us"] = prep_us
+        row["note"] = ("kernel_us is the GEMV from prepared operands alone; preparing them "
+                       "(one more launch, shared by every weight matrix that multiplies the "
+                       "same activations) takes prepare_us")
     if s["kind"] == "gemv":
-        kernel = gemv_kernel_name(M, K, fmt, act, s.get("splitk", False), N)
+        kernel = gemv_kernel_name(M, K, fmt, act, s.get("splitk", False), N, s.get("prepared"))
         row["roofline"] = hbm_roofline(algo_bytes, t["kernel_us"], name, kernel, "gemv")
         if s.get("splitk"):
             row["roofline"]["note"] = ("the time is the whole call: the split GEMV kernel plus "
@@ -410,7 +426,9 @@ def main():
             log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
-        for name, st in (("gemv_1x512x4096", args.steps), ("gemm_2048x1792x4096", 50),
+        for name, st in (("gemv_prepared_1x4096x4096", args.steps),
+                         ("gemv_prepared_8x4096x4096", args.steps),
+                         ("gemv_1x512x4096", args.steps), ("gemm_2048x1792x4096", 50),
                          ("gemv_1x512x14336", args.steps), ("gemv_splitk_1x512x14336", args.steps)):
             log("row: %s (one GPU's share of an 8-way row split)" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),

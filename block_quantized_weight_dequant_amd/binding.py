@@ -34,7 +34,9 @@ EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_ge
            "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize", "q4_gemm_bf16",
            "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes",
            "q4_gemv_bf16", "q8_gemv_bf16", "q4_gemv_splitk", "q4_gemv_splitk_workspace_bytes",
-           "q8_gemv_splitk", "q8_gemv_splitk_workspace_bytes")
+           "q8_gemv_splitk", "q8_gemv_splitk_workspace_bytes", "q4_gemv_prepare_bytes",
+           "q4_gemv_prepare", "q4_gemv_prepared", "q8_gemv_prepare_bytes", "q8_gemv_prepare",
+           "q8_gemv_prepared")
 
 
 class Q4Error(RuntimeError):
@@ -74,6 +76,12 @@ def _load_library():
         getattr(lib, f + "_gemv_splitk").argtypes = [P, P, sz, P, i32, i32, i32, i32, P, sz, P]
         getattr(lib, f + "_gemv_splitk_workspace_bytes").restype = sz
         getattr(lib, f + "_gemv_splitk_workspace_bytes").argtypes = [i32, i32, i32, i32]
+        getattr(lib, f + "_gemv_prepare_bytes").restype = sz
+        getattr(lib, f + "_gemv_prepare_bytes").argtypes = [i32, i32]
+        getattr(lib, f + "_gemv_prepare").restype = i32
+        getattr(lib, f + "_gemv_prepare").argtypes = [P, i32, i32, P, sz, P]
+        getattr(lib, f + "_gemv_prepared").restype = i32
+        getattr(lib, f + "_gemv_prepared").argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -159,6 +167,48 @@ def q4_gemv_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -
 def q8_gemv_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
     """As q8_gemv with ``a`` a [M, K] bfloat16 tensor (or its address)."""
     _gemv("q8_gemv_bf16", a, w_q, y, M, N, K, w_bytes, stream)
+
+
+def q4_gemv_prepare_bytes(M: int, K: int) -> int:
+    return int(lib.q4_gemv_prepare_bytes(int(M), int(K)))
+
+
+def q8_gemv_prepare_bytes(M: int, K: int) -> int:
+    return int(lib.q8_gemv_prepare_bytes(int(M), int(K)))
+
+
+def _gemv_prepare(entry, a, M, K, prep, prep_bytes, stream) -> None:
+    pb = _nbytes(prep) if prep_bytes is None else int(prep_bytes)
+    _check(getattr(lib, entry)(_addr(a), int(M), int(K), _addr(prep), pb, _stream(stream)), entry)
+
+
+def q4_gemv_prepare(a, M: int, K: int, prep, prep_bytes=None, stream=None) -> None:
+    """Prepared operands of the f32 activations ``a`` [M, K] for q4_gemv_prepared."""
+    _gemv_prepare("q4_gemv_prepare", a, M, K, prep, prep_bytes, stream)
+
+
+def q8_gemv_prepare(a, M: int, K: int, prep, prep_bytes=None, stream=None) -> None:
+    """As q4_gemv_prepare, for q8_gemv_prepared."""
+    _gemv_prepare("q8_gemv_prepare", a, M, K, prep, prep_bytes, stream)
+
+
+def _gemv_prepared(entry, prep, w_q, y, M, N, K, prep_bytes, w_bytes, stream) -> None:
+    pb = _nbytes(prep) if prep_bytes is None else int(prep_bytes)
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    _check(getattr(lib, entry)(_addr(prep), pb, _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                               _stream(stream)), entry)
+
+
+def q4_gemv_prepared(prep, w_q, y, M: int, N: int, K: int, prep_bytes=None, w_bytes=None,
+                     stream=None) -> None:
+    """y[M, N] = a @ dequant(W)^T from operands made by q4_gemv_prepare."""
+    _gemv_prepared("q4_gemv_prepared", prep, w_q, y, M, N, K, prep_bytes, w_bytes, stream)
+
+
+def q8_gemv_prepared(prep, w_q, y, M: int, N: int, K: int, prep_bytes=None, w_bytes=None,
+                     stream=None) -> None:
+    """As q4_gemv_prepared over a Q8_0 weight stream."""
+    _gemv_prepared("q8_gemv_prepared", prep, w_q, y, M, N, K, prep_bytes, w_bytes, stream)
 
 
 def q4_gemv_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:

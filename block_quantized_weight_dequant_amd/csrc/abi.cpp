@@ -97,6 +97,29 @@ static int gemv_splitk(q4k::WeightFormat fmt, size_t block_bytes, const float *a
                                             workspace, as_stream(stream)));
 }
 
+static int gemv_prepare(q4k::WeightFormat fmt, const float *a, int M, int K, void *prep,
+                        size_t prep_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_gemv_prepare(a, M, K, prep, prep_bytes, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemv_prepare(fmt, a, prep, M, K, as_stream(stream)));
+}
+
+static int gemv_prepared(q4k::WeightFormat fmt, size_t block_bytes, const void *prep,
+                         size_t prep_bytes, const void *w_q, size_t w_bytes, float *y, int M,
+                         int N, int K, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_gemv_prepared(prep, prep_bytes, w_q, w_bytes, y, M, N, K, block_bytes,
+                                      &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemv_prepared(fmt, prep, static_cast<const uint8_t *>(w_q), y, M,
+                                              N, K, as_stream(stream)));
+}
+
 static int gemv_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *a,
                      const void *w_q, size_t w_bytes, float *y, int M, int N, int K, void *stream)
 {
@@ -181,6 +204,36 @@ Q4_EXPORT int q8_gemv_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, f
                            int N, int K, void *stream)
 {
     return gemv_bf16(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT size_t q4_gemv_prepare_bytes(int M, int K) { return q4v::gemv_prepare_bytes(M, K); }
+
+Q4_EXPORT size_t q8_gemv_prepare_bytes(int M, int K) { return q4v::gemv_prepare_bytes(M, K); }
+
+Q4_EXPORT int q4_gemv_prepare(const float *a, int M, int K, void *prep, size_t prep_bytes,
+                              void *stream)
+{
+    return gemv_prepare(q4k::WeightFormat::kQ4_0, a, M, K, prep, prep_bytes, stream);
+}
+
+Q4_EXPORT int q8_gemv_prepare(const float *a, int M, int K, void *prep, size_t prep_bytes,
+                              void *stream)
+{
+    return gemv_prepare(q4k::WeightFormat::kQ8_0, a, M, K, prep, prep_bytes, stream);
+}
+
+Q4_EXPORT int q4_gemv_prepared(const void *prep, size_t prep_bytes, const void *w_q,
+                               size_t w_bytes, float *y, int M, int N, int K, void *stream)
+{
+    return gemv_prepared(q4k::WeightFormat::kQ4_0, 18, prep, prep_bytes, w_q, w_bytes, y, M, N, K,
+                         stream);
+}
+
+Q4_EXPORT int q8_gemv_prepared(const void *prep, size_t prep_bytes, const void *w_q,
+                               size_t w_bytes, float *y, int M, int N, int K, void *stream)
+{
+    return gemv_prepared(q4k::WeightFormat::kQ8_0, 34, prep, prep_bytes, w_q, w_bytes, y, M, N, K,
+                         stream);
 }
 
 Q4_EXPORT size_t q4_gemv_splitk_workspace_bytes(int M, int N, int K, int splits)

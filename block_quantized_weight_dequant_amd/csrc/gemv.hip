@@ -360,12 +360,16 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl<B0>(f, std::make_integer_sequence<int, B1 - B0>{});
 }
 
-// AL: the MFMAs read the chunk's A operands from LDS block by block instead of
-// holding all of them in registers (only where one pass holds the chunk's A
-// operands, AH == 1). That frees CH * 4 VGPRs, so two workgroups share a
-// compute unit and one's loads overlap the other's work: taken when there are
-// more workgroups than compute units or more than one chunk per wavefront.
-template <class F, int M, int NW, int CH, bool BF, bool AL>
+// MODE 0: as above. MODE 1 (AL): the MFMAs read the chunk's A operands from
+// LDS block by block instead of holding all of them in registers (only where
+// one pass holds the chunk's A operands, AH == 1). That frees CH * 4 VGPRs, so
+// two workgroups share a compute unit and one's loads overlap the other's
+// work: taken when there are more workgroups than compute units or more than
+// one chunk per wavefront. MODE 2 (PA, f32 activations): `a` holds operands
+// prepared once by k_gemv_prep_ops (the two-term A operands of every block in
+// [block][lane group][A row] order, then the per-row exponents), loaded
+// straight into the A registers: no per-chunk split, scale or LDS pass.
+template <class F, int M, int NW, int CH, bool BF, int MODE>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
@@ -373,13 +377,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
 {
     using C = GemvStreamCfg<F, M, NW, CH, BF>;
     using R = GemvRows<BF, M>;
+    constexpr bool AL = MODE == 1, PA = MODE == 2;
     static_assert(!AL || C::AH == 1, "A operands read from LDS need the whole chunk's in one pass");
+    static_assert(!PA || !BF, "prepared operands are made from f32 activations");
     constexpr int NACC = R::NACC;
     constexpr uint32_t ES = BF ? 2 : 4;           // bytes per activation
     constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
 
     // Per wavefront: [staged weight bytes | A operands].
-    __shared__ __attribute__((aligned(16))) uint8_t s_mem[NW * C::LDS_PER_WAVE];
+    // PA needs no A area: its operands go straight to registers.
+    constexpr int kLdsPerWave = PA ? C::WBYTES : C::LDS_PER_WAVE;
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[NW * kLdsPerWave];
     __shared__ float s_part[NW][M][16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     const int n0 = blockIdx.x * 16;
     const int nblk = K >> 5;
     const uint32_t row_bytes = (uint32_t)nblk * F::kBytes;
-    uint8_t *s_w = s_mem + wave * C::LDS_PER_WAVE;
+    uint8_t *s_w = s_mem + wave * kLdsPerWave;
     uint8_t *s_a = s_w + C::WBYTES;
 
     // The workgroup's K split: blocks [kb_lo, kb_hi) (the whole row unless the
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // exact and the first half of a chunk waits only for its own loads.
     auto fetch = [&](int cb0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < C::EPL; ++r) {
+        for (int r = 0; r < (PA ? 0 : C::EPL); ++r) {
             const int e = min(lane + 64 * r, C::NENT - 1);
             const int m = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
             const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * ES;
@@ -453,10 +461,26 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // branch (they would wait for the loads). A wavefront without blocks
     // (possible only when the workgroup's share is short) fetches the last full
     // chunk of the row, K/32 >= CH, and never reads it.
-    fetch(min(wb0, nblk - C::CH));
-
-    // A operands of a chunk live in registers (set by split_activations).
+    // A operands of a chunk live in registers (set by split_activations, or
+    // for PA loaded by fetch_ops).
     f16x8 aop[C::CH];
+    // PA: the chunk's prepared operands, operand (b, g, i) of block cb0 + b at
+    // ((cb0 + b) * 4 + g) * NI + i. Only lanes j < NI load: the other A rows
+    // belong to no activation row and only fill MFMA rows that are never read.
+    const u32x4 *ops = static_cast<const u32x4 *>(a);
+    auto fetch_ops = [&](int cb0) __attribute__((always_inline)) {
+        if constexpr (PA) {
+            if (j < C::NI) {
+#pragma unroll
+                for (int b = 0; b < C::CH; ++b)
+                    aop[b] = bitcast<f16x8>(ops[((size_t)(cb0 + b) * 4 + g) * C::NI + j]);
+            }
+        }
+    };
+    // The first chunk: prepared operands first (their loads drain before the
+    // weights', so part 0 waits only for its own weight bytes), then weights.
+    fetch_ops(min(wb0, nblk - C::CH));
+    fetch(min(wb0, nblk - C::CH));
     // Clamped, so the address stays inside the A area even where the read is
     // masked off.
     const uint8_t *a_lane = s_a + (g * C::NI + min(j, C::NI - 1)) * 16;
@@ -475,7 +499,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // no copy of the loaded registers is kept alive while the weight loads are
     // being issued.
     int pexp[M];
+    if constexpr (PA) {
+        // The per-row exponents follow the operands.
+        const int *row_exp = reinterpret_cast<const int *>(ops + (size_t)nblk * 4 * C::NI);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            pexp[m] = row_exp[m];
+    }
     auto split_activations = [&]() __attribute__((always_inline)) {
+        if constexpr (PA)
+            return;
         float mx[M];
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -651,7 +684,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 run_part();
             } else if (cb0 + kStride < kb_hi) {
                 // Every load of this chunk is staged: prefetch the next chunk,
-                // finish this one, then split the next chunk's activations. The
+                // finish this one, then split the next chunk's activations (PA:
+                // load its prepared operands, once this chunk's are used). The
                 // fetch and the split sit in one branch, so the loaded
                 // activation registers never meet a join.
                 fetch(cb0 + kStride);
@@ -659,6 +693,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 finish_chunk();
                 wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
                 split_activations();
+                fetch_ops(cb0 + kStride);
             } else {
                 run_part();
                 finish_chunk();
@@ -722,15 +757,15 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
         if (ch == 16) {
             if constexpr (GemvStreamCfg<F, M, NW, 16, BF>::AH == 1)
                 if (al)
-                    return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, true>, g2, dim3(64 * NW),
+                    return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 1>, g2, dim3(64 * NW),
                                          0, s, a, w, y, N, K, ks);
-            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, false>, g2, dim3(64 * NW), 0, s,
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0>, g2, dim3(64 * NW), 0, s,
                                  a, w, y, N, K, ks);
         }
         if (al)
-            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, true>, g2, dim3(64 * NW), 0, s, a,
+            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 1>, g2, dim3(64 * NW), 0, s, a,
                                  w, y, N, K, ks);
-        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, false>, g2, dim3(64 * NW), 0, s, a, w,
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0>, g2, dim3(64 * NW), 0, s, a, w,
                              y, N, K, ks);
     }
     return launch_kernel(k_gemv<F, M, BF>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
@@ -767,6 +802,111 @@ hipError_t launch_gemv_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *
     if (fmt == WeightFormat::kQ8_0)
         return launch_gemv_f<FmtQ8_0, true>(a, w, y, M, N, K, s);
     return launch_gemv_f<FmtQ4_0, true>(a, w, y, M, N, K, s);
+}
+
+// ---------------------------------------------------------------------------
+// Prepared activations. k_gemv_prep_ops makes, once, the A operands the
+// streaming kernel would otherwise split in every workgroup: one workgroup per
+// activation row finds the row's largest magnitude, takes the power of two p
+// that puts the row's largest A value (2^kHiLog2 max |a| 2^p) in [2^14, 2^15)
+// (row_scale_exp, as for a chunk), and writes for every block and lane group
+// the hi and lo binary16 operands of A rows 2m and 2m + 1 in the kernel's slot
+// order, then p. Operand (kb, g, i) sits at (kb * 4 + g) * 2M + i; the M
+// exponents follow the nblk * 4 * 2M operands. A whole row shares one scale
+// (the in-kernel split scales per chunk); elements far below the row maximum
+// keep 2^-25 2^-p absolutely, as in the GEMM.
+template <class F>
+__global__ __launch_bounds__(256) void k_gemv_prep_ops(const float *__restrict__ a,
+                                                      u32x4 *__restrict__ ops, int M, int K)
+{
+    __shared__ float s_mx[4];
+    const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const float *row = a + (size_t)m * K;
+    const float4 *row4 = reinterpret_cast<const float4 *>(row);
+    float mx = 0.0f;
+    for (int f = tid; f < K / 4; f += 256) {
+        const float4 v = row4[f];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    mx = wave_max_nonneg(mx);
+    if (lane == 0)
+        s_mx[tid >> 6] = mx;
+    __syncthreads();
+    const float am = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
+    const int p = row_scale_exp<F>(am);
+    const float sh = ldexpf(1.0f, p), sl = (float)(1 << F::kHiLog2) * sh;
+    const int nblk = K >> 5, NI = 2 * M;
+    for (int t = tid; t < nblk * 4; t += 256) {
+        const int kb = t >> 2, gg = t & 3;
+        const float *blk = row + (size_t)kb * 32;
+        const float4 L = *reinterpret_cast<const float4 *>(blk + F::a_lo(gg));
+        const float4 H = *reinterpret_cast<const float4 *>(blk + F::a_hi(gg));
+        const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
+                            H.x * sh, H.z * sh, H.y * sh, H.w * sh};
+        f16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f16 hh, ll;
+            split2(v[e], hh, ll);
+            hi[e] = hh;
+            lo[e] = ll;
+        }
+        u32x4 *dst = ops + ((size_t)kb * 4 + gg) * NI + 2 * m;
+        dst[0] = bitcast<u32x4>(hi);
+        dst[1] = bitcast<u32x4>(lo);
+    }
+    if (tid == 0)
+        reinterpret_cast<int *>(ops + (size_t)nblk * 4 * NI)[m] = p;
+}
+
+template <class F, int M>
+static hipError_t launch_gemv_prepared_m(const void *prep, const uint8_t *w, float *y, int N, int K,
+                                         hipStream_t s)
+{
+    constexpr int NW = kGemvStreamWaves;
+    const int nblk = K / 32;
+    const unsigned grid = (unsigned)((N + 15) / 16);
+    if (q4v::gemv_chunk_blocks(nblk, nblk) == 16)
+        return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2>, dim3(grid), dim3(64 * NW), 0,
+                             s, prep, w, y, N, K, nblk);
+    return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2>, dim3(grid), dim3(64 * NW), 0, s,
+                         prep, w, y, N, K, nblk);
+}
+
+template <class F>
+static hipError_t launch_gemv_prepared_f(const void *prep, const uint8_t *w, float *y, int M,
+                                         int N, int K, hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_gemv_prepared_m<F, 1>(prep, w, y, N, K, s);
+    case 2: return launch_gemv_prepared_m<F, 2>(prep, w, y, N, K, s);
+    case 3: return launch_gemv_prepared_m<F, 3>(prep, w, y, N, K, s);
+    case 4: return launch_gemv_prepared_m<F, 4>(prep, w, y, N, K, s);
+    case 5: return launch_gemv_prepared_m<F, 5>(prep, w, y, N, K, s);
+    case 6: return launch_gemv_prepared_m<F, 6>(prep, w, y, N, K, s);
+    case 7: return launch_gemv_prepared_m<F, 7>(prep, w, y, N, K, s);
+    case 8: return launch_gemv_prepared_m<F, 8>(prep, w, y, N, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_prepare(WeightFormat fmt, const float *a, void *prep, int M, int K,
+                               hipStream_t s)
+{
+    u32x4 *ops = static_cast<u32x4 *>(prep);
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_kernel(k_gemv_prep_ops<FmtQ8_0>, dim3((unsigned)M), dim3(256), 0, s, a, ops,
+                             M, K);
+    return launch_kernel(k_gemv_prep_ops<FmtQ4_0>, dim3((unsigned)M), dim3(256), 0, s, a, ops, M,
+                         K);
+}
+
+hipError_t launch_gemv_prepared(WeightFormat fmt, const void *prep, const uint8_t *w, float *y,
+                                int M, int N, int K, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemv_prepared_f<FmtQ8_0>(prep, w, y, M, N, K, s);
+    return launch_gemv_prepared_f<FmtQ4_0>(prep, w, y, M, N, K, s);
 }
 
 template <class F>

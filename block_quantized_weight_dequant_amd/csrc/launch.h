@@ -20,6 +20,13 @@ hipError_t launch_gemv(WeightFormat fmt, const float *a, const uint8_t *w, float
 // a: [M, K] bfloat16 bit patterns, 1 <= M <= 8.
 hipError_t launch_gemv_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
                             int N, int K, hipStream_t s);
+// Prepared activations for the GEMV: launch_gemv_prepare writes
+// q4v::gemv_prepare_bytes(M, K) bytes of operands for the format; the
+// prepared GEMV reads them instead of `a` (K % 256 == 0 only).
+hipError_t launch_gemv_prepare(WeightFormat fmt, const float *a, void *prep, int M, int K,
+                               hipStream_t s);
+hipError_t launch_gemv_prepared(WeightFormat fmt, const void *prep, const uint8_t *w, float *y,
+                                int M, int N, int K, hipStream_t s);
 // K split across workgroups: partials of sp.splits splits into `workspace`
 // (sp.splits * M * N f32), then summed into y in split order. sp.splits <= 1
 // runs launch_gemv's kernel (workspace unused).

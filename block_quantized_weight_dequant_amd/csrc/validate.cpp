@@ -107,6 +107,57 @@ size_t gemm_workspace_bytes(int M, int N, int K)
     return n;
 }
 
+int check_gemv_prepare(const float *a, int M, int K, const void *prep, size_t prep_bytes,
+                       bool *empty)
+{
+    *empty = false;
+    if (M < 0 || M > Q4_GEMV_MAX_ROWS || K < 256 || K % 256 != 0)
+        return Q4_ERR_SHAPE;
+    if (M == 0) {
+        *empty = true;
+        return Q4_OK;
+    }
+    const size_t need = gemv_prepare_bytes(M, K);
+    if (prep_bytes < need)
+        return Q4_ERR_SIZE;
+    if (!a || !prep)
+        return Q4_ERR_NULL;
+    if (!aligned16(a) || !aligned16(prep))
+        return Q4_ERR_ALIGN;
+    if (overlaps({prep, need}, {a, (size_t)M * (size_t)K * sizeof(float)}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
+int check_gemv_prepared(const void *prep, size_t prep_bytes, const void *w, size_t w_bytes,
+                        const float *y, int M, int N, int K, size_t block_bytes, bool *empty)
+{
+    *empty = false;
+    if (M < 0 || M > Q4_GEMV_MAX_ROWS || N < 0 || K < 256 || K % 256 != 0)
+        return Q4_ERR_SHAPE;
+    size_t w_want = 0, y_bytes = 0;
+    if (!mul_ok((size_t)N, (size_t)(K / 32) * block_bytes, &w_want) || w_bytes != w_want)
+        return Q4_ERR_SIZE;
+    if (!mul_ok((size_t)M, (size_t)N, &y_bytes) || !mul_ok(y_bytes, sizeof(float), &y_bytes))
+        return Q4_ERR_SIZE;
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return Q4_OK;
+    }
+    if (!gemv_streams(M, N, K, block_bytes, 4))
+        return Q4_ERR_SHAPE;   // weight offsets beyond 31 bits
+    const size_t need = gemv_prepare_bytes(M, K);
+    if (prep_bytes < need)
+        return Q4_ERR_SIZE;
+    if (!prep || !w || !y)
+        return Q4_ERR_NULL;
+    if (!aligned16(prep) || !aligned16(w) || !aligned16(y))
+        return Q4_ERR_ALIGN;
+    if (overlaps({y, y_bytes}, {prep, need}) || overlaps({y, y_bytes}, {w, w_bytes}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
 size_t gemv_splitk_workspace_bytes(int M, int N, int K, int requested, size_t block_bytes)
 {
     if (M <= 0 || M > Q4_GEMV_MAX_ROWS || N <= 0 || K < 32 || K % 32 != 0 || requested < 0)

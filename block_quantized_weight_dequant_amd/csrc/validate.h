@@ -97,6 +97,26 @@ inline GemvSplit gemv_split_plan(int M, int N, int K, int requested, size_t bloc
     return {(nblk + ks - 1) / ks, ks};
 }
 
+// Bytes of a GEMV's prepared activations (q4_gemv_prepare): the two-term A
+// operands of every block, K/32 * 4 * 2M * 16 bytes, then M int32 exponents
+// padded to 16 bytes. 0 for M outside [1, 8] or K not a positive multiple of
+// 256 (the prepared GEMV runs the streaming kernel only).
+inline size_t gemv_prepare_bytes(int M, int K)
+{
+    if (M < 1 || M > 8 || K <= 0 || K % 256 != 0)
+        return 0;
+    return (size_t)(K / 32) * 4 * 2 * (size_t)M * 16 + ((size_t)M * 4 + 15) / 16 * 16;
+}
+
+// Checks of q4_gemv_prepare (a [M, K] f32 -> prep) and of the prepared GEMV
+// (prep, W -> y): shape (1 <= M <= 8, K % 256 == 0, the streaming kernel's
+// offset limits), sizes (prep_bytes >= gemv_prepare_bytes), then NULL,
+// alignment and overlap, as check_product. M == 0 (or N == 0) is empty.
+int check_gemv_prepare(const float *a, int M, int K, const void *prep, size_t prep_bytes,
+                       bool *empty);
+int check_gemv_prepared(const void *prep, size_t prep_bytes, const void *w, size_t w_bytes,
+                        const float *y, int M, int N, int K, size_t block_bytes, bool *empty);
+
 // Workspace bytes of a K-split GEMV: splits * M * N f32 partials, or 0 when the
 // call does not split (then the workspace is not used).
 size_t gemv_splitk_workspace_bytes(int M, int N, int K, int requested, size_t block_bytes);

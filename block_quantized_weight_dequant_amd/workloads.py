@@ -48,6 +48,12 @@ WORKLOADS = {
     "gemv_1x512x14336": dict(kind="gemv", M=1, N=512, K=14336, w_seed=502, a_seed=503),
     "gemv_splitk_1x512x14336": dict(kind="gemv", splitk=True, M=1, N=512, K=14336, w_seed=502,
                                     a_seed=503),
+    # The decode GEMV from activations prepared once (``prepared``: the GEMV
+    # alone, as when several weight matrices share one prepared input).
+    "gemv_prepared_1x4096x4096": dict(kind="gemv", prepared=True, M=1, N=4096, K=4096,
+                                      w_seed=200, a_seed=201),
+    "gemv_prepared_8x4096x4096": dict(kind="gemv", prepared=True, M=8, N=4096, K=4096,
+                                      w_seed=200, a_seed=202),
     # The decode GEMVs and prefill GEMMs with bfloat16 activations (``act="bf16"``).
     "gemv_bf16_1x4096x4096": dict(kind="gemv", act="bf16", M=1, N=4096, K=4096, w_seed=200,
                                   a_seed=201),

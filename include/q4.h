@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 5
+#define Q4_ABI_VERSION 6
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -154,6 +154,42 @@ int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
  * the same function of (M, N, K) as q4_gemm_workspace_bytes.
  */
 size_t q8_gemm_workspace_bytes(int M, int N, int K);
+
+/*
+ * q4_gemv_prepare / q4_gemv_prepared — the decode GEMV in two steps, for
+ * activations that several weight matrices multiply (the projections that
+ * share one input) and for M > 1, where splitting the f32 activations into
+ * matrix-core operands in every workgroup is most of q4_gemv's time
+ * (section qmatvec_q4_0, widened to eight rows as q4_gemv).
+ *   q4_gemv_prepare(a, M, K, prep, prep_bytes, stream): a [M, K] f32,
+ *     1 <= M <= 8, K a positive multiple of 256 (else Q4_ERR_SHAPE); writes
+ *     q4_gemv_prepare_bytes(M, K) bytes of prepared operands to prep
+ *     (prep_bytes smaller: Q4_ERR_SIZE). Each row is scaled by the power of
+ *     two that puts its largest magnitude (times 16, the Q4_0 decode's factor)
+ *     in [2^14, 2^15), then split into two binary16 terms per element in
+ *     matrix-core operand order; the row exponents follow. M == 0 is empty.
+ *   q4_gemv_prepared(prep, prep_bytes, w_q, w_bytes, y, M, N, K, stream):
+ *     y = a @ dequant(W)^T from prep (made by q4_gemv_prepare for the same M
+ *     and K), w_q and y as q4_gemv. Shape errors as q4_gemv_prepare, and
+ *     Q4_ERR_SHAPE when W exceeds 2^31 bytes; sizes, pointers and overlap as
+ *     q4_gemv, with prep in place of a.
+ * The prepared buffer is specific to the weight format (q8_gemv_prepare's
+ * differs). Accuracy as q4_gemv; deterministic. Measured on MI355X, the
+ * prepared GEMV beats q4_gemv from M = 4 up (8 x 4096 x 4096: 5.8 us against
+ * 9.0 us, plus 3.0 us to prepare, once per shared input); at M <= 2 q4_gemv
+ * is faster.
+ */
+size_t q4_gemv_prepare_bytes(int M, int K);
+int q4_gemv_prepare(const float *a, int M, int K, void *prep, size_t prep_bytes, void *stream);
+int q4_gemv_prepared(const void *prep, size_t prep_bytes, const void *w_q, size_t w_bytes,
+                     float *y, int M, int N, int K, void *stream);
+
+/* q8_gemv_prepare / q8_gemv_prepared — the same two steps for Q8_0 weights
+ * (the row scale puts the largest magnitude itself in [2^14, 2^15)). */
+size_t q8_gemv_prepare_bytes(int M, int K);
+int q8_gemv_prepare(const float *a, int M, int K, void *prep, size_t prep_bytes, void *stream);
+int q8_gemv_prepared(const void *prep, size_t prep_bytes, const void *w_q, size_t w_bytes,
+                     float *y, int M, int N, int K, void *stream);
 
 /*
  * q4_gemv_splitk — q4_gemv with K split across workgroups, for decode shapes

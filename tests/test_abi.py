@@ -303,6 +303,44 @@ def test_gemv_splitk_checks(f):
     assert st(None, None, 0, 64, 4096, 4, None, 0) == S.Q4_OK          # empty
 
 
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemv_prepare_bytes(f):
+    pb = getattr(binding, f + "_gemv_prepare_bytes")
+    # Two binary16 terms per activation (K/32 blocks x 4 lane groups x 2M rows x 16 B),
+    # then M int32 exponents padded to 16 bytes.
+    assert pb(1, 4096) == 128 * 4 * 2 * 16 + 16
+    assert pb(8, 4096) == 128 * 4 * 16 * 16 + 32
+    assert pb(5, 256) == 8 * 4 * 10 * 16 + 32
+    for M, K in [(0, 4096), (9, 4096), (1, 4128), (1, 0), (1, -256), (-1, 256)]:
+        assert pb(M, K) == 0, (M, K)
+
+
+@fake_addresses
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemv_prepare_checks(f):
+    S = binding
+    need = getattr(binding, f + "_gemv_prepare_bytes")(2, 512)
+    PR = BASE + (3 << 32)
+    prep = lambda a, M, K, p, pb: binding.raw_status(f + "_gemv_prepare", a, M, K, p, pb, 0)
+    assert prep(A, 9, 512, PR, need) == S.Q4_ERR_SHAPE
+    assert prep(A, 2, 4128, PR, need) == S.Q4_ERR_SHAPE
+    assert prep(A, 2, 512, PR, need - 1) == S.Q4_ERR_SIZE
+    assert prep(None, 2, 512, PR, need) == S.Q4_ERR_NULL
+    assert prep(A, 2, 512, PR + 8, need) == S.Q4_ERR_ALIGN
+    assert prep(A, 2, 512, A + 16, need) == S.Q4_ERR_ALIAS
+    assert prep(None, 0, 512, None, 0) == S.Q4_OK
+    wbn = _wb(64, 512, f)
+    run = lambda p, pb, w, wb, y, M, N, K: binding.raw_status(f + "_gemv_prepared", p, pb, w, wb, y, M, N, K, 0)
+    assert run(PR, need, W, wbn, Y, 9, 64, 512) == S.Q4_ERR_SHAPE
+    assert run(PR, need, W, _wb(64, 4128, f), Y, 2, 64, 4128) == S.Q4_ERR_SHAPE
+    assert run(PR, need, W, wbn + 1, Y, 2, 64, 512) == S.Q4_ERR_SIZE
+    assert run(PR, need - 16, W, wbn, Y, 2, 64, 512) == S.Q4_ERR_SIZE
+    assert run(None, need, W, wbn, Y, 2, 64, 512) == S.Q4_ERR_NULL
+    assert run(PR, need, W, wbn, Y + 4, 2, 64, 512) == S.Q4_ERR_ALIGN
+    assert run(PR, need, W, wbn, PR + 32, 2, 64, 512) == S.Q4_ERR_ALIAS
+    assert run(None, 0, None, wbn, None, 0, 64, 512) == S.Q4_OK
+
+
 @fake_addresses
 def test_binding_raises_q4error():
     with pytest.raises(binding.Q4Error) as e:

@@ -24,6 +24,15 @@ What each function follows (the docs.rs page "fuel-vulkan-kernels — quantized
 * ``bf16_to_f32``    bfloat16 activations widened to f32 (exact: bfloat16 is
                      the upper half of binary32); the products of bfloat16
                      activations are the f32 products of the widened values.
+* ``q4_0_matmul_q8a`` / ``q8_0_matmul_q8a``  the product with activations that
+                     were quantized to Q8_0 blocks along K. The geistlib issue
+                     "vulkan: shader and sequencing efficiency backlog" (page 2,
+                     sections Reductions and the opening summary) names an
+                     activation-quantize kernel and its fusion, and defines
+                     neither; read plainly, each activation row goes through
+                     "quantize_q8_0" in 32-element blocks, and the product is
+                     then the one of the dequantized values ("dequant_q8_0"),
+                     which is exactly sum over blocks of d_w d_a sum q_w q_a.
 
 Every function is pinned in ``tests/test_oracle_pins.py`` against values that
 do not come from this module: hand-worked blocks, library routines
@@ -247,6 +256,40 @@ def q8_0_matmul(a, w_blob, N: int, K: int, threads: int = 0):
 def q8_0_matmul_sampled(a, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 0):
     """As q4_0_matmul_sampled, with W the [N, K/32] Q8_0 block stream."""
     return _matmul_sampled("q8_0", a, w_blob, N, K, m_idx, n_idx, threads)
+
+
+def _dequant_activations(a_q, M: int, K: int) -> np.ndarray:
+    b = _u8(a_q).reshape(-1)
+    if K % QK or b.size != M * (K // QK) * Q8_0_BLOCK_BYTES:
+        raise ValueError("activation blob does not match M=%d K=%d" % (M, K))
+    return q8_0_dequant(b).reshape(M, K)
+
+
+def q4_0_matmul_q8a(a_q, M: int, w_blob, N: int, K: int, threads: int = 0):
+    """Q8_0-quantized activations times Q4_0 weights: a_q is the [M, K/32]
+    Q8_0 block stream of the activations (row m's blocks contiguous, in K
+    order). The value is the f64 product of the dequantized activations
+    (dequant_q8_0) with the dequantized weights, and B the matching bound, as
+    q4_0_matmul. Each product of a Q8_0 value (8-bit code times an 11-bit
+    scale) with a weight is exact in f64."""
+    return _matmul("q4_0", _dequant_activations(a_q, M, K), w_blob, N, K, threads)
+
+
+def q8_0_matmul_q8a(a_q, M: int, w_blob, N: int, K: int, threads: int = 0):
+    """As q4_0_matmul_q8a, with W the [N, K/32] Q8_0 block stream."""
+    return _matmul("q8_0", _dequant_activations(a_q, M, K), w_blob, N, K, threads)
+
+
+def q4_0_matmul_q8a_sampled(a_q, M: int, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 0):
+    """q4_0_matmul_q8a at sampled outputs (m_idx[i], n_idx[i])."""
+    return _matmul_sampled("q4_0", _dequant_activations(a_q, M, K), w_blob, N, K, m_idx, n_idx,
+                           threads)
+
+
+def q8_0_matmul_q8a_sampled(a_q, M: int, w_blob, N: int, K: int, m_idx, n_idx, threads: int = 0):
+    """q8_0_matmul_q8a at sampled outputs (m_idx[i], n_idx[i])."""
+    return _matmul_sampled("q8_0", _dequant_activations(a_q, M, K), w_blob, N, K, m_idx, n_idx,
+                           threads)
 
 
 def max_threads() -> int:

@@ -19,6 +19,11 @@ oracle fails a test here:
   all-8 nibbles or all-zero bytes, the ramp block, integer data) and linearity,
   with weights packed here from the layout definition rather than by the
   oracle.
+* The products over Q8_0-quantized activations: the block-integer form
+  sum_b d_w d_a sum q_w q_a in exact rationals (the oracle sums dequantized
+  values instead), integer codes with unit scales against numpy's integer
+  product, one-hot activation codes, and per-(row, block) powers of two that
+  expose a transposed activation stream.
 """
 import json
 import math
@@ -448,3 +453,98 @@ def test_threads_do_not_change_results(orc):
     y1, b1 = orc.q4_0_matmul(a, blob, N, K, threads=1)
     y4, b4 = orc.q4_0_matmul(a, blob, N, K, threads=4)
     assert (y1 == y4).all() and (b1 == b4).all()
+
+
+# ------------------------------------------- Q8_0-quantized activations
+
+def _act_case(seed, M, K, dbits=None):
+    """Q8_0 activation stream from random codes and scales, packed here."""
+    codes = wl.uniform_ints(seed, -128, 128, (M, K))
+    if dbits is None:
+        dbits = _random_scales(seed + 5, M * (K // 32))
+    return codes, dbits, _pack_q8_0(codes, dbits)
+
+
+def _matmul_q8a(orc, fmt):
+    return getattr(orc, FORMATS[fmt]["matmul"] + "_q8a")
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 5, 32), (2, 4, 64), (3, 5, 96)])
+def test_q8a_product_block_integer_form(orc, fmt, M, N, K):
+    # The integer form of the same sum, from the codes and scales alone:
+    # y = sum_b d_w[n, b] d_a[m, b] sum_j (q_w - zero) q_a, exact rationals.
+    seed = 300 + 100 * M + 10 * N + K
+    wc, wd, wblob = _product_case(fmt, seed, N, K)
+    ac, ad, ablob = _act_case(seed + 1, M, K)
+    nb = K // 32
+    dw = [[Fraction(_f16_value(h)) for h in row] for row in np.asarray(wd).reshape(N, nb)]
+    da = [[Fraction(_f16_value(h)) for h in row] for row in np.asarray(ad).reshape(M, nb)]
+    y, bound = _matmul_q8a(orc, fmt)(ablob, M, wblob, N, K)
+    z = FORMATS[fmt]["zero"]
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(0)
+            babs = Fraction(0)
+            for b in range(nb):
+                ks = range(32 * b, 32 * b + 32)
+                isum = sum(int(wc[n, k] - z) * int(ac[m, k]) for k in ks)
+                iabs = sum(abs(int(wc[n, k] - z) * int(ac[m, k])) for k in ks)
+                exact += dw[n][b] * da[m][b] * isum
+                babs += abs(dw[n][b] * da[m][b]) * iabs
+            assert abs(Fraction(y[m, n]) - exact) <= Fraction(1, 10 ** 12) * babs
+            assert abs(Fraction(bound[m, n]) - babs) <= Fraction(1, 10 ** 12) * babs
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_q8a_product_integer_data_is_exact(orc, fmt):
+    # Every scale 1.0: the product is the integer matrix product of the codes.
+    M, N, K = 4, 7, 256
+    ones_w = np.full(N * K // 32, 0x3C00, dtype=np.uint16)
+    ones_a = np.full(M * K // 32, 0x3C00, dtype=np.uint16)
+    wc, _, wblob = _product_case(fmt, 311, N, K, dbits=ones_w)
+    ac, _, ablob = _act_case(312, M, K, dbits=ones_a)
+    y, _ = _matmul_q8a(orc, fmt)(ablob, M, wblob, N, K)
+    ref = ac @ (wc - FORMATS[fmt]["zero"]).T                  # numpy integers
+    assert (y == ref.astype(np.float64)).all()
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_q8a_product_one_hot_picks_the_weight(orc, fmt):
+    # Activation row m: d = 1, code 1 at element ks[m], 0 elsewhere.
+    N, K = 6, 128
+    wc, wd, wblob = _product_case(fmt, 321, N, K)
+    w = _weights_f64(wc, wd, fmt)
+    ks = [0, 31, 32, 95, 127]
+    codes = np.zeros((len(ks), K), dtype=np.int64)
+    for m, k in enumerate(ks):
+        codes[m, k] = 1
+    ablob = _pack_q8_0(codes, np.full(len(ks) * K // 32, 0x3C00, dtype=np.uint16))
+    y, _ = _matmul_q8a(orc, fmt)(ablob, len(ks), wblob, N, K)
+    for m, k in enumerate(ks):
+        assert (y[m] == w[:, k]).all()
+
+
+def test_q8a_activation_blocks_follow_k_within_a_row(orc):
+    # Row m's blocks are contiguous in K order: distinct powers of two per
+    # (row, block) expose a row/block transposition of the activation stream.
+    M, N, K = 2, 1, 96
+    wc = np.full((N, K), 9, dtype=np.int64)                         # every weight = d_w = 1
+    _, _, wblob = _product_case("q4_0", 0, N, K, codes=wc,
+                                dbits=np.full(K // 32, 0x3C00, dtype=np.uint16))
+    codes = np.ones((M, K), dtype=np.int64)
+    dvals = [[1.0, 2.0, 4.0], [8.0, 16.0, 32.0]]
+    dbits = np.array([np.float16(v).view(np.uint16) for row in dvals for v in row])
+    y, _ = orc.q4_0_matmul_q8a(_pack_q8_0(codes, dbits), M, wblob, N, K)
+    assert y[:, 0].tolist() == [32.0 * 7, 32.0 * 56]
+
+
+def test_q8a_sampled_equals_full(orc):
+    M, N, K = 3, 21, 256
+    _, _, wblob = _product_case("q8_0", 331, N, K)
+    _, _, ablob = _act_case(332, M, K)
+    y, b = orc.q8_0_matmul_q8a(ablob, M, wblob, N, K)
+    mi = wl.uniform_ints(333, 0, M, 40)
+    ni = wl.uniform_ints(334, 0, N, 40)
+    ys, bs = orc.q8_0_matmul_q8a_sampled(ablob, M, wblob, N, K, mi, ni)
+    assert (ys == y[mi, ni]).all() and (bs == b[mi, ni]).all()

@@ -154,7 +154,12 @@ def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
 
 
 def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=False):
-    """The kernel the library launches (mirrors launch_gemv_m and gemv_split_plan)."""
+    """The kernel the library launches (mirrors launch_gemv_m, launch_gemv_q8a_m and
+    gemv_split_plan)."""
+    if act == "q8_0":
+        if K % 256:
+            return "k_gemv_q8a_any<%s, %d>" % (FMT_TYPE[fmt], M)
+        return "k_gemv_q8a<%s, %d, 8, %d>" % (FMT_TYPE[fmt], M, 16 if (K // 32) % 16 == 0 else 8)
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
@@ -200,8 +205,16 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     wbytes = blob.numel()
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
-    prep_us = None
-    if s["kind"] == "gemv" and s.get("prepared"):
+    prep_us = quant_us = None
+    if s["kind"] == "gemv" and act == "q8_0":
+        # The activations are quantized once, outside the timed region (its own
+        # time is quant_us); the GEMV reads the Q8_0 blocks.
+        a_q = torch.empty(M * (K // 32) * 34, dtype=torch.uint8, device="cuda")
+        q4.q8_quantize(a, a_q)
+        gemv = getattr(q4, f + "_gemv_q8a")
+        fn = lambda k: gemv(a_q, blobs[k % R], y, M, N, K)
+        quant_us = run_timed(torch, lambda k: q4.q8_quantize(a, a_q), min(steps, 50), 5)["kernel_us"]
+    elif s["kind"] == "gemv" and s.get("prepared"):
         prep = torch.empty(getattr(q4, f + "_gemv_prepare_bytes")(M, K), dtype=torch.uint8,
                            device="cuda")
         prepare = getattr(q4, f + "_gemv_prepare")
@@ -224,7 +237,8 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         fn = lambda k: gemm(a, blobs[k % R], y, M, N, K, workspace=ws)
     t = run_timed(torch, fn, steps, warmup)
-    algo_bytes = wbytes + M * K * (2 if act == "bf16" else 4) + M * N * 4
+    a_bytes = M * (K // 32) * 34 if act == "q8_0" else M * K * (2 if act == "bf16" else 4)
+    algo_bytes = wbytes + a_bytes + M * N * 4
     flops = 2.0 * M * N * K
     kern_s = t["kernel_us"] * 1e-6
     row = {"workload": name, "format": fmt, "activations": act, "M": M, "N": N, "K": K,
@@ -234,6 +248,10 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
            "kernel_GBs": algo_bytes / kern_s / 1e9, "kernel_TFLOPs": flops / kern_s / 1e12,
            "job_GBs": algo_bytes * steps / t["wall_s"] / 1e9,
            "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
+    if quant_us is not None:
+        row["quantize_us"] = quant_us
+        row["note"] = ("kernel_us is the GEMV over Q8_0 activation blocks alone; quantizing the "
+                       "f32 activations (q8_quantize, one more launch) takes quantize_us")
     if prep_us is not None:
         row["prepare_us"] = prep_us
         row["note"] = ("kernel_us is the GEMV from prepared operands alone; preparing them "
@@ -430,9 +448,12 @@ def main():
                          ("gemv_prepared_8x4096x4096", args.steps),
                          ("gemv_1x512x4096", args.steps), ("gemm_2048x1792x4096", 50),
                          ("gemv_1x512x14336", args.steps), ("gemv_splitk_1x512x14336", args.steps)):
-            log("row: %s (one GPU's share of an 8-way row split)" % name)
+            log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
+        for name in ("gemv_q8a_1x4096x4096", "gemv_q8a_8x4096x4096", "q8_0_gemv_q8a_1x4096x4096"):
+            log("row: %s" % name)
+            rows.append(bench_product(torch, q4, wl, name, args.steps, min(args.warmup, 10)))
         log("row: Q8_0 dequant 14336x4096")
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10),
                                   "q8_0_dequant_14336x4096"))

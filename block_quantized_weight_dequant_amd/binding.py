@@ -36,7 +36,7 @@ EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_ge
            "q4_gemv_bf16", "q8_gemv_bf16", "q4_gemv_splitk", "q4_gemv_splitk_workspace_bytes",
            "q8_gemv_splitk", "q8_gemv_splitk_workspace_bytes", "q4_gemv_prepare_bytes",
            "q4_gemv_prepare", "q4_gemv_prepared", "q8_gemv_prepare_bytes", "q8_gemv_prepare",
-           "q8_gemv_prepared")
+           "q8_gemv_prepared", "q4_gemv_q8a", "q8_gemv_q8a")
 
 
 class Q4Error(RuntimeError):
@@ -82,6 +82,9 @@ def _load_library():
         getattr(lib, f + "_gemv_prepare").argtypes = [P, i32, i32, P, sz, P]
         getattr(lib, f + "_gemv_prepared").restype = i32
         getattr(lib, f + "_gemv_prepared").argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
+    for name in ("q4_gemv_q8a", "q8_gemv_q8a"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -209,6 +212,26 @@ def q8_gemv_prepared(prep, w_q, y, M: int, N: int, K: int, prep_bytes=None, w_by
                      stream=None) -> None:
     """As q4_gemv_prepared over a Q8_0 weight stream."""
     _gemv_prepared("q8_gemv_prepared", prep, w_q, y, M, N, K, prep_bytes, w_bytes, stream)
+
+
+def _gemv_q8a(entry, a_q, w_q, y, M, N, K, a_bytes, w_bytes, stream) -> None:
+    ab = _nbytes(a_q) if a_bytes is None else int(a_bytes)
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    _check(getattr(lib, entry)(_addr(a_q), ab, _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                               _stream(stream)), entry)
+
+
+def q4_gemv_q8a(a_q, w_q, y, M: int, N: int, K: int, a_bytes=None, w_bytes=None,
+                stream=None) -> None:
+    """y[M, N] = dequant(A_q[M, K/32]) @ dequant(W[N, K/32])^T for 1 <= M <= 8:
+    activations as Q8_0 blocks (uint8 tensor, e.g. from q8_quantize), W Q4_0."""
+    _gemv_q8a("q4_gemv_q8a", a_q, w_q, y, M, N, K, a_bytes, w_bytes, stream)
+
+
+def q8_gemv_q8a(a_q, w_q, y, M: int, N: int, K: int, a_bytes=None, w_bytes=None,
+                stream=None) -> None:
+    """As q4_gemv_q8a over a Q8_0 weight stream."""
+    _gemv_q8a("q8_gemv_q8a", a_q, w_q, y, M, N, K, a_bytes, w_bytes, stream)
 
 
 def q4_gemv_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:

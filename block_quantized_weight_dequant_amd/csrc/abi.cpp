@@ -132,6 +132,18 @@ static int gemv_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *
                                           as_stream(stream)));
 }
 
+static int gemv_q8a(q4k::WeightFormat fmt, size_t block_bytes, const void *a_q, size_t a_bytes,
+                    const void *w_q, size_t w_bytes, float *y, int M, int N, int K, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_gemv_q8a(a_q, a_bytes, w_q, w_bytes, y, M, N, K, block_bytes, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemv_q8a(fmt, static_cast<const uint8_t *>(a_q),
+                                         static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                         as_stream(stream)));
+}
+
 static int gemm_bf16(q4k::WeightFormat fmt, size_t block_bytes, const uint16_t *a,
                      const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
                      void *workspace, size_t workspace_bytes, void *stream)
@@ -304,4 +316,16 @@ Q4_EXPORT int q4_quantize(const float *x, size_t n_elems, void *out_q, size_t ou
         return st;
     return launched(q4k::launch_q4_quantize(x, n_elems / 32, static_cast<uint8_t *>(out_q),
                                             as_stream(stream)));
+}
+
+Q4_EXPORT int q4_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes,
+                          float *y, int M, int N, int K, void *stream)
+{
+    return gemv_q8a(q4k::WeightFormat::kQ4_0, 18, a_q, a_bytes, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT int q8_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes,
+                          float *y, int M, int N, int K, void *stream)
+{
+    return gemv_q8a(q4k::WeightFormat::kQ8_0, 34, a_q, a_bytes, w_q, w_bytes, y, M, N, K, stream);
 }

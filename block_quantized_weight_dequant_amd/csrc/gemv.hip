@@ -943,4 +943,361 @@ hipError_t launch_gemv_splitk(WeightFormat fmt, const float *a, const uint8_t *w
     return launch_gemv_splitk_f<FmtQ4_0>(a, w, y, M, N, K, sp, part, s);
 }
 
+// ---------------------------------------------------------------------------
+// Q8_0-quantized activations. a_q is the [M, K/32] Q8_0 block stream of the
+// activations (row m's blocks contiguous, in K order), so each block's dot
+// product is an integer one, sum_j w_j q_j over the weight codes (q - 8 for
+// Q4_0, the signed byte for Q8_0) and the activation codes, scaled by d_w d_a.
+// * The integer sums run exactly on v_mfma_i32_16x16x32_i8 (K = 32, one
+//   block): A rows are activation rows, B columns weight rows, so lane (j, g)
+//   holds C rows 4g..4g+3 of weight row j, as in the f16 kernels.
+// * The scale is applied in f32. d_w d_a has at most 22 significant bits and
+//   stays normal, so it is exact; |sum| <= 2^19 converts exactly; one fused
+//   multiply-add per block and C row adds sum d_w d_a to the chunk's partial
+//   with one rounding. Partials: block -> chunk -> wavefront -> workgroup,
+//   each level summed in a fixed order.
+// * Operands of lane group g, eight signed bytes in slot order. Q4_0: qs dword
+//   g; flipping bits 3 and 7 of each byte and masking nibbles gives bytes
+//   16 (q - 8), the low nibbles (elements 4g..4g+3) after a 4-bit shift in
+//   slots 0..3 and the high nibbles (elements 16+4g..16+4g+3) in slots 4..7.
+//   The factor 16 comes out of d_w (a power of two: exact). The activation
+//   operand takes its qs bytes 4g..4g+3 and 16+4g..16+4g+3. Q8_0: qs bytes
+//   8g..8g+7 of both, unchanged.
+// * Streaming form (K % 256 == 0): chunks of CH blocks dealt to the
+//   wavefronts in turn, weights staged through LDS as in k_gemv_stream; the
+//   chunk's M activation rows (CH * 34 bytes each, 16-byte aligned) are staged
+//   beside them with 16-byte loads, and their scales are widened once per
+//   chunk into an f32 [block][row] table.
+
+// Low and high nibbles of a Q4_0 qs dword as signed bytes 16 (q - 8).
+__device__ __forceinline__ long q4_codes_x16(uint32_t x)
+{
+    const uint32_t t = x ^ 0x88888888u;
+    const uint32_t lo = (t << 4) & 0xF0F0F0F0u;
+    const uint32_t hi = t & 0xF0F0F0F0u;
+    return (long)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long pack_operand(uint32_t lo, uint32_t hi)
+{
+    return (long)(((uint64_t)hi << 32) | lo);
+}
+
+// Quant dword i of Q8_0 block B of a run of blocks that starts on a 4-byte
+// boundary (the block's bytes 2 + 4i .. 5 + 4i).
+template <int B>
+__device__ __forceinline__ uint32_t q8_qs_dword(const uint32_t *row, int i)
+{
+    constexpr int o = kQ8Bytes * B + 2, i0 = o / 4, sh = o % 4;
+    const uint32_t *p = row + i0 + i;
+    if constexpr (sh != 0)
+        return __builtin_amdgcn_alignbyte(p[1], p[0], 2u);
+    else
+        return p[0];
+}
+
+// Lane group g's activation operand from Q8_0 block B of a staged row, in the
+// slot order of format F's weight operand.
+template <class F, int B>
+__device__ __forceinline__ long q8a_act_operand(const uint32_t *arow, int g)
+{
+    if constexpr (F::kBytes == kQ4Bytes)
+        return pack_operand(q8_qs_dword<B>(arow, g), q8_qs_dword<B>(arow, 4 + g));
+    else
+        return pack_operand(q8_qs_dword<B>(arow, 2 * g), q8_qs_dword<B>(arow, 2 * g + 1));
+}
+
+// Lane group g's weight operand from block B of a staged weight row.
+template <class F, int B>
+__device__ __forceinline__ long q8a_weight_operand(const uint32_t *wrow, int g)
+{
+    uint32_t x[F::kQsDwords];
+    read_qs<F, B>(wrow, g, x);
+    if constexpr (F::kBytes == kQ4Bytes)
+        return q4_codes_x16(x[0]);
+    else
+        return pack_operand(x[0], x[1]);
+}
+
+// d_w factor that undoes the weight operand's scaling (16 for Q4_0).
+template <class F>
+constexpr float q8a_weight_scale() { return F::kBytes == kQ4Bytes ? 0.0625f : 1.0f; }
+
+template <class F, int M, int NW, int CH>
+__global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict__ aq,
+                                                     const uint8_t *__restrict__ w,
+                                                     float *__restrict__ y, int N, int K)
+{
+    using C = GemvStreamCfg<F, M, NW, CH, false>;
+    constexpr int NACC = M < 4 ? M : 4;           // C rows a lane keeps (activation rows 4g + r)
+    constexpr int CPRA = CH * kQ8Bytes / 16;      // 16-byte columns of a chunk's activation row
+    constexpr int NAE = M * CPRA;                 // ... of its M rows
+    constexpr int NAL = (NAE + 63) / 64;          // ... per lane
+    constexpr int RSA = CH * kQ8Bytes + 16;       // LDS bytes per staged activation row
+    constexpr int ABYTES = M * RSA;
+    constexpr int NDA = CH * M;                   // activation scales per chunk
+    // Per wavefront: [staged weights | staged activations | scale table [CH][8]].
+    constexpr int kLdsPerWave = C::WBYTES + ABYTES + CH * 8 * 4;
+    static_assert(kLdsPerWave % 16 == 0, "16-byte aligned areas");
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[NW * kLdsPerWave];
+    __shared__ float s_part[NW][M][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int nblk = K >> 5;
+    const uint32_t row_bytes = (uint32_t)nblk * F::kBytes;
+    const uint32_t arow_bytes = (uint32_t)nblk * kQ8Bytes;
+    uint8_t *s_w = s_mem + wave * kLdsPerWave;
+    uint8_t *s_act = s_w + C::WBYTES;
+    float *s_da = reinterpret_cast<float *>(s_act + ABYTES);
+    const int wb0 = wave * CH;                    // this wavefront's first chunk
+    constexpr int kStride = NW * CH;              // ... and the step to its next
+
+    // Weight loader role as in k_gemv_stream: row lr, 16-byte columns lc0 + 4 i.
+    const int lr = lane & 15, lc0 = lane >> 4;
+    const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
+    const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
+
+    u32x4 wreg[C::NLOAD];
+    u32x4 areg[NAL];
+    // Activation columns first (they drain first), then the weight columns.
+    // Every lane issues every load; surplus lanes re-read the last activation
+    // column and never store it.
+    auto fetch = [&](int cb0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < NAL; ++r) {
+            const int e = min(lane + 64 * r, NAE - 1);
+            const int m = e / CPRA, col = e - m * CPRA;
+            areg[r] = *reinterpret_cast<const u32x4 *>(
+                aq + ((uint32_t)m * arow_bytes + (uint32_t)cb0 * kQ8Bytes + 16u * (uint32_t)col));
+        }
+        const uint32_t woff = lrow_off + (uint32_t)cb0 * F::kBytes + 16u * lc0;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < C::NFULL; ++i) {
+            wreg[i] = *reinterpret_cast<const u32x4 *>(w + (woff + 64u * i));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (C::NFULL < C::NLOAD)
+            wreg[C::NFULL] = *reinterpret_cast<const u32x4 *>(w + (woff + last_off));
+        asm volatile("" ::"s"(w), "s"(aq) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // A wavefront without blocks fetches the row's last chunk and never reads it.
+    fetch(min(wb0, nblk - CH));
+
+    const uint32_t *arow32 = reinterpret_cast<const uint32_t *>(s_act + min(j, M - 1) * RSA);
+    const uint32_t *wrow32 = reinterpret_cast<const uint32_t *>(s_w + j * C::RS);
+    const float *da_lane = s_da + 4 * min(g, 1);
+    const i32x4 zero4 = {0, 0, 0, 0};
+    float ysum[NACC];
+#pragma unroll
+    for (int r = 0; r < NACC; ++r)
+        ysum[r] = 0.0f;
+
+    for (int cb0 = wb0; cb0 < nblk; cb0 += kStride) {
+#pragma unroll
+        for (int r = 0; r < NAL; ++r) {
+            const int e = lane + 64 * r;
+            if (e < NAE) {
+                const int m = e / CPRA, col = e - m * CPRA;
+                *reinterpret_cast<u32x4 *>(s_act + m * RSA + 16 * col) = areg[r];
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < (NDA + 63) / 64; ++r) {
+            const int t = lane + 64 * r;
+            if (t < NDA) {
+                const int b = t / M, m = t - b * M;
+                s_da[b * 8 + m] = f16_bits_to_f32(
+                    *reinterpret_cast<const uint16_t *>(s_act + m * RSA + kQ8Bytes * b));
+            }
+        }
+        float acc[NACC];
+#pragma unroll
+        for (int r = 0; r < NACC; ++r)
+            acc[r] = 0.0f;
+        auto stage = [&](auto i0_c, auto i1_c) __attribute__((always_inline)) {
+            constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
+#pragma unroll
+            for (int i = I0; i < I1; ++i) {
+                const int col = lc0 + 4 * i;
+                if (col < C::CPR)
+                    *reinterpret_cast<u32x4 *>(s_w + lr * C::RS + 16 * col) = wreg[i];
+            }
+        };
+        // All integer MFMAs of a part are issued before its scale FMAs.
+        auto contract = [&](auto b0_c, auto b1_c) __attribute__((always_inline)) {
+            constexpr int B0 = decltype(b0_c)::value, B1 = decltype(b1_c)::value;
+            i32x4 Dv[B1 - B0];
+            float dw[B1 - B0];
+            static_for<B0, B1>([&](auto b_c) __attribute__((always_inline)) {
+                constexpr int b = decltype(b_c)::value;
+                const long bw = q8a_weight_operand<F, b>(wrow32, g);
+                const long av = q8a_act_operand<F, b>(arow32, g);
+                dw[b - B0] = f16_bits_to_f32(read_d_bits<F, b>(wrow32)) * q8a_weight_scale<F>();
+                Dv[b - B0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bw, zero4, 0, 0, 0);
+            });
+#pragma unroll
+            for (int u = 0; u < B1 - B0; ++u) {
+                const f32x4 da = *reinterpret_cast<const f32x4 *>(da_lane + (B0 + u) * 8);
+#pragma unroll
+                for (int r = 0; r < NACC; ++r)
+                    acc[r] = fmaf(dw[u] * da[r], (float)Dv[u][r], acc[r]);
+            }
+#pragma unroll
+            for (int u = 0; u < B1 - B0; ++u)
+                asm volatile("" ::"v"(Dv[u]));
+        };
+        for_each_part<C::NPART>([&](auto p_c) __attribute__((always_inline)) {
+            constexpr int P = decltype(p_c)::value;
+            constexpr int B0 = P * CH / C::NPART, B1 = (P + 1) * CH / C::NPART;
+            constexpr int L0 = C::loads_for(B0), L1 = C::loads_for(B1);
+            stage(std::integral_constant<int, L0>{}, std::integral_constant<int, L1>{});
+            auto run_part = [&]() __attribute__((always_inline)) {
+                wave_lds_sync();
+                contract(std::integral_constant<int, B0>{}, std::integral_constant<int, B1>{});
+            };
+            if constexpr (P < C::NPART - 1) {
+                run_part();
+            } else if (cb0 + kStride < nblk) {
+                fetch(cb0 + kStride);   // every register of this chunk is staged
+                run_part();
+            } else {
+                run_part();
+            }
+        });
+#pragma unroll
+        for (int r = 0; r < NACC; ++r)
+            ysum[r] += acc[r];
+        wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
+    }
+
+#pragma unroll
+    for (int r = 0; r < NACC; ++r) {
+        const int m = 4 * g + r;
+        if (m < M)
+            s_part[wave][m][j] = ysum[r];
+    }
+    __syncthreads();
+    if (tid < M * 16) {
+        const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
+        float sum = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww)
+            sum += s_part[ww][m][jj];
+        if (n < N)
+            y[(size_t)m * N + n] = sum;
+    }
+}
+
+// General shapes (K % 256 != 0, or offsets beyond 31 bits): the same
+// arithmetic with each lane loading its operands and scales from global memory
+// (2-byte aligned dword loads); wavefront w takes blocks w, w + 8, ...
+template <class F, int M>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_q8a_any(const uint8_t *__restrict__ aq,
+                                                              const uint8_t *__restrict__ w,
+                                                              float *__restrict__ y, int N, int K)
+{
+    constexpr int NW = kGemvWaves;
+    constexpr int NACC = M < 4 ? M : 4;
+    __shared__ float s_part[NW][M][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int nblk = K >> 5;
+    const uint8_t *wrow = w + (size_t)min(n0 + j, N - 1) * (size_t)nblk * F::kBytes;
+    const uint8_t *arow = aq + (size_t)min(j, M - 1) * (size_t)nblk * kQ8Bytes;
+    const uint8_t *drow[NACC];
+#pragma unroll
+    for (int r = 0; r < NACC; ++r)
+        drow[r] = aq + (size_t)min(4 * g + r, M - 1) * (size_t)nblk * kQ8Bytes;
+    const i32x4 zero4 = {0, 0, 0, 0};
+    float acc[NACC];
+#pragma unroll
+    for (int r = 0; r < NACC; ++r)
+        acc[r] = 0.0f;
+    for (int b = wave; b < nblk; b += NW) {
+        const uint8_t *wb = wrow + (size_t)b * F::kBytes;
+        const uint8_t *ab = arow + (size_t)b * kQ8Bytes + 2;
+        uint32_t x[F::kQsDwords];
+        load_qs<F>(wb, g, x);
+        long bw, av;
+        if constexpr (F::kBytes == kQ4Bytes) {
+            bw = q4_codes_x16(x[0]);
+            av = pack_operand(load_u32_unaligned(ab + 4 * g), load_u32_unaligned(ab + 16 + 4 * g));
+        } else {
+            bw = pack_operand(x[0], x[1]);
+            av = pack_operand(load_u32_unaligned(ab + 8 * g), load_u32_unaligned(ab + 8 * g + 4));
+        }
+        const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bw, zero4, 0, 0, 0);
+        const float dw = f16_bits_to_f32(load_u16(wb)) * q8a_weight_scale<F>();
+#pragma unroll
+        for (int r = 0; r < NACC; ++r)
+            acc[r] = fmaf(dw * f16_bits_to_f32(load_u16(drow[r] + (size_t)b * kQ8Bytes)),
+                          (float)D[r], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < NACC; ++r) {
+        const int m = 4 * g + r;
+        if (m < M)
+            s_part[wave][m][j] = acc[r];
+    }
+    __syncthreads();
+    if (tid < M * 16) {
+        const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
+        float sum = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww)
+            sum += s_part[ww][m][jj];
+        if (n < N)
+            y[(size_t)m * N + n] = sum;
+    }
+}
+
+template <class F, int M>
+static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *y, int N, int K,
+                                    hipStream_t s)
+{
+    constexpr int NW = kGemvStreamWaves;
+    const unsigned grid = (unsigned)((N + 15) / 16);
+    if (q4v::gemv_q8a_streams(M, N, K, F::kBytes)) {
+        const int nblk = K / 32;
+        if (q4v::gemv_chunk_blocks(nblk, nblk) == 16)
+            return launch_kernel(k_gemv_q8a<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s, aq, w,
+                                 y, N, K);
+        return launch_kernel(k_gemv_q8a<F, M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, aq, w, y,
+                             N, K);
+    }
+    return launch_kernel(k_gemv_q8a_any<F, M>, dim3(grid), dim3(kGemvThreads), 0, s, aq, w, y, N,
+                         K);
+}
+
+template <class F>
+static hipError_t launch_gemv_q8a_f(const uint8_t *aq, const uint8_t *w, float *y, int M, int N,
+                                    int K, hipStream_t s)
+{
+    switch (M) {
+    case 1: return launch_gemv_q8a_m<F, 1>(aq, w, y, N, K, s);
+    case 2: return launch_gemv_q8a_m<F, 2>(aq, w, y, N, K, s);
+    case 3: return launch_gemv_q8a_m<F, 3>(aq, w, y, N, K, s);
+    case 4: return launch_gemv_q8a_m<F, 4>(aq, w, y, N, K, s);
+    case 5: return launch_gemv_q8a_m<F, 5>(aq, w, y, N, K, s);
+    case 6: return launch_gemv_q8a_m<F, 6>(aq, w, y, N, K, s);
+    case 7: return launch_gemv_q8a_m<F, 7>(aq, w, y, N, K, s);
+    case 8: return launch_gemv_q8a_m<F, 8>(aq, w, y, N, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_q8a(WeightFormat fmt, const uint8_t *a_q, const uint8_t *w, float *y, int M,
+                           int N, int K, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemv_q8a_f<FmtQ8_0>(a_q, w, y, M, N, K, s);
+    return launch_gemv_q8a_f<FmtQ4_0>(a_q, w, y, M, N, K, s);
+}
+
 }  // namespace q4k

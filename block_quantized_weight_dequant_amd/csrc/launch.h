@@ -27,6 +27,9 @@ hipError_t launch_gemv_prepare(WeightFormat fmt, const float *a, void *prep, int
                                hipStream_t s);
 hipError_t launch_gemv_prepared(WeightFormat fmt, const void *prep, const uint8_t *w, float *y,
                                 int M, int N, int K, hipStream_t s);
+// a_q: the [M, K/32] Q8_0 block stream of the activations, 1 <= M <= 8.
+hipError_t launch_gemv_q8a(WeightFormat fmt, const uint8_t *a_q, const uint8_t *w, float *y, int M,
+                           int N, int K, hipStream_t s);
 // K split across workgroups: partials of sp.splits splits into `workspace`
 // (sp.splits * M * N f32), then summed into y in split order. sp.splits <= 1
 // runs launch_gemv's kernel (workspace unused).

@@ -72,6 +72,32 @@ int check_product(const void *a, size_t a_elem, const void *w, size_t w_bytes, c
     return Q4_OK;
 }
 
+int check_gemv_q8a(const void *a_q, size_t a_bytes, const void *w, size_t w_bytes, const float *y,
+                   int M, int N, int K, size_t block_bytes, bool *empty)
+{
+    *empty = false;
+    if (M < 0 || M > Q4_GEMV_MAX_ROWS || N < 0 || K < 32 || K % 32 != 0)
+        return Q4_ERR_SHAPE;
+    size_t w_want = 0, a_want = 0, y_bytes = 0;
+    if (!mul_ok((size_t)N, (size_t)(K / 32) * block_bytes, &w_want) || w_bytes != w_want)
+        return Q4_ERR_SIZE;
+    if (!mul_ok((size_t)M, (size_t)(K / 32) * 34, &a_want) || a_bytes != a_want)
+        return Q4_ERR_SIZE;
+    if (!mul_ok((size_t)M, (size_t)N, &y_bytes) || !mul_ok(y_bytes, sizeof(float), &y_bytes))
+        return Q4_ERR_SIZE;
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return Q4_OK;
+    }
+    if (!a_q || !w || !y)
+        return Q4_ERR_NULL;
+    if (!aligned16(a_q) || !aligned16(w) || !aligned16(y))
+        return Q4_ERR_ALIGN;
+    if (overlaps({y, y_bytes}, {a_q, a_bytes}) || overlaps({y, y_bytes}, {w, w_bytes}))
+        return Q4_ERR_ALIAS;
+    return Q4_OK;
+}
+
 int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_bytes,
                    size_t block_bytes, bool *empty)
 {

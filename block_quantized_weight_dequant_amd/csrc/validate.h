@@ -136,6 +136,22 @@ size_t gemm_bf16_workspace_bytes(int M, int N, int K);
 int check_workspace(size_t need, const void *a, size_t a_elem, const void *w, size_t w_bytes,
                     const float *y, int M, int N, int K, const void *ws, size_t ws_bytes);
 
+// The GEMV over Q8_0-quantized activations (q4_gemv_q8a / q8_gemv_q8a): a_q
+// is the [M, K/32] Q8_0 block stream of the activations, a_bytes ==
+// M (K/32) 34, then as check_product (1 <= M <= 8 rows; M == 0 or N == 0 is
+// empty).
+int check_gemv_q8a(const void *a_q, size_t a_bytes, const void *w, size_t w_bytes, const float *y,
+                   int M, int N, int K, size_t block_bytes, bool *empty);
+
+// Its streaming kernel's shapes: 16-byte aligned weight and activation rows
+// (K % 256 == 0) and byte offsets into W and a_q below 2^31. Other shapes take
+// its general kernel.
+inline bool gemv_q8a_streams(int M, int N, int K, size_t block_bytes)
+{
+    return K > 0 && K % 256 == 0 && (size_t)N * (size_t)(K / 32) * block_bytes < ((size_t)1 << 31) &&
+           (size_t)M * (size_t)(K / 32) * 34 < ((size_t)1 << 31);
+}
+
 bool aligned16(const void *p);
 bool overlaps(Span a, Span b);
 

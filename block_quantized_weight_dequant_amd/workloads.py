@@ -67,6 +67,14 @@ WORKLOADS = {
                                       w_seed=400, a_seed=401),
     "q8_0_gemm_bf16_2048x14336x4096": dict(kind="gemm", act="bf16", fmt="q8_0", M=2048, N=14336,
                                            K=4096, w_seed=400, a_seed=401),
+    # The decode GEMVs over activations quantized to Q8_0 blocks (``act="q8_0"``:
+    # the same f32 activation draws, Q8_0-quantized by the caller's quantizer).
+    "gemv_q8a_1x4096x4096": dict(kind="gemv", act="q8_0", M=1, N=4096, K=4096, w_seed=200,
+                                 a_seed=201),
+    "gemv_q8a_8x4096x4096": dict(kind="gemv", act="q8_0", M=8, N=4096, K=4096, w_seed=200,
+                                 a_seed=202),
+    "q8_0_gemv_q8a_1x4096x4096": dict(kind="gemv", act="q8_0", fmt="q8_0", M=1, N=4096, K=4096,
+                                      w_seed=200, a_seed=201),
 }
 
 WEIGHT_SIGMA = np.float32(0.02)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 6
+#define Q4_ABI_VERSION 7
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -299,6 +299,32 @@ int q8_gemm_bf16(const uint16_t *a, const void *w_q, size_t w_bytes, float *y,
 
 /* q8_gemm_bf16_workspace_bytes — the same function as q4_gemm_bf16_workspace_bytes. */
 size_t q8_gemm_bf16_workspace_bytes(int M, int N, int K);
+
+/*
+ * q4_gemv_q8a — the decode GEMV over activations quantized to Q8_0 blocks
+ * along K. The geistlib issue "vulkan: shader and sequencing efficiency
+ * backlog" names an activation-quantize kernel and its fusion without
+ * defining them; here each activation row is a run of Q8_0 blocks as
+ * q8_quantize writes them (section quantize_q8_0; any Q8_0 blocks are
+ * accepted), and y = dequant_q8_0(a_q) @ dequant(W)^T, that is
+ * y[m, n] = sum over blocks b of d_w[n, b] d_a[m, b] sum_j w_code q_a
+ * (sections dequant_q8_0, dequant_q4_0 and qmatvec_q4_0).
+ *   a_q       the [M, K/32] Q8_0 block stream of the activations, row m's
+ *             blocks contiguous in K order; a_bytes == M * (K/32) * 34.
+ *   w_q, w_bytes, y, M, N, K: as q4_gemv (1 <= M <= 8).
+ * Errors as q4_gemv, with a_bytes checked like w_bytes (Q4_ERR_SIZE).
+ * The block sums are integer and exact on the matrix cores; each is scaled by
+ * d_w d_a (exact in f32) and added with one rounding. Accuracy: |y - y_exact|
+ * <= 1e-5 * sum_k |a'[m, k] w[n, k]| + 1e-6, a' the dequantized activations.
+ * Against the f32 activations the quantization itself adds up to
+ * d_a / 2 per element. Deterministic.
+ */
+int q4_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes, float *y,
+                int M, int N, int K, void *stream);
+
+/* q8_gemv_q8a — q4_gemv_q8a over a Q8_0 weight stream (w_bytes == N * (K/32) * 34). */
+int q8_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes, float *y,
+                int M, int N, int K, void *stream);
 
 /*
  * q8_quantize — f32 to Q8_0 blocks (section quantize_q8_0).

@@ -354,3 +354,27 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     runtimes = {l.split()[-1] for l in maps if "libamdhip64" in l}
     assert len(runtimes) == 1, runtimes
+
+
+@fake_addresses
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemv_q8a_checks(f):
+    S = binding
+    ab = lambda M, K: M * (K // 32) * 34
+    st = lambda a, abn, w, wbn, y, M, N, K: binding.raw_status(f + "_gemv_q8a", a, abn, w, wbn,
+                                                                y, M, N, K, 0)
+    wb = _wb(4, 256, f)
+    assert st(A, ab(9, 256), W, wb, Y, 9, 4, 256) == S.Q4_ERR_SHAPE        # M > 8
+    assert st(A, ab(2, 256), W, wb, Y, 2, 4, 240) == S.Q4_ERR_SHAPE        # K % 32
+    assert st(A, ab(2, 256), W, wb, Y, -1, 4, 256) == S.Q4_ERR_SHAPE
+    assert st(A, ab(2, 256) - 34, W, wb, Y, 2, 4, 256) == S.Q4_ERR_SIZE   # activation blob
+    assert st(A, 2 * 256 * 4, W, wb, Y, 2, 4, 256) == S.Q4_ERR_SIZE       # f32 length, not Q8_0
+    assert st(A, ab(2, 256), W, wb + 1, Y, 2, 4, 256) == S.Q4_ERR_SIZE
+    assert st(None, ab(2, 256), W, wb, Y, 2, 4, 256) == S.Q4_ERR_NULL
+    assert st(A, ab(2, 256), W, wb, None, 2, 4, 256) == S.Q4_ERR_NULL
+    assert st(A + 2, ab(2, 256), W, wb, Y, 2, 4, 256) == S.Q4_ERR_ALIGN
+    assert st(A, ab(2, 256), W + 8, wb, Y, 2, 4, 256) == S.Q4_ERR_ALIGN
+    assert st(A, ab(2, 256), W, wb, A + 16, 2, 4, 256) == S.Q4_ERR_ALIAS   # y inside a_q
+    assert st(A, ab(2, 256), W, wb, W + 32, 2, 4, 256) == S.Q4_ERR_ALIAS   # y inside w
+    assert st(None, 0, None, wb, None, 0, 4, 256) == S.Q4_OK                # empty
+    assert st(None, ab(3, 256), None, 0, None, 3, 0, 256) == S.Q4_OK

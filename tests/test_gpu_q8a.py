@@ -1,0 +1,195 @@
+"""GPU parity of q4_gemv_q8a / q8_gemv_q8a, the decode GEMV over activations
+quantized to Q8_0 blocks, against the oracle's f64 product of the dequantized
+activations and weights (sections quantize_q8_0, dequant_q8_0, dequant_q4_0
+and qmatvec_q4_0 of "fuel-vulkan-kernels — quantized (GGML) kernel
+contracts"; the activation quantization is the one the geistlib issue "vulkan:
+shader and sequencing efficiency backlog" names without defining). Every
+output must satisfy |y - y_ref| <= 1e-5 * sum|a' w| + 1e-6, a' the dequantized
+activations; with unit scales the integer sums must come out exactly."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from block_quantized_weight_dequant_amd import binding  # noqa: E402
+from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
+from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance,  # noqa: E402
+                         random_blocks, to_dev, weight_blob)
+
+GEMV = {"q4_0": binding.q4_gemv_q8a, "q8_0": binding.q8_gemv_q8a}
+
+
+def _ref(fmt):
+    return getattr(oracle, fmt + "_matmul_q8a")
+
+
+def _act_blob(seed, M, K):
+    return oracle.q8_0_quantize(wl.activations_f32(seed, M, K))
+
+
+def _run(fmt, a_q, blob, M, N, K, a_dev=None, w_dev=None):
+    y = Guarded(M * N, torch.float32)
+    GEMV[fmt](to_dev(a_q) if a_dev is None else a_dev, to_dev(blob) if w_dev is None else w_dev,
+              y.view, M, N, K)
+    torch.cuda.synchronize()
+    assert y.guards_intact()
+    return y.host().reshape(M, N)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (33, 8192), (129, 14336),
+                                 (50, 96), (17, 4128)])
+def test_q8a_shapes(fmt, M, N, K):
+    # K % 256 == 0 takes the streaming kernel (16- or 8-block chunks, one or
+    # several per wavefront, wavefronts without blocks); 96 and 4128 the
+    # general one. N ragged against the 16 columns of a workgroup.
+    blob = weight_blob(fmt, N, K, 19 * M + N)
+    a_q = _act_blob(23 * M + K, M, K)
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert_within_tolerance(_run(fmt, a_q, blob, M, N, K), ref, bound,
+                            "%s q8a %dx%dx%d" % (fmt, M, N, K))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("name", ["gemv_q8a_1x4096x4096", "gemv_q8a_8x4096x4096"])
+def test_q8a_workloads_with_the_device_quantizer(fmt, name):
+    # The whole chain on the device: q8_quantize of the f32 activations (bit
+    # for bit the oracle's blocks), then the product.
+    s = wl.WORKLOADS[name]
+    M, N, K = s["M"], s["N"], s["K"]
+    a = wl.activations_f32(s["a_seed"], M, K)
+    a_q_dev = torch.empty(M * K // 32 * 34, dtype=torch.uint8, device=DEV)
+    binding.q8_quantize(to_dev(a), a_q_dev)
+    torch.cuda.synchronize()
+    a_q = oracle.q8_0_quantize(a)
+    assert np.array_equal(a_q_dev.cpu().numpy(), a_q)
+    blob = weight_blob(fmt, N, K, s["w_seed"])
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert_within_tolerance(_run(fmt, a_q, blob, M, N, K, a_dev=a_q_dev), ref, bound, name)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [4096, 4128])
+def test_q8a_every_code_and_random_scales(fmt, K):
+    # Random bytes in both streams: every weight code, every activation code
+    # (-128 included), normal scales over a wide exponent range.
+    M, N = 7, 160
+    blob = random_blocks(fmt, N * K // 32, 51)
+    a_q = random_blocks("q8_0", M * K // 32, 52)
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert_within_tolerance(_run(fmt, a_q, blob, M, N, K), ref, bound, "random blocks")
+
+
+def _unit_scale(blob, block_bytes):
+    b = blob.reshape(-1, block_bytes).copy()
+    b[:, 0], b[:, 1] = 0x00, 0x3C            # d = 1.0
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [2048, 160])
+def test_q8a_integer_sums_are_exact(fmt, K):
+    # Unit scales in both streams: every output is an integer below 2^24 and
+    # must come out exactly.
+    M, N = 8, 48
+    blob = _unit_scale(random_blocks(fmt, N * K // 32, 53), 18 if fmt == "q4_0" else 34)
+    a_q = _unit_scale(random_blocks("q8_0", M * K // 32, 54), 34)
+    ref, _ = _ref(fmt)(a_q, M, blob, N, K)
+    got = _run(fmt, a_q, blob, M, N, K)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_q8a_extreme_scales(fmt):
+    # The largest and smallest binary16 scales (65504 and the subnormal
+    # 2^-24) on both sides: d_w d_a stays exact in f32.
+    M, N, K = 3, 40, 512
+    bb = 18 if fmt == "q4_0" else 34
+    blob = random_blocks(fmt, N * K // 32, 55).reshape(-1, bb).copy()
+    a_q = random_blocks("q8_0", M * K // 32, 56).reshape(-1, 34).copy()
+    for arr, pattern in ((blob, (0xFF, 0x7B)), (a_q, (0x01, 0x00))):
+        arr[::3, 0], arr[::3, 1] = pattern
+    blob[1::3, 0], blob[1::3, 1] = 0x01, 0x80                    # -2^-24
+    a_q[1::3, 0], a_q[1::3, 1] = 0xFF, 0xFB                      # -65504
+    blob, a_q = blob.reshape(-1), a_q.reshape(-1)
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert_within_tolerance(_run(fmt, a_q, blob, M, N, K), ref, bound, "extreme scales")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_q8a_repeats_bitwise_and_tracks_the_f32_product(fmt):
+    # Deterministic; and against the f32-activation product the quantization
+    # moves each output by at most sum_k |a - a'| |w| (plus both tolerances).
+    M, N, K = 4, 512, 4096
+    a = wl.activations_f32(57, M, K)
+    a_q = oracle.q8_0_quantize(a)
+    blob = weight_blob(fmt, N, K, 58)
+    w = to_dev(blob)
+    y1 = _run(fmt, a_q, blob, M, N, K, w_dev=w)
+    y2 = _run(fmt, a_q, blob, M, N, K, w_dev=w)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    y_f32, b_f32 = getattr(oracle, fmt + "_matmul")(a, blob, N, K)
+    _, b_q = _ref(fmt)(a_q, M, blob, N, K)
+    wd = getattr(oracle, fmt + "_dequant")(blob).reshape(N, K).astype(np.float64)
+    dq = np.abs(a.astype(np.float64) - oracle.q8_0_dequant(a_q).reshape(M, K)) @ np.abs(wd).T
+    assert (np.abs(y1 - y_f32) <= dq + oracle.tolerance(b_f32) + oracle.tolerance(b_q)).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_q8a_errors_write_nothing(fmt):
+    M, N, K = 2, 64, 512
+    y = torch.full((M * N,), 3.0, device=DEV)
+    a_q = to_dev(_act_blob(1, M, K))
+    w = to_dev(weight_blob(fmt, N, K, 2))
+    with pytest.raises(binding.Q4Error) as e:
+        GEMV[fmt](a_q, w, y, M, N, K, a_bytes=a_q.numel() - 34)
+    assert e.value.status == binding.Q4_ERR_SIZE
+    with pytest.raises(binding.Q4Error) as e:
+        GEMV[fmt](a_q, w, y, 9, N, K)
+    assert e.value.status == binding.Q4_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_q8a_graph_replays_match_eager(fmt):
+    M, N, K = 8, 1024, 4096
+    a = to_dev(wl.activations_f32(59, M, K))
+    a_q = torch.empty(M * K // 32 * 34, dtype=torch.uint8, device=DEV)
+    w = to_dev(weight_blob(fmt, N, K, 60))
+    y_eager = torch.empty(M * N, device=DEV)
+    binding.q8_quantize(a, a_q)
+    GEMV[fmt](a_q, w, y_eager, M, N, K)
+    torch.cuda.synchronize()
+    y = torch.empty(M * N, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.q8_quantize(a, a_q)
+        GEMV[fmt](a_q, w, y, M, N, K)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.q8_quantize(a, a_q)
+        GEMV[fmt](a_q, w, y, M, N, K)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        a_q.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), rep
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_q8a_empty_problems_are_no_ops(fmt):
+    bb = 18 if fmt == "q4_0" else 34
+    GEMV[fmt](None, None, None, 0, 16, 256, a_bytes=0, w_bytes=16 * 8 * bb)
+    GEMV[fmt](None, None, None, 3, 0, 256, a_bytes=3 * 8 * 34, w_bytes=0)

@@ -206,13 +206,19 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     R = copies_for_cold(wbytes) if cold else 1
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
     prep_us = quant_us = None
-    if s["kind"] == "gemv" and act == "q8_0":
+    if act == "q8_0":
         # The activations are quantized once, outside the timed region (its own
-        # time is quant_us); the GEMV reads the Q8_0 blocks.
+        # time is quant_us); the product reads the Q8_0 blocks.
         a_q = torch.empty(M * (K // 32) * 34, dtype=torch.uint8, device="cuda")
         q4.q8_quantize(a, a_q)
-        gemv = getattr(q4, f + "_gemv_q8a")
-        fn = lambda k: gemv(a_q, blobs[k % R], y, M, N, K)
+        if s["kind"] == "gemv":
+            gemv = getattr(q4, f + "_gemv_q8a")
+            fn = lambda k: gemv(a_q, blobs[k % R], y, M, N, K)
+        else:
+            gemm = getattr(q4, f + "_gemm_q8a")
+            ws = torch.empty(max(getattr(q4, f + "_gemm_q8a_workspace_bytes")(M, N, K), 16),
+                             dtype=torch.uint8, device="cuda")
+            fn = lambda k: gemm(a_q, blobs[k % R], y, M, N, K, workspace=ws)
         quant_us = run_timed(torch, lambda k: q4.q8_quantize(a, a_q), min(steps, 50), 5)["kernel_us"]
     elif s["kind"] == "gemv" and s.get("prepared"):
         prep = torch.empty(getattr(q4, f + "_gemv_prepare_bytes")(M, K), dtype=torch.uint8,
@@ -250,8 +256,8 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
            "job_TFLOPs": flops * steps / t["wall_s"] / 1e12}
     if quant_us is not None:
         row["quantize_us"] = quant_us
-        row["note"] = ("kernel_us is the GEMV over Q8_0 activation blocks alone; quantizing the "
-                       "f32 activations (q8_quantize, one more launch) takes quantize_us")
+        row["note"] = ("kernel_us is the product over Q8_0 activation blocks alone; quantizing "
+                       "the f32 activations (q8_quantize, one more launch) takes quantize_us")
     if prep_us is not None:
         row["prepare_us"] = prep_us
         row["note"] = ("kernel_us is the GEMV from prepared operands alone; preparing them "
@@ -265,7 +271,11 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
                                        "the kernel that adds the splits' partials")
     else:
         kernel = gemm_kernel_name(K, fmt, act)
-        if act == "bf16":
+        if act == "q8_0":
+            note = ("useful 2MNK flops over the dense f16 MFMA peak; the Q8_0 activations are "
+                    "split into two binary16 terms, so 0.5 is this design's ceiling; the time is "
+                    "the whole step (row-exponent and split kernels plus the GEMM kernel)")
+        elif act == "bf16":
             note = ("useful 2MNK flops over the dense f16 MFMA peak; one binary16 term per "
                     "bfloat16 activation, so 1.0 is this design's ceiling; the time is the "
                     "whole step (row-exponent and operand kernels plus the GEMM kernel)")
@@ -451,9 +461,12 @@ def main():
             log("row: %s" % name)
             rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
                                       min(args.warmup, 10)))
-        for name in ("gemv_q8a_1x4096x4096", "gemv_q8a_8x4096x4096", "q8_0_gemv_q8a_1x4096x4096"):
+        for name, st in (("gemv_q8a_1x4096x4096", args.steps), ("gemv_q8a_8x4096x4096", args.steps),
+                         ("q8_0_gemv_q8a_1x4096x4096", args.steps),
+                         ("gemm_q8a_1024x4096x4096", 50), ("gemm_q8a_2048x14336x4096", 20)):
             log("row: %s" % name)
-            rows.append(bench_product(torch, q4, wl, name, args.steps, min(args.warmup, 10)))
+            rows.append(bench_product(torch, q4, wl, name, min(st, args.steps),
+                                      min(args.warmup, 10)))
         log("row: Q8_0 dequant 14336x4096")
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10),
                                   "q8_0_dequant_14336x4096"))

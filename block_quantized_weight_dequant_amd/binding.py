@@ -36,7 +36,8 @@ EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_ge
            "q4_gemv_bf16", "q8_gemv_bf16", "q4_gemv_splitk", "q4_gemv_splitk_workspace_bytes",
            "q8_gemv_splitk", "q8_gemv_splitk_workspace_bytes", "q4_gemv_prepare_bytes",
            "q4_gemv_prepare", "q4_gemv_prepared", "q8_gemv_prepare_bytes", "q8_gemv_prepare",
-           "q8_gemv_prepared", "q4_gemv_q8a", "q8_gemv_q8a")
+           "q8_gemv_prepared", "q4_gemv_q8a", "q8_gemv_q8a", "q4_gemm_q8a",
+           "q4_gemm_q8a_workspace_bytes", "q8_gemm_q8a", "q8_gemm_q8a_workspace_bytes")
 
 
 class Q4Error(RuntimeError):
@@ -82,9 +83,15 @@ def _load_library():
         getattr(lib, f + "_gemv_prepare").argtypes = [P, i32, i32, P, sz, P]
         getattr(lib, f + "_gemv_prepared").restype = i32
         getattr(lib, f + "_gemv_prepared").argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
-    for name in ("q4_gemv_q8a", "q8_gemv_q8a"):
+    for name in ("q4_gemv_q8a", "q8_gemv_q8a", "q4_gemm_q8a",
+           "q4_gemm_q8a_workspace_bytes", "q8_gemm_q8a", "q8_gemm_q8a_workspace_bytes"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
+    for name in ("q4_gemm_q8a", "q8_gemm_q8a"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [P, sz, P, sz, P, i32, i32, i32, P, sz, P]
+        getattr(lib, name + "_workspace_bytes").restype = sz
+        getattr(lib, name + "_workspace_bytes").argtypes = [i32, i32, i32]
     for name in ("q8_quantize", "q4_quantize"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P]
@@ -232,6 +239,47 @@ def q8_gemv_q8a(a_q, w_q, y, M: int, N: int, K: int, a_bytes=None, w_bytes=None,
                 stream=None) -> None:
     """As q4_gemv_q8a over a Q8_0 weight stream."""
     _gemv_q8a("q8_gemv_q8a", a_q, w_q, y, M, N, K, a_bytes, w_bytes, stream)
+
+
+def q4_gemm_q8a_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q4_gemm_q8a_workspace_bytes(int(M), int(N), int(K)))
+
+
+def q8_gemm_q8a_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.q8_gemm_q8a_workspace_bytes(int(M), int(N), int(K)))
+
+
+def _gemm_q8a(entry, a_q, w_q, y, M, N, K, workspace, workspace_bytes, a_bytes, w_bytes,
+              stream) -> None:
+    ab = _nbytes(a_q) if a_bytes is None else int(a_bytes)
+    wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
+    ws = workspace
+    if ws is None:
+        need = int(getattr(lib, entry + "_workspace_bytes")(int(M), int(N), int(K)))
+        if 0 < need < SIZE_MAX:
+            ws = _scratch(need, stream, y)
+    if workspace_bytes is not None:
+        wsb = int(workspace_bytes)
+    else:
+        wsb = _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0
+    _check(getattr(lib, entry)(_addr(a_q), ab, _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
+                               _addr(ws), wsb, _stream(stream)), entry)
+
+
+def q4_gemm_q8a(a_q, w_q, y, M: int, N: int, K: int, workspace=None, workspace_bytes=None,
+                a_bytes=None, w_bytes=None, stream=None) -> None:
+    """y[M, N] = dequant(A_q[M, K/32]) @ dequant(W[N, K/32])^T for any M: activations
+    as Q8_0 blocks, W Q4_0. The workspace comes from PyTorch's allocator when
+    none is passed."""
+    _gemm_q8a("q4_gemm_q8a", a_q, w_q, y, M, N, K, workspace, workspace_bytes, a_bytes, w_bytes,
+              stream)
+
+
+def q8_gemm_q8a(a_q, w_q, y, M: int, N: int, K: int, workspace=None, workspace_bytes=None,
+                a_bytes=None, w_bytes=None, stream=None) -> None:
+    """As q4_gemm_q8a over a Q8_0 weight stream."""
+    _gemm_q8a("q8_gemm_q8a", a_q, w_q, y, M, N, K, workspace, workspace_bytes, a_bytes, w_bytes,
+              stream)
 
 
 def q4_gemv_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:

@@ -136,11 +136,30 @@ static int gemv_q8a(q4k::WeightFormat fmt, size_t block_bytes, const void *a_q, 
                     const void *w_q, size_t w_bytes, float *y, int M, int N, int K, void *stream)
 {
     bool empty = false;
-    int st = q4v::check_gemv_q8a(a_q, a_bytes, w_q, w_bytes, y, M, N, K, block_bytes, &empty);
+    int st = q4v::check_product_q8a(a_q, a_bytes, w_q, w_bytes, y, M, N, K, Q4_GEMV_MAX_ROWS,
+                                    block_bytes, &empty);
     if (st != Q4_OK || empty)
         return st;
     return launched(q4k::launch_gemv_q8a(fmt, static_cast<const uint8_t *>(a_q),
                                          static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                         as_stream(stream)));
+}
+
+static int gemm_q8a(q4k::WeightFormat fmt, size_t block_bytes, const void *a_q, size_t a_bytes,
+                    const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product_q8a(a_q, a_bytes, w_q, w_bytes, y, M, N, K, 0, block_bytes,
+                                    &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    st = q4v::check_workspace_span(q4v::gemm_q8a_workspace_bytes(M, N, K), a_q, a_bytes, w_q,
+                                   w_bytes, y, M, N, workspace, workspace_bytes);
+    if (st != Q4_OK)
+        return st;
+    return launched(q4k::launch_gemm_q8a(fmt, static_cast<const uint8_t *>(a_q),
+                                         static_cast<const uint8_t *>(w_q), y, M, N, K, workspace,
                                          as_stream(stream)));
 }
 
@@ -328,4 +347,30 @@ Q4_EXPORT int q8_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size
                           float *y, int M, int N, int K, void *stream)
 {
     return gemv_q8a(q4k::WeightFormat::kQ8_0, 34, a_q, a_bytes, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT size_t q4_gemm_q8a_workspace_bytes(int M, int N, int K)
+{
+    return q4v::gemm_q8a_workspace_bytes(M, N, K);
+}
+
+Q4_EXPORT size_t q8_gemm_q8a_workspace_bytes(int M, int N, int K)
+{
+    return q4v::gemm_q8a_workspace_bytes(M, N, K);
+}
+
+Q4_EXPORT int q4_gemm_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes,
+                          float *y, int M, int N, int K, void *workspace, size_t workspace_bytes,
+                          void *stream)
+{
+    return gemm_q8a(q4k::WeightFormat::kQ4_0, 18, a_q, a_bytes, w_q, w_bytes, y, M, N, K,
+                    workspace, workspace_bytes, stream);
+}
+
+Q4_EXPORT int q8_gemm_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes,
+                          float *y, int M, int N, int K, void *workspace, size_t workspace_bytes,
+                          void *stream)
+{
+    return gemm_q8a(q4k::WeightFormat::kQ8_0, 34, a_q, a_bytes, w_q, w_bytes, y, M, N, K,
+                    workspace, workspace_bytes, stream);
 }

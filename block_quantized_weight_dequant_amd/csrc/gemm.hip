@@ -337,7 +337,8 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("" ::: "memory");
 }
 
-// row_exp: per-row exponents of the bfloat16 form (HO), else unused.
+// row_exp: per-row exponents of the activation operands (always for the
+// bfloat16 form, HO; for the two-term form when not null).
 template <class F, bool HO>
 __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const u32x4 *__restrict__ ahl, const uint8_t *__restrict__ w, float *__restrict__ y, int M,
@@ -625,6 +626,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     if (kg == 0) {
         // Lane (li, g) of tile (ms, ns) holds rows 4g..4g+3 of column li.
         // Offsets are 32-bit (M N < 2^31 on this path, checked at launch).
+        // Rows of scaled activations (the bfloat16 form, or Q8_0 activations
+        // split with a row exponent) are scaled back by 2^-row_exp[m].
+        const bool scaled_rows = HO || row_exp != nullptr;
         const int mb = m0 + wm * 64 + 4 * g, nb = n0 + wn * 64 + li;
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
@@ -633,12 +637,12 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 const int m = mb + ms * 16 + q;
                 const uint32_t row_off = (uint32_t)m * (uint32_t)N + (uint32_t)nb;
                 int pe = 0;
-                if constexpr (HO)
-                    pe = m < M ? row_exp[m] : 0;
+                if (scaled_rows && m < M)
+                    pe = row_exp[m];
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns) {
                     float v = acc[ms][ns][q] + red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane];
-                    if constexpr (HO)
+                    if (scaled_rows)
                         v = ldexpf(v, -pe);
                     if (m < M && nb + ns * 16 < N)
                         y[row_off + ns * 16] = v;
@@ -869,6 +873,164 @@ hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *
     if (fmt == WeightFormat::kQ8_0)
         return launch_gemm_bf16_f<FmtQ8_0>(a, w, y, M, N, K, workspace, s);
     return launch_gemm_bf16_f<FmtQ4_0>(a, w, y, M, N, K, workspace, s);
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0-quantized activations (a_q: the [M, K/32] Q8_0 block stream, row m's
+// blocks contiguous in K order). A dequantized activation q d is an 8-bit code
+// times an 11-bit binary16 scale, exact in f32 with at most 18 significant
+// bits; the two-term split of the f32 path (hi = f16(v), lo = f16((v - hi)
+// 2^11)) holds any such value exactly while it stays inside binary16's range,
+// so the f32 GEMM kernels run unchanged on operands made from the blocks.
+// * Range: a Q8_0 block can hold up to 128 x 65504 in magnitude. Each row is
+//   scaled by the power of two 2^p that puts 128 max_b |d_b| (an upper bound
+//   of the row's magnitudes) in [2^14, 2^15), p = 7 - E for the largest |d| in
+//   [2^E, 2^(E+1)) (0 for an all-zero row). The scaled values stay below 2^15
+//   and the epilogue scales each result row back by 2^-p.
+// * k_row_exp_q8a: one wavefront per row, the largest |d| as the largest
+//   binary16 bit pattern with the sign cleared.
+// * k_gemm_split_a_q8: as k_gemm_split_a, from the blocks: code q, d 2^p, the
+//   product exact in f32, then the same split and operand order.
+// * Off the split path: k_q8a_to_f32 writes the scaled values as f32 for
+//   k_gemm_any (which takes the same row exponents).
+
+__global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_q8a(const uint8_t *__restrict__ aq,
+                                                                  int *__restrict__ row_exp, int M,
+                                                                  int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
+    if (m >= M)   // whole wavefronts only
+        return;
+    const int nblk = K >> 5;
+    const uint8_t *row = aq + (size_t)m * (size_t)nblk * kQ8Bytes;
+    uint32_t mx = 0;
+    for (int b = lane; b < nblk; b += 64)
+        mx = max(mx, load_u16(row + (size_t)b * kQ8Bytes) & 0x7FFFu);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    int p = 0;
+    if (mx != 0 && mx < 0x7C00u) {
+        const int ef = (int)(mx >> 10);
+        // Subnormal binary16 scales are (mantissa) 2^-24.
+        const int E = ef > 0 ? ef - 15 : (31 - __builtin_clz(mx)) - 24;
+        p = 7 - E;
+    }
+    if (lane == 0)
+        row_exp[m] = p;
+}
+
+// Signed byte i of a dword as f32.
+__device__ __forceinline__ float code_f32(uint32_t x, int i)
+{
+    return (float)(int8_t)(x >> (8 * i));
+}
+
+template <class F>
+__global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a_q8(const uint8_t *__restrict__ aq,
+                                                                    const int *__restrict__ row_exp,
+                                                                    u32x4 *__restrict__ ahl, int M,
+                                                                    int K, long long n_waves)
+{
+    const int lane = threadIdx.x & 63;
+    const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
+    if (gw >= n_waves)   // whole wavefronts only
+        return;
+    const int nblk = K >> 5;
+    const long long R = gw / nblk;                // 16-row group
+    const int kb = (int)(gw - R * nblk);
+    const int li = lane & 15, g = lane >> 4;
+    const long long m = R * 16 + li;
+    f16x8 hi = {}, lo = {};
+    if (m < M) {
+        const uint8_t *blk = aq + ((size_t)m * (size_t)nblk + (size_t)kb) * kQ8Bytes;
+        const float d = f16_bits_to_f32(load_u16(blk));
+        const int p = row_exp[m];
+        // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code (as in
+        // k_gemm_split_a): they carry a further 2^-kHiLog2.
+        const float sl = ldexpf(d, p), sh = ldexpf(d, p - F::kHiLog2);
+        const uint32_t cl = load_u32_unaligned(blk + 2 + F::a_lo(g));
+        const uint32_t ch = load_u32_unaligned(blk + 2 + F::a_hi(g));
+        const float e[8] = {code_f32(cl, 0) * sl, code_f32(cl, 2) * sl, code_f32(cl, 1) * sl,
+                            code_f32(cl, 3) * sl, code_f32(ch, 0) * sh, code_f32(ch, 2) * sh,
+                            code_f32(ch, 1) * sh, code_f32(ch, 3) * sh};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const f16 h = (f16)e[s];
+            hi[s] = h;
+            lo[s] = (f16)((e[s] - (float)h) * 2048.0f);
+        }
+    }
+    const long long mt = R >> 3;
+    const long long idx = (mt * nblk + kb) * kOpsPerBlockTile + (R & 7) * 64 + lane;
+    ahl[idx] = bitcast<u32x4>(hi);
+    ahl[idx + 8 * 64] = bitcast<u32x4>(lo);
+}
+
+__global__ __launch_bounds__(256) void k_q8a_to_f32(const uint8_t *__restrict__ aq,
+                                                   const int *__restrict__ row_exp,
+                                                   float4 *__restrict__ out, int K,
+                                                   long long n_quads)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_quads)
+        return;
+    const long long e = i * 4;                    // K % 32 == 0: a quad never straddles blocks
+    const long long m = e / K;
+    const int k = (int)(e - m * K);
+    const uint8_t *blk = aq + ((size_t)m * (size_t)(K >> 5) + (size_t)(k >> 5)) * kQ8Bytes;
+    const float s = ldexpf(f16_bits_to_f32(load_u16(blk)), row_exp[m]);
+    const uint32_t c = load_u32_unaligned(blk + 2 + (k & 31));
+    out[i] = make_float4(code_f32(c, 0) * s, code_f32(c, 1) * s, code_f32(c, 2) * s,
+                         code_f32(c, 3) * s);
+}
+
+template <class F>
+static hipError_t launch_gemm_q8a_f(const uint8_t *aq, const uint8_t *w, float *y, int M, int N,
+                                    int K, void *workspace, hipStream_t s)
+{
+    const int tiles_m = (M + kGemmBM - 1) / kGemmBM, tiles_n = (N + kGemmBN - 1) / kGemmBN;
+    const long long T = (long long)tiles_m * tiles_n;
+    if (T > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    int *row_exp = static_cast<int *>(workspace);
+    void *act = static_cast<char *>(workspace) + q4v::gemm_bf16_row_exp_bytes(M);
+    hipError_t e = launch_kernel(k_row_exp_q8a, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
+                                 dim3(64 * kRowExpWaves), 0, s, aq, row_exp, M, K);
+    if (e != hipSuccess)
+        return e;
+    if (!q4v::gemm_splits_activations(K) || (long long)M * N >= (1LL << 31)) {
+        const long long n_quads = (long long)M * K / 4;
+        const long long grid = (n_quads + 255) / 256;
+        if (grid > 0x7fffffffLL)
+            return hipErrorInvalidValue;
+        e = launch_kernel(k_q8a_to_f32, dim3((unsigned)grid), dim3(256), 0, s, aq,
+                          (const int *)row_exp, static_cast<float4 *>(act), K, n_quads);
+        if (e != hipSuccess)
+            return e;
+        return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s,
+                             (const float *)act, w, y, M, N, K, tiles_m, tiles_n,
+                             (const int *)row_exp);
+    }
+    const long long n_waves = (long long)tiles_m * 8 * (K / 32);
+    const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
+    if (split_grid > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    e = launch_kernel(k_gemm_split_a_q8<F>, dim3((unsigned)split_grid), dim3(64 * kSplitWaves), 0,
+                      s, aq, (const int *)row_exp, static_cast<u32x4 *>(act), M, K, n_waves);
+    if (e != hipSuccess)
+        return e;
+    return launch_kernel(k_gemm_split<F, false>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
+                         (const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n, (const int *)row_exp);
+}
+
+hipError_t launch_gemm_q8a(WeightFormat fmt, const uint8_t *a_q, const uint8_t *w, float *y, int M,
+                           int N, int K, void *workspace, hipStream_t s)
+{
+    if (fmt == WeightFormat::kQ8_0)
+        return launch_gemm_q8a_f<FmtQ8_0>(a_q, w, y, M, N, K, workspace, s);
+    return launch_gemm_q8a_f<FmtQ4_0>(a_q, w, y, M, N, K, workspace, s);
 }
 
 }  // namespace q4k

@@ -44,6 +44,10 @@ hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float
 // q4v::gemm_bf16_workspace_bytes(M, N, K) bytes (always used).
 hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,
                             int N, int K, void *workspace, hipStream_t s);
+// a_q: the [M, K/32] Q8_0 block stream of the activations. workspace:
+// q4v::gemm_q8a_workspace_bytes(M, N, K) bytes (always used).
+hipError_t launch_gemm_q8a(WeightFormat fmt, const uint8_t *a_q, const uint8_t *w, float *y, int M,
+                           int N, int K, void *workspace, hipStream_t s);
 hipError_t launch_q8_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
 hipError_t launch_q4_quantize(const float *x, size_t n_blocks, uint8_t *out, hipStream_t s);
 

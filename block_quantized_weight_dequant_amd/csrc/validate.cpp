@@ -72,11 +72,12 @@ int check_product(const void *a, size_t a_elem, const void *w, size_t w_bytes, c
     return Q4_OK;
 }
 
-int check_gemv_q8a(const void *a_q, size_t a_bytes, const void *w, size_t w_bytes, const float *y,
-                   int M, int N, int K, size_t block_bytes, bool *empty)
+int check_product_q8a(const void *a_q, size_t a_bytes, const void *w, size_t w_bytes,
+                      const float *y, int M, int N, int K, int max_rows, size_t block_bytes,
+                      bool *empty)
 {
     *empty = false;
-    if (M < 0 || M > Q4_GEMV_MAX_ROWS || N < 0 || K < 32 || K % 32 != 0)
+    if (M < 0 || N < 0 || K < 32 || K % 32 != 0 || (max_rows > 0 && M > max_rows))
         return Q4_ERR_SHAPE;
     size_t w_want = 0, a_want = 0, y_bytes = 0;
     if (!mul_ok((size_t)N, (size_t)(K / 32) * block_bytes, &w_want) || w_bytes != w_want)
@@ -214,8 +215,32 @@ size_t gemm_bf16_workspace_bytes(int M, int N, int K)
     return n > SIZE_MAX - r ? SIZE_MAX : n + r;
 }
 
+size_t gemm_q8a_workspace_bytes(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0)
+        return 0;
+    size_t n = 0;
+    if (gemm_splits_activations(K) && (long long)M * N < (1LL << 31)) {
+        // Rows padded to whole 128-row tiles, two binary16 terms per element.
+        const size_t mp = ((size_t)M + 127) / 128 * 128;
+        if (!mul_ok(mp, (size_t)K, &n) || !mul_ok(n, 4, &n))
+            return SIZE_MAX;
+    } else if (!mul_ok((size_t)M, (size_t)K, &n) || !mul_ok(n, 4, &n)) {
+        return SIZE_MAX;
+    }
+    const size_t r = gemm_bf16_row_exp_bytes(M);
+    return n > SIZE_MAX - r ? SIZE_MAX : n + r;
+}
+
 int check_workspace(size_t need, const void *a, size_t a_elem, const void *w, size_t w_bytes,
                     const float *y, int M, int N, int K, const void *ws, size_t ws_bytes)
+{
+    return check_workspace_span(need, a, (size_t)M * (size_t)K * a_elem, w, w_bytes, y, M, N, ws,
+                                ws_bytes);
+}
+
+int check_workspace_span(size_t need, const void *a, size_t a_bytes, const void *w, size_t w_bytes,
+                         const float *y, int M, int N, const void *ws, size_t ws_bytes)
 {
     if (need == 0)
         return Q4_OK;   // this shape takes no workspace; ws is not read
@@ -227,7 +252,6 @@ int check_workspace(size_t need, const void *a, size_t a_elem, const void *w, si
         return Q4_ERR_NULL;
     if (!aligned16(ws))
         return Q4_ERR_ALIGN;
-    const size_t a_bytes = (size_t)M * (size_t)K * a_elem;
     const size_t y_bytes = (size_t)M * (size_t)N * sizeof(float);
     if (overlaps({ws, need}, {a, a_bytes}) || overlaps({ws, need}, {w, w_bytes}) ||
         overlaps({ws, need}, {y, y_bytes}))

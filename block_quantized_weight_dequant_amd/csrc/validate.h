@@ -135,13 +135,24 @@ size_t gemm_bf16_workspace_bytes(int M, int N, int K);
 // then NULL, alignment and overlap with a (a_elem bytes per element), w and y.
 int check_workspace(size_t need, const void *a, size_t a_elem, const void *w, size_t w_bytes,
                     const float *y, int M, int N, int K, const void *ws, size_t ws_bytes);
+// The same with the activations' byte count given directly.
+int check_workspace_span(size_t need, const void *a, size_t a_bytes, const void *w, size_t w_bytes,
+                         const float *y, int M, int N, const void *ws, size_t ws_bytes);
 
-// The GEMV over Q8_0-quantized activations (q4_gemv_q8a / q8_gemv_q8a): a_q
-// is the [M, K/32] Q8_0 block stream of the activations, a_bytes ==
-// M (K/32) 34, then as check_product (1 <= M <= 8 rows; M == 0 or N == 0 is
-// empty).
-int check_gemv_q8a(const void *a_q, size_t a_bytes, const void *w, size_t w_bytes, const float *y,
-                   int M, int N, int K, size_t block_bytes, bool *empty);
+// The products over Q8_0-quantized activations (q4_gemv_q8a, q4_gemm_q8a and
+// the Q8_0-weight forms): a_q is the [M, K/32] Q8_0 block stream of the
+// activations, a_bytes == M (K/32) 34, then as check_product (at most
+// max_rows rows when max_rows > 0; M == 0 or N == 0 is empty).
+int check_product_q8a(const void *a_q, size_t a_bytes, const void *w, size_t w_bytes,
+                      const float *y, int M, int N, int K, int max_rows, size_t block_bytes,
+                      bool *empty);
+
+// Workspace bytes q4_gemm_q8a and q8_gemm_q8a need: the row exponents (as the
+// bfloat16 GEMM's), then the activations as the f32 GEMM's split operands on
+// its split path (ceil(M / 128) * 128 * K * 4 bytes) or as scaled f32 values
+// otherwise (M * K * 4). 0 for an empty or invalid shape, SIZE_MAX when it
+// does not fit.
+size_t gemm_q8a_workspace_bytes(int M, int N, int K);
 
 // Its streaming kernel's shapes: 16-byte aligned weight and activation rows
 // (K % 256 == 0) and byte offsets into W and a_q below 2^31. Other shapes take

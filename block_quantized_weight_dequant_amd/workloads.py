@@ -75,6 +75,10 @@ WORKLOADS = {
                                  a_seed=202),
     "q8_0_gemv_q8a_1x4096x4096": dict(kind="gemv", act="q8_0", fmt="q8_0", M=1, N=4096, K=4096,
                                       w_seed=200, a_seed=201),
+    "gemm_q8a_1024x4096x4096": dict(kind="gemm", act="q8_0", M=1024, N=4096, K=4096, w_seed=200,
+                                    a_seed=203),
+    "gemm_q8a_2048x14336x4096": dict(kind="gemm", act="q8_0", M=2048, N=14336, K=4096,
+                                     w_seed=400, a_seed=401),
 }
 
 WEIGHT_SIGMA = np.float32(0.02)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 7
+#define Q4_ABI_VERSION 8
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -325,6 +325,38 @@ int q4_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes
 /* q8_gemv_q8a — q4_gemv_q8a over a Q8_0 weight stream (w_bytes == N * (K/32) * 34). */
 int q8_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes, float *y,
                 int M, int N, int K, void *stream);
+
+/*
+ * q4_gemm_q8a — the prefill product over Q8_0-quantized activations, any
+ * M >= 1: y = dequant_q8_0(a_q) @ dequant(W)^T as q4_gemv_q8a (section
+ * matmul_q4_0_tiled for the product; the activation blocks as there).
+ *   a_q, a_bytes: the [M, K/32] Q8_0 block stream, a_bytes == M * (K/32) * 34.
+ *   w_q, w_bytes, y, M, N, K: as q4_gemm.
+ *   workspace, workspace_bytes: at least q4_gemm_q8a_workspace_bytes(M, N, K)
+ *             bytes of device scratch, 16-byte aligned, overlapping nothing
+ *             else (smaller: Q4_ERR_WORKSPACE); always used for M, N > 0.
+ * Each dequantized activation (an 8-bit code times a binary16 scale) is exact
+ * in f32; every row is scaled by the power of two that puts 128 times its
+ * largest |d| in [2^14, 2^15) and split into two binary16 terms, which hold
+ * it exactly, then multiplied as in q4_gemm and scaled back. Accuracy: as
+ * q4_gemv_q8a. Deterministic. Errors: as q4_gemm, with a_bytes checked like
+ * w_bytes.
+ */
+int q4_gemm_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes, float *y,
+                int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+
+/* q4_gemm_q8a_workspace_bytes — the row exponents (M int32, padded to 256
+ * bytes), then ceil(M/128) * 128 * K * 4 bytes of operands when K % 64 == 0,
+ * K <= 2^22 and M * N < 2^31, else M * K * 4; 0 for an empty or invalid shape,
+ * SIZE_MAX when it does not fit in size_t. */
+size_t q4_gemm_q8a_workspace_bytes(int M, int N, int K);
+
+/* q8_gemm_q8a — q4_gemm_q8a over a Q8_0 weight stream; the same workspace. */
+int q8_gemm_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes, float *y,
+                int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+
+/* q8_gemm_q8a_workspace_bytes — the same function as q4_gemm_q8a_workspace_bytes. */
+size_t q8_gemm_q8a_workspace_bytes(int M, int N, int K);
 
 /*
  * q8_quantize — f32 to Q8_0 blocks (section quantize_q8_0).

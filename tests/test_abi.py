@@ -378,3 +378,41 @@ def test_gemv_q8a_checks(f):
     assert st(A, ab(2, 256), W, wb, W + 32, 2, 4, 256) == S.Q4_ERR_ALIAS   # y inside w
     assert st(None, 0, None, wb, None, 0, 4, 256) == S.Q4_OK                # empty
     assert st(None, ab(3, 256), None, 0, None, 3, 0, 256) == S.Q4_OK
+
+
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemm_q8a_workspace_bytes(f):
+    ws = getattr(binding, f + "_gemm_q8a_workspace_bytes")
+    # Row exponents padded to 256 bytes, then two binary16 terms per element of
+    # whole 128-row tiles on the split path (K % 64 == 0), else M K f32.
+    assert ws(1024, 4096, 4096) == 4096 + 1024 * 4096 * 4
+    assert ws(1, 64, 4096) == 256 + 128 * 4096 * 4
+    assert ws(65, 64, 96) == 512 + 65 * 96 * 4
+    assert ws(2, 64, 1 << 23) == 256 + 2 * (1 << 23) * 4           # K > 2^22: general kernel
+    for M, N, K in [(0, 64, 4096), (1, 0, 4096), (1, 64, 48), (-1, 64, 4096)]:
+        assert ws(M, N, K) == 0, (M, N, K)
+
+
+@fake_addresses
+@pytest.mark.parametrize("f", ["q4", "q8"])
+def test_gemm_q8a_checks(f):
+    S = binding
+    M, N, K = 130, 4, 256
+    ab = M * (K // 32) * 34
+    wb = _wb(N, K, f)
+    need = getattr(binding, f + "_gemm_q8a_workspace_bytes")(M, N, K)
+    WS = BASE + (3 << 32)
+    st = lambda a, abn, y, m, ws, wsb: binding.raw_status(f + "_gemm_q8a", a, abn, W, wb, y, m, N,
+                                                          K, ws, wsb, 0)
+    assert st(A, ab - 1, Y, M, WS, need) == S.Q4_ERR_SIZE
+    assert st(A, M * K * 4, Y, M, WS, need) == S.Q4_ERR_SIZE            # f32 length
+    assert st(A, ab, Y, -1, WS, need) == S.Q4_ERR_SHAPE
+    assert st(None, ab, Y, M, WS, need) == S.Q4_ERR_NULL
+    assert st(A + 2, ab, Y, M, WS, need) == S.Q4_ERR_ALIGN
+    assert st(A, ab, A + 32, M, WS, need) == S.Q4_ERR_ALIAS              # y inside a_q
+    assert st(A, ab, Y, M, WS, need - 1) == S.Q4_ERR_WORKSPACE
+    assert st(A, ab, Y, M, None, need) == S.Q4_ERR_NULL
+    assert st(A, ab, Y, M, WS + 8, need) == S.Q4_ERR_ALIGN
+    assert st(A, ab, Y, M, A + 16, need) == S.Q4_ERR_ALIAS               # workspace over a_q
+    assert st(A, ab, Y, M, Y, need) == S.Q4_ERR_ALIAS                    # workspace over y
+    assert st(None, 0, None, 0, None, 0) == S.Q4_OK                      # empty

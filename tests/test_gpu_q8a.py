@@ -193,3 +193,154 @@ def test_q8a_empty_problems_are_no_ops(fmt):
     bb = 18 if fmt == "q4_0" else 34
     GEMV[fmt](None, None, None, 0, 16, 256, a_bytes=0, w_bytes=16 * 8 * bb)
     GEMV[fmt](None, None, None, 3, 0, 256, a_bytes=3 * 8 * 34, w_bytes=0)
+
+
+# ---------------------------------------------------------------- GEMM
+
+GEMM = {"q4_0": binding.q4_gemm_q8a, "q8_0": binding.q8_gemm_q8a}
+GEMM_WS = {"q4_0": binding.q4_gemm_q8a_workspace_bytes,
+           "q8_0": binding.q8_gemm_q8a_workspace_bytes}
+
+
+def _run_gemm(fmt, a_q, blob, M, N, K, a_dev=None, w_dev=None, workspace=None):
+    y = Guarded(M * N, torch.float32)
+    GEMM[fmt](to_dev(a_q) if a_dev is None else a_dev, to_dev(blob) if w_dev is None else w_dev,
+              y.view, M, N, K, workspace=workspace)
+    torch.cuda.synchronize()
+    assert y.guards_intact()
+    return y.host().reshape(M, N)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (130, 300, 256), (257, 129, 1024),
+                                   (128, 128, 8192), (64, 200, 96), (33, 70, 4128),
+                                   (5, 17, 32)])
+def test_gemm_q8a_shapes(fmt, M, N, K):
+    # K % 64 == 0 takes the split path (several 128 x 128 tiles, ragged M and
+    # N); 96, 4128 and 32 the general kernel.
+    blob = weight_blob(fmt, N, K, 29 * M + N)
+    a_q = _act_blob(31 * M + K, M, K)
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert_within_tolerance(_run_gemm(fmt, a_q, blob, M, N, K), ref, bound,
+                            "%s gemm q8a %dx%dx%d" % (fmt, M, N, K))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_q8a_prefill_shape_sampled(fmt):
+    # The 1024 x 4096 x 4096 prefill with the device quantizer, checked at
+    # sampled outputs (every row group and column tile is hit).
+    M, N, K = 1024, 4096, 4096
+    a = wl.activations_f32(203, M, K)
+    a_q_dev = torch.empty(M * K // 32 * 34, dtype=torch.uint8, device=DEV)
+    binding.q8_quantize(to_dev(a), a_q_dev)
+    torch.cuda.synchronize()
+    a_q = oracle.q8_0_quantize(a)
+    assert np.array_equal(a_q_dev.cpu().numpy(), a_q)
+    blob = weight_blob(fmt, N, K, 200)
+    got = _run_gemm(fmt, a_q, blob, M, N, K, a_dev=a_q_dev)
+    mi = np.concatenate([np.arange(M), wl.uniform_ints(61, 0, M, 1000)])
+    ni = np.concatenate([(np.arange(M) * 37) % N, wl.uniform_ints(62, 0, N, 1000)])
+    ref, bound = getattr(oracle, fmt + "_matmul_q8a_sampled")(a_q, M, blob, N, K, mi, ni)
+    assert_within_tolerance(got[mi, ni], ref, bound, "prefill sampled")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [1024, 160])
+def test_gemm_q8a_every_code_and_scale_range(fmt, K):
+    # Random bytes in both streams, then rows whose scales reach binary16's
+    # extremes (65504: row exponent -8; the subnormal 2^-24: +31) and an
+    # all-zero row.
+    M, N = 140, 72
+    blob = random_blocks(fmt, N * K // 32, 63)
+    a_q = random_blocks("q8_0", M * K // 32, 64).reshape(M, K // 32, 34).copy()
+    a_q[3, :, 0], a_q[3, :, 1] = 0xFF, 0x7B                    # 65504
+    a_q[4, :, 0], a_q[4, :, 1] = 0x01, 0x00                    # 2^-24
+    a_q[5, ::2, 0], a_q[5, ::2, 1] = 0xFF, 0xFB                # -65504 next to
+    a_q[5, 1::2, 0], a_q[5, 1::2, 1] = 0x01, 0x80              # -2^-24
+    a_q[6, :, :] = 0                                           # all zero
+    a_q = a_q.reshape(-1)
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    got = _run_gemm(fmt, a_q, blob, M, N, K)
+    assert_within_tolerance(got, ref, bound, "scale range")
+    assert (got[6] == 0).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [512, 96])
+def test_gemm_q8a_integer_sums_are_exact(fmt, K):
+    # Unit scales: every output is an integer below 2^23 and must be exact.
+    M, N = 136, 40
+    blob = _unit_scale(random_blocks(fmt, N * K // 32, 65), 18 if fmt == "q4_0" else 34)
+    a_q = _unit_scale(random_blocks("q8_0", M * K // 32, 66), 34)
+    ref, _ = _ref(fmt)(a_q, M, blob, N, K)
+    got = _run_gemm(fmt, a_q, blob, M, N, K)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_q8a_rows_match_the_gemv(fmt):
+    # The GEMM's rows and the GEMV on the same rows: both within tolerance of
+    # the oracle, hence within twice of each other; repeated calls bit-equal.
+    M, N, K = 8, 384, 4096
+    blob = weight_blob(fmt, N, K, 67)
+    a_q = _act_blob(68, M, K)
+    w = to_dev(blob)
+    g1 = _run_gemm(fmt, a_q, blob, M, N, K, w_dev=w)
+    g2 = _run_gemm(fmt, a_q, blob, M, N, K, w_dev=w)
+    assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+    v = _run(fmt, a_q, blob, M, N, K, w_dev=w)
+    _, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert (np.abs(g1.astype(np.float64) - v) <= 2 * oracle.tolerance(bound)).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_q8a_exact_workspace_and_errors(fmt):
+    M, N, K = 130, 64, 1024
+    need = GEMM_WS[fmt](M, N, K)
+    ws = Guarded(need, torch.uint8)
+    ws.view.fill_(0x7F)
+    blob = weight_blob(fmt, N, K, 69)
+    a_q = _act_blob(70, M, K)
+    ref, bound = _ref(fmt)(a_q, M, blob, N, K)
+    assert_within_tolerance(_run_gemm(fmt, a_q, blob, M, N, K, workspace=ws.view), ref, bound,
+                            "exact workspace")
+    assert ws.guards_intact()
+    y = torch.full((M * N,), 3.0, device=DEV)
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(binding.Q4Error) as e:
+        GEMM[fmt](to_dev(a_q), to_dev(blob), y, M, N, K, workspace=small)
+    assert e.value.status == binding.Q4_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_q8a_graph_replays_match_eager(fmt):
+    M, N, K = 256, 512, 2048
+    a = to_dev(wl.activations_f32(71, M, K))
+    a_q = torch.empty(M * K // 32 * 34, dtype=torch.uint8, device=DEV)
+    w = to_dev(weight_blob(fmt, N, K, 72))
+    ws = torch.empty(GEMM_WS[fmt](M, N, K), dtype=torch.uint8, device=DEV)
+    y_eager = torch.empty(M * N, device=DEV)
+    binding.q8_quantize(a, a_q)
+    GEMM[fmt](a_q, w, y_eager, M, N, K, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty(M * N, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.q8_quantize(a, a_q)
+        GEMM[fmt](a_q, w, y, M, N, K, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.q8_quantize(a, a_q)
+        GEMM[fmt](a_q, w, y, M, N, K, workspace=ws)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), rep

@@ -153,6 +153,14 @@ def make_weight(torch, q4, wl, N, K, seed, fmt="q4_0"):
     return blob
 
 
+def digest(x) -> str:
+    """SHA-256 of a generated input's bytes (a device tensor or a numpy array), so
+    that the inputs behind a figure can be compared across runs and machines."""
+    if hasattr(x, "cpu"):
+        x = x.cpu().numpy()
+    return hashlib.sha256(x.tobytes()).hexdigest()
+
+
 def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=False):
     """The kernel the library launches (mirrors launch_gemv_m, launch_gemv_q8a_m and
     gemv_split_plan)."""
@@ -248,7 +256,7 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
     flops = 2.0 * M * N * K
     kern_s = t["kernel_us"] * 1e-6
     row = {"workload": name, "format": fmt, "activations": act, "M": M, "N": N, "K": K,
-           "weight_copies": R,
+           "weight_sha256": digest(blob), "activation_sha256": digest(a), "weight_copies": R,
            "cache": "cold" if R > 1 else "warm (one weight copy, MALL-resident)",
            "algorithmic_bytes": algo_bytes, "flops": flops, **t,
            "kernel_GBs": algo_bytes / kern_s / 1e9, "kernel_TFLOPs": flops / kern_s / 1e12,
@@ -307,7 +315,7 @@ def bench_dequant(torch, q4, wl, steps, warmup, name="dequant_14336x4096"):
     algo = blob.numel() + N * K * 4
     kern_s = t["kernel_us"] * 1e-6
     kernel = "k_dequant<%s>" % FMT_TYPE[fmt]
-    row = {"workload": name, "format": fmt, "kernel": kernel,
+    row = {"workload": name, "format": fmt, "kernel": kernel, "weight_sha256": digest(blob),
            "cache": "cold (%d MB per call)" % round(algo / 1e6), "algorithmic_bytes": algo, **t,
            "kernel_GBs": algo / kern_s / 1e9, "job_GBs": algo * steps / t["wall_s"] / 1e9}
     row["roofline"] = hbm_roofline(algo, t["kernel_us"], name, kernel, "dequant")
@@ -328,6 +336,7 @@ def bench_quantize(torch, q4, wl, steps, warmup):
     algo = n * 4 + n // 32 * 34
     kern_s = t["kernel_us"] * 1e-6
     row = {"workload": "quantize_2048x4096", "kernel": "k_quantize_q8_0", "input_copies": R,
+           "input_sha256": digest(x),
            "cache": "cold", "algorithmic_bytes": algo, **t, "kernel_GBs": algo / kern_s / 1e9,
            "job_GBs": algo * steps / t["wall_s"] / 1e9}
     row["roofline"] = hbm_roofline(algo, t["kernel_us"], "quantize_2048x4096", "k_quantize_q8_0",
@@ -397,9 +406,17 @@ def cpu_baseline(wl, seconds):
         reps += 1
     el = time.perf_counter() - t0
     algo = blob.size + M * K * 4 + M * N * 4
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": algo * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "%d full 1x4096x4096 decode GEMVs in %.1f s (%.2f ms each), f64 sums"
-                      % (reps, el, 1e3 * el / reps)}
+                      % (reps, el, 1e3 * el / reps),
+            "host": {"cpu_model": model, "logical_cpus": os.cpu_count(),
+                     "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}}
 
 
 # -------------------------------------------------------------------- main

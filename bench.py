@@ -451,6 +451,7 @@ def main():
         warm = bench_product(torch, q4, wl, "gemv_1x4096x4096", args.steps, args.warmup,
                              cold=False)
         warm["workload"] = "gemv_1x4096x4096_warm"
+        warm["roofline"]["traffic"] = None   # the counters were taken on the cold row
         rows.append(warm)
         log("row: dequant 14336x4096")
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10)))

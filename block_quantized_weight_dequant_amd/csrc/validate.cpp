@@ -125,7 +125,10 @@ int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_b
 
 size_t gemm_workspace_bytes(int M, int N, int K)
 {
-    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0 || !gemm_splits_activations(K))
+    // The split path also needs M N < 2^31 (its 32-bit output offsets); larger
+    // outputs take the general kernel, which needs no workspace.
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0 || !gemm_splits_activations(K) ||
+        (long long)M * N >= (1LL << 31))
         return 0;
     // Rows are padded to whole 128-row tiles; hi and lo binary16 per element.
     size_t mp = ((size_t)M + 127) / 128 * 128, n = 0;

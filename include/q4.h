@@ -100,7 +100,7 @@ int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
  *             q4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, not
  *             overlapping a, W or y, and not used by other work while this
  *             call runs on `stream`. When that function returns 0 (K % 64 != 0,
- *             K > 2^22 or an empty problem) the workspace is not read or
+ *             K > 2^22, M * N >= 2^31 or an empty problem) the workspace is not read or
  *             written and may be NULL. Errors, after those of q4_gemv's checks:
  *             Q4_ERR_SIZE if the needed size overflows size_t,
  *             Q4_ERR_WORKSPACE if workspace_bytes is smaller, then
@@ -114,7 +114,7 @@ int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
 
 /*
  * q4_gemm_workspace_bytes — bytes of workspace q4_gemm needs for this shape:
- * ceil(M / 128) * 128 * K * 4 when K % 64 == 0 and K <= 2^22 (the
+ * ceil(M / 128) * 128 * K * 4 when K % 64 == 0, K <= 2^22 and M * N < 2^31 (the
  * activations split once into binary16 hi and lo terms, in matrix-core
  * operand order), 0 otherwise or
  * when M, N or K is invalid or the problem is empty, and SIZE_MAX when the

@@ -210,8 +210,11 @@ def test_gemm_workspace_bytes(fn):
     assert f(129, 7, 4096) == 256 * 4096 * 4
     assert f(1024, 4096, 4096) == 1024 * 4096 * 4
     assert f(2 ** 31 - 1, 1, 2 ** 22) == 2 ** 31 * 2 ** 22 * 4
-    # No split path (K % 64 != 0, or K > 2^22), empty or invalid shapes: no workspace.
+    assert f(65536, 32767, 64) == 65536 * 64 * 4
+    # No split path (K % 64 != 0, K > 2^22, or M N >= 2^31: the general kernel),
+    # empty or invalid shapes: no workspace.
     for M, N, K in [(5, 5, 96), (5, 5, 32), (5, 5, 4128), (5, 5, 2 ** 22 + 64), (5, 5, 2 ** 31 - 64),
+                    (65536, 32768, 64), (2 ** 31 - 1, 2, 64),
                     (0, 5, 64), (5, 0, 64), (-1, 5, 64),
                     (5, -1, 64), (5, 5, 48), (5, 5, 0), (5, 5, -64)]:
         assert f(M, N, K) == 0, (M, N, K)

@@ -1,0 +1,58 @@
+"""The GEMMs at the largest output this library addresses with 32-bit offsets
+and beyond: M N = 2^31 f32 outputs (8 GiB) take the general kernel, whose
+offsets are 64-bit. Every output must be written (NaN prefill, all finite
+after the call) and sampled outputs, the last row and column included, must
+meet the products' bar against the oracle (section matmul_q4_0_tiled of
+"fuel-vulkan-kernels — quantized (GGML) kernel contracts"; bfloat16 and Q8_0
+activations as in their own tests)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from block_quantized_weight_dequant_amd import binding  # noqa: E402
+from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
+from gpu_helpers import DEV, assert_within_tolerance, to_dev, weight_blob  # noqa: E402
+
+M, N, K = 65536, 32768, 64        # M N = 2^31
+
+
+def _samples():
+    mi = np.concatenate([[0, M - 1, M - 1, 32767, 32768], wl.uniform_ints(81, 0, M, 400)])
+    ni = np.concatenate([[0, N - 1, 0, N - 1, 1], wl.uniform_ints(82, 0, N, 400)])
+    return mi.astype(np.int64), ni.astype(np.int64)
+
+
+def _gathered(y, mi, ni):
+    idx = torch.from_numpy(mi * N + ni).to(DEV)
+    return y[idx].cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "q8_0"])
+def test_gemm_output_of_2_31_elements(act):
+    assert binding.q4_gemm_workspace_bytes(M, N, K) == 0
+    blob = weight_blob("q4_0", N, K, 83)
+    a32 = wl.activations_f32(84, M, K)
+    y = torch.full((M * N,), float("nan"), dtype=torch.float32, device=DEV)
+    mi, ni = _samples()
+    if act == "f32":
+        binding.q4_gemm(to_dev(a32), to_dev(blob), y, M, N, K)
+        ref, bound = oracle.q4_0_matmul_sampled(a32, blob, N, K, mi, ni)
+    elif act == "bf16":
+        bits = wl.activations_bf16(84, M, K)
+        binding.q4_gemm_bf16(to_dev(bits.view(np.int16)), to_dev(blob), y, M, N, K)
+        ref, bound = oracle.q4_0_matmul_sampled(oracle.bf16_to_f32(bits), blob, N, K, mi, ni)
+    else:
+        a_q = oracle.q8_0_quantize(a32)
+        binding.q4_gemm_q8a(to_dev(a_q), to_dev(blob), y, M, N, K)
+        ref, bound = oracle.q4_0_matmul_q8a_sampled(a_q, M, blob, N, K, mi, ni)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    assert_within_tolerance(_gathered(y, mi, ni), ref, bound, "%s %dx%dx%d" % (act, M, N, K))
+    del y
+    torch.cuda.empty_cache()

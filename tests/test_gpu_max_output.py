@@ -1,6 +1,6 @@
-"""The GEMMs at the largest output this library addresses with 32-bit offsets
-and beyond: M N = 2^31 f32 outputs (8 GiB) take the general kernel, whose
-offsets are 64-bit. Every output must be written (NaN prefill, all finite
+"""Shapes past the 32-bit offsets of the fast kernels: GEMMs with M N = 2^31
+f32 outputs (8 GiB) and GEMVs over more than 2^31 weight bytes take the
+general kernels, whose offsets are 64-bit. Every output must be written (NaN prefill, all finite
 after the call) and sampled outputs, the last row and column included, must
 meet the products' bar against the oracle (section matmul_q4_0_tiled of
 "fuel-vulkan-kernels — quantized (GGML) kernel contracts"; bfloat16 and Q8_0
@@ -55,4 +55,36 @@ def test_gemm_output_of_2_31_elements(act):
     assert bool(torch.isfinite(y).all())
     assert_within_tolerance(_gathered(y, mi, ni), ref, bound, "%s %dx%dx%d" % (act, M, N, K))
     del y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "q8_0"])
+def test_gemv_over_weights_beyond_2_31_bytes(act):
+    # N (K/32) 18 > 2^31 bytes: the GEMVs take their general kernels (64-bit
+    # row offsets). Random blocks (every code, normal scales) keep the setup cheap.
+    from gpu_helpers import random_blocks
+    Mv, Nv, Kv = 2, (1 << 20) + 16, 4096
+    blob = random_blocks("q4_0", Nv * (Kv // 32), 85)
+    assert blob.size > 2 ** 31
+    w = to_dev(blob)
+    a32 = wl.activations_f32(86, Mv, Kv)
+    y = torch.full((Mv * Nv,), float("nan"), dtype=torch.float32, device=DEV)
+    mi = np.concatenate([[0, 1, 1, 0], wl.uniform_ints(87, 0, Mv, 300)]).astype(np.int64)
+    ni = np.concatenate([[0, Nv - 1, Nv - 16, Nv - 17], wl.uniform_ints(88, 0, Nv, 300)]).astype(np.int64)
+    if act == "f32":
+        binding.q4_gemv(to_dev(a32), w, y, Mv, Nv, Kv)
+        ref, bound = oracle.q4_0_matmul_sampled(a32, blob, Nv, Kv, mi, ni)
+    elif act == "bf16":
+        bits = wl.activations_bf16(86, Mv, Kv)
+        binding.q4_gemv_bf16(to_dev(bits.view(np.int16)), w, y, Mv, Nv, Kv)
+        ref, bound = oracle.q4_0_matmul_sampled(oracle.bf16_to_f32(bits), blob, Nv, Kv, mi, ni)
+    else:
+        a_q = oracle.q8_0_quantize(a32)
+        binding.q4_gemv_q8a(to_dev(a_q), w, y, Mv, Nv, Kv)
+        ref, bound = oracle.q4_0_matmul_q8a_sampled(a_q, Mv, blob, Nv, Kv, mi, ni)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    got = y[torch.from_numpy(mi * Nv + ni).to(DEV)].cpu().numpy().astype(np.float64)
+    assert_within_tolerance(got, ref, bound, "%s gemv %dx%dx%d" % (act, Mv, Nv, Kv))
+    del y, w
     torch.cuda.empty_cache()

@@ -457,6 +457,11 @@ def main():
         rows.append(bench_dequant(torch, q4, wl, min(50, args.steps), min(args.warmup, 10)))
         log("row: Q8_0 quantize 2048x4096")
         rows.append(bench_quantize(torch, q4, wl, args.steps, args.warmup))
+        # The tiny correctness configuration: 74 KB of weights, launch-dominated
+        # (one weight copy; at this size the timed launches stay MALL-resident).
+        log("row: gemv_1x256x512 (launch-dominated)")
+        rows.append(bench_product(torch, q4, wl, "gemv_1x256x512", args.steps, args.warmup,
+                                  cold=False))
         # The same path over Q8_0 weights.
         for name, st in (("q8_0_gemv_1x4096x4096", args.steps),
                          ("q8_0_gemv_8x4096x4096", args.steps),

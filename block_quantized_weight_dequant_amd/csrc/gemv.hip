@@ -1142,7 +1142,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
             });
 #pragma unroll
             for (int u = 0; u < B1 - B0; ++u) {
-                const f32x4 da = *reinterpret_cast<const f32x4 *>(da_lane + (B0 + u) * 8);
+                // Only the NACC scales this lane uses: whole 16-byte reads of the
+                // table would be hoisted for every block of the chunk and hold
+                // 64 VGPRs at M = 1.
+                float da[NACC];
+#pragma unroll
+                for (int r = 0; r < NACC; ++r)
+                    da[r] = da_lane[(B0 + u) * 8 + r];
 #pragma unroll
                 for (int r = 0; r < NACC; ++r)
                     acc[r] = fmaf(dw[u] * da[r], (float)Dv[u][r], acc[r]);
@@ -1265,7 +1271,11 @@ static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *
     const unsigned grid = (unsigned)((N + 15) / 16);
     if (q4v::gemv_q8a_streams(M, N, K, F::kBytes)) {
         const int nblk = K / 32;
-        if (q4v::gemv_chunk_blocks(nblk, nblk) == 16)
+        // 16-block chunks, except where there are more workgroups than compute
+        // units and M > 1: those kernels need more than 128 VGPRs, so one
+        // workgroup holds a compute unit, while the 8-block ones (under 100)
+        // let two or more share it and overlap one's loads with another's work.
+        if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && (grid <= 256 || M == 1))
             return launch_kernel(k_gemv_q8a<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s, aq, w,
                                  y, N, K);
         return launch_kernel(k_gemv_q8a<F, M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, aq, w, y,

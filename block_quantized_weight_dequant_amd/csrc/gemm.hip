@@ -345,6 +345,11 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     int N, int K, int tiles_m, int tiles_n, const int *__restrict__ row_exp)
 {
     using G = PairGeom<F>;
+    // MFMA tiles per wavefront: the hi-only form takes 128 rows x 32 columns
+    // (8 x 2), so no two wavefronts of a K group decode the same weight
+    // columns; the two-term form keeps 64 x 64 (4 x 4), which leaves room for
+    // its lo operands in registers.
+    constexpr int RM = HO ? 8 : 4, CN = HO ? 2 : 4;
     constexpr int SO = slab_ops<HO>();           // A operands per (tile, block)
     constexpr int NA = 2 * SO / (8 * 64);         // A loads (1 KB each) per wavefront per pair
     constexpr int NB = G::kBLoads, NL = NA + NB;
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const int tid = threadIdx.x, lane = tid & 63;
     // The wavefront index, made visibly uniform so that branches on it are scalar.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kg = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+    const int kg = wave >> 2, wm = HO ? 0 : (wave >> 1) & 1, wn = HO ? (wave & 3) : (wave & 1);
     const int li = lane & 15, g = lane >> 4;
     const int nblk = K >> 5, npairs = nblk >> 1;
     const uint32_t magic_v = magic_vgpr<F>();
@@ -402,11 +407,11 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 4, b_voff[k - NA], pb * (2 * F::kBytes), 0, 0);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[RM][CN];
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int ms = 0; ms < RM; ++ms)
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
+        for (int ns = 0; ns < CN; ++ns)
             acc[ms][ns] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const f16 sc = (f16)0x1p-11f;
@@ -423,25 +428,30 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             uint32_t dw;
         };
         auto read_b = [&](const uint32_t *bstage, int ns) __attribute__((always_inline)) {
-            const uint32_t *rb = bstage + (wn * 64 + ns * 16 + li) * G::kDwords;
+            const uint32_t *rb = bstage + (wn * (CN * 16) + ns * 16 + li) * G::kDwords;
             return BCol{read_qs_raw<F, KG>(rb, g), rb[d_dword<F, KG>()]};
         };
         // The operands of one pair held in registers: the A operands of the
-        // wavefront's four row groups and the raw B bytes of its four column
+        // wavefront's RM row groups and the raw B bytes of its CN column
         // groups.
         struct Ops {
-            f16x8 hi[4], lo[HO ? 1 : 4];
-            BCol b[4];
+            f16x8 hi[RM], lo[HO ? 1 : RM];
+            BCol b[CN];
         };
-        // Part i of pair q's operands (row group i, column group i).
+        // Part i of pair q's operands (row groups i RM/CN .. (i+1) RM/CN - 1,
+        // column group i).
         auto read_ops = [&](int q, Ops &o, int i) __attribute__((always_inline)) {
-            const u32x4 *ap = lds.a[q % DA] + KG * SO + wm * 4 * 64 + lane;
-            o.hi[i] = bitcast<f16x8>(ap[i * 64]);
-            if constexpr (!HO)
-                o.lo[i] = bitcast<f16x8>(ap[8 * 64 + i * 64]);
+            const u32x4 *ap = lds.a[q % DA] + KG * SO + wm * RM * 64 + lane;
+#pragma unroll
+            for (int r = i * (RM / CN); r < (i + 1) * (RM / CN); ++r) {
+                o.hi[r] = bitcast<f16x8>(ap[r * 64]);
+                if constexpr (!HO)
+                    o.lo[r] = bitcast<f16x8>(ap[8 * 64 + r * 64]);
+            }
             o.b[i] = read_b(lds.b[q % DB], i);
         };
-        constexpr int kDsReads = (HO ? 1 : 2) + QsRaw<F, KG>::n + 1;   // LDS reads of one part
+        // LDS reads of one part.
+        constexpr int kDsReads = (RM / CN) * (HO ? 1 : 2) + QsRaw<F, KG>::n + 1;
 
         // Software pipeline over the four column groups of a pair: the MFMAs of
         // group ns are issued between the scale FMAs of group ns - 1 (whose results
@@ -449,12 +459,12 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         // between two register sets by the parity of ns, and the group before
         // group 0 is group 3 of the previous pair (zeros before the first pair),
         // so every index is a compile-time constant.
-        f32x4 cbuf[2][4];
+        f32x4 cbuf[2][RM];
         float dbuf[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+            for (int ms = 0; ms < RM; ++ms)
                 cbuf[h][ms] = zero4;
         struct BOps {
             f16x8 q, s;   // the codes (x 2^kHiLog2 in slots 4..7) and the same times 2^-11
@@ -483,12 +493,12 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             BOps cur = decode_b(cur_ops.b[0]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
+            for (int ns = 0; ns < CN; ++ns) {
                 f32x4 *c = cbuf[ns & 1];
-                const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod 4)
+                const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod CN; CN is even)
                 const float dp = dbuf[(ns + 1) & 1];
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
+                for (int ms = 0; ms < RM; ++ms)
                     c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.hi[ms], cur.q, zero4, 0, 0, 0);
                 read_ops(next_pair, next_ops, ns);
                 // The step's loads go out spread over the four regions (loads
@@ -498,34 +508,38 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 // so they follow this region's LDS reads in program order (the
                 // compiler keeps LDS accesses it cannot tell apart in order).
 #pragma unroll
-                for (int k = (NL * ns + 3) / 4; k < (NL * (ns + 1) + 3) / 4; ++k)
+                for (int k = (NL * ns + CN - 1) / CN; k < (NL * (ns + 1) + CN - 1) / CN; ++k)
                     issue_load(dma_a, dma_b, k);
-                const int np = (ns + 3) & 3;
+                const int np = (ns + CN - 1) % CN;
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
+                for (int ms = 0; ms < RM; ++ms)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         acc[ms][np][q] = fmaf(dp, cp[ms][q], acc[ms][np][q]);
                 // Pin these FMAs to this region: IR passes would otherwise sink
                 // them past the scheduling barriers, to the end of the pair.
-                asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]));
+                if constexpr (RM == 4)
+                    asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]));
+                else
+                    asm volatile("" : "+v"(acc[0][np]), "+v"(acc[1][np]), "+v"(acc[2][np]), "+v"(acc[3][np]),
+                                      "+v"(acc[4][np]), "+v"(acc[5][np]), "+v"(acc[6][np]), "+v"(acc[7][np]));
                 BOps nxt = cur;
-                if (ns + 1 < 4)
+                if (ns + 1 < CN)
                     nxt = decode_b(cur_ops.b[ns + 1]);
                 if constexpr (!HO) {
 #pragma unroll
-                    for (int ms = 0; ms < 4; ++ms)
+                    for (int ms = 0; ms < RM; ++ms)
                         c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.lo[ms], cur.s, c[ms], 0, 0, 0);
                 }
                 dbuf[ns & 1] = cur.d;
-                // Eight MFMAs per region (four hi-only), each followed by LDS
-                // reads while any remain, the region's loads towards its end, and
-                // its share of the VALU work.
-                constexpr int NM = HO ? 4 : 8;
+                // Eight MFMAs per region, each followed by LDS reads while any
+                // remain, the region's loads towards its end, and its share of
+                // the VALU work.
+                constexpr int NM = RM * (HO ? 1 : 2);
                 constexpr int kDsPerSlot = (kDsReads + NM - 1) / NM;
-                constexpr int kValuPerSlot = HO ? 7 : 4;
-                constexpr int kRegionLoads = 3;   // at most (NL ns / 4 ranges hold 1 .. 3)
-                const int nl = (NL * (ns + 1) + 3) / 4 - (NL * ns + 3) / 4;
+                constexpr int kValuPerSlot = HO ? 6 : 4;
+                constexpr int kRegionLoads = (NL + CN - 1) / CN;   // at most, per region
+                const int nl = (NL * (ns + 1) + CN - 1) / CN - (NL * ns + CN - 1) / CN;
 #pragma unroll
                 for (int u = 0; u < NM; ++u) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -575,7 +589,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             ring_barrier<0>();
         Ops O0, O1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < CN; ++i)
             read_ops(0, O0, i);
         // Step 0 reloads stage 0 of both rings: every wavefront must have read
         // pair 0's operands first.
@@ -595,12 +609,12 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             if (p + 1 < npairs)
                 step(p + 1, O1, O0);
         }
-        // FMAs of the last column group (group 3 of the last pair, in set 1).
+        // FMAs of the last column group (group CN - 1 of the last pair, in set 1).
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
+        for (int ms = 0; ms < RM; ++ms)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                acc[ms][3][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][3][q]);
+                acc[ms][CN - 1][q] = fmaf(dbuf[1], cbuf[1][ms][q], acc[ms][CN - 1][q]);
     };
     if (kg == 0)
         run_group(std::integral_constant<int, 0>{});
@@ -615,12 +629,12 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const int wq = wave & 3;
     if (kg == 1) {
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
+        for (int ms = 0; ms < RM; ++ms)
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns)
+            for (int ns = 0; ns < CN; ++ns)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane] = acc[ms][ns][q];
+                    red[(wq * 64 + ms * (CN * 4) + ns * 4 + q) * 64 + lane] = acc[ms][ns][q];
     }
     __syncthreads();
     if (kg == 0) {
@@ -629,9 +643,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         // Rows of scaled activations (the bfloat16 form, or Q8_0 activations
         // split with a row exponent) are scaled back by 2^-row_exp[m].
         const bool scaled_rows = HO || row_exp != nullptr;
-        const int mb = m0 + wm * 64 + 4 * g, nb = n0 + wn * 64 + li;
+        const int mb = m0 + wm * (RM * 16) + 4 * g, nb = n0 + wn * (CN * 16) + li;
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
+        for (int ms = 0; ms < RM; ++ms) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int m = mb + ms * 16 + q;
@@ -640,8 +654,8 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 if (scaled_rows && m < M)
                     pe = row_exp[m];
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns) {
-                    float v = acc[ms][ns][q] + red[(wq * 64 + ms * 16 + ns * 4 + q) * 64 + lane];
+                for (int ns = 0; ns < CN; ++ns) {
+                    float v = acc[ms][ns][q] + red[(wq * 64 + ms * (CN * 4) + ns * 4 + q) * 64 + lane];
                     if (scaled_rows)
                         v = ldexpf(v, -pe);
                     if (m < M && nb + ns * 16 < N)

@@ -284,7 +284,9 @@ struct PairGeom {
 // do not fit next to its weight stages, at 3 / 4.
 // HO ("hi only") selects the bfloat16-activation form: one binary16 term per
 // activation (exact, see k_gemm_prep_bf16), so a slab is half the size and a
-// tile-block needs one MFMA instead of two.
+// tile-block needs one MFMA instead of two. With its 128 x 32 wavefront tiles
+// both formats are fastest at 4 / 4 (5 / 5 costs 3-4 %; 3 stages of its slab
+// would not hold the final reduction).
 template <class F, bool HO>
 struct RingDepth;
 template <>
@@ -297,11 +299,11 @@ struct RingDepth<FmtQ8_0, false> {
 };
 template <>
 struct RingDepth<FmtQ4_0, true> {
-    static constexpr int kA = 5, kB = 5;
+    static constexpr int kA = 4, kB = 4;
 };
 template <>
 struct RingDepth<FmtQ8_0, true> {
-    static constexpr int kA = 5, kB = 5;
+    static constexpr int kA = 4, kB = 4;
 };
 
 // 16-byte A operands per (128-row tile, block): hi and lo, or hi only.
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 // the VALU work.
                 constexpr int NM = RM * (HO ? 1 : 2);
                 constexpr int kDsPerSlot = (kDsReads + NM - 1) / NM;
-                constexpr int kValuPerSlot = HO ? 6 : 4;
+                constexpr int kValuPerSlot = HO ? (F::kBytes == kQ4Bytes ? 7 : 6) : 4;
                 constexpr int kRegionLoads = (NL + CN - 1) / CN;   // at most, per region
                 const int nl = (NL * (ns + 1) + CN - 1) / CN - (NL * ns + CN - 1) / CN;
 #pragma unroll

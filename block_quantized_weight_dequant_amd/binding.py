@@ -102,10 +102,14 @@ lib = _load_library()
 
 
 def _addr(x) -> int:
+    """Device address of a tensor argument (an int is taken as an address).
+    Host tensors are refused here: the kernels would fault on a host pointer."""
     if x is None:
         return 0
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError("expected a device (cuda) tensor, got one on %s" % getattr(x, "device", type(x)))
     return int(x.data_ptr())
 
 

@@ -419,3 +419,13 @@ def test_gemm_q8a_checks(f):
     assert st(A, ab, Y, M, A + 16, need) == S.Q4_ERR_ALIAS               # workspace over a_q
     assert st(A, ab, Y, M, Y, need) == S.Q4_ERR_ALIAS                    # workspace over y
     assert st(None, 0, None, 0, None, 0) == S.Q4_OK                      # empty
+
+
+def test_host_tensors_are_refused_before_any_call():
+    # A host tensor's data pointer would reach a kernel as a device address.
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        binding.q4_gemv(a, torch.zeros(4 * 2 * 18, dtype=torch.uint8), torch.zeros(16), 4, 4, 64)
+    with pytest.raises(ValueError):
+        binding.q8_quantize(torch.zeros(64), torch.zeros(68, dtype=torch.uint8))

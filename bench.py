@@ -407,6 +407,38 @@ def cpu_baseline(wl, seconds):
         reps += 1
     el = time.perf_counter() - t0
     algo = blob.size + M * K * 4 + M * N * 4
+    # The other configurations the oracle can time in a few seconds: the same
+    # decode GEMV on one core, the 8-row decode on all cores, and the
+    # single-threaded dequant and quantize of the FFN-sized tensors.
+    also = []
+
+    def timed_reps(fn, budget):
+        fn()
+        n, t1 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= budget:
+                return el1 / n
+    t_one = timed_reps(lambda: oracle.q4_0_matmul(a, blob, N, K, threads=1), 2.0)
+    also.append({"what": "1x4096x4096 decode GEMV", "value": algo / t_one / 1e9, "unit": "GB/s",
+                 "cores": 1, "ms_each": 1e3 * t_one})
+    s8 = wl.WORKLOADS["gemv_8x4096x4096"]
+    a8 = wl.activations_f32(s8["a_seed"], s8["M"], K)
+    t8 = timed_reps(lambda: oracle.q4_0_matmul(a8, blob, N, K, threads=threads), 1.0)
+    also.append({"what": "8x4096x4096 decode GEMV", "value": (blob.size + a8.size * 4 + 8 * N * 4) / t8 / 1e9,
+                 "unit": "GB/s", "cores": threads, "ms_each": 1e3 * t8})
+    sd = wl.WORKLOADS["dequant_14336x4096"]
+    wd = oracle.q4_0_quantize(wl.weights_f32(sd["w_seed"], sd["N"], sd["K"]))
+    td = timed_reps(lambda: oracle.q4_0_dequant(wd), 0.5)
+    also.append({"what": "dequant 14336x4096", "value": (wd.size + sd["N"] * sd["K"] * 4) / td / 1e9,
+                 "unit": "GB/s", "cores": 1, "ms_each": 1e3 * td})
+    sq = wl.WORKLOADS["quantize_2048x4096"]
+    xq = wl.activations_f32(sq["x_seed"], sq["M"], sq["K"])
+    tq = timed_reps(lambda: oracle.q8_0_quantize(xq), 0.5)
+    also.append({"what": "Q8_0 quantize 2048x4096", "value": (xq.size * 4 + xq.size // 32 * 34) / tq / 1e9,
+                 "unit": "GB/s", "cores": 1, "ms_each": 1e3 * tq})
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -417,7 +449,8 @@ def cpu_baseline(wl, seconds):
             "sample": "%d full 1x4096x4096 decode GEMVs in %.1f s (%.2f ms each), f64 sums"
                       % (reps, el, 1e3 * el / reps),
             "host": {"cpu_model": model, "logical_cpus": os.cpu_count(),
-                     "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}}
+                     "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")},
+            "also": also}
 
 
 # -------------------------------------------------------------------- main

@@ -548,3 +548,14 @@ def test_q8a_sampled_equals_full(orc):
     ni = wl.uniform_ints(334, 0, N, 40)
     ys, bs = orc.q8_0_matmul_q8a_sampled(ablob, M, wblob, N, K, mi, ni)
     assert (ys == y[mi, ni]).all() and (bs == b[mi, ni]).all()
+
+
+def test_q8a_product_of_the_golden_blocks_by_hand(orc):
+    # Q4_0 "ramp" (d = 2; codes 0, 1, 1, 2, 2, 3, 3 at j = 0..6) against Q8_0
+    # "rounding_mode" (d = 1; codes 127, -127, 1, -1, 2, -3, 64, then zeros):
+    # sum_j 2 (q_w - 8) q_a = -16*127 + -14*-127 + -14*1 + -12*-1 + -12*2
+    # + -10*-3 + -10*64 = -890, and the bound is the sum of magnitudes, 4530.
+    ramp = next(b for b in _golden("q4_0_blocks.json")["blocks"] if b["name"] == "ramp")
+    rnd = next(b for b in _golden("q8_0_blocks.json")["blocks"] if b["name"] == "rounding_mode")
+    y, bound = orc.q4_0_matmul_q8a(bytes.fromhex(rnd["bytes"]), 1, bytes.fromhex(ramp["bytes"]), 1, 32)
+    assert y[0, 0] == -890.0 and bound[0, 0] == 4530.0

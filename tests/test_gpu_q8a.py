@@ -344,3 +344,22 @@ def test_gemm_q8a_graph_replays_match_eager(fmt):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), rep
+
+
+def test_golden_blocks_give_the_hand_worked_value():
+    # Q4_0 "ramp" against Q8_0 "rounding_mode" (tests/golden): the integer sum
+    # is 16 * (-445), times d_w / 16 * d_a = 0.125: exactly -890 on both kernels.
+    import json
+    import os
+    g = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    ramp = next(b for b in json.load(open(os.path.join(g, "q4_0_blocks.json")))["blocks"]
+                if b["name"] == "ramp")
+    rnd = next(b for b in json.load(open(os.path.join(g, "q8_0_blocks.json")))["blocks"]
+               if b["name"] == "rounding_mode")
+    w = to_dev(np.frombuffer(bytes.fromhex(ramp["bytes"]), dtype=np.uint8))
+    a_q = to_dev(np.frombuffer(bytes.fromhex(rnd["bytes"]), dtype=np.uint8))
+    for fn in (binding.q4_gemv_q8a, binding.q4_gemm_q8a):
+        y = torch.full((1,), float("nan"), device=DEV)
+        fn(a_q, w, y, 1, 1, 32)
+        torch.cuda.synchronize()
+        assert y.item() == -890.0

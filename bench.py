@@ -586,6 +586,9 @@ def main():
         "cpu_baseline": cpu,
         "rows": rows,
         "device": props.name,
+        "device_arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "hip_runtime": torch.version.hip,
     }
     if calib:
         line["copy_calibration"] = calib

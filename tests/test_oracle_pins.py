@@ -559,3 +559,26 @@ def test_q8a_product_of_the_golden_blocks_by_hand(orc):
     rnd = next(b for b in _golden("q8_0_blocks.json")["blocks"] if b["name"] == "rounding_mode")
     y, bound = orc.q4_0_matmul_q8a(bytes.fromhex(rnd["bytes"]), 1, bytes.fromhex(ramp["bytes"]), 1, 32)
     assert y[0, 0] == -890.0 and bound[0, 0] == 4530.0
+
+
+# ------------------------------------------------------------- the parity bar
+
+def test_tolerance_is_the_stated_bar(orc):
+    # The products' accuracy bar, written out: an output passes when it is
+    # within 1e-5 of sum_k |a[m, k] w[n, k]| plus 1e-6 of the f64 reference.
+    # The literals below are that statement, not calls into the oracle, so a
+    # slip in either constant (1e-4 for 1e-5, 1e-5 for 1e-6) or a bound
+    # ignored, squared or taken as |y| fails here.
+    assert orc.tolerance(0.0) == 1e-6
+    assert orc.tolerance(np.float64(1.0)) == 1e-5 + 1e-6
+    assert orc.tolerance(1e6) == 10.0 + 1e-6
+    assert orc.tolerance(4530.0) == pytest.approx(0.045301, rel=1e-12, abs=0.0)
+    b = np.array([[0.0, 1.0, 2.5], [1e-3, 1e6, 1e12]])
+    t = orc.tolerance(b)
+    assert t.shape == b.shape and t.dtype == np.float64
+    expected = np.array([[1e-6, 1.1e-5, 2.6e-5], [1.01e-6, 10.000001, 1e7 + 1e-6]])
+    assert np.allclose(t, expected, rtol=1e-12, atol=0.0)
+    # An error just inside the bar passes and one just outside fails, at every B.
+    for B in (0.0, 1e-3, 1.0, 37.25, 1e4, 1e9):
+        bar = 1e-5 * B + 1e-6
+        assert bar * (1 - 1e-9) <= orc.tolerance(B) <= bar * (1 + 1e-9)

@@ -4,8 +4,9 @@ Each case copies the oracle into a temporary directory, plants one plausible
 mistake in the copy (a swapped nibble half, a dropped -8, the wrong rounding
 of q = round(x / d), a round-half-up binary16 encoder, reversed activation
 rows, the wrong Q4_0 rounding bias, /128 for /127, a transposed stream of
-quantized activations) and runs tests/test_oracle_pins.py against the copy in
-a fresh interpreter: the pins must fail. A mistake they let through would make
+quantized activations, the parity bar loosened in either of its two terms)
+and runs tests/test_oracle_pins.py against the copy in a fresh interpreter:
+the pins must fail. A mistake they let through would make
 every GPU parity test that trusts the oracle meaningless."""
 import os
 import shutil
@@ -31,6 +32,10 @@ PLANTED = [
     ("oracle.c", "float d = amax / 127.0f;", "float d = amax / 128.0f;", "Q8_0 scale /128"),
     ("__init__.py", "return q8_0_dequant(b).reshape(M, K)", "return q8_0_dequant(b).reshape(K, M).T.copy()",
      "quantized-activation stream transposed"),
+    ("__init__.py", "return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-6",
+     "return 1e-4 * np.asarray(bound, dtype=np.float64) + 1e-6", "parity bar loosened to 1e-4 relative"),
+    ("__init__.py", "return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-6",
+     "return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-5", "parity bar floor loosened to 1e-5"),
 ]
 
 

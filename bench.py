@@ -246,9 +246,9 @@ def bench_product(torch, q4, wl, name, steps, warmup, cold=True):
         gemv = getattr(q4, f + ("_gemv_bf16" if act == "bf16" else "_gemv"))
         fn = lambda k: gemv(a, blobs[k % R], y, M, N, K)
     else:
-        entry = f + ("_gemm_bf16" if act == "bf16" else "_gemm")
+        entry = f + ("_gemm_bf16" if act == "bf16" else "_gemm_ws")
         gemm = getattr(q4, entry)
-        ws_bytes = getattr(q4, entry + "_workspace_bytes")(M, N, K)
+        ws_bytes = getattr(q4, entry.replace("_gemm_ws", "_gemm") + "_workspace_bytes")(M, N, K)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         fn = lambda k: gemm(a, blobs[k % R], y, M, N, K, workspace=ws)
     t = run_timed(torch, fn, steps, warmup)

@@ -29,8 +29,8 @@ Q4_GEMV_MAX_ROWS = 8
 SIZE_MAX = 2 ** 64 - 1
 
 #: Every symbol include/q4.h declares.
-EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
-           "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm",
+EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm_ws",
+           "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm_ws",
            "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize", "q4_gemm_bf16",
            "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes",
            "q4_gemv_bf16", "q8_gemv_bf16", "q4_gemv_splitk", "q4_gemv_splitk_workspace_bytes",
@@ -68,11 +68,12 @@ def _load_library():
         for g in ("_gemv", "_gemv_bf16"):
             getattr(lib, f + g).restype = i32
             getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P]
-        for g in ("_gemm", "_gemm_bf16"):
+        for g in ("_gemm_ws", "_gemm_bf16"):
             getattr(lib, f + g).restype = i32
             getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P, sz, P]
-            getattr(lib, f + g + "_workspace_bytes").restype = sz
-            getattr(lib, f + g + "_workspace_bytes").argtypes = [i32, i32, i32]
+        for g in ("_gemm_workspace_bytes", "_gemm_bf16_workspace_bytes"):
+            getattr(lib, f + g).restype = sz
+            getattr(lib, f + g).argtypes = [i32, i32, i32]
         getattr(lib, f + "_gemv_splitk").restype = i32
         getattr(lib, f + "_gemv_splitk").argtypes = [P, P, sz, P, i32, i32, i32, i32, P, sz, P]
         getattr(lib, f + "_gemv_splitk_workspace_bytes").restype = sz
@@ -83,8 +84,7 @@ def _load_library():
         getattr(lib, f + "_gemv_prepare").argtypes = [P, i32, i32, P, sz, P]
         getattr(lib, f + "_gemv_prepared").restype = i32
         getattr(lib, f + "_gemv_prepared").argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
-    for name in ("q4_gemv_q8a", "q8_gemv_q8a", "q4_gemm_q8a",
-           "q4_gemm_q8a_workspace_bytes", "q8_gemm_q8a", "q8_gemm_q8a_workspace_bytes"):
+    for name in ("q4_gemv_q8a", "q8_gemv_q8a"):
         getattr(lib, name).restype = i32
         getattr(lib, name).argtypes = [P, sz, P, sz, P, i32, i32, i32, P]
     for name in ("q4_gemm_q8a", "q8_gemm_q8a"):
@@ -356,11 +356,12 @@ def q8_gemm_bf16_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib.q8_gemm_bf16_workspace_bytes(int(M), int(N), int(K)))
 
 
-def _gemm(entry, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes) -> None:
+def _gemm(entry, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes,
+          ws_entry=None) -> None:
     wb = _nbytes(w_q) if w_bytes is None else int(w_bytes)
     ws = workspace
     if ws is None:
-        need = int(getattr(lib, entry + "_workspace_bytes")(int(M), int(N), int(K)))
+        need = int(getattr(lib, ws_entry or entry + "_workspace_bytes")(int(M), int(N), int(K)))
         if 0 < need < SIZE_MAX:
             ws = _scratch(need, stream, y)
     if workspace_bytes is not None:
@@ -371,25 +372,28 @@ def _gemm(entry, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes
                                _addr(ws), wsb, _stream(stream)), entry)
 
 
-def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
-            workspace_bytes=None) -> None:
-    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M, W Q4_0.
+def q4_gemm_ws(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+               workspace_bytes=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M, W Q4_0, with the
+    caller's workspace.
 
     ``workspace=None`` takes a scratch tensor of q4_gemm_workspace_bytes(M, N, K)
     bytes from PyTorch's caching allocator for this call; pass a tensor (or an
     address with ``workspace_bytes``) to reuse one."""
-    _gemm("q4_gemm", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+    _gemm("q4_gemm_ws", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes,
+          "q4_gemm_workspace_bytes")
 
 
-def q8_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
-            workspace_bytes=None) -> None:
-    """As q4_gemm, with W a Q8_0 stream (workspace from q8_gemm_workspace_bytes)."""
-    _gemm("q8_gemm", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
+def q8_gemm_ws(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
+               workspace_bytes=None) -> None:
+    """As q4_gemm_ws, with W a Q8_0 stream (workspace from q8_gemm_workspace_bytes)."""
+    _gemm("q8_gemm_ws", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes,
+          "q8_gemm_workspace_bytes")
 
 
 def q4_gemm_bf16(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,
                  workspace_bytes=None) -> None:
-    """As q4_gemm with ``a`` a [M, K] bfloat16 tensor (or its address); the
+    """As q4_gemm_ws with ``a`` a [M, K] bfloat16 tensor (or its address); the
     workspace, from q4_gemm_bf16_workspace_bytes, is always needed."""
     _gemm("q4_gemm_bf16", a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes)
 

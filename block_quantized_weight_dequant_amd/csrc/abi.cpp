@@ -71,8 +71,7 @@ static int gemm(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const
     if (st != Q4_OK)
         return st;
     return launched(q4k::launch_gemm(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
-                                     q4v::gemm_splits_activations(K) ? workspace : nullptr,
-                                     as_stream(stream)));
+                                     workspace, as_stream(stream)));
 }
 
 static int gemv_splitk(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const void *w_q,
@@ -211,15 +210,15 @@ Q4_EXPORT size_t q8_gemm_workspace_bytes(int M, int N, int K)
     return q4v::gemm_workspace_bytes(M, N, K);
 }
 
-Q4_EXPORT int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
-                      void *workspace, size_t workspace_bytes, void *stream)
+Q4_EXPORT int q4_gemm_ws(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N,
+                         int K, void *workspace, size_t workspace_bytes, void *stream)
 {
     return gemm(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, workspace,
                 workspace_bytes, stream);
 }
 
-Q4_EXPORT int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
-                      void *workspace, size_t workspace_bytes, void *stream)
+Q4_EXPORT int q8_gemm_ws(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N,
+                         int K, void *workspace, size_t workspace_bytes, void *stream)
 {
     return gemm(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, workspace,
                 workspace_bytes, stream);

@@ -8,6 +8,20 @@
 // sections dequant_q4_0 and dequant_q8_0 (the quantized-matmul binding picks
 // either by quant type).
 //
+// Range: every activation row m is first scaled by a power of two 2^p_m
+// (k_row_exp_f32) that puts its largest magnitude in [2^14, 2^15), so any
+// finite f32 row fits the binary16 terms below; each result row is scaled back
+// by 2^-p_m (exact unless it lands among the f32 subnormals).
+//
+// Summation order (worst case, u = 2^-24): the two-term split is within 2^-22
+// (4u) of each scaled activation; an MFMA block partial adds the lo products
+// (each at most 2^-11 of its hi product) first and the hi products onto them,
+// about 32u; the scale FMAs d * C + acc then add at most kMaxChain block
+// partials in sequence per accumulator, the K groups' tiles are added once,
+// and longer K is cut into segments (separate launches, each adding its part
+// into y). With S segments the error is at most (36 + kMaxChain + S) u of
+// sum |a w|: 150u < 1e-5 for K up to 14336, and below 1e-5 while S <= 19.
+//
 // General kernel (k_gemm_any, any K % 32 == 0)
 // -------------------------------------------
 // * A 256-thread workgroup computes a 128 x 128 tile of y; its four wavefronts
@@ -18,10 +32,10 @@
 //   the exact binary16 weight codes plus the same values times 2^-11, with
 //   the f32 scales d of the 128 weight rows. For a in [2^e, 2^(e+1)) the
 //   residual a - hi is at most 2^(e-11), so lo is at most 2^e <= |a|: no
-//   overflow for |a| < 65504, and lo stays a normal binary16 unless the
-//   residual is below 2^-25. The matching 2^-11 on the weights (exact) makes
-//   hi * c + lo * c 2^-11 equal a c to about 2^-22 relative, so both land in
-//   one MFMA chain.
+//   overflow once the row is scaled below 2^15, and lo stays a normal binary16
+//   unless the residual is below 2^-25. The matching 2^-11 on the weights
+//   (exact) makes hi * c + lo * c 2^-11 equal a c to about 2^-22 relative, so
+//   both land in one MFMA chain.
 // * Every 16 x 16 tile's block partial is scaled by its column's d into an f32
 //   accumulator (d * C + acc): block partial -> scale -> sum of blocks.
 // * Two LDS stages with the next step's global loads issued before the current
@@ -52,14 +66,19 @@ struct GemmStage {
     float d[kGemmBN];
 };
 
-// row_exp: when not null, row m of a was scaled by 2^row_exp[m] (the bfloat16
-// path's per-row scale), and the result row is scaled back by 2^-row_exp[m].
+// One K segment of the product: a and w point at block kb0 of row 0 (a row
+// of a is K floats, a row of w K/32 blocks), and the segment spans nblk
+// blocks. row_exp: when not null, row m of the result is scaled back by
+// 2^-row_exp[m]; scale_in says whether the kernel scales row m of a by
+// 2^row_exp[m] itself (the f32 path) or a was scaled beforehand (the bfloat16
+// and Q8_0-activation paths). accumulate: add the segment's result to y.
 template <class F>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restrict__ a,
                                                           const uint8_t *__restrict__ w,
                                                           float *__restrict__ y, int M, int N,
-                                                          int K, int tiles_m, int tiles_n,
-                                                          const int *__restrict__ row_exp)
+                                                          int K, int nblk, int tiles_m, int tiles_n,
+                                                          const int *__restrict__ row_exp,
+                                                          int scale_in, int accumulate)
 {
     __shared__ GemmStage st[2];
 
@@ -71,15 +90,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int nblk = K >> 5;
-    const size_t row_bytes = (size_t)nblk * F::kBytes;
+    const size_t row_bytes = (size_t)(K >> 5) * F::kBytes;
 
     // Staging role: row r of the slab, half h (elements 16h..16h+15 of the
     // activation block; the quant bytes of lane groups 2h and 2h+1 of the
     // weight block).
     const int r = tid >> 1, h = tid & 1;
-    const float *arow = a + (size_t)min(m0 + r, M - 1) * K + 16 * h;
+    const int ar = min(m0 + r, M - 1);
+    const float *arow = a + (size_t)ar * K + 16 * h;
     const uint8_t *wrow = w + (size_t)min(n0 + r, N - 1) * row_bytes;
+    const int pin = scale_in ? row_exp[ar] : 0;
 
     float4 av[4];
     uint32_t wx[2][F::kQsDwords];
@@ -99,10 +119,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             // Elements 16h + 4q .. + 3 fill one slot half of one lane group.
+            // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code: they
+            // carry a further 2^-kHiLog2 (exact).
             const int e0 = 16 * h + 4 * q, gg = F::a_group(e0), half = F::a_half(e0);
-            const float sc = half ? 1.0f / (float)(1 << F::kHiLog2) : 1.0f;
+            const int sh = pin - (half ? F::kHiLog2 : 0);
             const float4 v = av[q];
-            const float e[4] = {v.x * sc, v.z * sc, v.y * sc, v.w * sc};   // slot order 0, 2, 1, 3
+            const float e[4] = {ldexpf(v.x, sh), ldexpf(v.z, sh), ldexpf(v.y, sh),
+                                ldexpf(v.w, sh)};   // slot order 0, 2, 1, 3
             f16x4 hi, lo;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -163,8 +186,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
         for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
-                f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bq[ns], zero4, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bs[ns], c, 0, 0, 0);
+                // The small lo products first, the hi products onto them.
+                f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ms], bs[ns], zero4, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ms], bq[ns], c, 0, 0, 0);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     acc[ms][ns][q] = fmaf(dv[ns], c[q], acc[ms][ns][q]);
@@ -187,8 +211,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
                 const int n = n0 + wn * 64 + ns * 16 + li;
-                if (n < N)
-                    y[(size_t)m * N + n] = ldexpf(acc[ms][ns][q], -pe);
+                if (n < N) {
+                    float v = ldexpf(acc[ms][ns][q], -pe);
+                    if (accumulate)
+                        v += y[(size_t)m * N + n];
+                    y[(size_t)m * N + n] = v;
+                }
             }
         }
     }
@@ -221,13 +249,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 //   the binary16 codes and the same times 2^-11, and d stays binary16 until
 //   the scale FMA.
 // * Accumulation as in the general kernel: two chained MFMAs per 16 x 16 tile
-//   and block (hi x code, lo x code 2^-11), then d * C + acc in f32.
+//   and block (lo x code 2^-11, then hi x code onto it), then d * C + acc in
+//   f32.
 
 constexpr int kSplitWaves = 4;
 constexpr int kOpsPerBlockTile = 2 * 8 * 64;   // 16-byte A operands per (128-row tile, block)
 
+// row_exp[m]: the power of two row m is scaled by before the split.
 template <class F>
 __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *__restrict__ a,
+                                                                 const int *__restrict__ row_exp,
                                                                  u32x4 *__restrict__ ahl, int M,
                                                                  int K, long long n_waves)
 {
@@ -246,9 +277,10 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *
         const float4 L = *reinterpret_cast<const float4 *>(blk + F::a_lo(g));
         const float4 H = *reinterpret_cast<const float4 *>(blk + F::a_hi(g));
         // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code: they carry
-        // a / 2^kHiLog2 (exact), so every product is a times the code.
-        constexpr float hs = 1.0f / (float)(1 << F::kHiLog2);
-        const float e[8] = {L.x, L.z, L.y, L.w, H.x * hs, H.z * hs, H.y * hs, H.w * hs};
+        // a further 2^-kHiLog2 (exact), so every product is a 2^p times the code.
+        const int p = row_exp[m], ph = p - F::kHiLog2;
+        const float e[8] = {ldexpf(L.x, p),  ldexpf(L.z, p),  ldexpf(L.y, p),  ldexpf(L.w, p),
+                            ldexpf(H.x, ph), ldexpf(H.z, ph), ldexpf(H.y, ph), ldexpf(H.w, ph)};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const f16 h = (f16)e[s];
@@ -339,12 +371,17 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("" ::: "memory");
 }
 
-// row_exp: per-row exponents of the activation operands (always for the
-// bfloat16 form, HO; for the two-term form when not null).
+// One K segment of the product: ahl points at the operands of block kb0 of
+// the first row tile (a row tile holds nblk_row blocks of operands) and w at
+// block kb0 of weight row 0 (a weight row is nblk_row blocks); the segment
+// spans nblk blocks (even). row_exp: per-row exponents of the activation
+// operands, undone on the result rows (always for the bfloat16 form, HO; for
+// the two-term form when not null). accumulate: add the segment's result to y.
 template <class F, bool HO>
 __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const u32x4 *__restrict__ ahl, const uint8_t *__restrict__ w, float *__restrict__ y, int M,
-    int N, int K, int tiles_m, int tiles_n, const int *__restrict__ row_exp)
+    int N, int nblk_row, int nblk, int tiles_m, int tiles_n, const int *__restrict__ row_exp,
+    int accumulate)
 {
     using G = PairGeom<F>;
     // MFMA tiles per wavefront: the hi-only form takes 128 rows x 32 columns
@@ -368,9 +405,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = wave >> 2, wm = HO ? 0 : (wave >> 1) & 1, wn = HO ? (wave & 3) : (wave & 1);
     const int li = lane & 15, g = lane >> 4;
-    const int nblk = K >> 5, npairs = nblk >> 1;
+    const int npairs = nblk >> 1;
     const uint32_t magic_v = magic_vgpr<F>();
-    const size_t row_bytes = (size_t)nblk * F::kBytes;
+    const size_t row_bytes = (size_t)nblk_row * F::kBytes;
 
     // Direct-to-LDS loads, NL per wavefront per pair (so every wavefront's
     // vmcnt moves in the same steps), as buffer loads: one buffer resource
@@ -381,13 +418,15 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     // order. B: NB 4-byte loads at dword slots j * 64 + lane, j = wave + 8 r;
     // slot t < 128 kDwords is dword t % kDwords of the pair's bytes of row
     // t / kDwords, higher slots re-read a valid dword into unused LDS. The
-    // ranges of both resources fit 32 bits (K <= 2^22 on this path).
+    // ranges of both resources fit 32 bits (K <= 2^22 on this path); each ends
+    // with the segment's last block.
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(ahl + (size_t)mt * nblk * SO), (short)0, (int)((uint32_t)nblk * SO * 16u),
+        (void *)(ahl + (size_t)mt * nblk_row * SO), (short)0, (int)((uint32_t)nblk * SO * 16u),
         kBufferRsrcWord3);
     const int brows = min(kGemmBN, N - n0);
     const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(w + (size_t)n0 * row_bytes), (short)0, (int)(brows * row_bytes), kBufferRsrcWord3);
+        (void *)(w + (size_t)n0 * row_bytes), (short)0,
+        (int)((brows - 1) * row_bytes + (size_t)nblk * F::kBytes), kBufferRsrcWord3);
     const uint32_t a_voff = (uint32_t)((wave * NA * 64 + lane) * 16);
     uint32_t b_voff[NB];
 #pragma unroll
@@ -482,8 +521,8 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 o.s = o.q * scale;
             return o;
         };
-        // One scheduling region per column group ns: its eight MFMAs (the four hi
-        // products, then the four lo products that add onto them) interleaved
+        // One scheduling region per column group ns: its eight MFMAs (the four lo
+        // products, then the four hi products that add onto them) interleaved
         // with the scale FMAs of group ns - 1, the decode of group ns + 1 and
         // part ns of the next pair's operands (LDS reads that land during this
         // pair's MFMAs, so no step starts by waiting on LDS). The scheduling-group
@@ -499,9 +538,16 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 f32x4 *c = cbuf[ns & 1];
                 const f32x4 *cp = cbuf[(ns + 1) & 1];      // group ns - 1 (mod CN; CN is even)
                 const float dp = dbuf[(ns + 1) & 1];
+                // The two-term form multiplies the small lo terms first and adds
+                // the hi products onto them (the rounding of the lo chain then
+                // acts on sums 2^-11 the size of the hi ones).
 #pragma unroll
-                for (int ms = 0; ms < RM; ++ms)
-                    c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.hi[ms], cur.q, zero4, 0, 0, 0);
+                for (int ms = 0; ms < RM; ++ms) {
+                    if constexpr (HO)
+                        c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.hi[ms], cur.q, zero4, 0, 0, 0);
+                    else
+                        c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.lo[ms], cur.s, zero4, 0, 0, 0);
+                }
                 read_ops(next_pair, next_ops, ns);
                 // The step's loads go out spread over the four regions (loads
                 // [NL ns / 4, NL (ns + 1) / 4), rounded up) and, within a region,
@@ -531,7 +577,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 if constexpr (!HO) {
 #pragma unroll
                     for (int ms = 0; ms < RM; ++ms)
-                        c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.lo[ms], cur.s, c[ms], 0, 0, 0);
+                        c[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur_ops.hi[ms], cur.q, c[ms], 0, 0, 0);
                 }
                 dbuf[ns & 1] = cur.d;
                 // Eight MFMAs per region, each followed by LDS reads while any
@@ -642,8 +688,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     if (kg == 0) {
         // Lane (li, g) of tile (ms, ns) holds rows 4g..4g+3 of column li.
         // Offsets are 32-bit (M N < 2^31 on this path, checked at launch).
-        // Rows of scaled activations (the bfloat16 form, or Q8_0 activations
-        // split with a row exponent) are scaled back by 2^-row_exp[m].
+        // Rows of scaled activations (every form that passes row exponents)
+        // are scaled back by 2^-row_exp[m]; a later K segment adds its part to
+        // what the earlier ones left in y.
         const bool scaled_rows = HO || row_exp != nullptr;
         const int mb = m0 + wm * (RM * 16) + 4 * g, nb = n0 + wn * (CN * 16) + li;
 #pragma unroll
@@ -660,8 +707,11 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                     float v = acc[ms][ns][q] + red[(wq * 64 + ms * (CN * 4) + ns * 4 + q) * 64 + lane];
                     if (scaled_rows)
                         v = ldexpf(v, -pe);
-                    if (m < M && nb + ns * 16 < N)
+                    if (m < M && nb + ns * 16 < N) {
+                        if (accumulate)
+                            v += y[row_off + ns * 16];
                         y[row_off + ns * 16] = v;
+                    }
                 }
             }
         }
@@ -809,6 +859,112 @@ __global__ __launch_bounds__(256) void k_gemm_prep_bf16_f32(const uint16_t *__re
                          ldexpf(bf16_bits_to_f32(v.y >> 16), p));
 }
 
+// ---------------------------------------------------------------------------
+// f32 activations: the row exponents. k_row_exp_f32 (one wavefront per row)
+// takes the largest |a| of the row as the largest f32 bit pattern with the
+// sign cleared (which orders finite values by magnitude) and sets p = 14 - E
+// for a largest magnitude in [2^E, 2^(E+1)); 0 for an all-zero row or one
+// that holds an infinity or NaN.
+
+// Largest |a| of row `row` (K f32 values, K % 32 == 0, 16-byte aligned) as a
+// cleared-sign bit pattern, in every lane of the wavefront.
+__device__ __forceinline__ uint32_t row_max_bits_f32(const float *__restrict__ row, int K, int lane)
+{
+    const uint4 *r4 = reinterpret_cast<const uint4 *>(row);
+    uint32_t mx = 0;
+#pragma unroll 8
+    for (int i = lane; i < K / 4; i += 64) {
+        const uint4 v = r4[i];
+        mx = max(mx, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu),
+                         max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    return mx;
+}
+
+__global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_f32(const float *__restrict__ a,
+                                                                  int *__restrict__ row_exp,
+                                                                  int M, int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
+    if (m >= M)   // whole wavefronts only
+        return;
+    const uint32_t mx = row_max_bits_f32(a + (size_t)m * K, K, lane);
+    int p = 0;
+    if (mx != 0 && mx < 0x7F800000u) {
+        const int ef = (int)(mx >> 23);
+        // Subnormals are (mantissa) 2^-149.
+        const int E = ef > 0 ? ef - 127 : (31 - __builtin_clz(mx)) - 149;
+        p = 14 - E;
+    }
+    if (lane == 0)
+        row_exp[m] = p;
+}
+
+// Longest run of block partials that one accumulator adds in sequence in a
+// launch. Longer K is cut into segments, one launch each, every launch after
+// the first adding its part into y; see the summation order at the top.
+constexpr int kMaxChain = 112;
+
+struct KSegments {
+    int n, len;   // n segments of len blocks (the last one the rest)
+};
+
+// per_term: blocks per term of an accumulator's chain, 2 on the split kernel
+// (its two K groups take alternate blocks), 1 on the general kernel.
+static KSegments k_segments(int nblk, int per_term)
+{
+    const int terms = (nblk + per_term - 1) / per_term;
+    const int n = (terms + kMaxChain - 1) / kMaxChain;
+    const int len = (terms + n - 1) / n * per_term;
+    return {(nblk + len - 1) / len, len};
+}
+
+template <class F, bool HO>
+static hipError_t launch_split_segments(const u32x4 *ops, const uint8_t *w, float *y, int M, int N,
+                                        int K, int tiles_m, int tiles_n, const int *row_exp,
+                                        hipStream_t s)
+{
+    const int nblk = K >> 5;
+    const KSegments sg = k_segments(nblk, 2);
+    const unsigned T = (unsigned)tiles_m * (unsigned)tiles_n;
+    for (int i = 0; i < sg.n; ++i) {
+        const int kb0 = i * sg.len, nb = min(sg.len, nblk - kb0);
+        const hipError_t e = launch_kernel(
+            k_gemm_split<F, HO>, dim3(T), dim3(kSplitGemmThreads), 0, s,
+            ops + (size_t)kb0 * slab_ops<HO>(), w + (size_t)kb0 * F::kBytes, y, M, N, nblk, nb,
+            tiles_m, tiles_n, row_exp, i > 0 ? 1 : 0);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <class F>
+static hipError_t launch_any_segments(const float *a, const uint8_t *w, float *y, int M, int N,
+                                      int K, int tiles_m, int tiles_n, const int *row_exp,
+                                      int scale_in, hipStream_t s)
+{
+    const int nblk = K >> 5;
+    const KSegments sg = k_segments(nblk, 1);
+    const unsigned T = (unsigned)tiles_m * (unsigned)tiles_n;
+    for (int i = 0; i < sg.n; ++i) {
+        const int kb0 = i * sg.len, nb = min(sg.len, nblk - kb0);
+        const hipError_t e = launch_kernel(k_gemm_any<F>, dim3(T), dim3(kGemmThreads), 0, s,
+                                           a + (size_t)kb0 * 32, w + (size_t)kb0 * F::kBytes, y,
+                                           M, N, K, nb, tiles_m, tiles_n, row_exp, scale_in,
+                                           i > 0 ? 1 : 0);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// workspace: the row exponents (q4v::gemm_row_exp_bytes(M)), then on the split
+// path the two-term operands.
 template <class F>
 static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int M, int N, int K,
                                 void *workspace, hipStream_t s)
@@ -817,21 +973,25 @@ static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int 
     const long long T = (long long)tiles_m * tiles_n;
     if (T > 0x7fffffffLL)
         return hipErrorInvalidValue;
+    int *row_exp = static_cast<int *>(workspace);
+    hipError_t e = launch_kernel(k_row_exp_f32, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
+                                 dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
+    if (e != hipSuccess)
+        return e;
     if (!q4v::gemm_splits_activations(K) ||
         (long long)M * N >= (1LL << 31))   // the split kernel stores with 32-bit offsets
-        return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s, a, w, y,
-                             M, N, K, tiles_m, tiles_n, (const int *)nullptr);
-    u32x4 *ahl = static_cast<u32x4 *>(workspace);
+        return launch_any_segments<F>(a, w, y, M, N, K, tiles_m, tiles_n, row_exp, 1, s);
+    u32x4 *ahl = reinterpret_cast<u32x4 *>(static_cast<char *>(workspace) +
+                                           q4v::gemm_row_exp_bytes(M));
     const long long n_waves = (long long)tiles_m * 8 * (K / 32);
     const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
     if (split_grid > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    hipError_t e = launch_kernel(k_gemm_split_a<F>, dim3((unsigned)split_grid),
-                                 dim3(64 * kSplitWaves), 0, s, a, ahl, M, K, n_waves);
+    e = launch_kernel(k_gemm_split_a<F>, dim3((unsigned)split_grid), dim3(64 * kSplitWaves), 0, s,
+                      a, (const int *)row_exp, ahl, M, K, n_waves);
     if (e != hipSuccess)
         return e;
-    return launch_kernel(k_gemm_split<F, false>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
-                         (const u32x4 *)ahl, w, y, M, N, K, tiles_m, tiles_n, (const int *)nullptr);
+    return launch_split_segments<F, false>(ahl, w, y, M, N, K, tiles_m, tiles_n, row_exp, s);
 }
 
 template <class F>
@@ -843,7 +1003,7 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
     if (T > 0x7fffffffLL)
         return hipErrorInvalidValue;
     int *row_exp = static_cast<int *>(workspace);
-    void *act = static_cast<char *>(workspace) + q4v::gemm_bf16_row_exp_bytes(M);
+    void *act = static_cast<char *>(workspace) + q4v::gemm_row_exp_bytes(M);
     hipError_t e = launch_kernel(k_row_exp_bf16, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
                                  dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
     if (e != hipSuccess)
@@ -857,9 +1017,8 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
                           (const int *)row_exp, static_cast<float4 *>(act), K, n_quads);
         if (e != hipSuccess)
             return e;
-        return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s,
-                             (const float *)act, w, y, M, N, K, tiles_m, tiles_n,
-                             (const int *)row_exp);
+        return launch_any_segments<F>((const float *)act, w, y, M, N, K, tiles_m, tiles_n,
+                                      row_exp, 0, s);
     }
     // One wavefront per 16-row group of the padded tiles and pair of blocks
     // (groups past M write zeros).
@@ -871,8 +1030,8 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
                       (const int *)row_exp, static_cast<u32x4 *>(act), M, K, n_waves);
     if (e != hipSuccess)
         return e;
-    return launch_kernel(k_gemm_split<F, true>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
-                         (const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n, (const int *)row_exp);
+    return launch_split_segments<F, true>((const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n,
+                                          row_exp, s);
 }
 
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
@@ -1011,7 +1170,7 @@ static hipError_t launch_gemm_q8a_f(const uint8_t *aq, const uint8_t *w, float *
     if (T > 0x7fffffffLL)
         return hipErrorInvalidValue;
     int *row_exp = static_cast<int *>(workspace);
-    void *act = static_cast<char *>(workspace) + q4v::gemm_bf16_row_exp_bytes(M);
+    void *act = static_cast<char *>(workspace) + q4v::gemm_row_exp_bytes(M);
     hipError_t e = launch_kernel(k_row_exp_q8a, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
                                  dim3(64 * kRowExpWaves), 0, s, aq, row_exp, M, K);
     if (e != hipSuccess)
@@ -1025,9 +1184,8 @@ static hipError_t launch_gemm_q8a_f(const uint8_t *aq, const uint8_t *w, float *
                           (const int *)row_exp, static_cast<float4 *>(act), K, n_quads);
         if (e != hipSuccess)
             return e;
-        return launch_kernel(k_gemm_any<F>, dim3((unsigned)T), dim3(kGemmThreads), 0, s,
-                             (const float *)act, w, y, M, N, K, tiles_m, tiles_n,
-                             (const int *)row_exp);
+        return launch_any_segments<F>((const float *)act, w, y, M, N, K, tiles_m, tiles_n,
+                                      row_exp, 0, s);
     }
     const long long n_waves = (long long)tiles_m * 8 * (K / 32);
     const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
@@ -1037,8 +1195,8 @@ static hipError_t launch_gemm_q8a_f(const uint8_t *aq, const uint8_t *w, float *
                       s, aq, (const int *)row_exp, static_cast<u32x4 *>(act), M, K, n_waves);
     if (e != hipSuccess)
         return e;
-    return launch_kernel(k_gemm_split<F, false>, dim3((unsigned)T), dim3(kSplitGemmThreads), 0, s,
-                         (const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n, (const int *)row_exp);
+    return launch_split_segments<F, false>((const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n,
+                                           row_exp, s);
 }
 
 hipError_t launch_gemm_q8a(WeightFormat fmt, const uint8_t *a_q, const uint8_t *w, float *y, int M,

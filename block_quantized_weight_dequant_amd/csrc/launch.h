@@ -36,8 +36,8 @@ hipError_t launch_gemv_q8a(WeightFormat fmt, const uint8_t *a_q, const uint8_t *
 hipError_t launch_gemv_splitk(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M,
                               int N, int K, const q4v::GemvSplit &sp, void *workspace,
                               hipStream_t s);
-// workspace: q4v::gemm_workspace_bytes(M, N, K) bytes when the split path is
-// taken (q4v::gemm_splits_activations(K)), else unused.
+// workspace: q4v::gemm_workspace_bytes(M, N, K) bytes (always used: the row
+// exponents, then on the split path the two-term operands).
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
                        int K, void *workspace, hipStream_t s);
 // a: [M, K] bfloat16 bit patterns. workspace:

@@ -125,16 +125,18 @@ int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_b
 
 size_t gemm_workspace_bytes(int M, int N, int K)
 {
-    // The split path also needs M N < 2^31 (its 32-bit output offsets); larger
-    // outputs take the general kernel, which needs no workspace.
-    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0 || !gemm_splits_activations(K) ||
-        (long long)M * N >= (1LL << 31))
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 != 0)
         return 0;
+    const size_t r = gemm_row_exp_bytes(M);
+    // The split path also needs M N < 2^31 (its 32-bit output offsets); larger
+    // outputs take the general kernel, which needs the row exponents only.
+    if (!gemm_splits_activations(K) || (long long)M * N >= (1LL << 31))
+        return r;
     // Rows are padded to whole 128-row tiles; hi and lo binary16 per element.
     size_t mp = ((size_t)M + 127) / 128 * 128, n = 0;
     if (!mul_ok(mp, (size_t)K, &n) || !mul_ok(n, 4, &n))
         return SIZE_MAX;
-    return n;
+    return n > SIZE_MAX - r ? SIZE_MAX : n + r;
 }
 
 int check_gemv_prepare(const float *a, int M, int K, const void *prep, size_t prep_bytes,
@@ -214,7 +216,7 @@ size_t gemm_bf16_workspace_bytes(int M, int N, int K)
     } else if (!mul_ok((size_t)M, (size_t)K, &n) || !mul_ok(n, 4, &n)) {
         return SIZE_MAX;
     }
-    const size_t r = gemm_bf16_row_exp_bytes(M);
+    const size_t r = gemm_row_exp_bytes(M);
     return n > SIZE_MAX - r ? SIZE_MAX : n + r;
 }
 
@@ -231,7 +233,7 @@ size_t gemm_q8a_workspace_bytes(int M, int N, int K)
     } else if (!mul_ok((size_t)M, (size_t)K, &n) || !mul_ok(n, 4, &n)) {
         return SIZE_MAX;
     }
-    const size_t r = gemm_bf16_row_exp_bytes(M);
+    const size_t r = gemm_row_exp_bytes(M);
     return n > SIZE_MAX - r ? SIZE_MAX : n + r;
 }
 

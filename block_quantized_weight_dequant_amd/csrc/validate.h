@@ -24,15 +24,17 @@ int check_product(const void *a, size_t a_elem, const void *w, size_t w_bytes, c
 int check_quantize(const float *x, size_t n_elems, const void *out, size_t out_bytes,
                    size_t block_bytes, bool *empty);
 
-// True when q4_gemm / q8_gemm take the split-activation path for this K (the
-// path that needs a workspace). The GEMM launcher branches on the same
-// predicate.
+// True when the GEMMs take the split-activation path for this K (with
+// M N < 2^31, the split kernel's 32-bit output offsets). The GEMM launchers
+// branch on the same predicate.
 // K <= 2^22 keeps every byte offset of the split kernel's buffer loads within
 // 32 bits.
 inline bool gemm_splits_activations(int K) { return K > 0 && K % 64 == 0 && K <= (1 << 22); }
 
-// Workspace bytes q4_gemm and q8_gemm need: 0 when none (no split path, or an empty or
-// invalid shape), SIZE_MAX when the size does not fit in size_t.
+// Workspace bytes the f32 GEMM (q4_gemm_ws, q8_gemm_ws) needs: the row
+// exponents, then on the split path ceil(M / 128) * 128 * K * 4 bytes of
+// two-term operands. 0 for an empty or invalid shape, SIZE_MAX when the size
+// does not fit in size_t.
 size_t gemm_workspace_bytes(int M, int N, int K);
 
 // The bfloat16 GEMM's split path: K % 64 == 0 and M N < 2^31 (the split
@@ -121,9 +123,9 @@ int check_gemv_prepared(const void *prep, size_t prep_bytes, const void *w, size
 // call does not split (then the workspace is not used).
 size_t gemv_splitk_workspace_bytes(int M, int N, int K, int requested, size_t block_bytes);
 
-// Bytes at the start of a bfloat16 GEMM workspace that hold the per-row
-// exponents (M int32, padded to 256 bytes); the activation operands follow.
-inline size_t gemm_bf16_row_exp_bytes(int M) { return ((size_t)M * 4 + 255) / 256 * 256; }
+// Bytes at the start of every GEMM workspace that hold the per-row exponents
+// (M int32, padded to 256 bytes); the activation operands follow.
+inline size_t gemm_row_exp_bytes(int M) { return ((size_t)M * 4 + 255) / 256 * 256; }
 
 // Workspace bytes q4_gemm_bf16 and q8_gemm_bf16 need: the row exponents, then
 // ceil(M / 128) * 128 * K binary16 operands on the split path or M * K f32

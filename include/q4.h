@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 8
+#define Q4_ABI_VERSION 9
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -90,35 +90,49 @@ int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
             int M, int N, int K, void *stream);
 
 /*
- * q4_gemm — prefill-shaped product y = a @ dequant(W)^T for any M >= 1
- * (section matmul_q4_0_tiled), tiled through LDS onto the matrix cores.
- *   Arguments, layouts and the accuracy statement are those of q4_gemv, with
- *   M >= 1 unbounded (M == 0 or N == 0 is an empty problem).
- *   Activations must satisfy |a| < 65504 (they are split into two binary16
- *   terms); results for larger activations are unspecified.
+ * q4_gemm_ws — prefill-shaped product y = a @ dequant(W)^T for any M >= 1
+ * (section matmul_q4_0_tiled), tiled through LDS onto the matrix cores, with
+ * the caller's scratch memory.
+ *   a, w_q, w_bytes, y, M, N, K: as q4_gemv, with M >= 1 unbounded (M == 0 or
+ *             N == 0 is an empty problem). Any finite activations: each row
+ *             of a is scaled by the power of two that puts its largest
+ *             magnitude in [2^14, 2^15), split into two binary16 terms
+ *             (within 2^-22 of each scaled element) and the result row is
+ *             scaled back.
  *   workspace, workspace_bytes: device scratch owned by the caller, at least
- *             q4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned, not
- *             overlapping a, W or y, and not used by other work while this
- *             call runs on `stream`. When that function returns 0 (K % 64 != 0,
- *             K > 2^22, M * N >= 2^31 or an empty problem) the workspace is not read or
- *             written and may be NULL. Errors, after those of q4_gemv's checks:
- *             Q4_ERR_SIZE if the needed size overflows size_t,
- *             Q4_ERR_WORKSPACE if workspace_bytes is smaller, then
- *             Q4_ERR_NULL, Q4_ERR_ALIGN, Q4_ERR_ALIAS for the pointer.
- *             The library allocates nothing, so the call may be captured in
- *             a HIP graph; its contents after the call are unspecified.
- * The reduction order is fixed, so repeated calls return identical bits.
+ *             q4_gemm_workspace_bytes(M, N, K) bytes (non-zero for every
+ *             non-empty shape), 16-byte aligned, not overlapping a, W or y,
+ *             and not used by other work while this call runs on `stream`.
+ *             Errors, after those of q4_gemv's checks: Q4_ERR_SIZE if the
+ *             needed size overflows size_t, Q4_ERR_WORKSPACE if
+ *             workspace_bytes is smaller, then Q4_ERR_NULL, Q4_ERR_ALIGN,
+ *             Q4_ERR_ALIAS for the pointer. The library allocates nothing,
+ *             so the call may be captured in a HIP graph; the workspace's
+ *             contents after the call are unspecified.
+ * Accuracy: |y - y_exact| <= 1e-5 * sum_k |a[m, k] * w[n, k]| + 1e-6 per
+ * element. The worst-case error is (36 + L + S) * 2^-24 of that sum, to first
+ * order: 4 for the split, 32 for a block's 32 products, L <= 112 block
+ * partials added in sequence per accumulator, and S K segments (longer K runs
+ * as several launches, each adding its part to y); S = ceil(K / 7168) when
+ * K % 64 == 0, K <= 2^22 and M * N < 2^31, else ceil(K / 3584) (one fewer
+ * term). This stays below 1e-5 for K <= 136192 (K <= 71680 on the other
+ * shapes). Binary16's floor adds a second term: each activation's split is
+ * within 2^-22 of it or within 2^-46 of its row's largest magnitude,
+ * whichever is larger, so a row whose magnitudes span more than 2^24 can add
+ * up to 2^-46 * max|a[m, :]| * sum_k |w[n, k]|. The reduction order is
+ * fixed, so repeated calls return identical bits.
  */
-int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
-            int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+int q4_gemm_ws(const float *a, const void *w_q, size_t w_bytes, float *y,
+               int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * q4_gemm_workspace_bytes — bytes of workspace q4_gemm needs for this shape:
- * ceil(M / 128) * 128 * K * 4 when K % 64 == 0, K <= 2^22 and M * N < 2^31 (the
- * activations split once into binary16 hi and lo terms, in matrix-core
- * operand order), 0 otherwise or
- * when M, N or K is invalid or the problem is empty, and SIZE_MAX when the
- * product does not fit in size_t. Pure function of its arguments.
+ * q4_gemm_workspace_bytes — bytes of workspace q4_gemm_ws needs for this
+ * shape: the row exponents (M int32, padded to a multiple of 256 bytes), then,
+ * when K % 64 == 0, K <= 2^22 and M * N < 2^31, ceil(M / 128) * 128 * K * 4
+ * bytes of operands (the scaled activations split once into binary16 hi and
+ * lo terms, in matrix-core operand order). 0 when M, N or K is invalid or the
+ * problem is empty, and SIZE_MAX when the size does not fit in size_t. Pure
+ * function of its arguments.
  */
 size_t q4_gemm_workspace_bytes(int M, int N, int K);
 
@@ -142,16 +156,16 @@ int q8_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
             int M, int N, int K, void *stream);
 
 /*
- * q8_gemm — q4_gemm over a Q8_0 weight stream, with w_bytes == N * (K/32) * 34.
- * Arguments, errors, the activation range, the workspace contract (with
- * q8_gemm_workspace_bytes) and determinism as q4_gemm.
+ * q8_gemm_ws — q4_gemm_ws over a Q8_0 weight stream, with w_bytes == N * (K/32)
+ * * 34. Arguments, errors, accuracy, the workspace contract (with
+ * q8_gemm_workspace_bytes) and determinism as q4_gemm_ws.
  */
-int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
-            int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
+int q8_gemm_ws(const float *a, const void *w_q, size_t w_bytes, float *y,
+               int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * q8_gemm_workspace_bytes — bytes of workspace q8_gemm needs for this shape;
- * the same function of (M, N, K) as q4_gemm_workspace_bytes.
+ * q8_gemm_workspace_bytes — bytes of workspace q8_gemm_ws needs for this
+ * shape; the same function of (M, N, K) as q4_gemm_workspace_bytes.
  */
 size_t q8_gemm_workspace_bytes(int M, int N, int K);
 

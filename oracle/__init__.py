@@ -296,6 +296,18 @@ def max_threads() -> int:
     return int(_load().orc_max_threads())
 
 
+#: The products' parity bar: |y_gpu - y_ref| <= REL_TOL * B + ABS_TOL, with B
+#: the bound sum_k |a[m, k] w[n, k]| that the product functions return.
+REL_TOL = 1e-5
+ABS_TOL = 1e-6
+
+
 def tolerance(bound: np.ndarray) -> np.ndarray:
     """The product's parity tolerance, |y_gpu - y_ref| <= 1e-5 * B + 1e-6."""
-    return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-6
+    return REL_TOL * np.asarray(bound, dtype=np.float64) + ABS_TOL
+
+
+def tolerance_relative(bound: np.ndarray) -> np.ndarray:
+    """The bar's relative term alone, 1e-5 * B: for inputs whose results are
+    so small that the absolute 1e-6 would pass any output."""
+    return REL_TOL * np.asarray(bound, dtype=np.float64)

@@ -86,7 +86,7 @@ BLOCK_BYTES = {"q4": 18, "q8": 34}
 
 
 def _prod(entry, a, w, wb, y, M, N, K):
-    if entry.endswith(("_gemm", "_gemm_bf16")):   # no workspace: these checks come before its own
+    if entry.endswith(("_gemm_ws", "_gemm_bf16")):   # no workspace: these checks come before its own
         return binding.raw_status(entry, a, w, wb, y, M, N, K, 0, 0, 0)
     return binding.raw_status(entry, a, w, wb, y, M, N, K, 0)
 
@@ -96,7 +96,7 @@ def _wb(N, K, fmt="q4"):
 
 
 @fake_addresses
-@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm", "q8_gemv", "q8_gemm", "q4_gemm_bf16",
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm_ws", "q8_gemv", "q8_gemm_ws", "q4_gemm_bf16",
                                    "q8_gemm_bf16", "q4_gemv_bf16", "q8_gemv_bf16"])
 def test_product_argument_checks(entry):
     S = binding
@@ -132,7 +132,7 @@ def test_bf16_activations_are_two_bytes(f):
     # an output at a + 256 overlaps the f32 form only. The bfloat16 call then
     # passes every product check and stops at its (missing) workspace.
     wb = _wb(4, 64, f)
-    assert _prod(f + "_gemm", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_ALIAS
+    assert _prod(f + "_gemm_ws", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_ALIAS
     assert _prod(f + "_gemm_bf16", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_WORKSPACE
     assert _prod(f + "_gemm_bf16", A, W, wb, A + 240, 2, 4, 64) == binding.Q4_ERR_ALIAS
     assert _prod(f + "_gemv", A, W, wb, A + 256, 2, 4, 64) == binding.Q4_ERR_ALIAS
@@ -195,7 +195,7 @@ def test_rejected_call_writes_nothing():
     y = np.full(64, 7.0, dtype=np.float32)
     a = np.ones(64, dtype=np.float32)
     w = np.zeros(4 * 18, dtype=np.uint8)
-    st = binding.raw_status("q4_gemm", a.ctypes.data, w.ctypes.data, w.size + 1, y.ctypes.data,
+    st = binding.raw_status("q4_gemm_ws", a.ctypes.data, w.ctypes.data, w.size + 1, y.ctypes.data,
                             1, 2, 64, 0, 0, 0)
     assert st == binding.Q4_ERR_SIZE
     assert (y == 7.0).all()
@@ -204,19 +204,22 @@ def test_rejected_call_writes_nothing():
 @pytest.mark.parametrize("fn", ["q4_gemm_workspace_bytes", "q8_gemm_workspace_bytes"])
 def test_gemm_workspace_bytes(fn):
     f = getattr(binding, fn)
-    # Rows padded to whole 128-row tiles, binary16 hi and lo per element.
-    assert f(1, 1, 64) == 128 * 64 * 4
-    assert f(128, 7, 4096) == 128 * 4096 * 4
-    assert f(129, 7, 4096) == 256 * 4096 * 4
-    assert f(1024, 4096, 4096) == 1024 * 4096 * 4
-    assert f(2 ** 31 - 1, 1, 2 ** 22) == 2 ** 31 * 2 ** 22 * 4
-    assert f(65536, 32767, 64) == 65536 * 64 * 4
-    # No split path (K % 64 != 0, K > 2^22, or M N >= 2^31: the general kernel),
-    # empty or invalid shapes: no workspace.
+    # Row exponents (int32, padded to 256 bytes), then the rows padded to whole
+    # 128-row tiles, binary16 hi and lo per element.
+    assert f(1, 1, 64) == 256 + 128 * 64 * 4
+    assert f(128, 7, 4096) == 512 + 128 * 4096 * 4
+    assert f(129, 7, 4096) == 768 + 256 * 4096 * 4
+    assert f(1024, 4096, 4096) == 4096 + 1024 * 4096 * 4
+    assert f(2 ** 31 - 1, 1, 2 ** 22) == 2 ** 33 + 2 ** 31 * 2 ** 22 * 4
+    assert f(65536, 32767, 64) == 65536 * 4 + 65536 * 64 * 4
+    # No split path (K % 64 != 0, K > 2^22, or M N >= 2^31: the general kernel):
+    # the row exponents only.
     for M, N, K in [(5, 5, 96), (5, 5, 32), (5, 5, 4128), (5, 5, 2 ** 22 + 64), (5, 5, 2 ** 31 - 64),
-                    (65536, 32768, 64), (2 ** 31 - 1, 2, 64),
-                    (0, 5, 64), (5, 0, 64), (-1, 5, 64),
-                    (5, -1, 64), (5, 5, 48), (5, 5, 0), (5, 5, -64)]:
+                    (65536, 32768, 64), (2 ** 31 - 1, 2, 64)]:
+        assert f(M, N, K) == ((M * 4 + 255) // 256) * 256, (M, N, K)
+    # Empty or invalid shapes: no workspace.
+    for M, N, K in [(0, 5, 64), (5, 0, 64), (-1, 5, 64), (5, -1, 64), (5, 5, 48), (5, 5, 0),
+                    (5, 5, -64)]:
         assert f(M, N, K) == 0, (M, N, K)
 
 
@@ -241,16 +244,14 @@ def test_gemm_bf16_workspace_bytes(fn):
 
 
 @fake_addresses
-@pytest.mark.parametrize("g", ["q4_gemm", "q8_gemm", "q4_gemm_bf16", "q8_gemm_bf16"])
+@pytest.mark.parametrize("g", ["q4_gemm_ws", "q8_gemm_ws", "q4_gemm_bf16", "q8_gemm_bf16"])
 @pytest.mark.parametrize("K", [64, 96])
 def test_gemm_workspace_checks(g, K):
     S = binding
     f = g[:2]
     M, N = 3, 4
-    need = getattr(binding, g + "_workspace_bytes")(M, N, K)
-    if need == 0:   # only the f32 GEMM with K % 64 != 0 takes no workspace
-        assert g.endswith("_gemm") and K % 64
-        return
+    need = getattr(binding, g.replace("_ws", "") + "_workspace_bytes")(M, N, K)
+    assert need > 0   # every non-empty shape takes a workspace
     WS = BASE + (3 << 32)
     wbn = _wb(N, K, f)
     st = lambda ws, wsb: binding.raw_status(g, A, W, wbn, Y, M, N, K, ws, wsb, 0)
@@ -347,7 +348,8 @@ def test_gemv_prepare_checks(f):
 @fake_addresses
 def test_binding_raises_q4error():
     with pytest.raises(binding.Q4Error) as e:
-        binding.q4_gemm(A, W, Y, 1, 4, 48, w_bytes=_wb(4, 64), stream=0)
+        binding.q4_gemm_ws(A, W, Y, 1, 4, 48, w_bytes=_wb(4, 64), stream=0, workspace=A + 4096,
+                           workspace_bytes=4096)
     assert e.value.status == binding.Q4_ERR_SHAPE
 
 

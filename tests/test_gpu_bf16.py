@@ -23,7 +23,7 @@ from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_
 
 GEMM_BF16 = {"q4_0": binding.q4_gemm_bf16, "q8_0": binding.q8_gemm_bf16}
 GEMV_BF16 = {"q4_0": binding.q4_gemv_bf16, "q8_0": binding.q8_gemv_bf16}
-GEMM_F32 = {"q4_0": binding.q4_gemm, "q8_0": binding.q8_gemm}
+GEMM_F32 = {"q4_0": binding.q4_gemm_ws, "q8_0": binding.q8_gemm_ws}
 GEMV_F32 = {"q4_0": binding.q4_gemv, "q8_0": binding.q8_gemv}
 WS_BYTES = {"q4_0": binding.q4_gemm_bf16_workspace_bytes,
             "q8_0": binding.q8_gemm_bf16_workspace_bytes}

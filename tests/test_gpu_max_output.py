@@ -35,13 +35,13 @@ def _gathered(y, mi, ni):
 
 @pytest.mark.parametrize("act", ["f32", "bf16", "q8_0"])
 def test_gemm_output_of_2_31_elements(act):
-    assert binding.q4_gemm_workspace_bytes(M, N, K) == 0
+    assert binding.q4_gemm_workspace_bytes(M, N, K) == M * 4   # row exponents only
     blob = weight_blob("q4_0", N, K, 83)
     a32 = wl.activations_f32(84, M, K)
     y = torch.full((M * N,), float("nan"), dtype=torch.float32, device=DEV)
     mi, ni = _samples()
     if act == "f32":
-        binding.q4_gemm(to_dev(a32), to_dev(blob), y, M, N, K)
+        binding.q4_gemm_ws(to_dev(a32), to_dev(blob), y, M, N, K)
         ref, bound = oracle.q4_0_matmul_sampled(a32, blob, N, K, mi, ni)
     elif act == "bf16":
         bits = wl.activations_bf16(84, M, K)

@@ -1,5 +1,5 @@
 """GPU parity of the block-quantized x f32 products against the oracle:
-q4_gemv / q4_gemm over Q4_0 weights and q8_gemv / q8_gemm over Q8_0 weights
+q4_gemv / q4_gemm_ws over Q4_0 weights and q8_gemv / q8_gemm_ws over Q8_0 weights
 (sections qmatvec_q4_0 and matmul_q4_0_tiled of "fuel-vulkan-kernels —
 quantized (GGML) kernel contracts", whose quantized-matmul binding picks
 either block format; blocks of sections dequant_q4_0 and dequant_q8_0).
@@ -20,8 +20,8 @@ from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
 from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_matmul,  # noqa: E402
                          oracle_matmul_sampled, random_blocks, to_dev, weight_blob)
 
-ENTRY = {("q4_0", "gemv"): binding.q4_gemv, ("q4_0", "gemm"): binding.q4_gemm,
-         ("q8_0", "gemv"): binding.q8_gemv, ("q8_0", "gemm"): binding.q8_gemm}
+ENTRY = {("q4_0", "gemv"): binding.q4_gemv, ("q4_0", "gemm"): binding.q4_gemm_ws,
+         ("q8_0", "gemv"): binding.q8_gemv, ("q8_0", "gemm"): binding.q8_gemm_ws}
 WS_BYTES = {"q4_0": binding.q4_gemm_workspace_bytes, "q8_0": binding.q8_gemm_workspace_bytes}
 
 
@@ -35,10 +35,10 @@ def _run(fmt, kind, a: np.ndarray, blob: np.ndarray, N: int, K: int, w_dev=None)
     return y.host().reshape(M, N)
 
 
-def _full_check(fmt, kind, a, blob, N, K, what):
+def _full_check(fmt, kind, a, blob, N, K, what, relative_only=False):
     got = _run(fmt, kind, a, blob, N, K)
     ref, bound = oracle_matmul(fmt)(a, blob, N, K)
-    return assert_within_tolerance(got, ref, bound, "%s %s" % (fmt, what))
+    return assert_within_tolerance(got, ref, bound, "%s %s" % (fmt, what), relative_only)
 
 
 # ------------------------------------------------------------- the workloads
@@ -87,7 +87,13 @@ def test_gemv_shapes(fmt, M, N, K):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M,N,K", [(1, 300, 256), (8, 129, 64), (65, 70, 160), (5, 257, 128),
                                    (33, 6144, 2048), (128, 128, 32), (129, 129, 96),
-                                   (300, 17, 4128), (257, 384, 512), (1, 1, 32)])
+                                   (300, 17, 4128), (257, 384, 512), (1, 1, 32),
+                                   # Longer K runs in segments of at most 112 block
+                                   # partials per accumulator: 2 segments at K = 14336
+                                   # (the FFN down-projection), 3 at 16384; the general
+                                   # kernel (K % 64 != 0) at 7200 takes 3 of 75 blocks.
+                                   (96, 200, 14336), (130, 160, 16384), (40, 96, 7200),
+                                   (3, 33, 7168), (17, 40, 7232)])
 def test_gemm_shapes(fmt, M, N, K):
     blob = weight_blob(fmt, N, K, 3 * M + N)
     a = wl.activations_f32(5 * M + K, M, K)
@@ -146,12 +152,61 @@ def test_zero_activations(fmt, kind):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("kind", ["gemv", "gemm"])
-@pytest.mark.parametrize("scale", [1e-20, 1e-6, 1e-3, 1e3, 6e4])
+@pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e-8, 1e-3, 1e3, 6e4, 1e5, 1e30])
 def test_activation_magnitudes(fmt, kind, scale):
+    # Any finite activations, unclipped (up to 4e30 and down into the f32
+    # subnormals), against weights with |d| in [1024, 8192): |y| stays far
+    # from both the f32 range's ends, and the check drops the bar's absolute
+    # 1e-6, which would pass anything at the small scales.
     N, K, M = 80, 2048, 4
-    a = wl.activations_f32(6, M, K) * np.float32(scale)
-    a = np.clip(a, -65000, 65000).astype(np.float32)
-    _full_check(fmt, kind, a, weight_blob(fmt, N, K, 7), N, K, "%s scale %g" % (kind, scale))
+    a = (wl.activations_f32(6, M, K) * np.float32(scale)).astype(np.float32)
+    blob = random_blocks(fmt, N * K // 32, 7, 25, 28)
+    _full_check(fmt, kind, a, blob, N, K, "%s scale %g" % (kind, scale), relative_only=True)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind,M", [("gemv", 1), ("gemv", 8), ("gemm", 70)])
+def test_power_of_two_row_scaling_is_exact(fmt, kind, M):
+    # Row m scaled by 2^k_m (|k| up to 100, so activations reach 1.6e30)
+    # scales row m of y by exactly 2^k_m, bit for bit: each row's (or K
+    # stretch's) own power of two absorbs the factor before the split.
+    N, K = 96, 2048
+    blob = weight_blob(fmt, N, K, 61)
+    a = wl.activations_f32(62, M, K)
+    ks = np.array([100, -100, 37, -61, 0, 90, -1, 12] * ((M + 7) // 8))[:M]
+    a2 = (a * np.ldexp(np.float32(1), ks)[:, None]).astype(np.float32)
+    y1 = _run(fmt, kind, a, blob, N, K)
+    y2 = _run(fmt, kind, a2, blob, N, K)
+    want = (y1 * np.ldexp(np.float32(1), ks)[:, None]).astype(np.float32)
+    assert np.array_equal(y2.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_tiny_activations_against_large_scales(fmt, kind):
+    # Rows of very different magnitudes in one call, tiny ones included,
+    # against |d| in [1024, 8192): every row must meet the relative bar on its
+    # own, which rules out a scale shared across rows.
+    N, K, M = 72, 1024, 5
+    a = wl.activations_f32(63, M, K)
+    for m, s in enumerate([1e-30, 1e-8, 1.0, 7e4, 3e29]):
+        a[m] *= np.float32(s)
+    blob = random_blocks(fmt, N * K // 32, 64, 25, 28)
+    _full_check(fmt, kind, a, blob, N, K, "%s rows 1e-30 .. 3e29" % kind, relative_only=True)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_ffn_down_projection_sampled(fmt):
+    # 512 x 4096 x 14336: the long-K GEMM (two K segments), sampled outputs.
+    M, N, K = 512, 4096, 14336
+    blob = weight_blob(fmt, N, K, 65)
+    a = wl.activations_f32(66, M, K)
+    got = _run(fmt, "gemm", a, blob, N, K)
+    mi = np.concatenate([wl.uniform_ints(67, 0, M, 2048), np.arange(M), np.full(N, M - 1)])
+    ni = np.concatenate([wl.uniform_ints(68, 0, N, 2048), np.full(M, N - 1), np.arange(N)])
+    ref, bound = oracle_matmul_sampled(fmt)(a, blob, N, K, mi, ni)
+    assert np.isfinite(got).all()
+    assert_within_tolerance(got[mi, ni], ref, bound, "%s gemm %dx%dx%d" % (fmt, M, N, K))
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -268,7 +323,7 @@ def test_gemm_workspace_exact_size_and_garbage(fmt):
     # written.
     M, N, K = 130, 200, 512
     need = WS_BYTES[fmt](M, N, K)
-    assert need == 256 * K * 4
+    assert need == 768 + 256 * K * 4
     ws = Guarded(need, torch.uint8)
     ws.view.fill_(0x7F)                      # binary16 NaN patterns everywhere
     blob = weight_blob(fmt, N, K, 21)

@@ -19,7 +19,7 @@ from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
 from gpu_helpers import Guarded, assert_within_tolerance, to_dev, weight_blob  # noqa: E402
 
-KINDS = ["gemv", "gemm", "gemv_bf16", "gemm_bf16", "gemv_q8a", "gemm_q8a", "gemv_splitk"]
+KINDS = ["gemv", "gemm_ws", "gemv_bf16", "gemm_bf16", "gemv_q8a", "gemm_q8a", "gemv_splitk"]
 
 
 def _case(i):

@@ -582,3 +582,10 @@ def test_tolerance_is_the_stated_bar(orc):
     for B in (0.0, 1e-3, 1.0, 37.25, 1e4, 1e9):
         bar = 1e-5 * B + 1e-6
         assert bar * (1 - 1e-9) <= orc.tolerance(B) <= bar * (1 + 1e-9)
+    # The relative term alone, for results far below the absolute 1e-6.
+    assert orc.tolerance_relative(0.0) == 0.0
+    assert orc.tolerance_relative(1.0) == 1e-5
+    for B in (2e-23, 3.5e-30, 1.0, 6e37):
+        assert orc.tolerance_relative(B) == pytest.approx(1e-5 * B, rel=1e-12, abs=0.0)
+    r = orc.tolerance_relative(b)
+    assert r.shape == b.shape and np.allclose(r, expected - 1e-6, rtol=1e-9, atol=0.0)

@@ -32,10 +32,11 @@ PLANTED = [
     ("oracle.c", "float d = amax / 127.0f;", "float d = amax / 128.0f;", "Q8_0 scale /128"),
     ("__init__.py", "return q8_0_dequant(b).reshape(M, K)", "return q8_0_dequant(b).reshape(K, M).T.copy()",
      "quantized-activation stream transposed"),
-    ("__init__.py", "return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-6",
-     "return 1e-4 * np.asarray(bound, dtype=np.float64) + 1e-6", "parity bar loosened to 1e-4 relative"),
-    ("__init__.py", "return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-6",
-     "return 1e-5 * np.asarray(bound, dtype=np.float64) + 1e-5", "parity bar floor loosened to 1e-5"),
+    ("__init__.py", "REL_TOL = 1e-5", "REL_TOL = 1e-4", "parity bar loosened to 1e-4 relative"),
+    ("__init__.py", "ABS_TOL = 1e-6", "ABS_TOL = 1e-5", "parity bar floor loosened to 1e-5"),
+    ("__init__.py", "return REL_TOL * np.asarray(bound, dtype=np.float64) + ABS_TOL",
+     "return REL_TOL * np.abs(np.asarray(bound, dtype=np.float64)) * 10 + ABS_TOL",
+     "parity bar's relative term ten times too loose"),
 ]
 
 

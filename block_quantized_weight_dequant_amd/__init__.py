@@ -5,7 +5,7 @@ ctypes layer over it with the same function names. ``workloads`` holds the
 seeded synthetic inputs. The binding is imported on first use, so importing the
 package does not require the built library.
 """
-_BINDING_NAMES = ("q4_dequant", "q4_gemv", "q4_gemm_ws", "q8_quantize", "q4_quantize",
+_BINDING_NAMES = ("q4_dequant", "q4_gemv", "q4_gemm", "q4_gemm_ws", "q8_quantize", "q4_quantize",
                   "q4_status_string", "q4_abi_version", "Q4Error")
 
 

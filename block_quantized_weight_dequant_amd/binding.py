@@ -26,11 +26,12 @@ Q4_ERR_ALIAS = 5
 Q4_ERR_LAUNCH = 6
 Q4_ERR_WORKSPACE = 7
 Q4_GEMV_MAX_ROWS = 8
+Q4_GEMM_SCRATCH_BYTES = 64 << 20
 SIZE_MAX = 2 ** 64 - 1
 
 #: Every symbol include/q4.h declares.
-EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm_ws",
-           "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm_ws",
+EXPORTS = ("q4_abi_version", "q4_status_string", "q4_dequant", "q4_gemv", "q4_gemm",
+           "q4_gemm_ws", "q4_gemm_workspace_bytes", "q8_dequant", "q8_gemv", "q8_gemm", "q8_gemm_ws",
            "q8_gemm_workspace_bytes", "q8_quantize", "q4_quantize", "q4_gemm_bf16",
            "q4_gemm_bf16_workspace_bytes", "q8_gemm_bf16", "q8_gemm_bf16_workspace_bytes",
            "q4_gemv_bf16", "q8_gemv_bf16", "q4_gemv_splitk", "q4_gemv_splitk_workspace_bytes",
@@ -65,7 +66,7 @@ def _load_library():
     for f in ("q4", "q8"):
         getattr(lib, f + "_dequant").restype = i32
         getattr(lib, f + "_dequant").argtypes = [P, sz, P, sz, P]
-        for g in ("_gemv", "_gemv_bf16"):
+        for g in ("_gemv", "_gemv_bf16", "_gemm"):
             getattr(lib, f + g).restype = i32
             getattr(lib, f + g).argtypes = [P, P, sz, P, i32, i32, i32, P]
         for g in ("_gemm_ws", "_gemm_bf16"):
@@ -370,6 +371,18 @@ def _gemm(entry, a, w_q, y, M, N, K, w_bytes, stream, workspace, workspace_bytes
         wsb = _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0
     _check(getattr(lib, entry)(_addr(a), _addr(w_q), wb, _addr(y), int(M), int(N), int(K),
                                _addr(ws), wsb, _stream(stream)), entry)
+
+
+def q4_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """y[M, N] = a[M, K] @ dequant(W[N, K/32])^T for any M, W Q4_0, with no
+    workspace: the library's own device scratch (Q4_GEMM_SCRATCH_BYTES per
+    GPU) serves it, so calls that overlap in time on one GPU race."""
+    _gemv("q4_gemm", a, w_q, y, M, N, K, w_bytes, stream)
+
+
+def q8_gemm(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None) -> None:
+    """As q4_gemm, with W a Q8_0 stream (the same scratch)."""
+    _gemv("q8_gemm", a, w_q, y, M, N, K, w_bytes, stream)
 
 
 def q4_gemm_ws(a, w_q, y, M: int, N: int, K: int, w_bytes=None, stream=None, workspace=None,

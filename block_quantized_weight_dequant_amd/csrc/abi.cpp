@@ -74,6 +74,17 @@ static int gemm(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const
                                      workspace, as_stream(stream)));
 }
 
+static int gemm_noalloc(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const void *w_q,
+                        size_t w_bytes, float *y, int M, int N, int K, void *stream)
+{
+    bool empty = false;
+    int st = q4v::check_product(a, sizeof(float), w_q, w_bytes, y, M, N, K, 0, block_bytes, &empty);
+    if (st != Q4_OK || empty)
+        return st;
+    return launched(q4k::launch_gemm_noalloc(fmt, a, static_cast<const uint8_t *>(w_q), y, M, N, K,
+                                             as_stream(stream)));
+}
+
 static int gemv_splitk(q4k::WeightFormat fmt, size_t block_bytes, const float *a, const void *w_q,
                        size_t w_bytes, float *y, int M, int N, int K, int splits, void *workspace,
                        size_t workspace_bytes, void *stream)
@@ -208,6 +219,18 @@ Q4_EXPORT size_t q4_gemm_workspace_bytes(int M, int N, int K)
 Q4_EXPORT size_t q8_gemm_workspace_bytes(int M, int N, int K)
 {
     return q4v::gemm_workspace_bytes(M, N, K);
+}
+
+Q4_EXPORT int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                      void *stream)
+{
+    return gemm_noalloc(q4k::WeightFormat::kQ4_0, 18, a, w_q, w_bytes, y, M, N, K, stream);
+}
+
+Q4_EXPORT int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N, int K,
+                      void *stream)
+{
+    return gemm_noalloc(q4k::WeightFormat::kQ8_0, 34, a, w_q, w_bytes, y, M, N, K, stream);
 }
 
 Q4_EXPORT int q4_gemm_ws(const float *a, const void *w_q, size_t w_bytes, float *y, int M, int N,

@@ -46,6 +46,8 @@
 // The slot order of the operands and the decode of the weight bytes are the
 // format's (formats.h); where the decode leaves a factor 2^kHiLog2 on slots
 // 4..7 (Q4_0), the activations of those slots carry 2^-kHiLog2.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -964,10 +966,11 @@ static hipError_t launch_any_segments(const float *a, const uint8_t *w, float *y
 }
 
 // workspace: the row exponents (q4v::gemm_row_exp_bytes(M)), then on the split
-// path the two-term operands.
+// path (split: the caller's choice, q4v::gemm_splits_activations(K) with
+// M N < 2^31) the two-term operands.
 template <class F>
 static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int M, int N, int K,
-                                void *workspace, hipStream_t s)
+                                void *workspace, hipStream_t s, bool split)
 {
     const int tiles_m = (M + kGemmBM - 1) / kGemmBM, tiles_n = (N + kGemmBN - 1) / kGemmBN;
     const long long T = (long long)tiles_m * tiles_n;
@@ -978,8 +981,7 @@ static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int 
                                  dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
     if (e != hipSuccess)
         return e;
-    if (!q4v::gemm_splits_activations(K) ||
-        (long long)M * N >= (1LL << 31))   // the split kernel stores with 32-bit offsets
+    if (!split)
         return launch_any_segments<F>(a, w, y, M, N, K, tiles_m, tiles_n, row_exp, 1, s);
     u32x4 *ahl = reinterpret_cast<u32x4 *>(static_cast<char *>(workspace) +
                                            q4v::gemm_row_exp_bytes(M));
@@ -1034,12 +1036,108 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
                                           row_exp, s);
 }
 
+// The split kernel stores with 32-bit offsets: M N < 2^31 on its path.
+static bool gemm_f32_splits(int M, int N, int K)
+{
+    return q4v::gemm_splits_activations(K) && (long long)M * N < (1LL << 31);
+}
+
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
                        int K, void *workspace, hipStream_t s)
 {
+    const bool split = gemm_f32_splits(M, N, K);
     if (fmt == WeightFormat::kQ8_0)
-        return launch_gemm_f<FmtQ8_0>(a, w, y, M, N, K, workspace, s);
-    return launch_gemm_f<FmtQ4_0>(a, w, y, M, N, K, workspace, s);
+        return launch_gemm_f<FmtQ8_0>(a, w, y, M, N, K, workspace, s, split);
+    return launch_gemm_f<FmtQ4_0>(a, w, y, M, N, K, workspace, s, split);
+}
+
+// ---------------------------------------------------------------------------
+// The f32 GEMM with no workspace argument (q4_gemm, q8_gemm): for callers that
+// cannot allocate. Its scratch, the row exponents and two-term operands of one
+// chunk of rows, is this file-scope device array, which every GPU the library
+// runs on holds (its own copy) until the process ends. On the host the array's
+// name denotes a host-side stand-in, not device memory, so host code uses only
+// the address hipGetSymbolAddress returns for the device a call runs on,
+// looked up once per device (with that device current) and kept.
+//
+// Rows are taken in chunks whose workspace fits the array: multiples of 128
+// rows on the split path, so every 128-row tile computes exactly what it would
+// in one launch over all rows (the result equals q4_gemm_ws's bit for bit).
+// Every kernel writes the scratch it reads before reading it, so nothing has to
+// start at zero; calls that overlap in time on one GPU share the array and
+// race.
+static __device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex scratch_mu;
+std::atomic<void *> scratch_ptr[kScratchDevices];
+}  // namespace
+
+// The device address of `scratch` on the device of stream s (the current
+// device for the null stream).
+static hipError_t scratch_address(hipStream_t s, void **out)
+{
+    int dev = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = 0;
+            if ((e = hipGetDevice(&cur)) != hipSuccess)
+                return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+                return e;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t back = hipSetDevice(cur);
+                if (e == hipSuccess)
+                    e = back;
+            }
+            if (e != hipSuccess || !p)
+                return e != hipSuccess ? e : hipErrorInvalidSymbol;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t launch_gemm_noalloc(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M,
+                               int N, int K, hipStream_t s)
+{
+    void *scr = nullptr;
+    hipError_t e = scratch_address(s, &scr);
+    if (e != hipSuccess)
+        return e;
+    bool split = gemm_f32_splits(M, N, K);
+    long long rows = 0;
+    if (split) {
+        // q4v::gemm_workspace_bytes(R, N, K) = pad256(4 R) + R K 4 for R a
+        // multiple of 128 (<= 256 + R (K 4 + 4)).
+        rows = (long long)((kGemmScratchBytes - 256) / ((size_t)K * 4 + 4)) / kGemmBM * kGemmBM;
+        if (rows < kGemmBM)
+            split = false;   // K too long for one tile of operands: the general kernel
+    }
+    if (!split)
+        rows = (long long)(kGemmScratchBytes / 4) / 256 * 256;   // the row exponents only
+    for (long long r0 = 0; r0 < M; r0 += rows) {
+        const int rc = (int)(M - r0 < rows ? M - r0 : rows);
+        const float *ac = a + r0 * K;
+        float *yc = y + r0 * N;
+        e = fmt == WeightFormat::kQ8_0
+                ? launch_gemm_f<FmtQ8_0>(ac, w, yc, rc, N, K, scr, s, split)
+                : launch_gemm_f<FmtQ4_0>(ac, w, yc, rc, N, K, scr, s, split);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,

@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "q4.h"
 #include "validate.h"
 
 namespace q4k {
@@ -40,6 +41,12 @@ hipError_t launch_gemv_splitk(WeightFormat fmt, const float *a, const uint8_t *w
 // exponents, then on the split path the two-term operands).
 hipError_t launch_gemm(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M, int N,
                        int K, void *workspace, hipStream_t s);
+// The same without a workspace: the library's own device scratch of
+// kGemmScratchBytes per GPU, rows taken in chunks that fit it. Calls that
+// overlap in time on one GPU race on the scratch.
+constexpr size_t kGemmScratchBytes = Q4_GEMM_SCRATCH_BYTES;
+hipError_t launch_gemm_noalloc(WeightFormat fmt, const float *a, const uint8_t *w, float *y, int M,
+                               int N, int K, hipStream_t s);
 // a: [M, K] bfloat16 bit patterns. workspace:
 // q4v::gemm_bf16_workspace_bytes(M, N, K) bytes (always used).
 hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *w, float *y, int M,

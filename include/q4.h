@@ -18,7 +18,9 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a DEVICE pointer owned by the caller; the library
- *     allocates and frees nothing and keeps no state between calls.
+ *     allocates and frees nothing and keeps no state between calls, except
+ *     the device scratch of q4_gemm and q8_gemm (below), whose contents no
+ *     call relies on.
  *   - Every pointer must be 16-byte aligned (the pages' alignment_bytes: 16),
  *     else Q4_ERR_ALIGN. Arrays are dense and contiguous; f32 matrices are
  *     row-major.
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define Q4_ABI_VERSION 9
+#define Q4_ABI_VERSION 10
 
 #define Q4_OK 0
 #define Q4_ERR_NULL 1   /* a required pointer is NULL */
@@ -57,6 +59,9 @@ extern "C" {
 
 /* Largest number of activation rows q4_gemv and q8_gemv accept. */
 #define Q4_GEMV_MAX_ROWS 8
+
+/* Bytes of device memory each GPU holds for q4_gemm and q8_gemm (64 MiB). */
+#define Q4_GEMM_SCRATCH_BYTES 67108864u
 
 /* Returns Q4_ABI_VERSION of the library actually loaded. */
 int q4_abi_version(void);
@@ -87,6 +92,33 @@ int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, vo
  * element. The reduction order is fixed, so repeated calls return identical bits.
  */
 int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
+            int M, int N, int K, void *stream);
+
+/*
+ * q4_gemm — the prefill GEMM of q4_gemm_ws with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The operation is
+ * section matmul_q4_0_tiled's, y = a @ dequant(W)^T for any M >= 1.
+ *   a, w_q, w_bytes, y, M, N, K, stream: as q4_gemm_ws; errors as q4_gemm_ws's
+ *             checks before its workspace; no size is rejected.
+ * Scratch: the library's own device array of Q4_GEMM_SCRATCH_BYTES, held by
+ * each GPU the library runs on until the process ends (its address is looked
+ * up on the first call on a device). The call allocates and frees nothing.
+ * Rows are taken in chunks whose row exponents and operands fit the array
+ * (whole 128-row tiles; 16384 rows at K = 4096), one after another on
+ * `stream`, so the results equal q4_gemm_ws's bit for bit; for K >= 131072 a
+ * tile's operands do not fit and the general kernel runs (the accuracy bound
+ * of q4_gemm_ws's general-kernel shapes). Calls that overlap in time on one
+ * GPU (on different streams, or from different threads) share the array and
+ * race: the caller orders them, or uses q4_gemm_ws with its own workspaces.
+ * Accuracy and determinism as q4_gemm_ws.
+ */
+int q4_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
+            int M, int N, int K, void *stream);
+
+/* q8_gemm — q4_gemm over a Q8_0 weight stream (w_bytes == N * (K/32) * 34),
+ * for the same callers; it shares q4_gemm's scratch array (and its race). */
+int q8_gemm(const float *a, const void *w_q, size_t w_bytes, float *y,
             int M, int N, int K, void *stream);
 
 /*

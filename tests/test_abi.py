@@ -72,7 +72,8 @@ def test_version_and_status_codes():
     defs = _header_defines()
     assert binding.q4_abi_version() == defs["Q4_ABI_VERSION"]
     for name in ("Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_SIZE", "Q4_ERR_ALIGN",
-                 "Q4_ERR_ALIAS", "Q4_ERR_LAUNCH", "Q4_ERR_WORKSPACE", "Q4_GEMV_MAX_ROWS"):
+                 "Q4_ERR_ALIAS", "Q4_ERR_LAUNCH", "Q4_ERR_WORKSPACE", "Q4_GEMV_MAX_ROWS",
+                 "Q4_GEMM_SCRATCH_BYTES"):
         assert getattr(binding, name) == defs[name]
     strings = {binding.q4_status_string(c) for c in range(0, 8)}
     assert len(strings) == 8 and binding.q4_status_string(99) == "unknown status"
@@ -96,7 +97,8 @@ def _wb(N, K, fmt="q4"):
 
 
 @fake_addresses
-@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm_ws", "q8_gemv", "q8_gemm_ws", "q4_gemm_bf16",
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm", "q4_gemm_ws", "q8_gemv", "q8_gemm",
+                                   "q8_gemm_ws", "q4_gemm_bf16",
                                    "q8_gemm_bf16", "q4_gemv_bf16", "q8_gemv_bf16"])
 def test_product_argument_checks(entry):
     S = binding

@@ -90,6 +90,9 @@ def parse_args():
     p.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
     p.add_argument("--mfma", help="rocprofv3 --pmc SQ_* output directory")
     p.add_argument("--out", default=PROFILES)
+    p.add_argument("--probe-sweep", action="store_true",
+                   help="sweep the streaming-read probe's launch shapes (no other rows)")
+    p.add_argument("--sweep-out", help="write the sweep table here")
     return p.parse_args()
 
 
@@ -503,6 +506,64 @@ def bench_stream_ceiling(torch, nbytes, steps, warmup, reps, profile, cold=True)
     return row
 
 
+def probe_sweep(torch, sizes, steps, warmup, reps, out_path=None):
+    """The streaming read (libq4probe) of each size, cold, over every launch
+    shape q4probe_stream_read_cfg offers: threads per workgroup x loads per
+    thread x plain / non-temporal loads x grid-strided / blocked. The fastest shape at a size is the
+    practical ceiling of one launch that reads that many bytes."""
+    path = os.path.join(ROOT, "block_quantized_weight_dequant_amd", "libq4probe.so")
+    lib = ctypes.CDLL(path)
+    lib.q4probe_stream_read_cfg.restype = ctypes.c_int
+    lib.q4probe_stream_read_cfg.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p]
+    lines, best = [], {}
+    for nbytes in sizes:
+        R = copies_for_cold(nbytes)
+        bufs = [torch.full((nbytes,), 0x37, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+        lines.append("")
+        lines.append("%d bytes, cold (%d copies), %d launches per replay, median of %d replays"
+                     % (nbytes, R, steps, reps))
+        lines.append("%8s %6s %4s %4s %9s %10s %10s %8s" % ("threads", "loads", "nt", "blk",
+                                                             "grid", "us", "GB/s", "frac"))
+        for nt, blk in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            for T in (64, 128, 256, 512, 1024):
+                for L in (1, 2, 4, 8, 16):
+                    n16 = nbytes // 16
+                    grid = -(-n16 // (T * L))
+
+                    def fn(k, T=T, L=L, fl=nt | (blk << 1)):
+                        st = lib.q4probe_stream_read_cfg(bufs[k % R].data_ptr(), nbytes,
+                                                         sink.data_ptr(), T, L, fl,
+                                                         torch.cuda.current_stream().cuda_stream)
+                        if st != 0:
+                            raise RuntimeError("q4probe_stream_read_cfg status %d" % st)
+
+                    t = run_timed(torch, fn, steps, warmup, reps,
+                                  "sweep_%dB_t%d_l%d_nt%d_b%d" % (nbytes, T, L, nt, blk), True)
+                    gbs = nbytes / (t["kernel_us"] * 1e-6) / 1e9
+                    lines.append("%8d %6d %4d %4d %9d %10.3f %10.1f %8.3f" % (
+                        T, L, nt, blk, grid, t["kernel_us"], gbs, gbs / HBM_PEAK_GBS))
+                    if nbytes not in best or t["kernel_us"] < best[nbytes]["us"]:
+                        best[nbytes] = {"threads": T, "loads": L, "nontemporal": nt,
+                                        "blocked": blk, "grid": grid, "us": t["kernel_us"],
+                                        "GBs": gbs}
+        lines.append("best: %s" % json.dumps(best[nbytes]))
+        del bufs, sink
+        torch.cuda.empty_cache()
+    text = ["Streaming-read ceiling: q4probe_stream_read_cfg over its launch shapes (one MI355X, "
+            "gfx950)", "",
+            "command: python3 bench.py --probe-sweep --steps %d --warmup %d --reps %d" % (
+                steps, warmup, reps)] + lines
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write("\n".join(text) + "\n")
+    for l in text:
+        log(l)
+    return best
+
+
 def copy_calibration(torch):
     """Three 256 MiB device-to-device copies (each reads 256 MiB and writes
     256 MiB), for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -637,6 +698,10 @@ def main_bench(args):
                                       props.multi_processor_count))
     S, W, P, reps = args.steps, args.warmup, args.profile, args.reps
     small_w = min(W, 10)
+    if args.probe_sweep:
+        best = probe_sweep(torch, [9469952, 42467328], S, W, reps, args.sweep_out)
+        print(json.dumps({"probe_sweep_best": best}), flush=True)
+        return
 
     log("headline: decode GEMV 1x4096x4096, cold inputs")
     head = bench_product(torch, q4, wl, "gemv_1x4096x4096", S, W, reps, P)

@@ -310,8 +310,14 @@ struct GemvStreamCfg {
     static constexpr int AH = (CH == 16 && NI > 8) ? 2 : 1;
     static constexpr int CHH = CH / AH;                   // blocks per A pass
     static constexpr int ABYTES = CHH * 4 * NI * 16;      // A operands per wavefront
-    static constexpr int NENT = CH * 4 * M;               // 8-element activation groups per chunk
-    static constexpr int EPL = (NENT + 63) / 64;          // ... per lane
+    // Activation split: lane l handles activation row l / QN (QN = 64 / MP,
+    // MP = M rounded up to a power of two) and, in each A pass, the 8-element
+    // groups l % QN + QN r (r < EPP) of that pass's 4 CHH (block, lane group)
+    // pairs, so consecutive lanes read consecutive activations.
+    static constexpr int MP = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
+    static constexpr int QN = 64 / MP;                    // lanes per activation row
+    static constexpr int EPP = (4 * CHH + QN - 1) / QN;   // groups per lane per A pass
+    static constexpr int EPL = AH * EPP;                  // ... per chunk
     static constexpr int LDS_PER_WAVE = WBYTES + ABYTES;
     static constexpr int NPART = CH == 16 ? 4 : 2;        // parts a chunk is contracted in
     // Loads (per lane) that hold every byte of the chunk's first b blocks.
@@ -346,6 +352,50 @@ __device__ __forceinline__ float wave_max_nonneg(float v)
     const int r = max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
                       max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
     return __builtin_bit_cast(float, r);
+}
+
+// Maximum of a non-negative float over each run of QN consecutive lanes (QN
+// = 8, 16, 32 or 64), returned to each lane of the run: DPP within quads,
+// half-rows and rows, then across rows.
+template <int QN>
+__device__ __forceinline__ float lane_run_max_nonneg(float v)
+{
+    static_assert(QN == 8 || QN == 16 || QN == 32 || QN == 64, "runs of 8, 16, 32 or 64 lanes");
+    if constexpr (QN == 64) {
+        return wave_max_nonneg(v);
+    } else {
+        int x = __builtin_bit_cast(int, v);
+        x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+        x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+        x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+        if constexpr (QN >= 16)
+            x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false));   // row_mirror
+        if constexpr (QN >= 32)
+            x = max(x, __shfl_xor(x, 16));
+        return __builtin_bit_cast(float, x);
+    }
+}
+
+// A operand (block b, lane group g, A row i) sits in LDS at slot
+// b ASTRIDE / 16 + g NI + (i ^ a_swz<NI>(b, g)). A write instruction of the
+// activation split has eight consecutive lanes on one A row (or hi / lo
+// pair) of two consecutive blocks times the four lane groups; unswizzled,
+// NI a multiple of 8 puts all eight in one bank group. The XOR, below NI,
+// gives each of the eight its own 16-byte bank group, and within one (b, g)
+// it only permutes the NI slots, so the operand reads (lane j of group g
+// reads row j) stay conflict-free. Other NI keep the plain layout, where the
+// conflicts are at most four-way.
+template <int NI>
+__device__ __forceinline__ int a_swz(int b, int g)
+{
+    if constexpr (NI == 8 || NI == 16)
+        return ((b & 1) << 2) | g;
+    else if constexpr (NI == 4)
+        return ((b & 1) << 1) | (g >> 1);
+    else if constexpr (NI == 2)
+        return b & 1;
+    else
+        return 0;
 }
 
 // Calls f(integral_constant<int, B>) for B = B0 .. B1-1, in order.
@@ -420,10 +470,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // Four activations per half group: f32, or bfloat16 pairs.
     using AV = std::conditional_t<BF, uint2, float4>;
     AV areg[C::EPL][2];
-    // Activation group e = (m * CH + b) * 4 + gg: row m, block b of the chunk,
-    // elements lo(gg)..lo(gg)+3 and hi(gg)..hi(gg)+3. Activations are requested
-    // first (vmcnt drains in issue order), so their split overlaps the weight
-    // loads.
+    // Entry r of a lane: A pass h = r / EPP, group c = sq + QN (r % EPP) of
+    // that pass (block h CHH + c / 4 of the chunk, lane group gg = c % 4), row
+    // sm: elements lo(gg)..lo(gg)+3 and hi(gg)..hi(gg)+3. Activations are
+    // requested first (vmcnt drains in issue order), so their split overlaps
+    // the weight loads.
+    const int sq = lane % C::QN, sm = lane / C::QN;
+    const int sm_ld = min(sm, M - 1);
     const uint8_t *a8 = reinterpret_cast<const uint8_t *>(a);
     // Every lane issues every load (surplus lanes re-read an in-bounds group or
     // column that is then ignored), so the compiler's in-order wait counts are
@@ -431,9 +484,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     auto fetch = [&](int cb0) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < (PA ? 0 : C::EPL); ++r) {
-            const int e = min(lane + 64 * r, C::NENT - 1);
-            const int m = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
-            const uint32_t off = ((uint32_t)m * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * ES;
+            const int c = min(sq + C::QN * (r % C::EPP), 4 * C::CHH - 1);
+            const int b = (r / C::EPP) * C::CHH + (c >> 2), gg = c & 3;
+            const uint32_t off = ((uint32_t)sm_ld * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * ES;
             areg[r][0] = *reinterpret_cast<const AV *>(a8 + off);
             areg[r][1] = *reinterpret_cast<const AV *>(a8 + off + ES * (F::a_hi(0) - F::a_lo(0)));
         }
@@ -483,7 +536,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     fetch(min(wb0, nblk - C::CH));
     // Clamped, so the address stays inside the A area even where the read is
     // masked off.
-    const uint8_t *a_lane = s_a + (g * C::NI + min(j, C::NI - 1)) * 16;
+    // Operand reads: lane (g, j) reads A row j of lane group g; the swizzle
+    // depends on the block's parity (ASTRIDE is a whole number of slots).
+    const int jr = min(j, C::NI - 1);
+    const uint8_t *a_lane0 = s_a + (g * C::NI + (jr ^ a_swz<C::NI>(0, g))) * 16;
+    const uint8_t *a_lane1 = s_a + (g * C::NI + (jr ^ a_swz<C::NI>(1, g))) * 16;
     // The decode's exponent pattern in a VGPR (one v_mov at kernel start; no
     // MFMA is in flight there).
     const uint32_t magic_v = magic_vgpr<F>();
@@ -509,85 +566,79 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     auto split_activations = [&]() __attribute__((always_inline)) {
         if constexpr (PA)
             return;
-        float mx[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-            mx[m] = 0.0f;
+        // Every entry of a lane belongs to its row sm: one running maximum,
+        // then one reduction over the lanes of the row. Clamped entries repeat
+        // a group of the same row and lanes sm >= M a row that is never used,
+        // so neither needs a mask here.
+        float mx = 0.0f;
 #pragma unroll
         for (int r = 0; r < C::EPL; ++r) {
-            const int e = lane + 64 * r;
-            const int me = e / (4 * C::CH);
-            if (e < C::NENT) {
-                float v;
-                if constexpr (BF) {
-                    const uint2 L = areg[r][0], H = areg[r][1];
-                    v = fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(L.x)), fabsf(bf16_hi(L.x))),
-                                    fmaxf(fabsf(bf16_lo(L.y)), fabsf(bf16_hi(L.y)))),
-                              fmaxf(fmaxf(fabsf(bf16_lo(H.x)), fabsf(bf16_hi(H.x))),
-                                    fmaxf(fabsf(bf16_lo(H.y)), fabsf(bf16_hi(H.y)))));
-                } else {
-                    const float4 L = areg[r][0], H = areg[r][1];
-                    v = fmaxf(fmaxf(fmaxf(fabsf(L.x), fabsf(L.y)), fmaxf(fabsf(L.z), fabsf(L.w))),
-                              fmaxf(fmaxf(fabsf(H.x), fabsf(H.y)), fmaxf(fabsf(H.z), fabsf(H.w))));
-                }
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (m == me)
-                        mx[m] = fmaxf(mx[m], v);
+            float v;
+            if constexpr (BF) {
+                const uint2 L = areg[r][0], H = areg[r][1];
+                v = fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(L.x)), fabsf(bf16_hi(L.x))),
+                                fmaxf(fabsf(bf16_lo(L.y)), fabsf(bf16_hi(L.y)))),
+                          fmaxf(fmaxf(fabsf(bf16_lo(H.x)), fabsf(bf16_hi(H.x))),
+                                fmaxf(fabsf(bf16_lo(H.y)), fabsf(bf16_hi(H.y)))));
+            } else {
+                const float4 L = areg[r][0], H = areg[r][1];
+                v = fmaxf(fmaxf(fmaxf(fabsf(L.x), fabsf(L.y)), fmaxf(fabsf(L.z), fabsf(L.w))),
+                          fmaxf(fmaxf(fabsf(H.x), fabsf(H.y)), fmaxf(fabsf(H.z), fabsf(H.w))));
             }
+            mx = fmaxf(mx, v);
         }
+        const float am = lane_run_max_nonneg<C::QN>(mx);
+        const int pe = BF ? row_scale_exp_bf16<F>(am) : row_scale_exp<F>(am);
+        // Lane m QN holds row m's exponent; the epilogue needs every row's.
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float am = wave_max_nonneg(mx[m]);
-            pexp[m] = BF ? row_scale_exp_bf16<F>(am) : row_scale_exp<F>(am);
-        }
-        // Each pass writes the groups of its blocks (a lane's groups all belong
-        // to one block, b = (lane / 4) % CH) and reads them back as A operands
-        // at once; the next pass reuses the same LDS area.
+        for (int m = 0; m < M; ++m)
+            pexp[m] = __builtin_amdgcn_readlane(pe, m * C::QN);
+        // Each pass writes the groups of its blocks and reads them back as A
+        // operands at once; the next pass reuses the same LDS area. A lane's
+        // groups share its lane group gg = sq % 4 and block parity (sq / 4) % 2
+        // (QN / 4 is even), so its slots within a block are fixed.
+        const int gg = sq & 3, sw = a_swz<C::NI>(sq >> 2, gg);
+        const int slot_hi = gg * C::NI + ((BF ? sm : 2 * sm) ^ sw);
+        const int slot_lo = gg * C::NI + ((2 * sm + 1) ^ sw);
 #pragma unroll
         for (int h = 0; h < C::AH; ++h) {
         if (h > 0)
             wave_lds_sync();   // the previous pass's reads precede these writes
 #pragma unroll
-        for (int r = 0; r < C::EPL; ++r) {
-            const int e = lane + 64 * r;
-            const int me = e / (4 * C::CH), b = (e >> 2) & (C::CH - 1), gg = e & 3;
-            if (e < C::NENT && b / C::CHH == h) {
-                int pm = 0;
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (m == me)
-                        pm = pexp[m];
+        for (int rr = 0; rr < C::EPP; ++rr) {
+            const int r = h * C::EPP + rr, c = sq + C::QN * rr;
+            if ((C::QN * C::EPP == 4 * C::CHH || c < 4 * C::CHH) && (C::MP == M || sm < M)) {
+                uint8_t *blk = s_a + (c >> 2) * ASTRIDE;
                 if constexpr (BF) {
                     const uint2 L = areg[r][0], H = areg[r][1];
-                    const int pl = pm + F::kHiLog2;
+                    const int pl = pe + F::kHiLog2;
                     const float v[8] = {ldexpf(bf16_lo(L.x), pl), ldexpf(bf16_lo(L.y), pl),
                                         ldexpf(bf16_hi(L.x), pl), ldexpf(bf16_hi(L.y), pl),
-                                        ldexpf(bf16_lo(H.x), pm), ldexpf(bf16_lo(H.y), pm),
-                                        ldexpf(bf16_hi(H.x), pm), ldexpf(bf16_hi(H.y), pm)};
+                                        ldexpf(bf16_lo(H.x), pe), ldexpf(bf16_lo(H.y), pe),
+                                        ldexpf(bf16_hi(H.x), pe), ldexpf(bf16_hi(H.y), pe)};
                     f16x8 hi;
 #pragma unroll
                     for (int s = 0; s < 8; ++s)
                         hi[s] = (f16)v[s];
-                    *reinterpret_cast<u32x4 *>(s_a + (b % C::CHH) * ASTRIDE + (gg * C::NI + me) * 16) =
-                        bitcast<u32x4>(hi);
+                    *reinterpret_cast<u32x4 *>(blk + slot_hi * 16) = bitcast<u32x4>(hi);
                 } else {
-                    const float sh = ldexpf(1.0f, pm), sl = (float)(1 << F::kHiLog2) * sh;
+                    // hi = f16(x sc) and lo = f16(x sc - hi), sc the power of
+                    // two (times 2^kHiLog2 on slots 0..3): x sc is exact and so
+                    // is x sc - hi in f32, so each term is one rounding, as in
+                    // split2.
+                    const float sh = ldexpf(1.0f, pe), sl = (float)(1 << F::kHiLog2) * sh;
                     const float4 L = areg[r][0], H = areg[r][1];
-                    const float v[8] = {L.x * sl, L.z * sl, L.y * sl, L.w * sl,
-                                        H.x * sh, H.z * sh, H.y * sh, H.w * sh};
+                    const float x[8] = {L.x, L.z, L.y, L.w, H.x, H.z, H.y, H.w};
                     f16x8 hi, lo;
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
-                        f16 hh, ll;
-                        split2(v[s], hh, ll);
+                        const float sc = s < 4 ? sl : sh;
+                        const f16 hh = (f16)fmaf(x[s], sc, -0.0f);
                         hi[s] = hh;
-                        lo[s] = ll;
+                        lo[s] = (f16)fmaf(x[s], sc, -(float)hh);
                     }
-                    u32x4 *dst = reinterpret_cast<u32x4 *>(s_a + (b % C::CHH) * ASTRIDE +
-                                                           (gg * C::NI + 2 * me) * 16);
-                    dst[0] = bitcast<u32x4>(hi);
-                    dst[1] = bitcast<u32x4>(lo);
+                    *reinterpret_cast<u32x4 *>(blk + slot_hi * 16) = bitcast<u32x4>(hi);
+                    *reinterpret_cast<u32x4 *>(blk + slot_lo * 16) = bitcast<u32x4>(lo);
                 }
             }
         }
@@ -598,11 +649,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         if (!AL && j < C::NI) {
 #pragma unroll
             for (int b = h * C::CHH; b < (h + 1) * C::CHH; ++b)
-                aop[b] = *reinterpret_cast<const f16x8 *>(a_lane + (b - h * C::CHH) * ASTRIDE);
+                aop[b] = *reinterpret_cast<const f16x8 *>((b & 1 ? a_lane1 : a_lane0) +
+                                                          (b - h * C::CHH) * ASTRIDE);
         }
         }
     };
-
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     split_activations();
     for (int cb0 = wb0; cb0 < kb_hi; cb0 += kStride) {
@@ -640,7 +691,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 d[b - B0] = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(wl + b * F::kBytes));
                 f16x8 av;
                 if constexpr (AL)
-                    av = *reinterpret_cast<const f16x8 *>(a_lane + b * ASTRIDE);
+                    av = *reinterpret_cast<const f16x8 *>((b & 1 ? a_lane1 : a_lane0) + b * ASTRIDE);
                 else
                     av = aop[b];
                 Cv[b - B0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, F::decode(x, magic_v),

@@ -1,4 +1,4 @@
-// Streaming-read ceiling kernel of libq4probe.so (include/q4_probe.h): each
+// Streaming-read ceiling kernels of libq4probe.so (include/q4_probe.h): each
 // thread XORs a few grid-strided 16-byte words. Measurement only; no part of
 // the block-quantized method.
 #include <hip/hip_runtime.h>
@@ -10,44 +10,76 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-
 // Thread t reads words t, t + S, ..., t + (R - 1) S (S = all threads of the
 // grid), every load issued before any is used, so each thread has R loads in
-// flight at once and no load waits for another.
-template <int R>
-__global__ __launch_bounds__(kThreads) void k_stream_read(const u32x4 *__restrict__ src, size_t n16,
-                                                         u32x4 *__restrict__ sink)
+// flight at once and no load waits for another. NT marks the loads
+// non-temporal (streamed past the caches). BL (blocked) gives each workgroup
+// one contiguous run of T R words instead (load r of the workgroup covers
+// words T r .. T r + T - 1 of it), the pattern of a workgroup that owns whole
+// weight rows.
+template <int T, int R, bool NT, bool BL>
+__global__ __launch_bounds__(T) void k_stream_read(const u32x4 *__restrict__ src, size_t n16,
+                                                  u32x4 *__restrict__ sink)
 {
-    const size_t stride = (size_t)gridDim.x * kThreads;
-    const size_t i0 = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const size_t stride = BL ? (size_t)T : (size_t)gridDim.x * T;
+    const size_t i0 = (size_t)blockIdx.x * (BL ? (size_t)T * R : (size_t)T) + threadIdx.x;
+    // Every load is unconditional (an index past the end re-reads the last
+    // word, whose value is then dropped): a load under a branch would make the
+    // compiler wait for it before the join, serializing a thread's loads.
     u32x4 x[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const size_t i = i0 + r * stride;
-        x[r] = i < n16 ? src[i] : (u32x4){0u, 0u, 0u, 0u};
+        const size_t i = min(i0 + r * stride, n16 - 1);
+        x[r] = NT ? __builtin_nontemporal_load(src + i) : src[i];
     }
     u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        acc ^= x[r];
+        if (i0 + r * stride < n16)
+            acc ^= x[r];
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x5bd1e995u)
         *sink = acc;
 }
 
-template <int R>
+template <int T, int R, bool NT, bool BL>
 hipError_t launch_read(const u32x4 *src, size_t n16, u32x4 *sink, hipStream_t s)
 {
-    const size_t blocks = (n16 + (size_t)R * kThreads - 1) / ((size_t)R * kThreads);
-    hipLaunchKernelGGL(k_stream_read<R>, dim3((unsigned)blocks), dim3(kThreads), 0, s, src, n16, sink);
+    const size_t blocks = (n16 + (size_t)R * T - 1) / ((size_t)R * T);
+    if (blocks > 0x7fffffffu)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_stream_read<T, R, NT, BL>), dim3((unsigned)blocks), dim3(T), 0, s, src,
+                       n16, sink);
     return hipGetLastError();
 }
 
-}  // namespace
+template <int T, bool NT, bool BL>
+hipError_t launch_read_r(int loads, const u32x4 *src, size_t n16, u32x4 *sink, hipStream_t s)
+{
+    switch (loads) {
+    case 1: return launch_read<T, 1, NT, BL>(src, n16, sink, s);
+    case 2: return launch_read<T, 2, NT, BL>(src, n16, sink, s);
+    case 4: return launch_read<T, 4, NT, BL>(src, n16, sink, s);
+    case 8: return launch_read<T, 8, NT, BL>(src, n16, sink, s);
+    case 16: return launch_read<T, 16, NT, BL>(src, n16, sink, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 
-extern "C" __attribute__((visibility("default"))) int q4probe_stream_read(const void *src,
-                                                                          size_t n_bytes,
-                                                                          void *sink, void *stream)
+template <bool NT, bool BL>
+hipError_t launch_read_t(int threads, int loads, const u32x4 *src, size_t n16, u32x4 *sink,
+                         hipStream_t s)
+{
+    switch (threads) {
+    case 64: return launch_read_r<64, NT, BL>(loads, src, n16, sink, s);
+    case 128: return launch_read_r<128, NT, BL>(loads, src, n16, sink, s);
+    case 256: return launch_read_r<256, NT, BL>(loads, src, n16, sink, s);
+    case 512: return launch_read_r<512, NT, BL>(loads, src, n16, sink, s);
+    case 1024: return launch_read_r<1024, NT, BL>(loads, src, n16, sink, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int check(const void *src, size_t n_bytes, const void *sink)
 {
     if (n_bytes % 16 != 0)
         return 3;
@@ -57,23 +89,43 @@ extern "C" __attribute__((visibility("default"))) int q4probe_stream_read(const 
         return 1;
     if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) & 15u)
         return 4;
+    if (n_bytes / 16 > ((size_t)4 << 30) / 16)
+        return 2;   // more than 4 GiB: not a size this measurement is for
+    return -1;
+}
+
+}  // namespace
+
+extern "C" __attribute__((visibility("default"))) int q4probe_stream_read_cfg(
+    const void *src, size_t n_bytes, void *sink, int threads, int loads, int flags, void *stream)
+{
+    const int st = check(src, n_bytes, sink);
+    if (st >= 0)
+        return st;
     const size_t n16 = n_bytes / 16;
-    // One to four loads per thread: the fewest that keep the grid within
-    // 65,536 workgroups. Measured on MI355X at 9.47 MB, every load issued up
-    // front reads 13% faster than a grid-stride loop of four-load batches,
-    // whose leftover loads each wait for the one before.
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const u32x4 *in = static_cast<const u32x4 *>(src);
     u32x4 *out = static_cast<u32x4 *>(sink);
-    const size_t per_r1 = (n16 + kThreads - 1) / kThreads;   // workgroups at one load per thread
-    if (per_r1 > 4 * (size_t)65536)
-        return 2;   // more than 4 GiB: not a size this measurement is for
-    hipError_t e;
-    if (per_r1 <= 65536)
-        e = launch_read<1>(in, n16, out, s);
-    else if (per_r1 <= 2 * (size_t)65536)
-        e = launch_read<2>(in, n16, out, s);
-    else
-        e = launch_read<4>(in, n16, out, s);
-    return e == hipSuccess ? 0 : 6;
+    const bool nt = flags & 1, bl = flags & 2;
+    const hipError_t e =
+        nt ? (bl ? launch_read_t<true, true>(threads, loads, in, n16, out, s)
+                 : launch_read_t<true, false>(threads, loads, in, n16, out, s))
+           : (bl ? launch_read_t<false, true>(threads, loads, in, n16, out, s)
+                 : launch_read_t<false, false>(threads, loads, in, n16, out, s));
+    return e == hipSuccess ? 0 : (e == hipErrorInvalidValue ? 5 : 6);
+}
+
+extern "C" __attribute__((visibility("default"))) int q4probe_stream_read(const void *src,
+                                                                          size_t n_bytes,
+                                                                          void *sink, void *stream)
+{
+    const int st = check(src, n_bytes, sink);
+    if (st >= 0)
+        return st;
+    // Within about 1% of the fastest launch shape of the sweep at 9.47 MB and
+    // at 42.5 MB, cold (bench.py --probe-sweep): 512 threads, one
+    // non-temporal 16-byte load per thread. The non-temporal hint is worth
+    // about 10% at 9.47 MB and 5% at 42.5 MB; grid and loads per thread
+    // matter less.
+    return q4probe_stream_read_cfg(src, n_bytes, sink, 512, 1, 1, stream);
 }

@@ -31,6 +31,20 @@ extern "C" {
  */
 int q4probe_stream_read(const void *src, size_t n_bytes, void *sink, void *stream);
 
+/*
+ * q4probe_stream_read_cfg — the same read with a chosen launch shape, for
+ * sweeping it: `threads` per workgroup (64, 128, 256, 512 or 1024), `loads`
+ * 16-byte loads per thread, all issued before any is used (1, 2, 4, 8 or 16;
+ * the grid is ceil(n_bytes / (16 threads loads)) workgroups), and `flags`:
+ * bit 0 non-temporal loads, bit 1 blocked (each workgroup reads one
+ * contiguous run of 16 threads loads bytes; otherwise a thread's loads are a
+ * grid's width apart). Returns as q4probe_stream_read, and 5 for a shape
+ * outside those sets. q4probe_stream_read is this with 512 threads, one load
+ * and non-temporal loads, the sweep's fastest shape.
+ */
+int q4probe_stream_read_cfg(const void *src, size_t n_bytes, void *sink, int threads, int loads,
+                            int flags, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,8 +20,12 @@ from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
 from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_matmul,  # noqa: E402
                          oracle_matmul_sampled, random_blocks, to_dev, weight_blob)
 
+# "gemm" is the workspace form; "gemm_noalloc" the form with the pages' argument
+# list, on the library's own scratch (the same kernels and results).
 ENTRY = {("q4_0", "gemv"): binding.q4_gemv, ("q4_0", "gemm"): binding.q4_gemm_ws,
-         ("q8_0", "gemv"): binding.q8_gemv, ("q8_0", "gemm"): binding.q8_gemm_ws}
+         ("q4_0", "gemm_noalloc"): binding.q4_gemm,
+         ("q8_0", "gemv"): binding.q8_gemv, ("q8_0", "gemm"): binding.q8_gemm_ws,
+         ("q8_0", "gemm_noalloc"): binding.q8_gemm}
 WS_BYTES = {"q4_0": binding.q4_gemm_workspace_bytes, "q8_0": binding.q8_gemm_workspace_bytes}
 
 
@@ -53,13 +57,14 @@ def test_gemv_workloads_full_output(fmt, name):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["gemm", "gemm_noalloc"])
 @pytest.mark.parametrize("name", ["gemm_1024x4096x4096", "gemm_2048x14336x4096"])
-def test_gemm_workloads_sampled(fmt, name):
+def test_gemm_workloads_sampled(fmt, kind, name):
     s = wl.WORKLOADS[name]
     M, N, K = s["M"], s["N"], s["K"]
     blob = weight_blob(fmt, N, K, s["w_seed"])
     a = wl.activations_f32(s["a_seed"], M, K)
-    got = _run(fmt, "gemm", a, blob, N, K)
+    got = _run(fmt, kind, a, blob, N, K)
     # 4096 random outputs plus whole first/last rows and columns of the tiles.
     mi = np.concatenate([wl.uniform_ints(7, 0, M, 4096), np.zeros(N, np.int64),
                          np.full(N, M - 1), np.arange(M), np.arange(M)])
@@ -67,7 +72,7 @@ def test_gemm_workloads_sampled(fmt, name):
                          np.zeros(M, np.int64), np.full(M, N - 1)])
     ref, bound = oracle_matmul_sampled(fmt)(a, blob, N, K, mi, ni)
     assert np.isfinite(got).all()
-    assert_within_tolerance(got[mi, ni], ref, bound, "%s %s" % (fmt, name))
+    assert_within_tolerance(got[mi, ni], ref, bound, "%s %s %s" % (fmt, kind, name))
 
 
 # ------------------------------------------------------ shapes and tails
@@ -94,10 +99,11 @@ def test_gemv_shapes(fmt, M, N, K):
                                    # kernel (K % 64 != 0) at 7200 takes 3 of 75 blocks.
                                    (96, 200, 14336), (130, 160, 16384), (40, 96, 7200),
                                    (3, 33, 7168), (17, 40, 7232)])
-def test_gemm_shapes(fmt, M, N, K):
+@pytest.mark.parametrize("kind", ["gemm", "gemm_noalloc"])
+def test_gemm_shapes(fmt, M, N, K, kind):
     blob = weight_blob(fmt, N, K, 3 * M + N)
     a = wl.activations_f32(5 * M + K, M, K)
-    _full_check(fmt, "gemm", a, blob, N, K, "gemm %dx%dx%d" % (M, N, K))
+    _full_check(fmt, kind, a, blob, N, K, "%s %dx%dx%d" % (kind, M, N, K))
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -151,7 +157,7 @@ def test_zero_activations(fmt, kind):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_noalloc"])
 @pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e-8, 1e-3, 1e3, 6e4, 1e5, 1e30])
 def test_activation_magnitudes(fmt, kind, scale):
     # Any finite activations, unclipped (up to 4e30 and down into the f32

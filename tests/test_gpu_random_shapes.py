@@ -19,7 +19,7 @@ from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
 from gpu_helpers import Guarded, assert_within_tolerance, to_dev, weight_blob  # noqa: E402
 
-KINDS = ["gemv", "gemm_ws", "gemv_bf16", "gemm_bf16", "gemv_q8a", "gemm_q8a", "gemv_splitk"]
+KINDS = ["gemv", "gemm_ws", "gemv_bf16", "gemm_bf16", "gemv_q8a", "gemm_q8a", "gemv_splitk", "gemm"]
 
 
 def _case(i):
@@ -38,7 +38,7 @@ def _case(i):
     return kind, fmt, M, N, K
 
 
-@pytest.mark.parametrize("i", range(56))
+@pytest.mark.parametrize("i", range(64))
 def test_random_shape(i):
     kind, fmt, M, N, K = _case(i)
     f = fmt[:2]

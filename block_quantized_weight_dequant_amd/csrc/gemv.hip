@@ -58,6 +58,23 @@ __device__ __forceinline__ void split2(float v, f16 &hi, f16 &lo)
     lo = (f16)(v - (float)hi);
 }
 
+// split2 of x0 sc and x1 sc (sc a power of two, so x sc is exact), packed:
+// hi = (f16(x0 sc), f16(x1 sc)) and lo = (f16(x0 sc - hi0), f16(x1 sc - hi1)).
+// Each half is one mixed-precision FMA (f32 operands, f16 result, one
+// rounding), and lo reads its hi half straight from the packed register.
+__device__ __forceinline__ void split2_pair(float x0, float x1, float sc, uint32_t &hi,
+                                            uint32_t &lo)
+{
+    uint32_t h, l;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(h) : "v"(x0), "v"(sc));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(h) : "v"(x1), "v"(sc));
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(l) : "v"(x0), "v"(sc), "v"(h));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "+v"(l) : "v"(x1), "v"(sc), "v"(h));
+    hi = h;
+    lo = l;
+}
+
 // Largest A value of a row is 2^kHiLog2 max|a| 2^p: p puts it in [2^14, 2^15).
 template <class F>
 __device__ __forceinline__ int row_scale_exp(float am)
@@ -460,8 +477,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     constexpr int kStride = NW * C::CH;         // ... and the step to its next
     y += (size_t)blockIdx.y * (size_t)M * (size_t)N;
 
-    // Loader role: row lr = lane % 16, 16-byte columns lc0 + 4 i.
-    const int lr = lane & 15, lc0 = lane >> 4;
+    // Loader role: row lr, 16-byte columns lc0 + 4 i. Quad order (lr = lane
+    // / 4, lc0 = lane % 4: each quad of lanes reads 64 contiguous bytes of one
+    // row) is faster wherever a compute unit streams more than one chunk of
+    // rows, the activations are several rows or the blocks are Q8_0's; the
+    // single-chunk M = 1 Q4_0 launch is about 1% faster with rows across
+    // consecutive lanes (lr = lane % 16).
+    constexpr bool kRowFastLoader = F::kBytes == kQ4Bytes && M == 1 && MODE == 0;
+    const int lr = kRowFastLoader ? lane & 15 : lane >> 2;
+    const int lc0 = kRowFastLoader ? lane >> 4 : lane & 3;
     const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
     // Offset of the last (clamped) 16-byte column from column lc0.
     const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
@@ -570,24 +594,31 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         // then one reduction over the lanes of the row. Clamped entries repeat
         // a group of the same row and lanes sm >= M a row that is never used,
         // so neither needs a mask here.
-        float mx = 0.0f;
+        // |a| compared as integers (non-negative floats order like their
+        // bit patterns; no canonicalizing of the loaded values), bfloat16
+        // halves two at a time.
+        uint32_t mb = 0;
+        u16x2 mb16 = {0, 0};
+        constexpr uint32_t kAbs = 0x7fffffffu, kAbs2 = 0x7fff7fffu;
 #pragma unroll
         for (int r = 0; r < C::EPL; ++r) {
-            float v;
             if constexpr (BF) {
                 const uint2 L = areg[r][0], H = areg[r][1];
-                v = fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(L.x)), fabsf(bf16_hi(L.x))),
-                                fmaxf(fabsf(bf16_lo(L.y)), fabsf(bf16_hi(L.y)))),
-                          fmaxf(fmaxf(fabsf(bf16_lo(H.x)), fabsf(bf16_hi(H.x))),
-                                fmaxf(fabsf(bf16_lo(H.y)), fabsf(bf16_hi(H.y)))));
+                mb16 = __builtin_elementwise_max(
+                    mb16, __builtin_elementwise_max(bitcast<u16x2>(L.x & kAbs2), bitcast<u16x2>(L.y & kAbs2)));
+                mb16 = __builtin_elementwise_max(
+                    mb16, __builtin_elementwise_max(bitcast<u16x2>(H.x & kAbs2), bitcast<u16x2>(H.y & kAbs2)));
             } else {
                 const float4 L = areg[r][0], H = areg[r][1];
-                v = fmaxf(fmaxf(fmaxf(fabsf(L.x), fabsf(L.y)), fmaxf(fabsf(L.z), fabsf(L.w))),
-                          fmaxf(fmaxf(fabsf(H.x), fabsf(H.y)), fmaxf(fabsf(H.z), fabsf(H.w))));
+                mb = max(mb, max(max(__float_as_uint(L.x) & kAbs, __float_as_uint(L.y) & kAbs),
+                                 max(__float_as_uint(L.z) & kAbs, __float_as_uint(L.w) & kAbs)));
+                mb = max(mb, max(max(__float_as_uint(H.x) & kAbs, __float_as_uint(H.y) & kAbs),
+                                 max(__float_as_uint(H.z) & kAbs, __float_as_uint(H.w) & kAbs)));
             }
-            mx = fmaxf(mx, v);
         }
-        const float am = lane_run_max_nonneg<C::QN>(mx);
+        if constexpr (BF)
+            mb = (uint32_t)max(mb16.x, mb16.y) << 16;
+        const float am = lane_run_max_nonneg<C::QN>(__uint_as_float(mb));
         const int pe = BF ? row_scale_exp_bf16<F>(am) : row_scale_exp<F>(am);
         // Lane m QN holds row m's exponent; the epilogue needs every row's.
 #pragma unroll
@@ -622,23 +653,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                         hi[s] = (f16)v[s];
                     *reinterpret_cast<u32x4 *>(blk + slot_hi * 16) = bitcast<u32x4>(hi);
                 } else {
-                    // hi = f16(x sc) and lo = f16(x sc - hi), sc the power of
-                    // two (times 2^kHiLog2 on slots 0..3): x sc is exact and so
-                    // is x sc - hi in f32, so each term is one rounding, as in
-                    // split2.
+                    // sc the power of two (times 2^kHiLog2 on slots 0..3);
+                    // slots (L.x, L.z, L.y, L.w, H.x, H.z, H.y, H.w).
                     const float sh = ldexpf(1.0f, pe), sl = (float)(1 << F::kHiLog2) * sh;
                     const float4 L = areg[r][0], H = areg[r][1];
-                    const float x[8] = {L.x, L.z, L.y, L.w, H.x, H.z, H.y, H.w};
-                    f16x8 hi, lo;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const float sc = s < 4 ? sl : sh;
-                        const f16 hh = (f16)fmaf(x[s], sc, -0.0f);
-                        hi[s] = hh;
-                        lo[s] = (f16)fmaf(x[s], sc, -(float)hh);
-                    }
-                    *reinterpret_cast<u32x4 *>(blk + slot_hi * 16) = bitcast<u32x4>(hi);
-                    *reinterpret_cast<u32x4 *>(blk + slot_lo * 16) = bitcast<u32x4>(lo);
+                    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+                    split2_pair(L.x, L.z, sl, h0, l0);
+                    split2_pair(L.y, L.w, sl, h1, l1);
+                    split2_pair(H.x, H.z, sh, h2, l2);
+                    split2_pair(H.y, H.w, sh, h3, l3);
+                    *reinterpret_cast<u32x4 *>(blk + slot_hi * 16) = u32x4{h0, h1, h2, h3};
+                    *reinterpret_cast<u32x4 *>(blk + slot_lo * 16) = u32x4{l0, l1, l2, l3};
                 }
             }
         }
@@ -1105,8 +1130,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
     const int wb0 = wave * CH;                    // this wavefront's first chunk
     constexpr int kStride = NW * CH;              // ... and the step to its next
 
-    // Weight loader role as in k_gemv_stream: row lr, 16-byte columns lc0 + 4 i.
-    const int lr = lane & 15, lc0 = lane >> 4;
+    // Weight loader role as in k_gemv_stream, in quad order: row lr, 16-byte
+    // columns lc0 + 4 i.
+    const int lr = lane >> 2, lc0 = lane & 3;
     const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
     const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
 

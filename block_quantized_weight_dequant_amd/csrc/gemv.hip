@@ -317,8 +317,12 @@ template <class F, int M, int NW, int CH_, bool BF>
 struct GemvStreamCfg {
     static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
     static constexpr int CPR = CH * F::kBytes / 16;       // 16-byte columns per staged row
-    static constexpr int NLOAD = (CPR + 3) / 4;           // 16-byte loads per lane per chunk
-    static constexpr int NFULL = CPR / 4;                 // ... that no lane clamps
+    // Weight loads: eight lanes per row take 128 contiguous bytes (one cache
+    // line's worth), eight rows per load: loads 2c and 2c + 1 cover columns
+    // 8c..8c+7 of rows 0..7 and 8..15, for each of the NG whole groups of
+    // eight columns; one more load covers the TC tail columns of all 16 rows.
+    static constexpr int NG = CPR / 8, TC = CPR % 8;
+    static constexpr int NLOAD = 2 * NG + (TC > 0 ? 1 : 0);   // 16-byte loads per lane per chunk
     static constexpr int RS = CH * F::kBytes + 16;        // LDS bytes per staged row
     static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
     static constexpr int NI = GemvRows<BF, M>::NI;        // A rows in use
@@ -338,7 +342,12 @@ struct GemvStreamCfg {
     static constexpr int LDS_PER_WAVE = WBYTES + ABYTES;
     static constexpr int NPART = CH == 16 ? 4 : 2;        // parts a chunk is contracted in
     // Loads (per lane) that hold every byte of the chunk's first b blocks.
-    static constexpr int loads_for(int b) { return b == 0 ? 0 : ((F::kBytes * b - 1) / 16) / 4 + 1; }
+    static constexpr int cols_for(int b) { return (F::kBytes * b + 15) / 16; }
+    static constexpr int loads_for(int b)
+    {
+        return b == 0 ? 0 : (cols_for(b) <= 8 * NG ? 2 * ((cols_for(b) + 7) / 8) : NLOAD);
+    }
+    static_assert(TC <= 4, "the tail columns fit four lanes per row");
     static_assert(CH == 8 || CH == 16, "chunks are 8 or 16 blocks");
     static_assert((CH * F::kBytes) % 16 == 0, "a chunk row is whole 16-byte columns");
 };
@@ -477,18 +486,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     constexpr int kStride = NW * C::CH;         // ... and the step to its next
     y += (size_t)blockIdx.y * (size_t)M * (size_t)N;
 
-    // Loader role: row lr, 16-byte columns lc0 + 4 i. Quad order (lr = lane
-    // / 4, lc0 = lane % 4: each quad of lanes reads 64 contiguous bytes of one
-    // row) is faster wherever a compute unit streams more than one chunk of
-    // rows, the activations are several rows or the blocks are Q8_0's; the
-    // single-chunk M = 1 Q4_0 launch is about 1% faster with rows across
-    // consecutive lanes (lr = lane % 16).
-    constexpr bool kRowFastLoader = F::kBytes == kQ4Bytes && M == 1 && MODE == 0;
-    const int lr = kRowFastLoader ? lane & 15 : lane >> 2;
-    const int lc0 = kRowFastLoader ? lane >> 4 : lane & 3;
-    const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
-    // Offset of the last (clamped) 16-byte column from column lc0.
-    const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
+    // Loader role (GemvStreamCfg): in load i < 2 NG, row lrow + 8 (i % 2),
+    // column lcol + 8 (i / 2); in the tail load, row trow, column
+    // 8 NG + tcol (clamped to the last column: surplus lanes re-read it).
+    // Each load thus touches one cache line's worth per row, eight rows.
+    const int lrow = lane >> 3, lcol = lane & 7, trow = lane >> 2, tcol = lane & 3;
+    const uint32_t row_off0 = (uint32_t)min(n0 + lrow, N - 1) * row_bytes;
+    const uint32_t row_off1 = (uint32_t)min(n0 + lrow + 8, N - 1) * row_bytes;
+    const uint32_t tail_off = (uint32_t)min(n0 + trow, N - 1) * row_bytes +
+                              16u * (uint32_t)(8 * C::NG + min(tcol, C::TC > 0 ? C::TC - 1 : 0));
 
     u32x4 wreg[C::NLOAD];
     // Four activations per half group: f32, or bfloat16 pairs.
@@ -514,18 +520,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
             areg[r][0] = *reinterpret_cast<const AV *>(a8 + off);
             areg[r][1] = *reinterpret_cast<const AV *>(a8 + off + ES * (F::a_hi(0) - F::a_lo(0)));
         }
-        // Columns lc0 + 4 i are in the row for i < NFULL on every lane: one
-        // address with immediate offsets. The last load clamps its column.
         // The scheduling barriers keep the loads in column order.
-        const uint32_t woff = lrow_off + (uint32_t)cb0 * F::kBytes + 16u * lc0;
+        const uint32_t cbo = (uint32_t)cb0 * F::kBytes;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < C::NFULL; ++i) {
-            wreg[i] = *reinterpret_cast<const u32x4 *>(w + (woff + 64u * i));
+        for (int i = 0; i < 2 * C::NG; ++i) {
+            wreg[i] = *reinterpret_cast<const u32x4 *>(
+                w + ((i & 1 ? row_off1 : row_off0) + cbo + 16u * (uint32_t)(lcol + 8 * (i >> 1))));
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (C::NFULL < C::NLOAD)
-            wreg[C::NFULL] = *reinterpret_cast<const u32x4 *>(w + (woff + last_off));
+        if constexpr (C::TC > 0)
+            wreg[2 * C::NG] = *reinterpret_cast<const u32x4 *>(w + (tail_off + cbo));
         // Issue point: the weight pointer escapes into an empty asm statement
         // with a memory clobber, so no pass sinks the loads below this line,
         // and the scheduling barrier keeps later work (which waits on loads)
@@ -690,9 +695,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
-                const int col = lc0 + 4 * i;
-                if (col < C::CPR)
-                    *reinterpret_cast<u32x4 *>(s_w + lr * C::RS + 16 * col) = wreg[i];
+                if (i < 2 * C::NG)
+                    *reinterpret_cast<u32x4 *>(s_w + (lrow + 8 * (i & 1)) * C::RS +
+                                               16 * (lcol + 8 * (i >> 1))) = wreg[i];
+                else if (tcol < C::TC)
+                    *reinterpret_cast<u32x4 *>(s_w + trow * C::RS + 16 * (8 * C::NG + tcol)) = wreg[i];
             }
         };
         float acc[NACC];
@@ -1130,11 +1137,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
     const int wb0 = wave * CH;                    // this wavefront's first chunk
     constexpr int kStride = NW * CH;              // ... and the step to its next
 
-    // Weight loader role as in k_gemv_stream, in quad order: row lr, 16-byte
-    // columns lc0 + 4 i.
-    const int lr = lane >> 2, lc0 = lane & 3;
-    const uint32_t lrow_off = (uint32_t)min(n0 + lr, N - 1) * row_bytes;
-    const uint32_t last_off = 16u * (uint32_t)(min(lc0 + 4 * C::NFULL, C::CPR - 1) - lc0);
+    // Weight loader role as in k_gemv_stream: eight lanes per row, eight rows
+    // per load, then the tail columns.
+    const int lrow = lane >> 3, lcol = lane & 7, trow = lane >> 2, tcol = lane & 3;
+    const uint32_t row_off0 = (uint32_t)min(n0 + lrow, N - 1) * row_bytes;
+    const uint32_t row_off1 = (uint32_t)min(n0 + lrow + 8, N - 1) * row_bytes;
+    const uint32_t tail_off = (uint32_t)min(n0 + trow, N - 1) * row_bytes +
+                              16u * (uint32_t)(8 * C::NG + min(tcol, C::TC > 0 ? C::TC - 1 : 0));
 
     u32x4 wreg[C::NLOAD];
     u32x4 areg[NAL];
@@ -1149,15 +1158,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
             areg[r] = *reinterpret_cast<const u32x4 *>(
                 aq + ((uint32_t)m * arow_bytes + (uint32_t)cb0 * kQ8Bytes + 16u * (uint32_t)col));
         }
-        const uint32_t woff = lrow_off + (uint32_t)cb0 * F::kBytes + 16u * lc0;
+        const uint32_t cbo = (uint32_t)cb0 * F::kBytes;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < C::NFULL; ++i) {
-            wreg[i] = *reinterpret_cast<const u32x4 *>(w + (woff + 64u * i));
+        for (int i = 0; i < 2 * C::NG; ++i) {
+            wreg[i] = *reinterpret_cast<const u32x4 *>(
+                w + ((i & 1 ? row_off1 : row_off0) + cbo + 16u * (uint32_t)(lcol + 8 * (i >> 1))));
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (C::NFULL < C::NLOAD)
-            wreg[C::NFULL] = *reinterpret_cast<const u32x4 *>(w + (woff + last_off));
+        if constexpr (C::TC > 0)
+            wreg[2 * C::NG] = *reinterpret_cast<const u32x4 *>(w + (tail_off + cbo));
         asm volatile("" ::"s"(w), "s"(aq) : "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -1200,9 +1210,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
-                const int col = lc0 + 4 * i;
-                if (col < C::CPR)
-                    *reinterpret_cast<u32x4 *>(s_w + lr * C::RS + 16 * col) = wreg[i];
+                if (i < 2 * C::NG)
+                    *reinterpret_cast<u32x4 *>(s_w + (lrow + 8 * (i & 1)) * C::RS +
+                                               16 * (lcol + 8 * (i >> 1))) = wreg[i];
+                else if (tcol < C::TC)
+                    *reinterpret_cast<u32x4 *>(s_w + trow * C::RS + 16 * (8 * C::NG + tcol)) = wreg[i];
             }
         };
         // All integer MFMAs of a part are issued before its scale FMAs.

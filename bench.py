@@ -263,6 +263,13 @@ def digest(x) -> str:
     return hashlib.sha256(x.tobytes()).hexdigest()
 
 
+def quantize_kernel_name(n_blocks):
+    """The Q8_0 quantizer instance the library launches for n_blocks blocks
+    (mirrors launch_quant: two blocks per lane group while that still gives
+    1024 workgroups, else one)."""
+    return "k_quantize_q8_0<%d>" % (2 if -(-n_blocks // 64) >= 1024 else 1)
+
+
 def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=False):
     """The kernel the library launches (mirrors launch_gemv_m, launch_gemv_q8a_m and
     gemv_split_plan)."""
@@ -464,11 +471,12 @@ def bench_quantize(torch, q4, wl, steps, warmup, reps, profile):
     MARKS.pop()
     algo = n * 4 + n // 32 * 34
     kern_s = t["kernel_us"] * 1e-6
-    row = {"workload": name, "kernel": "k_quantize_q8_0", "input_sets": R,
+    kernel = quantize_kernel_name(n // 32)
+    row = {"workload": name, "kernel": kernel, "input_sets": R,
            "input_sha256": digest(x),
            "cache": "cold", "algorithmic_bytes": algo, **t, "kernel_GBs": algo / kern_s / 1e9,
            "job_GBs": algo * steps / t["wall_s"] / 1e9}
-    row["roofline"] = hbm_roofline(algo, t["kernel_us"], name, "k_quantize_q8_0")
+    row["roofline"] = hbm_roofline(algo, t["kernel_us"], name, kernel)
     del xs, x, out
     torch.cuda.empty_cache()
     return row

@@ -257,27 +257,65 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 constexpr int kSplitWaves = 4;
 constexpr int kOpsPerBlockTile = 2 * 8 * 64;   // 16-byte A operands per (128-row tile, block)
 
-// row_exp[m]: the power of two row m is scaled by before the split.
+// Order a wavefront's LDS writes before its later LDS reads (its LDS
+// operations execute in issue order; the fences keep the compiler's order).
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Largest of a non-negative 32-bit value over the wavefront, in every lane:
+// DPP within quads, half-rows and rows, then one readlane per row.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    int x = (int)v;
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false));   // row_mirror
+    return max(max((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
+}
+
+// row_exp[m]: the power of two row m is scaled by before the split. One
+// wavefront per (16-row group, block): lane l loads 16-byte piece l % 8 of
+// rows l / 8 and 8 + l / 8 (whole 128-byte block rows, eight lanes per row;
+// rows past M re-read row M - 1 and are written as zeros), and a padded LDS
+// tile ([16 rows][9 pieces]: conflict-free both ways) hands lane (g, li) its
+// two pieces, the slots of lane group g of row li.
 template <class F>
 __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *__restrict__ a,
                                                                  const int *__restrict__ row_exp,
                                                                  u32x4 *__restrict__ ahl, int M,
                                                                  int K, long long n_waves)
 {
-    const int lane = threadIdx.x & 63;
-    const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
+    __shared__ float4 tile[kSplitWaves][16 * 9];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long gw = (long long)blockIdx.x * kSplitWaves + wave;
     if (gw >= n_waves)   // whole wavefronts only
         return;
     const int nblk = K >> 5;
     const long long R = gw / nblk;                // 16-row group
     const int kb = (int)(gw - R * nblk);
+    const int pr = lane >> 3, pc = lane & 7;
+    float4 v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const long long row = min(R * 16 + pr + 8 * i, (long long)M - 1);
+        v[i] = *reinterpret_cast<const float4 *>(a + row * K + (long long)kb * 32 + 4 * pc);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        tile[wave][(pr + 8 * i) * 9 + pc] = v[i];
+    wave_lds_fence();
     const int li = lane & 15, g = lane >> 4;
     const long long m = R * 16 + li;
     f16x8 hi = {}, lo = {};
     if (m < M) {
-        const float *blk = a + m * K + (long long)kb * 32;
-        const float4 L = *reinterpret_cast<const float4 *>(blk + F::a_lo(g));
-        const float4 H = *reinterpret_cast<const float4 *>(blk + F::a_hi(g));
+        const float4 L = tile[wave][li * 9 + F::a_lo(g) / 4];
+        const float4 H = tile[wave][li * 9 + F::a_hi(g) / 4];
         // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code: they carry
         // a further 2^-kHiLog2 (exact), so every product is a 2^p times the code.
         const int p = row_exp[m], ph = p - F::kHiLog2;
@@ -765,10 +803,7 @@ __device__ __forceinline__ uint32_t row_max_bits_bf16(const uint16_t *__restrict
         for (int j = 0; j < 4; ++j)
             mx = max(mx, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    return mx;
+    return wave_max_u32(mx);
 }
 
 // p = 15 - E for a largest magnitude in [2^E, 2^(E+1)); 0 for zero or non-finite.
@@ -869,21 +904,21 @@ __global__ __launch_bounds__(256) void k_gemm_prep_bf16_f32(const uint16_t *__re
 // that holds an infinity or NaN.
 
 // Largest |a| of row `row` (K f32 values, K % 32 == 0, 16-byte aligned) as a
-// cleared-sign bit pattern, in every lane of the wavefront.
+// cleared-sign bit pattern, in every lane of the wavefront. Sixteen 16-byte
+// loads per lane per round are issued before any is used (a 4096-element row
+// in one round), so a compute unit keeps enough bytes in flight even with one
+// wavefront per row.
 __device__ __forceinline__ uint32_t row_max_bits_f32(const float *__restrict__ row, int K, int lane)
 {
     const uint4 *r4 = reinterpret_cast<const uint4 *>(row);
     uint32_t mx = 0;
-#pragma unroll 8
+#pragma unroll 16
     for (int i = lane; i < K / 4; i += 64) {
         const uint4 v = r4[i];
         mx = max(mx, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu),
                          max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    return mx;
+    return wave_max_u32(mx);
 }
 
 __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_f32(const float *__restrict__ a,

@@ -313,18 +313,20 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <class F, int M, int NW, int CH_, bool BF>
+template <class F, int M, int NW, int CH_, bool BF, int RPW_ = 16>
 struct GemvStreamCfg {
     static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
+    static constexpr int RPW = RPW_;                      // weight rows per workgroup (16 or 8)
     static constexpr int CPR = CH * F::kBytes / 16;       // 16-byte columns per staged row
     // Weight loads: eight lanes per row take 128 contiguous bytes (one cache
-    // line's worth), eight rows per load: loads 2c and 2c + 1 cover columns
-    // 8c..8c+7 of rows 0..7 and 8..15, for each of the NG whole groups of
-    // eight columns; one more load covers the TC tail columns of all 16 rows.
-    static constexpr int NG = CPR / 8, TC = CPR % 8;
-    static constexpr int NLOAD = 2 * NG + (TC > 0 ? 1 : 0);   // 16-byte loads per lane per chunk
+    // line's worth), eight rows per load: loads (RPW / 8) c + h cover columns
+    // 8c..8c+7 of rows 8h..8h+7, for each of the NG whole groups of eight
+    // columns; one more load covers the TC tail columns of all RPW rows
+    // (TLPR = 64 / RPW lanes per row).
+    static constexpr int NG = CPR / 8, TC = CPR % 8, RH = RPW / 8, TLPR = 64 / RPW;
+    static constexpr int NLOAD = RH * NG + (TC > 0 ? 1 : 0);   // 16-byte loads per lane per chunk
     static constexpr int RS = CH * F::kBytes + 16;        // LDS bytes per staged row
-    static constexpr int WBYTES = 16 * RS;                // staged weight bytes per wavefront
+    static constexpr int WBYTES = RPW * RS;               // staged weight bytes per wavefront
     static constexpr int NI = GemvRows<BF, M>::NI;        // A rows in use
     // The A operands of a chunk pass through LDS in AH halves when a whole
     // chunk's would not fit (16 blocks of more than eight A rows).
@@ -345,9 +347,10 @@ struct GemvStreamCfg {
     static constexpr int cols_for(int b) { return (F::kBytes * b + 15) / 16; }
     static constexpr int loads_for(int b)
     {
-        return b == 0 ? 0 : (cols_for(b) <= 8 * NG ? 2 * ((cols_for(b) + 7) / 8) : NLOAD);
+        return b == 0 ? 0 : (cols_for(b) <= 8 * NG ? RH * ((cols_for(b) + 7) / 8) : NLOAD);
     }
-    static_assert(TC <= 4, "the tail columns fit four lanes per row");
+    static_assert(RPW == 8 || RPW == 16, "eight or sixteen weight rows per workgroup");
+    static_assert(TC <= TLPR, "the tail columns fit the lanes of a row");
     static_assert(CH == 8 || CH == 16, "chunks are 8 or 16 blocks");
     static_assert((CH * F::kBytes) % 16 == 0, "a chunk row is whole 16-byte columns");
 };
@@ -445,13 +448,13 @@ __device__ __forceinline__ void static_for(F &&f)
 // prepared once by k_gemv_prep_ops (the two-term A operands of every block in
 // [block][lane group][A row] order, then the per-row exponents), loaded
 // straight into the A registers: no per-chunk split, scale or LDS pass.
-template <class F, int M, int NW, int CH, bool BF, int MODE>
+template <class F, int M, int NW, int CH, bool BF, int MODE, int RPW = 16>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
                                                         int ks)
 {
-    using C = GemvStreamCfg<F, M, NW, CH, BF>;
+    using C = GemvStreamCfg<F, M, NW, CH, BF, RPW>;
     using R = GemvRows<BF, M>;
     constexpr bool AL = MODE == 1, PA = MODE == 2;
     static_assert(!AL || C::AH == 1, "A operands read from LDS need the whole chunk's in one pass");
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * RPW;
     const int nblk = K >> 5;
     const uint32_t row_bytes = (uint32_t)nblk * F::kBytes;
     uint8_t *s_w = s_mem + wave * kLdsPerWave;
@@ -486,11 +489,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     constexpr int kStride = NW * C::CH;         // ... and the step to its next
     y += (size_t)blockIdx.y * (size_t)M * (size_t)N;
 
-    // Loader role (GemvStreamCfg): in load i < 2 NG, row lrow + 8 (i % 2),
-    // column lcol + 8 (i / 2); in the tail load, row trow, column
+    // Loader role (GemvStreamCfg): in load i < RH NG, row lrow + 8 (i % RH),
+    // column lcol + 8 (i / RH); in the tail load, row trow, column
     // 8 NG + tcol (clamped to the last column: surplus lanes re-read it).
     // Each load thus touches one cache line's worth per row, eight rows.
-    const int lrow = lane >> 3, lcol = lane & 7, trow = lane >> 2, tcol = lane & 3;
+    const int lrow = lane >> 3, lcol = lane & 7, trow = lane / C::TLPR, tcol = lane % C::TLPR;
     const uint32_t row_off0 = (uint32_t)min(n0 + lrow, N - 1) * row_bytes;
     const uint32_t row_off1 = (uint32_t)min(n0 + lrow + 8, N - 1) * row_bytes;
     const uint32_t tail_off = (uint32_t)min(n0 + trow, N - 1) * row_bytes +
@@ -524,13 +527,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         const uint32_t cbo = (uint32_t)cb0 * F::kBytes;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 2 * C::NG; ++i) {
+        for (int i = 0; i < C::RH * C::NG; ++i) {
             wreg[i] = *reinterpret_cast<const u32x4 *>(
-                w + ((i & 1 ? row_off1 : row_off0) + cbo + 16u * (uint32_t)(lcol + 8 * (i >> 1))));
+                w + ((i % C::RH ? row_off1 : row_off0) + cbo + 16u * (uint32_t)(lcol + 8 * (i / C::RH))));
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (C::TC > 0)
-            wreg[2 * C::NG] = *reinterpret_cast<const u32x4 *>(w + (tail_off + cbo));
+            wreg[C::RH * C::NG] = *reinterpret_cast<const u32x4 *>(w + (tail_off + cbo));
         // Issue point: the weight pointer escapes into an empty asm statement
         // with a memory clobber, so no pass sinks the loads below this line,
         // and the scheduling barrier keeps later work (which waits on loads)
@@ -695,9 +698,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
-                if (i < 2 * C::NG)
-                    *reinterpret_cast<u32x4 *>(s_w + (lrow + 8 * (i & 1)) * C::RS +
-                                               16 * (lcol + 8 * (i >> 1))) = wreg[i];
+                if (i < C::RH * C::NG)
+                    *reinterpret_cast<u32x4 *>(s_w + (lrow + 8 * (i % C::RH)) * C::RS +
+                                               16 * (lcol + 8 * (i / C::RH))) = wreg[i];
                 else if (tcol < C::TC)
                     *reinterpret_cast<u32x4 *>(s_w + trow * C::RS + 16 * (8 * C::NG + tcol)) = wreg[i];
             }
@@ -710,7 +713,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         // quant bytes of lane group g where they straddle dwords. All MFMAs of a
         // part are issued before its scale FMAs, so the matrix-core latency
         // overlaps the decode of the following blocks.
-        const uint8_t *wl = s_w + j * C::RS;
+        // Lane j decodes weight row j; with eight rows per workgroup the
+        // upper eight MFMA columns repeat row 7 and are never read.
+        const uint8_t *wl = s_w + min(j, C::RPW - 1) * C::RS;
         const uint32_t *wrow32 = reinterpret_cast<const uint32_t *>(wl);
         auto contract = [&](auto b0_c, auto b1_c) __attribute__((always_inline)) {
             constexpr int B0 = decltype(b0_c)::value, B1 = decltype(b1_c)::value;
@@ -787,12 +792,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
 #pragma unroll
     for (int h = 0; h < R::NOUT; ++h) {
         const int m = R::row(g, h);
-        if (m < M)
+        if (m < M && j < RPW)
             s_part[wave][m][j] = ysum[h];
     }
     __syncthreads();
-    if (tid < M * 16) {
-        const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
+    if (tid < M * RPW) {
+        const int m = tid / RPW, jj = tid % RPW, n = n0 + jj;
         float s = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww)
@@ -837,6 +842,17 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
         // A operands from LDS when a compute unit gets more than one workgroup
         // or a wavefront more than one chunk (and one pass holds them).
         const bool al = (long long)grid * splits > 256 || ks > NW * ch;
+        // One activation row, a grid of at most half the compute units and one
+        // chunk per wavefront (1x512x4096, 1x2048x4096: 5% and 4% faster):
+        // eight weight rows per workgroup instead, twice the workgroups, with
+        // the A operands in LDS. At 4096 rows (one workgroup per compute unit)
+        // or longer K the doubled per-workgroup split and reduction cost more
+        // (1x4096x4096 4.53 -> 5.23 us, 1x4096x14336 8.9 -> 11.6 us).
+        if constexpr (M == 1)
+            if (splits == 1 && ch == 16 && grid <= 128 && ks <= NW * ch)
+                return launch_kernel(k_gemv_stream<F, 1, NW, 16, BF, 1, 8>,
+                                     dim3((unsigned)((N + 7) / 8), 1u), dim3(64 * NW), 0, s, a, w,
+                                     y, N, K, ks);
         if (ch == 16) {
             if constexpr (GemvStreamCfg<F, M, NW, 16, BF>::AH == 1)
                 if (al)
@@ -1210,9 +1226,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
 #pragma unroll
             for (int i = I0; i < I1; ++i) {
-                if (i < 2 * C::NG)
-                    *reinterpret_cast<u32x4 *>(s_w + (lrow + 8 * (i & 1)) * C::RS +
-                                               16 * (lcol + 8 * (i >> 1))) = wreg[i];
+                if (i < C::RH * C::NG)
+                    *reinterpret_cast<u32x4 *>(s_w + (lrow + 8 * (i % C::RH)) * C::RS +
+                                               16 * (lcol + 8 * (i / C::RH))) = wreg[i];
                 else if (tcol < C::TC)
                     *reinterpret_cast<u32x4 *>(s_w + trow * C::RS + 16 * (8 * C::NG + tcol)) = wreg[i];
             }

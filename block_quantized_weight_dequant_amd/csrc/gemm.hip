@@ -344,9 +344,8 @@ template <class F>
 struct PairGeom {
     static constexpr int kDwords = 2 * F::kBytes / 4;                 // raw dwords per row: 9 or 17
     static constexpr int kBDwords = kGemmBN * kDwords;                // ... per tile
-    static constexpr int kBLoads = (kBDwords + 511) / 512;            // 4-byte loads per wavefront
+    static constexpr int kBLoads = (kBDwords + 511) / 512;            // 4-byte loads per 512 threads
     static constexpr int kBSlots = kBLoads * 512;                     // LDS dwords per weight stage
-    static constexpr int kLoads = 4 + kBLoads;                        // loads per wavefront per pair
 };
 
 // Ring depths: a pair's activation slab is loaded kA steps before the pair is
@@ -430,7 +429,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     // its lo operands in registers.
     constexpr int RM = HO ? 8 : 4, CN = HO ? 2 : 4;
     constexpr int SO = slab_ops<HO>();           // A operands per (tile, block)
-    constexpr int NA = 2 * SO / (8 * 64);         // A loads (1 KB each) per wavefront per pair
+    // Loads per pair in eighths of the workgroup (the four loading wavefronts
+    // issue twice these): A loads of 1 KB each, and 4-byte B loads.
+    constexpr int NA = 2 * SO / (8 * 64);
     constexpr int NB = G::kBLoads, NL = NA + NB;
     constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
     static_assert(DA >= 3 && DB >= DA, "ring depths");

@@ -229,8 +229,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 // weight row, a whole number of pairs of 36 or 68 bytes, starts on a 4-byte
 // boundary).
 //
-// * k_gemm_split_a writes the activations once, already split (hi = f16(a),
-//   lo = f16((a - hi) 2^11)) and laid out as the matrix cores' A operands:
+// * k_gemm_prep_f32 finds the row exponents and writes the activations once,
+//   already split (hi = f16(a), lo = f16((a - hi) 2^11), after the row's power
+//   of two) and laid out as the matrix cores' A operands:
 //   16-byte operand [mt][kb][hl][sub][lane] holds, for row 128 mt + 16 sub +
 //   lane % 16 and block kb, the slots of lane group g = lane / 16 in the
 //   format's order (formats.h), hi for hl = 0 and lo for hl = 1. Rows past M
@@ -254,8 +255,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 //   and block (lo x code 2^-11, then hi x code onto it), then d * C + acc in
 //   f32.
 
-constexpr int kSplitWaves = 4;
 constexpr int kOpsPerBlockTile = 2 * 8 * 64;   // 16-byte A operands per (128-row tile, block)
+
+// The fused preparations (k_gemm_prep_f32, k_gemm_prep_bf16): one wavefront
+// per row of a 16-row group.
+constexpr int kPrepWaves = 16;
+constexpr long long kPrepTarget = 256;   // workgroups the preparation aims for
+
+// Blocks per K part of a fused preparation: enough parts for about
+// kPrepTarget workgroups over `groups` row groups, each part a whole number
+// of `unit` blocks and at least one unit per wavefront.
+static int prep_part_blocks(long long groups, int nblk, int unit)
+{
+    const long long units = nblk / unit;
+    const long long parts = max(1LL, min(units / kPrepWaves, (kPrepTarget + groups - 1) / groups));
+    return (int)((units + parts - 1) / parts) * unit;
+}
 
 // Order a wavefront's LDS writes before its later LDS reads (its LDS
 // operations execute in issue order; the fences keep the compiler's order).
@@ -279,46 +294,49 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
                max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
 }
 
-// row_exp[m]: the power of two row m is scaled by before the split. One
-// wavefront per (16-row group, block): lane l loads 16-byte piece l % 8 of
-// rows l / 8 and 8 + l / 8 (whole 128-byte block rows, eight lanes per row;
-// rows past M re-read row M - 1 and are written as zeros), and a padded LDS
-// tile ([16 rows][9 pieces]: conflict-free both ways) hands lane (g, li) its
-// two pieces, the slots of lane group g of row li.
-template <class F>
-__global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a(const float *__restrict__ a,
-                                                                 const int *__restrict__ row_exp,
-                                                                 u32x4 *__restrict__ ahl, int M,
-                                                                 int K, long long n_waves)
-{
-    __shared__ float4 tile[kSplitWaves][16 * 9];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const long long gw = (long long)blockIdx.x * kSplitWaves + wave;
-    if (gw >= n_waves)   // whole wavefronts only
-        return;
-    const int nblk = K >> 5;
-    const long long R = gw / nblk;                // 16-row group
-    const int kb = (int)(gw - R * nblk);
-    const int pr = lane >> 3, pc = lane & 7;
+// The split of one (16-row group R, block kb) by one wavefront: lane l loads
+// 16-byte piece l % 8 of rows l / 8 and 8 + l / 8 (whole 128-byte block rows,
+// eight lanes per row; rows past M re-read row M - 1 and are written as
+// zeros), and a padded LDS tile ([16 rows][9 pieces]: conflict-free both
+// ways) hands lane (g, li) its two pieces, the slots of lane group g of row
+// li, which it splits with row li's power of two p.
+struct SplitRows {
     float4 v[2];
+};
+
+__device__ __forceinline__ SplitRows split_load(const float *__restrict__ a, int M, int K,
+                                                long long R, int kb, int lane)
+{
+    const int pr = lane >> 3, pc = lane & 7;
+    SplitRows x;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const long long row = min(R * 16 + pr + 8 * i, (long long)M - 1);
-        v[i] = *reinterpret_cast<const float4 *>(a + row * K + (long long)kb * 32 + 4 * pc);
+        x.v[i] = *reinterpret_cast<const float4 *>(a + row * K + (long long)kb * 32 + 4 * pc);
     }
+    return x;
+}
+
+template <class F>
+__device__ __forceinline__ void split_store(const SplitRows &x, int p, u32x4 *__restrict__ ahl,
+                                            int M, int nblk, long long R, int kb, float4 *tile,
+                                            int lane)
+{
+    const int pr = lane >> 3, pc = lane & 7;
+    wave_lds_fence();   // the tile's previous reads precede these writes
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        tile[wave][(pr + 8 * i) * 9 + pc] = v[i];
+        tile[(pr + 8 * i) * 9 + pc] = x.v[i];
     wave_lds_fence();
     const int li = lane & 15, g = lane >> 4;
     const long long m = R * 16 + li;
     f16x8 hi = {}, lo = {};
     if (m < M) {
-        const float4 L = tile[wave][li * 9 + F::a_lo(g) / 4];
-        const float4 H = tile[wave][li * 9 + F::a_hi(g) / 4];
+        const float4 L = tile[li * 9 + F::a_lo(g) / 4];
+        const float4 H = tile[li * 9 + F::a_hi(g) / 4];
         // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code: they carry
         // a further 2^-kHiLog2 (exact), so every product is a 2^p times the code.
-        const int p = row_exp[m], ph = p - F::kHiLog2;
+        const int ph = p - F::kHiLog2;
         const float e[8] = {ldexpf(L.x, p),  ldexpf(L.z, p),  ldexpf(L.y, p),  ldexpf(L.w, p),
                             ldexpf(H.x, ph), ldexpf(H.z, ph), ldexpf(H.y, ph), ldexpf(H.w, ph)};
 #pragma unroll
@@ -786,12 +804,15 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
 //   pattern with the sign cleared (which orders finite values by magnitude),
 //   and p = 15 - E; p = 0 for an all-zero row or one that holds an infinity
 //   or NaN.
-// * k_row_exp_bf16: one wavefront per row, all of its loads in flight at once.
-// * k_gemm_prep_bf16 (split path): as k_gemm_split_a, one wavefront per
-//   16-row group and pair of blocks, writing only the hi operand: operand
-//   [mt][kb][sub][lane] in the format's slot order, rows past M zero. (One
-//   workgroup per 16-row group doing both passes was measured slower: at
-//   M = 1024 it leaves three quarters of the CUs idle.)
+// * k_row_exp_bf16 (general kernel's shapes): one wavefront per row, all of
+//   its loads in flight at once.
+// * k_gemm_prep_bf16 (split path): the exponents and the operands in one
+//   launch, arranged as k_gemm_prep_f32 (a workgroup per 16-row group and K
+//   part, each finding its group's exponents over the whole rows), writing
+//   only the hi operand: operand [mt][kb][sub][lane] in the format's slot
+//   order, rows past M zero. (One workgroup per 16-row group, without the K
+//   parts, was measured slower: at M = 1024 it leaves three quarters of the
+//   CUs idle.)
 // * k_gemm_prep_bf16_f32 (general kernel's shapes): the scaled activations as
 //   f32, row-major (f16(a') is then exact and the lo term 0).
 
@@ -842,23 +863,17 @@ __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_bf16(const uint16
         row_exp[m] = p;
 }
 
-// Blocks per wavefront of k_gemm_prep_bf16 (the split path has an even number
-// of blocks per row): each lane's row segment is a whole 128-byte line.
+// Blocks a wavefront of k_gemm_prep_bf16 takes at a time (the split path has
+// an even number of blocks per row): each row's segment is a whole 128-byte
+// line.
 constexpr int kPrepBlocks = 2;
 
 template <class F>
-__global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_prep_bf16(const uint16_t *__restrict__ a,
-                                                                   const int *__restrict__ row_exp,
-                                                                   u32x4 *__restrict__ ops, int M,
-                                                                   int K, long long n_waves)
+__device__ __forceinline__ void prep_bf16_pair(const uint16_t *__restrict__ a, int p,
+                                               u32x4 *__restrict__ ops, int M, int K, long long R,
+                                               int kb0, int lane)
 {
-    const int lane = threadIdx.x & 63;
-    const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
-    if (gw >= n_waves)   // whole wavefronts only
-        return;
-    const int nblk = K >> 5, npb = nblk / kPrepBlocks;
-    const long long R = gw / npb;                 // 16-row group
-    const int kb0 = (int)(gw - R * npb) * kPrepBlocks;
+    const int nblk = K >> 5;
     const int li = lane & 15, g = lane >> 4;
     const long long m = R * 16 + li;
     f16x8 hi[kPrepBlocks] = {};
@@ -870,7 +885,6 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_prep_bf16(const uint1
             L[u] = *reinterpret_cast<const uint2 *>(blk0 + u * 32 + F::a_lo(g));
             H[u] = *reinterpret_cast<const uint2 *>(blk0 + u * 32 + F::a_hi(g));
         }
-        const int p = row_exp[m];
         const int ph = p - F::kHiLog2;   // slots 4..7 carry a further 2^-kHiLog2
 #pragma unroll
         for (int u = 0; u < kPrepBlocks; ++u) {
@@ -890,6 +904,39 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_prep_bf16(const uint1
 #pragma unroll
     for (int u = 0; u < kPrepBlocks; ++u)
         dst[u * slab_ops<true>()] = bitcast<u32x4>(hi[u]);
+}
+
+// The bfloat16 split path's preparation in one launch, arranged as
+// k_gemm_prep_f32: workgroup (R, q) finds the 16 rows' exponents of group R
+// over the whole rows (one row per wavefront; part 0 writes row_exp), then
+// its wavefronts take the pairs of blocks of K part q in turn. Each pair:
+// lane (g, li) reads row li's slots of lane group g for both blocks and
+// writes their binary16 values (row past M: zeros) in slab order.
+template <class F>
+__global__ __launch_bounds__(64 * kPrepWaves) void k_gemm_prep_bf16(const uint16_t *__restrict__ a,
+                                                                  int *__restrict__ row_exp,
+                                                                  u32x4 *__restrict__ ops, int M,
+                                                                  int K, int part_blocks)
+{
+    __shared__ int s_p[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long R = blockIdx.x;
+    const int nblk = K >> 5;
+    const int kb0 = (int)blockIdx.y * part_blocks, kb1 = min(kb0 + part_blocks, nblk);
+    static_assert(kPrepWaves == 16, "one row of the group per wavefront");
+    const long long m = R * 16 + wave;
+    int pw = 0;
+    if (R * 16 < M)
+        pw = row_exp_from_bits(row_max_bits_bf16(a + min(m, (long long)M - 1) * K, K, lane));
+    if (lane == 0) {
+        s_p[wave] = pw;
+        if (blockIdx.y == 0 && m < M)
+            row_exp[m] = pw;
+    }
+    __syncthreads();
+    const int p = s_p[lane & 15];
+    for (int kb = kb0 + kPrepBlocks * wave; kb < kb1; kb += kPrepBlocks * kPrepWaves)
+        prep_bf16_pair<F>(a, p, ops, M, K, R, kb, lane);
 }
 
 __global__ __launch_bounds__(256) void k_gemm_prep_bf16_f32(const uint16_t *__restrict__ a,
@@ -933,6 +980,19 @@ __device__ __forceinline__ uint32_t row_max_bits_f32(const float *__restrict__ r
     return wave_max_u32(mx);
 }
 
+// The row's power of two from its largest cleared-sign bit pattern.
+__device__ __forceinline__ int row_exp_from_bits_f32(uint32_t mx)
+{
+    int p = 0;
+    if (mx != 0 && mx < 0x7F800000u) {
+        const int ef = (int)(mx >> 23);
+        // Subnormals are (mantissa) 2^-149.
+        const int E = ef > 0 ? ef - 127 : (31 - __builtin_clz(mx)) - 149;
+        p = 14 - E;
+    }
+    return p;
+}
+
 __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_f32(const float *__restrict__ a,
                                                                   int *__restrict__ row_exp,
                                                                   int M, int K)
@@ -941,16 +1001,57 @@ __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_f32(const float *
     const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
     if (m >= M)   // whole wavefronts only
         return;
-    const uint32_t mx = row_max_bits_f32(a + (size_t)m * K, K, lane);
-    int p = 0;
-    if (mx != 0 && mx < 0x7F800000u) {
-        const int ef = (int)(mx >> 23);
-        // Subnormals are (mantissa) 2^-149.
-        const int E = ef > 0 ? ef - 127 : (31 - __builtin_clz(mx)) - 149;
-        p = 14 - E;
-    }
+    const int p = row_exp_from_bits_f32(row_max_bits_f32(a + (size_t)m * K, K, lane));
     if (lane == 0)
         row_exp[m] = p;
+}
+
+// The split path's preparation in one launch: the row exponents and the
+// two-term operands (the same values as k_row_exp_f32 and a split per block).
+// Workgroup (R, q) takes 16-row group R and K part q (blocks [q L, q L + L)).
+// Every element of a row bounds its exponent, so each of a row group's
+// workgroups first finds the 16 rows' maxima over the whole row itself (the
+// rows stay in L2 after the first reads; repeating the maxima avoids a
+// grid-wide dependency), one row per wavefront; part 0 writes them to
+// row_exp. Then its sixteen wavefronts split the part's blocks in turn, two
+// at a time.
+
+template <class F>
+__global__ __launch_bounds__(64 * kPrepWaves) void k_gemm_prep_f32(const float *__restrict__ a,
+                                                                 int *__restrict__ row_exp,
+                                                                 u32x4 *__restrict__ ahl, int M,
+                                                                 int K, int part_blocks)
+{
+    __shared__ float4 tile[kPrepWaves][16 * 9];
+    __shared__ int s_p[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long R = blockIdx.x;
+    const int nblk = K >> 5;
+    const int kb0 = (int)blockIdx.y * part_blocks, kb1 = min(kb0 + part_blocks, nblk);
+    // Row `wave` of the group (a group wholly past M, part of the last tile,
+    // needs no exponents: its operands are zeros).
+    static_assert(kPrepWaves == 16, "one row of the group per wavefront");
+    const long long m = R * 16 + wave;
+    int pw = 0;
+    if (R * 16 < M)
+        pw = row_exp_from_bits_f32(row_max_bits_f32(a + min(m, (long long)M - 1) * K, K, lane));
+    if (lane == 0) {
+        s_p[wave] = pw;
+        if (blockIdx.y == 0 && m < M)
+            row_exp[m] = pw;
+    }
+    __syncthreads();
+    const int p = s_p[lane & 15];
+    float4 *t = tile[wave];
+    int kb = kb0 + wave;
+    for (; kb + kPrepWaves < kb1; kb += 2 * kPrepWaves) {
+        const SplitRows x0 = split_load(a, M, K, R, kb, lane);
+        const SplitRows x1 = split_load(a, M, K, R, kb + kPrepWaves, lane);
+        split_store<F>(x0, p, ahl, M, nblk, R, kb, t, lane);
+        split_store<F>(x1, p, ahl, M, nblk, R, kb + kPrepWaves, t, lane);
+    }
+    if (kb < kb1)
+        split_store<F>(split_load(a, M, K, R, kb, lane), p, ahl, M, nblk, R, kb, t, lane);
 }
 
 // Longest run of block partials that one accumulator adds in sequence in a
@@ -1024,20 +1125,26 @@ static hipError_t launch_gemm_f(const float *a, const uint8_t *w, float *y, int 
     if (T > 0x7fffffffLL)
         return hipErrorInvalidValue;
     int *row_exp = static_cast<int *>(workspace);
-    hipError_t e = launch_kernel(k_row_exp_f32, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
-                                 dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
-    if (e != hipSuccess)
-        return e;
-    if (!split)
+    if (!split) {
+        const hipError_t e = launch_kernel(
+            k_row_exp_f32, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
+            dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
+        if (e != hipSuccess)
+            return e;
         return launch_any_segments<F>(a, w, y, M, N, K, tiles_m, tiles_n, row_exp, 1, s);
+    }
     u32x4 *ahl = reinterpret_cast<u32x4 *>(static_cast<char *>(workspace) +
                                            q4v::gemm_row_exp_bytes(M));
-    const long long n_waves = (long long)tiles_m * 8 * (K / 32);
-    const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
-    if (split_grid > 0x7fffffffLL)
+    // Row groups of every tile (those past M get zero operands).
+    const long long groups = (long long)tiles_m * 8;
+    const int nblk = K / 32;
+    const int part_blocks = prep_part_blocks(groups, nblk, 1);
+    const unsigned qn = (unsigned)((nblk + part_blocks - 1) / part_blocks);
+    if (groups > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    e = launch_kernel(k_gemm_split_a<F>, dim3((unsigned)split_grid), dim3(64 * kSplitWaves), 0, s,
-                      a, (const int *)row_exp, ahl, M, K, n_waves);
+    const hipError_t e = launch_kernel(k_gemm_prep_f32<F>, dim3((unsigned)groups, qn),
+                                       dim3(64 * kPrepWaves), 0, s, a, row_exp, ahl, M, K,
+                                       part_blocks);
     if (e != hipSuccess)
         return e;
     return launch_split_segments<F, false>(ahl, w, y, M, N, K, tiles_m, tiles_n, row_exp, s);
@@ -1053,11 +1160,12 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
         return hipErrorInvalidValue;
     int *row_exp = static_cast<int *>(workspace);
     void *act = static_cast<char *>(workspace) + q4v::gemm_row_exp_bytes(M);
-    hipError_t e = launch_kernel(k_row_exp_bf16, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
-                                 dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
-    if (e != hipSuccess)
-        return e;
+    hipError_t e;
     if (!q4v::gemm_bf16_splits(M, N, K)) {
+        e = launch_kernel(k_row_exp_bf16, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
+                          dim3(64 * kRowExpWaves), 0, s, a, row_exp, M, K);
+        if (e != hipSuccess)
+            return e;
         const long long n_quads = (long long)M * K / 4;
         const long long grid = (n_quads + 255) / 256;
         if (grid > 0x7fffffffLL)
@@ -1069,14 +1177,16 @@ static hipError_t launch_gemm_bf16_f(const uint16_t *a, const uint8_t *w, float 
         return launch_any_segments<F>((const float *)act, w, y, M, N, K, tiles_m, tiles_n,
                                       row_exp, 0, s);
     }
-    // One wavefront per 16-row group of the padded tiles and pair of blocks
-    // (groups past M write zeros).
-    const long long n_waves = (long long)tiles_m * 8 * (K / 32 / kPrepBlocks);
-    const long long grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
-    if (grid > 0x7fffffffLL)
+    // Every 16-row group of the padded tiles (groups past M write zeros), in
+    // K parts of whole pairs.
+    const long long groups = (long long)tiles_m * 8;
+    const int part_blocks = prep_part_blocks(groups, K / 32, kPrepBlocks);
+    if (groups > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    e = launch_kernel(k_gemm_prep_bf16<F>, dim3((unsigned)grid), dim3(64 * kSplitWaves), 0, s, a,
-                      (const int *)row_exp, static_cast<u32x4 *>(act), M, K, n_waves);
+    e = launch_kernel(k_gemm_prep_bf16<F>,
+                      dim3((unsigned)groups, (unsigned)((K / 32 + part_blocks - 1) / part_blocks)),
+                      dim3(64 * kPrepWaves), 0, s, a, row_exp, static_cast<u32x4 *>(act), M, K,
+                      part_blocks);
     if (e != hipSuccess)
         return e;
     return launch_split_segments<F, true>((const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n,
@@ -1207,23 +1317,19 @@ hipError_t launch_gemm_bf16(WeightFormat fmt, const uint16_t *a, const uint8_t *
 //   of the row's magnitudes) in [2^14, 2^15), p = 7 - E for the largest |d| in
 //   [2^E, 2^(E+1)) (0 for an all-zero row). The scaled values stay below 2^15
 //   and the epilogue scales each result row back by 2^-p.
-// * k_row_exp_q8a: one wavefront per row, the largest |d| as the largest
-//   binary16 bit pattern with the sign cleared.
-// * k_gemm_split_a_q8: as k_gemm_split_a, from the blocks: code q, d 2^p, the
-//   product exact in f32, then the same split and operand order.
+// * row_exp_q8a: one wavefront per row, the largest |d| as the largest
+//   binary16 bit pattern with the sign cleared (k_row_exp_q8a off the split
+//   path).
+// * k_gemm_prep_q8a (split path): the exponents and the split in one launch,
+//   arranged as k_gemm_prep_f32; split_q8_block splits as the f32 path
+//   (split_store) from the blocks: code q, d 2^p, the product exact in f32,
+//   then the same split and operand order.
 // * Off the split path: k_q8a_to_f32 writes the scaled values as f32 for
 //   k_gemm_any (which takes the same row exponents).
 
-__global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_q8a(const uint8_t *__restrict__ aq,
-                                                                  int *__restrict__ row_exp, int M,
-                                                                  int K)
+// The exponent of row `row` (nblk Q8_0 blocks), in every lane of the wavefront.
+__device__ __forceinline__ int row_exp_q8a(const uint8_t *__restrict__ row, int nblk, int lane)
 {
-    const int lane = threadIdx.x & 63;
-    const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
-    if (m >= M)   // whole wavefronts only
-        return;
-    const int nblk = K >> 5;
-    const uint8_t *row = aq + (size_t)m * (size_t)nblk * kQ8Bytes;
     uint32_t mx = 0;
     for (int b = lane; b < nblk; b += 64)
         mx = max(mx, load_u16(row + (size_t)b * kQ8Bytes) & 0x7FFFu);
@@ -1237,6 +1343,19 @@ __global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_q8a(const uint8_t
         const int E = ef > 0 ? ef - 15 : (31 - __builtin_clz(mx)) - 24;
         p = 7 - E;
     }
+    return p;
+}
+
+__global__ __launch_bounds__(64 * kRowExpWaves) void k_row_exp_q8a(const uint8_t *__restrict__ aq,
+                                                                  int *__restrict__ row_exp, int M,
+                                                                  int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * kRowExpWaves + (threadIdx.x >> 6);
+    if (m >= M)   // whole wavefronts only
+        return;
+    const int nblk = K >> 5;
+    const int p = row_exp_q8a(aq + (size_t)m * (size_t)nblk * kQ8Bytes, nblk, lane);
     if (lane == 0)
         row_exp[m] = p;
 }
@@ -1248,27 +1367,18 @@ __device__ __forceinline__ float code_f32(uint32_t x, int i)
 }
 
 template <class F>
-__global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a_q8(const uint8_t *__restrict__ aq,
-                                                                    const int *__restrict__ row_exp,
-                                                                    u32x4 *__restrict__ ahl, int M,
-                                                                    int K, long long n_waves)
+__device__ __forceinline__ void split_q8_block(const uint8_t *__restrict__ aq, int p,
+                                               u32x4 *__restrict__ ahl, int M, int nblk,
+                                               long long R, int kb, int lane)
 {
-    const int lane = threadIdx.x & 63;
-    const long long gw = (long long)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
-    if (gw >= n_waves)   // whole wavefronts only
-        return;
-    const int nblk = K >> 5;
-    const long long R = gw / nblk;                // 16-row group
-    const int kb = (int)(gw - R * nblk);
     const int li = lane & 15, g = lane >> 4;
     const long long m = R * 16 + li;
     f16x8 hi = {}, lo = {};
     if (m < M) {
         const uint8_t *blk = aq + ((size_t)m * (size_t)nblk + (size_t)kb) * kQ8Bytes;
         const float d = f16_bits_to_f32(load_u16(blk));
-        const int p = row_exp[m];
         // Slots 4..7 meet weights decoded at 2^kHiLog2 x their code (as in
-        // k_gemm_split_a): they carry a further 2^-kHiLog2.
+        // split_store): they carry a further 2^-kHiLog2.
         const float sl = ldexpf(d, p), sh = ldexpf(d, p - F::kHiLog2);
         const uint32_t cl = load_u32_unaligned(blk + 2 + F::a_lo(g));
         const uint32_t ch = load_u32_unaligned(blk + 2 + F::a_hi(g));
@@ -1286,6 +1396,37 @@ __global__ __launch_bounds__(64 * kSplitWaves) void k_gemm_split_a_q8(const uint
     const long long idx = (mt * nblk + kb) * kOpsPerBlockTile + (R & 7) * 64 + lane;
     ahl[idx] = bitcast<u32x4>(hi);
     ahl[idx + 8 * 64] = bitcast<u32x4>(lo);
+}
+
+// The split path's preparation in one launch, arranged as k_gemm_prep_f32:
+// workgroup (R, q) finds group R's row exponents from the whole rows' block
+// scales (one row per wavefront; part 0 writes row_exp), then its wavefronts
+// split the blocks of K part q in turn.
+template <class F>
+__global__ __launch_bounds__(64 * kPrepWaves) void k_gemm_prep_q8a(const uint8_t *__restrict__ aq,
+                                                                 int *__restrict__ row_exp,
+                                                                 u32x4 *__restrict__ ahl, int M,
+                                                                 int K, int part_blocks)
+{
+    __shared__ int s_p[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long R = blockIdx.x;
+    const int nblk = K >> 5;
+    const int kb0 = (int)blockIdx.y * part_blocks, kb1 = min(kb0 + part_blocks, nblk);
+    static_assert(kPrepWaves == 16, "one row of the group per wavefront");
+    const long long m = R * 16 + wave;
+    int pw = 0;
+    if (R * 16 < M)
+        pw = row_exp_q8a(aq + (size_t)min(m, (long long)M - 1) * (size_t)nblk * kQ8Bytes, nblk, lane);
+    if (lane == 0) {
+        s_p[wave] = pw;
+        if (blockIdx.y == 0 && m < M)
+            row_exp[m] = pw;
+    }
+    __syncthreads();
+    const int p = s_p[lane & 15];
+    for (int kb = kb0 + wave; kb < kb1; kb += kPrepWaves)
+        split_q8_block<F>(aq, p, ahl, M, nblk, R, kb, lane);
 }
 
 __global__ __launch_bounds__(256) void k_q8a_to_f32(const uint8_t *__restrict__ aq,
@@ -1316,11 +1457,12 @@ static hipError_t launch_gemm_q8a_f(const uint8_t *aq, const uint8_t *w, float *
         return hipErrorInvalidValue;
     int *row_exp = static_cast<int *>(workspace);
     void *act = static_cast<char *>(workspace) + q4v::gemm_row_exp_bytes(M);
-    hipError_t e = launch_kernel(k_row_exp_q8a, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
-                                 dim3(64 * kRowExpWaves), 0, s, aq, row_exp, M, K);
-    if (e != hipSuccess)
-        return e;
+    hipError_t e;
     if (!q4v::gemm_splits_activations(K) || (long long)M * N >= (1LL << 31)) {
+        e = launch_kernel(k_row_exp_q8a, dim3((unsigned)((M + kRowExpWaves - 1) / kRowExpWaves)),
+                          dim3(64 * kRowExpWaves), 0, s, aq, row_exp, M, K);
+        if (e != hipSuccess)
+            return e;
         const long long n_quads = (long long)M * K / 4;
         const long long grid = (n_quads + 255) / 256;
         if (grid > 0x7fffffffLL)
@@ -1332,12 +1474,15 @@ static hipError_t launch_gemm_q8a_f(const uint8_t *aq, const uint8_t *w, float *
         return launch_any_segments<F>((const float *)act, w, y, M, N, K, tiles_m, tiles_n,
                                       row_exp, 0, s);
     }
-    const long long n_waves = (long long)tiles_m * 8 * (K / 32);
-    const long long split_grid = (n_waves + kSplitWaves - 1) / kSplitWaves;
-    if (split_grid > 0x7fffffffLL)
+    const long long groups = (long long)tiles_m * 8;
+    const int nblk = K / 32;
+    const int part_blocks = prep_part_blocks(groups, nblk, 1);
+    if (groups > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    e = launch_kernel(k_gemm_split_a_q8<F>, dim3((unsigned)split_grid), dim3(64 * kSplitWaves), 0,
-                      s, aq, (const int *)row_exp, static_cast<u32x4 *>(act), M, K, n_waves);
+    e = launch_kernel(k_gemm_prep_q8a<F>,
+                      dim3((unsigned)groups, (unsigned)((nblk + part_blocks - 1) / part_blocks)),
+                      dim3(64 * kPrepWaves), 0, s, aq, row_exp, static_cast<u32x4 *>(act), M, K,
+                      part_blocks);
     if (e != hipSuccess)
         return e;
     return launch_split_segments<F, false>((const u32x4 *)act, w, y, M, N, K, tiles_m, tiles_n,

@@ -104,9 +104,12 @@ def test_gemv_shapes(fmt, M, N, K):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M,N,K", [(1, 300, 256), (8, 129, 64), (65, 70, 160), (5, 257, 128),
                                    (33, 6144, 2048), (128, 128, 32), (129, 129, 96),
-                                   (300, 17, 4128), (257, 384, 512), (1, 1, 32), (200, 1000, 4096)])
+                                   (300, 17, 4128), (257, 384, 512), (1, 1, 32), (200, 1000, 4096),
+                                   (1500, 64, 2048), (4200, 40, 1024)])
 def test_shapes(fmt, M, N, K):
     # K % 64 != 0 (32, 96, 160, 4128) takes the general kernel on scaled f32.
+    # The preparation cuts each 16-row group's pairs of blocks into K parts for
+    # about 256 workgroups: 2 at 1500 rows, one at 4200.
     blob = weight_blob(fmt, N, K, 3 * M + N)
     bits = wl.activations_bf16(5 * M + K, M, K)
     _full_check(fmt, bits, blob, N, K, "gemm_bf16 %dx%dx%d" % (M, N, K))

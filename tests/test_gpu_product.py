@@ -98,7 +98,11 @@ def test_gemv_shapes(fmt, M, N, K):
                                    # (the FFN down-projection), 3 at 16384; the general
                                    # kernel (K % 64 != 0) at 7200 takes 3 of 75 blocks.
                                    (96, 200, 14336), (130, 160, 16384), (40, 96, 7200),
-                                   (3, 33, 7168), (17, 40, 7232)])
+                                   (3, 33, 7168), (17, 40, 7232),
+                                   # The preparation cuts each 16-row group's K into
+                                   # parts for about 256 workgroups: 3 uneven parts
+                                   # (22, 22, 20 blocks) at 1500 rows, one at 4200.
+                                   (1500, 64, 2048), (4200, 40, 1024)])
 @pytest.mark.parametrize("kind", ["gemm", "gemm_noalloc"])
 def test_gemm_shapes(fmt, M, N, K, kind):
     blob = weight_blob(fmt, N, K, 3 * M + N)

@@ -214,10 +214,11 @@ def _run_gemm(fmt, a_q, blob, M, N, K, a_dev=None, w_dev=None, workspace=None):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M,N,K", [(1, 64, 4096), (130, 300, 256), (257, 129, 1024),
                                    (128, 128, 8192), (64, 200, 96), (33, 70, 4128),
-                                   (5, 17, 32)])
+                                   (5, 17, 32), (1500, 64, 2048), (4200, 40, 1024)])
 def test_gemm_q8a_shapes(fmt, M, N, K):
     # K % 64 == 0 takes the split path (several 128 x 128 tiles, ragged M and
-    # N); 96, 4128 and 32 the general kernel.
+    # N; the preparation's K parts: 3 uneven ones at 1500 rows, one at 4200);
+    # 96, 4128 and 32 the general kernel.
     blob = weight_blob(fmt, N, K, 29 * M + N)
     a_q = _act_blob(31 * M + K, M, K)
     ref, bound = _ref(fmt)(a_q, M, blob, N, K)

@@ -362,8 +362,11 @@ template <class F>
 struct PairGeom {
     static constexpr int kDwords = 2 * F::kBytes / 4;                 // raw dwords per row: 9 or 17
     static constexpr int kBDwords = kGemmBN * kDwords;                // ... per tile
-    static constexpr int kBLoads = (kBDwords + 511) / 512;            // 4-byte loads per 512 threads
-    static constexpr int kBSlots = kBLoads * 512;                     // LDS dwords per weight stage
+    // A weight stage holds two consecutive pairs: row r's 2 kDwords dwords
+    // (pair 2Q, then pair 2Q + 1, contiguous in the row) at r * 2 kDwords.
+    static constexpr int kBQDwords = 2 * kBDwords;                    // ... per stage
+    static constexpr int kBQLoads = (kBQDwords + 255) / 256;          // 4-byte loads per 256 threads
+    static constexpr int kBQSlots = kBQLoads * 256;                   // LDS dwords per stage
 };
 
 // Ring depths: a pair's activation slab is loaded kA steps before the pair is
@@ -402,8 +405,8 @@ constexpr int slab_ops() { return HO ? kOpsPerBlockTile / 2 : kOpsPerBlockTile; 
 template <class F, bool HO>
 struct SplitLds {
     static constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
-    u32x4 a[DA][2 * slab_ops<HO>()];        // a pair's slab: [kg][hl][sub][lane], as in the workspace
-    uint32_t b[DB][PairGeom<F>::kBSlots];   // [row][kDwords]; slots past the tile are never read
+    u32x4 a[DA][2 * slab_ops<HO>()];          // a pair's slab: [kg][hl][sub][lane], as in the workspace
+    uint32_t b[DB / 2][PairGeom<F>::kBQSlots];   // two pairs: [row][2 kDwords]; slots past the tile are never read
 };
 static_assert(sizeof(SplitLds<FmtQ4_0, false>) <= kLdsBytes &&
                   sizeof(SplitLds<FmtQ8_0, false>) <= kLdsBytes &&
@@ -447,12 +450,11 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     // its lo operands in registers.
     constexpr int RM = HO ? 8 : 4, CN = HO ? 2 : 4;
     constexpr int SO = slab_ops<HO>();           // A operands per (tile, block)
-    // Loads per pair in eighths of the workgroup (the four loading wavefronts
-    // issue twice these): A loads of 1 KB each, and 4-byte B loads.
+    // A loads (1 KB each) per pair in eighths of the workgroup (the four
+    // loading wavefronts issue twice these).
     constexpr int NA = 2 * SO / (8 * 64);
-    constexpr int NB = G::kBLoads, NL = NA + NB;
     constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
-    static_assert(DA >= 3 && DB >= DA, "ring depths");
+    static_assert((DA == 3 || DA == 4) && DB == 4, "ring depths");
     __shared__ SplitLds<F, HO> lds;
 
     const int T = tiles_m * tiles_n, L = blockIdx.x;
@@ -469,18 +471,21 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const size_t row_bytes = (size_t)nblk_row * F::kBytes;
 
     // Direct-to-LDS loads, issued by the four wavefronts of K group 0 only
-    // (2 NL per wavefront per pair, so their vmcnt moves in the same steps;
-    // K group 1 issues none and computes through the loads' issue stalls:
-    // 2-3% faster than spreading the loads over all eight), as buffer loads:
-    // one buffer resource per operand for the workgroup's tile, a fixed
-    // per-lane offset and a per-pair scalar offset, so the step's addressing
-    // is scalar work. A: 2 NA (8, or 4 hi-only) 16-byte loads, 1 KB each, at
-    // entries (2 NA lw + i) * 64 + lane of the slab (lw = wave % 4), whose
-    // workspace order is the LDS order. B: 2 NB 4-byte loads at dword slots
-    // j * 64 + lane, j = lw + 4 r; slot t < 128 kDwords is dword t % kDwords
-    // of the pair's bytes of row t / kDwords, higher slots re-read a valid
-    // dword into unused LDS. The ranges of both resources fit 32 bits
-    // (K <= 2^22 on this path); each ends with the segment's last block.
+    // (the same count on each, so their vmcnt moves in the same steps; K group
+    // 1 issues none and computes through the loads' issue stalls: 2-3% faster
+    // than spreading the loads over all eight), as buffer loads: one buffer
+    // resource per operand for the workgroup's tile, a fixed per-lane offset
+    // and a per-pair scalar offset, so the step's addressing is scalar work.
+    // A, per pair: 2 NA (8, or 4 hi-only) 16-byte loads, 1 KB each, at entries
+    // (2 NA lw + i) * 64 + lane of the slab (lw = wave % 4), whose workspace
+    // order is the LDS order. B, per two pairs (every other step): NBQ 4-byte
+    // loads at dword slots j * 64 + lane, j = lw + 4 r; slot t < 128 2 kDwords
+    // is dword t % (2 kDwords) of the two pairs' bytes of row t / (2 kDwords),
+    // higher slots re-read a valid dword into unused LDS. Two pairs per load
+    // instruction put each row's 72 (or 136) contiguous bytes in one
+    // instruction instead of 36 (68) in each of two: about half the cache
+    // lines per byte, and less padding. The ranges of both resources fit 32
+    // bits (K <= 2^22 on this path); each ends with the segment's last block.
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(ahl + (size_t)mt * nblk_row * SO), (short)0, (int)((uint32_t)nblk * SO * 16u),
         kBufferRsrcWord3);
@@ -488,28 +493,31 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(w + (size_t)n0 * row_bytes), (short)0,
         (int)((brows - 1) * row_bytes + (size_t)nblk * F::kBytes), kBufferRsrcWord3);
-    constexpr int NA2 = 2 * NA, NB2 = 2 * NB;       // loads of a loading wavefront per pair
+    // Loads of a loading wavefront: NA2 A loads per pair, NBQ B loads per
+    // two pairs.
+    constexpr int NA2 = 2 * NA, NBQ = G::kBQLoads;
+    constexpr int kDQ = 2 * G::kDwords;             // B dwords per row and stage
     const int lw = wave & 3;
     const uint32_t a_voff = (uint32_t)((lw * NA2 * 64 + lane) * 16);
-    uint32_t b_voff[NB2];
+    uint32_t b_voff[NBQ];
 #pragma unroll
-    for (int r = 0; r < NB2; ++r) {
-        const int tt = min((lw + 4 * r) * 64 + lane, G::kBDwords - 1);
-        const int row = tt / G::kDwords, dw = tt % G::kDwords;
+    for (int r = 0; r < NBQ; ++r) {
+        const int tt = min((lw + 4 * r) * 64 + lane, G::kBQDwords - 1);
+        const int row = tt / kDQ, dw = tt % kDQ;
         b_voff[r] = (uint32_t)(min(row, brows - 1) * (int)row_bytes + 4 * dw);
     }
-    // Load k (0 .. 2 NL - 1) of a step on a loading wavefront: the 2 NA A loads
-    // of pair pa, then the 2 NB B loads of pair pb (k is a compile-time
-    // constant where this is called).
-    auto issue_load = [&](int pa, int pb, int k) __attribute__((always_inline)) {
+    // Load k of a step on a loading wavefront: the NA2 A loads of pair pa,
+    // then (odd steps) the NBQ B loads of pairs 2 qb and 2 qb + 1 (k is a
+    // compile-time constant where this is called).
+    auto issue_load = [&](int pa, int qb, int k) __attribute__((always_inline)) {
         if (k < NA2)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 arsrc, (__attribute__((address_space(3))) void *)(lds.a[pa % DA] + (lw * NA2 + k) * 64),
                 16, a_voff + k * 1024, (int)((uint32_t)pa * (2u * SO * 16u)), 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                brsrc, (__attribute__((address_space(3))) void *)(lds.b[pb % DB] + (lw + 4 * (k - NA2)) * 64),
-                4, b_voff[k - NA2], pb * (2 * F::kBytes), 0, 0);
+                brsrc, (__attribute__((address_space(3))) void *)(lds.b[qb & 1] + (lw + 4 * (k - NA2)) * 64),
+                4, b_voff[k - NA2], qb * (4 * F::kBytes), 0, 0);
     };
 
     f32x4 acc[RM][CN];
@@ -524,9 +532,10 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
 
     auto run_group = [&](auto kg_c) __attribute__((always_inline)) {
         constexpr int KG = decltype(kg_c)::value;
-        // Loads per step of this wavefront: all of the workgroup's on K group
-        // 0's four, none on K group 1's.
-        constexpr int NLK = KG == 0 ? 2 * NL : 0, NAK = KG == 0 ? NA2 : 0, NBK = KG == 0 ? NB2 : 0;
+        // Loads per step of this wavefront (even steps: A only; odd steps: A
+        // and B): all of the workgroup's on K group 0's four, none on K group
+        // 1's.
+        constexpr int NAK = KG == 0 ? NA2 : 0, NBK = KG == 0 ? NBQ : 0;
         // B of column group ns, block 2p + KG: the row's raw pair bytes hold block
         // KG at byte kBytes KG. KG is a compile-time constant (the loop exists
         // once per K group), so the realignment (where the quant bytes straddle
@@ -536,7 +545,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             uint32_t dw;
         };
         auto read_b = [&](const uint32_t *bstage, int ns) __attribute__((always_inline)) {
-            const uint32_t *rb = bstage + (wn * (CN * 16) + ns * 16 + li) * G::kDwords;
+            const uint32_t *rb = bstage + (wn * (CN * 16) + ns * 16 + li) * kDQ;
             return BCol{read_qs_raw<F, KG>(rb, g), rb[d_dword<F, KG>()]};
         };
         // The operands of one pair held in registers: the A operands of the
@@ -556,7 +565,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 if constexpr (!HO)
                     o.lo[r] = bitcast<f16x8>(ap[8 * 64 + r * 64]);
             }
-            o.b[i] = read_b(lds.b[q % DB], i);
+            o.b[i] = read_b(lds.b[(q >> 1) & 1] + (q & 1) * G::kDwords, i);
         };
         // LDS reads of one part.
         constexpr int kDsReads = (RM / CN) * (HO ? 1 : 2) + QsRaw<F, KG>::n + 1;
@@ -596,8 +605,9 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         // barriers ask for one MFMA, one LDS read while any remain, then four VALU
         // instructions, eight times per region; hard barriers between regions
         // keep that order.
-        auto compute_pair = [&](const Ops &cur_ops, Ops &next_ops, int next_pair, int dma_a,
-                                int dma_b) __attribute__((always_inline)) {
+        auto compute_pair = [&](auto odd_c, const Ops &cur_ops, Ops &next_ops, int next_pair,
+                                int dma_a, int dma_b) __attribute__((always_inline)) {
+            constexpr int NLK = NAK + (decltype(odd_c)::value ? NBK : 0);
             BOps cur = decode_b(cur_ops.b[0]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -669,63 +679,69 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             }
         };
 
-        // Ring schedule: step p issues the A loads of pair p + DA, then the B loads
-        // of pair p + DB, so pair q's A slab goes to A stage q % DA during step
-        // q - DA and its B bytes to B stage q % DB during step q - DB. Both are
-        // complete by the barrier ending step q - 2, are read into registers
-        // during step q - 1, and pair q is computed in step q. Each stage is
-        // loaded again in step q (pair q + DA or q + DB), after the barrier that
-        // ends step q - 1, by which every wavefront has read it. Loads complete
-        // in issue order. The last loads pair p + 2 needs are its A loads (step
-        // p + 2 - DA) when DB > DA, else its B loads, which follow them in the
-        // same step; at the barrier ending step p the loads issued after those
-        // may still be in flight: the B loads of that step (when DB > DA) and all
-        // loads of the DA - 2 later steps (near the end, where fewer are issued,
-        // the barrier waits for everything). The last step reads stages no load
-        // is writing any more, and discards what it read.
-        constexpr int kInFlight = (DB > DA ? NBK : 0) + (DA - 2) * NLK;
-        static_assert(kInFlight < 64, "vmcnt counts to 63");
+        // Ring schedule: step p issues the A loads of pair p + DA and, when p is
+        // odd, then the B loads of pairs p + 3 and p + 4 (double stage Q =
+        // (p + 3) / 2 of two, Q % 2). Pair q's A slab goes to A stage q % DA
+        // during step q - DA, its B bytes to B stage (q / 2) % 2 during step
+        // 2 (q / 2) - 3 (q - 3 or q - 4). Both are complete by the barrier
+        // ending step q - 2, are read into registers during step q - 1, and
+        // pair q is computed in step q. An A stage is loaded again in step q
+        // (pair q + DA), after the barrier that ends step q - 1, by which every
+        // wavefront has read it; B stage Q % 2 again in step 2 Q + 1, after
+        // the barrier ending step 2 Q, by which pair 2 Q + 1's bytes are read.
+        // Loads complete in issue order. At the barrier ending step p, pair
+        // p + 2 is complete once these are: for even p, everything through the
+        // B loads of step p - 1, so step p's A loads may be in flight; for odd
+        // p, the B loads of step p - 2 (and, with DA = 3, the A loads of step
+        // p - 1), so step p's loads and, with DA = 4, step p - 1's may be (near
+        // the end, where fewer are issued, the barrier waits for everything).
+        // The last step reads stages no load is writing any more, and discards
+        // what it read.
+        constexpr int kInFlightEven = NAK;
+        constexpr int kInFlightOdd = (DA == 4 ? NAK : 0) + NAK + NBK;
+        static_assert(kInFlightOdd < 64, "vmcnt counts to 63");
         // The loads of steps -DB .. -1, in the order those steps would issue them
         // (a step before the first A load issues only its B loads). A step whose
-        // pair is past the last one reloads the last pair into its own stage
-        // (the same bytes), so every step issues NLK loads and, with at least DB
-        // pairs, every barrier can count them; shorter problems wait for all.
-        // K group 1 has no loads of its own in flight: its barriers only
-        // order, and wait for the loaders, which wait for theirs before the
-        // barrier.
+        // pair is past the last one reloads the last pair (or two) into its own
+        // stage (the same bytes), so every step issues its count of loads and,
+        // with at least DB pairs, every barrier can count them; shorter problems
+        // wait for all. K group 1 has no loads of its own in flight: its
+        // barriers only order, and wait for the loaders, which wait for theirs
+        // before the barrier.
         const bool counted = npairs >= DB;
-        const int last = npairs - 1;
+        const int last = npairs - 1, lastq = last >> 1;
         for (int t = -DB; t < 0; ++t) {
 #pragma unroll
-            for (int k = 0; k < NLK; ++k)
-                if (k >= NAK || t + DA >= 0)
-                    issue_load(min(t + DA, last), min(t + DB, last), k);
+            for (int k = 0; k < NAK + NBK; ++k)
+                if (k < NAK ? t + DA >= 0 : (t & 1) != 0)
+                    issue_load(min(t + DA, last), min((t + 3) / 2, lastq), k);
         }
         if (counted)
-            ring_barrier<kInFlight>();   // pairs 0 and 1 complete
+            ring_barrier<kInFlightOdd>();   // pairs 0 and 1 complete
         else
             ring_barrier<0>();
         Ops O0, O1;
 #pragma unroll
         for (int i = 0; i < CN; ++i)
             read_ops(0, O0, i);
-        // Step 0 reloads stage 0 of both rings: every wavefront must have read
-        // pair 0's operands first.
+        // Step 0 reloads A stage 0: every wavefront must have read pair 0's
+        // operands first.
         if (counted)
-            ring_barrier<kInFlight>();
+            ring_barrier<kInFlightOdd>();
         else
             ring_barrier<0>();
-        auto step = [&](int p, const Ops &cur_ops, Ops &next_ops) __attribute__((always_inline)) {
-            compute_pair(cur_ops, next_ops, p + 1, min(p + DA, last), min(p + DB, last));
+        auto step = [&](auto odd_c, int p, const Ops &cur_ops, Ops &next_ops) __attribute__((always_inline)) {
+            constexpr bool odd = decltype(odd_c)::value;
+            compute_pair(odd_c, cur_ops, next_ops, p + 1, min(p + DA, last), min((p + 3) / 2, lastq));
             if (counted)
-                ring_barrier<kInFlight>();   // pair p + 2 complete
+                ring_barrier<odd ? kInFlightOdd : kInFlightEven>();   // pair p + 2 complete
             else
                 ring_barrier<0>();
         };
         for (int p = 0; p < npairs; p += 2) {
-            step(p, O0, O1);
+            step(std::false_type{}, p, O0, O1);
             if (p + 1 < npairs)
-                step(p + 1, O1, O0);
+                step(std::true_type{}, p + 1, O1, O0);
         }
         // FMAs of the last column group (group CN - 1 of the last pair, in set 1).
 #pragma unroll

@@ -383,19 +383,19 @@ template <class F, bool HO>
 struct RingDepth;
 template <>
 struct RingDepth<FmtQ4_0, false> {
-    static constexpr int kA = 4, kB = 4;
+    static constexpr int kA = 4, kBQ = 2;
 };
 template <>
 struct RingDepth<FmtQ8_0, false> {
-    static constexpr int kA = 3, kB = 4;
+    static constexpr int kA = 3, kBQ = 2;
 };
 template <>
 struct RingDepth<FmtQ4_0, true> {
-    static constexpr int kA = 4, kB = 4;
+    static constexpr int kA = 4, kBQ = 2;
 };
 template <>
 struct RingDepth<FmtQ8_0, true> {
-    static constexpr int kA = 4, kB = 4;
+    static constexpr int kA = 4, kBQ = 2;
 };
 
 // 16-byte A operands per (128-row tile, block): hi and lo, or hi only.
@@ -404,9 +404,9 @@ constexpr int slab_ops() { return HO ? kOpsPerBlockTile / 2 : kOpsPerBlockTile; 
 
 template <class F, bool HO>
 struct SplitLds {
-    static constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
+    static constexpr int DA = RingDepth<F, HO>::kA, DBQ = RingDepth<F, HO>::kBQ;
     u32x4 a[DA][2 * slab_ops<HO>()];          // a pair's slab: [kg][hl][sub][lane], as in the workspace
-    uint32_t b[DB / 2][PairGeom<F>::kBQSlots];   // two pairs: [row][2 kDwords]; slots past the tile are never read
+    uint32_t b[DBQ][PairGeom<F>::kBQSlots];   // two pairs: [row][2 kDwords]; slots past the tile are never read
 };
 static_assert(sizeof(SplitLds<FmtQ4_0, false>) <= kLdsBytes &&
                   sizeof(SplitLds<FmtQ8_0, false>) <= kLdsBytes &&
@@ -431,6 +431,29 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("" ::: "memory");
 }
 
+// Loads a loading wavefront may still have in flight at the barrier that ends
+// step p (parity par) of k_gemm_split's ring, when pair p + 2 must be
+// complete: step s issues na A loads (pair s + da) and, for odd s, then nb B
+// loads (pairs s + lb and s + lb + 1), in that order; a load is identified by
+// (step, slot), and the count is the loads after the last one pair p + 2 needs.
+constexpr int ring_in_flight(int par, int da, int lb, int na, int nb)
+{
+    const int p = 1000 + par, q = p + 2;
+    const int a_step = q - da, a_slot = na - 1;
+    const int b_step = 2 * (q / 2) - lb, b_slot = na + nb - 1;
+    int ls = a_step, lk = a_slot;
+    if (b_step > ls || (b_step == ls && b_slot > lk))
+        ls = b_step, lk = b_slot;
+    int n = 0;
+    for (int st = ls; st <= p; ++st) {
+        const int slots = na + ((st & 1) ? nb : 0);
+        for (int k = 0; k < slots; ++k)
+            if (st > ls || k > lk)
+                ++n;
+    }
+    return n;
+}
+
 // One K segment of the product: ahl points at the operands of block kb0 of
 // the first row tile (a row tile holds nblk_row blocks of operands) and w at
 // block kb0 of weight row 0 (a weight row is nblk_row blocks); the segment
@@ -453,8 +476,11 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
     // A loads (1 KB each) per pair in eighths of the workgroup (the four
     // loading wavefronts issue twice these).
     constexpr int NA = 2 * SO / (8 * 64);
-    constexpr int DA = RingDepth<F, HO>::kA, DB = RingDepth<F, HO>::kB;
-    static_assert((DA == 3 || DA == 4) && DB == 4, "ring depths");
+    constexpr int DA = RingDepth<F, HO>::kA, DBQ = RingDepth<F, HO>::kBQ;
+    // Weight stages are loaded LB = 2 DBQ - 1 steps ahead of their first pair;
+    // the first PRO steps' loads precede the first pair.
+    constexpr int LB = 2 * DBQ - 1, PRO = DA > LB ? DA : LB;
+    static_assert(DA >= 3 && DBQ >= 2, "ring depths");
     __shared__ SplitLds<F, HO> lds;
 
     const int T = tiles_m * tiles_n, L = blockIdx.x;
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 16, a_voff + k * 1024, (int)((uint32_t)pa * (2u * SO * 16u)), 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                brsrc, (__attribute__((address_space(3))) void *)(lds.b[qb & 1] + (lw + 4 * (k - NA2)) * 64),
+                brsrc, (__attribute__((address_space(3))) void *)(lds.b[(unsigned)qb % DBQ] + (lw + 4 * (k - NA2)) * 64),
                 4, b_voff[k - NA2], qb * (4 * F::kBytes), 0, 0);
     };
 
@@ -565,7 +591,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
                 if constexpr (!HO)
                     o.lo[r] = bitcast<f16x8>(ap[8 * 64 + r * 64]);
             }
-            o.b[i] = read_b(lds.b[(q >> 1) & 1] + (q & 1) * G::kDwords, i);
+            o.b[i] = read_b(lds.b[((unsigned)q >> 1) % DBQ] + (q & 1) * G::kDwords, i);
         };
         // LDS reads of one part.
         constexpr int kDsReads = (RM / CN) * (HO ? 1 : 2) + QsRaw<F, KG>::n + 1;
@@ -680,41 +706,39 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
         };
 
         // Ring schedule: step p issues the A loads of pair p + DA and, when p is
-        // odd, then the B loads of pairs p + 3 and p + 4 (double stage Q =
-        // (p + 3) / 2 of two, Q % 2). Pair q's A slab goes to A stage q % DA
-        // during step q - DA, its B bytes to B stage (q / 2) % 2 during step
-        // 2 (q / 2) - 3 (q - 3 or q - 4). Both are complete by the barrier
-        // ending step q - 2, are read into registers during step q - 1, and
-        // pair q is computed in step q. An A stage is loaded again in step q
-        // (pair q + DA), after the barrier that ends step q - 1, by which every
-        // wavefront has read it; B stage Q % 2 again in step 2 Q + 1, after
-        // the barrier ending step 2 Q, by which pair 2 Q + 1's bytes are read.
-        // Loads complete in issue order. At the barrier ending step p, pair
-        // p + 2 is complete once these are: for even p, everything through the
-        // B loads of step p - 1, so step p's A loads may be in flight; for odd
-        // p, the B loads of step p - 2 (and, with DA = 3, the A loads of step
-        // p - 1), so step p's loads and, with DA = 4, step p - 1's may be (near
-        // the end, where fewer are issued, the barrier waits for everything).
-        // The last step reads stages no load is writing any more, and discards
-        // what it read.
-        constexpr int kInFlightEven = NAK;
-        constexpr int kInFlightOdd = (DA == 4 ? NAK : 0) + NAK + NBK;
-        static_assert(kInFlightOdd < 64, "vmcnt counts to 63");
-        // The loads of steps -DB .. -1, in the order those steps would issue them
-        // (a step before the first A load issues only its B loads). A step whose
+        // odd, then the B loads of pairs p + LB and p + LB + 1 (double stage
+        // Q = (p + LB) / 2, in B stage Q % DBQ). Pair q's A slab goes to A
+        // stage q % DA during step q - DA, its B bytes to B stage (q / 2) % DBQ
+        // during step 2 (q / 2) - LB (q - LB or q - LB - 1). Both are complete
+        // by the barrier ending step q - 2, are read into registers during
+        // step q - 1, and pair q is computed in step q. An A stage is loaded
+        // again in step q (pair q + DA), after the barrier that ends step
+        // q - 1, by which every wavefront has read it; B stage Q % DBQ again
+        // in step 2 Q + 1, after the barrier ending step 2 Q, by which pair
+        // 2 Q + 1's bytes are read. Loads complete in issue order, so at the
+        // barrier ending step p the loads issued after the last one pair p + 2
+        // needs may still be in flight: ring_in_flight counts them, one count
+        // for even and one for odd p (near the end, where fewer are issued, the
+        // barrier waits for everything). The last step reads stages no load is
+        // writing any more, and discards what it read.
+        constexpr int kInFlightEven = ring_in_flight(0, DA, LB, NAK, NBK);
+        constexpr int kInFlightOdd = ring_in_flight(1, DA, LB, NAK, NBK);
+        static_assert(kInFlightEven < 64 && kInFlightOdd < 64, "vmcnt counts to 63");
+        // The loads of steps -PRO .. -1, in the order those steps would issue
+        // them (a step before the first A load issues only its B loads). A step whose
         // pair is past the last one reloads the last pair (or two) into its own
         // stage (the same bytes), so every step issues its count of loads and,
-        // with at least DB pairs, every barrier can count them; shorter problems
+        // with at least PRO pairs, every barrier can count them; shorter problems
         // wait for all. K group 1 has no loads of its own in flight: its
         // barriers only order, and wait for the loaders, which wait for theirs
         // before the barrier.
-        const bool counted = npairs >= DB;
+        const bool counted = npairs >= PRO;
         const int last = npairs - 1, lastq = last >> 1;
-        for (int t = -DB; t < 0; ++t) {
+        for (int t = -PRO; t < 0; ++t) {
 #pragma unroll
             for (int k = 0; k < NAK + NBK; ++k)
                 if (k < NAK ? t + DA >= 0 : (t & 1) != 0)
-                    issue_load(min(t + DA, last), min((t + 3) / 2, lastq), k);
+                    issue_load(min(t + DA, last), min((t + LB) / 2, lastq), k);
         }
         if (counted)
             ring_barrier<kInFlightOdd>();   // pairs 0 and 1 complete
@@ -732,7 +756,7 @@ __global__ __launch_bounds__(kSplitGemmThreads) void k_gemm_split(
             ring_barrier<0>();
         auto step = [&](auto odd_c, int p, const Ops &cur_ops, Ops &next_ops) __attribute__((always_inline)) {
             constexpr bool odd = decltype(odd_c)::value;
-            compute_pair(odd_c, cur_ops, next_ops, p + 1, min(p + DA, last), min((p + 3) / 2, lastq));
+            compute_pair(odd_c, cur_ops, next_ops, p + 1, min(p + DA, last), min((p + LB) / 2, lastq));
             if (counted)
                 ring_barrier<odd ? kInFlightOdd : kInFlightEven>();   // pair p + 2 complete
             else

@@ -283,8 +283,10 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
     if prepared:
-        return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16>" % (FMT_TYPE[fmt], M,
-                                                               16 if nblk % 16 == 0 else 8)
+        ch = 16 if nblk % 16 == 0 else 8
+        nt = (N + 15) // 16 <= 256 and nblk <= 8 * ch
+        return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s>" % (FMT_TYPE[fmt], M, ch,
+                                                                   "true" if nt else "false")
     ks = kl = nblk
     if splitk:   # the library's automatic split
         groups = (N + 15) // 16
@@ -299,9 +301,11 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     ni = M if act == "bf16" else 2 * M
     splits = -(-nblk // ks)
     if M == 1 and splits == 1 and ch == 16 and (N + 15) // 16 <= 128 and ks <= 8 * ch:
-        return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8>" % (FMT_TYPE[fmt], bf)   # eight rows per workgroup
-    al = ((N + 15) // 16 * splits > 256 or ks > 8 * ch) and not (ch == 16 and ni > 8)
-    return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0)
+        return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8, true>" % (FMT_TYPE[fmt], bf)   # eight rows per workgroup
+    spread = (N + 15) // 16 * splits > 256 or ks > 8 * ch   # non-temporal loads otherwise
+    al = spread and not (ch == 16 and ni > 8)
+    return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16, %s>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0,
+                                                             "false" if spread else "true")
 
 
 def gemm_kernel_name(K, fmt="q4_0", act="f32"):

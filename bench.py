@@ -277,7 +277,9 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
         if K % 256:
             return "k_gemv_q8a_any<%s, %d>" % (FMT_TYPE[fmt], M)
         ch16 = (K // 32) % 16 == 0 and ((N + 15) // 16 <= 256 or M == 1)
-        return "k_gemv_q8a<%s, %d, 8, %d>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8)
+        nt = ch16 and (N + 15) // 16 <= 256 and K // 32 <= 128   # non-temporal weight loads
+        return "k_gemv_q8a<%s, %d, 8, %d, %s>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8,
+                                                 "true" if nt else "false")
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)

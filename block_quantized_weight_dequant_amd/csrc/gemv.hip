@@ -1143,7 +1143,7 @@ __device__ __forceinline__ long q8a_weight_operand(const uint32_t *wrow, int g)
 template <class F>
 constexpr float q8a_weight_scale() { return F::kBytes == kQ4Bytes ? 0.0625f : 1.0f; }
 
-template <class F, int M, int NW, int CH>
+template <class F, int M, int NW, int CH, bool NT = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict__ aq,
                                                      const uint8_t *__restrict__ w,
                                                      float *__restrict__ y, int N, int K)
@@ -1199,12 +1199,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 2 * C::NG; ++i) {
-            wreg[i] = *reinterpret_cast<const u32x4 *>(
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
                 w + ((i & 1 ? row_off1 : row_off0) + cbo + 16u * (uint32_t)(lcol + 8 * (i >> 1))));
+            wreg[i] = NT ? __builtin_nontemporal_load(src) : *src;
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (C::TC > 0)
-            wreg[2 * C::NG] = *reinterpret_cast<const u32x4 *>(w + (tail_off + cbo));
+        {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(w + (tail_off + cbo));
+            wreg[2 * C::NG] = NT ? __builtin_nontemporal_load(src) : *src;
+        }
         asm volatile("" ::"s"(w), "s"(aq) : "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -1401,6 +1405,11 @@ static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *
         // units and M > 1: those kernels need more than 128 VGPRs, so one
         // workgroup holds a compute unit, while the 8-block ones (under 100)
         // let two or more share it and overlap one's loads with another's work.
+        // Non-temporal weight loads as in launch_gemv_m: one chunk per
+        // wavefront and one workgroup per compute unit.
+        if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && grid <= 256 && nblk <= NW * 16)
+            return launch_kernel(k_gemv_q8a<F, M, NW, 16, true>, dim3(grid), dim3(64 * NW), 0, s,
+                                 aq, w, y, N, K);
         if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && (grid <= 256 || M == 1))
             return launch_kernel(k_gemv_q8a<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s, aq, w,
                                  y, N, K);

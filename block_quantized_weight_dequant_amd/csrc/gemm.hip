@@ -257,8 +257,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_any(const float *__restri
 
 constexpr int kOpsPerBlockTile = 2 * 8 * 64;   // 16-byte A operands per (128-row tile, block)
 
-// The fused preparations (k_gemm_prep_f32, k_gemm_prep_bf16): one wavefront
-// per row of a 16-row group.
+// The one-launch preparations (k_gemm_prep_f32, k_gemm_prep_bf16,
+// k_gemm_prep_q8a): one wavefront per row of a 16-row group.
 constexpr int kPrepWaves = 16;
 constexpr long long kPrepTarget = 256;   // workgroups the preparation aims for
 
@@ -370,15 +370,18 @@ struct PairGeom {
 };
 
 // Ring depths: a pair's activation slab is loaded kA steps before the pair is
-// computed, its raw weight bytes kB >= kA steps before. Measured on MI355X
-// (2048 x 14336 x 4096, one process): Q4_0 is fastest at 4 / 4 (3 / 3 costs
-// 2.5 %, deeper weight rings cost more), Q8_0, whose four activation stages
-// do not fit next to its weight stages, at 3 / 4.
+// computed; the raw weight bytes go two pairs per stage into kBQ stages, each
+// loaded 2 kBQ - 1 steps before its first pair. Measured on MI355X
+// (2048 x 14336 x 4096, one process), with one pair per weight stage: Q4_0
+// is fastest at 4 activation stages (3 costs 2.5 %), Q8_0, whose four
+// activation stages do not fit next to its weight stages, at 3; two pairs
+// per weight stage gained about 1 %, and a third weight stage (five steps
+// ahead) cost 1-3 % on every form.
 // HO ("hi only") selects the bfloat16-activation form: one binary16 term per
 // activation (exact, see k_gemm_prep_bf16), so a slab is half the size and a
 // tile-block needs one MFMA instead of two. With its 128 x 32 wavefront tiles
-// both formats are fastest at 4 / 4 (5 / 5 costs 3-4 %; 3 stages of its slab
-// would not hold the final reduction).
+// both formats are fastest at 4 activation stages (5 costs 3-4 %; 3 stages of
+// its slab would not hold the final reduction).
 template <class F, bool HO>
 struct RingDepth;
 template <>

@@ -75,6 +75,18 @@ __device__ __forceinline__ void split2_pair(float x0, float x1, float sc, uint32
     lo = l;
 }
 
+// max(m, |a|, |b|) for m >= 0, one instruction: the absolute values are
+// operand modifiers, and in inline asm the compiler adds no canonicalizing
+// of the loaded values (as it would for fmaxf). For finite values the result
+// equals the largest cleared-sign bit pattern; only loaded activations and
+// the running maximum are read (no result of an in-flight MFMA).
+__device__ __forceinline__ float max3_abs(float m, float a, float b)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+    return r;
+}
+
 // Largest A value of a row is 2^kHiLog2 max|a| 2^p: p puts it in [2^14, 2^15).
 template <class F>
 __device__ __forceinline__ int row_scale_exp(float am)
@@ -610,12 +622,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         // then one reduction over the lanes of the row. Clamped entries repeat
         // a group of the same row and lanes sm >= M a row that is never used,
         // so neither needs a mask here.
-        // |a| compared as integers (non-negative floats order like their
-        // bit patterns; no canonicalizing of the loaded values), bfloat16
-        // halves two at a time.
+        // f32: |a| through v_max3_f32 with absolute-value modifiers, two
+        // elements an instruction; bfloat16: the halves compared as integers
+        // (non-negative floats order like their bit patterns), two at a time.
         uint32_t mb = 0;
         u16x2 mb16 = {0, 0};
-        constexpr uint32_t kAbs = 0x7fffffffu, kAbs2 = 0x7fff7fffu;
+        float mf = 0.0f;
+        constexpr uint32_t kAbs2 = 0x7fff7fffu;
 #pragma unroll
         for (int r = 0; r < C::EPL; ++r) {
             if constexpr (BF) {
@@ -626,14 +639,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                     mb16, __builtin_elementwise_max(bitcast<u16x2>(H.x & kAbs2), bitcast<u16x2>(H.y & kAbs2)));
             } else {
                 const float4 L = areg[r][0], H = areg[r][1];
-                mb = max(mb, max(max(__float_as_uint(L.x) & kAbs, __float_as_uint(L.y) & kAbs),
-                                 max(__float_as_uint(L.z) & kAbs, __float_as_uint(L.w) & kAbs)));
-                mb = max(mb, max(max(__float_as_uint(H.x) & kAbs, __float_as_uint(H.y) & kAbs),
-                                 max(__float_as_uint(H.z) & kAbs, __float_as_uint(H.w) & kAbs)));
+                mf = max3_abs(max3_abs(mf, L.x, L.y), L.z, L.w);
+                mf = max3_abs(max3_abs(mf, H.x, H.y), H.z, H.w);
             }
         }
         if constexpr (BF)
             mb = (uint32_t)max(mb16.x, mb16.y) << 16;
+        else
+            mb = __float_as_uint(mf);
         const float am = lane_run_max_nonneg<C::QN>(__uint_as_float(mb));
         const int pe = BF ? row_scale_exp_bf16<F>(am) : row_scale_exp<F>(am);
         // Lane m QN holds row m's exponent; the epilogue needs every row's.

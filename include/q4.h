@@ -89,7 +89,14 @@ int q4_dequant(const void *w_q, size_t w_bytes, float *out, size_t out_elems, vo
  *   M in [1, 8], N >= 1, K >= 32 and K % 32 == 0 (else Q4_ERR_SHAPE);
  *   M == 0 or N == 0 is an empty problem.
  * Accuracy: |y - y_exact| <= 1e-5 * sum_k |a[m, k] * w[n, k]| + 1e-6 per
- * element. The reduction order is fixed, so repeated calls return identical bits.
+ * element. Each stretch of K that the kernel handles at once is scaled by
+ * the power of two that puts its largest A value in [2^14, 2^15) and split
+ * into two binary16 terms; binary16's floor adds a second term: each
+ * activation's split is within 2^-22 of it or within 2^-35 (2^-39 for
+ * q8_gemv) of its row's largest magnitude, whichever is larger, so a row
+ * whose magnitudes span more than about 2^18 can add up to
+ * 2^-35 * max|a[m, :]| * sum_k |w[n, k]|. The reduction order is fixed, so
+ * repeated calls return identical bits.
  */
 int q4_gemv(const float *a, const void *w_q, size_t w_bytes, float *y,
             int M, int N, int K, void *stream);
@@ -204,9 +211,9 @@ size_t q8_gemm_workspace_bytes(int M, int N, int K);
 /*
  * q4_gemv_prepare / q4_gemv_prepared — the decode GEMV in two steps, for
  * activations that several weight matrices multiply (the projections that
- * share one input) and for M > 1, where splitting the f32 activations into
- * matrix-core operands in every workgroup is most of q4_gemv's time
- * (section qmatvec_q4_0, widened to eight rows as q4_gemv).
+ * share one input) and for M > 1, where every workgroup of q4_gemv splits the
+ * same f32 activations into matrix-core operands (section qmatvec_q4_0,
+ * widened to eight rows as q4_gemv).
  *   q4_gemv_prepare(a, M, K, prep, prep_bytes, stream): a [M, K] f32,
  *     1 <= M <= 8, K a positive multiple of 256 (else Q4_ERR_SHAPE); writes
  *     q4_gemv_prepare_bytes(M, K) bytes of prepared operands to prep
@@ -220,10 +227,12 @@ size_t q8_gemm_workspace_bytes(int M, int N, int K);
  *     Q4_ERR_SHAPE when W exceeds 2^31 bytes; sizes, pointers and overlap as
  *     q4_gemv, with prep in place of a.
  * The prepared buffer is specific to the weight format (q8_gemv_prepare's
- * differs). Accuracy as q4_gemv; deterministic. Measured on MI355X, the
- * prepared GEMV beats q4_gemv from M = 4 up (8 x 4096 x 4096: 5.8 us against
- * 9.0 us, plus 3.0 us to prepare, once per shared input); at M <= 2 q4_gemv
- * is faster.
+ * differs). Accuracy as q4_gemv (the floor relative to the whole row's
+ * largest magnitude); deterministic. Measured on MI355X (N = K = 4096, cold
+ * weights), the prepared GEMV is faster than q4_gemv from M = 3 up (8 rows:
+ * 5.4 us against 6.2 us, plus 3.1 us to prepare, once per shared input) and
+ * q8_gemv_prepared than q8_gemv from M = 5 up; with fewer rows the one-step
+ * GEMV is faster (one row: 4.25 against 5.1 us).
  */
 size_t q4_gemv_prepare_bytes(int M, int K);
 int q4_gemv_prepare(const float *a, int M, int K, void *prep, size_t prep_bytes, void *stream);

@@ -17,8 +17,9 @@ if not torch.cuda.is_available():
 import oracle  # noqa: E402
 from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
-from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_matmul,  # noqa: E402
-                         oracle_matmul_sampled, random_blocks, to_dev, weight_blob)
+from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_dequant,  # noqa: E402
+                         oracle_matmul, oracle_matmul_sampled, random_blocks, to_dev,
+                         weight_blob)
 
 # "gemm" is the workspace form; "gemm_noalloc" the form with the pages' argument
 # list, on the library's own scratch (the same kernels and results).
@@ -203,6 +204,44 @@ def test_tiny_activations_against_large_scales(fmt, kind):
         a[m] *= np.float32(s)
     blob = random_blocks(fmt, N * K // 32, 64, 25, 28)
     _full_check(fmt, kind, a, blob, N, K, "%s rows 1e-30 .. 3e29" % kind, relative_only=True)
+
+
+# The binary16 floor of the two-term split that the headers state beside the
+# relative bar: an activation's split is within 2^-22 of it or within FLOOR of
+# its row's largest magnitude, whichever is larger. The GEMV's lo term is not
+# lifted by 2^11 and Q4_0's high-nibble slots sit 2^4 below the stretch's
+# largest A value; the GEMM lifts lo by 2^11 (2^-50, or 2^-46 on those slots).
+SPLIT_FLOOR = {("q4_0", "gemv"): 2.0 ** -35, ("q8_0", "gemv"): 2.0 ** -39,
+               ("q4_0", "gemm"): 2.0 ** -46, ("q8_0", "gemm"): 2.0 ** -46}
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("K", [1024, 992])   # streaming / split path, and the general kernels
+def test_wide_span_rows_meet_the_stated_bound(fmt, kind, K):
+    # Rows whose magnitudes span up to 2^60 inside one stretch of K, against
+    # |d| in [1024, 8192): every output must be within 1e-5 sum|a w| + 1e-6
+    # plus FLOOR * max|a[m, :]| * sum_k |w[n, k]|.
+    N, M = 64, 4
+    a = wl.activations_f32(71, M, K).astype(np.float64)
+    e = wl.uniform_ints(72, -60, 1, (M, K))
+    a[0] *= np.ldexp(1.0, e[0])                  # log-uniform over 2^-60 .. 2^0
+    a[1, ::5] *= 2.0 ** -40                      # tiny elements among N(0,1) ones
+    a[2] *= 2.0 ** -30
+    a[2, 100] = 2.0 ** 20                        # one large element
+    a[3] *= np.ldexp(1.0, e[3] + 80)             # the same span near 2^80
+    a = a.astype(np.float32)
+    blob = random_blocks(fmt, N * K // 32, 73, 25, 28)
+    got = np.asarray(_run(fmt, kind, a, blob, N, K), dtype=np.float64)
+    ref, bound = oracle_matmul(fmt)(a, blob, N, K)
+    w_abs = np.abs(oracle_dequant(fmt)(blob).astype(np.float64).reshape(N, K)).sum(axis=1)
+    a_max = np.abs(a.astype(np.float64)).max(axis=1)
+    tol = oracle.tolerance(bound) + SPLIT_FLOOR[fmt, kind] * a_max[:, None] * w_abs[None, :]
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, "%s %s K=%d: %d outputs beyond the stated bound, first %s: err %r tol %r" % (
+        fmt, kind, K, len(bad), tuple(bad[0]), err[tuple(bad[0])], tol[tuple(bad[0])])
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

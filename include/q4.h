@@ -392,10 +392,14 @@ int q8_gemv_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes
  *             else (smaller: Q4_ERR_WORKSPACE); always used for M, N > 0.
  * Each dequantized activation (an 8-bit code times a binary16 scale) is exact
  * in f32; every row is scaled by the power of two that puts 128 times its
- * largest |d| in [2^14, 2^15) and split into two binary16 terms, which hold
- * it exactly, then multiplied as in q4_gemm and scaled back. Accuracy: as
- * q4_gemv_q8a. Deterministic. Errors: as q4_gemm, with a_bytes checked like
- * w_bytes.
+ * largest |d| in [2^14, 2^15) and split into two binary16 terms, then
+ * multiplied as in q4_gemm and scaled back. The two terms hold every
+ * dequantized activation exactly (its last bit never falls below the lo
+ * term's grid), with one exception in q4_gemm_q8a, whose high-nibble slots
+ * take a / 16: on a row whose largest |d| is 2^15 or more, activations of
+ * blocks with |d| below 2^-13 are rounded to within 2^-24 (2^-39 of that
+ * largest |d|). Accuracy: as q4_gemv_q8a, plus that rounding on such rows.
+ * Deterministic. Errors: as q4_gemm, with a_bytes checked like w_bytes.
  */
 int q4_gemm_q8a(const void *a_q, size_t a_bytes, const void *w_q, size_t w_bytes, float *y,
                 int M, int N, int K, void *workspace, size_t workspace_bytes, void *stream);

@@ -18,7 +18,7 @@ if not torch.cuda.is_available():
 import oracle  # noqa: E402
 from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
-from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance,  # noqa: E402
+from gpu_helpers import (BLOCK_BYTES, DEV, FORMATS, Guarded, assert_within_tolerance,  # noqa: E402
                          random_blocks, to_dev, weight_blob)
 
 GEMV = {"q4_0": binding.q4_gemv_q8a, "q8_0": binding.q8_gemv_q8a}
@@ -264,6 +264,62 @@ def test_gemm_q8a_every_code_and_scale_range(fmt, K):
     got = _run_gemm(fmt, a_q, blob, M, N, K)
     assert_within_tolerance(got, ref, bound, "scale range")
     assert (got[6] == 0).all()
+
+
+def _diagonal_blob(fmt, K, value):
+    """Unit-scale weights [K, K] whose row n holds `value` at element n and zeros
+    elsewhere, so y[m, n] = a'[m, n] * value: one product per output."""
+    nb = K // 32
+    blob = np.zeros((K, nb, BLOCK_BYTES[fmt]), np.uint8)
+    blob[:, :, 1] = 0x3C                                        # d = 1.0
+    n = np.arange(K)
+    if fmt == "q4_0":
+        blob[:, :, 2:] = 0x88                                   # every nibble 8: zero
+        j = n % 32
+        byte = 2 + j % 16
+        nib = np.uint8(8 + value)
+        blob[n, n // 32, byte] = np.where(j < 16, 0x80 | nib, (nib << 4) | 0x08).astype(np.uint8)
+    else:
+        blob[n, n // 32, 2 + n % 32] = np.uint8(value & 0xFF)
+    return blob.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("K", [1024, 992])   # split path, general kernel
+def test_gemm_q8a_split_is_exact_where_stated(fmt, K):
+    # Rows whose block scales run from their largest down to binary16's
+    # subnormal 2^-24, against one power-of-two product per output. The
+    # two-term split holds every dequantized activation exactly, except on
+    # Q4_0's a / 16 slots in a row whose largest |d| is 2^15 or more, where
+    # blocks with |d| below 2^-13 round to within 2^-24.
+    M, nb = 3, K // 32
+    value = 4 if fmt == "q4_0" else 64
+    a_q = np.zeros((M, nb, 34), np.uint8)
+    for m, e_top in enumerate([15, 14, 10]):
+        e = np.round(e_top - np.arange(nb) * (e_top + 24) / (nb - 1)).astype(np.int64)
+        mant = wl.uniform_ints(80 + m, 0, 1024, nb)
+        d = np.ldexp(1.0 + mant / 1024.0, e).astype(np.float16)    # rounds below 2^-14
+        d[0] = np.float16(np.ldexp(1.0 + 1023 / 1024.0, e_top))      # the row's largest
+        d_bits = d.view(np.uint16)
+        a_q[m, :, 0], a_q[m, :, 1] = d_bits & 0xFF, d_bits >> 8
+        q = wl.uniform_ints(90 + m, -128, 128, (nb, 32))
+        q[q == 0] = 1
+        a_q[m, :, 2:] = (q & 0xFF).astype(np.uint8)
+    blob = _diagonal_blob(fmt, K, value)
+    got = _run_gemm(fmt, a_q.reshape(-1), blob, M, K, K).astype(np.float64)
+    a_deq = np.stack([oracle.q8_0_dequant(a_q[m].reshape(-1)) for m in range(M)]).astype(np.float64)
+    want = a_deq * value                                        # exact in f32 and f64
+    d_abs = np.abs(np.stack([oracle.f16_to_f32(int(x)) for x in
+                             a_q[:, :, 0].astype(np.uint16).reshape(-1) |
+                             (a_q[:, :, 1].astype(np.uint16).reshape(-1) << 8)]).reshape(M, nb))
+    exact = np.ones((M, K), bool)
+    if fmt == "q4_0":
+        hi_slot = (np.arange(K) % 32) >= 16
+        small = np.repeat(d_abs < 2.0 ** -13, 32, axis=1)
+        exact = ~(small & hi_slot[None, :] & (d_abs.max(axis=1) >= 2.0 ** 15)[:, None])
+    assert np.array_equal(got[exact], want[exact])
+    assert (np.abs(got - want)[~exact] <= 2.0 ** -24 * value).all()
+    assert exact[1:].all() and (fmt == "q8_0" or not exact[0].all())
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

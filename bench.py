@@ -287,8 +287,8 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     if prepared:
         ch = 16 if nblk % 16 == 0 else 8
         nt = (N + 15) // 16 <= 256 and nblk <= 8 * ch
-        return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s>" % (FMT_TYPE[fmt], M, ch,
-                                                                   "true" if nt else "false")
+        return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s, false>" % (FMT_TYPE[fmt], M, ch,
+                                                                          "true" if nt else "false")
     ks = kl = nblk
     if splitk:   # the library's automatic split
         groups = (N + 15) // 16
@@ -303,11 +303,14 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     ni = M if act == "bf16" else 2 * M
     splits = -(-nblk // ks)
     if M == 1 and splits == 1 and ch == 16 and (N + 15) // 16 <= 128 and ks <= 8 * ch:
-        return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8, true>" % (FMT_TYPE[fmt], bf)   # eight rows per workgroup
+        return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8, true, false>" % (FMT_TYPE[fmt], bf)   # eight rows per workgroup
+    if splits == 1 and ch == 16 and ks == 8 * 16 and (N + 15) // 16 > 256:   # row-group loops
+        return "k_gemv_stream<%s, %d, 8, 16, %s, 0, 16, %s, true>" % (FMT_TYPE[fmt], M, bf,
+                                                                      "true" if M > 1 else "false")
     spread = (N + 15) // 16 * splits > 256 or ks > 8 * ch   # non-temporal loads otherwise
     al = spread and not (ch == 16 and ni > 8)
-    return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16, %s>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0,
-                                                             "false" if spread else "true")
+    return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16, %s, false>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0,
+                                                                    "false" if spread else "true")
 
 
 def gemm_kernel_name(K, fmt="q4_0", act="f32"):

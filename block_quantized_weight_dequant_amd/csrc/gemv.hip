@@ -453,18 +453,27 @@ __device__ __forceinline__ void static_for(F &&f)
 
 // NT: the weight loads are non-temporal. Taken where every wavefront streams
 // one chunk and no second workgroup shares its compute unit (about 6% faster
-// at 1 x 4096 x 4096 and 8 x 4096 x 4096); with more chunks per wavefront or
-// workgroups per compute unit it was 3-5% slower.
+// at 1 x 4096 x 4096 and 8 x 4096 x 4096), and by the row-group loops (LN)
+// from two activation rows; with more chunks per wavefront or workgroups per
+// compute unit it was 3-5% slower.
 // MODE 0: as above. MODE 1 (AL): the MFMAs read the chunk's A operands from
 // LDS block by block instead of holding all of them in registers (only where
 // one pass holds the chunk's A operands, AH == 1). That frees CH * 4 VGPRs, so
 // two workgroups share a compute unit and one's loads overlap the other's
-// work: taken when there are more workgroups than compute units or more than
-// one chunk per wavefront. MODE 2 (PA, f32 activations): `a` holds operands
+// work: taken when there are more workgroups than compute units (and LN,
+// below, does not apply) or more than one chunk per wavefront. MODE 2 (PA, f32 activations): `a` holds operands
 // prepared once by k_gemv_prep_ops (the two-term A operands of every block in
 // [block][lane group][A row] order, then the per-row exponents), loaded
 // straight into the A registers: no per-chunk split, scale or LDS pass.
-template <class F, int M, int NW, int CH, bool BF, int MODE, int RPW = 16, bool NT = false>
+// LN (MODE 0, one chunk per wavefront, no K split): the workgroup walks the
+// row groups blockIdx.x, blockIdx.x + gridDim.x, ... of 16 weight rows with
+// the same chunk, so its activations are loaded and split once for all of
+// them; once a group's weight bytes are staged, the next group's loads are
+// issued, and each group ends with its own reduction and store (partials in
+// alternate LDS buffers, one barrier per group). Every output sees the same
+// arithmetic as without LN.
+template <class F, int M, int NW, int CH, bool BF, int MODE, int RPW = 16, bool NT = false,
+          bool LN = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
@@ -475,6 +484,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     constexpr bool AL = MODE == 1, PA = MODE == 2;
     static_assert(!AL || C::AH == 1, "A operands read from LDS need the whole chunk's in one pass");
     static_assert(!PA || !BF, "prepared operands are made from f32 activations");
+    static_assert(!LN || MODE == 0, "row-group loops keep the A operands in registers");
     constexpr int NACC = R::NACC;
     constexpr uint32_t ES = BF ? 2 : 4;           // bytes per activation
     constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
@@ -483,11 +493,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // PA needs no A area: its operands go straight to registers.
     constexpr int kLdsPerWave = PA ? C::WBYTES : C::LDS_PER_WAVE;
     __shared__ __attribute__((aligned(16))) uint8_t s_mem[NW * kLdsPerWave];
-    __shared__ float s_part[NW][M][16];
+    __shared__ float s_part[LN ? 2 : 1][NW][M][16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * RPW;
+    int n0 = blockIdx.x * RPW;
     const int nblk = K >> 5;
     const uint32_t row_bytes = (uint32_t)nblk * F::kBytes;
     uint8_t *s_w = s_mem + wave * kLdsPerWave;
@@ -510,10 +520,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // 8 NG + tcol (clamped to the last column: surplus lanes re-read it).
     // Each load thus touches one cache line's worth per row, eight rows.
     const int lrow = lane >> 3, lcol = lane & 7, trow = lane / C::TLPR, tcol = lane % C::TLPR;
-    const uint32_t row_off0 = (uint32_t)min(n0 + lrow, N - 1) * row_bytes;
-    const uint32_t row_off1 = (uint32_t)min(n0 + lrow + 8, N - 1) * row_bytes;
-    const uint32_t tail_off = (uint32_t)min(n0 + trow, N - 1) * row_bytes +
-                              16u * (uint32_t)(8 * C::NG + min(tcol, C::TC > 0 ? C::TC - 1 : 0));
+    uint32_t row_off0, row_off1, tail_off;
+    auto set_rows = [&](int r0) __attribute__((always_inline)) {
+        row_off0 = (uint32_t)min(r0 + lrow, N - 1) * row_bytes;
+        row_off1 = (uint32_t)min(r0 + lrow + 8, N - 1) * row_bytes;
+        tail_off = (uint32_t)min(r0 + trow, N - 1) * row_bytes +
+                   16u * (uint32_t)(8 * C::NG + min(tcol, C::TC > 0 ? C::TC - 1 : 0));
+    };
+    set_rows(n0);
 
     u32x4 wreg[C::NLOAD];
     // Four activations per half group: f32, or bfloat16 pairs.
@@ -530,9 +544,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     // Every lane issues every load (surplus lanes re-read an in-bounds group or
     // column that is then ignored), so the compiler's in-order wait counts are
     // exact and the first half of a chunk waits only for its own loads.
-    auto fetch = [&](int cb0) __attribute__((always_inline)) {
+    auto fetch_impl = [&](int cb0, auto acts_c) __attribute__((always_inline)) {
+        constexpr bool kActs = decltype(acts_c)::value && !PA;
 #pragma unroll
-        for (int r = 0; r < (PA ? 0 : C::EPL); ++r) {
+        for (int r = 0; r < (kActs ? C::EPL : 0); ++r) {
             const int c = min(sq + C::QN * (r % C::EPP), 4 * C::CHH - 1);
             const int b = (r / C::EPP) * C::CHH + (c >> 2), gg = c & 3;
             const uint32_t off = ((uint32_t)sm_ld * K + (uint32_t)(cb0 + b) * 32 + F::a_lo(1) * gg) * ES;
@@ -561,6 +576,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         asm volatile("" ::"s"(w) : "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto fetch = [&](int cb0) __attribute__((always_inline)) { fetch_impl(cb0, std::true_type{}); };
+    auto fetch_w = [&](int cb0) __attribute__((always_inline)) { fetch_impl(cb0, std::false_type{}); };
 
     // Unconditional, so no copies of the loaded registers are needed after a
     // branch (they would wait for the loads). A wavefront without blocks
@@ -710,7 +727,31 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     split_activations();
-    for (int cb0 = wb0; cb0 < kb_hi; cb0 += kStride) {
+    // Epilogue of one row group: wavefront partials into LDS (buffer buf),
+    // then summed in wavefront order and stored.
+    auto write_out = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < R::NOUT; ++h) {
+            const int m = R::row(g, h);
+            if (m < M && j < RPW)
+                s_part[buf][wave][m][j] = ysum[h];
+            ysum[h] = 0.0f;
+        }
+        __syncthreads();
+        if (tid < M * RPW) {
+            const int m = tid / RPW, jj = tid % RPW, n = n0 + jj;
+            float sum = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww)
+                sum += s_part[buf][ww][m][jj];
+            if (n < N)
+                y[(size_t)m * N + n] = sum;
+        }
+    };
+    // LN: this workgroup's row group (it walks groups blockIdx.x, + gridDim.x, ...).
+    int rg = blockIdx.x, it = 0;
+    for (int cb0 = wb0; cb0 < kb_hi; cb0 += LN ? 0 : kStride) {
+        const bool more = LN ? (rg + (int)gridDim.x) * RPW < N : cb0 + kStride < kb_hi;
         // The chunk is contracted in NPART parts. Part p needs only loads
         // [0, loads_for(end of p)) of every lane, which drain first (vmcnt
         // counts in issue order), so its decode and MFMAs run while the rest of
@@ -791,7 +832,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
             };
             if constexpr (P < C::NPART - 1) {
                 run_part();
-            } else if (cb0 + kStride < kb_hi) {
+            } else if (LN && more) {
+                // Every load of this group is staged: prefetch the next
+                // group's weights for the same chunk, then finish this one.
+                set_rows((rg + (int)gridDim.x) * RPW);
+                fetch_w(cb0);
+                run_part();
+                finish_chunk();
+            } else if (more) {
                 // Every load of this chunk is staged: prefetch the next chunk,
                 // finish this one, then split the next chunk's activations (PA:
                 // load its prepared operands, once this chunk's are used). The
@@ -808,24 +856,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 finish_chunk();
             }
         });
+        if constexpr (LN) {
+            write_out(it & 1);
+            if (!more)
+                break;
+            rg += (int)gridDim.x;
+            ++it;
+            n0 = rg * RPW;
+            wave_lds_sync();   // this group's LDS reads precede the next group's writes
+        }
     }
-
-#pragma unroll
-    for (int h = 0; h < R::NOUT; ++h) {
-        const int m = R::row(g, h);
-        if (m < M && j < RPW)
-            s_part[wave][m][j] = ysum[h];
-    }
-    __syncthreads();
-    if (tid < M * RPW) {
-        const int m = tid / RPW, jj = tid % RPW, n = n0 + jj;
-        float s = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww)
-            s += s_part[ww][m][jj];
-        if (n < N)
-            y[(size_t)m * N + n] = s;
-    }
+    if constexpr (!LN)
+        write_out(0);
 }
 
 // Sums the partials of a K-split GEMV in split order: y[i] = sum_s part[s][i].
@@ -875,6 +917,15 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
                 return launch_kernel(k_gemv_stream<F, 1, NW, 16, BF, 1, 8, true>,
                                      dim3((unsigned)((N + 7) / 8), 1u), dim3(64 * NW), 0, s, a, w,
                                      y, N, K, ks);
+        // More row groups than compute units, one chunk per wavefront (K/32 ==
+        // 8 x 16): 256 workgroups walk the row groups (LN), each splitting its
+        // activations once instead of once per 16 rows, with the next group's
+        // weights in flight while a group finishes (8 x 14336 x 4096: 19.8 ->
+        // 10.9 us, 4 x 14336 x 4096: 16.0 -> 10.0, 1 x 14336 x 4096: 9.5 ->
+        // 9.0). Non-temporal loads from M = 2 (1-3% there, 1.5% slower at M = 1).
+        if (splits == 1 && ch == 16 && ks == NW * 16 && grid > 256)
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0, 16, (M > 1), true>,
+                                 dim3(256u), dim3(64 * NW), 0, s, a, w, y, N, K, ks);
         if (ch == 16) {
             if constexpr (GemvStreamCfg<F, M, NW, 16, BF>::AH == 1)
                 if (al)

@@ -17,9 +17,9 @@ if not torch.cuda.is_available():
 import oracle  # noqa: E402
 from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
-from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_dequant,  # noqa: E402
-                         oracle_matmul, oracle_matmul_sampled, random_blocks, to_dev,
-                         weight_blob)
+from gpu_helpers import (BLOCK_BYTES, DEV, FORMATS, Guarded, assert_within_tolerance,  # noqa: E402
+                         oracle_dequant, oracle_matmul, oracle_matmul_sampled, random_blocks,
+                         to_dev, weight_blob)
 
 # "gemm" is the workspace form; "gemm_noalloc" the form with the pages' argument
 # list, on the library's own scratch (the same kernels and results).
@@ -79,12 +79,39 @@ def test_gemm_workloads_sampled(fmt, kind, name):
 # ------------------------------------------------------ shapes and tails
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_gemv_row_group_loop_matches_single_groups(fmt, M):
+    # 9000 weight rows at K = 4096: 256 workgroups walk 563 row groups, each
+    # splitting its activations once. The first and second 4096 rows run again
+    # as GEMVs of their own (one row group per workgroup): every output must
+    # come out with the same bits.
+    N, K = 9000, 4096
+    blob = weight_blob(fmt, N, K, 91 + M)
+    a = wl.activations_f32(92 + M, M, K)
+    w = to_dev(blob)
+    a_dev = to_dev(a)
+    full = torch.empty(M * N, dtype=torch.float32, device=DEV)
+    binding_gemv = ENTRY[fmt, "gemv"]
+    binding_gemv(a_dev, w, full, M, N, K)
+    row_bytes = K // 32 * BLOCK_BYTES[fmt]
+    for r0 in (0, 4096):
+        part = torch.empty(M * 4096, dtype=torch.float32, device=DEV)
+        binding_gemv(a_dev, w[r0 * row_bytes:(r0 + 4096) * row_bytes], part, M, 4096, K)
+        torch.cuda.synchronize()
+        got = full.view(M, N)[:, r0:r0 + 4096].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), part.view(M, 4096).cpu().numpy().view(np.uint32)), r0
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(17, 32), (300, 256), (129, 1056), (64, 4096), (33, 8192),
-                                 (4200, 4096), (5000, 2048)])
+                                 (4200, 4096), (9000, 4096), (5000, 2048)])
 def test_gemv_shapes(fmt, M, N, K):
-    # N > 4096 gives more workgroups than compute units and K = 8192 several
-    # chunks per wavefront: the streaming kernel then reads A from LDS.
+    # More than 256 row groups at K = 4096 (one chunk per wavefront): 256
+    # workgroups walk the groups, two or three each, the last one ragged.
+    # K = 8192 gives several chunks per wavefront and N = 5000 at K = 2048
+    # more workgroups than compute units: the streaming kernel then reads A
+    # from LDS.
     blob = weight_blob(fmt, N, K, 10 * M + K)
     a = wl.activations_f32(20 * M + N, M, K)
     _full_check(fmt, "gemv", a, blob, N, K, "gemv %dx%dx%d" % (M, N, K))

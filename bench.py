@@ -675,6 +675,7 @@ MORE_ROWS = [
     ("q8_0_gemv_bf16_1x4096x4096", None), ("gemm_bf16_1024x4096x4096", 50),
     ("gemm_bf16_2048x14336x4096", 20), ("q8_0_gemm_bf16_2048x14336x4096", 20),
     ("gemv_prepared_1x4096x4096", None), ("gemv_prepared_8x4096x4096", None),
+    ("gemv_8x14336x4096", None),
     ("gemv_1x512x4096", None), ("gemm_2048x1792x4096", 50), ("gemv_1x512x14336", None),
     ("gemv_splitk_1x512x14336", None), ("gemv_q8a_1x4096x4096", None),
     ("gemv_q8a_8x4096x4096", None), ("q8_0_gemv_q8a_1x4096x4096", None),
@@ -756,7 +757,8 @@ def main_bench(args):
         emit_row(bench_product(torch, q4, wl, "gemv_1x256x512", S, W, reps, P, cold=False), rows)
         for name, st in MORE_ROWS:
             r = bench_product(torch, q4, wl, name, min(st or S, S), small_w, reps, P)
-            if name in ("gemv_1x512x4096", "gemv_1x512x14336", "gemv_splitk_1x512x14336"):
+            if name in ("gemv_1x512x4096", "gemv_1x512x14336", "gemv_splitk_1x512x14336",
+                        "gemv_8x14336x4096"):
                 c = bench_stream_ceiling(torch, r["algorithmic_bytes"], S, W, reps, P)
                 r["roofline"]["measured_read_ceiling_GBs"] = c["kernel_GBs"]
                 r["roofline"]["frac_of_measured_read_ceiling"] = r["roofline"]["achieved"] / c["kernel_GBs"]

@@ -48,6 +48,10 @@ WORKLOADS = {
     "gemv_1x512x14336": dict(kind="gemv", M=1, N=512, K=14336, w_seed=502, a_seed=503),
     "gemv_splitk_1x512x14336": dict(kind="gemv", splitk=True, M=1, N=512, K=14336, w_seed=502,
                                     a_seed=503),
+    # Batched decode through an FFN up-projection: eight activation rows
+    # against the 14336 x 4096 weight of the prefill GEMM (more row groups
+    # than compute units).
+    "gemv_8x14336x4096": dict(kind="gemv", M=8, N=14336, K=4096, w_seed=400, a_seed=202),
     # The decode GEMV from activations prepared once (``prepared``: the GEMV
     # alone, as when several weight matrices share one prepared input).
     "gemv_prepared_1x4096x4096": dict(kind="gemv", prepared=True, M=1, N=4096, K=4096,

@@ -276,16 +276,22 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     if act == "q8_0":
         if K % 256:
             return "k_gemv_q8a_any<%s, %d>" % (FMT_TYPE[fmt], M)
-        ch16 = (K // 32) % 16 == 0 and ((N + 15) // 16 <= 256 or M == 1)
-        nt = ch16 and (N + 15) // 16 <= 256 and K // 32 <= 128   # non-temporal weight loads
-        return "k_gemv_q8a<%s, %d, 8, %d, %s>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8,
-                                                 "true" if nt else "false")
+        groups = (N + 15) // 16
+        if M > 1 and (K // 32) % 16 == 0 and groups > 256 and K // 32 == 128:   # row-group loops
+            return "k_gemv_q8a<%s, %d, 8, 16, %s, true>" % (FMT_TYPE[fmt], M,
+                                                           "true" if fmt == "q4_0" else "false")
+        ch16 = (K // 32) % 16 == 0 and (groups <= 256 or M == 1)
+        nt = ch16 and groups <= 256 and K // 32 <= 128   # non-temporal weight loads
+        return "k_gemv_q8a<%s, %d, 8, %d, %s, false>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8,
+                                                        "true" if nt else "false")
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
     if prepared:
         ch = 16 if nblk % 16 == 0 else 8
+        if ch == 16 and (N + 15) // 16 > 256 and nblk == 8 * 16:   # row-group loops
+            return "k_gemv_stream<%s, %d, 8, 16, false, 2, 16, false, true>" % (FMT_TYPE[fmt], M)
         nt = (N + 15) // 16 <= 256 and nblk <= 8 * ch
         return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s, false>" % (FMT_TYPE[fmt], M, ch,
                                                                           "true" if nt else "false")

@@ -465,13 +465,13 @@ __device__ __forceinline__ void static_for(F &&f)
 // prepared once by k_gemv_prep_ops (the two-term A operands of every block in
 // [block][lane group][A row] order, then the per-row exponents), loaded
 // straight into the A registers: no per-chunk split, scale or LDS pass.
-// LN (MODE 0, one chunk per wavefront, no K split): the workgroup walks the
-// row groups blockIdx.x, blockIdx.x + gridDim.x, ... of 16 weight rows with
-// the same chunk, so its activations are loaded and split once for all of
-// them; once a group's weight bytes are staged, the next group's loads are
-// issued, and each group ends with its own reduction and store (partials in
-// alternate LDS buffers, one barrier per group). Every output sees the same
-// arithmetic as without LN.
+// LN (MODE 0 or 2, one chunk per wavefront, no K split): the workgroup
+// walks the row groups blockIdx.x, blockIdx.x + gridDim.x, ... of 16 weight
+// rows with the same chunk, so its activations are loaded and split (or its
+// prepared operands loaded) once for all of them; once a group's weight bytes
+// are staged, the next group's loads are issued, and each group ends with its
+// own reduction and store (partials in alternate LDS buffers, one barrier per
+// group). Every output sees the same arithmetic as without LN.
 template <class F, int M, int NW, int CH, bool BF, int MODE, int RPW = 16, bool NT = false,
           bool LN = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
     constexpr bool AL = MODE == 1, PA = MODE == 2;
     static_assert(!AL || C::AH == 1, "A operands read from LDS need the whole chunk's in one pass");
     static_assert(!PA || !BF, "prepared operands are made from f32 activations");
-    static_assert(!LN || MODE == 0, "row-group loops keep the A operands in registers");
+    static_assert(!LN || MODE != 1, "row-group loops keep the A operands in registers");
     constexpr int NACC = R::NACC;
     constexpr uint32_t ES = BF ? 2 : 4;           // bytes per activation
     constexpr int ASTRIDE = 4 * C::NI * 16;       // A bytes per block
@@ -1042,8 +1042,14 @@ static hipError_t launch_gemv_prepared_m(const void *prep, const uint8_t *w, flo
     const int nblk = K / 32;
     const unsigned grid = (unsigned)((N + 15) / 16);
     // Non-temporal weight loads with one chunk per wavefront and one
-    // workgroup per compute unit, as in launch_gemv_m.
+    // workgroup per compute unit, as in launch_gemv_m; row-group loops (plain
+    // loads) where there are more row groups than compute units, so each
+    // workgroup loads the prepared operands once (8 x 14336 x 4096: 15.5 ->
+    // 10.9 us, 1 x 14336 x 4096: 14.1 -> 9.9).
     if (q4v::gemv_chunk_blocks(nblk, nblk) == 16) {
+        if (grid > 256 && nblk == NW * 16)
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, false, true>, dim3(256u),
+                                 dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
         if (grid <= 256 && nblk <= NW * 16)
             return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, true>, dim3(grid),
                                  dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
@@ -1152,6 +1158,10 @@ hipError_t launch_gemv_splitk(WeightFormat fmt, const float *a, const uint8_t *w
 //   chunk's M activation rows (CH * 34 bytes each, 16-byte aligned) are staged
 //   beside them with 16-byte loads, and their scales are widened once per
 //   chunk into an f32 [block][row] table.
+// * LN (one chunk per wavefront, more row groups than compute units): the
+//   workgroup walks row groups blockIdx.x, + gridDim.x, ... as k_gemv_stream
+//   does; the chunk's activation blocks and scale table are staged once and
+//   stay in LDS, and each group ends with its own reduction and store.
 
 // Low and high nibbles of a Q4_0 qs dword as signed bytes 16 (q - 8).
 __device__ __forceinline__ long q4_codes_x16(uint32_t x)
@@ -1207,7 +1217,7 @@ __device__ __forceinline__ long q8a_weight_operand(const uint32_t *wrow, int g)
 template <class F>
 constexpr float q8a_weight_scale() { return F::kBytes == kQ4Bytes ? 0.0625f : 1.0f; }
 
-template <class F, int M, int NW, int CH, bool NT = false>
+template <class F, int M, int NW, int CH, bool NT = false, bool LN = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict__ aq,
                                                      const uint8_t *__restrict__ w,
                                                      float *__restrict__ y, int N, int K)
@@ -1224,11 +1234,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
     constexpr int kLdsPerWave = C::WBYTES + ABYTES + CH * 8 * 4;
     static_assert(kLdsPerWave % 16 == 0, "16-byte aligned areas");
     __shared__ __attribute__((aligned(16))) uint8_t s_mem[NW * kLdsPerWave];
-    __shared__ float s_part[NW][M][16];
+    __shared__ float s_part[LN ? 2 : 1][NW][M][16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    int n0 = blockIdx.x * 16;
     const int nblk = K >> 5;
     const uint32_t row_bytes = (uint32_t)nblk * F::kBytes;
     const uint32_t arow_bytes = (uint32_t)nblk * kQ8Bytes;
@@ -1241,19 +1251,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
     // Weight loader role as in k_gemv_stream: eight lanes per row, eight rows
     // per load, then the tail columns.
     const int lrow = lane >> 3, lcol = lane & 7, trow = lane >> 2, tcol = lane & 3;
-    const uint32_t row_off0 = (uint32_t)min(n0 + lrow, N - 1) * row_bytes;
-    const uint32_t row_off1 = (uint32_t)min(n0 + lrow + 8, N - 1) * row_bytes;
-    const uint32_t tail_off = (uint32_t)min(n0 + trow, N - 1) * row_bytes +
-                              16u * (uint32_t)(8 * C::NG + min(tcol, C::TC > 0 ? C::TC - 1 : 0));
+    uint32_t row_off0, row_off1, tail_off;
+    auto set_rows = [&](int r0) __attribute__((always_inline)) {
+        row_off0 = (uint32_t)min(r0 + lrow, N - 1) * row_bytes;
+        row_off1 = (uint32_t)min(r0 + lrow + 8, N - 1) * row_bytes;
+        tail_off = (uint32_t)min(r0 + trow, N - 1) * row_bytes +
+                   16u * (uint32_t)(8 * C::NG + min(tcol, C::TC > 0 ? C::TC - 1 : 0));
+    };
+    set_rows(n0);
 
     u32x4 wreg[C::NLOAD];
     u32x4 areg[NAL];
     // Activation columns first (they drain first), then the weight columns.
     // Every lane issues every load; surplus lanes re-read the last activation
     // column and never store it.
-    auto fetch = [&](int cb0) __attribute__((always_inline)) {
+    auto fetch_impl = [&](int cb0, auto acts_c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < NAL; ++r) {
+        for (int r = 0; r < (decltype(acts_c)::value ? NAL : 0); ++r) {
             const int e = min(lane + 64 * r, NAE - 1);
             const int m = e / CPRA, col = e - m * CPRA;
             areg[r] = *reinterpret_cast<const u32x4 *>(
@@ -1276,6 +1290,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
         asm volatile("" ::"s"(w), "s"(aq) : "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto fetch = [&](int cb0) __attribute__((always_inline)) { fetch_impl(cb0, std::true_type{}); };
+    auto fetch_w = [&](int cb0) __attribute__((always_inline)) { fetch_impl(cb0, std::false_type{}); };
     // A wavefront without blocks fetches the row's last chunk and never reads it.
     fetch(min(wb0, nblk - CH));
 
@@ -1288,23 +1304,50 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
     for (int r = 0; r < NACC; ++r)
         ysum[r] = 0.0f;
 
-    for (int cb0 = wb0; cb0 < nblk; cb0 += kStride) {
+    // Epilogue of one row group: wavefront partials into LDS (buffer buf),
+    // then summed in wavefront order and stored.
+    auto write_out = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < NAL; ++r) {
-            const int e = lane + 64 * r;
-            if (e < NAE) {
-                const int m = e / CPRA, col = e - m * CPRA;
-                *reinterpret_cast<u32x4 *>(s_act + m * RSA + 16 * col) = areg[r];
-            }
+        for (int r = 0; r < NACC; ++r) {
+            const int m = 4 * g + r;
+            if (m < M)
+                s_part[buf][wave][m][j] = ysum[r];
+            ysum[r] = 0.0f;
         }
-        wave_lds_sync();
+        __syncthreads();
+        if (tid < M * 16) {
+            const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
+            float sum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < (NDA + 63) / 64; ++r) {
-            const int t = lane + 64 * r;
-            if (t < NDA) {
-                const int b = t / M, m = t - b * M;
-                s_da[b * 8 + m] = f16_bits_to_f32(
-                    *reinterpret_cast<const uint16_t *>(s_act + m * RSA + kQ8Bytes * b));
+            for (int ww = 0; ww < NW; ++ww)
+                sum += s_part[buf][ww][m][jj];
+            if (n < N)
+                y[(size_t)m * N + n] = sum;
+        }
+    };
+    // LN: this workgroup's row group (it walks groups blockIdx.x, + gridDim.x,
+    // ...); the chunk's activation blocks and scale table stay in LDS.
+    int rg = blockIdx.x, it = 0;
+    for (int cb0 = wb0; cb0 < nblk; cb0 += LN ? 0 : kStride) {
+        const bool more = LN ? (rg + (int)gridDim.x) * 16 < N : cb0 + kStride < nblk;
+        if (!LN || it == 0) {
+#pragma unroll
+            for (int r = 0; r < NAL; ++r) {
+                const int e = lane + 64 * r;
+                if (e < NAE) {
+                    const int m = e / CPRA, col = e - m * CPRA;
+                    *reinterpret_cast<u32x4 *>(s_act + m * RSA + 16 * col) = areg[r];
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int r = 0; r < (NDA + 63) / 64; ++r) {
+                const int t = lane + 64 * r;
+                if (t < NDA) {
+                    const int b = t / M, m = t - b * M;
+                    s_da[b * 8 + m] = f16_bits_to_f32(
+                        *reinterpret_cast<const uint16_t *>(s_act + m * RSA + kQ8Bytes * b));
+                }
             }
         }
         float acc[NACC];
@@ -1362,7 +1405,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
             };
             if constexpr (P < C::NPART - 1) {
                 run_part();
-            } else if (cb0 + kStride < nblk) {
+            } else if (LN && more) {
+                // Every weight register of this group is staged: the next
+                // group's loads for the same chunk, then this group's last part.
+                set_rows((rg + (int)gridDim.x) * 16);
+                fetch_w(cb0);
+                run_part();
+            } else if (more) {
                 fetch(cb0 + kStride);   // every register of this chunk is staged
                 run_part();
             } else {
@@ -1373,25 +1422,19 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
         for (int r = 0; r < NACC; ++r)
             ysum[r] += acc[r];
         wave_lds_sync();   // this chunk's LDS reads precede the next chunk's writes
+        if constexpr (LN) {
+            write_out(it & 1);
+            if (!more)
+                break;
+            rg += (int)gridDim.x;
+            ++it;
+            n0 = rg * 16;
+        }
     }
-
-#pragma unroll
-    for (int r = 0; r < NACC; ++r) {
-        const int m = 4 * g + r;
-        if (m < M)
-            s_part[wave][m][j] = ysum[r];
-    }
-    __syncthreads();
-    if (tid < M * 16) {
-        const int m = tid >> 4, jj = tid & 15, n = n0 + jj;
-        float sum = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww)
-            sum += s_part[ww][m][jj];
-        if (n < N)
-            y[(size_t)m * N + n] = sum;
-    }
+    if constexpr (!LN)
+        write_out(0);
 }
+
 
 // General shapes (K % 256 != 0, or offsets beyond 31 bits): the same
 // arithmetic with each lane loading its operands and scales from global memory
@@ -1471,6 +1514,16 @@ static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *
         // let two or more share it and overlap one's loads with another's work.
         // Non-temporal weight loads as in launch_gemv_m: one chunk per
         // wavefront and one workgroup per compute unit.
+        // More row groups than compute units and one 16-block chunk per
+        // wavefront, from two activation rows: 256 workgroups walk the row
+        // groups, staging each chunk's activation blocks and scales once (as
+        // launch_gemv_m; 8 x 14336 x 4096: 13.6 -> 11.4 us, 8 x 8192 x 4096:
+        // 8.2 -> 7.2; one row: 9.1 -> 9.5, so not there). Non-temporal loads
+        // for Q4_0 weights only (Q8_0 8 x 14336 x 4096: 15.4 us plain, 16.3).
+        if constexpr (M > 1)
+            if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && grid > 256 && nblk == NW * 16)
+                return launch_kernel(k_gemv_q8a<F, M, NW, 16, F::kBytes == kQ4Bytes, true>,
+                                     dim3(256u), dim3(64 * NW), 0, s, aq, w, y, N, K);
         if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && grid <= 256 && nblk <= NW * 16)
             return launch_kernel(k_gemv_q8a<F, M, NW, 16, true>, dim3(grid), dim3(64 * NW), 0, s,
                                  aq, w, y, N, K);

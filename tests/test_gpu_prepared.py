@@ -15,8 +15,8 @@ if not torch.cuda.is_available():
 import oracle  # noqa: E402
 from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
-from gpu_helpers import (DEV, FORMATS, Guarded, assert_within_tolerance, oracle_matmul,  # noqa: E402
-                         random_blocks, to_dev, weight_blob)
+from gpu_helpers import (BLOCK_BYTES, DEV, FORMATS, Guarded, assert_within_tolerance,  # noqa: E402
+                         oracle_matmul, random_blocks, to_dev, weight_blob)
 
 F = {"q4_0": "q4", "q8_0": "q8"}
 
@@ -46,13 +46,34 @@ def _run(fmt, a, blob, N, K):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (33, 8192), (129, 14336)])
+@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (9000, 4096), (33, 8192),
+                                 (129, 14336)])
 def test_prepared_shapes(fmt, M, N, K):
+    # More than 256 row groups at K = 4096 (4200, 9000): 256 workgroups walk
+    # the groups, loading the prepared operands once.
     blob = weight_blob(fmt, N, K, 13 * M + N)
     a = wl.activations_f32(17 * M + K, M, K)
     got = _run(fmt, a, blob, N, K)
     ref, bound = oracle_matmul(fmt)(a, blob, N, K)
     assert_within_tolerance(got, ref, bound, "%s prepared %dx%dx%d" % (fmt, M, N, K))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M", [1, 8])
+def test_prepared_row_group_loop_matches_single_groups(fmt, M):
+    # 9000 weight rows from one prepared buffer: the row-group loops' outputs
+    # for the first and second 4096 rows equal, bit for bit, GEMVs over those
+    # rows alone (one group per workgroup, the same operands and chunks).
+    N, K = 9000, 4096
+    blob = weight_blob(fmt, N, K, 95 + M)
+    a = wl.activations_f32(96 + M, M, K)
+    prep = _prepare(fmt, to_dev(a), M, K)
+    w = to_dev(blob)
+    full = _prepared(fmt, prep, w, M, N, K)
+    row_bytes = K // 32 * BLOCK_BYTES[fmt]
+    for r0 in (0, 4096):
+        part = _prepared(fmt, prep, w[r0 * row_bytes:(r0 + 4096) * row_bytes], M, 4096, K)
+        assert np.array_equal(full[:, r0:r0 + 4096].view(np.uint32), part.view(np.uint32)), r0
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

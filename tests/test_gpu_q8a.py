@@ -43,8 +43,8 @@ def _run(fmt, a_q, blob, M, N, K, a_dev=None, w_dev=None):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (33, 8192), (129, 14336),
-                                 (50, 96), (17, 4128)])
+@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (9000, 4096), (33, 8192),
+                                 (129, 14336), (50, 96), (17, 4128)])
 def test_q8a_shapes(fmt, M, N, K):
     # K % 256 == 0 takes the streaming kernel (16- or 8-block chunks, one or
     # several per wavefront, wavefronts without blocks); 96 and 4128 the
@@ -54,6 +54,24 @@ def test_q8a_shapes(fmt, M, N, K):
     ref, bound = _ref(fmt)(a_q, M, blob, N, K)
     assert_within_tolerance(_run(fmt, a_q, blob, M, N, K), ref, bound,
                             "%s q8a %dx%dx%d" % (fmt, M, N, K))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_q8a_row_group_loop_matches_single_groups(fmt, M):
+    # 9000 weight rows at K = 4096 from two activation rows: 256 workgroups
+    # walk 563 row groups with the activation blocks staged once. The first and
+    # second 4096 rows as GEMVs of their own (one group per workgroup, the same
+    # 16-block chunks) must give the same bits.
+    N, K = 9000, 4096
+    blob = weight_blob(fmt, N, K, 93 + M)
+    a_q = _act_blob(94 + M, M, K)
+    w, a_dev = to_dev(blob), to_dev(a_q)
+    full = _run(fmt, a_q, blob, M, N, K, a_dev=a_dev, w_dev=w)
+    row_bytes = K // 32 * BLOCK_BYTES[fmt]
+    for r0 in (0, 4096):
+        part = _run(fmt, a_q, blob, M, 4096, K, a_dev=a_dev, w_dev=w[r0 * row_bytes:(r0 + 4096) * row_bytes])
+        assert np.array_equal(full[:, r0:r0 + 4096].view(np.uint32), part.view(np.uint32)), r0
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

@@ -277,9 +277,11 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
         if K % 256:
             return "k_gemv_q8a_any<%s, %d>" % (FMT_TYPE[fmt], M)
         groups = (N + 15) // 16
-        if M > 1 and (K // 32) % 16 == 0 and groups > 256 and K // 32 == 128:   # row-group loops
-            return "k_gemv_q8a<%s, %d, 8, 16, %s, true>" % (FMT_TYPE[fmt], M,
+        if M > 1 and groups > 256 and K // 32 in (64, 128):   # row-group loops
+            return "k_gemv_q8a<%s, %d, 8, %d, %s, true>" % (FMT_TYPE[fmt], M, K // 256,
                                                            "true" if fmt == "q4_0" else "false")
+        if groups <= 256 and K // 32 == 64:   # one 8-block chunk per wavefront
+            return "k_gemv_q8a<%s, %d, 8, 8, true, false>" % (FMT_TYPE[fmt], M)
         ch16 = (K // 32) % 16 == 0 and (groups <= 256 or M == 1)
         nt = ch16 and groups <= 256 and K // 32 <= 128   # non-temporal weight loads
         return "k_gemv_q8a<%s, %d, 8, %d, %s, false>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8,
@@ -290,8 +292,11 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     nblk = K // 32
     if prepared:
         ch = 16 if nblk % 16 == 0 else 8
-        if ch == 16 and (N + 15) // 16 > 256 and nblk == 8 * 16:   # row-group loops
-            return "k_gemv_stream<%s, %d, 8, 16, false, 2, 16, false, true>" % (FMT_TYPE[fmt], M)
+        if (N + 15) // 16 > 256 and nblk in (64, 128):   # row-group loops
+            return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, false, true>" % (FMT_TYPE[fmt], M,
+                                                                                nblk // 8)
+        if nblk == 64:   # one 8-block chunk per wavefront
+            return "k_gemv_stream<%s, %d, 8, 8, false, 2, 16, true, false>" % (FMT_TYPE[fmt], M)
         nt = (N + 15) // 16 <= 256 and nblk <= 8 * ch
         return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s, false>" % (FMT_TYPE[fmt], M, ch,
                                                                           "true" if nt else "false")
@@ -310,9 +315,11 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     splits = -(-nblk // ks)
     if M == 1 and splits == 1 and ch == 16 and (N + 15) // 16 <= 128 and ks <= 8 * ch:
         return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8, true, false>" % (FMT_TYPE[fmt], bf)   # eight rows per workgroup
-    if splits == 1 and ch == 16 and ks == 8 * 16 and (N + 15) // 16 > 256:   # row-group loops
-        return "k_gemv_stream<%s, %d, 8, 16, %s, 0, 16, %s, true>" % (FMT_TYPE[fmt], M, bf,
-                                                                      "true" if M > 1 else "false")
+    if splits == 1 and ((ch == 16 and ks == 8 * 16) or ks == 8 * 8) and (N + 15) // 16 > 256:
+        return "k_gemv_stream<%s, %d, 8, %d, %s, 0, 16, %s, true>" % (   # row-group loops
+            FMT_TYPE[fmt], M, ks // 8, bf, "true" if M > 1 else "false")
+    if splits == 1 and ks == 8 * 8:   # one 8-block chunk per wavefront
+        return "k_gemv_stream<%s, %d, 8, 8, %s, 0, 16, true, false>" % (FMT_TYPE[fmt], M, bf)
     spread = (N + 15) // 16 * splits > 256 or ks > 8 * ch   # non-temporal loads otherwise
     al = spread and not (ch == 16 and ni > 8)
     return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16, %s, false>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0,

@@ -94,10 +94,10 @@ def test_gemv_workloads_full_output(name):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(17, 32), (300, 256), (129, 1056), (64, 4096), (33, 8192),
-                                 (4200, 4096), (9000, 4096)])
+                                 (4200, 4096), (9000, 4096), (1000, 2048), (5000, 2048)])
 def test_gemv_shapes(fmt, M, N, K):
     # K % 256 != 0 (32, 1056) takes the general kernel; more than 256 row
-    # groups at K = 4096 the row-group loops.
+    # groups at K = 4096 or 2048 the row-group loops.
     blob = weight_blob(fmt, N, K, 10 * M + K)
     bits = wl.activations_bf16(20 * M + N, M, K)
     _full_check(fmt, bits, blob, N, K, "gemv_bf16 %dx%dx%d" % (M, N, K), kind="gemv")

@@ -47,7 +47,7 @@ def _run(fmt, a, blob, N, K):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (9000, 4096), (33, 8192),
-                                 (129, 14336)])
+                                 (129, 14336), (1000, 2048), (5000, 2048)])
 def test_prepared_shapes(fmt, M, N, K):
     # More than 256 row groups at K = 4096 (4200, 9000): 256 workgroups walk
     # the groups, loading the prepared operands once.

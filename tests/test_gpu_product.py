@@ -105,10 +105,12 @@ def test_gemv_row_group_loop_matches_single_groups(fmt, M):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K", [(17, 32), (300, 256), (129, 1056), (64, 4096), (33, 8192),
-                                 (4200, 4096), (9000, 4096), (1000, 2048), (5000, 2048)])
+                                 (4097, 4096), (4200, 4096), (9000, 4096), (1000, 2048),
+                                 (5000, 2048)])
 def test_gemv_shapes(fmt, M, N, K):
     # More than 256 row groups at K = 4096 (one chunk per wavefront): 256
-    # workgroups walk the groups, two or three each, the last one ragged.
+    # workgroups walk the groups, two or three each, the last one ragged (at
+    # N = 4097 one workgroup takes a second group of one row).
     # K = 2048 gives one 8-block chunk per wavefront (row-group loops at
     # N = 5000); K = 8192 several chunks per wavefront, where the streaming
     # kernel reads A from LDS.

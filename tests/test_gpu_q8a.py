@@ -43,7 +43,7 @@ def _run(fmt, a_q, blob, M, N, K, a_dev=None, w_dev=None):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4200, 4096), (9000, 4096), (33, 8192),
+@pytest.mark.parametrize("N,K", [(300, 256), (64, 4096), (4097, 4096), (4200, 4096), (9000, 4096), (33, 8192),
                                  (129, 14336), (50, 96), (17, 4128), (1000, 2048), (5000, 2048)])
 def test_q8a_shapes(fmt, M, N, K):
     # K % 256 == 0 takes the streaming kernel (16- or 8-block chunks, one or

@@ -538,6 +538,55 @@ def bench_stream_ceiling(torch, nbytes, steps, warmup, reps, profile, cold=True)
     return row
 
 
+def bench_rw_ceiling(torch, groups, read_words, write_words, steps, warmup, reps, profile):
+    """Reading groups * read_words and writing groups * write_words 16-byte
+    words, interleaved in that proportion (q4probe_stream_rw), cold: the
+    ceiling for one launch that turns that many input bytes into that many
+    output bytes (the quantizer 64 : 17, the dequant 9 : 64)."""
+    path = os.path.join(ROOT, "block_quantized_weight_dequant_amd", "libq4probe.so")
+    lib = ctypes.CDLL(path)
+    lib.q4probe_stream_rw.restype = ctypes.c_int
+    lib.q4probe_stream_rw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    rb, wb = groups * read_words * 16, groups * write_words * 16
+    name = "stream_rw_%dB_%dB" % (rb, wb)
+    MARKS.push(name)
+    R = copies_for_cold(rb + wb)
+    srcs = [torch.full((rb,), 0x37, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dsts = [torch.empty(wb, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+
+    # The fastest of the probe's shapes (groups per wavefront, cached or
+    # non-temporal loads and stores) is the ceiling.
+    best = None
+    for loads in (1, 2, 4, 8):
+        for flags in range(4):
+            def fn(k, loads=loads, flags=flags):
+                st = lib.q4probe_stream_rw(srcs[k % R].data_ptr(), dsts[k % R].data_ptr(), groups,
+                                           read_words, write_words, loads, flags, sink.data_ptr(),
+                                           torch.cuda.current_stream().cuda_stream)
+                if st != 0:
+                    raise RuntimeError("q4probe_stream_rw status %d" % st)
+
+            t = run_timed(torch, fn, steps, warmup, reps, "%s/l%d_f%d" % (name, loads, flags),
+                          profile)
+            t["loads"], t["flags"] = loads, flags
+            if best is None or t["kernel_us"] < best["kernel_us"]:
+                best = t
+    t = best
+    MARKS.pop()
+    row = {"workload": name, "kernel": "k_stream_rw<%d, %s, %s> (libq4probe)" % (
+               t["loads"], "true" if t["flags"] & 1 else "false",
+               "true" if t["flags"] & 2 else "false"), "copies": R,
+           "cache": "cold", "read_bytes": rb, "write_bytes": wb, **t,
+           "kernel_GBs": (rb + wb) / (t["kernel_us"] * 1e-6) / 1e9}
+    row["frac_of_hbm_peak"] = row["kernel_GBs"] / HBM_PEAK_GBS
+    del srcs, dsts, sink
+    torch.cuda.empty_cache()
+    return row
+
+
 def probe_sweep(torch, sizes, steps, warmup, reps, out_path=None):
     """The streaming read (libq4probe) of each size, cold, over every launch
     shape q4probe_stream_read_cfg offers: threads per workgroup x loads per
@@ -765,6 +814,16 @@ def main_bench(args):
         by["quantize"]["roofline"]["frac_of_measured_read_ceiling"] = (
             by["quantize"]["roofline"]["achieved"] / qceil["kernel_GBs"])
         emit_row(qceil, rows)
+        # Read-and-write ceilings in each kernel's own proportion (eight blocks a
+        # group: 1024 bytes in, 272 out for the quantizer; 144 in, 1024 out for
+        # the dequant).
+        for key, nblocks, a_w, b_w in (("quantize", 2048 * 4096 // 32, 64, 17),
+                                       ("dequant", 14336 * 4096 // 32, 9, 64)):
+            c = bench_rw_ceiling(torch, nblocks // 8, a_w, b_w, min(50, S), small_w, reps, P)
+            by[key]["roofline"]["measured_rw_ceiling_GBs"] = c["kernel_GBs"]
+            by[key]["roofline"]["frac_of_measured_rw_ceiling"] = (
+                by[key]["roofline"]["achieved"] / c["kernel_GBs"])
+            emit_row(c, rows)
         # The tiny correctness configuration: 74 KB of weights, launch-dominated
         # (one set of inputs; at this size the timed launches stay MALL-resident).
         emit_row(bench_product(torch, q4, wl, "gemv_1x256x512", S, W, reps, P, cold=False), rows)
@@ -831,6 +890,10 @@ def main_bench(args):
                         "2048x14336x4096": compact_gemm(by["gemm_2048x14336x4096"])}
         line["dequant_14336x4096"] = compact_hbm(by["dequant"])
         line["quantize_2048x4096"] = compact_hbm(by["quantize"])
+        for key, lk in (("dequant", "dequant_14336x4096"), ("quantize", "quantize_2048x4096")):
+            fr = by[key]["roofline"].get("frac_of_measured_rw_ceiling")
+            if fr is not None:
+                line[lk]["frac_of_rw_ceiling"] = sig(fr, 3)
     if cpu:
         line["cpu_baseline"] = {"value": sig(cpu["value"]), "unit": "GB/s", "cores": cpu["cores"],
                                 "kind": "oracle",

@@ -79,6 +79,71 @@ hipError_t launch_read_t(int threads, int loads, const u32x4 *src, size_t n16, u
     }
 }
 
+// Read and write streams in a fixed proportion, as a kernel that turns
+// blocks of one size into blocks of another does: a group is A words read and
+// B words written (16 bytes each, max(A, B) = 64), handled by one wavefront,
+// lane r reading word r A / 64 of the group and writing word r B / 64 when it
+// is the first lane on it. A wavefront takes L groups a grid's width apart,
+// all loads issued before any store. NTL / NTS: non-temporal loads / stores.
+// A lane that writes nothing folds its word into the sink test.
+template <int L, bool NTL, bool NTS>
+__global__ __launch_bounds__(256) void k_stream_rw(const u32x4 *__restrict__ src,
+                                                   u32x4 *__restrict__ dst, size_t groups, int A,
+                                                   int B, u32x4 *__restrict__ sink)
+{
+    const size_t w0 = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const size_t waves = (size_t)gridDim.x * 4;
+    const int r = threadIdx.x & 63;
+    u32x4 x[L];
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+        const size_t g = min(w0 + l * waves, groups - 1);   // past the end: re-read, unused
+        const u32x4 *p = src + g * A + ((r * A) >> 6);
+        x[l] = NTL ? __builtin_nontemporal_load(p) : *p;
+    }
+    const bool writer = ((r * B) & 63) < B;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+        const size_t g = w0 + l * waves;
+        if (g < groups) {
+            if (writer) {
+                u32x4 *q = dst + g * B + ((r * B) >> 6);
+                if constexpr (NTS)
+                    __builtin_nontemporal_store(x[l], q);
+                else
+                    *q = x[l];
+            } else
+                acc ^= x[l];
+        }
+    }
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x5bd1e995u)
+        *sink = acc;
+}
+
+template <int L, bool NTL, bool NTS>
+hipError_t launch_rw(const u32x4 *src, u32x4 *dst, size_t groups, int A, int B, u32x4 *sink,
+                     hipStream_t s)
+{
+    const size_t waves = (groups + L - 1) / L;
+    const size_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((k_stream_rw<L, NTL, NTS>), dim3((unsigned)blocks), dim3(256), 0, s, src,
+                       dst, groups, A, B, sink);
+    return hipGetLastError();
+}
+
+template <bool NTL, bool NTS>
+hipError_t launch_rw_l(int loads, const u32x4 *src, u32x4 *dst, size_t groups, int A, int B,
+                       u32x4 *sink, hipStream_t s)
+{
+    switch (loads) {
+    case 1: return launch_rw<1, NTL, NTS>(src, dst, groups, A, B, sink, s);
+    case 2: return launch_rw<2, NTL, NTS>(src, dst, groups, A, B, sink, s);
+    case 4: return launch_rw<4, NTL, NTS>(src, dst, groups, A, B, sink, s);
+    default: return launch_rw<8, NTL, NTS>(src, dst, groups, A, B, sink, s);
+    }
+}
+
 int check(const void *src, size_t n_bytes, const void *sink)
 {
     if (n_bytes % 16 != 0)
@@ -128,4 +193,35 @@ extern "C" __attribute__((visibility("default"))) int q4probe_stream_read(const 
     // about 10% at 9.47 MB and 5% at 42.5 MB; grid and loads per thread
     // matter less.
     return q4probe_stream_read_cfg(src, n_bytes, sink, 512, 1, 1, stream);
+}
+
+extern "C" __attribute__((visibility("default"))) int q4probe_stream_rw(
+    const void *src, void *dst, size_t groups, int read_words, int write_words, int loads,
+    int flags, void *sink, void *stream)
+{
+    if (read_words < 1 || write_words < 1 || read_words > 64 || write_words > 64 ||
+        (read_words != 64 && write_words != 64) ||
+        (loads != 1 && loads != 2 && loads != 4 && loads != 8) || (flags & ~3))
+        return 5;
+    if (groups == 0)
+        return 0;
+    if (!src || !dst || !sink)
+        return 1;
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) |
+         reinterpret_cast<uintptr_t>(sink)) & 15u)
+        return 4;
+    if (groups > ((size_t)4 << 30) / (16 * 64))
+        return 2;   // more than 4 GiB on either side
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const u32x4 *in = static_cast<const u32x4 *>(src);
+    u32x4 *out = static_cast<u32x4 *>(dst), *sk = static_cast<u32x4 *>(sink);
+    const int A = read_words, B = write_words;
+    hipError_t e;
+    switch (flags) {
+    case 0: e = launch_rw_l<false, false>(loads, in, out, groups, A, B, sk, s); break;
+    case 1: e = launch_rw_l<true, false>(loads, in, out, groups, A, B, sk, s); break;
+    case 2: e = launch_rw_l<false, true>(loads, in, out, groups, A, B, sk, s); break;
+    default: e = launch_rw_l<true, true>(loads, in, out, groups, A, B, sk, s); break;
+    }
+    return e == hipSuccess ? 0 : 6;
 }

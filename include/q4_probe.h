@@ -45,6 +45,28 @@ int q4probe_stream_read(const void *src, size_t n_bytes, void *sink, void *strea
 int q4probe_stream_read_cfg(const void *src, size_t n_bytes, void *sink, int threads, int loads,
                             int flags, void *stream);
 
+/*
+ * q4probe_stream_rw — read groups * read_words and write groups * write_words
+ * 16-byte words in that proportion, evenly interleaved (one wavefront per
+ * group of read_words words in and write_words words out, max of the two 64),
+ * with non-temporal loads and stores: the read-and-write ceiling for a kernel
+ * that turns one block stream into another of a different size (Q8_0
+ * quantize: 64 words read per 17 written; Q4_0 dequant: 9 per 64). Each
+ * wavefront takes `loads` groups (1, 2, 4 or 8) a grid's width apart, all
+ * loads issued before any store; `flags` bit 0 makes the loads and bit 1 the
+ * stores non-temporal. The fastest of these shapes is the ceiling.
+ *   src       groups * read_words * 16 bytes, read once.
+ *   dst       groups * write_words * 16 bytes, every byte written once with a
+ *             copy of a word of src (contents not meaningful).
+ *   sink      as q4probe_stream_read.
+ * Returns 0 on success (groups == 0 launches nothing), 1 for a NULL pointer,
+ * 2 for more than 4 GiB on either side, 4 for a misaligned pointer, 5 for
+ * word counts outside [1, 64] or with neither equal to 64, another `loads`
+ * or other flag bits, 6 if the launch is refused.
+ */
+int q4probe_stream_rw(const void *src, void *dst, size_t groups, int read_words, int write_words,
+                      int loads, int flags, void *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,7 +65,8 @@ def test_probe_library_exports_its_header():
     out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True,
                          check=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("q4"))
-    assert declared == exported == ["q4probe_stream_read", "q4probe_stream_read_cfg"]
+    assert declared == exported == ["q4probe_stream_read", "q4probe_stream_read_cfg",
+                                   "q4probe_stream_rw"]
 
 
 def test_version_and_status_codes():

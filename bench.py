@@ -35,7 +35,8 @@ and profiles/trace.json under the same rule.
 
 The oracle (CPU, f64) is timed on this host's cores as ``cpu_baseline``: the
 median of 5 runs of repeated full decode GEMVs, with the tiny and 8-row GEMVs,
-one-core runs and the dequant and quantize beside it.
+one-core runs, 16 rows of the 1024 x 4096 x 4096 prefill GEMM (TFLOP/s) and
+the dequant and quantize beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|headline]
     python bench.py --summarize --trace DIR [--fetch DIR --write DIR --mfma DIR]
@@ -697,9 +698,24 @@ def cpu_baseline(wl):
         return {"what": wname, "value": rate, "unit": "GB/s", "cores": cores,
                 "ms_each": nbytes / rate / 1e6, "calls": calls}
 
+    def gemm_case(wname, rows, cores, run_s):
+        # The first `rows` activation rows of the GEMM against its whole
+        # weight: the same per-output work as the full product, in TFLOP/s.
+        s = wl.WORKLOADS[wname]
+        N, K = s["N"], s["K"]
+        blob = oracle.q4_0_quantize(wl.weights_f32(s["w_seed"], N, K))
+        a = wl.activations_f32(s["a_seed"], s["M"], K)[:rows]
+        flops = 2.0 * rows * N * K
+        rate, calls = median_rate(lambda: oracle.q4_0_matmul(a, blob, N, K, threads=cores),
+                                  flops / 1e3, run_s)
+        return {"what": "%s (first %d rows)" % (wname, rows), "value": rate, "unit": "TFLOP/s",
+                "cores": cores, "ms_each": flops / (rate * 1e12) * 1e3, "calls": calls}
+
     head = gemv_case("gemv_1x4096x4096", threads, 1.0)
     also = [gemv_case("gemv_1x256x512", threads, 0.2), gemv_case("gemv_1x4096x4096", 1, 1.0),
             gemv_case("gemv_8x4096x4096", threads, 1.0), gemv_case("gemv_8x4096x4096", 1, 0.6)]
+    gemm = gemm_case("gemm_1024x4096x4096", 16, threads, 1.0)
+    also.append(gemm)
     sd = wl.WORKLOADS["dequant_14336x4096"]
     wd = oracle.q4_0_quantize(wl.weights_f32(sd["w_seed"], sd["N"], sd["K"]))
     nb = wd.size + sd["N"] * sd["K"] * 4
@@ -899,6 +915,10 @@ def main_bench(args):
                                 "kind": "oracle",
                                 "sample": "median of 5 ~1 s runs of full 1x4096x4096 GEMVs (f64)",
                                 "cpu": cpu["host"]["cpu_model"][:40]}
+        g = next((x for x in cpu["also"] if x["unit"] == "TFLOP/s"), None)
+        if g:
+            line["cpu_baseline"]["gemm"] = {"what": g["what"], "value": sig(g["value"], 3),
+                                            "unit": "TFLOP/s", "cores": g["cores"]}
     line["device"] = "%s %s, %d CUs" % (props.name, getattr(props, "gcnArchName", ""),
                                         props.multi_processor_count)
     print(json.dumps(line, ensure_ascii=False), flush=True)

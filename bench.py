@@ -292,16 +292,22 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)
     nblk = K // 32
+    # Whole-line weight loads where every row is a whole number of 128-byte
+    # lines (the bench's buffers are line-aligned); with them every launch
+    # takes non-temporal loads.
+    la = K % 2048 == 0
+    LA = "true" if la else "false"
+    tf = lambda b: "true" if b else "false"
     if prepared:
         ch = 16 if nblk % 16 == 0 else 8
         if (N + 15) // 16 > 256 and nblk in (64, 128):   # row-group loops
-            return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, false, true>" % (FMT_TYPE[fmt], M,
-                                                                                nblk // 8)
+            return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s, true, %s>" % (
+                FMT_TYPE[fmt], M, nblk // 8, tf(la), LA)
         if nblk == 64:   # one 8-block chunk per wavefront
-            return "k_gemv_stream<%s, %d, 8, 8, false, 2, 16, true, false>" % (FMT_TYPE[fmt], M)
-        nt = (N + 15) // 16 <= 256 and nblk <= 8 * ch
-        return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s, false>" % (FMT_TYPE[fmt], M, ch,
-                                                                          "true" if nt else "false")
+            return "k_gemv_stream<%s, %d, 8, 8, false, 2, 16, true, false, %s>" % (FMT_TYPE[fmt], M, LA)
+        nt = la or ((N + 15) // 16 <= 256 and nblk <= 8 * ch)
+        return "k_gemv_stream<%s, %d, 8, %d, false, 2, 16, %s, false, %s>" % (FMT_TYPE[fmt], M, ch,
+                                                                              tf(nt), LA)
     ks = kl = nblk
     if splitk:   # the library's automatic split
         groups = (N + 15) // 16
@@ -316,16 +322,16 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
     ni = M if act == "bf16" else 2 * M
     splits = -(-nblk // ks)
     if M == 1 and splits == 1 and ch == 16 and (N + 15) // 16 <= 128 and ks <= 8 * ch:
-        return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8, true, false>" % (FMT_TYPE[fmt], bf)   # eight rows per workgroup
+        return "k_gemv_stream<%s, 1, 8, 16, %s, 1, 8, true, false, %s>" % (FMT_TYPE[fmt], bf, LA)   # eight rows per workgroup
     if splits == 1 and ((ch == 16 and ks == 8 * 16) or ks == 8 * 8) and (N + 15) // 16 > 256:
-        return "k_gemv_stream<%s, %d, 8, %d, %s, 0, 16, %s, true>" % (   # row-group loops
-            FMT_TYPE[fmt], M, ks // 8, bf, "true" if M > 1 else "false")
+        return "k_gemv_stream<%s, %d, 8, %d, %s, 0, 16, %s, true, %s>" % (   # row-group loops
+            FMT_TYPE[fmt], M, ks // 8, bf, tf(la or M > 1), LA)
     if splits == 1 and ks == 8 * 8:   # one 8-block chunk per wavefront
-        return "k_gemv_stream<%s, %d, 8, 8, %s, 0, 16, true, false>" % (FMT_TYPE[fmt], M, bf)
+        return "k_gemv_stream<%s, %d, 8, 8, %s, 0, 16, true, false, %s>" % (FMT_TYPE[fmt], M, bf, LA)
     spread = (N + 15) // 16 * splits > 256 or ks > 8 * ch   # non-temporal loads otherwise
     al = spread and not (ch == 16 and ni > 8)
-    return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16, %s, false>" % (FMT_TYPE[fmt], M, ch, bf, 1 if al else 0,
-                                                                    "false" if spread else "true")
+    return "k_gemv_stream<%s, %d, 8, %d, %s, %d, 16, %s, false, %s>" % (
+        FMT_TYPE[fmt], M, ch, bf, 1 if al else 0, tf(la or not spread), LA)
 
 
 def gemm_kernel_name(K, fmt="q4_0", act="f32"):

@@ -325,11 +325,23 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <class F, int M, int NW, int CH_, bool BF, int RPW_ = 16>
+template <class F, int M, int NW, int CH_, bool BF, int RPW_ = 16, bool LA_ = false>
 struct GemvStreamCfg {
     static constexpr int CH = CH_;                        // blocks per chunk (8 or 16)
     static constexpr int RPW = RPW_;                      // weight rows per workgroup (16 or 8)
-    static constexpr int CPR = CH * F::kBytes / 16;       // 16-byte columns per staged row
+    // LA (line-aligned loads; rows a whole number of 128-byte lines from a
+    // line-aligned base): a chunk row is fetched as the NLN whole lines that
+    // hold it. A chunk starts at a multiple of its byte count, so its offset
+    // into its first line is a multiple of that count's lowest set bit, at
+    // most kMaxShift; from every such offset it spans exactly NLN lines
+    // (asserted), so the lines never pass the end of the row.
+    static constexpr bool LA = LA_;
+    static constexpr int kChunkBytes = CH * F::kBytes;
+    static constexpr int kMaxShift = (kChunkBytes & 127) == 0 ? 0 : 128 - (kChunkBytes & -kChunkBytes);
+    static constexpr int NLN = (kMaxShift + kChunkBytes + 127) / 128;
+    static_assert(!LA || (kChunkBytes + 127) / 128 == NLN,
+                  "a chunk spans the same number of lines from every start offset");
+    static constexpr int CPR = LA ? 8 * NLN : CH * F::kBytes / 16;   // 16-byte columns per staged row
     // Weight loads: eight lanes per row take 128 contiguous bytes (one cache
     // line's worth), eight rows per load: loads (RPW / 8) c + h cover columns
     // 8c..8c+7 of rows 8h..8h+7, for each of the NG whole groups of eight
@@ -337,7 +349,7 @@ struct GemvStreamCfg {
     // (TLPR = 64 / RPW lanes per row).
     static constexpr int NG = CPR / 8, TC = CPR % 8, RH = RPW / 8, TLPR = 64 / RPW;
     static constexpr int NLOAD = RH * NG + (TC > 0 ? 1 : 0);   // 16-byte loads per lane per chunk
-    static constexpr int RS = CH * F::kBytes + 16;        // LDS bytes per staged row
+    static constexpr int RS = 16 * CPR + 16;              // LDS bytes per staged row
     static constexpr int WBYTES = RPW * RS;               // staged weight bytes per wavefront
     static constexpr int NI = GemvRows<BF, M>::NI;        // A rows in use
     // The A operands of a chunk pass through LDS in AH halves when a whole
@@ -357,10 +369,14 @@ struct GemvStreamCfg {
     static constexpr int NPART = CH == 16 ? 4 : 2;        // parts a chunk is contracted in
     // Loads (per lane) that hold every byte of the chunk's first b blocks.
     static constexpr int cols_for(int b) { return (F::kBytes * b + 15) / 16; }
+    // LA: the lines that hold them at the largest start offset.
     static constexpr int loads_for(int b)
     {
+        if constexpr (LA)
+            return b == 0 ? 0 : RH * min_c((kMaxShift + F::kBytes * b + 127) / 128, NLN);
         return b == 0 ? 0 : (cols_for(b) <= 8 * NG ? RH * ((cols_for(b) + 7) / 8) : NLOAD);
     }
+    static constexpr int min_c(int x, int y) { return x < y ? x : y; }
     static_assert(RPW == 8 || RPW == 16, "eight or sixteen weight rows per workgroup");
     static_assert(TC <= TLPR, "the tail columns fit the lanes of a row");
     static_assert(CH == 8 || CH == 16, "chunks are 8 or 16 blocks");
@@ -451,11 +467,12 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl<B0>(f, std::make_integer_sequence<int, B1 - B0>{});
 }
 
-// NT: the weight loads are non-temporal. Taken where every wavefront streams
-// one chunk and no second workgroup shares its compute unit (about 6% faster
-// at 1 x 4096 x 4096 and 8 x 4096 x 4096), and by the row-group loops (LN)
-// from two activation rows; with more chunks per wavefront or workgroups per
-// compute unit it was 3-5% slower.
+// NT: the weight loads are non-temporal. With whole-line loads (LA, below) on
+// every launch. Otherwise where every wavefront streams one chunk and no
+// second workgroup shares its compute unit (about 6% faster at 1 x 4096 x
+// 4096 and 8 x 4096 x 4096), and by the row-group loops (LN) from two
+// activation rows; with partial lines and more chunks per wavefront or
+// workgroups per compute unit it was 3-5% slower.
 // MODE 0: as above. MODE 1 (AL): the MFMAs read the chunk's A operands from
 // LDS block by block instead of holding all of them in registers (only where
 // one pass holds the chunk's A operands, AH == 1). That frees CH * 4 VGPRs, so
@@ -472,14 +489,20 @@ __device__ __forceinline__ void static_for(F &&f)
 // are staged, the next group's loads are issued, and each group ends with its
 // own reduction and store (partials in alternate LDS buffers, one barrier per
 // group). Every output sees the same arithmetic as without LN.
+// LA (weight rows a whole number of 128-byte lines from a line-aligned base):
+// each chunk row is fetched as the whole lines that hold it, starting at the
+// line of its first byte, so no load instruction touches part of a line (up to
+// a line more per row than the chunk's bytes; the lines a neighbouring
+// wavefront also fetches are cache hits). The staged chunk row then begins
+// (chunk byte offset mod 128) bytes into the staged lines. Same arithmetic.
 template <class F, int M, int NW, int CH, bool BF, int MODE, int RPW = 16, bool NT = false,
-          bool LN = false>
+          bool LN = false, bool LA = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict__ a,
                                                         const uint8_t *__restrict__ w,
                                                         float *__restrict__ y, int N, int K,
                                                         int ks)
 {
-    using C = GemvStreamCfg<F, M, NW, CH, BF, RPW>;
+    using C = GemvStreamCfg<F, M, NW, CH, BF, RPW, LA>;
     using R = GemvRows<BF, M>;
     constexpr bool AL = MODE == 1, PA = MODE == 2;
     static_assert(!AL || C::AH == 1, "A operands read from LDS need the whole chunk's in one pass");
@@ -554,8 +577,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
             areg[r][0] = *reinterpret_cast<const AV *>(a8 + off);
             areg[r][1] = *reinterpret_cast<const AV *>(a8 + off + ES * (F::a_hi(0) - F::a_lo(0)));
         }
-        // The scheduling barriers keep the loads in column order.
-        const uint32_t cbo = (uint32_t)cb0 * F::kBytes;
+        // The scheduling barriers keep the loads in column order. LA: the
+        // columns count from the line that holds the chunk's first byte.
+        const uint32_t cbo = ((uint32_t)cb0 * F::kBytes) & (LA ? ~127u : ~0u);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < C::RH * C::NG; ++i) {
@@ -777,7 +801,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         // overlaps the decode of the following blocks.
         // Lane j decodes weight row j; with eight rows per workgroup the
         // upper eight MFMA columns repeat row 7 and are never read.
-        const uint8_t *wl = s_w + min(j, C::RPW - 1) * C::RS;
+        // LA: the chunk starts (cb0 kBytes) mod 128 bytes into the staged lines.
+        const uint8_t *wl = s_w + min(j, C::RPW - 1) * C::RS +
+                            (LA ? (((uint32_t)cb0 * F::kBytes) & 127u) : 0u);
         const uint32_t *wrow32 = reinterpret_cast<const uint32_t *>(wl);
         auto contract = [&](auto b0_c, auto b1_c) __attribute__((always_inline)) {
             constexpr int B0 = decltype(b0_c)::value, B1 = decltype(b1_c)::value;
@@ -885,9 +911,25 @@ __global__ __launch_bounds__(256) void k_gemv_split_sum(const float *__restrict_
 }
 
 
-template <class F, int M, bool BF>
-static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N, int K,
-                                hipStream_t s, const q4v::GemvSplit &sp = {1, 0})
+// True where every weight row is a whole number of 128-byte lines from a
+// line-aligned base (K % 2048 == 0 in either format), so the streaming kernels
+// can fetch whole lines (LA). Against loads that start at each chunk's first
+// byte (same process, cold, bit-identical results): 1 x 4096 x 4096 4.24 ->
+// 4.15 us, 2 x 4096 x 4096 4.85 -> 4.60, 1 x 4096 x 2048 3.44 -> 3.28, Q8_0
+// 1 x 4096 x 4096 5.64 -> 5.31. With them the non-temporal hint pays on every
+// launch (it cost 1.5-5% with partial lines where a compute unit holds two
+// workgroups or a wavefront walks several chunks): 1 x 14336 x 4096 9.07 ->
+// 8.69 us, 1 x 4096 x 14336 8.86 -> 8.56, 1 x 11008 x 2048 5.66 -> 5.16, Q8_0
+// 1 x 4096 x 14336 13.7 -> 12.5.
+template <class F>
+static bool gemv_rows_line_aligned(const uint8_t *w, int K)
+{
+    return ((size_t)(K / 32) * F::kBytes) % 128 == 0 && ((uintptr_t)w & 127u) == 0;
+}
+
+template <class F, int M, bool BF, bool LA>
+static hipError_t launch_gemv_m_la(const void *a, const uint8_t *w, float *y, int N, int K,
+                                   hipStream_t s, const q4v::GemvSplit &sp)
 {
     const unsigned grid = (unsigned)((N + 15) / 16);
     // Streaming path: 16-byte aligned rows (K % 256 == 0, so K/32 % 8 == 0 and
@@ -904,7 +946,8 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
         const int ch = q4v::gemv_chunk_blocks(ks, kl);
         // A operands from LDS when a compute unit gets more than one workgroup
         // or a wavefront more than one chunk (and one pass holds them);
-        // otherwise the weight loads are non-temporal (NT).
+        // otherwise, or with whole-line loads, the weight loads are
+        // non-temporal (NT).
         const bool al = (long long)grid * splits > 256 || ks > NW * ch;
         // One activation row, a grid of at most half the compute units and one
         // chunk per wavefront (1x512x4096, 1x2048x4096: 5% and 4% faster):
@@ -914,7 +957,7 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
         // (1x4096x4096 4.53 -> 5.23 us, 1x4096x14336 8.9 -> 11.6 us).
         if constexpr (M == 1)
             if (splits == 1 && ch == 16 && grid <= 128 && ks <= NW * ch)
-                return launch_kernel(k_gemv_stream<F, 1, NW, 16, BF, 1, 8, true>,
+                return launch_kernel(k_gemv_stream<F, 1, NW, 16, BF, 1, 8, true, false, LA>,
                                      dim3((unsigned)((N + 7) / 8), 1u), dim3(64 * NW), 0, s, a, w,
                                      y, N, K, ks);
         // More row groups than compute units, one chunk per wavefront (K/32 ==
@@ -922,38 +965,48 @@ static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N
         // activations once instead of once per 16 rows, with the next group's
         // weights in flight while a group finishes (8 x 14336 x 4096: 19.8 ->
         // 10.9 us, 4 x 14336 x 4096: 16.0 -> 10.0, 1 x 14336 x 4096: 9.5 ->
-        // 9.0). Non-temporal loads from M = 2 (1-3% there, 1.5% slower at M = 1).
+        // 9.0). Non-temporal loads from M = 2 (1-3% there, 1.5% slower at M = 1
+        // with partial-line loads), and always with whole lines (LA).
         if (splits == 1 && ch == 16 && ks == NW * 16 && grid > 256)
-            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0, 16, (M > 1), true>,
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0, 16, (LA || M > 1), true, LA>,
                                  dim3(256u), dim3(64 * NW), 0, s, a, w, y, N, K, ks);
         // K = 8 x 8 blocks (2048): one 8-block chunk per wavefront rather than
         // 16-block chunks on half of them, looping over row groups as above
         // where there are more than 256 (8 x 11008 x 2048: 12.3 -> 6.6 us;
         // 8 x 4096 x 2048: 5.2 -> 4.45, 1 x 4096 x 2048: 3.50 -> 3.44).
         if (splits == 1 && ks == NW * 8 && grid > 256)
-            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0, 16, (M > 1), true>,
+            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0, 16, (LA || M > 1), true, LA>,
                                  dim3(256u), dim3(64 * NW), 0, s, a, w, y, N, K, ks);
         if (splits == 1 && ks == NW * 8)
-            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0, 16, true>, g2, dim3(64 * NW), 0, s,
-                                 a, w, y, N, K, ks);
+            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0, 16, true, false, LA>, g2,
+                                 dim3(64 * NW), 0, s, a, w, y, N, K, ks);
         if (ch == 16) {
             if constexpr (GemvStreamCfg<F, M, NW, 16, BF>::AH == 1)
                 if (al)
-                    return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 1>, g2, dim3(64 * NW),
+                    return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 1, 16, LA, false, LA>, g2, dim3(64 * NW),
                                          0, s, a, w, y, N, K, ks);
             if (al)
-                return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0>, g2, dim3(64 * NW), 0, s,
+                return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0, 16, LA, false, LA>, g2, dim3(64 * NW), 0, s,
                                      a, w, y, N, K, ks);
-            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0, 16, true>, g2, dim3(64 * NW),
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, BF, 0, 16, true, false, LA>, g2, dim3(64 * NW),
                                  0, s, a, w, y, N, K, ks);
         }
         if (al)
-            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 1>, g2, dim3(64 * NW), 0, s, a,
+            return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 1, 16, LA, false, LA>, g2, dim3(64 * NW), 0, s, a,
                                  w, y, N, K, ks);
-        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0, 16, true>, g2, dim3(64 * NW), 0, s, a, w,
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, BF, 0, 16, true, false, LA>, g2, dim3(64 * NW), 0, s, a, w,
                              y, N, K, ks);
     }
     return launch_kernel(k_gemv<F, M, BF>, dim3(grid), dim3(kGemvThreads), 0, s, a, w, y, N, K);
+}
+
+template <class F, int M, bool BF>
+static hipError_t launch_gemv_m(const void *a, const uint8_t *w, float *y, int N, int K,
+                                hipStream_t s, const q4v::GemvSplit &sp = {1, 0})
+{
+    if (gemv_rows_line_aligned<F>(w, K))
+        return launch_gemv_m_la<F, M, BF, true>(a, w, y, N, K, s, sp);
+    return launch_gemv_m_la<F, M, BF, false>(a, w, y, N, K, s, sp);
 }
 
 template <class F, bool BF>
@@ -1044,41 +1097,50 @@ __global__ __launch_bounds__(256) void k_gemv_prep_ops(const float *__restrict__
         reinterpret_cast<int *>(ops + (size_t)nblk * 4 * NI)[m] = p;
 }
 
-template <class F, int M>
-static hipError_t launch_gemv_prepared_m(const void *prep, const uint8_t *w, float *y, int N, int K,
-                                         hipStream_t s)
+template <class F, int M, bool LA>
+static hipError_t launch_gemv_prepared_la(const void *prep, const uint8_t *w, float *y, int N,
+                                          int K, hipStream_t s)
 {
     constexpr int NW = kGemvStreamWaves;
     const int nblk = K / 32;
     const unsigned grid = (unsigned)((N + 15) / 16);
-    // Non-temporal weight loads with one chunk per wavefront and one
-    // workgroup per compute unit, as in launch_gemv_m; row-group loops (plain
-    // loads) where there are more row groups than compute units, so each
+    // Non-temporal weight loads with whole-line loads (LA), or with one chunk
+    // per wavefront and one workgroup per compute unit, as in launch_gemv_m;
+    // row-group loops where there are more row groups than compute units, so each
     // workgroup loads the prepared operands once (8 x 14336 x 4096: 15.5 ->
     // 10.9 us, 1 x 14336 x 4096: 14.1 -> 9.9).
     // K = 2048: one 8-block chunk per wavefront (8 x 4096 x 2048: 4.15 ->
     // 3.8 us; with the row-group loops, 8 x 11008 x 2048: 8.3 -> 6.0).
     if (grid > 256 && nblk == NW * 8)
-        return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, false, true>, dim3(256u),
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, LA, true, LA>, dim3(256u),
                              dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
     if (nblk == NW * 8)
-        return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, true>, dim3(grid),
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, true, false, LA>, dim3(grid),
                              dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
     if (q4v::gemv_chunk_blocks(nblk, nblk) == 16) {
         if (grid > 256 && nblk == NW * 16)
-            return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, false, true>, dim3(256u),
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, LA, true, LA>, dim3(256u),
                                  dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
         if (grid <= 256 && nblk <= NW * 16)
-            return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, true>, dim3(grid),
+            return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, true, false, LA>, dim3(grid),
                                  dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
-        return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2>, dim3(grid), dim3(64 * NW), 0,
+        return launch_kernel(k_gemv_stream<F, M, NW, 16, false, 2, 16, LA, false, LA>, dim3(grid), dim3(64 * NW), 0,
                              s, prep, w, y, N, K, nblk);
     }
     if (grid <= 256 && nblk <= NW * 8)
-        return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, true>, dim3(grid),
+        return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, true, false, LA>, dim3(grid),
                              dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
-    return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2>, dim3(grid), dim3(64 * NW), 0, s,
-                         prep, w, y, N, K, nblk);
+    return launch_kernel(k_gemv_stream<F, M, NW, 8, false, 2, 16, LA, false, LA>, dim3(grid),
+                         dim3(64 * NW), 0, s, prep, w, y, N, K, nblk);
+}
+
+template <class F, int M>
+static hipError_t launch_gemv_prepared_m(const void *prep, const uint8_t *w, float *y, int N, int K,
+                                         hipStream_t s)
+{
+    if (gemv_rows_line_aligned<F>(w, K))
+        return launch_gemv_prepared_la<F, M, true>(prep, w, y, N, K, s);
+    return launch_gemv_prepared_la<F, M, false>(prep, w, y, N, K, s);
 }
 
 template <class F>

@@ -279,15 +279,17 @@ def gemv_kernel_name(M, K, fmt="q4_0", act="f32", splitk=False, N=0, prepared=Fa
         if K % 256:
             return "k_gemv_q8a_any<%s, %d>" % (FMT_TYPE[fmt], M)
         groups = (N + 15) // 16
+        la = K % 2048 == 0   # whole-line weight loads (and then non-temporal ones)
+        LA = "true" if la else "false"
         if M > 1 and groups > 256 and K // 32 in (64, 128):   # row-group loops
-            return "k_gemv_q8a<%s, %d, 8, %d, %s, true>" % (FMT_TYPE[fmt], M, K // 256,
-                                                           "true" if fmt == "q4_0" else "false")
+            return "k_gemv_q8a<%s, %d, 8, %d, %s, true, %s>" % (
+                FMT_TYPE[fmt], M, K // 256, "true" if (la or fmt == "q4_0") else "false", LA)
         if groups <= 256 and K // 32 == 64:   # one 8-block chunk per wavefront
-            return "k_gemv_q8a<%s, %d, 8, 8, true, false>" % (FMT_TYPE[fmt], M)
+            return "k_gemv_q8a<%s, %d, 8, 8, true, false, %s>" % (FMT_TYPE[fmt], M, LA)
         ch16 = (K // 32) % 16 == 0 and (groups <= 256 or M == 1)
-        nt = ch16 and groups <= 256 and K // 32 <= 128   # non-temporal weight loads
-        return "k_gemv_q8a<%s, %d, 8, %d, %s, false>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8,
-                                                        "true" if nt else "false")
+        nt = la or (ch16 and groups <= 256 and K // 32 <= 128)   # non-temporal weight loads
+        return "k_gemv_q8a<%s, %d, 8, %d, %s, false, %s>" % (FMT_TYPE[fmt], M, 16 if ch16 else 8,
+                                                            "true" if nt else "false", LA)
     bf = "true" if act == "bf16" else "false"
     if K % 256:
         return "k_gemv<%s, %d, %s>" % (FMT_TYPE[fmt], M, bf)

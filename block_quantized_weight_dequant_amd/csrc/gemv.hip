@@ -1297,12 +1297,12 @@ __device__ __forceinline__ long q8a_weight_operand(const uint32_t *wrow, int g)
 template <class F>
 constexpr float q8a_weight_scale() { return F::kBytes == kQ4Bytes ? 0.0625f : 1.0f; }
 
-template <class F, int M, int NW, int CH, bool NT = false, bool LN = false>
+template <class F, int M, int NW, int CH, bool NT = false, bool LN = false, bool LA = false>
 __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict__ aq,
                                                      const uint8_t *__restrict__ w,
                                                      float *__restrict__ y, int N, int K)
 {
-    using C = GemvStreamCfg<F, M, NW, CH, false>;
+    using C = GemvStreamCfg<F, M, NW, CH, false, 16, LA>;
     constexpr int NACC = M < 4 ? M : 4;           // C rows a lane keeps (activation rows 4g + r)
     constexpr int CPRA = CH * kQ8Bytes / 16;      // 16-byte columns of a chunk's activation row
     constexpr int NAE = M * CPRA;                 // ... of its M rows
@@ -1353,7 +1353,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
             areg[r] = *reinterpret_cast<const u32x4 *>(
                 aq + ((uint32_t)m * arow_bytes + (uint32_t)cb0 * kQ8Bytes + 16u * (uint32_t)col));
         }
-        const uint32_t cbo = (uint32_t)cb0 * F::kBytes;
+        const uint32_t cbo = ((uint32_t)cb0 * F::kBytes) & (LA ? ~127u : ~0u);   // LA: from the chunk's first line
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 2 * C::NG; ++i) {
@@ -1376,7 +1376,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
     fetch(min(wb0, nblk - CH));
 
     const uint32_t *arow32 = reinterpret_cast<const uint32_t *>(s_act + min(j, M - 1) * RSA);
-    const uint32_t *wrow32 = reinterpret_cast<const uint32_t *>(s_w + j * C::RS);
+    const uint8_t *wrow = s_w + j * C::RS;
     const float *da_lane = s_da + 4 * min(g, 1);
     const i32x4 zero4 = {0, 0, 0, 0};
     float ysum[NACC];
@@ -1434,6 +1434,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q8a(const uint8_t *__restrict_
 #pragma unroll
         for (int r = 0; r < NACC; ++r)
             acc[r] = 0.0f;
+        // LA: the chunk starts (cb0 kBytes) mod 128 bytes into the staged lines.
+        const uint32_t *wrow32 = reinterpret_cast<const uint32_t *>(
+            wrow + (LA ? (((uint32_t)cb0 * F::kBytes) & 127u) : 0u));
         auto stage = [&](auto i0_c, auto i1_c) __attribute__((always_inline)) {
             constexpr int I0 = decltype(i0_c)::value, I1 = decltype(i1_c)::value;
 #pragma unroll
@@ -1580,9 +1583,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_q8a_any(const uint8_t *__
     }
 }
 
-template <class F, int M>
-static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *y, int N, int K,
-                                    hipStream_t s)
+template <class F, int M, bool LA>
+static hipError_t launch_gemv_q8a_la(const uint8_t *aq, const uint8_t *w, float *y, int N, int K,
+                                     hipStream_t s)
 {
     constexpr int NW = kGemvStreamWaves;
     const unsigned grid = (unsigned)((N + 15) / 16);
@@ -1592,38 +1595,52 @@ static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *
         // units and M > 1: those kernels need more than 128 VGPRs, so one
         // workgroup holds a compute unit, while the 8-block ones (under 100)
         // let two or more share it and overlap one's loads with another's work.
-        // Non-temporal weight loads as in launch_gemv_m: one chunk per
-        // wavefront and one workgroup per compute unit.
+        // Non-temporal weight loads as in launch_gemv_m: with whole-line
+        // loads (LA) everywhere (1 x 14336 x 4096 9.08 -> 8.59 us, Q8_0
+        // weights 1 x 4096 x 4096 5.55 -> 5.12, 8 x 11008 x 2048 6.69 ->
+        // 6.15), otherwise one chunk per wavefront and one workgroup per
+        // compute unit.
         // More row groups than compute units and one 16-block chunk per
         // wavefront, from two activation rows: 256 workgroups walk the row
         // groups, staging each chunk's activation blocks and scales once (as
         // launch_gemv_m; 8 x 14336 x 4096: 13.6 -> 11.4 us, 8 x 8192 x 4096:
         // 8.2 -> 7.2; one row: 9.1 -> 9.5, so not there). Non-temporal loads
-        // for Q4_0 weights only (Q8_0 8 x 14336 x 4096: 15.4 us plain, 16.3).
+        // with whole lines, else for Q4_0 weights only (Q8_0 8 x 14336 x 4096
+        // with partial lines: 15.4 us plain, 16.3; whole lines and
+        // non-temporal: 14.4).
         if constexpr (M > 1)
             if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && grid > 256 && nblk == NW * 16)
-                return launch_kernel(k_gemv_q8a<F, M, NW, 16, F::kBytes == kQ4Bytes, true>,
+                return launch_kernel(k_gemv_q8a<F, M, NW, 16, LA || F::kBytes == kQ4Bytes, true, LA>,
                                      dim3(256u), dim3(64 * NW), 0, s, aq, w, y, N, K);
         // K = 2048: one 8-block chunk per wavefront, with the row-group loops
         // from two rows on wide grids (8 x 11008 x 2048: 7.25 -> 6.7 us).
         if constexpr (M > 1)
             if (grid > 256 && nblk == NW * 8)
-                return launch_kernel(k_gemv_q8a<F, M, NW, 8, F::kBytes == kQ4Bytes, true>,
+                return launch_kernel(k_gemv_q8a<F, M, NW, 8, LA || F::kBytes == kQ4Bytes, true, LA>,
                                      dim3(256u), dim3(64 * NW), 0, s, aq, w, y, N, K);
         if (grid <= 256 && nblk == NW * 8)
-            return launch_kernel(k_gemv_q8a<F, M, NW, 8, true>, dim3(grid), dim3(64 * NW), 0, s,
+            return launch_kernel(k_gemv_q8a<F, M, NW, 8, true, false, LA>, dim3(grid), dim3(64 * NW), 0, s,
                                  aq, w, y, N, K);
         if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && grid <= 256 && nblk <= NW * 16)
-            return launch_kernel(k_gemv_q8a<F, M, NW, 16, true>, dim3(grid), dim3(64 * NW), 0, s,
+            return launch_kernel(k_gemv_q8a<F, M, NW, 16, true, false, LA>, dim3(grid), dim3(64 * NW), 0, s,
                                  aq, w, y, N, K);
         if (q4v::gemv_chunk_blocks(nblk, nblk) == 16 && (grid <= 256 || M == 1))
-            return launch_kernel(k_gemv_q8a<F, M, NW, 16>, dim3(grid), dim3(64 * NW), 0, s, aq, w,
+            return launch_kernel(k_gemv_q8a<F, M, NW, 16, LA, false, LA>, dim3(grid), dim3(64 * NW), 0, s, aq, w,
                                  y, N, K);
-        return launch_kernel(k_gemv_q8a<F, M, NW, 8>, dim3(grid), dim3(64 * NW), 0, s, aq, w, y,
+        return launch_kernel(k_gemv_q8a<F, M, NW, 8, LA, false, LA>, dim3(grid), dim3(64 * NW), 0, s, aq, w, y,
                              N, K);
     }
     return launch_kernel(k_gemv_q8a_any<F, M>, dim3(grid), dim3(kGemvThreads), 0, s, aq, w, y, N,
                          K);
+}
+
+template <class F, int M>
+static hipError_t launch_gemv_q8a_m(const uint8_t *aq, const uint8_t *w, float *y, int N, int K,
+                                    hipStream_t s)
+{
+    if (gemv_rows_line_aligned<F>(w, K))
+        return launch_gemv_q8a_la<F, M, true>(aq, w, y, N, K, s);
+    return launch_gemv_q8a_la<F, M, false>(aq, w, y, N, K, s);
 }
 
 template <class F>

@@ -16,6 +16,7 @@ if not torch.cuda.is_available():
 
 from block_quantized_weight_dequant_amd import binding  # noqa: E402
 from block_quantized_weight_dequant_amd import workloads as wl  # noqa: E402
+import oracle  # noqa: E402
 from gpu_helpers import (DEV, Guarded, assert_within_tolerance, oracle_matmul,  # noqa: E402
                          oracle_matmul_sampled, to_dev, weight_blob)
 
@@ -25,6 +26,7 @@ PREPARE = {"q4_0": (binding.q4_gemv_prepare_bytes, binding.q4_gemv_prepare, bind
            "q8_0": (binding.q8_gemv_prepare_bytes, binding.q8_gemv_prepare, binding.q8_gemv_prepared)}
 SPLITK = {"q4_0": (binding.q4_gemv_splitk_workspace_bytes, binding.q4_gemv_splitk),
           "q8_0": (binding.q8_gemv_splitk_workspace_bytes, binding.q8_gemv_splitk)}
+GEMV_Q8A = {"q4_0": binding.q4_gemv_q8a, "q8_0": binding.q8_gemv_q8a}
 
 
 def _placed(blob: np.ndarray, offset: int):
@@ -130,3 +132,18 @@ def test_line_and_column_loads_agree_splitk(fmt):
     y0, y16 = _both(lambda w, y: splitk(a_dev, w, y, M, N, K, workspace=ws), blob, M, N)
     np.testing.assert_array_equal(y0.view(np.uint32), y16.view(np.uint32))
     _check(fmt, a, blob, N, K, y0, "split-K %s" % fmt, sampled=False)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (8, 4096, 4096), (4, 4100, 4096), (8, 4200, 2048),
+                                   (1, 1000, 14336)])
+def test_line_and_column_loads_agree_q8a(fmt, M, N, K):
+    """The GEMV over Q8_0-quantized activations (reading 15: the product of the
+    dequantized activations) takes the same two load forms."""
+    blob = weight_blob(fmt, N, K, 940)
+    a_q = oracle.q8_0_quantize(wl.activations_f32(941, M, K))
+    aq_dev = to_dev(a_q)
+    y0, y16 = _both(lambda w, y: GEMV_Q8A[fmt](aq_dev, w, y, M, N, K), blob, M, N)
+    np.testing.assert_array_equal(y0.view(np.uint32), y16.view(np.uint32))
+    a_deq = oracle.q8_0_dequant(a_q).reshape(M, K)
+    _check(fmt, a_deq, blob, N, K, y0, "q8a %s %dx%dx%d" % (fmt, M, N, K), sampled=True)

@@ -847,16 +847,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 ysum[h] += ldexpf(BF ? acc[h] : acc[2 * h] + acc[2 * h + 1], -pm - F::kHiLog2);
             }
         };
-        for_each_part<C::NPART>([&](auto p_c) __attribute__((always_inline)) {
+        // In the row-group loops a group's bytes have mostly landed by the
+        // time its wavefront gets to them (they were requested a group
+        // earlier), so parts no longer overlap arrival and only chain LDS
+        // round trips: Q4_0 groups take 8-block parts there (1 x 14336 x 4096
+        // 8.75 -> 8.48 us, 8 x 14336 x 4096 11.02 -> 10.81, 1 x 11008 x 2048
+        // 5.19 -> 4.98; Q8_0 was 1-2% slower with fewer parts and keeps them).
+        constexpr int NPX = (LN && F::kBytes == kQ4Bytes) ? CH / 8 : C::NPART;
+        for_each_part<NPX>([&](auto p_c) __attribute__((always_inline)) {
             constexpr int P = decltype(p_c)::value;
-            constexpr int B0 = P * C::CH / C::NPART, B1 = (P + 1) * C::CH / C::NPART;
+            constexpr int B0 = P * C::CH / NPX, B1 = (P + 1) * C::CH / NPX;
             constexpr int L0 = C::loads_for(B0), L1 = C::loads_for(B1);
             stage(std::integral_constant<int, L0>{}, std::integral_constant<int, L1>{});
             auto run_part = [&]() __attribute__((always_inline)) {
                 wave_lds_sync();
                 contract(std::integral_constant<int, B0>{}, std::integral_constant<int, B1>{});
             };
-            if constexpr (P < C::NPART - 1) {
+            if constexpr (P < NPX - 1) {
                 run_part();
             } else if (LN && more) {
                 // Every load of this group is staged: prefetch the next

@@ -847,13 +847,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
                 ysum[h] += ldexpf(BF ? acc[h] : acc[2 * h] + acc[2 * h + 1], -pm - F::kHiLog2);
             }
         };
-        // In the row-group loops a group's bytes have mostly landed by the
-        // time its wavefront gets to them (they were requested a group
-        // earlier), so parts no longer overlap arrival and only chain LDS
-        // round trips: Q4_0 groups take 8-block parts there (1 x 14336 x 4096
-        // 8.75 -> 8.48 us, 8 x 14336 x 4096 11.02 -> 10.81, 1 x 11008 x 2048
-        // 5.19 -> 4.98; Q8_0 was 1-2% slower with fewer parts and keeps them).
-        constexpr int NPX = (LN && F::kBytes == kQ4Bytes) ? CH / 8 : C::NPART;
+        // In the row-group loops, and where a wavefront walks several chunks
+        // (the launches with the A operands in LDS or plain loads), a group's
+        // or chunk's bytes have mostly landed by the time its wavefront gets
+        // to them (they were requested one round earlier), so parts no longer
+        // overlap arrival and only chain LDS round trips: Q4_0 takes 8-block
+        // parts there (1 x 14336 x 4096 8.75 -> 8.48 us, 1 x 11008 x 2048
+        // 5.19 -> 4.98, 1 x 4096 x 14336 8.51 -> 8.25, bfloat16 1 x 4096 x
+        // 14336 8.37 -> 7.86; Q8_0 was 1-2% slower with fewer parts).
+        constexpr bool kRounds = LN || (MODE == 1 && RPW == 16) || (MODE == 0 && !NT);
+        constexpr int NPX = (kRounds && F::kBytes == kQ4Bytes) ? CH / 8 : C::NPART;
         for_each_part<NPX>([&](auto p_c) __attribute__((always_inline)) {
             constexpr int P = decltype(p_c)::value;
             constexpr int B0 = P * C::CH / NPX, B1 = (P + 1) * C::CH / NPX;

@@ -854,9 +854,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_stream(const void *__restrict_
         // overlap arrival and only chain LDS round trips: Q4_0 takes 8-block
         // parts there (1 x 14336 x 4096 8.75 -> 8.48 us, 1 x 11008 x 2048
         // 5.19 -> 4.98, 1 x 4096 x 14336 8.51 -> 8.25, bfloat16 1 x 4096 x
-        // 14336 8.37 -> 7.86; Q8_0 was 1-2% slower with fewer parts).
+        // 14336 8.37 -> 7.86; Q8_0 was 1-2% slower with fewer parts). With
+        // whole-line loads a Q4_0 chunk's first and second halves wait for the
+        // same loads as the parts within them, so they are one part each there
+        // too (1 x 4096 x 4096 4.15 -> 4.11 us, 4 x 4096 x 4096 5.22 -> 5.12).
         constexpr bool kRounds = LN || (MODE == 1 && RPW == 16) || (MODE == 0 && !NT);
-        constexpr int NPX = (kRounds && F::kBytes == kQ4Bytes) ? CH / 8 : C::NPART;
+        constexpr int NPX = ((kRounds || LA) && F::kBytes == kQ4Bytes) ? CH / 8 : C::NPART;
         for_each_part<NPX>([&](auto p_c) __attribute__((always_inline)) {
             constexpr int P = decltype(p_c)::value;
             constexpr int B0 = P * C::CH / NPX, B1 = (P + 1) * C::CH / NPX;
